@@ -1,0 +1,50 @@
+"""Helpers shared by the tests: turn the seeded host inputs into the oracle's
+float64 model, and the comparison rules used by the parity tests."""
+
+import numpy as np
+import torch
+
+from oracle import TinyModel, fp8_e4m3fn_decode
+
+
+def to_f64(t):
+    """Exact float64 value of a host tensor (bf16 / f32 / e4m3fn bytes need a
+    scale, see ``expert_f64``)."""
+    return t.to(torch.float64).numpy()
+
+
+def expert_f64(w, s):
+    """Dequantized expert weights: e4m3fn bytes times the per-row scale, or
+    the float values as given when the tensor is not uint8."""
+    if w.dtype == torch.uint8:
+        return fp8_e4m3fn_decode(w.numpy()) * s.to(torch.float64).numpy()[..., None]
+    return to_f64(w)
+
+
+def oracle_model(dims, weights, layers=None):
+    nl = dims.NL if layers is None else layers
+    m = TinyModel(D=dims.D, Hq=dims.Hq, Hkv=dims.Hkv, dh=dims.dh, E=dims.E,
+                  k=dims.k, I=dims.I, V=dims.V, emb=to_f64(weights["emb"]),
+                  lm=to_f64(weights["lm"]))
+    for l in range(nl):
+        m.layers.append(dict(
+            wqkv=to_f64(weights[f"wqkv.{l}"]), wo=to_f64(weights[f"wo.{l}"]),
+            wr=to_f64(weights[f"wr.{l}"]),
+            w_gate_up=expert_f64(weights[f"wgu.{l}"], weights[f"sgu.{l}"]),
+            w_down=expert_f64(weights[f"wd.{l}"], weights[f"sd.{l}"])))
+    return m
+
+
+def empty_caches(dims, B, Tmax, layers=None):
+    nl = dims.NL if layers is None else layers
+    shape = (B, dims.Hkv, Tmax, dims.dh)
+    return [np.zeros(shape) for _ in range(nl)], [np.zeros(shape) for _ in range(nl)]
+
+
+def rel_err_rows(got, ref):
+    """Max over rows of ||got - ref|| / ||ref|| (rows = last axis)."""
+    got = np.asarray(got, np.float64).reshape(-1, np.shape(ref)[-1])
+    ref = np.asarray(ref, np.float64).reshape(-1, np.shape(ref)[-1])
+    num = np.linalg.norm(got - ref, axis=1)
+    den = np.maximum(np.linalg.norm(ref, axis=1), 1e-30)
+    return float((num / den).max())
