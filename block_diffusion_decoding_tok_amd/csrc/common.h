@@ -1,0 +1,84 @@
+// Shared device/host helpers of libdg (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string>
+
+#include "../../include/dg.h"
+
+namespace dg {
+
+// ------------------------------------------------------------ error state
+void set_error(const std::string& msg);
+dg_status fail(dg_status st, const std::string& msg);
+
+#define DG_CHECK_ARG(cond, msg) \
+  do { if (!(cond)) return ::dg::fail(DG_ERR_INVALID_ARG, msg); } while (0)
+#define DG_CHECK_SHAPE(cond, msg) \
+  do { if (!(cond)) return ::dg::fail(DG_ERR_SHAPE, msg); } while (0)
+#define DG_HIP(call)                                                              \
+  do {                                                                            \
+    hipError_t e_ = (call);                                                       \
+    if (e_ != hipSuccess)                                                         \
+      return ::dg::fail(DG_ERR_HIP, std::string(#call) + ": " + hipGetErrorString(e_)); \
+  } while (0)
+#define DG_LAUNCH_CHECK() DG_HIP(hipGetLastError())
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// ------------------------------------------------------------ bf16 helpers
+typedef uint16_t bf16_t;   // raw bits
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+// Round-to-nearest-even float -> bf16 (NaN stays NaN).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<bf16_t>(u >> 16);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+// Element loads/stores for the two activation types.
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  __device__ static float load(const float* p, size_t i) { return p[i]; }
+  __device__ static void store(float* p, size_t i, float v) { p[i] = v; }
+};
+template <> struct Elem<bf16_t> {
+  __device__ static float load(const bf16_t* p, size_t i) { return bf16_to_f32(p[i]); }
+  __device__ static void store(bf16_t* p, size_t i, float v) { p[i] = f32_to_bf16(v); }
+};
+
+// ------------------------------------------------------------ reductions
+__device__ __forceinline__ float warp_max(float v) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float warp_sum(float v) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ __forceinline__ double warp_sum_d(double v) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// RoPE angle for (position, pair j) reduced to [-pi, pi] in double, then
+// evaluated in float: pos * theta^(-2j/dh).
+__device__ __forceinline__ void rope_cos_sin(int pos, int j, int dh, float theta, float* c,
+                                             float* s) {
+  double inv = exp(-2.0 * static_cast<double>(j) / dh * log(static_cast<double>(theta)));
+  double ang = static_cast<double>(pos) * inv;
+  const double two_pi = 6.283185307179586476925286766559;
+  ang -= two_pi * rint(ang / two_pi);
+  float a = static_cast<float>(ang);
+  sincosf(a, s, c);
+}
+
+}  // namespace dg

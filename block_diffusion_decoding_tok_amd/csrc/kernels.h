@@ -1,0 +1,73 @@
+// Internal launchers of libdg (host side).  Each launcher assumes its
+// arguments were validated by the C ABI layer.
+#pragma once
+
+#include "common.h"
+
+namespace dg {
+
+// sampler.hip
+size_t sampler_workspace_bytes(int B, int L, int V);
+dg_status launch_sampler(const void* logits, int logit_dtype, int B, int L, int V, int step,
+                         const dg_sampler_cfg& cfg, const int32_t* prefix_len, int32_t* tokens,
+                         uint8_t* committed, uint8_t* renoised, float* maxprob, float* entropy,
+                         float* mean_entropy, int32_t* done, int32_t* status,
+                         int32_t* steps_taken, void* ws, hipStream_t stream);
+dg_status launch_init_canvas(const int32_t* prefix_len, int B, int L, int V, uint64_t seed,
+                             int32_t* tokens, uint8_t* committed, int32_t* done,
+                             hipStream_t stream);
+dg_status launch_philox(const uint32_t* ctr, int64_t n, uint64_t seed, uint32_t* out,
+                        hipStream_t stream);
+dg_status launch_gumbel(const uint32_t* w, int64_t n, float* out, hipStream_t stream);
+
+// attention.hip
+// Row strides (in elements) between consecutive tokens of q / k_new / v_new
+// let the model pass slices of its fused QKV output.
+struct AttnArgs {
+  const void* q; const void* k_new; const void* v_new;
+  int64_t q_stride, kv_stride;        // elements between tokens
+  void* k_cache; void* v_cache;
+  const int32_t* prefix_len;
+  int B, Lq, Hq, Hkv, dh, Tmax, mask_mode;
+  float rope_theta;
+  int dtype;
+  void* out;                          // [B, Lq, Hq, dh] dense
+};
+size_t attention_workspace_bytes(int B, int Lq, int Hq, int Hkv, int dh, int Tmax, int dtype);
+dg_status launch_attention(const AttnArgs& a, void* ws, hipStream_t stream);
+dg_status launch_commit(const void* k_new, const void* v_new, int64_t kv_stride, void* k_cache,
+                        void* v_cache, int32_t* prefix_len, int B, int L, int Hkv, int dh,
+                        int Tmax, float rope_theta, int dtype, bool advance, hipStream_t stream);
+dg_status launch_advance_prefix(int32_t* prefix_len, int B, int L, hipStream_t stream);
+
+// moe.hip
+size_t moe_route_workspace_bytes(int T, int E, int k);
+dg_status launch_moe_route(const float* logits, int T, int E, int k, int32_t* topk_ids,
+                           float* gates, int32_t* offsets, int32_t* sorted_rows, void* ws,
+                           hipStream_t stream);
+size_t moe_ffn_workspace_bytes(int T, int D, int I, int E, int k, int x_dtype);
+dg_status launch_moe_ffn(const void* x, int x_dtype, const void* w_gate_up, const void* w_down,
+                         int w_dtype, const float* s_gate_up, const float* s_down,
+                         const int32_t* topk_ids, const float* gates, const int32_t* offsets,
+                         const int32_t* sorted_rows, int T, int D, int I, int E, int k, float* y,
+                         void* ws, hipStream_t stream);
+
+// dense.hip: C = A W^T with A [M, K] (bf16 or f32), W [N, K] (same dtype),
+// fp32 accumulation.  Epilogues: store in out_dtype, or add into f32 C.
+enum GemmEpilogue { kStore = 0, kAccumulateF32 = 1 };
+dg_status launch_gemm(const void* A, const void* W, void* C, int M, int N, int K, int dtype,
+                      int out_dtype, GemmEpilogue ep, hipStream_t stream);
+// RMSNorm of f32 rows x [M, D] (eps 1e-6, unit gain) into out_dtype.
+dg_status launch_rmsnorm(const float* x, void* out, int M, int D, int out_dtype,
+                         hipStream_t stream);
+// x[t] = emb[tokens[t]] as f32.
+dg_status launch_embed(const int32_t* tokens, const void* emb, float* x, int M, int D,
+                       int dtype, hipStream_t stream);
+
+// init.hip
+dg_status launch_fill_normal(void* dst, int dtype, size_t n, float std, uint64_t seed,
+                             uint32_t stream_id, hipStream_t stream);
+dg_status launch_quantize_fp8_rows(const float* src, uint8_t* q, float* scale, int64_t rows,
+                                   int cols, hipStream_t stream);
+
+}  // namespace dg

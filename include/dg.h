@@ -1,0 +1,282 @@
+/*
+ * dg.h -- C ABI of libdg.so: the canvas denoising step of a block-
+ * autoregressive, uniform-state text-diffusion decoder on MI355X (gfx950).
+ *
+ * Pages cited (by title; sections are the pages' own headings):
+ *   [TR]    "[AI] DiffusionGemma: 256토큰 블록을 병렬 정제하는 확산 LLM"
+ *           (summary of the DiffusionGemma technical report)
+ *   [GUIDE] aisparkup "diffusion-gemma tutorial / developer guide"
+ *   [GN]    "DiffusionGemma: 4배 빠른 텍스트 생성" (GeekNews)
+ *   [WE0]   test.we0.ai article on DiffusionGemma
+ *
+ * Conventions for every entry point
+ *   - All tensor arguments are DEVICE pointers owned by the caller, row-major,
+ *     densely packed in the order of the dimensions given.  Arrays of per-layer
+ *     pointers (``void* const*``) are HOST arrays of device pointers.
+ *   - ``stream`` is a hipStream_t (NULL = the default stream).  Every call is
+ *     asynchronous on that stream; results are valid once it is synchronized.
+ *     Nothing is allocated per call: the caller passes a workspace of at least
+ *     the size returned by the matching *_workspace_size() function.
+ *   - Arguments are validated on the host before anything is launched; an
+ *     invalid call returns a negative dg_status and launches nothing.  The
+ *     message of the last failure on the calling thread is dg_last_error().
+ *   - Device-side conditions (non-finite logits) are reported through a
+ *     caller-provided device status word (see dg_sampler_step).
+ */
+#ifndef DG_H_
+#define DG_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DG_OK = 0,
+  DG_ERR_INVALID_ARG = -1,   /* null pointer, bad enum, negative size */
+  DG_ERR_SHAPE = -2,         /* sizes inconsistent or outside supported set */
+  DG_ERR_UNSUPPORTED = -3,   /* valid but not implemented combination */
+  DG_ERR_WORKSPACE = -4,     /* workspace missing or too small */
+  DG_ERR_HIP = -5,           /* a HIP runtime call failed (see dg_last_error) */
+  DG_ERR_NONFINITE = -6      /* reserved: non-finite input detected */
+} dg_status;
+
+typedef enum { DG_F32 = 0, DG_BF16 = 1, DG_FP8_E4M3 = 2 /* OCP e4m3fn */ } dg_dtype;
+
+typedef enum { DG_MASK_CANVAS = 0, DG_MASK_CAUSAL = 1 } dg_mask_mode;
+
+/* Device status-word bits. */
+#define DG_STATUS_NONFINITE_LOGITS 1
+
+/*
+ * Sampler settings.  [TR] section "DiffusionGemma의 구성" (sampler settings):
+ * canvas length 256, at most 48 denoising steps, temperature linear from 0.8 to
+ * 0.4, adaptive stop threshold 0.005.  The commit / re-noise probabilities
+ * (0.9 / 0.1) are not given by the pages.
+ *   canvas_len    L, tokens per block
+ *   max_steps     S, step cap; the temperature schedule runs over S
+ *   fixed_steps   0 = adaptive stop; F > 0 = exactly F steps, no stop test
+ *   seed          Philox4x32-10 key (lo, hi words)
+ */
+typedef struct {
+  int32_t canvas_len;
+  int32_t max_steps;
+  int32_t fixed_steps;
+  float temp_start;
+  float temp_end;
+  float stop_entropy;
+  float commit_prob;
+  float renoise_prob;
+  uint64_t seed;
+} dg_sampler_cfg;
+
+/* Library version (major * 10000 + minor * 100 + patch). */
+int dg_version(void);
+/* Message of the last failing call on this thread ("" if none). */
+const char* dg_last_error(void);
+
+/* ------------------------------------------------------------------ sampler
+ * dg_sampler_step: one step of the canvas sampler over B rows.
+ * Defines: [TR] "DiffusionGemma의 구성" (temperature schedule, step cap, stop
+ * threshold); [GUIDE] "Uniform State Diffusion" (confident tokens anchor,
+ * unconfident ones are re-randomized); [GN] "텍스트 확산의 작동 방식".
+ *   T_s = temp_start + (temp_end - temp_start) * step / (max_steps - 1)
+ *   per position: z = logits / T_s; maxprob = max softmax(z); entropy (nats);
+ *   sample = argmax_v (z_v + Gumbel_v) with Gumbel from Philox4x32-10 counter
+ *   (v >> 2, prefix_len[b] + i, step, b), lane v & 3 (ties -> lowest v).
+ *   mean_entropy[b] = mean over all L positions; the step ends the row if
+ *   fixed_steps ? step == fixed_steps - 1 : (mean < stop_entropy || step ==
+ *   max_steps - 1).  For uncommitted positions: maxprob >= commit_prob ->
+ *   token = sample, committed = 1; else maxprob < renoise_prob and the step
+ *   does not end the row -> token = uniform id from counter (0, pos, step,
+ *   (1 << 24) | b), renoised = 1; else token = sample.  done[b] = ends.
+ * Arguments
+ *   logits     [B, L, V] DG_BF16 or DG_F32 (logit_dtype); V % 8 == 0, V < 2^31
+ *   prefix_len [B] int32: absolute position of canvas slot 0
+ *   tokens, committed [B, L] in/out; renoised, maxprob, entropy [B, L] out;
+ *   mean_entropy [B] out; done [B] in/out (rows with done = 1 on entry are not
+ *   touched at all, outputs included)
+ *   status     optional int32 device word: DG_STATUS_NONFINITE_LOGITS is OR-ed
+ *              in when a processed row holds a NaN/Inf logit
+ *   ws         >= dg_sampler_workspace_size(B, L, V) bytes
+ * Errors: DG_ERR_INVALID_ARG (null pointer, bad dtype), DG_ERR_SHAPE (sizes,
+ * step outside [0, max_steps) or [0, fixed_steps)), DG_ERR_WORKSPACE.
+ */
+size_t dg_sampler_workspace_size(int B, int L, int V);
+dg_status dg_sampler_step(const void* logits, int logit_dtype, int B, int L, int V,
+                          int step, const dg_sampler_cfg* cfg, const int32_t* prefix_len,
+                          int32_t* tokens, uint8_t* committed, uint8_t* renoised,
+                          float* maxprob, float* entropy, float* mean_entropy,
+                          int32_t* done, int32_t* status, void* ws, size_t ws_bytes,
+                          void* stream);
+
+/* dg_init_canvas: the block's starting canvas ([GN] "텍스트 확산의 작동 방식";
+ * [GUIDE] "Uniform State Diffusion": random placeholder tokens).
+ * tokens[b, i] = uniform id in [0, V) from Philox counter
+ * (0, prefix_len[b] + i, 0, (2 << 24) | b); committed = 0; done = 0.
+ *   prefix_len [B] int32; tokens [B, L] int32; committed [B, L] u8; done [B]. */
+dg_status dg_init_canvas(const int32_t* prefix_len, int B, int L, int V, uint64_t seed,
+                         int32_t* tokens, uint8_t* committed, int32_t* done, void* stream);
+
+/* ---------------------------------------------------------------- attention
+ * dg_canvas_attention: attention of a block of Lq queries per row over the
+ * cached prefix plus the block itself.  Every canvas position sees every
+ * other ([GN] "핵심 트레이드오프"; [WE0] "양방향 어텐션과 자기 수정의 역할") and
+ * the prefix from the KV cache ([GUIDE] "Block Autoregressive Diffusion"); the
+ * prompt never sees the canvas ([TR] "DiffusionGemma의 구성", block-diagonal
+ * mask).  Scores q.k / sqrt(dh); query head h reads KV head h / (Hq / Hkv);
+ * RoPE (pairs j, j + dh/2, angle pos * theta^(-2j/dh)) at absolute positions
+ * P_b + i rotates q and k_new.  Mode CANVAS: query i sees keys [0, P_b + Lq);
+ * mode CAUSAL: keys [0, P_b + i].  The rotated k_new and v_new are written to
+ * cache slots [P_b, P_b + Lq); prefix_len is NOT advanced.
+ *   q        [B, Lq, Hq, dh]      k_new, v_new [B, Lq, Hkv, dh] (k un-rotated)
+ *   k_cache, v_cache [B, Hkv, Tmax, dh], slots [0, P_b) hold rotated keys
+ *   prefix_len [B] int32 device; requires P_b + Lq <= Tmax (not checked on the
+ *   device: the caller guarantees it)
+ *   out      [B, Lq, Hq, dh]
+ *   dtype    DG_BF16 (MFMA path, fp32 accumulation) or DG_F32
+ *   dh in {16, 64, 128} for DG_F32 and dh == 128 for DG_BF16; Hq % Hkv == 0.
+ */
+size_t dg_attention_workspace_size(int B, int Lq, int Hq, int Hkv, int dh, int Tmax, int dtype);
+dg_status dg_canvas_attention(const void* q, const void* k_new, const void* v_new,
+                              void* k_cache, void* v_cache, const int32_t* prefix_len,
+                              int B, int Lq, int Hq, int Hkv, int dh, int Tmax,
+                              int mask_mode, float rope_theta, int dtype, void* out,
+                              void* ws, size_t ws_bytes, void* stream);
+
+/* dg_commit_block: commit a finished block to the KV cache ([TR]
+ * "DiffusionGemma의 구성", flowchart; [GUIDE] "Block Autoregressive Diffusion";
+ * [WE0] "DiffusionGemma가 다르게 하는 점").  Rotates k_new at positions
+ * P_b + i, writes k and v_new to cache slots [P_b, P_b + L), then
+ * prefix_len[b] += L.  Same layouts and dtypes as dg_canvas_attention.  The
+ * caller guarantees P_b + L <= Tmax. */
+dg_status dg_commit_block(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                          int32_t* prefix_len, int B, int L, int Hkv, int dh, int Tmax,
+                          float rope_theta, int dtype, void* stream);
+
+/* ---------------------------------------------------------------------- MoE
+ * dg_moe_route: top-k routing of T tokens over E experts ([WE0] "26B MoE 설계가
+ * 의미하는 것": only selected experts run).  Order: logit descending, ties to
+ * the lower expert id; gates = softmax of the k selected logits;
+ * expert_offsets = exclusive prefix sum of per-expert counts; sorted_rows = the
+ * slot entries t * k + j ordered stably by expert.
+ *   router_logits [T, E] f32; topk_ids [T, k] i32; gates [T, k] f32;
+ *   expert_offsets [E + 1] i32; sorted_rows [T * k] i32.
+ *   E <= 256, k <= min(E, 16), T * k < 2^31.  ws >= dg_moe_route_workspace_size.
+ */
+size_t dg_moe_route_workspace_size(int T, int E, int k);
+dg_status dg_moe_route(const float* router_logits, int T, int E, int k, int32_t* topk_ids,
+                       float* gates, int32_t* expert_offsets, int32_t* sorted_rows,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/* dg_moe_ffn: y[t] += sum_j gates[t, j] * FFN_{topk_ids[t, j]}(x[t]) with
+ * FFN_e(u) = (GELU_erf(u Wg_e^T) * (u Wu_e^T)) Wd_e^T, summed in slot order.
+ *   x          [T, D] DG_BF16 (with DG_BF16 / DG_FP8_E4M3 weights) or DG_F32
+ *              (with DG_F32 weights)
+ *   w_gate_up  [E, 2I, D]: rows 0..I-1 gate, I..2I-1 up;  w_down [E, D, I]
+ *   s_gate_up  [E, 2I], s_down [E, D] f32 per-row scales (DG_FP8_E4M3 only;
+ *              the weight is byte value * scale); ignored otherwise
+ *   routing tables as produced by dg_moe_route; y [T, D] f32, accumulated.
+ *   D % 64 == 0 and I % 64 == 0 for the MFMA paths.
+ * ws >= dg_moe_ffn_workspace_size(T, D, I, E, k, x_dtype). */
+size_t dg_moe_ffn_workspace_size(int T, int D, int I, int E, int k, int x_dtype);
+dg_status dg_moe_ffn(const void* x, int x_dtype, const void* w_gate_up, const void* w_down,
+                     int w_dtype, const float* s_gate_up, const float* s_down,
+                     const int32_t* topk_ids, const float* gates, const int32_t* expert_offsets,
+                     const int32_t* sorted_rows, int T, int D, int I, int E, int k, float* y,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* ----------------------------------------------------------- whole decoder
+ * A random-init decoder of n_layers pre-norm layers: RMSNorm (eps 1e-6, unit
+ * gain) -> fused QKV -> canvas attention -> O projection + residual -> RMSNorm
+ * -> router -> top-k MoE + residual; final RMSNorm -> untied LM head.  Dense
+ * weights and activations use act_dtype (DG_BF16 or DG_F32); experts use
+ * expert_dtype (DG_BF16, DG_FP8_E4M3, or DG_F32 with DG_F32 activations).
+ * The residual stream is f32.  Weight layouts: emb, lm_head [V, D]; wqkv
+ * [(Hq + 2 Hkv) dh, D] (rows q | k | v); wo [D, Hq dh]; wr [E, D]; experts as
+ * in dg_moe_ffn.  KV caches: per layer [B, Hkv, Tmax, dh] in act_dtype.
+ */
+typedef struct {
+  int32_t n_layers, d_model, n_heads, n_kv_heads, head_dim;
+  int32_t n_experts, top_k, d_ff, vocab;
+  float rope_theta;
+  int32_t act_dtype;
+  int32_t expert_dtype;
+} dg_model_dims;
+
+typedef struct {
+  const void* emb;
+  const void* lm_head;
+  const void* const* wqkv;        /* host array [n_layers] of device pointers */
+  const void* const* wo;
+  const void* const* wr;
+  const void* const* w_gate_up;
+  const void* const* w_down;
+  const float* const* s_gate_up;  /* NULL entries allowed unless fp8 */
+  const float* const* s_down;
+} dg_model_weights;
+
+typedef struct dg_ctx dg_ctx;
+
+/* Workspace for a context serving up to max_batch rows of max_tokens tokens
+ * per forward (the canvas length, also the prefill chunk). */
+size_t dg_ctx_workspace_size(const dg_model_dims* dims, int max_batch, int max_tokens);
+/* Creates a context holding the dims, copies of the weight pointers (not the
+ * weights) and the workspace pointer; the caller keeps every buffer alive. */
+dg_status dg_ctx_create(dg_ctx** out, const dg_model_dims* dims, const dg_model_weights* w,
+                        int max_batch, int max_tokens, void* ws, size_t ws_bytes);
+dg_status dg_ctx_destroy(dg_ctx* ctx);
+/* use_graphs != 0 (default): dg_denoise_block replays a captured hipGraph. */
+dg_status dg_ctx_set_graphs(dg_ctx* ctx, int use_graphs);
+
+/* dg_model_forward: one forward over n tokens per row at cache positions
+ * [P_b, P_b + n).  If tokens != NULL the residual x is first set to the
+ * embeddings; layers [layer_begin, layer_end) are applied to x [B * n, D] f32
+ * in place (each writes its rotated K/V to its cache at [P_b, P_b + n)); if
+ * logits != NULL (requires layer_end == n_layers) the final RMSNorm + LM head
+ * writes logits [B, n, V] in act_dtype.  prefix_len is not advanced. */
+dg_status dg_model_forward(dg_ctx* ctx, const int32_t* tokens, float* x, int B, int n,
+                           int layer_begin, int layer_end, void* const* k_caches,
+                           void* const* v_caches, int Tmax, const int32_t* prefix_len,
+                           int mask_mode, void* logits, void* stream);
+
+/* dg_prefill: encode a prompt into the KV cache ([TR] "DiffusionGemma의 구성",
+ * flowchart: prompt -> KV cache) with a causal mask, in chunks of at most
+ * max_tokens, starting at prefix_len[b] and advancing it by n. */
+dg_status dg_prefill(dg_ctx* ctx, const int32_t* prompt, int B, int n, void* const* k_caches,
+                     void* const* v_caches, int Tmax, int32_t* prefix_len, void* stream);
+
+/* dg_denoise_block: one whole block ([TR] "DiffusionGemma의 구성", flowchart;
+ * [GUIDE] "Block Autoregressive Diffusion"): init canvas; per step a forward
+ * over the canvas (canvas mask), the LM head and dg_sampler_step, until every
+ * row is done (adaptive) or fixed_steps; then one more forward of the final
+ * tokens commits every layer's K/V to slots [P_b, P_b + L) and prefix_len += L.
+ *   tokens_out [B, L] i32; steps_taken [B] i32 (steps each row ran).
+ *   requires B <= max_batch, L <= max_tokens, P_b + L <= Tmax. */
+dg_status dg_denoise_block(dg_ctx* ctx, const dg_sampler_cfg* cfg, int B, void* const* k_caches,
+                           void* const* v_caches, int Tmax, int32_t* prefix_len,
+                           int32_t* tokens_out, int32_t* steps_taken, void* stream);
+
+/* ------------------------------------------------------------- utilities
+ * Seeded synthetic data and checks used by tests and the benchmark. */
+
+/* dst[i] = std * N(0,1) from Philox4x32-10 (counter (i / 4, 0, stream_id,
+ * 0xFF000000), Box-Muller) in DG_F32 or DG_BF16. */
+dg_status dg_fill_normal(void* dst, int dtype, size_t n, float std, uint64_t seed,
+                         uint32_t stream_id, void* stream);
+/* Per-row e4m3fn quantization of src [rows, cols] f32: scale = max|row| / 448,
+ * q = round-to-nearest-even(src / scale) saturated to +-448. */
+dg_status dg_quantize_fp8_rows(const float* src, uint8_t* q, float* scale, int64_t rows,
+                               int cols, void* stream);
+/* Philox4x32-10 words for n counters: out[4i..4i+3] = Philox(ctr[4i..4i+3], seed). */
+dg_status dg_philox(const uint32_t* counters, int64_t n, uint64_t seed, uint32_t* out,
+                    void* stream);
+/* The device Gumbel draw the sampler uses for each 32-bit word. */
+dg_status dg_gumbel(const uint32_t* words, int64_t n, float* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DG_H_ */

@@ -48,3 +48,25 @@ def rel_err_rows(got, ref):
     num = np.linalg.norm(got - ref, axis=1)
     den = np.maximum(np.linalg.norm(ref, axis=1), 1e-30)
     return float((num / den).max())
+
+
+# ------------------------------------------------------------ sampler rules
+
+TAU_BAND = 1e-6          # |maxprob - threshold| below this: decision excluded
+STOP_BAND = 1e-6         # |mean entropy - stop threshold| below this: row excluded
+
+
+def gumbel_band(top_score):
+    """Top-2 perturbed-score gap below which the Gumbel-max id is excluded:
+    1e-6 * max(1, |score|) (float32 scores on the device vs float64 here)."""
+    return 1e-6 * np.maximum(1.0, np.abs(top_score))
+
+
+def sampler_exclusions(ref, cfg):
+    """Boolean [B, L] mask of positions whose integer outputs are excluded from
+    the bit-exact comparison, and [B] mask of rows whose stop decision is."""
+    mp = ref["maxprob"]
+    near_tau = (np.abs(mp - cfg.commit_prob) < TAU_BAND) | (np.abs(mp - cfg.renoise_prob) < TAU_BAND)
+    near_tie = ref["gap"] < gumbel_band(ref["top_score"])
+    row = np.abs(ref["mean_entropy"] - cfg.stop_entropy) < STOP_BAND
+    return near_tau | near_tie | row[:, None], row
