@@ -1,0 +1,447 @@
+// Decoder context, forward, prefill and the block loop.
+//
+// Block loop (technical-report summary, "DiffusionGemma의 구성", flowchart;
+// developer guide, "Block Autoregressive Diffusion"): canvas of random ids ->
+// repeat {forward over the canvas with the canvas mask; LM head; sampler step}
+// until every row is done -> one more forward of the final tokens writes every
+// layer's K/V into cache slots [P, P + L) -> P += L.
+//
+// On a non-default stream the whole block (init, every step, commit) is
+// captured once into a hipGraph per argument set and replayed; on the default
+// stream it is launched eagerly.  Inside the graph nothing is allocated and no
+// memset node is recorded (zeroing uses a fill kernel).
+#include <map>
+#include <tuple>
+#include <vector>
+
+#include "kernels.h"
+
+namespace dg {
+
+__global__ void fill_i32_kernel(int32_t* p, int n, int v) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+__global__ void copy_i32_kernel(const int32_t* s, int32_t* d, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) d[i] = s[i];
+}
+
+static dg_status fill_i32(int32_t* p, int n, int v, hipStream_t s) {
+  fill_i32_kernel<<<(n + 255) / 256, 256, 0, s>>>(p, n, v);
+  DG_LAUNCH_CHECK();
+  return DG_OK;
+}
+
+}  // namespace dg
+
+using namespace dg;
+
+struct GraphKey {
+  int B, Tmax, L, S, F;
+  float t0, t1, eps, tc, tr;
+  uint64_t seed;
+  std::vector<void*> ptrs;
+  bool operator<(const GraphKey& o) const {
+    return std::tie(B, Tmax, L, S, F, t0, t1, eps, tc, tr, seed, ptrs) <
+           std::tie(o.B, o.Tmax, o.L, o.S, o.F, o.t0, o.t1, o.eps, o.tc, o.tr, o.seed, o.ptrs);
+  }
+};
+
+struct dg_ctx {
+  dg_model_dims d;
+  const void* emb = nullptr;
+  const void* lm = nullptr;
+  std::vector<const void*> wqkv, wo, wr, wgu, wd;
+  std::vector<const float*> sgu, sd;
+  int max_batch = 0, max_tokens = 0;
+  // workspace carve-up
+  float* x = nullptr;
+  void* h = nullptr;
+  void* qkv = nullptr;
+  void* attn_out = nullptr;
+  float* router = nullptr;
+  int32_t* topk_ids = nullptr;
+  float* gates = nullptr;
+  int32_t* offsets = nullptr;
+  int32_t* sorted_rows = nullptr;
+  void* attn_ws = nullptr;
+  void* moe_ws = nullptr;
+  void* logits = nullptr;
+  void* samp_ws = nullptr;
+  int32_t* tokens = nullptr;
+  uint8_t* committed = nullptr;
+  uint8_t* renoised = nullptr;
+  float* maxprob = nullptr;
+  float* entropy = nullptr;
+  float* mean_entropy = nullptr;
+  int32_t* done = nullptr;
+  int32_t* status = nullptr;
+  bool use_graphs = true;
+  std::map<GraphKey, hipGraphExec_t> graphs;
+};
+
+namespace {
+
+struct Layout {
+  size_t x, h, qkv, attn_out, router, topk_ids, gates, offsets, sorted_rows, attn_ws, moe_ws,
+      logits, samp_ws, tokens, committed, renoised, maxprob, entropy, mean_entropy, done, status,
+      total;
+};
+
+size_t esz(int dt) { return dt == DG_F32 ? 4 : 2; }
+
+size_t attn_ws_max(const dg_model_dims& d, int maxB, int maxT) {
+  size_t m = 0;
+  for (int B = 1; B <= maxB; ++B)
+    for (int n = 1; n <= maxT; ++n)
+      m = std::max(m, attention_workspace_bytes(B, n, d.n_heads, d.n_kv_heads, d.head_dim,
+                                                1 << 30, d.act_dtype));
+  return m;
+}
+
+Layout layout(const dg_model_dims& d, int maxB, int maxT) {
+  Layout L{};
+  const size_t T = static_cast<size_t>(maxB) * maxT;
+  const size_t qkv_w = static_cast<size_t>(d.n_heads + 2 * d.n_kv_heads) * d.head_dim;
+  const size_t a = esz(d.act_dtype);
+  size_t off = 0;
+  auto take = [&](size_t bytes) { const size_t o = off; off += align_up(bytes, 256); return o; };
+  L.x = take(T * d.d_model * 4);
+  L.h = take(T * d.d_model * a);
+  L.qkv = take(T * qkv_w * a);
+  L.attn_out = take(T * d.n_heads * d.head_dim * a);
+  L.router = take(T * d.n_experts * 4);
+  L.topk_ids = take(T * d.top_k * 4);
+  L.gates = take(T * d.top_k * 4);
+  L.offsets = take((d.n_experts + 1) * 4);
+  L.sorted_rows = take(T * d.top_k * 4);
+  L.attn_ws = take(attn_ws_max(d, maxB, maxT));
+  L.moe_ws = take(std::max(moe_ffn_workspace_bytes(static_cast<int>(T), d.d_model, d.d_ff,
+                                                   d.n_experts, d.top_k, d.act_dtype),
+                           moe_route_workspace_bytes(static_cast<int>(T), d.n_experts, d.top_k)));
+  L.logits = take(T * d.vocab * a);
+  L.samp_ws = take(sampler_workspace_bytes(maxB, maxT, d.vocab));
+  L.tokens = take(T * 4);
+  L.committed = take(T);
+  L.renoised = take(T);
+  L.maxprob = take(T * 4);
+  L.entropy = take(T * 4);
+  L.mean_entropy = take(maxB * 4);
+  L.done = take(maxB * 4);
+  L.status = take(4);
+  L.total = off;
+  return L;
+}
+
+dg_status check_dims(const dg_model_dims* d) {
+  DG_CHECK_ARG(d != nullptr, "dims is null");
+  DG_CHECK_SHAPE(d->n_layers > 0 && d->d_model > 0 && d->n_heads > 0 && d->n_kv_heads > 0 &&
+                     d->head_dim > 0 && d->n_experts > 0 && d->top_k > 0 && d->d_ff > 0 &&
+                     d->vocab > 0,
+                 "dims must be positive");
+  DG_CHECK_SHAPE(d->n_heads % d->n_kv_heads == 0, "n_heads must be a multiple of n_kv_heads");
+  DG_CHECK_SHAPE(d->n_experts <= 256 && d->top_k <= d->n_experts && d->top_k <= 16,
+                 "need n_experts <= 256 and top_k <= min(n_experts, 16)");
+  DG_CHECK_SHAPE(d->vocab % 8 == 0, "vocab must be a multiple of 8");
+  DG_CHECK_ARG(d->rope_theta > 1.f, "rope_theta must be > 1");
+  if (d->act_dtype == DG_BF16) {
+    DG_CHECK_ARG(d->expert_dtype == DG_BF16 || d->expert_dtype == DG_FP8_E4M3,
+                 "bf16 activations need bf16 or fp8 experts");
+    DG_CHECK_SHAPE(d->head_dim == 128, "the bf16 path needs head_dim 128");
+    const int qkv_n = (d->n_heads + 2 * d->n_kv_heads) * d->head_dim;
+    DG_CHECK_SHAPE(d->d_model % 128 == 0 && qkv_n % 128 == 0 && d->n_experts % 128 == 0 &&
+                       d->vocab % 128 == 0 && (d->n_heads * d->head_dim) % 64 == 0 &&
+                       d->d_ff % 64 == 0,
+                   "the bf16 path needs d_model, QKV width, n_experts, vocab % 128 == 0 "
+                   "and attention width, d_ff % 64 == 0");
+  } else {
+    DG_CHECK_ARG(d->act_dtype == DG_F32 && d->expert_dtype == DG_F32,
+                 "act_dtype must be DG_BF16 or DG_F32 (f32 needs f32 experts)");
+    DG_CHECK_SHAPE(d->head_dim % 2 == 0 && d->head_dim <= 128, "f32 head_dim must be even, <= 128");
+    DG_CHECK_SHAPE(d->d_model % 4 == 0, "d_model must be a multiple of 4");
+  }
+  return DG_OK;
+}
+
+// One decoder layer over T = B * n tokens (residual ctx->x).
+dg_status layer(dg_ctx* c, int l, int B, int n, void* kc, void* vc, int Tmax,
+                const int32_t* prefix_len, int mode, bool kv_only, hipStream_t s) {
+  const dg_model_dims& d = c->d;
+  const int T = B * n;
+  const int qd = d.n_heads * d.head_dim, kd = d.n_kv_heads * d.head_dim;
+  const int qkv_w = qd + 2 * kd;
+  const size_t a = esz(d.act_dtype);
+  dg_status st;
+  if ((st = launch_rmsnorm(c->x, c->h, T, d.d_model, d.act_dtype, s))) return st;
+  if ((st = launch_gemm(c->h, c->wqkv[l], c->qkv, T, qkv_w, d.d_model, d.act_dtype, d.act_dtype,
+                        kStore, s)))
+    return st;
+  char* qkv = static_cast<char*>(c->qkv);
+  if (kv_only)
+    return launch_commit(qkv + qd * a, qkv + (qd + kd) * a, qkv_w, kc, vc,
+                         const_cast<int32_t*>(prefix_len), B, n, d.n_kv_heads, d.head_dim, Tmax,
+                         d.rope_theta, d.act_dtype, false, s);
+  AttnArgs aa{qkv, qkv + qd * a, qkv + (qd + kd) * a, qkv_w, qkv_w, kc, vc, prefix_len, B, n,
+              d.n_heads, d.n_kv_heads, d.head_dim, Tmax, mode, d.rope_theta, d.act_dtype,
+              c->attn_out};
+  if ((st = launch_attention(aa, c->attn_ws, s))) return st;
+  if ((st = launch_gemm(c->attn_out, c->wo[l], c->x, T, d.d_model, qd, d.act_dtype, DG_F32,
+                        kAccumulateF32, s)))
+    return st;
+  if ((st = launch_rmsnorm(c->x, c->h, T, d.d_model, d.act_dtype, s))) return st;
+  if ((st = launch_gemm(c->h, c->wr[l], c->router, T, d.n_experts, d.d_model, d.act_dtype, DG_F32,
+                        kStore, s)))
+    return st;
+  if ((st = launch_moe_route(c->router, T, d.n_experts, d.top_k, c->topk_ids, c->gates,
+                             c->offsets, c->sorted_rows, c->moe_ws, s)))
+    return st;
+  return launch_moe_ffn(c->h, d.act_dtype, c->wgu[l], c->wd[l], d.expert_dtype, c->sgu[l],
+                        c->sd[l], c->topk_ids, c->gates, c->offsets, c->sorted_rows, T, d.d_model,
+                        d.d_ff, d.n_experts, d.top_k, c->x, c->moe_ws, s);
+}
+
+dg_status forward(dg_ctx* c, const int32_t* tokens, int B, int n, int l0, int l1,
+                  void* const* kcs, void* const* vcs, int Tmax, const int32_t* prefix_len,
+                  int mode, void* logits, bool commit_only, hipStream_t s) {
+  const dg_model_dims& d = c->d;
+  dg_status st;
+  if (tokens && (st = launch_embed(tokens, c->emb, c->x, B * n, d.d_model, d.act_dtype, s)))
+    return st;
+  for (int l = l0; l < l1; ++l) {
+    const bool kv_only = commit_only && l == d.n_layers - 1;
+    if ((st = layer(c, l, B, n, kcs[l], vcs[l], Tmax, prefix_len, mode, kv_only, s))) return st;
+  }
+  if (logits) {
+    if ((st = launch_rmsnorm(c->x, c->h, B * n, d.d_model, d.act_dtype, s))) return st;
+    if ((st = launch_gemm(c->h, c->lm, logits, B * n, d.vocab, d.d_model, d.act_dtype,
+                          d.act_dtype, kStore, s)))
+      return st;
+  }
+  return DG_OK;
+}
+
+dg_status enqueue_block(dg_ctx* c, const dg_sampler_cfg& cfg, int B, void* const* kcs,
+                        void* const* vcs, int Tmax, int32_t* prefix_len, int32_t* tokens_out,
+                        int32_t* steps_taken, hipStream_t s) {
+  const dg_model_dims& d = c->d;
+  const int L = cfg.canvas_len;
+  const int n_steps = cfg.fixed_steps > 0 ? cfg.fixed_steps : cfg.max_steps;
+  dg_status st;
+  if ((st = launch_init_canvas(prefix_len, B, L, d.vocab, cfg.seed, c->tokens, c->committed,
+                               c->done, s)))
+    return st;
+  if ((st = fill_i32(steps_taken, B, 0, s))) return st;
+  if ((st = fill_i32(c->status, 1, 0, s))) return st;
+  for (int step = 0; step < n_steps; ++step) {
+    if ((st = forward(c, c->tokens, B, L, 0, d.n_layers, kcs, vcs, Tmax, prefix_len,
+                      DG_MASK_CANVAS, c->logits, false, s)))
+      return st;
+    if ((st = launch_sampler(c->logits, d.act_dtype, B, L, d.vocab, step, cfg, prefix_len,
+                             c->tokens, c->committed, c->renoised, c->maxprob, c->entropy,
+                             c->mean_entropy, c->done, c->status, steps_taken, c->samp_ws, s)))
+      return st;
+  }
+  // commit: the final tokens' K/V of every layer into slots [P, P + L)
+  if ((st = forward(c, c->tokens, B, L, 0, d.n_layers, kcs, vcs, Tmax, prefix_len,
+                    DG_MASK_CANVAS, nullptr, true, s)))
+    return st;
+  if ((st = launch_advance_prefix(prefix_len, B, L, s))) return st;
+  copy_i32_kernel<<<(B * L + 255) / 256, 256, 0, s>>>(c->tokens, tokens_out, B * L);
+  DG_LAUNCH_CHECK();
+  return DG_OK;
+}
+
+dg_status check_run(dg_ctx* c, int B, int n, void* const* kcs, void* const* vcs, int Tmax,
+                    const int32_t* prefix_len, const char* fn) {
+  DG_CHECK_ARG(c != nullptr, std::string(fn) + ": ctx is null");
+  DG_CHECK_ARG(kcs && vcs && prefix_len, std::string(fn) + ": null pointer");
+  for (int l = 0; l < c->d.n_layers; ++l)
+    DG_CHECK_ARG(kcs[l] && vcs[l], std::string(fn) + ": null cache pointer");
+  DG_CHECK_SHAPE(B > 0 && B <= c->max_batch, std::string(fn) + ": B outside [1, max_batch]");
+  DG_CHECK_SHAPE(n > 0 && n <= c->max_tokens, std::string(fn) + ": n outside [1, max_tokens]");
+  DG_CHECK_SHAPE(Tmax >= n, std::string(fn) + ": Tmax smaller than the block");
+  return DG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t dg_ctx_workspace_size(const dg_model_dims* dims, int max_batch, int max_tokens) {
+  if (!dims || max_batch <= 0 || max_tokens <= 0 || check_dims(dims) != DG_OK) return 0;
+  return layout(*dims, max_batch, max_tokens).total;
+}
+
+dg_status dg_ctx_create(dg_ctx** out, const dg_model_dims* dims, const dg_model_weights* w,
+                        int max_batch, int max_tokens, void* ws, size_t ws_bytes) {
+  set_error("");
+  DG_CHECK_ARG(out && w, "dg_ctx_create: null pointer");
+  dg_status st = check_dims(dims);
+  if (st != DG_OK) return st;
+  DG_CHECK_SHAPE(max_batch > 0 && max_batch < (1 << 24) && max_tokens > 0 && max_tokens <= 4096,
+                 "dg_ctx_create: bad max_batch / max_tokens");
+  const int nl = dims->n_layers;
+  DG_CHECK_ARG(w->emb && w->lm_head && w->wqkv && w->wo && w->wr && w->w_gate_up && w->w_down,
+               "dg_ctx_create: null weight pointer");
+  for (int l = 0; l < nl; ++l) {
+    DG_CHECK_ARG(w->wqkv[l] && w->wo[l] && w->wr[l] && w->w_gate_up[l] && w->w_down[l],
+                 "dg_ctx_create: null per-layer weight pointer");
+    if (dims->expert_dtype == DG_FP8_E4M3)
+      DG_CHECK_ARG(w->s_gate_up && w->s_down && w->s_gate_up[l] && w->s_down[l],
+                   "dg_ctx_create: fp8 experts need scales");
+  }
+  const Layout L = layout(*dims, max_batch, max_tokens);
+  if (!ws || ws_bytes < L.total) return fail(DG_ERR_WORKSPACE, "dg_ctx_create: workspace too small");
+  dg_ctx* c = new dg_ctx();
+  c->d = *dims;
+  c->emb = w->emb;
+  c->lm = w->lm_head;
+  for (int l = 0; l < nl; ++l) {
+    c->wqkv.push_back(w->wqkv[l]);
+    c->wo.push_back(w->wo[l]);
+    c->wr.push_back(w->wr[l]);
+    c->wgu.push_back(w->w_gate_up[l]);
+    c->wd.push_back(w->w_down[l]);
+    c->sgu.push_back(w->s_gate_up ? w->s_gate_up[l] : nullptr);
+    c->sd.push_back(w->s_down ? w->s_down[l] : nullptr);
+  }
+  c->max_batch = max_batch;
+  c->max_tokens = max_tokens;
+  char* b = static_cast<char*>(ws);
+  c->x = reinterpret_cast<float*>(b + L.x);
+  c->h = b + L.h;
+  c->qkv = b + L.qkv;
+  c->attn_out = b + L.attn_out;
+  c->router = reinterpret_cast<float*>(b + L.router);
+  c->topk_ids = reinterpret_cast<int32_t*>(b + L.topk_ids);
+  c->gates = reinterpret_cast<float*>(b + L.gates);
+  c->offsets = reinterpret_cast<int32_t*>(b + L.offsets);
+  c->sorted_rows = reinterpret_cast<int32_t*>(b + L.sorted_rows);
+  c->attn_ws = b + L.attn_ws;
+  c->moe_ws = b + L.moe_ws;
+  c->logits = b + L.logits;
+  c->samp_ws = b + L.samp_ws;
+  c->tokens = reinterpret_cast<int32_t*>(b + L.tokens);
+  c->committed = reinterpret_cast<uint8_t*>(b + L.committed);
+  c->renoised = reinterpret_cast<uint8_t*>(b + L.renoised);
+  c->maxprob = reinterpret_cast<float*>(b + L.maxprob);
+  c->entropy = reinterpret_cast<float*>(b + L.entropy);
+  c->mean_entropy = reinterpret_cast<float*>(b + L.mean_entropy);
+  c->done = reinterpret_cast<int32_t*>(b + L.done);
+  c->status = reinterpret_cast<int32_t*>(b + L.status);
+  *out = c;
+  return DG_OK;
+}
+
+dg_status dg_ctx_destroy(dg_ctx* ctx) {
+  if (!ctx) return DG_OK;
+  for (auto& kv : ctx->graphs) (void)hipGraphExecDestroy(kv.second);
+  delete ctx;
+  return DG_OK;
+}
+
+dg_status dg_ctx_set_graphs(dg_ctx* ctx, int use_graphs) {
+  DG_CHECK_ARG(ctx != nullptr, "dg_ctx_set_graphs: ctx is null");
+  ctx->use_graphs = use_graphs != 0;
+  return DG_OK;
+}
+
+dg_status dg_model_forward(dg_ctx* ctx, const int32_t* tokens, float* x, int B, int n,
+                           int layer_begin, int layer_end, void* const* k_caches,
+                           void* const* v_caches, int Tmax, const int32_t* prefix_len,
+                           int mask_mode, void* logits, void* stream) {
+  set_error("");
+  dg_status st = check_run(ctx, B, n, k_caches, v_caches, Tmax, prefix_len, "dg_model_forward");
+  if (st != DG_OK) return st;
+  DG_CHECK_ARG(x != nullptr, "dg_model_forward: x is null");
+  DG_CHECK_ARG(mask_mode == DG_MASK_CANVAS || mask_mode == DG_MASK_CAUSAL,
+               "dg_model_forward: bad mask_mode");
+  DG_CHECK_SHAPE(0 <= layer_begin && layer_begin <= layer_end && layer_end <= ctx->d.n_layers,
+                 "dg_model_forward: bad layer range");
+  DG_CHECK_SHAPE(!logits || layer_end == ctx->d.n_layers,
+                 "dg_model_forward: logits need layer_end == n_layers");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t bytes = static_cast<size_t>(B) * n * ctx->d.d_model * 4;
+  // the residual lives in the context workspace; x is the caller's view of it
+  if (!tokens) DG_HIP(hipMemcpyAsync(ctx->x, x, bytes, hipMemcpyDeviceToDevice, s));
+  if ((st = forward(ctx, tokens, B, n, layer_begin, layer_end, k_caches, v_caches, Tmax,
+                    prefix_len, mask_mode, logits, false, s)))
+    return st;
+  DG_HIP(hipMemcpyAsync(x, ctx->x, bytes, hipMemcpyDeviceToDevice, s));
+  return DG_OK;
+}
+
+dg_status dg_prefill(dg_ctx* ctx, const int32_t* prompt, int B, int n, void* const* k_caches,
+                     void* const* v_caches, int Tmax, int32_t* prefix_len, void* stream) {
+  set_error("");
+  DG_CHECK_ARG(ctx && prompt, "dg_prefill: null pointer");
+  DG_CHECK_SHAPE(n > 0 && n <= Tmax, "dg_prefill: n outside [1, Tmax]");
+  const int chunk = ctx->max_tokens;
+  dg_status st = check_run(ctx, B, std::min(n, chunk), k_caches, v_caches, Tmax, prefix_len,
+                           "dg_prefill");
+  if (st != DG_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // the chunk's token ids, contiguous per row, staged in the canvas buffer
+  for (int c0 = 0; c0 < n; c0 += chunk) {
+    const int m = std::min(chunk, n - c0);
+    DG_HIP(hipMemcpy2DAsync(ctx->tokens, m * sizeof(int32_t), prompt + c0, n * sizeof(int32_t),
+                            m * sizeof(int32_t), B, hipMemcpyDeviceToDevice, s));
+    if ((st = forward(ctx, ctx->tokens, B, m, 0, ctx->d.n_layers, k_caches, v_caches, Tmax,
+                      prefix_len, DG_MASK_CAUSAL, nullptr, true, s)))
+      return st;
+    if ((st = launch_advance_prefix(prefix_len, B, m, s))) return st;
+  }
+  return DG_OK;
+}
+
+dg_status dg_denoise_block(dg_ctx* ctx, const dg_sampler_cfg* cfg, int B, void* const* k_caches,
+                           void* const* v_caches, int Tmax, int32_t* prefix_len,
+                           int32_t* tokens_out, int32_t* steps_taken, void* stream) {
+  set_error("");
+  DG_CHECK_ARG(ctx && cfg && tokens_out && steps_taken, "dg_denoise_block: null pointer");
+  DG_CHECK_SHAPE(cfg->max_steps >= 1 && cfg->fixed_steps >= 0 && cfg->fixed_steps <= cfg->max_steps,
+                 "dg_denoise_block: bad step settings");
+  DG_CHECK_ARG(cfg->temp_start > 0.f && cfg->temp_end > 0.f, "dg_denoise_block: bad temperatures");
+  dg_status st = check_run(ctx, B, cfg->canvas_len, k_caches, v_caches, Tmax, prefix_len,
+                           "dg_denoise_block");
+  if (st != DG_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!ctx->use_graphs || s == nullptr)
+    return enqueue_block(ctx, *cfg, B, k_caches, v_caches, Tmax, prefix_len, tokens_out,
+                         steps_taken, s);
+  GraphKey key{B, Tmax, cfg->canvas_len, cfg->max_steps, cfg->fixed_steps, cfg->temp_start,
+               cfg->temp_end, cfg->stop_entropy, cfg->commit_prob, cfg->renoise_prob, cfg->seed,
+               {}};
+  for (int l = 0; l < ctx->d.n_layers; ++l) {
+    key.ptrs.push_back(k_caches[l]);
+    key.ptrs.push_back(v_caches[l]);
+  }
+  key.ptrs.push_back(prefix_len);
+  key.ptrs.push_back(tokens_out);
+  key.ptrs.push_back(steps_taken);
+  auto it = ctx->graphs.find(key);
+  if (it == ctx->graphs.end()) {
+    DG_HIP(hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal));
+    st = enqueue_block(ctx, *cfg, B, k_caches, v_caches, Tmax, prefix_len, tokens_out,
+                       steps_taken, s);
+    hipGraph_t g = nullptr;
+    hipError_t e = hipStreamEndCapture(s, &g);
+    if (st != DG_OK) {
+      if (g) (void)hipGraphDestroy(g);
+      return st;
+    }
+    if (e != hipSuccess)
+      return fail(DG_ERR_HIP, std::string("hipStreamEndCapture: ") + hipGetErrorString(e));
+    hipGraphExec_t exec = nullptr;
+    e = hipGraphInstantiate(&exec, g, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(g);
+    if (e != hipSuccess)
+      return fail(DG_ERR_HIP, std::string("hipGraphInstantiate: ") + hipGetErrorString(e));
+    it = ctx->graphs.emplace(key, exec).first;
+  }
+  DG_HIP(hipGraphLaunch(it->second, s));
+  return DG_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,266 @@
+// Sparse MoE feed-forward: top-k router, expert-sorted grouped GEMMs, combine.
+//
+// What is computed: only the experts selected for a token run on it (test.we0
+// article, "26B MoE 설계가 의미하는 것"); the router takes the top-k logits
+// (ties to the lower expert id) and the gates are the softmax of the selected
+// logits; each expert is a gated FFN (GELU(u Wg^T) * (u Wu^T)) Wd^T; the token
+// output is the gate-weighted sum of its k slots in slot order.
+//
+// Kernels:
+//   route_topk_kernel   one wave per token: k rounds of a wave-wide
+//                       (logit desc, id asc) max; gates in float.
+//   route_sort_kernel   one 1024-thread workgroup: histogram, exclusive scan
+//                       -> expert_offsets, stable scatter of the slot entries
+//                       t * k + j by expert (ballot-based ranks, deterministic).
+//   gemm_stream_kernel  (gemm_mfma.h) gate/up + GELU*up -> h [T*k, I] bf16 in
+//                       sorted order; down + gate -> y_slot [T*k, D] f32.
+//   combine_kernel      y[t] += sum_j y_slot[t*k + j] in slot order.
+//   f32 path            plain SIMT kernels over the same tables (parity path).
+#include "common.h"
+#include "gemm_mfma.h"
+#include "kernels.h"
+
+namespace dg {
+
+// ------------------------------------------------------------------ router
+__global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits, int T,
+                                                         int E, int k, int32_t* __restrict__ ids,
+                                                         float* __restrict__ gates) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (t >= T) return;
+  constexpr int PER = 4;                 // E <= 256
+  float v[PER];
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    const int e = q * 64 + lane;
+    v[q] = e < E ? logits[static_cast<int64_t>(t) * E + e] : -INFINITY;
+  }
+  bool taken[PER] = {false, false, false, false};
+  float sel[16];
+  int sel_id[16];
+  for (int j = 0; j < k; ++j) {
+    float best = -INFINITY;
+    int bid = 0x7fffffff;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int e = q * 64 + lane;
+      if (e < E && !taken[q] && (v[q] > best || (v[q] == best && e < bid))) { best = v[q]; bid = e; }
+    }
+    for (int o = 32; o > 0; o >>= 1) {
+      const float ob = __shfl_xor(best, o);
+      const int oi = __shfl_xor(bid, o);
+      if (ob > best || (ob == best && oi < bid)) { best = ob; bid = oi; }
+    }
+#pragma unroll
+    for (int q = 0; q < PER; ++q)
+      if (q * 64 + lane == bid) taken[q] = true;
+    sel[j] = best;
+    sel_id[j] = bid;
+  }
+  if (lane == 0) {
+    const float m = sel[0];
+    float z = 0.f;
+    for (int j = 0; j < k; ++j) z += expf(sel[j] - m);
+    for (int j = 0; j < k; ++j) {
+      ids[static_cast<int64_t>(t) * k + j] = sel_id[j];
+      gates[static_cast<int64_t>(t) * k + j] = expf(sel[j] - m) / z;
+    }
+  }
+}
+
+__global__ __launch_bounds__(1024) void route_sort_kernel(const int32_t* __restrict__ ids, int n,
+                                                          int E, int32_t* __restrict__ offsets,
+                                                          int32_t* __restrict__ sorted_rows) {
+  __shared__ int s_count[256];
+  __shared__ int s_base[256];            // running start of each expert
+  __shared__ int s_wave[16][256];        // per-wave counts in the current chunk
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid < 256) s_count[tid] = 0;
+  __syncthreads();
+  for (int i = tid; i < n; i += 1024) atomicAdd(&s_count[ids[i]], 1);
+  __syncthreads();
+  if (tid == 0) {
+    int acc = 0;
+    for (int e = 0; e < E; ++e) { s_base[e] = acc; offsets[e] = acc; acc += s_count[e]; }
+    offsets[E] = acc;
+  }
+  __syncthreads();
+  for (int c0 = 0; c0 < n; c0 += 1024) {
+    const int i = c0 + tid;
+    const int e = i < n ? ids[i] : -1;
+    // lanes of this wave with the same expert
+    uint64_t same = __ballot(i < n);
+#pragma unroll
+    for (int bit = 0; bit < 8; ++bit) {
+      const uint64_t bal = __ballot(e >= 0 && ((e >> bit) & 1));
+      same &= ((e >> bit) & 1) ? bal : ~bal;
+    }
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const int rank_in_wave = __popcll(same & below);
+    for (int q = tid; q < 16 * 256; q += 1024) (&s_wave[0][0])[q] = 0;
+    __syncthreads();
+    if (e >= 0 && rank_in_wave == 0) s_wave[wave][e] = __popcll(same);
+    __syncthreads();
+    if (e >= 0) {
+      int before = 0;
+      for (int w = 0; w < wave; ++w) before += s_wave[w][e];
+      sorted_rows[s_base[e] + before + rank_in_wave] = i;
+    }
+    __syncthreads();
+    if (tid < E) {
+      int tot = 0;
+      for (int w = 0; w < 16; ++w) tot += s_wave[w][tid];
+      s_base[tid] += tot;
+    }
+    __syncthreads();
+  }
+}
+
+size_t moe_route_workspace_bytes(int, int, int) { return 0; }
+
+dg_status launch_moe_route(const float* logits, int T, int E, int k, int32_t* topk_ids,
+                           float* gates, int32_t* offsets, int32_t* sorted_rows, void*,
+                           hipStream_t stream) {
+  route_topk_kernel<<<(T + 3) / 4, 256, 0, stream>>>(logits, T, E, k, topk_ids, gates);
+  DG_LAUNCH_CHECK();
+  route_sort_kernel<<<1, 1024, 0, stream>>>(topk_ids, T * k, E, offsets, sorted_rows);
+  DG_LAUNCH_CHECK();
+  return DG_OK;
+}
+
+// ------------------------------------------------------------- combine
+__global__ void combine_kernel(const float* __restrict__ y_slot, int T, int D, int k,
+                               float* __restrict__ y) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;   // float4 index
+  const int64_t n4 = static_cast<int64_t>(T) * D / 4;
+  if (idx >= n4) return;
+  const int64_t t = idx / (D / 4), d4 = idx % (D / 4);
+  float4 acc = reinterpret_cast<float4*>(y)[idx];
+  for (int j = 0; j < k; ++j) {
+    const float4 v = reinterpret_cast<const float4*>(y_slot + (t * k + j) * D)[d4];
+    acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+  }
+  reinterpret_cast<float4*>(y)[idx] = acc;
+}
+
+// ------------------------------------------------------------- f32 path
+__global__ void gateup_f32_kernel(const float* __restrict__ x, const float* __restrict__ wgu,
+                                  const int32_t* __restrict__ offsets,
+                                  const int32_t* __restrict__ sorted_rows, int n_slots, int E,
+                                  int D, int I, int k, float* __restrict__ h) {
+  const int p = blockIdx.x;               // sorted position
+  if (p >= n_slots) return;
+  int e = 0;
+  while (e < E - 1 && offsets[e + 1] <= p) ++e;
+  const int t = sorted_rows[p] / k;
+  const float* xr = x + static_cast<int64_t>(t) * D;
+  for (int n = threadIdx.x; n < I; n += blockDim.x) {
+    const float* wg = wgu + (static_cast<int64_t>(e) * 2 * I + n) * D;
+    const float* wu = wgu + (static_cast<int64_t>(e) * 2 * I + I + n) * D;
+    float g = 0.f, u = 0.f;
+    for (int d = 0; d < D; ++d) { g = fmaf(xr[d], wg[d], g); u = fmaf(xr[d], wu[d], u); }
+    h[static_cast<int64_t>(p) * I + n] = gelu_erf(g) * u;
+  }
+}
+
+__global__ void down_f32_kernel(const float* __restrict__ h, const float* __restrict__ wd,
+                                const int32_t* __restrict__ offsets,
+                                const int32_t* __restrict__ sorted_rows,
+                                const float* __restrict__ gates, int n_slots, int E, int D, int I,
+                                float* __restrict__ y_slot) {
+  const int p = blockIdx.x;
+  if (p >= n_slots) return;
+  int e = 0;
+  while (e < E - 1 && offsets[e + 1] <= p) ++e;
+  const int s = sorted_rows[p];
+  const float g = gates[s];
+  const float* hr = h + static_cast<int64_t>(p) * I;
+  for (int d = threadIdx.x; d < D; d += blockDim.x) {
+    const float* w = wd + (static_cast<int64_t>(e) * D + d) * I;
+    float acc = 0.f;
+    for (int i = 0; i < I; ++i) acc = fmaf(hr[i], w[i], acc);
+    y_slot[static_cast<int64_t>(s) * D + d] = g * acc;
+  }
+}
+
+// ------------------------------------------------------------- launchers
+constexpr int kMoeTB = 4;      // 64 tokens per tile
+constexpr int kMoeKS = 4;      // 256 k per LDS stage
+
+size_t moe_ffn_workspace_bytes(int T, int D, int I, int E, int k, int x_dtype) {
+  const size_t slots = static_cast<size_t>(T) * k;
+  const size_t esz = x_dtype == DG_F32 ? 4 : 2;
+  return align_up(slots * I * esz, 256) + align_up(slots * D * 4, 256);
+}
+
+template <bool FP8>
+static dg_status launch_grouped(const void* x, const void* wgu, const void* wd, const float* sgu,
+                                const float* sd, const float* gates, const int32_t* offsets,
+                                const int32_t* sorted_rows, int T, int D, int I, int E, int k,
+                                bf16_t* h, float* y_slot, hipStream_t stream) {
+  constexpr int MT = 16 * kMoeTB;
+  const int max_ty = E + (T * k + MT - 1) / MT;
+  GemmArgs g{};
+  g.W = wgu; g.w_group_stride = static_cast<int64_t>(2) * I * D;
+  g.w_scale = FP8 ? sgu : nullptr; g.s_group_stride = 2 * I;
+  g.X = static_cast<const bf16_t*>(x);
+  g.N = 2 * I; g.K = D; g.n_groups = E; g.topk = k;
+  g.offsets = offsets; g.sorted_rows = sorted_rows; g.gates = gates;
+  g.out = h;
+  g.n_tiles_x = I / 64;
+  g.n_tiles_total = g.n_tiles_x * max_ty;
+  gemm_stream_kernel<2, kMoeTB, kMoeKS, FP8, kGateUp>
+      <<<(g.n_tiles_total + 7) / 8 * 8, 256, 0, stream>>>(g);
+  DG_LAUNCH_CHECK();
+  GemmArgs d{};
+  d.W = wd; d.w_group_stride = static_cast<int64_t>(D) * I;
+  d.w_scale = FP8 ? sd : nullptr; d.s_group_stride = D;
+  d.X = h;
+  d.N = D; d.K = I; d.n_groups = E; d.topk = k;
+  d.offsets = offsets; d.sorted_rows = sorted_rows; d.gates = gates;
+  d.out = y_slot;
+  d.n_tiles_x = D / 128;
+  d.n_tiles_total = d.n_tiles_x * max_ty;
+  gemm_stream_kernel<2, kMoeTB, kMoeKS, FP8, kDown>
+      <<<(d.n_tiles_total + 7) / 8 * 8, 256, 0, stream>>>(d);
+  DG_LAUNCH_CHECK();
+  return DG_OK;
+}
+
+dg_status launch_moe_ffn(const void* x, int x_dtype, const void* w_gate_up, const void* w_down,
+                         int w_dtype, const float* s_gate_up, const float* s_down,
+                         const int32_t* topk_ids, const float* gates, const int32_t* offsets,
+                         const int32_t* sorted_rows, int T, int D, int I, int E, int k, float* y,
+                         void* ws, hipStream_t stream) {
+  const size_t slots = static_cast<size_t>(T) * k;
+  char* w = static_cast<char*>(ws);
+  const size_t esz = x_dtype == DG_F32 ? 4 : 2;
+  void* h = w;
+  float* y_slot = reinterpret_cast<float*>(w + align_up(slots * I * esz, 256));
+  dg_status st = DG_OK;
+  if (x_dtype == DG_F32) {
+    gateup_f32_kernel<<<T * k, 128, 0, stream>>>(static_cast<const float*>(x),
+                                                 static_cast<const float*>(w_gate_up), offsets,
+                                                 sorted_rows, T * k, E, D, I, k,
+                                                 static_cast<float*>(h));
+    DG_LAUNCH_CHECK();
+    down_f32_kernel<<<T * k, 128, 0, stream>>>(static_cast<const float*>(h),
+                                               static_cast<const float*>(w_down), offsets,
+                                               sorted_rows, gates, T * k, E, D, I, y_slot);
+    DG_LAUNCH_CHECK();
+  } else if (w_dtype == DG_FP8_E4M3) {
+    st = launch_grouped<true>(x, w_gate_up, w_down, s_gate_up, s_down, gates, offsets,
+                              sorted_rows, T, D, I, E, k, static_cast<bf16_t*>(h), y_slot, stream);
+  } else {
+    st = launch_grouped<false>(x, w_gate_up, w_down, nullptr, nullptr, gates, offsets,
+                               sorted_rows, T, D, I, E, k, static_cast<bf16_t*>(h), y_slot, stream);
+  }
+  if (st != DG_OK) return st;
+  const int64_t n4 = static_cast<int64_t>(T) * D / 4;
+  combine_kernel<<<static_cast<unsigned>((n4 + 255) / 256), 256, 0, stream>>>(y_slot, T, D, k, y);
+  DG_LAUNCH_CHECK();
+  return DG_OK;
+}
+
+}  // namespace dg

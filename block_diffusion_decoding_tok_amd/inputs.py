@@ -25,6 +25,7 @@ vocabulary of 2^18, 30-layer MoE decoder with 128 experts, top-8):
                   random id on 60% of positions (154 of 256).
 """
 
+import os
 from dataclasses import dataclass
 
 import numpy as np
@@ -157,12 +158,28 @@ def router_logits_skewed(T, E, k, seed, hot_frac=0.1, share=0.40):
     return x, hot, beta
 
 
-def _normal_f32(rng, shape, std, chunk=1 << 26):
-    out = np.empty(int(np.prod(shape)), np.float32)
-    for i in range(0, out.size, chunk):
-        n = min(chunk, out.size - i)
-        out[i:i + n] = rng.standard_normal(n, dtype=np.float32)
-    out *= np.float32(std)
+def _normal_f32(rng, shape, std, chunk=1 << 24):
+    """std * N(0, 1) float32 array.  Chunks of 2^24 values each take their own
+    child generator (seeded from ``rng``), so the result does not depend on
+    how many threads fill it."""
+    n = int(np.prod(shape))
+    out = np.empty(n, np.float32)
+    nchunks = (n + chunk - 1) // chunk
+    seeds = rng.integers(0, 2**63, size=nchunks, dtype=np.int64)
+
+    def fill(c):
+        g = np.random.Generator(np.random.PCG64(int(seeds[c])))
+        lo = c * chunk
+        hi = min(n, lo + chunk)
+        out[lo:hi] = g.standard_normal(hi - lo, dtype=np.float32)
+        out[lo:hi] *= np.float32(std)
+
+    if nchunks == 1:
+        fill(0)
+    else:
+        import concurrent.futures as cf
+        with cf.ThreadPoolExecutor(min(16, os.cpu_count() or 4)) as ex:
+            list(ex.map(fill, range(nchunks)))
     return out.reshape(shape)
 
 

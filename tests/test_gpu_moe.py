@@ -1,0 +1,104 @@
+"""GPU parity of the MoE router and expert FFN against the oracle, through
+the C ABI: bit-exact routing tables on identical logits; FFN outputs within
+2e-2 (bf16 weights), 5e-2 (fp8 weights) and 1e-5 (f32) relative per token."""
+
+import numpy as np
+import pytest
+import torch
+
+from block_diffusion_decoding_tok_amd import dg
+from block_diffusion_decoding_tok_amd.inputs import moe_case
+from oracle.moe import moe_route, moe_ffn
+from tests.util import ExpertWeights, rel_err_rows, to_f64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+TOL = {"bf16": 2e-2, "fp8": 5e-2, "f32": 1e-5}
+
+
+def _route_gpu(logits, k):
+    ids, gates, off, rows = dg.dg_moe_route(logits.to(DEV), k)
+    torch.cuda.synchronize()
+    return ids.cpu().numpy(), gates.cpu().numpy(), off.cpu().numpy(), rows.cpu().numpy()
+
+
+def _check_route(logits, k):
+    ids, gates, off, rows = _route_gpu(logits, k)
+    r_ids, r_gates, r_off, r_rows = moe_route(logits.double().numpy(), k)
+    assert np.array_equal(ids, r_ids)
+    assert np.array_equal(off, r_off)
+    assert np.array_equal(rows, r_rows)
+    assert np.allclose(gates, r_gates, rtol=2e-6, atol=1e-7)
+    return ids, gates, off, rows
+
+
+@pytest.mark.parametrize("T,E,k", [(256, 128, 8), (1024, 128, 8), (37, 5, 2), (300, 256, 16),
+                                   (64, 1, 1), (10, 200, 3)])
+def test_route_matches_oracle(T, E, k):
+    rng = np.random.default_rng(T + E + k)
+    logits = torch.from_numpy(rng.standard_normal((T, E)).astype(np.float32))
+    logits[0, :] = 0.25                     # a fully tied row: lowest ids win
+    _check_route(logits, k)
+
+
+def test_route_planted_skew_share():
+    case = moe_case(T=256, w_dtype="bf16", seed=0, D=128, I=64, E=128)
+    ids, _, off, _ = _check_route(case.router_logits, 8)
+    share = np.isin(ids, case.hot).mean()
+    assert abs(share - 0.40) <= 0.005
+    assert (np.diff(off) > 0).all()          # every expert receives tokens
+
+
+def _ffn_case(case, k, sample=None):
+    T, D = case.x.shape
+    ids, gates, off, rows = _check_route(case.router_logits, k)
+    y0 = torch.randn(T, D, generator=torch.Generator().manual_seed(1)) * 0.1
+    y = y0.clone().to(DEV)
+    xd = case.x.to(DEV)
+    wgu, wd = case.w_gate_up.to(DEV), case.w_down.to(DEV)
+    sgu, sd = case.s_gate_up.to(DEV), case.s_down.to(DEV)
+    dg.dg_moe_ffn(xd, wgu, wd, sgu, sd, torch.from_numpy(ids).to(DEV),
+                  torch.from_numpy(gates).to(DEV), torch.from_numpy(off).to(DEV),
+                  torch.from_numpy(rows).to(DEV), y)
+    torch.cuda.synchronize()
+    got = (y.cpu() - y0).double().numpy()
+    sel = np.arange(T) if sample is None else sample
+    wg = ExpertWeights(case.w_gate_up, case.s_gate_up)
+    wdn = ExpertWeights(case.w_down, case.s_down)
+    ref = moe_ffn(to_f64(case.x)[sel], wg, wdn, ids[sel], gates[sel].astype(np.float64))
+    return rel_err_rows(got[sel], ref), y
+
+
+@pytest.mark.parametrize("w_dtype", ["bf16", "fp8"])
+def test_moe_ffn_full_size_bs1(w_dtype):
+    case = moe_case(T=256, w_dtype=w_dtype, seed=0)
+    err, _ = _ffn_case(case, 8)
+    assert err < TOL[w_dtype], err
+
+
+def test_moe_ffn_full_size_bs4_fp8_sampled():
+    case = moe_case(T=1024, w_dtype="fp8", seed=1)
+    sample = np.random.default_rng(0).choice(1024, 96, replace=False)
+    err, _ = _ffn_case(case, 8, sample)
+    assert err < TOL["fp8"], err
+
+
+@pytest.mark.parametrize("w_dtype", ["bf16", "fp8"])
+def test_moe_ffn_ragged_small(w_dtype):
+    """Few tokens, experts with 0 and > 64 tokens, several row tiles."""
+    case = moe_case(T=70, D=256, E=6, k=2, I=128, w_dtype=w_dtype, seed=5, skew=False)
+    err, _ = _ffn_case(case, 2)
+    assert err < TOL[w_dtype], err
+
+
+def test_moe_ffn_f32_tiny():
+    case = moe_case(T=48, D=64, E=4, k=2, I=128, w_dtype="f32", seed=2, skew=False)
+    err, _ = _ffn_case(case, 2)
+    assert err < TOL["f32"], err
+
+
+def test_moe_ffn_deterministic():
+    case = moe_case(T=256, D=512, E=16, k=4, I=128, w_dtype="fp8", seed=3)
+    _, y1 = _ffn_case(case, 4, sample=np.arange(4))
+    _, y2 = _ffn_case(case, 4, sample=np.arange(4))
+    assert torch.equal(y1, y2)

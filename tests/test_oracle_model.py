@@ -63,7 +63,7 @@ def test_tiny_loop_random_weights_renoises_until_the_cap():
 
 
 def test_tiny_loop_planted_commits_and_stops():
-    m, kc, vc, P, _ = _tiny(boost_rows=8, boost=60.0)
+    m, kc, vc, P, _ = _tiny(boost_rows=4, boost=400.0)
     cfg = SamplerCfg(canvas_len=16, max_steps=8, seed=0)
     tokens, steps, trace, _ = denoise_block(m, cfg, kc, vc, P)
     com_prev = np.zeros((1, 16))

@@ -70,3 +70,22 @@ def sampler_exclusions(ref, cfg):
     near_tie = ref["gap"] < gumbel_band(ref["top_score"])
     row = np.abs(ref["mean_entropy"] - cfg.stop_entropy) < STOP_BAND
     return near_tau | near_tie | row[:, None], row
+
+
+class ExpertWeights:
+    """Per-expert float64 view of host expert weights (bf16/f32 values, or
+    e4m3fn bytes times per-row scales), dequantized one expert at a time so
+    the full tensor never exists in float64."""
+
+    def __init__(self, w, s=None):
+        self.w, self.s = w, s
+        self.shape = tuple(w.shape)
+
+    def __getitem__(self, e):
+        if self.w.dtype == torch.uint8:
+            return _FP8_TABLE[self.w[e].numpy()] * self.s[e].to(torch.float64).numpy()[:, None]
+        return to_f64(self.w[e])
+
+
+# value of every e4m3fn byte, from the oracle's decoder
+_FP8_TABLE = fp8_e4m3fn_decode(np.arange(256, dtype=np.uint8))
