@@ -1,0 +1,263 @@
+"""Benchmark of the canvas denoising hot path on one MI355X.
+
+Workload (the end-to-end block-autoregressive decode): a random-init decoder
+of 30 layers (D 2816; 16 query / 8 KV heads of 128; MoE of 128 experts, top-8,
+FFN 704, fp8-e4m3 experts with per-row scales, bf16 dense weights), vocabulary
+2^18, an 8192-token prompt prefilled into the KV cache (untimed), then blocks
+of 256 canvas tokens, each run for a fixed number of denoise steps (default 12;
+the random weights do not converge) and committed to the KV cache.
+
+A "step" is one canvas denoise step: the forward over the canvas (all 30
+layers, canvas attention over the cache, MoE), the LM head and the sampler.
+``--steps K`` steps are timed as K / block_steps consecutive blocks (each one
+hipGraph replay, commit included), bracketed by device synchronization.
+
+Printed: one JSON line with steps/s (value), canvas tok/s, ms per step,
+tok/s at 12 steps per block, the roofline of the dominant op (the MoE FFN),
+and the oracle's throughput on the host cores for a bounded sample.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from block_diffusion_decoding_tok_amd import dg  # noqa: E402
+from block_diffusion_decoding_tok_amd.inputs import FULL_DIMS, ModelDims, prompt_ids  # noqa: E402
+
+METRIC = "canvas denoise steps/s & canvas tok/s (256-tok, bs1); % of MFMA/HBM roofline"
+HBM_PEAK_GBS = 8000.0
+CANVAS = 256
+PROMPT = 8192
+
+
+def make_weights(d, seed=0):
+    """Device weights N(0, 0.02): bf16 dense, fp8 experts (quantized per row
+    from a float32 draw)."""
+    dev = "cuda"
+    w = {}
+
+    def bf16(shape, sid):
+        t = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+        dg.dg_fill_normal(t, 0.02, seed, sid)
+        return t
+
+    w["emb"] = bf16((d.V, d.D), 1)
+    w["lm"] = bf16((d.V, d.D), 2)
+    tmp = torch.empty((d.E, 2 * d.I, d.D), dtype=torch.float32, device=dev)
+    for l in range(d.NL):
+        base = 16 + 16 * l
+        w[f"wqkv.{l}"] = bf16(((d.Hq + 2 * d.Hkv) * d.dh, d.D), base)
+        w[f"wo.{l}"] = bf16((d.D, d.Hq * d.dh), base + 1)
+        w[f"wr.{l}"] = bf16((d.E, d.D), base + 2)
+        for name, shape, sid in (("gu", (d.E, 2 * d.I, d.D), base + 3), ("d", (d.E, d.D, d.I), base + 4)):
+            src = tmp.view(-1)[: int(np.prod(shape))].view(shape)
+            dg.dg_fill_normal(src, 0.02, seed, sid)
+            q = torch.empty(shape, dtype=torch.uint8, device=dev)
+            s = torch.empty(shape[:-1], dtype=torch.float32, device=dev)
+            dg.dg_quantize_fp8_rows(src, q, s)
+            w[f"w{name}.{l}"] = q
+            w[f"s{name}.{l}"] = s
+    torch.cuda.synchronize()
+    del tmp
+    return w
+
+
+def moe_roofline(model_w, d, B, reps=20):
+    """Event-timed dg_moe_ffn (gate/up + down + combine) on layer 0's experts
+    for the canvas tokens; algorithmic bytes = every expert's fp8 weights and
+    scales read once + activations read + h written/read + slot outputs
+    written/read + y read/written."""
+    T = CANVAS * B
+    dev = "cuda"
+    g = torch.Generator(device=dev).manual_seed(5)
+    logits = torch.randn((T, d.E), device=dev, generator=g)
+    x = (torch.randn((T, d.D), device=dev, generator=g)).to(torch.bfloat16)
+    y = torch.zeros((T, d.D), device=dev)
+    ids, gates, off, rows = dg.dg_moe_route(logits, d.k)
+    ws = torch.empty(dg.lib().dg_moe_ffn_workspace_size(T, d.D, d.I, d.E, d.k, dg.DG_BF16),
+                     dtype=torch.uint8, device=dev)
+    args = (x, model_w["wgu.0"], model_w["wd.0"], model_w["sgu.0"], model_w["sd.0"], ids, gates,
+            off, rows, y)
+    for _ in range(3):
+        dg.dg_moe_ffn(*args, ws=ws)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    for i in range(reps):
+        starts[i].record()
+        dg.dg_moe_ffn(*args, ws=ws)
+        ends[i].record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([s.elapsed_time(e) for s, e in zip(starts, ends)]))
+    slots = T * d.k
+    w_bytes = d.E * 3 * d.I * d.D * 1 + d.E * (2 * d.I + d.D) * 4
+    act_bytes = (T * d.D * 2 + slots * d.I * 2 * 2 + slots * d.D * 4 * 2 + T * d.D * 4 * 2)
+    algo = w_bytes + act_bytes
+    gbs = algo / (ms * 1e-3) / 1e9
+    return dict(op="moe_ffn (gate_up + down + combine kernels), layer shapes, "
+                   f"{T} tokens, fp8 experts", ms=ms, algo_bytes=algo, gbs=gbs)
+
+
+def cpu_baseline(d, B, P, seed=0):
+    """The oracle (float64 NumPy) on the host cores for a bounded sample of one
+    denoise step: one decoder layer over the whole canvas of one row, plus the
+    LM head and sampler for 8 of its 256 positions; scaled to one full step
+    (30 layers, 256 positions) of B rows."""
+    from oracle import SamplerCfg, layer_forward, position_stats, sampler_step, rmsnorm
+    from oracle.attention import CANVAS as MASK_CANVAS
+    from block_diffusion_decoding_tok_amd.inputs import model_weights
+    from tests.util import oracle_model
+
+    d1 = ModelDims(NL=1, D=d.D, Hq=d.Hq, Hkv=d.Hkv, dh=d.dh, E=d.E, k=d.k, I=d.I, V=d.V)
+    w = model_weights(d1, seed=seed, expert_dtype="fp8", dense_dtype="bf16")
+    m = oracle_model(d1, w)
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((1, CANVAS, d.D)) * 0.02
+    kc = rng.standard_normal((1, d.Hkv, P + CANVAS, d.dh)) / np.sqrt(d.dh)
+    vc = rng.standard_normal((1, d.Hkv, P + CANVAS, d.dh)) / np.sqrt(d.dh)
+    t0 = time.perf_counter()
+    layer_forward(m, m.layers[0], x, kc, vc, np.array([P]), MASK_CANVAS)
+    t_layer = time.perf_counter() - t0
+    n_pos = 8
+    lm = w["lm"].to(torch.float64).numpy()
+    t0 = time.perf_counter()
+    logits = rmsnorm(x[0, :n_pos]) @ lm.T
+    cfg = SamplerCfg(canvas_len=n_pos)
+    sampler_step(logits[None], 0, cfg, np.array([P]), np.zeros((1, n_pos), np.int64),
+                 np.zeros((1, n_pos), np.int64), np.zeros(1, np.int64))
+    t_head = time.perf_counter() - t0
+    t_step = B * (d.NL * t_layer + t_head * CANVAS / n_pos)
+    cores = len(os.sched_getaffinity(0))
+    omp = os.environ.get("OMP_NUM_THREADS")
+    if omp and omp.isdigit():
+        cores = min(cores, int(omp))
+    return dict(value=1.0 / t_step, unit="steps/s", cores=cores, kind="oracle",
+                sample=(f"1 of {d.NL} layers over the 256-token canvas ({t_layer:.2f} s) + LM head "
+                        f"and sampler on {n_pos} of 256 positions ({t_head:.2f} s), prefix {P}, "
+                        f"scaled to one full step of batch {B}"),
+                measured_s=t_layer + t_head)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=48)
+    ap.add_argument("--warmup", type=int, default=12)
+    ap.add_argument("--batch", type=int, default=1)
+    ap.add_argument("--block-steps", type=int, default=12)
+    ap.add_argument("--layers", type=int, default=FULL_DIMS.NL)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-roofline", action="store_true")
+    ap.add_argument("--steps48", action="store_true",
+                    help="also time 4 blocks at 48 fixed steps each")
+    a = ap.parse_args()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the canvas path would shard by batch rows; see the design notes).",
+              file=sys.stderr)
+        sys.exit(2)
+    if a.steps % a.block_steps or a.warmup % a.block_steps:
+        sys.exit("--steps and --warmup must be multiples of --block-steps")
+    d = ModelDims(NL=a.layers, D=FULL_DIMS.D, Hq=FULL_DIMS.Hq, Hkv=FULL_DIMS.Hkv,
+                  dh=FULL_DIMS.dh, E=FULL_DIMS.E, k=FULL_DIMS.k, I=FULL_DIMS.I, V=FULL_DIMS.V)
+    B = a.batch
+    torch.cuda.set_device(0)
+    n_blocks = a.steps // a.block_steps
+    Tmax = PROMPT + CANVAS * max(n_blocks, 4)
+    t_setup = time.perf_counter()
+    w = make_weights(d)
+    model = dg.DGModel(d, w, B, CANVAS, dg.DG_BF16, dg.DG_FP8_E4M3)
+    kc = [torch.zeros((B, d.Hkv, Tmax, d.dh), dtype=torch.bfloat16, device="cuda") for _ in range(d.NL)]
+    vc = [torch.zeros_like(kc[0]) for _ in range(d.NL)]
+    Pd = torch.zeros(B, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.Stream()
+    tok = torch.empty((B, CANVAS), dtype=torch.int32, device="cuda")
+    steps_taken = torch.empty(B, dtype=torch.int32, device="cuda")
+    with torch.cuda.stream(stream):
+        dg.dg_prefill(model, prompt_ids(B, PROMPT, d.V, seed=0).to("cuda"), kc, vc, Pd)
+        stream.synchronize()
+        assert Pd.cpu().tolist() == [PROMPT] * B
+        cfg = dg.sampler_cfg(CANVAS, 48, a.block_steps, seed=0)
+
+        def run_blocks(nb, c):
+            for _ in range(nb):
+                dg.dg_denoise_block(model, c, B, kc, vc, Pd, tok, steps_taken)
+
+        # warmup (captures the graph), then rewind the prefix
+        run_blocks(max(1, a.warmup // a.block_steps), cfg)
+        stream.synchronize()
+        Pd.fill_(PROMPT)
+        stream.synchronize()
+        print(f"[bench] setup {time.perf_counter() - t_setup:.1f} s; timing {n_blocks} blocks "
+              f"x {a.block_steps} steps, batch {B}", file=sys.stderr, flush=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        run_blocks(n_blocks, cfg)
+        stream.synchronize()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        assert Pd.cpu().tolist() == [PROMPT + CANVAS * n_blocks] * B
+        assert steps_taken.cpu().tolist() == [a.block_steps] * B
+        t48 = None
+        if a.steps48:
+            cfg48 = dg.sampler_cfg(CANVAS, 48, 48, seed=0)
+            Pd.fill_(PROMPT)
+            run_blocks(1, cfg48)
+            stream.synchronize()
+            Pd.fill_(PROMPT)
+            stream.synchronize()
+            t1 = time.perf_counter()
+            run_blocks(4, cfg48)
+            stream.synchronize()
+            t48 = time.perf_counter() - t1
+        roof = None
+        if not a.no_roofline:
+            roof = moe_roofline(w, d, B)
+    steps_per_s = a.steps / elapsed
+    out = {
+        "metric": METRIC,
+        "value": round(steps_per_s, 3),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(1e3 * elapsed / a.steps, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": (f"block-autoregressive canvas decode: {d.NL}-layer MoE decoder "
+                                f"(D 2816, 16/8 heads x 128, 128 experts top-8 FFN 704 fp8-e4m3, "
+                                f"bf16 dense), vocab 262144, prompt {PROMPT} prefilled, "
+                                f"{n_blocks} consecutive 256-token canvases x {a.block_steps} "
+                                f"fixed steps + commit"),
+                   "batch": B, "canvas": CANVAS, "prefix": PROMPT, "layers": d.NL,
+                   "block_steps": a.block_steps, "parallelism": "single GPU"},
+        "canvas_tok_per_s": round(steps_per_s * CANVAS * B, 1),
+        "tok_per_s_at_block_steps": round(n_blocks * CANVAS * B / elapsed, 1),
+    }
+    if t48 is not None:
+        out["tok_per_s_at_48"] = round(4 * CANVAS * B / t48, 1)
+    if roof is not None:
+        out["roofline"] = {"bound": "hbm", "achieved": round(roof["gbs"], 1), "peak": HBM_PEAK_GBS,
+                           "unit": "GB/s", "frac": round(roof["gbs"] / HBM_PEAK_GBS, 4),
+                           "traffic": None, "kernel": roof["op"],
+                           "ms_per_launch": round(roof["ms"], 4),
+                           "algorithmic_bytes": int(roof["algo_bytes"])}
+    if not a.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(d, B, PROMPT)
+        out["cpu_baseline"]["value"] = float(f"{out['cpu_baseline']['value']:.4g}")
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,97 @@
+"""The C ABI without a GPU: libdg.so loads, exports every entry point that
+include/dg.h declares, and rejects invalid calls on the host (before any
+launch) with the documented status codes."""
+
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from block_diffusion_decoding_tok_amd import dg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(dg.LIB_PATH):
+        from block_diffusion_decoding_tok_amd.build import build
+        build()
+    return dg.lib()
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "dg.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dg_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) >= 20
+    missing = [n for n in names if getattr(lib, n, None) is None]
+    assert not missing, missing
+    assert set(names) == set(dg.EXPORTED), set(names) ^ set(dg.EXPORTED)
+    assert not dg.missing_symbols()
+    assert lib.dg_version() >= 100
+
+
+def _last_error(lib):
+    return lib.dg_last_error().decode()
+
+
+def test_sampler_rejects_bad_calls(lib):
+    cfg = dg.sampler_cfg()
+    fake = C.c_void_p(256)        # never dereferenced: validation fails first
+    args = [fake, dg.DG_BF16, 1, 256, 262144, 0, C.byref(cfg)] + [fake] * 9 + [fake, 1 << 30, None]
+    bad = list(args)
+    bad[0] = None
+    assert lib.dg_sampler_step(*bad) == -1 and "null" in _last_error(lib)
+    bad = list(args)
+    bad[1] = 7
+    assert lib.dg_sampler_step(*bad) == -1
+    bad = list(args)
+    bad[4] = 262143                      # V % 8 != 0
+    assert lib.dg_sampler_step(*bad) == -2
+    bad = list(args)
+    bad[5] = 48                          # step == max_steps
+    assert lib.dg_sampler_step(*bad) == -2
+    bad = list(args)
+    bad[-2] = 16                         # workspace too small
+    assert lib.dg_sampler_step(*bad) == -4
+    assert lib.dg_sampler_workspace_size(1, 256, 262144) == 256 * 16 * 32
+
+
+def test_attention_and_moe_reject_bad_shapes(lib):
+    f = C.c_void_p(256)
+    # Hq not a multiple of Hkv
+    assert lib.dg_canvas_attention(f, f, f, f, f, f, 1, 256, 12, 8, 128, 2304, 0, 10000.0,
+                                   dg.DG_BF16, f, f, 1 << 30, None) == -2
+    # bf16 path needs head_dim 128
+    assert lib.dg_canvas_attention(f, f, f, f, f, f, 1, 256, 16, 8, 64, 2304, 0, 10000.0,
+                                   dg.DG_BF16, f, f, 1 << 30, None) == -2
+    # bad mask mode
+    assert lib.dg_canvas_attention(f, f, f, f, f, f, 1, 256, 16, 8, 128, 2304, 5, 10000.0,
+                                   dg.DG_BF16, f, f, 1 << 30, None) == -1
+    # k > E
+    assert lib.dg_moe_route(f, 10, 4, 5, f, f, f, f, f, 0, None) == -2
+    # fp8 without scales
+    assert lib.dg_moe_ffn(f, dg.DG_BF16, f, f, dg.DG_FP8_E4M3, None, None, f, f, f, f,
+                          256, 2816, 704, 128, 8, f, f, 1 << 30, None) == -1
+    # MFMA path shape constraint
+    assert lib.dg_moe_ffn(f, dg.DG_BF16, f, f, dg.DG_BF16, None, None, f, f, f, f,
+                          256, 2800, 704, 128, 8, f, f, 1 << 30, None) == -2
+
+
+def test_ctx_validation(lib):
+    dims = dg.dg_model_dims(30, 2816, 16, 8, 128, 128, 8, 704, 262144, 10000.0,
+                            dg.DG_BF16, dg.DG_FP8_E4M3)
+    n = lib.dg_ctx_workspace_size(C.byref(dims), 1, 256)
+    assert n > 256 * 262144 * 2           # holds at least the logits
+    bad = dg.dg_model_dims(30, 2816, 16, 8, 64, 128, 8, 704, 262144, 10000.0,
+                           dg.DG_BF16, dg.DG_FP8_E4M3)
+    assert lib.dg_ctx_workspace_size(C.byref(bad), 1, 256) == 0
+    w = dg.dg_model_weights()
+    h = C.c_void_p()
+    assert lib.dg_ctx_create(C.byref(h), C.byref(dims), C.byref(w), 1, 256, None, 0) == -1

@@ -30,8 +30,8 @@ def oracle_model(dims, weights, layers=None):
         m.layers.append(dict(
             wqkv=to_f64(weights[f"wqkv.{l}"]), wo=to_f64(weights[f"wo.{l}"]),
             wr=to_f64(weights[f"wr.{l}"]),
-            w_gate_up=expert_f64(weights[f"wgu.{l}"], weights[f"sgu.{l}"]),
-            w_down=expert_f64(weights[f"wd.{l}"], weights[f"sd.{l}"])))
+            w_gate_up=ExpertWeights(weights[f"wgu.{l}"], weights[f"sgu.{l}"]),
+            w_down=ExpertWeights(weights[f"wd.{l}"], weights[f"sd.{l}"])))
     return m
 
 
