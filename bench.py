@@ -71,10 +71,9 @@ def make_weights(d, seed=0):
 
 
 def moe_roofline(model_w, d, B, reps=20):
-    """Event-timed dg_moe_ffn (gate/up + down + combine) on layer 0's experts
-    for the canvas tokens; algorithmic bytes = every expert's fp8 weights and
-    scales read once + activations read + h written/read + slot outputs
-    written/read + y read/written."""
+    """HIP-event-timed dg_moe_ffn (gate/up + down + combine) on layer 0's
+    experts for the canvas tokens; algorithmic bytes = every expert's fp8
+    weights and scales read once + the activations it must move."""
     T = CANVAS * B
     dev = "cuda"
     g = torch.Generator(device=dev).manual_seed(5)
@@ -89,21 +88,42 @@ def moe_roofline(model_w, d, B, reps=20):
     for _ in range(3):
         dg.dg_moe_ffn(*args, ws=ws)
     torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
-    for i in range(reps):
-        starts[i].record()
-        dg.dg_moe_ffn(*args, ws=ws)
-        ends[i].record()
+    # the calls are captured into one graph and replayed between a pair of
+    # HIP events on the replay stream: host launch cost is not counted
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(reps):
+            dg.dg_moe_ffn(*args, ws=ws)
+    graph.replay()
     torch.cuda.synchronize()
-    ms = float(np.mean([s.elapsed_time(e) for s, e in zip(starts, ends)]))
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    graph.replay()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / reps
     slots = T * d.k
     w_bytes = d.E * 3 * d.I * d.D * 1 + d.E * (2 * d.I + d.D) * 4
-    act_bytes = (T * d.D * 2 + slots * d.I * 2 * 2 + slots * d.D * 4 * 2 + T * d.D * 4 * 2)
+    # x read, h written + read (bf16), gate-weighted slot outputs written +
+    # read (bf16), y read + written (f32)
+    act_bytes = (T * d.D * 2 + slots * d.I * 2 * 2 + slots * d.D * 2 * 2 + T * d.D * 4 * 2)
     algo = w_bytes + act_bytes
     gbs = algo / (ms * 1e-3) / 1e9
     return dict(op="moe_ffn (gate_up + down + combine kernels), layer shapes, "
                    f"{T} tokens, fp8 experts", ms=ms, algo_bytes=algo, gbs=gbs)
+
+
+def copy_calibration(nbytes=1 << 28):
+    """One plain device copy of a known size, so FETCH_SIZE / WRITE_SIZE
+    counters taken over this run can be scaled to bytes (the copy reads and
+    writes exactly ``nbytes``)."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    return nbytes
 
 
 def cpu_baseline(d, B, P, seed=0):
@@ -156,13 +176,15 @@ def main():
     ap.add_argument("--layers", type=int, default=FULL_DIMS.NL)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-roofline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run one 256 MiB device copy (scale for byte counters)")
     ap.add_argument("--steps48", action="store_true",
                     help="also time 4 blocks at 48 fixed steps each")
     a = ap.parse_args()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the canvas path would shard by batch rows; see the design notes).",
-              file=sys.stderr)
+        print("bench.py measures one GPU only: there is no multi-GPU path (the canvas "
+              "path would shard by batch rows, one model replica per GPU, with no "
+              "collective on the step).", file=sys.stderr)
         sys.exit(2)
     if a.steps % a.block_steps or a.warmup % a.block_steps:
         sys.exit("--steps and --warmup must be multiples of --block-steps")
@@ -218,6 +240,8 @@ def main():
             run_blocks(4, cfg48)
             stream.synchronize()
             t48 = time.perf_counter() - t1
+        if a.copy_calibration:
+            copy_calibration()
         roof = None
         if not a.no_roofline:
             roof = moe_roofline(w, d, B)

@@ -9,7 +9,8 @@
 // positions, rotated keys in the cache.
 //
 // Launch sequence:
-//   1. rope_kernel: per token, rotates the block's q (into a packed workspace
+//   1. rope_kernel: per token (heads spread over the workgroup's threads),
+//      rotates the block's q (into a packed workspace
 //      [B, Hkv, Lq * G, dh], packed row r = token * G + (head % G)) and k
 //      (into cache slots [P, P + Lq)), copies v into the cache.
 //   2. bf16: attn_mfma_kernel, grid (row tiles of 128, KV splits, B * Hkv);
@@ -29,24 +30,27 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 
 // ---------------------------------------------------------------- RoPE / KV
 template <typename T>
-__global__ void rope_kernel(const T* __restrict__ q, const T* __restrict__ k_new,
-                            const T* __restrict__ v_new, int64_t q_stride, int64_t kv_stride,
-                            T* __restrict__ q_out, T* __restrict__ k_cache,
-                            T* __restrict__ v_cache, const int32_t* __restrict__ prefix_len,
-                            int Lq, int Hq, int Hkv, int dh, int Tmax, float theta) {
+__global__ __launch_bounds__(256) void rope_kernel(
+    const T* __restrict__ q, const T* __restrict__ k_new, const T* __restrict__ v_new,
+    int64_t q_stride, int64_t kv_stride, T* __restrict__ q_out, T* __restrict__ k_cache,
+    T* __restrict__ v_cache, const int32_t* __restrict__ prefix_len, int Lq, int Hq, int Hkv,
+    int dh, int Tmax, float theta) {
+  // one workgroup per token; thread (pair j, head lane hl) handles heads
+  // hl, hl + lanes, ... of the query heads and then of the KV heads
   const int tok = blockIdx.x;          // b * Lq + i
   const int b = tok / Lq, i = tok % Lq;
   const int half = dh / 2;
-  const int j = threadIdx.x;           // pair index
-  if (j >= half) return;
-  const int P = prefix_len[b];
-  const int pos = P + i;
+  const int j = threadIdx.x % half;
+  const int hl = threadIdx.x / half;
+  const int lanes = blockDim.x / half;
+  if (hl >= lanes) return;
+  const int pos = prefix_len[b] + i;
   float c, s;
   rope_cos_sin(pos, j, dh, theta, &c, &s);
   const int G = Hq / Hkv;
   if (q_out) {
     const T* qt = q + static_cast<int64_t>(tok) * q_stride;
-    for (int h = 0; h < Hq; ++h) {
+    for (int h = hl; h < Hq; h += lanes) {
       const float x1 = Elem<T>::load(qt, h * dh + j), x2 = Elem<T>::load(qt, h * dh + j + half);
       const int g = h / G;
       const int64_t r = static_cast<int64_t>(i) * G + (h % G);
@@ -57,7 +61,7 @@ __global__ void rope_kernel(const T* __restrict__ q, const T* __restrict__ k_new
   }
   const T* kt = k_new + static_cast<int64_t>(tok) * kv_stride;
   const T* vt = v_new + static_cast<int64_t>(tok) * kv_stride;
-  for (int g = 0; g < Hkv; ++g) {
+  for (int g = hl; g < Hkv; g += lanes) {
     const float x1 = Elem<T>::load(kt, g * dh + j), x2 = Elem<T>::load(kt, g * dh + j + half);
     const int64_t o = ((static_cast<int64_t>(b) * Hkv + g) * Tmax + pos) * dh;
     Elem<T>::store(k_cache + o, j, x1 * c - x2 * s);
@@ -65,6 +69,11 @@ __global__ void rope_kernel(const T* __restrict__ q, const T* __restrict__ k_new
     v_cache[o + j] = vt[g * dh + j];
     v_cache[o + j + half] = vt[g * dh + j + half];
   }
+}
+
+static int rope_threads(int dh) {
+  const int half = dh / 2;
+  return (256 / half) * half;          // a whole number of head lanes
 }
 
 __global__ void advance_prefix_kernel(int32_t* prefix_len, int B, int L) {
@@ -380,7 +389,7 @@ static AttnPlan plan_attention(int B, int Lq, int Hq, int Hkv, int dh, int Tmax,
   if (dtype == DG_BF16) {
     p.tiles = (rows + kAttnRows - 1) / kAttnRows;
     const int base = p.tiles * B * Hkv;
-    const int target = 512;
+    const int target = 256;
     int ns = (target + base - 1) / base;
     const int max_ns = (Tmax + kAttnKeys - 1) / kAttnKeys;
     ns = max(1, min(ns, max_ns));
@@ -404,7 +413,7 @@ dg_status launch_attention(const AttnArgs& a, void* ws, hipStream_t stream) {
   char* w = static_cast<char*>(ws);
   void* qrot = w;
   if (a.dtype == DG_BF16) {
-    rope_kernel<bf16_t><<<a.B * a.Lq, a.dh / 2, 0, stream>>>(
+    rope_kernel<bf16_t><<<a.B * a.Lq, rope_threads(a.dh), 0, stream>>>(
         static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.k_new),
         static_cast<const bf16_t*>(a.v_new), a.q_stride, a.kv_stride,
         static_cast<bf16_t*>(qrot), static_cast<bf16_t*>(a.k_cache),
@@ -425,7 +434,7 @@ dg_status launch_attention(const AttnArgs& a, void* ws, hipStream_t stream) {
         static_cast<bf16_t*>(a.out));
     DG_LAUNCH_CHECK();
   } else {
-    rope_kernel<float><<<a.B * a.Lq, a.dh / 2, 0, stream>>>(
+    rope_kernel<float><<<a.B * a.Lq, rope_threads(a.dh), 0, stream>>>(
         static_cast<const float*>(a.q), static_cast<const float*>(a.k_new),
         static_cast<const float*>(a.v_new), a.q_stride, a.kv_stride, static_cast<float*>(qrot),
         static_cast<float*>(a.k_cache), static_cast<float*>(a.v_cache), a.prefix_len, a.Lq,
@@ -445,12 +454,12 @@ dg_status launch_commit(const void* k_new, const void* v_new, int64_t kv_stride,
                         void* v_cache, int32_t* prefix_len, int B, int L, int Hkv, int dh,
                         int Tmax, float rope_theta, int dtype, bool advance, hipStream_t stream) {
   if (dtype == DG_BF16)
-    rope_kernel<bf16_t><<<B * L, dh / 2, 0, stream>>>(
+    rope_kernel<bf16_t><<<B * L, rope_threads(dh), 0, stream>>>(
         nullptr, static_cast<const bf16_t*>(k_new), static_cast<const bf16_t*>(v_new), 0,
         kv_stride, nullptr, static_cast<bf16_t*>(k_cache), static_cast<bf16_t*>(v_cache),
         prefix_len, L, Hkv, Hkv, dh, Tmax, rope_theta);
   else
-    rope_kernel<float><<<B * L, dh / 2, 0, stream>>>(
+    rope_kernel<float><<<B * L, rope_threads(dh), 0, stream>>>(
         nullptr, static_cast<const float*>(k_new), static_cast<const float*>(v_new), 0,
         kv_stride, nullptr, static_cast<float*>(k_cache), static_cast<float*>(v_cache),
         prefix_len, L, Hkv, Hkv, dh, Tmax, rope_theta);

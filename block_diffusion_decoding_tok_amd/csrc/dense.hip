@@ -1,8 +1,9 @@
 // Dense projections (QKV, O, router, LM head), RMSNorm and the embedding
 // gather of the decoder layer.
 //
-//   bf16: gemm_stream_kernel (gemm_mfma.h) in dense mode -- weights streamed
-//         once per 128-token tile, tokens staged in LDS.
+//   bf16: gemm_stream_kernel (gemm_mfma.h) in dense mode -- 64 weight rows x
+//         64 tokens per workgroup (16 tokens for narrow outputs), the token
+//         tiles of the same rows adjacent so they share one XCD's L2.
 //   f32:  plain SIMT kernels (parity path of the tiny fp32 model).
 // RMSNorm: x / sqrt(mean(x^2) + 1e-6), unit gain, f32 statistics.
 #include "common.h"
@@ -11,8 +12,15 @@
 
 namespace dg {
 
-constexpr int kDenseTB = 8;    // 128 tokens per tile
-constexpr int kDenseKS = 2;    // 128 k per LDS stage
+// projection-sized outputs (QKV, O, router): split-K register streaming
+constexpr int kSplitNR = 2;
+// other shapes: 64 rows x 64 tokens per workgroup, LDS-staged tokens
+constexpr int kDenseRT = 1, kDenseTB = 4, kDenseKS = 2, kDensePF = 2;
+// up to 256 tokens: register streaming, 16 tokens per tile, ring of 4 chunks
+constexpr int kDenseNR = 4;
+// vocabulary-sized outputs (LM head): 128 rows x 256 tokens, so each weight
+// row is read once per 256 tokens
+constexpr int kWideRT = 2, kWideTB = 16, kWideKS = 1, kWidePF = 2;
 
 __global__ void gemm_f32_kernel(const float* __restrict__ A, const float* __restrict__ W,
                                 float* __restrict__ C, int M, int N, int K, int accumulate) {
@@ -38,17 +46,38 @@ dg_status launch_gemm(const void* A, const void* W, void* C, int M, int N, int K
     DG_LAUNCH_CHECK();
     return DG_OK;
   }
-  constexpr int MT = 16 * kDenseTB;
   GemmArgs g{};
   g.W = W; g.X = static_cast<const bf16_t*>(A);
   g.N = N; g.K = K; g.M = M; g.n_groups = 1;
   g.out = C;
   g.out_dtype = ep == kAccumulateF32 ? DG_F32 : out_dtype;
   g.accumulate = ep == kAccumulateF32;
-  g.n_tiles_x = N / 128;
-  g.n_tiles_total = g.n_tiles_x * ((M + MT - 1) / MT);
-  gemm_stream_kernel<2, kDenseTB, kDenseKS, false, kDense>
-      <<<(g.n_tiles_total + 7) / 8 * 8, 256, 0, stream>>>(g);
+  g.y_fastest = 1;
+  if (N >= 32768) {
+    g.n_tiles_x = N / (64 * kWideRT);
+    g.n_tiles_y = (M + 16 * kWideTB - 1) / (16 * kWideTB);
+    g.n_tiles_total = g.n_tiles_x * g.n_tiles_y;
+    gemm_stream_kernel<kWideRT, kWideTB, kWideKS, kWidePF, false, kDense>
+        <<<(g.n_tiles_total + 7) / 8 * 8, 256, 0, stream>>>(g);
+  } else if (K % 256 == 0 && N % 64 == 0) {
+    // projections: 64 rows x 64 tokens per workgroup, K split over its waves
+    // (16-token tiles when the output is too narrow to fill the chip)
+    const bool narrow = N < 1024;
+    g.n_tiles_x = N / 64;
+    g.n_tiles_y = narrow ? (M + 15) / 16 : (M + 63) / 64;
+    g.n_tiles_total = g.n_tiles_x * g.n_tiles_y;
+    const unsigned grid = (g.n_tiles_total + 7) / 8 * 8;
+    if (narrow)
+      gemm_splitk_kernel<4, 1, kSplitNR><<<grid, 256, 0, stream>>>(g);
+    else
+      gemm_splitk_kernel<4, 4, kSplitNR><<<grid, 256, 0, stream>>>(g);
+  } else {
+    g.n_tiles_x = N / (64 * kDenseRT);
+    g.n_tiles_y = (M + 16 * kDenseTB - 1) / (16 * kDenseTB);
+    g.n_tiles_total = g.n_tiles_x * g.n_tiles_y;
+    gemm_stream_kernel<kDenseRT, kDenseTB, kDenseKS, kDensePF, false, kDense>
+        <<<(g.n_tiles_total + 7) / 8 * 8, 256, 0, stream>>>(g);
+  }
   DG_LAUNCH_CHECK();
   return DG_OK;
 }

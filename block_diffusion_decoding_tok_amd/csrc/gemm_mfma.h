@@ -13,7 +13,8 @@
 // Per 64-k chunk a lane holds 16 consecutive k of its row (16 B of fp8 or
 // 32 B of bf16 starting at 16 * (lane / 16)); the two v_mfma_f32_16x16x32_bf16
 // of the chunk take its first and second 8 values.  The token fragments use
-// the same k order, so the products pair up.  fp8 (OCP e4m3fn) weights are
+// the same k order, so the products pair up.  The weight ring holds PF
+// stages, so weight loads are issued PF stages before their use.  fp8 (OCP e4m3fn) weights are
 // widened to bf16 exactly in registers; their per-row scale is applied in the
 // epilogue, where it factors out of the sum.
 //
@@ -22,7 +23,7 @@
 //            I + n0 + ...; epilogue h = GELU_erf(s_g acc0) * (s_u acc1) -> bf16
 //            h[sorted position, n]; tokens are the slots of one expert.
 //   kDown    A rows = W_down rows; X = h rows in sorted order; epilogue
-//            y_slot[slot, row] = gate[slot] * s * acc (f32).
+//            y_slot[slot, row] = gate[slot] * s * acc (bf16).
 //   kDense   one group; X rows = tokens; epilogue stores (bf16 / f32) or adds
 //            into an f32 output.
 #pragma once
@@ -51,12 +52,14 @@ struct GemmArgs {
   const int32_t* offsets;   // [E + 1] (grouped)
   const int32_t* sorted_rows;
   const float* gates;       // [T * k]
-  void* out;                // gate_up: h bf16 [T*k, I]; down: y_slot f32 [T*k, D];
+  void* out;                // gate_up: h bf16 [T*k, I]; down: y_slot bf16 [T*k, D];
                             // dense: [M, N] in out_dtype
   int out_dtype;            // dense: DG_BF16 / DG_F32
   int accumulate;           // dense: out (f32) += result
   int n_tiles_x;            // row tiles per group
+  int n_tiles_y;            // token-tile slots
   int n_tiles_total;        // logical workgroups (x * y)
+  int y_fastest;            // logical order: token tiles of the same rows adjacent
 };
 
 __device__ __forceinline__ float gelu_erf(float x) {
@@ -104,7 +107,7 @@ __device__ __forceinline__ int xcd_logical_tile(int linear, int total) {
   return (linear % 8) * per + linear / 8;
 }
 
-template <int RT, int TB, int KS, bool FP8, int MODE>
+template <int RT, int TB, int KS, int PF, bool FP8, int MODE>
 __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
   using WT = typename std::conditional<FP8, uint8_t, bf16_t>::type;
   constexpr int MT = 16 * TB;           // tokens per tile
@@ -119,8 +122,9 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
   const int l16 = lane & 15, g4 = lane >> 4;
   const int logical = xcd_logical_tile(blockIdx.x, gridDim.x);
   if (logical >= a.n_tiles_total) return;
-  const int tx = logical % a.n_tiles_x;       // row tile within the group
-  const int ty = logical / a.n_tiles_x;       // token-tile slot
+  // row tile within the group / token-tile slot
+  const int tx = a.y_fastest ? logical / a.n_tiles_y : logical % a.n_tiles_x;
+  const int ty = a.y_fastest ? logical % a.n_tiles_y : logical / a.n_tiles_x;
 
   // ---- which group / token range this tile covers
   int grp = 0, m0 = 0, m_count = 0, base_pos = 0;
@@ -176,34 +180,46 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
   const int nchunks = (a.K + 63) / 64;
   const int nstages = (nchunks + KS - 1) / KS;
 
-  WChunk<FP8> wr[KS][RT];
-  auto load_w = [&](int stage) {
+  // weight ring: PF stages of KS chunks in flight per wave
+  WChunk<FP8> wr[PF][KS][RT];
+  // unconditional loads (clamped chunk; rows are in range by contract) keep
+  // the compiler's memory-counter waits precise
+  auto load_w = [&](int stage, WChunk<FP8> (&slot)[KS][RT]) {
 #pragma unroll
     for (int j = 0; j < KS; ++j) {
-      const int c = stage * KS + j;
+      const int c = min(stage * KS + j, nchunks - 1);
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        if (c < nchunks && wrow[rt] < a.N)
-          wr[j][rt].load(Wg + static_cast<int64_t>(wrow[rt]) * a.K + c * 64 + g4 * 16);
-        else
-          wr[j][rt].zero();
-      }
+      for (int rt = 0; rt < RT; ++rt)
+        slot[j][rt].load(Wg + static_cast<int64_t>(wrow[rt]) * a.K + c * 64 + g4 * 16);
     }
   };
-  auto stage_x = [&](int stage, int buf) {
-    // MT rows x SK k of bf16: 16-byte pieces, SK / 8 per row
-    constexpr int PIECES = MT * SK / 8;
+  // token rows: a stage of MT rows x SK k of bf16 = PIECES 16-byte pieces,
+  // loaded into registers one stage ahead and written to LDS at stage start
+  constexpr int PIECES = MT * SK / 8;
+  constexpr int XP = (PIECES + 255) / 256;
+  uint4 xr[PF][XP];                     // PF stages of token rows in flight
+  // raw loads from clamped addresses; the mask is applied when the stage is
+  // written to LDS (a select right after a load would wait for it at once)
+  auto load_x = [&](int stage, uint4 (&slot)[XP]) {
+    const int k0 = min(stage, nstages - 1) * SK;
+#pragma unroll
+    for (int it = 0; it < XP; ++it) {
+      const int piece = it * 256 + tid;
+      const int r = min(piece / (SK / 8), MT - 1), kk = (piece % (SK / 8)) * 8;
+      const int src = s_rows[r];
+      const int kc = min(k0 + kk, a.K - 8);
+      slot[it] = *reinterpret_cast<const uint4*>(a.X + static_cast<int64_t>(src >= 0 ? src : s_rows[0]) * a.K + kc);
+    }
+  };
+  auto store_x = [&](int stage, int buf, const uint4 (&slot)[XP]) {
     const int k0 = stage * SK;
 #pragma unroll
-    for (int it = 0; it < (PIECES + 255) / 256; ++it) {
+    for (int it = 0; it < XP; ++it) {
       const int piece = it * 256 + tid;
       if (piece < PIECES) {
         const int r = piece / (SK / 8), kk = (piece % (SK / 8)) * 8;
-        const int src = s_rows[r];
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (src >= 0 && k0 + kk < a.K)
-          v = *reinterpret_cast<const uint4*>(a.X + static_cast<int64_t>(src) * a.K + k0 + kk);
-        *reinterpret_cast<uint4*>(&s_x[buf][r * XS + kk]) = v;
+        const bool ok = s_rows[r] >= 0 && k0 + kk < a.K;
+        *reinterpret_cast<uint4*>(&s_x[buf][r * XS + kk]) = ok ? slot[it] : make_uint4(0, 0, 0, 0);
       }
     }
   };
@@ -215,37 +231,42 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
     for (int tb = 0; tb < TB; ++tb) acc[rt][tb] = f32x4_v{0.f, 0.f, 0.f, 0.f};
 
   const int tb_used = (m_count + 15) / 16;
-  load_w(0);
-  for (int s = 0; s < nstages; ++s) {
-    const int buf = s & 1;
-    stage_x(s, buf);
-    __syncthreads();
 #pragma unroll
-    for (int j = 0; j < KS; ++j) {
-      // widen chunk j, then refill its ring slot with chunk j of stage s + 1
-      bf16x8_v wa[RT][2];
+  for (int p = 0; p < PF; ++p) {
+    load_w(p, wr[p]);
+    load_x(p, xr[p]);
+  }
+  for (int s0 = 0; s0 < nstages; s0 += PF) {
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) wr[j][rt].get(wa[rt][0], wa[rt][1]);
-      if (s + 1 < nstages) {
-        const int c = (s + 1) * KS + j;
+    for (int p = 0; p < PF; ++p) {
+      const int s = s0 + p;
+      if (s >= nstages) break;
+      const int buf = s & 1;
+      store_x(s, buf, xr[p]);
+      __syncthreads();
+      load_x(s + PF, xr[p]);
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-          if (c < nchunks && wrow[rt] < a.N)
-            wr[j][rt].load(Wg + static_cast<int64_t>(wrow[rt]) * a.K + c * 64 + g4 * 16);
-          else
-            wr[j][rt].zero();
-        }
-      }
+      for (int j = 0; j < KS; ++j) {
+        // widen chunk j of stage s, then refill its slot with stage s + PF
+        bf16x8_v wa[RT][2];
 #pragma unroll
-      for (int tb = 0; tb < TB; ++tb) {
-        if (tb < tb_used) {
-          const bf16_t* xp = &s_x[buf][(tb * 16 + l16) * XS + j * 64 + g4 * 16];
-          const bf16x8_v x0 = *reinterpret_cast<const bf16x8_v*>(xp);
-          const bf16x8_v x1 = *reinterpret_cast<const bf16x8_v*>(xp + 8);
+        for (int rt = 0; rt < RT; ++rt) wr[p][j][rt].get(wa[rt][0], wa[rt][1]);
+        const int c = min((s + PF) * KS + j, nchunks - 1);
 #pragma unroll
-          for (int rt = 0; rt < RT; ++rt) {
-            acc[rt][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[rt][0], x0, acc[rt][tb], 0, 0, 0);
-            acc[rt][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[rt][1], x1, acc[rt][tb], 0, 0, 0);
+        for (int rt = 0; rt < RT; ++rt)
+          wr[p][j][rt].load(Wg + static_cast<int64_t>(wrow[rt]) * a.K + c * 64 + g4 * 16);
+        if (s * KS + j >= nchunks) continue;
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) {
+          if (tb < tb_used) {
+            const bf16_t* xp = &s_x[buf][(tb * 16 + l16) * XS + j * 64 + g4 * 16];
+            const bf16x8_v x0 = *reinterpret_cast<const bf16x8_v*>(xp);
+            const bf16x8_v x1 = *reinterpret_cast<const bf16x8_v*>(xp + 8);
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+              acc[rt][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[rt][0], x0, acc[rt][tb], 0, 0, 0);
+              acc[rt][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[rt][1], x1, acc[rt][tb], 0, 0, 0);
+            }
           }
         }
       }
@@ -283,8 +304,11 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
         for (int r = 0; r < 4; ++r) v[r] = acc[rt][tb][r] * (sc ? sc[n + r] : 1.f);
         if (MODE == kDown) {
           const float g = a.gates[dst];
-          float* o = static_cast<float*>(a.out) + static_cast<int64_t>(dst) * a.N + n;
-          *reinterpret_cast<float4*>(o) = make_float4(g * v[0], g * v[1], g * v[2], g * v[3]);
+          bf16_t* o = static_cast<bf16_t*>(a.out) + static_cast<int64_t>(dst) * a.N + n;
+          uint2 pk;
+          pk.x = pack_bf16x2(g * v[0], g * v[1]);
+          pk.y = pack_bf16x2(g * v[2], g * v[3]);
+          *reinterpret_cast<uint2*>(o) = pk;
         } else if (a.out_dtype == DG_F32) {
           float* o = static_cast<float*>(a.out) + static_cast<int64_t>(dst) * a.N + n;
           if (a.accumulate) {
@@ -300,6 +324,477 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
           pk.y = pack_bf16x2(v[2], v[3]);
           *reinterpret_cast<uint2*>(o) = pk;
         }
+      }
+    }
+  }
+}
+
+}  // namespace dg
+
+namespace dg {
+
+// Register-streaming variant for tiles of 16 tokens (small per-expert token
+// counts and narrow dense outputs).  No LDS and no barrier in the K loop:
+// every wave streams its own 16 * RT weight rows and its 16 token rows
+// straight into a ring of NR chunks (64 k each) of registers, so NR chunks
+// of both operands are in flight per wave while the MFMAs consume the oldest.
+// Same operand layout, k order, modes and epilogues as gemm_stream_kernel
+// with TB = 1.
+template <int RT, int NR, bool FP8, int MODE>
+__global__ __launch_bounds__(256) void gemm_reg_kernel(GemmArgs a) {
+  using WT = typename std::conditional<FP8, uint8_t, bf16_t>::type;
+  constexpr int MT = 16;
+  __shared__ int s_rows[MT];
+  __shared__ int s_dst[MT];
+  __shared__ int s_scan[256];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const int logical = xcd_logical_tile(blockIdx.x, gridDim.x);
+  if (logical >= a.n_tiles_total) return;
+  const int tx = a.y_fastest ? logical / a.n_tiles_y : logical % a.n_tiles_x;
+  const int ty = a.y_fastest ? logical % a.n_tiles_y : logical / a.n_tiles_x;
+
+  int grp = 0, m0 = 0, m_count = 0, base_pos = 0;
+  if (MODE == kDense) {
+    m0 = ty * MT;
+    if (m0 >= a.M) return;
+    m_count = min(MT, a.M - m0);
+  } else {
+    const int E = a.n_groups;
+    int tiles_e = 0;
+    if (tid < E) tiles_e = (a.offsets[tid + 1] - a.offsets[tid] + MT - 1) / MT;
+    s_scan[tid] = tiles_e;
+    __syncthreads();
+    for (int o = 1; o < 256; o <<= 1) {
+      const int v = (tid >= o) ? s_scan[tid - o] : 0;
+      __syncthreads();
+      s_scan[tid] += v;
+      __syncthreads();
+    }
+    if (ty >= s_scan[E - 1]) return;
+    int lo = 0, hi = E - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (s_scan[mid] > ty) hi = mid; else lo = mid + 1;
+    }
+    grp = lo;
+    const int first_tile = grp ? s_scan[grp - 1] : 0;
+    base_pos = a.offsets[grp];
+    m0 = (ty - first_tile) * MT;
+    m_count = min(MT, a.offsets[grp + 1] - base_pos - m0);
+  }
+  if (tid < MT) {
+    int src = -1, dst = -1;
+    if (tid < m_count) {
+      const int m = m0 + tid;
+      if (MODE == kDense) { src = m; dst = m; }
+      else if (MODE == kGateUp) { const int p = base_pos + m; src = a.sorted_rows[p] / a.topk; dst = p; }
+      else { const int p = base_pos + m; src = p; dst = a.sorted_rows[p]; }
+    }
+    s_rows[tid] = src;
+    s_dst[tid] = dst;
+  }
+  __syncthreads();
+
+  // Every load below is unconditional (clamped addresses, masked after the
+  // fact): conditional loads would make the compiler drain the whole ring
+  // (vmcnt(0)) at each step.  Row counts are multiples of the tile by contract.
+  const WT* Wg = static_cast<const WT*>(a.W) + static_cast<int64_t>(grp) * a.w_group_stride;
+  const WT* wp[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int row = (MODE == kGateUp) ? (rt == 0 ? 0 : a.N / 2) + tx * 64 + wave * 16 + l16
+                                      : tx * (64 * RT) + wave * (16 * RT) + rt * 16 + l16;
+    wp[rt] = Wg + static_cast<int64_t>(row) * a.K + g4 * 16;
+  }
+  const int src = s_rows[l16];
+  const bool xok = src >= 0;
+  const bf16_t* xp = a.X + static_cast<int64_t>(xok ? src : s_rows[0]) * a.K + g4 * 16;
+  const int nchunks = a.K / 64;
+
+  struct Slot {
+    uint4 x0, x1;
+    WChunk<FP8> w[RT];
+  };
+  Slot ring[NR];
+  auto issue = [&](Slot& sl, int c) {
+    const int cc = min(c, nchunks - 1);      // tail slots reload the last chunk, unused
+    sl.x0 = *reinterpret_cast<const uint4*>(xp + cc * 64);
+    sl.x1 = *reinterpret_cast<const uint4*>(xp + cc * 64 + 8);
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) sl.w[rt].load(wp[rt] + cc * 64);
+  };
+  const uint4 zero4 = make_uint4(0, 0, 0, 0);
+
+  f32x4_v acc[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) acc[rt] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+  // the ring's loads must reach the memory counter in slot order, or waiting
+  // for the oldest slot waits for all of them: pin the issue order
+#pragma unroll
+  for (int p = 0; p < NR; ++p) {
+    issue(ring[p], p);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  for (int c0 = 0; c0 < nchunks; c0 += NR) {
+#pragma unroll
+    for (int p = 0; p < NR; ++p) {
+      const Slot cur = ring[p];
+      __builtin_amdgcn_sched_barrier(0);
+      issue(ring[p], c0 + p + NR);
+      __builtin_amdgcn_sched_barrier(0);
+      if (c0 + p < nchunks) {
+        bf16x8_v wa[RT][2];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) cur.w[rt].get(wa[rt][0], wa[rt][1]);
+        const uint4 u0 = xok ? cur.x0 : zero4, u1 = xok ? cur.x1 : zero4;
+        const bf16x8_v x0 = *reinterpret_cast<const bf16x8_v*>(&u0);
+        const bf16x8_v x1 = *reinterpret_cast<const bf16x8_v*>(&u1);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[rt][0], x0, acc[rt], 0, 0, 0);
+          acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[rt][1], x1, acc[rt], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // ---- epilogue (lane: rows 4 g4 + r of each tile, token l16)
+  const int t = l16;
+  if (t >= m_count) return;
+  const int dst = s_dst[t];
+  const float* sc = a.w_scale ? a.w_scale + static_cast<int64_t>(grp) * a.s_group_stride : nullptr;
+  if (MODE == kGateUp) {
+    const int I = a.N / 2;
+    const int n = tx * 64 + wave * 16 + g4 * 4;
+    if (n >= I) return;
+    float hv[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float sg = sc ? sc[n + r] : 1.f, su = sc ? sc[I + n + r] : 1.f;
+      hv[r] = gelu_erf(acc[0][r] * sg) * (acc[1][r] * su);
+    }
+    uint2 pk;
+    pk.x = pack_bf16x2(hv[0], hv[1]);
+    pk.y = pack_bf16x2(hv[2], hv[3]);
+    *reinterpret_cast<uint2*>(static_cast<bf16_t*>(a.out) + static_cast<int64_t>(dst) * I + n) = pk;
+    return;
+  }
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int n = tx * (64 * RT) + wave * (16 * RT) + rt * 16 + g4 * 4;
+    if (n >= a.N) continue;
+    float v[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[r] = acc[rt][r] * (sc ? sc[n + r] : 1.f);
+    if (MODE == kDown) {
+      const float g = a.gates[dst];
+      bf16_t* o = static_cast<bf16_t*>(a.out) + static_cast<int64_t>(dst) * a.N + n;
+      uint2 pk;
+      pk.x = pack_bf16x2(g * v[0], g * v[1]);
+      pk.y = pack_bf16x2(g * v[2], g * v[3]);
+      *reinterpret_cast<uint2*>(o) = pk;
+    } else if (a.out_dtype == DG_F32) {
+      float* o = static_cast<float*>(a.out) + static_cast<int64_t>(dst) * a.N + n;
+      if (a.accumulate) {
+        const float4 c = *reinterpret_cast<float4*>(o);
+        *reinterpret_cast<float4*>(o) = make_float4(c.x + v[0], c.y + v[1], c.z + v[2], c.w + v[3]);
+      } else {
+        *reinterpret_cast<float4*>(o) = make_float4(v[0], v[1], v[2], v[3]);
+      }
+    } else {
+      bf16_t* o = static_cast<bf16_t*>(a.out) + static_cast<int64_t>(dst) * a.N + n;
+      uint2 pk;
+      pk.x = pack_bf16x2(v[0], v[1]);
+      pk.y = pack_bf16x2(v[2], v[3]);
+      *reinterpret_cast<uint2*>(o) = pk;
+    }
+  }
+}
+
+}  // namespace dg
+
+namespace dg {
+
+// One-wave workgroups for the grouped (expert) GEMMs with 16-token tiles.
+// A wave owns RT tiles of 16 weight rows (gate/up: RT/2 gate tiles and the
+// matching RT/2 up tiles, i.e. 8 * RT intermediate columns; down: 16 * RT
+// rows) and its 16 tokens, so each token row is read once per row block and
+// no LDS or barrier is needed.  The tile decode (which expert, which 16
+// tokens) runs in registers with wave shuffles.  The K loop streams a ring of
+// NR chunks of both operands, unconditional loads in a pinned order.
+template <int RT, int NR, bool FP8, int MODE>
+__global__ __launch_bounds__(64) void gemm_wave_kernel(GemmArgs a) {
+  static_assert(MODE == kGateUp || MODE == kDown, "grouped modes only");
+  static_assert(MODE != kGateUp || RT % 2 == 0, "gate/up needs paired tiles");
+  using WT = typename std::conditional<FP8, uint8_t, bf16_t>::type;
+  const int lane = threadIdx.x;
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const int logical = xcd_logical_tile(blockIdx.x, gridDim.x);
+  if (logical >= a.n_tiles_total) return;
+  const int tx = a.y_fastest ? logical / a.n_tiles_y : logical % a.n_tiles_x;
+  const int ty = a.y_fastest ? logical % a.n_tiles_y : logical / a.n_tiles_x;
+
+  // ---- tile decode: inclusive scan of 16-token tiles per expert (E <= 256)
+  const int E = a.n_groups;
+  int cnt[4], incl[4];
+  int carry = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = q * 64 + lane;
+    cnt[q] = e < E ? (a.offsets[e + 1] - a.offsets[e] + 15) / 16 : 0;
+    int v = cnt[q];
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int t = __shfl_up(v, o);
+      if (lane >= o) v += t;
+    }
+    incl[q] = v + carry;
+    carry += __shfl(v, 63);
+  }
+  if (ty >= carry) return;
+  int grp = -1, first_tile = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint64_t m = __ballot(incl[q] > ty);
+    if (grp < 0 && m) {
+      const int src_lane = __ffsll(static_cast<unsigned long long>(m)) - 1;
+      grp = q * 64 + src_lane;
+      first_tile = __shfl(incl[q] - cnt[q], src_lane);
+    }
+  }
+  const int base_pos = a.offsets[grp];
+  const int m0 = (ty - first_tile) * 16;
+  const int m_count = min(16, a.offsets[grp + 1] - base_pos - m0);
+  const int my_m = l16 < m_count ? l16 : 0;
+  const int p_pos = base_pos + m0 + my_m;
+  const int src = (MODE == kGateUp) ? a.sorted_rows[p_pos] / a.topk : p_pos;
+  const bool xok = l16 < m_count;
+
+  const WT* Wg = static_cast<const WT*>(a.W) + static_cast<int64_t>(grp) * a.w_group_stride;
+  const WT* wp[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int row = (MODE == kGateUp)
+                        ? (rt < RT / 2 ? 0 : a.N / 2) + tx * (8 * RT) + (rt % (RT / 2)) * 16 + l16
+                        : tx * (16 * RT) + rt * 16 + l16;
+    wp[rt] = Wg + static_cast<int64_t>(row) * a.K + g4 * 16;
+  }
+  const bf16_t* xp = a.X + static_cast<int64_t>(src) * a.K + g4 * 16;
+  const int nchunks = a.K / 64;
+
+  struct Slot {
+    uint4 x0, x1;
+    WChunk<FP8> w[RT];
+  };
+  Slot ring[NR];
+  auto issue = [&](Slot& sl, int c) {
+    const int cc = min(c, nchunks - 1);
+    sl.x0 = *reinterpret_cast<const uint4*>(xp + cc * 64);
+    sl.x1 = *reinterpret_cast<const uint4*>(xp + cc * 64 + 8);
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) sl.w[rt].load(wp[rt] + cc * 64);
+  };
+  const uint4 zero4 = make_uint4(0, 0, 0, 0);
+  f32x4_v acc[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) acc[rt] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int p = 0; p < NR; ++p) {
+    issue(ring[p], p);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  for (int c0 = 0; c0 < nchunks; c0 += NR) {
+#pragma unroll
+    for (int p = 0; p < NR; ++p) {
+      const Slot cur = ring[p];
+      __builtin_amdgcn_sched_barrier(0);
+      issue(ring[p], c0 + p + NR);
+      __builtin_amdgcn_sched_barrier(0);
+      if (c0 + p < nchunks) {
+        const uint4 u0 = xok ? cur.x0 : zero4, u1 = xok ? cur.x1 : zero4;
+        const bf16x8_v x0 = *reinterpret_cast<const bf16x8_v*>(&u0);
+        const bf16x8_v x1 = *reinterpret_cast<const bf16x8_v*>(&u1);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          bf16x8_v w0, w1;
+          cur.w[rt].get(w0, w1);
+          acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w0, x0, acc[rt], 0, 0, 0);
+          acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w1, x1, acc[rt], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // ---- epilogue (lane: rows 4 g4 + r of each 16-row tile, token l16)
+  if (!xok) return;
+  const float* sc = a.w_scale ? a.w_scale + static_cast<int64_t>(grp) * a.s_group_stride : nullptr;
+  if (MODE == kGateUp) {
+    const int I = a.N / 2;
+#pragma unroll
+    for (int i = 0; i < RT / 2; ++i) {
+      const int n = tx * (8 * RT) + i * 16 + g4 * 4;
+      float hv[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float sg = sc ? sc[n + r] : 1.f, su = sc ? sc[I + n + r] : 1.f;
+        hv[r] = gelu_erf(acc[i][r] * sg) * (acc[RT / 2 + i][r] * su);
+      }
+      uint2 pk;
+      pk.x = pack_bf16x2(hv[0], hv[1]);
+      pk.y = pack_bf16x2(hv[2], hv[3]);
+      *reinterpret_cast<uint2*>(static_cast<bf16_t*>(a.out) + static_cast<int64_t>(p_pos) * I + n) = pk;
+    }
+  } else {
+    const int slot = a.sorted_rows[p_pos];
+    const float g = a.gates[slot];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const int n = tx * (16 * RT) + rt * 16 + g4 * 4;
+      float v[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[r] = g * acc[rt][r] * (sc ? sc[n + r] : 1.f);
+      uint2 pk;
+      pk.x = pack_bf16x2(v[0], v[1]);
+      pk.y = pack_bf16x2(v[2], v[3]);
+      *reinterpret_cast<uint2*>(static_cast<bf16_t*>(a.out) + static_cast<int64_t>(slot) * a.N + n) = pk;
+    }
+  }
+}
+
+}  // namespace dg
+
+namespace dg {
+
+// Dense GEMM for canvas-sized token counts (M <= 1024), bf16 weights:
+// out[m, n] = sum_k X[m, k] W[n, k].  A workgroup owns a tile of 16 * RT
+// weight rows x 16 * TB tokens; its four waves split K into quarters
+// (K % 256 == 0), so a projection with few output tiles still fills the
+// chip, and each wave streams its weight rows and token rows through a
+// register ring of NR chunks (unconditional loads, pinned issue order).  The
+// four partial accumulators are summed through LDS in wave order (fixed
+// order: deterministic), each wave finishing RT / 4 of the row tiles.
+template <int RT, int TB, int NR>
+__global__ __launch_bounds__(256) void gemm_splitk_kernel(GemmArgs a) {
+  static_assert(RT % 4 == 0, "each wave finishes RT / 4 row tiles");
+  __shared__ __attribute__((aligned(16))) float s_acc[4][RT * TB * 4][64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const int logical = xcd_logical_tile(blockIdx.x, gridDim.x);
+  if (logical >= a.n_tiles_total) return;
+  const int tx = logical / a.n_tiles_y;       // row tile (token tiles adjacent)
+  const int ty = logical % a.n_tiles_y;
+  const int m0 = ty * 16 * TB;
+  const int n0 = tx * 16 * RT;
+  const int Kq = a.K / 4;
+  const int k_begin = wave * Kq;
+  const int nchunks = Kq / 64;
+
+  const bf16_t* W = static_cast<const bf16_t*>(a.W);
+  const bf16_t* wp[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+    wp[rt] = W + static_cast<int64_t>(n0 + rt * 16 + l16) * a.K + k_begin + g4 * 16;
+  const bf16_t* xp[TB];
+  bool xok[TB];
+#pragma unroll
+  for (int tb = 0; tb < TB; ++tb) {
+    const int m = m0 + tb * 16 + l16;
+    xok[tb] = m < a.M;
+    xp[tb] = a.X + static_cast<int64_t>(xok[tb] ? m : m0) * a.K + k_begin + g4 * 16;
+  }
+
+  struct Slot {
+    uint4 x[TB][2];
+    uint4 w[RT][2];
+  };
+  Slot ring[NR];
+  auto issue = [&](Slot& sl, int c) {
+    const int cc = min(c, nchunks - 1);
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      sl.w[rt][0] = *reinterpret_cast<const uint4*>(wp[rt] + cc * 64);
+      sl.w[rt][1] = *reinterpret_cast<const uint4*>(wp[rt] + cc * 64 + 8);
+    }
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+      sl.x[tb][0] = *reinterpret_cast<const uint4*>(xp[tb] + cc * 64);
+      sl.x[tb][1] = *reinterpret_cast<const uint4*>(xp[tb] + cc * 64 + 8);
+    }
+  };
+  const uint4 zero4 = make_uint4(0, 0, 0, 0);
+  f32x4_v acc[RT][TB];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) acc[rt][tb] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int p = 0; p < NR; ++p) {
+    issue(ring[p], p);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  for (int c0 = 0; c0 < nchunks; c0 += NR) {
+#pragma unroll
+    for (int p = 0; p < NR; ++p) {
+      const Slot cur = ring[p];
+      __builtin_amdgcn_sched_barrier(0);
+      issue(ring[p], c0 + p + NR);
+      __builtin_amdgcn_sched_barrier(0);
+      if (c0 + p < nchunks) {
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) {
+          const uint4 u0 = xok[tb] ? cur.x[tb][0] : zero4, u1 = xok[tb] ? cur.x[tb][1] : zero4;
+          const bf16x8_v x0 = *reinterpret_cast<const bf16x8_v*>(&u0);
+          const bf16x8_v x1 = *reinterpret_cast<const bf16x8_v*>(&u1);
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) {
+            const bf16x8_v w0 = *reinterpret_cast<const bf16x8_v*>(&cur.w[rt][0]);
+            const bf16x8_v w1 = *reinterpret_cast<const bf16x8_v*>(&cur.w[rt][1]);
+            acc[rt][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w0, x0, acc[rt][tb], 0, 0, 0);
+            acc[rt][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w1, x1, acc[rt][tb], 0, 0, 0);
+          }
+        }
+      }
+    }
+  }
+
+  // ---- deterministic split-K reduction through LDS
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s_acc[wave][(rt * TB + tb) * 4 + r][lane] = acc[rt][tb][r];
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < RT / 4; ++q) {
+    const int rt = wave * (RT / 4) + q;
+    const int n = n0 + rt * 16 + g4 * 4;
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+      const int m = m0 + tb * 16 + l16;
+      float v[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int idx = (rt * TB + tb) * 4 + r;
+        v[r] = ((s_acc[0][idx][lane] + s_acc[1][idx][lane]) + s_acc[2][idx][lane]) + s_acc[3][idx][lane];
+      }
+      if (m >= a.M) continue;
+      if (a.out_dtype == DG_F32) {
+        float* o = static_cast<float*>(a.out) + static_cast<int64_t>(m) * a.N + n;
+        if (a.accumulate) {
+          const float4 c = *reinterpret_cast<float4*>(o);
+          *reinterpret_cast<float4*>(o) = make_float4(c.x + v[0], c.y + v[1], c.z + v[2], c.w + v[3]);
+        } else {
+          *reinterpret_cast<float4*>(o) = make_float4(v[0], v[1], v[2], v[3]);
+        }
+      } else {
+        bf16_t* o = static_cast<bf16_t*>(a.out) + static_cast<int64_t>(m) * a.N + n;
+        uint2 pk;
+        pk.x = pack_bf16x2(v[0], v[1]);
+        pk.y = pack_bf16x2(v[2], v[3]);
+        *reinterpret_cast<uint2*>(o) = pk;
       }
     }
   }

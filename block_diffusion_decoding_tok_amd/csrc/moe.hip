@@ -13,7 +13,7 @@
 //                       -> expert_offsets, stable scatter of the slot entries
 //                       t * k + j by expert (ballot-based ranks, deterministic).
 //   gemm_stream_kernel  (gemm_mfma.h) gate/up + GELU*up -> h [T*k, I] bf16 in
-//                       sorted order; down + gate -> y_slot [T*k, D] f32.
+//                       sorted order; down + gate -> y_slot [T*k, D] bf16.
 //   combine_kernel      y[t] += sum_j y_slot[t*k + j] in slot order.
 //   f32 path            plain SIMT kernels over the same tables (parity path).
 #include "common.h"
@@ -130,16 +130,20 @@ dg_status launch_moe_route(const float* logits, int T, int E, int k, int32_t* to
 }
 
 // ------------------------------------------------------------- combine
-__global__ void combine_kernel(const float* __restrict__ y_slot, int T, int D, int k,
+template <typename TS>
+__global__ void combine_kernel(const TS* __restrict__ y_slot, int T, int D, int k,
                                float* __restrict__ y) {
-  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;   // float4 index
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;   // 4-wide
   const int64_t n4 = static_cast<int64_t>(T) * D / 4;
   if (idx >= n4) return;
   const int64_t t = idx / (D / 4), d4 = idx % (D / 4);
   float4 acc = reinterpret_cast<float4*>(y)[idx];
   for (int j = 0; j < k; ++j) {
-    const float4 v = reinterpret_cast<const float4*>(y_slot + (t * k + j) * D)[d4];
-    acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    const TS* src = y_slot + (t * k + j) * D + d4 * 4;
+    acc.x += Elem<TS>::load(src, 0);
+    acc.y += Elem<TS>::load(src, 1);
+    acc.z += Elem<TS>::load(src, 2);
+    acc.w += Elem<TS>::load(src, 3);
   }
   reinterpret_cast<float4*>(y)[idx] = acc;
 }
@@ -186,20 +190,27 @@ __global__ void down_f32_kernel(const float* __restrict__ h, const float* __rest
 
 // ------------------------------------------------------------- launchers
 constexpr int kMoeTB = 4;      // 64 tokens per tile
-constexpr int kMoeKS = 4;      // 256 k per LDS stage
+constexpr int kMoeKS = 2;      // 128 k per LDS stage
+constexpr int kMoePF = 3;      // weight stages in flight
 
 size_t moe_ffn_workspace_bytes(int T, int D, int I, int E, int k, int x_dtype) {
   const size_t slots = static_cast<size_t>(T) * k;
   const size_t esz = x_dtype == DG_F32 ? 4 : 2;
-  return align_up(slots * I * esz, 256) + align_up(slots * D * 4, 256);
+  return align_up(slots * I * esz, 256) + align_up(slots * D * esz, 256);
 }
+
+constexpr int kMoeNR = 3;      // register ring depth (chunks of 64 k), one-wave kernels
+constexpr int kMoeWaveRT = 8;  // one-wave kernels: 8 tiles of 16 rows per wave
 
 template <bool FP8>
 static dg_status launch_grouped(const void* x, const void* wgu, const void* wd, const float* sgu,
                                 const float* sd, const float* gates, const int32_t* offsets,
                                 const int32_t* sorted_rows, int T, int D, int I, int E, int k,
-                                bf16_t* h, float* y_slot, hipStream_t stream) {
-  constexpr int MT = 16 * kMoeTB;
+                                bf16_t* h, bf16_t* y_slot, hipStream_t stream) {
+  // few tokens per expert (the canvas of one or two rows): 16-token tiles,
+  // register streaming; more: 64-token tiles staged through LDS
+  const bool small = static_cast<int64_t>(T) * k <= 40ll * E;
+  const int MT = small ? 16 : 16 * kMoeTB;
   const int max_ty = E + (T * k + MT - 1) / MT;
   GemmArgs g{};
   g.W = wgu; g.w_group_stride = static_cast<int64_t>(2) * I * D;
@@ -209,9 +220,17 @@ static dg_status launch_grouped(const void* x, const void* wgu, const void* wd, 
   g.offsets = offsets; g.sorted_rows = sorted_rows; g.gates = gates;
   g.out = h;
   g.n_tiles_x = I / 64;
+  g.n_tiles_y = max_ty;
   g.n_tiles_total = g.n_tiles_x * max_ty;
-  gemm_stream_kernel<2, kMoeTB, kMoeKS, FP8, kGateUp>
-      <<<(g.n_tiles_total + 7) / 8 * 8, 256, 0, stream>>>(g);
+  g.y_fastest = small;
+  const unsigned gwg = (g.n_tiles_total + 7) / 8 * 8;
+  if (small) {
+    g.n_tiles_x = I / (8 * kMoeWaveRT);
+    g.n_tiles_total = g.n_tiles_x * max_ty;
+    gemm_wave_kernel<kMoeWaveRT, kMoeNR, FP8, kGateUp>
+        <<<(g.n_tiles_total + 7) / 8 * 8, 64, 0, stream>>>(g);
+  } else
+    gemm_stream_kernel<2, kMoeTB, kMoeKS, kMoePF, FP8, kGateUp><<<gwg, 256, 0, stream>>>(g);
   DG_LAUNCH_CHECK();
   GemmArgs d{};
   d.W = wd; d.w_group_stride = static_cast<int64_t>(D) * I;
@@ -221,9 +240,17 @@ static dg_status launch_grouped(const void* x, const void* wgu, const void* wd, 
   d.offsets = offsets; d.sorted_rows = sorted_rows; d.gates = gates;
   d.out = y_slot;
   d.n_tiles_x = D / 128;
+  d.n_tiles_y = max_ty;
   d.n_tiles_total = d.n_tiles_x * max_ty;
-  gemm_stream_kernel<2, kMoeTB, kMoeKS, FP8, kDown>
-      <<<(d.n_tiles_total + 7) / 8 * 8, 256, 0, stream>>>(d);
+  d.y_fastest = small;
+  const unsigned dwg = (d.n_tiles_total + 7) / 8 * 8;
+  if (small) {
+    d.n_tiles_x = D / (16 * kMoeWaveRT);
+    d.n_tiles_total = d.n_tiles_x * max_ty;
+    gemm_wave_kernel<kMoeWaveRT, kMoeNR, FP8, kDown>
+        <<<(d.n_tiles_total + 7) / 8 * 8, 64, 0, stream>>>(d);
+  } else
+    gemm_stream_kernel<2, kMoeTB, kMoeKS, kMoePF, FP8, kDown><<<dwg, 256, 0, stream>>>(d);
   DG_LAUNCH_CHECK();
   return DG_OK;
 }
@@ -237,7 +264,9 @@ dg_status launch_moe_ffn(const void* x, int x_dtype, const void* w_gate_up, cons
   char* w = static_cast<char*>(ws);
   const size_t esz = x_dtype == DG_F32 ? 4 : 2;
   void* h = w;
-  float* y_slot = reinterpret_cast<float*>(w + align_up(slots * I * esz, 256));
+  void* y_slot = w + align_up(slots * I * esz, 256);
+  const int64_t n4 = static_cast<int64_t>(T) * D / 4;
+  const unsigned cblocks = static_cast<unsigned>((n4 + 255) / 256);
   dg_status st = DG_OK;
   if (x_dtype == DG_F32) {
     gateup_f32_kernel<<<T * k, 128, 0, stream>>>(static_cast<const float*>(x),
@@ -247,18 +276,23 @@ dg_status launch_moe_ffn(const void* x, int x_dtype, const void* w_gate_up, cons
     DG_LAUNCH_CHECK();
     down_f32_kernel<<<T * k, 128, 0, stream>>>(static_cast<const float*>(h),
                                                static_cast<const float*>(w_down), offsets,
-                                               sorted_rows, gates, T * k, E, D, I, y_slot);
+                                               sorted_rows, gates, T * k, E, D, I,
+                                               static_cast<float*>(y_slot));
     DG_LAUNCH_CHECK();
-  } else if (w_dtype == DG_FP8_E4M3) {
-    st = launch_grouped<true>(x, w_gate_up, w_down, s_gate_up, s_down, gates, offsets,
-                              sorted_rows, T, D, I, E, k, static_cast<bf16_t*>(h), y_slot, stream);
-  } else {
-    st = launch_grouped<false>(x, w_gate_up, w_down, nullptr, nullptr, gates, offsets,
-                               sorted_rows, T, D, I, E, k, static_cast<bf16_t*>(h), y_slot, stream);
+    combine_kernel<float><<<cblocks, 256, 0, stream>>>(static_cast<const float*>(y_slot), T, D, k, y);
+    DG_LAUNCH_CHECK();
+    return DG_OK;
   }
+  if (w_dtype == DG_FP8_E4M3)
+    st = launch_grouped<true>(x, w_gate_up, w_down, s_gate_up, s_down, gates, offsets,
+                              sorted_rows, T, D, I, E, k, static_cast<bf16_t*>(h),
+                              static_cast<bf16_t*>(y_slot), stream);
+  else
+    st = launch_grouped<false>(x, w_gate_up, w_down, nullptr, nullptr, gates, offsets,
+                               sorted_rows, T, D, I, E, k, static_cast<bf16_t*>(h),
+                               static_cast<bf16_t*>(y_slot), stream);
   if (st != DG_OK) return st;
-  const int64_t n4 = static_cast<int64_t>(T) * D / 4;
-  combine_kernel<<<static_cast<unsigned>((n4 + 255) / 256), 256, 0, stream>>>(y_slot, T, D, k, y);
+  combine_kernel<bf16_t><<<cblocks, 256, 0, stream>>>(static_cast<const bf16_t*>(y_slot), T, D, k, y);
   DG_LAUNCH_CHECK();
   return DG_OK;
 }
