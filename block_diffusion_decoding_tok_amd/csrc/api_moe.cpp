@@ -31,7 +31,7 @@ size_t dg_moe_ffn_workspace_size(int T, int D, int I, int E, int k, int x_dtype)
 }
 
 dg_status dg_moe_ffn(const void* x, int x_dtype, const void* w_gate_up, const void* w_down,
-                     int w_dtype, const float* s_gate_up, const float* s_down,
+                     int w_dtype, int w_layout, const float* s_gate_up, const float* s_down,
                      const int32_t* topk_ids, const float* gates, const int32_t* expert_offsets,
                      const int32_t* sorted_rows, int T, int D, int I, int E, int k, float* y,
                      void* ws, size_t ws_bytes, void* stream) {
@@ -43,6 +43,10 @@ dg_status dg_moe_ffn(const void* x, int x_dtype, const void* w_gate_up, const vo
                "dg_moe_ffn: bad w_dtype");
   DG_CHECK_ARG((x_dtype == DG_F32) == (w_dtype == DG_F32),
                "dg_moe_ffn: f32 activations go with f32 weights only");
+  DG_CHECK_ARG(w_layout == DG_LAYOUT_ROWMAJOR || w_layout == DG_LAYOUT_TILED,
+               "dg_moe_ffn: bad w_layout");
+  DG_CHECK_ARG(w_layout == DG_LAYOUT_ROWMAJOR || x_dtype != DG_F32,
+               "dg_moe_ffn: the tiled layout needs bf16 activations");
   DG_CHECK_ARG(w_dtype != DG_FP8_E4M3 || (s_gate_up && s_down),
                "dg_moe_ffn: fp8 weights need s_gate_up and s_down");
   DG_CHECK_SHAPE(T > 0 && E > 0 && E <= 256 && k > 0 && k <= E && k <= 16,
@@ -53,7 +57,8 @@ dg_status dg_moe_ffn(const void* x, int x_dtype, const void* w_gate_up, const vo
                    "dg_moe_ffn: the MFMA path needs D % 128 == 0 and I % 64 == 0");
   if (ws == nullptr || ws_bytes < moe_ffn_workspace_bytes(T, D, I, E, k, x_dtype))
     return fail(DG_ERR_WORKSPACE, "dg_moe_ffn: workspace too small");
-  return launch_moe_ffn(x, x_dtype, w_gate_up, w_down, w_dtype, s_gate_up, s_down, topk_ids, gates,
+  return launch_moe_ffn(x, x_dtype, w_gate_up, w_down, w_dtype, w_layout, s_gate_up, s_down,
+                        topk_ids, gates,
                         expert_offsets, sorted_rows, T, D, I, E, k, y, ws,
                         static_cast<hipStream_t>(stream));
 }

@@ -22,4 +22,17 @@ dg_status dg_quantize_fp8_rows(const float* src, uint8_t* q, float* scale, int64
   return launch_quantize_fp8_rows(src, q, scale, rows, cols, static_cast<hipStream_t>(stream));
 }
 
+dg_status dg_pack_weights(const void* src, void* dst, int64_t groups, int N, int K, int dtype,
+                          void* stream) {
+  set_error("");
+  DG_CHECK_ARG(src && dst && src != dst, "dg_pack_weights: null or aliased pointer");
+  DG_CHECK_ARG(dtype == DG_BF16 || dtype == DG_FP8_E4M3, "dg_pack_weights: dtype must be bf16 or fp8");
+  DG_CHECK_SHAPE(groups > 0 && N > 0 && K > 0 && N % 16 == 0 && K % 64 == 0,
+                 "dg_pack_weights: need N % 16 == 0 and K % 64 == 0");
+  DG_CHECK_SHAPE(groups * N * static_cast<int64_t>(K) / 8 < (1ll << 31) * 256ll,
+                 "dg_pack_weights: tensor too large");
+  return launch_pack_weights(src, dst, groups, N, K, dtype == DG_BF16 ? 2 : 1,
+                             static_cast<hipStream_t>(stream));
+}
+
 }  // extern "C"

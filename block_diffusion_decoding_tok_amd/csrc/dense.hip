@@ -35,8 +35,11 @@ __global__ void gemm_f32_kernel(const float* __restrict__ A, const float* __rest
   *c = accumulate ? *c + acc : acc;
 }
 
+template <bool TILED>
+static void launch_gemm_bf16(GemmArgs& g, int M, int N, int K, hipStream_t stream);
+
 dg_status launch_gemm(const void* A, const void* W, void* C, int M, int N, int K, int dtype,
-                      int out_dtype, GemmEpilogue ep, hipStream_t stream) {
+                      int w_layout, int out_dtype, GemmEpilogue ep, hipStream_t stream) {
   if (dtype == DG_F32) {
     dim3 grid((N + 127) / 128, M);
     gemm_f32_kernel<<<grid, 128, 0, stream>>>(static_cast<const float*>(A),
@@ -53,11 +56,21 @@ dg_status launch_gemm(const void* A, const void* W, void* C, int M, int N, int K
   g.out_dtype = ep == kAccumulateF32 ? DG_F32 : out_dtype;
   g.accumulate = ep == kAccumulateF32;
   g.y_fastest = 1;
+  if (w_layout == DG_LAYOUT_TILED)
+    launch_gemm_bf16<true>(g, M, N, K, stream);
+  else
+    launch_gemm_bf16<false>(g, M, N, K, stream);
+  DG_LAUNCH_CHECK();
+  return DG_OK;
+}
+
+template <bool TILED>
+static void launch_gemm_bf16(GemmArgs& g, int M, int N, int K, hipStream_t stream) {
   if (N >= 32768) {
     g.n_tiles_x = N / (64 * kWideRT);
     g.n_tiles_y = (M + 16 * kWideTB - 1) / (16 * kWideTB);
     g.n_tiles_total = g.n_tiles_x * g.n_tiles_y;
-    gemm_stream_kernel<kWideRT, kWideTB, kWideKS, kWidePF, false, kDense>
+    gemm_stream_kernel<kWideRT, kWideTB, kWideKS, kWidePF, false, kDense, TILED>
         <<<(g.n_tiles_total + 7) / 8 * 8, 256, 0, stream>>>(g);
   } else if (K % 256 == 0 && N % 64 == 0) {
     // projections: 64 rows x 64 tokens per workgroup, K split over its waves
@@ -68,18 +81,16 @@ dg_status launch_gemm(const void* A, const void* W, void* C, int M, int N, int K
     g.n_tiles_total = g.n_tiles_x * g.n_tiles_y;
     const unsigned grid = (g.n_tiles_total + 7) / 8 * 8;
     if (narrow)
-      gemm_splitk_kernel<4, 1, kSplitNR><<<grid, 256, 0, stream>>>(g);
+      gemm_splitk_kernel<4, 1, kSplitNR, TILED><<<grid, 256, 0, stream>>>(g);
     else
-      gemm_splitk_kernel<4, 4, kSplitNR><<<grid, 256, 0, stream>>>(g);
+      gemm_splitk_kernel<4, 4, kSplitNR, TILED><<<grid, 256, 0, stream>>>(g);
   } else {
     g.n_tiles_x = N / (64 * kDenseRT);
     g.n_tiles_y = (M + 16 * kDenseTB - 1) / (16 * kDenseTB);
     g.n_tiles_total = g.n_tiles_x * g.n_tiles_y;
-    gemm_stream_kernel<kDenseRT, kDenseTB, kDenseKS, kDensePF, false, kDense>
+    gemm_stream_kernel<kDenseRT, kDenseTB, kDenseKS, kDensePF, false, kDense, TILED>
         <<<(g.n_tiles_total + 7) / 8 * 8, 256, 0, stream>>>(g);
   }
-  DG_LAUNCH_CHECK();
-  return DG_OK;
 }
 
 template <typename TO>

@@ -82,21 +82,39 @@ __device__ __forceinline__ void fp8x16_to_bf16(const uint4& q, bf16x8_v& lo, bf1
 template <bool FP8> struct WChunk;
 template <> struct WChunk<true> {
   uint4 q;
+  template <int SECOND = 0>
   __device__ void load(const uint8_t* p) { q = *reinterpret_cast<const uint4*>(p); }
   __device__ void zero() { q = make_uint4(0, 0, 0, 0); }
   __device__ void get(bf16x8_v& a, bf16x8_v& b) const { fp8x16_to_bf16(q, a, b); }
 };
 template <> struct WChunk<false> {
   uint4 q0, q1;
+  template <int SECOND = 8>
   __device__ void load(const bf16_t* p) {
     q0 = *reinterpret_cast<const uint4*>(p);
-    q1 = *reinterpret_cast<const uint4*>(p + 8);
+    q1 = *reinterpret_cast<const uint4*>(p + SECOND);
   }
   __device__ void zero() { q0 = q1 = make_uint4(0, 0, 0, 0); }
   __device__ void get(bf16x8_v& a, bf16x8_v& b) const {
     a = *reinterpret_cast<const bf16x8_v*>(&q0);
     b = *reinterpret_cast<const bf16x8_v*>(&q1);
   }
+};
+
+// Address of a lane's 16 k-values of chunk c (64 k) of a 16-row weight tile,
+// row-major or tile-packed (DG_LAYOUT_TILED: the tile's chunk c is one
+// contiguous block of 1024 elements in lane order).
+template <typename WT, bool TILED>
+struct WRow {
+  const WT* base;
+  static constexpr int kSecond = TILED ? 512 : 8;   // 2-byte types: values 8..15
+  __device__ void init(const WT* Wg, int row0, int K, int lane) {
+    if (TILED)
+      base = Wg + static_cast<int64_t>(row0 / 16) * (K / 64) * 1024 + lane * (sizeof(WT) == 1 ? 16 : 8);
+    else
+      base = Wg + static_cast<int64_t>(row0 + (lane & 15)) * K + (lane >> 4) * 16;
+  }
+  __device__ const WT* at(int c) const { return base + c * (TILED ? 1024 : 64); }
 };
 
 // Logical workgroup index: consecutive logical tiles go to the same XCD
@@ -107,7 +125,7 @@ __device__ __forceinline__ int xcd_logical_tile(int linear, int total) {
   return (linear % 8) * per + linear / 8;
 }
 
-template <int RT, int TB, int KS, int PF, bool FP8, int MODE>
+template <int RT, int TB, int KS, int PF, bool FP8, int MODE, bool TILED>
 __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
   using WT = typename std::conditional<FP8, uint8_t, bf16_t>::type;
   constexpr int MT = 16 * TB;           // tokens per tile
@@ -171,11 +189,12 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
 
   // ---- weight rows of this wave
   const WT* Wg = static_cast<const WT*>(a.W) + static_cast<int64_t>(grp) * a.w_group_stride;
-  int wrow[RT];
+  WRow<WT, TILED> wr_at[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    if (MODE == kGateUp) wrow[rt] = (rt == 0 ? 0 : a.N / 2) + tx * 64 + wave * 16 + l16;
-    else wrow[rt] = tx * (64 * RT) + wave * (16 * RT) + rt * 16 + l16;
+    const int row0 = (MODE == kGateUp) ? (rt == 0 ? 0 : a.N / 2) + tx * 64 + wave * 16
+                                       : tx * (64 * RT) + wave * (16 * RT) + rt * 16;
+    wr_at[rt].init(Wg, row0, a.K, lane);
   }
   const int nchunks = (a.K + 63) / 64;
   const int nstages = (nchunks + KS - 1) / KS;
@@ -190,7 +209,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
       const int c = min(stage * KS + j, nchunks - 1);
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt)
-        slot[j][rt].load(Wg + static_cast<int64_t>(wrow[rt]) * a.K + c * 64 + g4 * 16);
+        slot[j][rt].template load<WRow<WT, TILED>::kSecond>(wr_at[rt].at(c));
     }
   };
   // token rows: a stage of MT rows x SK k of bf16 = PIECES 16-byte pieces,
@@ -254,7 +273,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
         const int c = min((s + PF) * KS + j, nchunks - 1);
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
-          wr[p][j][rt].load(Wg + static_cast<int64_t>(wrow[rt]) * a.K + c * 64 + g4 * 16);
+          wr[p][j][rt].template load<WRow<WT, TILED>::kSecond>(wr_at[rt].at(c));
         if (s * KS + j >= nchunks) continue;
 #pragma unroll
         for (int tb = 0; tb < TB; ++tb) {
@@ -331,189 +350,6 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
 
 }  // namespace dg
 
-namespace dg {
-
-// Register-streaming variant for tiles of 16 tokens (small per-expert token
-// counts and narrow dense outputs).  No LDS and no barrier in the K loop:
-// every wave streams its own 16 * RT weight rows and its 16 token rows
-// straight into a ring of NR chunks (64 k each) of registers, so NR chunks
-// of both operands are in flight per wave while the MFMAs consume the oldest.
-// Same operand layout, k order, modes and epilogues as gemm_stream_kernel
-// with TB = 1.
-template <int RT, int NR, bool FP8, int MODE>
-__global__ __launch_bounds__(256) void gemm_reg_kernel(GemmArgs a) {
-  using WT = typename std::conditional<FP8, uint8_t, bf16_t>::type;
-  constexpr int MT = 16;
-  __shared__ int s_rows[MT];
-  __shared__ int s_dst[MT];
-  __shared__ int s_scan[256];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int l16 = lane & 15, g4 = lane >> 4;
-  const int logical = xcd_logical_tile(blockIdx.x, gridDim.x);
-  if (logical >= a.n_tiles_total) return;
-  const int tx = a.y_fastest ? logical / a.n_tiles_y : logical % a.n_tiles_x;
-  const int ty = a.y_fastest ? logical % a.n_tiles_y : logical / a.n_tiles_x;
-
-  int grp = 0, m0 = 0, m_count = 0, base_pos = 0;
-  if (MODE == kDense) {
-    m0 = ty * MT;
-    if (m0 >= a.M) return;
-    m_count = min(MT, a.M - m0);
-  } else {
-    const int E = a.n_groups;
-    int tiles_e = 0;
-    if (tid < E) tiles_e = (a.offsets[tid + 1] - a.offsets[tid] + MT - 1) / MT;
-    s_scan[tid] = tiles_e;
-    __syncthreads();
-    for (int o = 1; o < 256; o <<= 1) {
-      const int v = (tid >= o) ? s_scan[tid - o] : 0;
-      __syncthreads();
-      s_scan[tid] += v;
-      __syncthreads();
-    }
-    if (ty >= s_scan[E - 1]) return;
-    int lo = 0, hi = E - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (s_scan[mid] > ty) hi = mid; else lo = mid + 1;
-    }
-    grp = lo;
-    const int first_tile = grp ? s_scan[grp - 1] : 0;
-    base_pos = a.offsets[grp];
-    m0 = (ty - first_tile) * MT;
-    m_count = min(MT, a.offsets[grp + 1] - base_pos - m0);
-  }
-  if (tid < MT) {
-    int src = -1, dst = -1;
-    if (tid < m_count) {
-      const int m = m0 + tid;
-      if (MODE == kDense) { src = m; dst = m; }
-      else if (MODE == kGateUp) { const int p = base_pos + m; src = a.sorted_rows[p] / a.topk; dst = p; }
-      else { const int p = base_pos + m; src = p; dst = a.sorted_rows[p]; }
-    }
-    s_rows[tid] = src;
-    s_dst[tid] = dst;
-  }
-  __syncthreads();
-
-  // Every load below is unconditional (clamped addresses, masked after the
-  // fact): conditional loads would make the compiler drain the whole ring
-  // (vmcnt(0)) at each step.  Row counts are multiples of the tile by contract.
-  const WT* Wg = static_cast<const WT*>(a.W) + static_cast<int64_t>(grp) * a.w_group_stride;
-  const WT* wp[RT];
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int row = (MODE == kGateUp) ? (rt == 0 ? 0 : a.N / 2) + tx * 64 + wave * 16 + l16
-                                      : tx * (64 * RT) + wave * (16 * RT) + rt * 16 + l16;
-    wp[rt] = Wg + static_cast<int64_t>(row) * a.K + g4 * 16;
-  }
-  const int src = s_rows[l16];
-  const bool xok = src >= 0;
-  const bf16_t* xp = a.X + static_cast<int64_t>(xok ? src : s_rows[0]) * a.K + g4 * 16;
-  const int nchunks = a.K / 64;
-
-  struct Slot {
-    uint4 x0, x1;
-    WChunk<FP8> w[RT];
-  };
-  Slot ring[NR];
-  auto issue = [&](Slot& sl, int c) {
-    const int cc = min(c, nchunks - 1);      // tail slots reload the last chunk, unused
-    sl.x0 = *reinterpret_cast<const uint4*>(xp + cc * 64);
-    sl.x1 = *reinterpret_cast<const uint4*>(xp + cc * 64 + 8);
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) sl.w[rt].load(wp[rt] + cc * 64);
-  };
-  const uint4 zero4 = make_uint4(0, 0, 0, 0);
-
-  f32x4_v acc[RT];
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) acc[rt] = f32x4_v{0.f, 0.f, 0.f, 0.f};
-  // the ring's loads must reach the memory counter in slot order, or waiting
-  // for the oldest slot waits for all of them: pin the issue order
-#pragma unroll
-  for (int p = 0; p < NR; ++p) {
-    issue(ring[p], p);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  for (int c0 = 0; c0 < nchunks; c0 += NR) {
-#pragma unroll
-    for (int p = 0; p < NR; ++p) {
-      const Slot cur = ring[p];
-      __builtin_amdgcn_sched_barrier(0);
-      issue(ring[p], c0 + p + NR);
-      __builtin_amdgcn_sched_barrier(0);
-      if (c0 + p < nchunks) {
-        bf16x8_v wa[RT][2];
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) cur.w[rt].get(wa[rt][0], wa[rt][1]);
-        const uint4 u0 = xok ? cur.x0 : zero4, u1 = xok ? cur.x1 : zero4;
-        const bf16x8_v x0 = *reinterpret_cast<const bf16x8_v*>(&u0);
-        const bf16x8_v x1 = *reinterpret_cast<const bf16x8_v*>(&u1);
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-          acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[rt][0], x0, acc[rt], 0, 0, 0);
-          acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[rt][1], x1, acc[rt], 0, 0, 0);
-        }
-      }
-    }
-  }
-
-  // ---- epilogue (lane: rows 4 g4 + r of each tile, token l16)
-  const int t = l16;
-  if (t >= m_count) return;
-  const int dst = s_dst[t];
-  const float* sc = a.w_scale ? a.w_scale + static_cast<int64_t>(grp) * a.s_group_stride : nullptr;
-  if (MODE == kGateUp) {
-    const int I = a.N / 2;
-    const int n = tx * 64 + wave * 16 + g4 * 4;
-    if (n >= I) return;
-    float hv[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float sg = sc ? sc[n + r] : 1.f, su = sc ? sc[I + n + r] : 1.f;
-      hv[r] = gelu_erf(acc[0][r] * sg) * (acc[1][r] * su);
-    }
-    uint2 pk;
-    pk.x = pack_bf16x2(hv[0], hv[1]);
-    pk.y = pack_bf16x2(hv[2], hv[3]);
-    *reinterpret_cast<uint2*>(static_cast<bf16_t*>(a.out) + static_cast<int64_t>(dst) * I + n) = pk;
-    return;
-  }
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int n = tx * (64 * RT) + wave * (16 * RT) + rt * 16 + g4 * 4;
-    if (n >= a.N) continue;
-    float v[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) v[r] = acc[rt][r] * (sc ? sc[n + r] : 1.f);
-    if (MODE == kDown) {
-      const float g = a.gates[dst];
-      bf16_t* o = static_cast<bf16_t*>(a.out) + static_cast<int64_t>(dst) * a.N + n;
-      uint2 pk;
-      pk.x = pack_bf16x2(g * v[0], g * v[1]);
-      pk.y = pack_bf16x2(g * v[2], g * v[3]);
-      *reinterpret_cast<uint2*>(o) = pk;
-    } else if (a.out_dtype == DG_F32) {
-      float* o = static_cast<float*>(a.out) + static_cast<int64_t>(dst) * a.N + n;
-      if (a.accumulate) {
-        const float4 c = *reinterpret_cast<float4*>(o);
-        *reinterpret_cast<float4*>(o) = make_float4(c.x + v[0], c.y + v[1], c.z + v[2], c.w + v[3]);
-      } else {
-        *reinterpret_cast<float4*>(o) = make_float4(v[0], v[1], v[2], v[3]);
-      }
-    } else {
-      bf16_t* o = static_cast<bf16_t*>(a.out) + static_cast<int64_t>(dst) * a.N + n;
-      uint2 pk;
-      pk.x = pack_bf16x2(v[0], v[1]);
-      pk.y = pack_bf16x2(v[2], v[3]);
-      *reinterpret_cast<uint2*>(o) = pk;
-    }
-  }
-}
-
-}  // namespace dg
 
 namespace dg {
 
@@ -523,8 +359,11 @@ namespace dg {
 // rows) and its 16 tokens, so each token row is read once per row block and
 // no LDS or barrier is needed.  The tile decode (which expert, which 16
 // tokens) runs in registers with wave shuffles.  The K loop streams a ring of
-// NR chunks of both operands, unconditional loads in a pinned order.
-template <int RT, int NR, bool FP8, int MODE>
+// NR chunks of both operands, unconditional loads in a pinned order.  (Giving
+// a wave all of an expert's tokens in passes instead, so that every work item
+// streams the same bytes, measured slower: later passes wait on the same
+// serial load chain.)
+template <int RT, int NR, bool FP8, int MODE, bool TILED>
 __global__ __launch_bounds__(64) void gemm_wave_kernel(GemmArgs a) {
   static_assert(MODE == kGateUp || MODE == kDown, "grouped modes only");
   static_assert(MODE != kGateUp || RT % 2 == 0, "gate/up needs paired tiles");
@@ -573,13 +412,13 @@ __global__ __launch_bounds__(64) void gemm_wave_kernel(GemmArgs a) {
   const bool xok = l16 < m_count;
 
   const WT* Wg = static_cast<const WT*>(a.W) + static_cast<int64_t>(grp) * a.w_group_stride;
-  const WT* wp[RT];
+  WRow<WT, TILED> wp[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    const int row = (MODE == kGateUp)
-                        ? (rt < RT / 2 ? 0 : a.N / 2) + tx * (8 * RT) + (rt % (RT / 2)) * 16 + l16
-                        : tx * (16 * RT) + rt * 16 + l16;
-    wp[rt] = Wg + static_cast<int64_t>(row) * a.K + g4 * 16;
+    const int row0 = (MODE == kGateUp)
+                         ? (rt < RT / 2 ? 0 : a.N / 2) + tx * (8 * RT) + (rt % (RT / 2)) * 16
+                         : tx * (16 * RT) + rt * 16;
+    wp[rt].init(Wg, row0, a.K, lane);
   }
   const bf16_t* xp = a.X + static_cast<int64_t>(src) * a.K + g4 * 16;
   const int nchunks = a.K / 64;
@@ -594,7 +433,7 @@ __global__ __launch_bounds__(64) void gemm_wave_kernel(GemmArgs a) {
     sl.x0 = *reinterpret_cast<const uint4*>(xp + cc * 64);
     sl.x1 = *reinterpret_cast<const uint4*>(xp + cc * 64 + 8);
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) sl.w[rt].load(wp[rt] + cc * 64);
+    for (int rt = 0; rt < RT; ++rt) sl.w[rt].template load<WRow<WT, TILED>::kSecond>(wp[rt].at(cc));
   };
   const uint4 zero4 = make_uint4(0, 0, 0, 0);
   f32x4_v acc[RT];
@@ -675,7 +514,7 @@ namespace dg {
 // register ring of NR chunks (unconditional loads, pinned issue order).  The
 // four partial accumulators are summed through LDS in wave order (fixed
 // order: deterministic), each wave finishing RT / 4 of the row tiles.
-template <int RT, int TB, int NR>
+template <int RT, int TB, int NR, bool TILED>
 __global__ __launch_bounds__(256) void gemm_splitk_kernel(GemmArgs a) {
   static_assert(RT % 4 == 0, "each wave finishes RT / 4 row tiles");
   __shared__ __attribute__((aligned(16))) float s_acc[4][RT * TB * 4][64];
@@ -692,10 +531,10 @@ __global__ __launch_bounds__(256) void gemm_splitk_kernel(GemmArgs a) {
   const int nchunks = Kq / 64;
 
   const bf16_t* W = static_cast<const bf16_t*>(a.W);
-  const bf16_t* wp[RT];
+  WRow<bf16_t, TILED> wp[RT];
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt)
-    wp[rt] = W + static_cast<int64_t>(n0 + rt * 16 + l16) * a.K + k_begin + g4 * 16;
+  for (int rt = 0; rt < RT; ++rt) wp[rt].init(W, n0 + rt * 16, a.K, lane);
+  const int c_begin = k_begin / 64;
   const bf16_t* xp[TB];
   bool xok[TB];
 #pragma unroll
@@ -714,8 +553,9 @@ __global__ __launch_bounds__(256) void gemm_splitk_kernel(GemmArgs a) {
     const int cc = min(c, nchunks - 1);
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-      sl.w[rt][0] = *reinterpret_cast<const uint4*>(wp[rt] + cc * 64);
-      sl.w[rt][1] = *reinterpret_cast<const uint4*>(wp[rt] + cc * 64 + 8);
+      const bf16_t* pw = wp[rt].at(c_begin + cc);
+      sl.w[rt][0] = *reinterpret_cast<const uint4*>(pw);
+      sl.w[rt][1] = *reinterpret_cast<const uint4*>(pw + WRow<bf16_t, TILED>::kSecond);
     }
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) {

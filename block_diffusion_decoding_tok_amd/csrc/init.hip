@@ -4,6 +4,7 @@
 //   0xFF000000) -> four 24-bit uniforms -> two Box-Muller pairs.
 //   quantize: scale = max|row| / 448; byte = e4m3fn round-to-nearest-even of
 //   x / scale, saturated to +-448.
+//   pack: row-major weights -> DG_LAYOUT_TILED.
 #include "common.h"
 #include "kernels.h"
 #include "philox.h"
@@ -65,6 +66,36 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const float* __restr
   const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
   if (threadIdx.x == 0) scale[row] = sc;
   for (int c = threadIdx.x; c < cols; c += blockDim.x) q[row * cols + c] = f32_to_e4m3fn_rne(s[c] / sc);
+}
+
+// Row-major [G, N, K] -> tile-packed (16 rows x 64 k blocks in wave-load
+// order); one thread per 16-byte piece of the destination.
+__global__ void pack_weights_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
+                                    int64_t pieces, int N, int K, int elem_bytes) {
+  const int64_t q = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (q >= pieces) return;
+  const int per_block = 1024 * elem_bytes / 16;        // 64 (1-byte) or 128 (2-byte) pieces
+  const int64_t blk = q / per_block;
+  const int within = static_cast<int>(q % per_block);
+  const int lane = within % 64, h = within / 64;
+  const int r = lane % 16, g4 = lane / 16;
+  const int64_t NC = K / 64, NT = N / 16;
+  const int64_t c = blk % NC;
+  const int64_t gt = blk / NC;                          // g * NT + t
+  const int64_t g = gt / NT, t = gt % NT;
+  const int vals = 16 / elem_bytes;                     // values per piece
+  const int64_t elem = (g * N + 16 * t + r) * static_cast<int64_t>(K) + 64 * c + 16 * g4 + vals * h;
+  dst[q] = src[elem * elem_bytes / 16];
+}
+
+dg_status launch_pack_weights(const void* src, void* dst, int64_t groups, int N, int K,
+                              int elem_bytes, hipStream_t stream) {
+  const int64_t pieces = groups * N * static_cast<int64_t>(K) * elem_bytes / 16;
+  if (pieces == 0) return DG_OK;
+  pack_weights_kernel<<<static_cast<unsigned>((pieces + 255) / 256), 256, 0, stream>>>(
+      static_cast<const uint4*>(src), static_cast<uint4*>(dst), pieces, N, K, elem_bytes);
+  DG_LAUNCH_CHECK();
+  return DG_OK;
 }
 
 dg_status launch_fill_normal(void* dst, int dtype, size_t n, float std, uint64_t seed,

@@ -47,16 +47,17 @@ dg_status launch_moe_route(const float* logits, int T, int E, int k, int32_t* to
                            hipStream_t stream);
 size_t moe_ffn_workspace_bytes(int T, int D, int I, int E, int k, int x_dtype);
 dg_status launch_moe_ffn(const void* x, int x_dtype, const void* w_gate_up, const void* w_down,
-                         int w_dtype, const float* s_gate_up, const float* s_down,
+                         int w_dtype, int w_layout, const float* s_gate_up, const float* s_down,
                          const int32_t* topk_ids, const float* gates, const int32_t* offsets,
                          const int32_t* sorted_rows, int T, int D, int I, int E, int k, float* y,
                          void* ws, hipStream_t stream);
 
-// dense.hip: C = A W^T with A [M, K] (bf16 or f32), W [N, K] (same dtype),
-// fp32 accumulation.  Epilogues: store in out_dtype, or add into f32 C.
+// dense.hip: C = A W^T with A [M, K] (bf16 or f32), W [N, K] (same dtype,
+// row-major or DG_LAYOUT_TILED for bf16), fp32 accumulation.  Epilogues: store
+// in out_dtype, or add into f32 C.
 enum GemmEpilogue { kStore = 0, kAccumulateF32 = 1 };
 dg_status launch_gemm(const void* A, const void* W, void* C, int M, int N, int K, int dtype,
-                      int out_dtype, GemmEpilogue ep, hipStream_t stream);
+                      int w_layout, int out_dtype, GemmEpilogue ep, hipStream_t stream);
 // RMSNorm of f32 rows x [M, D] (eps 1e-6, unit gain) into out_dtype.
 dg_status launch_rmsnorm(const float* x, void* out, int M, int D, int out_dtype,
                          hipStream_t stream);
@@ -69,5 +70,7 @@ dg_status launch_fill_normal(void* dst, int dtype, size_t n, float std, uint64_t
                              uint32_t stream_id, hipStream_t stream);
 dg_status launch_quantize_fp8_rows(const float* src, uint8_t* q, float* scale, int64_t rows,
                                    int cols, hipStream_t stream);
+dg_status launch_pack_weights(const void* src, void* dst, int64_t groups, int N, int K,
+                              int elem_bytes, hipStream_t stream);
 
 }  // namespace dg

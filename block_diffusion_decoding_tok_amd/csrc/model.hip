@@ -79,6 +79,8 @@ struct dg_ctx {
   int32_t* status = nullptr;
   bool use_graphs = true;
   std::map<GraphKey, hipGraphExec_t> graphs;
+  std::vector<const float*> router_override;   // empty: the model's own routing
+  int router_override_tokens = 0;
 };
 
 namespace {
@@ -145,6 +147,9 @@ dg_status check_dims(const dg_model_dims* d) {
                  "need n_experts <= 256 and top_k <= min(n_experts, 16)");
   DG_CHECK_SHAPE(d->vocab % 8 == 0, "vocab must be a multiple of 8");
   DG_CHECK_ARG(d->rope_theta > 1.f, "rope_theta must be > 1");
+  DG_CHECK_ARG(d->weight_layout == DG_LAYOUT_ROWMAJOR ||
+                   (d->weight_layout == DG_LAYOUT_TILED && d->act_dtype == DG_BF16),
+               "weight_layout must be row-major, or tiled with bf16 activations");
   if (d->act_dtype == DG_BF16) {
     DG_CHECK_ARG(d->expert_dtype == DG_BF16 || d->expert_dtype == DG_FP8_E4M3,
                  "bf16 activations need bf16 or fp8 experts");
@@ -174,8 +179,8 @@ dg_status layer(dg_ctx* c, int l, int B, int n, void* kc, void* vc, int Tmax,
   const size_t a = esz(d.act_dtype);
   dg_status st;
   if ((st = launch_rmsnorm(c->x, c->h, T, d.d_model, d.act_dtype, s))) return st;
-  if ((st = launch_gemm(c->h, c->wqkv[l], c->qkv, T, qkv_w, d.d_model, d.act_dtype, d.act_dtype,
-                        kStore, s)))
+  if ((st = launch_gemm(c->h, c->wqkv[l], c->qkv, T, qkv_w, d.d_model, d.act_dtype,
+                        d.weight_layout, d.act_dtype, kStore, s)))
     return st;
   char* qkv = static_cast<char*>(c->qkv);
   if (kv_only)
@@ -186,17 +191,19 @@ dg_status layer(dg_ctx* c, int l, int B, int n, void* kc, void* vc, int Tmax,
               d.n_heads, d.n_kv_heads, d.head_dim, Tmax, mode, d.rope_theta, d.act_dtype,
               c->attn_out};
   if ((st = launch_attention(aa, c->attn_ws, s))) return st;
-  if ((st = launch_gemm(c->attn_out, c->wo[l], c->x, T, d.d_model, qd, d.act_dtype, DG_F32,
-                        kAccumulateF32, s)))
+  if ((st = launch_gemm(c->attn_out, c->wo[l], c->x, T, d.d_model, qd, d.act_dtype,
+                        d.weight_layout, DG_F32, kAccumulateF32, s)))
     return st;
   if ((st = launch_rmsnorm(c->x, c->h, T, d.d_model, d.act_dtype, s))) return st;
-  if ((st = launch_gemm(c->h, c->wr[l], c->router, T, d.n_experts, d.d_model, d.act_dtype, DG_F32,
-                        kStore, s)))
+  if ((st = launch_gemm(c->h, c->wr[l], c->router, T, d.n_experts, d.d_model, d.act_dtype,
+                        d.weight_layout, DG_F32, kStore, s)))
     return st;
-  if ((st = launch_moe_route(c->router, T, d.n_experts, d.top_k, c->topk_ids, c->gates,
+  const float* route_in = c->router_override.empty() ? c->router : c->router_override[l];
+  if ((st = launch_moe_route(route_in, T, d.n_experts, d.top_k, c->topk_ids, c->gates,
                              c->offsets, c->sorted_rows, c->moe_ws, s)))
     return st;
-  return launch_moe_ffn(c->h, d.act_dtype, c->wgu[l], c->wd[l], d.expert_dtype, c->sgu[l],
+  return launch_moe_ffn(c->h, d.act_dtype, c->wgu[l], c->wd[l], d.expert_dtype, d.weight_layout,
+                        c->sgu[l],
                         c->sd[l], c->topk_ids, c->gates, c->offsets, c->sorted_rows, T, d.d_model,
                         d.d_ff, d.n_experts, d.top_k, c->x, c->moe_ws, s);
 }
@@ -215,7 +222,7 @@ dg_status forward(dg_ctx* c, const int32_t* tokens, int B, int n, int l0, int l1
   if (logits) {
     if ((st = launch_rmsnorm(c->x, c->h, B * n, d.d_model, d.act_dtype, s))) return st;
     if ((st = launch_gemm(c->h, c->lm, logits, B * n, d.vocab, d.d_model, d.act_dtype,
-                          d.act_dtype, kStore, s)))
+                          d.weight_layout, d.act_dtype, kStore, s)))
       return st;
   }
   return DG_OK;
@@ -261,6 +268,8 @@ dg_status check_run(dg_ctx* c, int B, int n, void* const* kcs, void* const* vcs,
   DG_CHECK_SHAPE(B > 0 && B <= c->max_batch, std::string(fn) + ": B outside [1, max_batch]");
   DG_CHECK_SHAPE(n > 0 && n <= c->max_tokens, std::string(fn) + ": n outside [1, max_tokens]");
   DG_CHECK_SHAPE(Tmax >= n, std::string(fn) + ": Tmax smaller than the block");
+  DG_CHECK_SHAPE(c->router_override.empty() || B * n <= c->router_override_tokens,
+                 std::string(fn) + ": more tokens than the router override holds");
   return DG_OK;
 }
 
@@ -344,6 +353,23 @@ dg_status dg_ctx_destroy(dg_ctx* ctx) {
 dg_status dg_ctx_set_graphs(dg_ctx* ctx, int use_graphs) {
   DG_CHECK_ARG(ctx != nullptr, "dg_ctx_set_graphs: ctx is null");
   ctx->use_graphs = use_graphs != 0;
+  return DG_OK;
+}
+
+dg_status dg_ctx_set_router_override(dg_ctx* ctx, const float* const* logits, int n_tokens) {
+  set_error("");
+  DG_CHECK_ARG(ctx != nullptr, "dg_ctx_set_router_override: ctx is null");
+  ctx->router_override.clear();
+  ctx->router_override_tokens = 0;
+  // captured graphs embed the routing inputs
+  for (auto& kv : ctx->graphs) (void)hipGraphExecDestroy(kv.second);
+  ctx->graphs.clear();
+  if (!logits) return DG_OK;
+  DG_CHECK_SHAPE(n_tokens > 0, "dg_ctx_set_router_override: n_tokens must be positive");
+  for (int l = 0; l < ctx->d.n_layers; ++l)
+    DG_CHECK_ARG(logits[l] != nullptr, "dg_ctx_set_router_override: null layer pointer");
+  ctx->router_override.assign(logits, logits + ctx->d.n_layers);
+  ctx->router_override_tokens = n_tokens;
   return DG_OK;
 }
 

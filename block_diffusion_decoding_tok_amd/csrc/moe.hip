@@ -202,7 +202,7 @@ size_t moe_ffn_workspace_bytes(int T, int D, int I, int E, int k, int x_dtype) {
 constexpr int kMoeNR = 3;      // register ring depth (chunks of 64 k), one-wave kernels
 constexpr int kMoeWaveRT = 8;  // one-wave kernels: 8 tiles of 16 rows per wave
 
-template <bool FP8>
+template <bool FP8, bool TILED>
 static dg_status launch_grouped(const void* x, const void* wgu, const void* wd, const float* sgu,
                                 const float* sd, const float* gates, const int32_t* offsets,
                                 const int32_t* sorted_rows, int T, int D, int I, int E, int k,
@@ -227,10 +227,10 @@ static dg_status launch_grouped(const void* x, const void* wgu, const void* wd, 
   if (small) {
     g.n_tiles_x = I / (8 * kMoeWaveRT);
     g.n_tiles_total = g.n_tiles_x * max_ty;
-    gemm_wave_kernel<kMoeWaveRT, kMoeNR, FP8, kGateUp>
+    gemm_wave_kernel<kMoeWaveRT, kMoeNR, FP8, kGateUp, TILED>
         <<<(g.n_tiles_total + 7) / 8 * 8, 64, 0, stream>>>(g);
   } else
-    gemm_stream_kernel<2, kMoeTB, kMoeKS, kMoePF, FP8, kGateUp><<<gwg, 256, 0, stream>>>(g);
+    gemm_stream_kernel<2, kMoeTB, kMoeKS, kMoePF, FP8, kGateUp, TILED><<<gwg, 256, 0, stream>>>(g);
   DG_LAUNCH_CHECK();
   GemmArgs d{};
   d.W = wd; d.w_group_stride = static_cast<int64_t>(D) * I;
@@ -247,16 +247,16 @@ static dg_status launch_grouped(const void* x, const void* wgu, const void* wd, 
   if (small) {
     d.n_tiles_x = D / (16 * kMoeWaveRT);
     d.n_tiles_total = d.n_tiles_x * max_ty;
-    gemm_wave_kernel<kMoeWaveRT, kMoeNR, FP8, kDown>
+    gemm_wave_kernel<kMoeWaveRT, kMoeNR, FP8, kDown, TILED>
         <<<(d.n_tiles_total + 7) / 8 * 8, 64, 0, stream>>>(d);
   } else
-    gemm_stream_kernel<2, kMoeTB, kMoeKS, kMoePF, FP8, kDown><<<dwg, 256, 0, stream>>>(d);
+    gemm_stream_kernel<2, kMoeTB, kMoeKS, kMoePF, FP8, kDown, TILED><<<dwg, 256, 0, stream>>>(d);
   DG_LAUNCH_CHECK();
   return DG_OK;
 }
 
 dg_status launch_moe_ffn(const void* x, int x_dtype, const void* w_gate_up, const void* w_down,
-                         int w_dtype, const float* s_gate_up, const float* s_down,
+                         int w_dtype, int w_layout, const float* s_gate_up, const float* s_down,
                          const int32_t* topk_ids, const float* gates, const int32_t* offsets,
                          const int32_t* sorted_rows, int T, int D, int I, int E, int k, float* y,
                          void* ws, hipStream_t stream) {
@@ -283,14 +283,19 @@ dg_status launch_moe_ffn(const void* x, int x_dtype, const void* w_gate_up, cons
     DG_LAUNCH_CHECK();
     return DG_OK;
   }
+  const bool tiled = w_layout == DG_LAYOUT_TILED;
+  bf16_t* hb = static_cast<bf16_t*>(h);
+  bf16_t* yb = static_cast<bf16_t*>(y_slot);
   if (w_dtype == DG_FP8_E4M3)
-    st = launch_grouped<true>(x, w_gate_up, w_down, s_gate_up, s_down, gates, offsets,
-                              sorted_rows, T, D, I, E, k, static_cast<bf16_t*>(h),
-                              static_cast<bf16_t*>(y_slot), stream);
+    st = tiled ? launch_grouped<true, true>(x, w_gate_up, w_down, s_gate_up, s_down, gates, offsets,
+                                            sorted_rows, T, D, I, E, k, hb, yb, stream)
+               : launch_grouped<true, false>(x, w_gate_up, w_down, s_gate_up, s_down, gates, offsets,
+                                             sorted_rows, T, D, I, E, k, hb, yb, stream);
   else
-    st = launch_grouped<false>(x, w_gate_up, w_down, nullptr, nullptr, gates, offsets,
-                               sorted_rows, T, D, I, E, k, static_cast<bf16_t*>(h),
-                               static_cast<bf16_t*>(y_slot), stream);
+    st = tiled ? launch_grouped<false, true>(x, w_gate_up, w_down, nullptr, nullptr, gates, offsets,
+                                             sorted_rows, T, D, I, E, k, hb, yb, stream)
+               : launch_grouped<false, false>(x, w_gate_up, w_down, nullptr, nullptr, gates, offsets,
+                                              sorted_rows, T, D, I, E, k, hb, yb, stream);
   if (st != DG_OK) return st;
   combine_kernel<bf16_t><<<cblocks, 256, 0, stream>>>(static_cast<const bf16_t*>(y_slot), T, D, k, y);
   DG_LAUNCH_CHECK();

@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(_PKG, "libdg.so")
 
 DG_F32, DG_BF16, DG_FP8_E4M3 = 0, 1, 2
 DG_MASK_CANVAS, DG_MASK_CAUSAL = 0, 1
+DG_LAYOUT_ROWMAJOR, DG_LAYOUT_TILED = 0, 1
 STATUS_NONFINITE_LOGITS = 1
 
 _STATUS = {0: "DG_OK", -1: "DG_ERR_INVALID_ARG", -2: "DG_ERR_SHAPE",
@@ -51,7 +52,7 @@ class dg_model_dims(C.Structure):
                 ("head_dim", C.c_int32), ("n_experts", C.c_int32),
                 ("top_k", C.c_int32), ("d_ff", C.c_int32), ("vocab", C.c_int32),
                 ("rope_theta", C.c_float), ("act_dtype", C.c_int32),
-                ("expert_dtype", C.c_int32)]
+                ("expert_dtype", C.c_int32), ("weight_layout", C.c_int32)]
 
 
 class dg_model_weights(C.Structure):
@@ -80,13 +81,14 @@ _SIGS = {
     "dg_moe_route_workspace_size": (_SZ, [_I, _I, _I]),
     "dg_moe_route": (_I, [_VP, _I, _I, _I, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
     "dg_moe_ffn_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I]),
-    "dg_moe_ffn": (_I, [_VP, _I, _VP, _VP, _I, _VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I,
-                        _I, _VP, _VP, _SZ, _VP]),
+    "dg_moe_ffn": (_I, [_VP, _I, _VP, _VP, _I, _I, _VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _I,
+                        _I, _I, _VP, _VP, _SZ, _VP]),
     "dg_ctx_workspace_size": (_SZ, [C.POINTER(dg_model_dims), _I, _I]),
     "dg_ctx_create": (_I, [C.POINTER(_VP), C.POINTER(dg_model_dims),
                            C.POINTER(dg_model_weights), _I, _I, _VP, _SZ]),
     "dg_ctx_destroy": (_I, [_VP]),
     "dg_ctx_set_graphs": (_I, [_VP, _I]),
+    "dg_ctx_set_router_override": (_I, [_VP, C.POINTER(_VP), _I]),
     "dg_model_forward": (_I, [_VP, _VP, _VP, _I, _I, _I, _I, C.POINTER(_VP), C.POINTER(_VP),
                               _I, _VP, _I, _VP, _VP]),
     "dg_prefill": (_I, [_VP, _VP, _I, _I, C.POINTER(_VP), C.POINTER(_VP), _I, _VP, _VP]),
@@ -94,6 +96,7 @@ _SIGS = {
                               C.POINTER(_VP), _I, _VP, _VP, _VP, _VP]),
     "dg_fill_normal": (_I, [_VP, _I, _SZ, _F, _U64, C.c_uint32, _VP]),
     "dg_quantize_fp8_rows": (_I, [_VP, _VP, _VP, _I64, _I, _VP]),
+    "dg_pack_weights": (_I, [_VP, _VP, _I64, _I, _I, _I, _VP]),
     "dg_philox": (_I, [_VP, _I64, _U64, _VP, _VP]),
     "dg_gumbel": (_I, [_VP, _I64, _VP, _VP]),
 }
@@ -271,17 +274,20 @@ def dg_moe_route(router_logits, k, topk_ids=None, gates=None, expert_offsets=Non
 
 
 def dg_moe_ffn(x, w_gate_up, w_down, s_gate_up, s_down, topk_ids, gates, expert_offsets,
-               sorted_rows, y, ws=None, stream=None):
+               sorted_rows, y, ws=None, stream=None, w_layout=DG_LAYOUT_ROWMAJOR, E=None, I=None):
+    """w_gate_up / w_down: [E, 2I, D] / [E, D, I] row-major, or the same bytes
+    in DG_LAYOUT_TILED (then pass E and I, or keep the logical shape)."""
     T, D = x.shape
-    E, I2, _ = w_gate_up.shape
-    I = I2 // 2
+    if E is None:
+        E, I2 = w_gate_up.shape[0], w_gate_up.shape[1]
+        I = I2 // 2
     k = topk_ids.shape[1]
     xd = _dtype_code(x)
     wd = _dtype_code(w_gate_up)
     if ws is None:
         ws = _workspace(lib().dg_moe_ffn_workspace_size(T, D, I, E, k, xd), x.device)
     _check(lib().dg_moe_ffn(
-        _dev(x, "x"), xd, _dev(w_gate_up, "w_gate_up"), _dev(w_down, "w_down"), wd,
+        _dev(x, "x"), xd, _dev(w_gate_up, "w_gate_up"), _dev(w_down, "w_down"), wd, int(w_layout),
         _dev(s_gate_up, "s_gate_up", (torch.float32,)), _dev(s_down, "s_down", (torch.float32,)),
         _dev(topk_ids, "topk_ids", (torch.int32,)), _dev(gates, "gates", (torch.float32,)),
         _dev(expert_offsets, "expert_offsets", (torch.int32,)),
@@ -298,12 +304,14 @@ class DGModel:
     workspace outlive the context."""
 
     def __init__(self, dims, weights, max_batch, max_tokens, act_dtype, expert_dtype,
-                 rope_theta=10000.0, device="cuda"):
+                 rope_theta=10000.0, device="cuda", weight_layout=DG_LAYOUT_ROWMAJOR):
         self.dims = dims
         self.weights = weights
         nl = dims.NL
         self.cdims = dg_model_dims(nl, dims.D, dims.Hq, dims.Hkv, dims.dh, dims.E, dims.k,
-                                   dims.I, dims.V, rope_theta, act_dtype, expert_dtype)
+                                   dims.I, dims.V, rope_theta, act_dtype, expert_dtype,
+                                   weight_layout)
+        self._override = None
         self._arrays = {n: _ptr_array([weights.get(f"{n}.{l}") for l in range(nl)])
                         for n in ("wqkv", "wo", "wr", "wgu", "wd", "sgu", "sd")}
         a = self._arrays
@@ -330,6 +338,17 @@ class DGModel:
 
     def set_graphs(self, on):
         _check(lib().dg_ctx_set_graphs(self.ctx, int(bool(on))))
+
+    def set_router_override(self, logits_per_layer):
+        """Route with the given per-layer f32 [n_tokens, E] logits (None: the
+        model's own routing)."""
+        if logits_per_layer is None:
+            self._override = None
+            _check(lib().dg_ctx_set_router_override(self.ctx, None, 0))
+            return
+        self._override = (list(logits_per_layer), _ptr_array(logits_per_layer))
+        _check(lib().dg_ctx_set_router_override(self.ctx, self._override[1],
+                                                logits_per_layer[0].shape[0]))
 
 
 def dg_model_forward(model, tokens, x, B, n, layer_begin, layer_end, k_caches, v_caches,
@@ -366,6 +385,19 @@ def dg_fill_normal(dst, std, seed, stream_id, stream=None):
     _check(lib().dg_fill_normal(_dev(dst, "dst", (torch.float32, torch.bfloat16)),
                                 _dtype_code(dst), dst.numel(), float(std), int(seed),
                                 int(stream_id), _stream(stream)))
+
+
+def dg_pack_weights(src, dst=None, stream=None):
+    """Row-major [.., N, K] (bf16 or 1-byte) -> DG_LAYOUT_TILED, same shape."""
+    if dst is None:
+        dst = torch.empty_like(src)
+    N, K = src.shape[-2], src.shape[-1]
+    groups = src.numel() // (N * K)
+    code = DG_BF16 if src.dtype == torch.bfloat16 else DG_FP8_E4M3
+    _check(lib().dg_pack_weights(_dev(src, "src", (torch.bfloat16, torch.uint8)),
+                                 _dev(dst, "dst", (torch.bfloat16, torch.uint8)), groups, N, K,
+                                 code, _stream(stream)))
+    return dst
 
 
 def dg_quantize_fp8_rows(src, q, scale, stream=None):

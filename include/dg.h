@@ -47,6 +47,18 @@ typedef enum { DG_F32 = 0, DG_BF16 = 1, DG_FP8_E4M3 = 2 /* OCP e4m3fn */ } dg_dt
 
 typedef enum { DG_MASK_CANVAS = 0, DG_MASK_CAUSAL = 1 } dg_mask_mode;
 
+/* Weight layouts for [G, N, K] weight tensors (G groups, e.g. experts).
+ *   DG_LAYOUT_ROWMAJOR  element (g, n, k) at (g * N + n) * K + k.
+ *   DG_LAYOUT_TILED     blocks of 16 rows x 64 k, block (g, n / 16, k / 64) at
+ *                       ((g * N / 16 + n / 16) * K / 64 + k / 64) * 1024 elements;
+ *                       inside a block, with r = n % 16, q = (k % 64) / 16:
+ *                       1-byte types: lane = r + 16 q holds k % 16 at lane * 16;
+ *                       2-byte types: half h = (k % 16) / 8 at h * 512 + lane * 8.
+ *                       It is the order in which a 64-lane wave loads an MFMA
+ *                       A-operand tile, so every load reads 1 KB contiguous.
+ *                       Needs N % 16 == 0 and K % 64 == 0 (dg_pack_weights). */
+typedef enum { DG_LAYOUT_ROWMAJOR = 0, DG_LAYOUT_TILED = 1 } dg_layout;
+
 /* Device status-word bits. */
 #define DG_STATUS_NONFINITE_LOGITS 1
 
@@ -175,7 +187,8 @@ dg_status dg_moe_route(const float* router_logits, int T, int E, int k, int32_t*
  * FFN_e(u) = (GELU_erf(u Wg_e^T) * (u Wu_e^T)) Wd_e^T, summed in slot order.
  *   x          [T, D] DG_BF16 (with DG_BF16 / DG_FP8_E4M3 weights) or DG_F32
  *              (with DG_F32 weights)
- *   w_gate_up  [E, 2I, D]: rows 0..I-1 gate, I..2I-1 up;  w_down [E, D, I]
+ *   w_gate_up  [E, 2I, D]: rows 0..I-1 gate, I..2I-1 up;  w_down [E, D, I];
+ *              in w_layout (DG_LAYOUT_TILED only with DG_BF16 / DG_FP8_E4M3)
  *   s_gate_up  [E, 2I], s_down [E, D] f32 per-row scales (DG_FP8_E4M3 only;
  *              the weight is byte value * scale); ignored otherwise
  *   routing tables as produced by dg_moe_route; y [T, D] f32, accumulated.
@@ -183,7 +196,7 @@ dg_status dg_moe_route(const float* router_logits, int T, int E, int k, int32_t*
  * ws >= dg_moe_ffn_workspace_size(T, D, I, E, k, x_dtype). */
 size_t dg_moe_ffn_workspace_size(int T, int D, int I, int E, int k, int x_dtype);
 dg_status dg_moe_ffn(const void* x, int x_dtype, const void* w_gate_up, const void* w_down,
-                     int w_dtype, const float* s_gate_up, const float* s_down,
+                     int w_dtype, int w_layout, const float* s_gate_up, const float* s_down,
                      const int32_t* topk_ids, const float* gates, const int32_t* expert_offsets,
                      const int32_t* sorted_rows, int T, int D, int I, int E, int k, float* y,
                      void* ws, size_t ws_bytes, void* stream);
@@ -194,9 +207,11 @@ dg_status dg_moe_ffn(const void* x, int x_dtype, const void* w_gate_up, const vo
  * -> router -> top-k MoE + residual; final RMSNorm -> untied LM head.  Dense
  * weights and activations use act_dtype (DG_BF16 or DG_F32); experts use
  * expert_dtype (DG_BF16, DG_FP8_E4M3, or DG_F32 with DG_F32 activations).
- * The residual stream is f32.  Weight layouts: emb, lm_head [V, D]; wqkv
+ * The residual stream is f32.  Weight shapes: emb, lm_head [V, D]; wqkv
  * [(Hq + 2 Hkv) dh, D] (rows q | k | v); wo [D, Hq dh]; wr [E, D]; experts as
- * in dg_moe_ffn.  KV caches: per layer [B, Hkv, Tmax, dh] in act_dtype.
+ * in dg_moe_ffn.  emb is always row-major; every other weight is in
+ * weight_layout (DG_LAYOUT_TILED only with bf16 activations).  KV caches: per
+ * layer [B, Hkv, Tmax, dh] in act_dtype.
  */
 typedef struct {
   int32_t n_layers, d_model, n_heads, n_kv_heads, head_dim;
@@ -204,6 +219,7 @@ typedef struct {
   float rope_theta;
   int32_t act_dtype;
   int32_t expert_dtype;
+  int32_t weight_layout;
 } dg_model_dims;
 
 typedef struct {
@@ -230,6 +246,14 @@ dg_status dg_ctx_create(dg_ctx** out, const dg_model_dims* dims, const dg_model_
 dg_status dg_ctx_destroy(dg_ctx* ctx);
 /* use_graphs != 0 (default): dg_denoise_block replays a captured hipGraph. */
 dg_status dg_ctx_set_graphs(dg_ctx* ctx, int use_graphs);
+/* Benchmarking hook: route every forward with caller-supplied router logits
+ * instead of the router projection's output (the projection still runs).
+ * logits: host array [n_layers] of device pointers to f32 [n_tokens, E]; a
+ * forward over B * n tokens uses the first B * n rows (requires B * n <=
+ * n_tokens).  NULL restores the model's own routing.  Lets a random-init model
+ * run with a stated routing distribution (e.g. a planted hot-expert skew)
+ * instead of the one its random weights produce. */
+dg_status dg_ctx_set_router_override(dg_ctx* ctx, const float* const* logits, int n_tokens);
 
 /* dg_model_forward: one forward over n tokens per row at cache positions
  * [P_b, P_b + n).  If tokens != NULL the residual x is first set to the
@@ -270,6 +294,10 @@ dg_status dg_fill_normal(void* dst, int dtype, size_t n, float std, uint64_t see
  * q = round-to-nearest-even(src / scale) saturated to +-448. */
 dg_status dg_quantize_fp8_rows(const float* src, uint8_t* q, float* scale, int64_t rows,
                                int cols, void* stream);
+/* Repack weights [groups, N, K] from row-major into DG_LAYOUT_TILED (dst must
+ * not alias src).  dtype: DG_BF16 or DG_FP8_E4M3 (any 1-byte type). */
+dg_status dg_pack_weights(const void* src, void* dst, int64_t groups, int N, int K, int dtype,
+                          void* stream);
 /* Philox4x32-10 words for n counters: out[4i..4i+3] = Philox(ctr[4i..4i+3], seed). */
 dg_status dg_philox(const uint32_t* counters, int64_t n, uint64_t seed, uint32_t* out,
                     void* stream);

@@ -54,11 +54,13 @@ class TinyModel:
     theta: float = 10000.0
 
 
-def layer_forward(m, lw, x, k_cache, v_cache, P, mode, trace=None):
+def layer_forward(m, lw, x, k_cache, v_cache, P, mode, trace=None, router_logits=None):
     """One decoder layer over x [B, n, D] at cache positions [P_b, P_b + n).
 
     k_cache, v_cache [B, Hkv, Tmax, dh] are updated in place with the block's
-    rotated keys and values.  Returns the new residual stream."""
+    rotated keys and values.  ``router_logits`` [B * n, E], when given, replace
+    the router projection's output (a stated routing distribution for a
+    random-init model).  Returns the new residual stream."""
     B, n, D = x.shape
     qd, kd = m.Hq * m.dh, m.Hkv * m.dh
     h = rmsnorm(x)
@@ -77,6 +79,8 @@ def layer_forward(m, lw, x, k_cache, v_cache, P, mode, trace=None):
     x = x + o @ np.asarray(lw["wo"], np.float64).T
     h2 = rmsnorm(x).reshape(B * n, D)
     r = h2 @ np.asarray(lw["wr"], np.float64).T
+    if router_logits is not None:
+        r = np.asarray(router_logits, np.float64)
     ids, gates, _, _ = moe_route(r, m.k)
     y = moe_ffn(h2, lw["w_gate_up"], lw["w_down"], ids, gates)
     if trace is not None:

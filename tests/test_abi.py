@@ -77,20 +77,25 @@ def test_attention_and_moe_reject_bad_shapes(lib):
     # k > E
     assert lib.dg_moe_route(f, 10, 4, 5, f, f, f, f, f, 0, None) == -2
     # fp8 without scales
-    assert lib.dg_moe_ffn(f, dg.DG_BF16, f, f, dg.DG_FP8_E4M3, None, None, f, f, f, f,
+    assert lib.dg_moe_ffn(f, dg.DG_BF16, f, f, dg.DG_FP8_E4M3, 0, None, None, f, f, f, f,
                           256, 2816, 704, 128, 8, f, f, 1 << 30, None) == -1
+    # tiled layout needs bf16 activations
+    assert lib.dg_moe_ffn(f, dg.DG_F32, f, f, dg.DG_F32, 1, None, None, f, f, f, f,
+                          48, 64, 128, 4, 2, f, f, 1 << 30, None) == -1
+    # pack: K must be a multiple of 64
+    assert lib.dg_pack_weights(f, C.c_void_p(512), 1, 16, 100, dg.DG_BF16, None) == -2
     # MFMA path shape constraint
-    assert lib.dg_moe_ffn(f, dg.DG_BF16, f, f, dg.DG_BF16, None, None, f, f, f, f,
+    assert lib.dg_moe_ffn(f, dg.DG_BF16, f, f, dg.DG_BF16, 0, None, None, f, f, f, f,
                           256, 2800, 704, 128, 8, f, f, 1 << 30, None) == -2
 
 
 def test_ctx_validation(lib):
     dims = dg.dg_model_dims(30, 2816, 16, 8, 128, 128, 8, 704, 262144, 10000.0,
-                            dg.DG_BF16, dg.DG_FP8_E4M3)
+                            dg.DG_BF16, dg.DG_FP8_E4M3, dg.DG_LAYOUT_TILED)
     n = lib.dg_ctx_workspace_size(C.byref(dims), 1, 256)
     assert n > 256 * 262144 * 2           # holds at least the logits
     bad = dg.dg_model_dims(30, 2816, 16, 8, 64, 128, 8, 704, 262144, 10000.0,
-                           dg.DG_BF16, dg.DG_FP8_E4M3)
+                           dg.DG_BF16, dg.DG_FP8_E4M3, 0)
     assert lib.dg_ctx_workspace_size(C.byref(bad), 1, 256) == 0
     w = dg.dg_model_weights()
     h = C.c_void_p()

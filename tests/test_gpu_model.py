@@ -19,6 +19,7 @@ from block_diffusion_decoding_tok_amd.inputs import (TINY_DIMS, ModelDims, model
                                                      prompt_ids)
 from oracle import SamplerCfg, prefill, denoise_block, layer_forward, rmsnorm
 from oracle.attention import CANVAS
+from block_diffusion_decoding_tok_amd.inputs import router_logits_skewed
 from tests.util import oracle_model, empty_caches, rel_err_rows, to_f64
 
 pytestmark = pytest.mark.gpu
@@ -114,17 +115,42 @@ def test_graph_replay_matches_eager():
 FULL_LAYER = ModelDims(NL=2, D=2816, Hq=16, Hkv=8, dh=128, E=128, k=8, I=704, V=4096)
 
 
-@pytest.fixture(scope="module")
-def full_layers():
+def _packed(w):
+    """Device copies of the weights with every weight but the embedding in
+    the tiled layout."""
+    out = {}
+    for k, v in w.items():
+        v = v.to(DEV)
+        if k != "emb" and not k.startswith(("sgu", "sd")):
+            v = dg.dg_pack_weights(v)
+        out[k] = v
+    return out
+
+
+@pytest.fixture(scope="module", params=["rowmajor", "tiled"])
+def full_layers(request):
     d = FULL_LAYER
     w = model_weights(d, seed=3, expert_dtype="fp8", dense_dtype="bf16")
-    model = dg.DGModel(d, _dev_weights(w), 4, 256, dg.DG_BF16, dg.DG_FP8_E4M3)
+    if request.param == "tiled":
+        model = dg.DGModel(d, _packed(w), 4, 256, dg.DG_BF16, dg.DG_FP8_E4M3,
+                           weight_layout=dg.DG_LAYOUT_TILED)
+    else:
+        model = dg.DGModel(d, _dev_weights(w), 4, 256, dg.DG_BF16, dg.DG_FP8_E4M3)
     return d, w, model
 
 
-@pytest.mark.parametrize("B,P0", [(1, 256), (4, 512)])
-def test_full_width_layers_teacher_forced(full_layers, B, P0):
+@pytest.mark.parametrize("B,P0,planted", [(1, 256, False), (4, 512, False), (1, 256, True)])
+def test_full_width_layers_teacher_forced(full_layers, B, P0, planted):
+    """planted: the router override supplies N(0,1) + hot-expert-skew logits
+    (the stated MoE routing) instead of the random router's."""
     d, w, model = full_layers
+    override = None
+    if planted:
+        override = [torch.from_numpy(router_logits_skewed(B * 256, d.E, d.k, seed=40 + l)[0])
+                    for l in range(d.NL)]
+        model.set_router_override([o.to(DEV) for o in override])
+    else:
+        model.set_router_override(None)
     m = oracle_model(d, w)
     Tmax = P0 + 256
     kc, vc = _caches(d, B, Tmax, torch.bfloat16)
@@ -144,7 +170,8 @@ def test_full_width_layers_teacher_forced(full_layers, B, P0):
         torch.cuda.synchronize()
         x_out = x.cpu().double().numpy().reshape(B, 256, d.D)
         trace = []
-        ref = layer_forward(m, m.layers[l], x_in, cache_k, cache_v, P_host, CANVAS, trace=trace)
+        ref = layer_forward(m, m.layers[l], x_in, cache_k, cache_v, P_host, CANVAS, trace=trace,
+                            router_logits=None if override is None else override[l].numpy())
         got_d = (x_out - x_in).reshape(-1, d.D)
         ref_d = (ref - x_in).reshape(-1, d.D)
         err = np.linalg.norm(got_d - ref_d, axis=1) / np.linalg.norm(ref_d, axis=1)
@@ -159,6 +186,8 @@ def test_full_width_layers_teacher_forced(full_layers, B, P0):
               f"(gaps {np.sort(gap[bad])[:8]}), max err of the others {err[~bad].max():.3g}")
         assert np.all(gap[bad] < 2e-2), (l, gap[bad].max())
         assert bad.mean() < 0.1, (l, bad.mean())
+        if planted:                      # identical routing inputs: no exceptions
+            assert not bad.any()
         # the canvas K/V written by the device vs the oracle's (same inputs)
         got_k = kc[l].cpu().double().numpy()[:, :, P0:P0 + 256]
         assert rel_err_rows(got_k, cache_k[:, :, P0:P0 + 256]) < 3e-2

@@ -9,7 +9,7 @@ import torch
 from block_diffusion_decoding_tok_amd import dg
 from block_diffusion_decoding_tok_amd.inputs import moe_case
 from oracle.moe import moe_route, moe_ffn
-from tests.util import ExpertWeights, rel_err_rows, to_f64
+from tests.util import ExpertWeights, rel_err_rows, to_f64, pack_tiled
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -49,17 +49,20 @@ def test_route_planted_skew_share():
     assert (np.diff(off) > 0).all()          # every expert receives tokens
 
 
-def _ffn_case(case, k, sample=None):
+def _ffn_case(case, k, sample=None, tiled=False):
     T, D = case.x.shape
     ids, gates, off, rows = _check_route(case.router_logits, k)
     y0 = torch.randn(T, D, generator=torch.Generator().manual_seed(1)) * 0.1
     y = y0.clone().to(DEV)
     xd = case.x.to(DEV)
     wgu, wd = case.w_gate_up.to(DEV), case.w_down.to(DEV)
+    if tiled:
+        wgu, wd = dg.dg_pack_weights(wgu), dg.dg_pack_weights(wd)
     sgu, sd = case.s_gate_up.to(DEV), case.s_down.to(DEV)
     dg.dg_moe_ffn(xd, wgu, wd, sgu, sd, torch.from_numpy(ids).to(DEV),
                   torch.from_numpy(gates).to(DEV), torch.from_numpy(off).to(DEV),
-                  torch.from_numpy(rows).to(DEV), y)
+                  torch.from_numpy(rows).to(DEV), y,
+                  w_layout=dg.DG_LAYOUT_TILED if tiled else dg.DG_LAYOUT_ROWMAJOR)
     torch.cuda.synchronize()
     got = (y.cpu() - y0).double().numpy()
     sel = np.arange(T) if sample is None else sample
@@ -70,10 +73,25 @@ def _ffn_case(case, k, sample=None):
 
 
 @pytest.mark.parametrize("w_dtype", ["bf16", "fp8"])
-def test_moe_ffn_full_size_bs1(w_dtype):
+@pytest.mark.parametrize("tiled", [False, True])
+def test_moe_ffn_full_size_bs1(w_dtype, tiled):
     case = moe_case(T=256, w_dtype=w_dtype, seed=0)
-    err, _ = _ffn_case(case, 8)
+    err, _ = _ffn_case(case, 8, tiled=tiled)
     assert err < TOL[w_dtype], err
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.uint8])
+def test_pack_weights_layout(dtype):
+    g = torch.Generator().manual_seed(7)
+    if dtype == torch.uint8:
+        w = torch.randint(0, 256, (3, 48, 192), dtype=torch.uint8, generator=g)
+        ref = pack_tiled(w.numpy())
+        got = dg.dg_pack_weights(w.to(DEV)).cpu().numpy()
+    else:
+        w = torch.randn((3, 48, 192), generator=g).to(torch.bfloat16)
+        ref = pack_tiled(w.view(torch.int16).numpy())
+        got = dg.dg_pack_weights(w.to(DEV)).cpu().view(torch.int16).numpy()
+    assert np.array_equal(got, ref)
 
 
 def test_moe_ffn_full_size_bs4_fp8_sampled():
@@ -84,11 +102,20 @@ def test_moe_ffn_full_size_bs4_fp8_sampled():
 
 
 @pytest.mark.parametrize("w_dtype", ["bf16", "fp8"])
-def test_moe_ffn_ragged_small(w_dtype):
+@pytest.mark.parametrize("tiled", [False, True])
+def test_moe_ffn_ragged_small(w_dtype, tiled):
     """Few tokens, experts with 0 and > 64 tokens, several row tiles."""
     case = moe_case(T=70, D=256, E=6, k=2, I=128, w_dtype=w_dtype, seed=5, skew=False)
-    err, _ = _ffn_case(case, 2)
+    err, _ = _ffn_case(case, 2, tiled=tiled)
     assert err < TOL[w_dtype], err
+
+
+@pytest.mark.parametrize("tiled", [False, True])
+def test_moe_ffn_many_tokens_per_expert(tiled):
+    """Above 40 tokens per expert the LDS-staged 64-token tiles take over."""
+    case = moe_case(T=512, D=256, E=8, k=2, I=128, w_dtype="fp8", seed=6, skew=False)
+    err, _ = _ffn_case(case, 2, tiled=tiled)
+    assert err < TOL["fp8"], err
 
 
 def test_moe_ffn_f32_tiny():

@@ -89,3 +89,18 @@ class ExpertWeights:
 
 # value of every e4m3fn byte, from the oracle's decoder
 _FP8_TABLE = fp8_e4m3fn_decode(np.arange(256, dtype=np.uint8))
+
+
+def pack_tiled(w):
+    """Row-major [.., N, K] -> the DG_LAYOUT_TILED element order (numpy view of
+    the same shape): blocks of 16 rows x 64 k in wave-load order."""
+    a = np.asarray(w)
+    N, K = a.shape[-2], a.shape[-1]
+    G = a.size // (N * K)
+    x = a.reshape(G, N // 16, 16, K // 64, 4, 16)           # g, t, r, c, q, j
+    if a.itemsize == 1:
+        out = x.transpose(0, 1, 3, 4, 2, 5)                  # g, t, c, q, r, j
+    else:
+        x = x.reshape(G, N // 16, 16, K // 64, 4, 2, 8)     # g, t, r, c, q, h, j
+        out = x.transpose(0, 1, 3, 5, 4, 2, 6)               # g, t, c, h, q, r, j
+    return np.ascontiguousarray(out).reshape(a.shape)
