@@ -13,8 +13,9 @@ layers, canvas attention over the cache, MoE), the LM head and the sampler.
 hipGraph replay, commit included), bracketed by device synchronization.
 
 Printed: one JSON line with steps/s (value), canvas tok/s, ms per step,
-tok/s at 12 steps per block, the roofline of the dominant op (the MoE FFN),
-and the oracle's throughput on the host cores for a bounded sample.
+tok/s at 12 steps per block, the roofline of the dominant kernel (the experts'
+gate/up GEMM), and the oracle's throughput on the host cores for a bounded
+sample.
 """
 
 import argparse
@@ -82,32 +83,17 @@ def planted_router_logits(d, T, seed=100):
             for l in range(d.NL)]
 
 
-def moe_roofline(model_w, d, B, reps=20):
-    """HIP-event-timed dg_moe_ffn (gate/up + down + combine) on a middle
-    layer's experts for the canvas tokens with the planted routing;
-    algorithmic bytes = every expert's fp8 weights and scales read once + the
-    activations it must move."""
-    T = CANVAS * B
-    dev = "cuda"
-    layer = d.NL // 2
-    g = torch.Generator(device=dev).manual_seed(5)
-    logits = torch.from_numpy(router_logits_skewed(T, d.E, d.k, seed=7)[0]).to(dev)
-    x = (torch.randn((T, d.D), device=dev, generator=g)).to(torch.bfloat16)
-    y = torch.zeros((T, d.D), device=dev)
-    ids, gates, off, rows = dg.dg_moe_route(logits, d.k)
-    ws = torch.empty(dg.lib().dg_moe_ffn_workspace_size(T, d.D, d.I, d.E, d.k, dg.DG_BF16),
-                     dtype=torch.uint8, device=dev)
-    args = (x, model_w[f"wgu.{layer}"], model_w[f"wd.{layer}"], model_w[f"sgu.{layer}"],
-            model_w[f"sd.{layer}"], ids, gates, off, rows, y)
+def _graph_ms(fn, reps):
+    """Average device time of fn over reps calls captured into one graph and
+    replayed between two HIP events on the replay stream (host launch cost is
+    not counted)."""
     for _ in range(3):
-        dg.dg_moe_ffn(*args, ws=ws, w_layout=dg.DG_LAYOUT_TILED)
+        fn()
     torch.cuda.synchronize()
-    # the calls are captured into one graph and replayed between a pair of
-    # HIP events on the replay stream: host launch cost is not counted
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         for _ in range(reps):
-            dg.dg_moe_ffn(*args, ws=ws, w_layout=dg.DG_LAYOUT_TILED)
+            fn()
     graph.replay()
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -115,17 +101,82 @@ def moe_roofline(model_w, d, B, reps=20):
     graph.replay()
     end.record()
     torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / reps
+    return start.elapsed_time(end) / reps
+
+
+def moe_roofline(model_w, d, B, reps=20):
+    """The dominant kernel of the step, the experts' gate/up GEMM
+    (dg_moe_gate_up), timed on a middle layer's experts for the canvas tokens
+    with that layer's planted routing (every expert active).  Algorithmic
+    bytes: every expert's fp8 gate/up rows and their scales read once, the
+    token rows read once, the hidden rows written once, the routing tables.
+    The whole expert FFN (gate/up + down + combine) is timed beside it."""
+    T = CANVAS * B
+    dev = "cuda"
+    layer = d.NL // 2
     slots = T * d.k
-    w_bytes = d.E * 3 * d.I * d.D * 1 + d.E * (2 * d.I + d.D) * 4
-    # x read, h written + read (bf16), gate-weighted slot outputs written +
-    # read (bf16), y read + written (f32)
-    act_bytes = (T * d.D * 2 + slots * d.I * 2 * 2 + slots * d.D * 2 * 2 + T * d.D * 4 * 2)
-    algo = w_bytes + act_bytes
-    gbs = algo / (ms * 1e-3) / 1e9
-    return dict(op=f"moe_ffn (gate_up + down + combine kernels), layer {layer}, {T} tokens, "
-                   "fp8 experts, planted routing (all 128 experts active)", ms=ms,
-                algo_bytes=algo, gbs=gbs)
+    g = torch.Generator(device=dev).manual_seed(5)
+    logits = torch.from_numpy(router_logits_skewed(T, d.E, d.k, seed=100 + layer)[0]).to(dev)
+    x = (torch.randn((T, d.D), device=dev, generator=g)).to(torch.bfloat16)
+    y = torch.zeros((T, d.D), device=dev)
+    ids, gates, off, rows = dg.dg_moe_route(logits, d.k)
+    h = torch.empty((slots, d.I), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(dg.lib().dg_moe_ffn_workspace_size(T, d.D, d.I, d.E, d.k, dg.DG_BF16),
+                     dtype=torch.uint8, device=dev)
+    wgu, wd = model_w[f"wgu.{layer}"], model_w[f"wd.{layer}"]
+    sgu, sd = model_w[f"sgu.{layer}"], model_w[f"sd.{layer}"]
+    kw = dict(w_layout=dg.DG_LAYOUT_TILED, E=d.E, I=d.I)
+    ms_gu = _graph_ms(lambda: dg.dg_moe_gate_up(x, wgu, sgu, off, rows, d.k, h=h, **kw), reps)
+    ms_ffn = _graph_ms(lambda: dg.dg_moe_ffn(x, wgu, wd, sgu, sd, ids, gates, off, rows, y,
+                                             ws=ws, **kw), reps)
+    route_bytes = (d.E + 1) * 4 + slots * 4
+    gu_bytes = (d.E * 2 * d.I * d.D            # fp8 gate/up rows
+                + d.E * 2 * d.I * 4            # their scales
+                + T * d.D * 2                  # token rows (bf16)
+                + slots * d.I * 2              # hidden rows written (bf16)
+                + route_bytes)
+    # whole FFN: + down rows and scales, h read, gate-weighted slot rows
+    # written + read (bf16), y read + written (f32)
+    ffn_bytes = (gu_bytes + d.E * d.D * d.I + d.E * d.D * 4 + slots * d.I * 2
+                 + slots * d.D * 2 * 2 + T * d.D * 4 * 2 + slots * 4)
+    return dict(kernel=(f"gemm_wave_kernel (dg_moe_gate_up): experts of layer {layer}, {T} "
+                        "tokens, fp8 tiled weights, planted routing (all 128 experts active)"),
+                ms=ms_gu, algo_bytes=gu_bytes, gbs=gu_bytes / (ms_gu * 1e-3) / 1e9,
+                ffn_ms=ms_ffn, ffn_bytes=ffn_bytes, ffn_gbs=ffn_bytes / (ms_ffn * 1e-3) / 1e9)
+
+
+# Sources of the gate/up kernel: a traffic figure taken with byte counters
+# is used only while these files are unchanged.
+_KERNEL_SOURCES = ["block_diffusion_decoding_tok_amd/csrc/gemm_mfma.h",
+                   "block_diffusion_decoding_tok_amd/csrc/moe.hip",
+                   "block_diffusion_decoding_tok_amd/csrc/common.h"]
+_COUNTER_FILE = os.path.join(ROOT, "profiles", "moe_gate_up_counters_canvas256.md")
+
+
+def kernel_source_hash():
+    import hashlib
+    hsh = hashlib.sha256()
+    for f in _KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            hsh.update(fh.read())
+    return hsh.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the gate/up kernel from the committed counter
+    summary (FETCH_SIZE and WRITE_SIZE, scaled by a plain copy), or None when
+    there is none or the kernel's sources changed since it was taken."""
+    if not os.path.exists(_COUNTER_FILE):
+        return None
+    vals = {}
+    with open(_COUNTER_FILE) as fh:
+        for line in fh:
+            if line.startswith("- ") and ":" in line:
+                key, _, val = line[2:].partition(":")
+                vals[key.strip()] = val.strip().strip("`")
+    if vals.get("source_hash") != kernel_source_hash() or "traffic_bytes_per_launch" not in vals:
+        return None
+    return int(float(vals["traffic_bytes_per_launch"]))
 
 
 def copy_calibration(nbytes=1 << 28):
@@ -191,6 +242,8 @@ def main():
     ap.add_argument("--layers", type=int, default=FULL_DIMS.NL)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-roofline", action="store_true")
+    ap.add_argument("--no-natural", action="store_true",
+                    help="skip the secondary timing with the random router's own routing")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 256 MiB device copy (scale for byte counters)")
     ap.add_argument("--steps48", action="store_true",
@@ -250,7 +303,7 @@ def main():
         print(f"[bench] setup {time.perf_counter() - t_setup:.1f} s; timing {n_blocks} blocks "
               f"x {a.block_steps} steps, batch {B}", file=sys.stderr, flush=True)
         # the model's own routing (random router: few experts after layer 0)
-        elapsed_natural = timed(n_blocks, cfg)
+        elapsed_natural = None if a.no_natural else timed(n_blocks, cfg)
         # the stated routing: N(0,1) + planted skew, every expert active
         model.set_router_override(planted_router_logits(d, CANVAS * B))
         elapsed = timed(n_blocks, cfg)
@@ -287,19 +340,25 @@ def main():
                    "block_steps": a.block_steps, "parallelism": "single GPU"},
         "canvas_tok_per_s": round(steps_per_s * CANVAS * B, 1),
         "tok_per_s_at_block_steps": round(n_blocks * CANVAS * B / elapsed, 1),
-        "natural_routing": {"steps_per_s": round(a.steps / elapsed_natural, 3),
-                            "ms_per_step": round(1e3 * elapsed_natural / a.steps, 3),
-                            "note": "the random-init router's own top-8 (concentrated on a "
-                                    "few experts after layer 0, so fewer expert bytes move)"},
     }
+    if elapsed_natural is not None:
+        out["natural_routing"] = {
+            "steps_per_s": round(a.steps / elapsed_natural, 3),
+            "ms_per_step": round(1e3 * elapsed_natural / a.steps, 3),
+            "note": "the random-init router's own top-8 (concentrated on a few experts after "
+                    "layer 0, so fewer expert bytes move)"}
     if t48 is not None:
         out["tok_per_s_at_48"] = round(4 * CANVAS * B / t48, 1)
     if roof is not None:
         out["roofline"] = {"bound": "hbm", "achieved": round(roof["gbs"], 1), "peak": HBM_PEAK_GBS,
                            "unit": "GB/s", "frac": round(roof["gbs"] / HBM_PEAK_GBS, 4),
-                           "traffic": None, "kernel": roof["op"],
+                           "traffic": measured_traffic(), "kernel": roof["kernel"],
                            "ms_per_launch": round(roof["ms"], 4),
-                           "algorithmic_bytes": int(roof["algo_bytes"])}
+                           "algorithmic_bytes": int(roof["algo_bytes"]),
+                           "kernel_source_hash": kernel_source_hash(),
+                           "moe_ffn": {"ms_per_launch": round(roof["ffn_ms"], 4),
+                                       "algorithmic_bytes": int(roof["ffn_bytes"]),
+                                       "achieved_gbs": round(roof["ffn_gbs"], 1)}}
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(d, B, PROMPT)
         out["cpu_baseline"]["value"] = float(f"{out['cpu_baseline']['value']:.4g}")

@@ -59,7 +59,7 @@ struct GemmArgs {
   int n_tiles_x;            // row tiles per group
   int n_tiles_y;            // token-tile slots
   int n_tiles_total;        // logical workgroups (x * y)
-  int y_fastest;            // logical order: token tiles of the same rows adjacent
+  int y_fastest;            // dense: logical order with token tiles of the same rows adjacent
 };
 
 __device__ __forceinline__ float gelu_erf(float x) {
@@ -138,15 +138,16 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g4 = lane >> 4;
-  const int logical = xcd_logical_tile(blockIdx.x, gridDim.x);
-  if (logical >= a.n_tiles_total) return;
-  // row tile within the group / token-tile slot
-  const int tx = a.y_fastest ? logical / a.n_tiles_y : logical % a.n_tiles_x;
-  const int ty = a.y_fastest ? logical % a.n_tiles_y : logical / a.n_tiles_x;
 
-  // ---- which group / token range this tile covers
+  // ---- row tile within the group (tx), token tile (ty), and which group /
+  // token range the tile covers
+  int tx = 0, ty = 0;
   int grp = 0, m0 = 0, m_count = 0, base_pos = 0;
   if (MODE == kDense) {
+    const int logical = xcd_logical_tile(blockIdx.x, gridDim.x);
+    if (logical >= a.n_tiles_total) return;
+    tx = a.y_fastest ? logical / a.n_tiles_y : logical % a.n_tiles_x;
+    ty = a.y_fastest ? logical % a.n_tiles_y : logical / a.n_tiles_x;
     m0 = ty * MT;
     if (m0 >= a.M) return;
     m_count = min(MT, a.M - m0);
@@ -162,7 +163,18 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
       s_scan[tid] += v;
       __syncthreads();
     }
-    if (ty >= s_scan[E - 1]) return;
+    // the grid is an upper bound of the item count: the live items are dealt
+    // out evenly over the 8 XCDs (workgroup i runs on XCD i % 8) in
+    // contiguous ranges with the token tiles of a row tile adjacent
+    const int n_tiles = s_scan[E - 1];
+    const int live = n_tiles * a.n_tiles_x;
+    const int per_xcd = (live + 7) / 8;
+    const int slot = blockIdx.x / 8;
+    if (slot >= per_xcd) return;
+    const int item = (blockIdx.x % 8) * per_xcd + slot;
+    if (item >= live) return;
+    tx = item / n_tiles;
+    ty = item % n_tiles;
     int lo = 0, hi = E - 1;                    // first e with scan[e] > ty
     while (lo < hi) {
       const int mid = (lo + hi) >> 1;
@@ -353,36 +365,36 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
 
 namespace dg {
 
-// One-wave workgroups for the grouped (expert) GEMMs with 16-token tiles.
-// A wave owns RT tiles of 16 weight rows (gate/up: RT/2 gate tiles and the
-// matching RT/2 up tiles, i.e. 8 * RT intermediate columns; down: 16 * RT
-// rows) and its 16 tokens, so each token row is read once per row block and
-// no LDS or barrier is needed.  The tile decode (which expert, which 16
-// tokens) runs in registers with wave shuffles.  The K loop streams a ring of
-// NR chunks of both operands, unconditional loads in a pinned order.  (Giving
-// a wave all of an expert's tokens in passes instead, so that every work item
-// streams the same bytes, measured slower: later passes wait on the same
-// serial load chain.)
-template <int RT, int NR, bool FP8, int MODE, bool TILED>
+// One-wave workgroups for the grouped (expert) GEMMs at canvas-sized token
+// counts.  A work item is (token tile of 16 * TB rows of one expert, group of
+// RT weight tiles of 16 rows): for gate/up, RT/2 gate tiles and the matching
+// RT/2 up tiles (8 * RT intermediate columns); for down, 16 * RT output rows.
+// Every item streams the same weight bytes, and a tile holds up to 16 * TB
+// tokens so that the few experts that draw many tokens need few items: the
+// launch then fits (nearly) one round of resident waves instead of ending
+// with a short extra round.  Token blocks of a tile past the expert's count
+// skip their MFMAs (wave-uniform).  The item decode runs in registers with
+// wave shuffles.  The K loop streams a ring of NR chunks of both operands,
+// unconditional loads in a pinned order; no LDS, no barrier.  (Giving a wave
+// all of an expert's tokens in consecutive passes measured slower: the busy
+// experts' items then take several times longer than the rest.)
+template <int RT, int TB, int NR, bool FP8, int MODE, bool TILED>
 __global__ __launch_bounds__(64) void gemm_wave_kernel(GemmArgs a) {
   static_assert(MODE == kGateUp || MODE == kDown, "grouped modes only");
   static_assert(MODE != kGateUp || RT % 2 == 0, "gate/up needs paired tiles");
   using WT = typename std::conditional<FP8, uint8_t, bf16_t>::type;
+  constexpr int MT = 16 * TB;
   const int lane = threadIdx.x;
   const int l16 = lane & 15, g4 = lane >> 4;
-  const int logical = xcd_logical_tile(blockIdx.x, gridDim.x);
-  if (logical >= a.n_tiles_total) return;
-  const int tx = a.y_fastest ? logical / a.n_tiles_y : logical % a.n_tiles_x;
-  const int ty = a.y_fastest ? logical % a.n_tiles_y : logical / a.n_tiles_x;
 
-  // ---- tile decode: inclusive scan of 16-token tiles per expert (E <= 256)
+  // ---- item decode: inclusive scan of MT-token tiles per expert (E <= 256)
   const int E = a.n_groups;
   int cnt[4], incl[4];
   int carry = 0;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int e = q * 64 + lane;
-    cnt[q] = e < E ? (a.offsets[e + 1] - a.offsets[e] + 15) / 16 : 0;
+    cnt[q] = e < E ? (a.offsets[e + 1] - a.offsets[e] + MT - 1) / MT : 0;
     int v = cnt[q];
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -392,7 +404,18 @@ __global__ __launch_bounds__(64) void gemm_wave_kernel(GemmArgs a) {
     incl[q] = v + carry;
     carry += __shfl(v, 63);
   }
-  if (ty >= carry) return;
+  // The grid is an upper bound of the item count; the carry * n_tiles_x
+  // live items are dealt out evenly over the 8 XCDs (workgroup i runs on XCD
+  // i % 8), each XCD taking a contiguous range in which the token tiles of a
+  // row group are adjacent, so an expert's tiles share its weight rows in
+  // one L2.
+  const int live = carry * a.n_tiles_x;
+  const int per_xcd = (live + 7) / 8;
+  const int slot = blockIdx.x / 8;
+  if (slot >= per_xcd) return;
+  const int item = (blockIdx.x % 8) * per_xcd + slot;
+  if (item >= live) return;
+  const int tx = item / carry, ty = item % carry;
   int grp = -1, first_tile = 0;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -404,12 +427,20 @@ __global__ __launch_bounds__(64) void gemm_wave_kernel(GemmArgs a) {
     }
   }
   const int base_pos = a.offsets[grp];
-  const int m0 = (ty - first_tile) * 16;
-  const int m_count = min(16, a.offsets[grp + 1] - base_pos - m0);
-  const int my_m = l16 < m_count ? l16 : 0;
-  const int p_pos = base_pos + m0 + my_m;
-  const int src = (MODE == kGateUp) ? a.sorted_rows[p_pos] / a.topk : p_pos;
-  const bool xok = l16 < m_count;
+  const int m0 = (ty - first_tile) * MT;
+  const int m_count = min(MT, a.offsets[grp + 1] - base_pos - m0);
+  const int tb_used = (m_count + 15) / 16;   // wave-uniform
+  bool xok[TB];
+  int p_pos[TB];
+  const bf16_t* xp[TB];
+#pragma unroll
+  for (int tb = 0; tb < TB; ++tb) {
+    const int m = tb * 16 + l16;
+    xok[tb] = m < m_count;
+    p_pos[tb] = base_pos + m0 + (xok[tb] ? m : 0);
+    const int src = (MODE == kGateUp) ? a.sorted_rows[p_pos[tb]] / a.topk : p_pos[tb];
+    xp[tb] = a.X + static_cast<int64_t>(src) * a.K + g4 * 16;
+  }
 
   const WT* Wg = static_cast<const WT*>(a.W) + static_cast<int64_t>(grp) * a.w_group_stride;
   WRow<WT, TILED> wp[RT];
@@ -420,25 +451,29 @@ __global__ __launch_bounds__(64) void gemm_wave_kernel(GemmArgs a) {
                          : tx * (16 * RT) + rt * 16;
     wp[rt].init(Wg, row0, a.K, lane);
   }
-  const bf16_t* xp = a.X + static_cast<int64_t>(src) * a.K + g4 * 16;
   const int nchunks = a.K / 64;
 
   struct Slot {
-    uint4 x0, x1;
+    uint4 x[TB][2];
     WChunk<FP8> w[RT];
   };
   Slot ring[NR];
   auto issue = [&](Slot& sl, int c) {
     const int cc = min(c, nchunks - 1);
-    sl.x0 = *reinterpret_cast<const uint4*>(xp + cc * 64);
-    sl.x1 = *reinterpret_cast<const uint4*>(xp + cc * 64 + 8);
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+      sl.x[tb][0] = *reinterpret_cast<const uint4*>(xp[tb] + cc * 64);
+      sl.x[tb][1] = *reinterpret_cast<const uint4*>(xp[tb] + cc * 64 + 8);
+    }
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) sl.w[rt].template load<WRow<WT, TILED>::kSecond>(wp[rt].at(cc));
   };
   const uint4 zero4 = make_uint4(0, 0, 0, 0);
-  f32x4_v acc[RT];
+  f32x4_v acc[RT][TB];
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) acc[rt] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) acc[rt][tb] = f32x4_v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int p = 0; p < NR; ++p) {
     issue(ring[p], p);
@@ -452,52 +487,66 @@ __global__ __launch_bounds__(64) void gemm_wave_kernel(GemmArgs a) {
       issue(ring[p], c0 + p + NR);
       __builtin_amdgcn_sched_barrier(0);
       if (c0 + p < nchunks) {
-        const uint4 u0 = xok ? cur.x0 : zero4, u1 = xok ? cur.x1 : zero4;
-        const bf16x8_v x0 = *reinterpret_cast<const bf16x8_v*>(&u0);
-        const bf16x8_v x1 = *reinterpret_cast<const bf16x8_v*>(&u1);
+        bf16x8_v xa[TB][2];
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) {
+          const uint4 u0 = xok[tb] ? cur.x[tb][0] : zero4;
+          const uint4 u1 = xok[tb] ? cur.x[tb][1] : zero4;
+          xa[tb][0] = *reinterpret_cast<const bf16x8_v*>(&u0);
+          xa[tb][1] = *reinterpret_cast<const bf16x8_v*>(&u1);
+        }
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
           bf16x8_v w0, w1;
           cur.w[rt].get(w0, w1);
-          acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w0, x0, acc[rt], 0, 0, 0);
-          acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w1, x1, acc[rt], 0, 0, 0);
+#pragma unroll
+          for (int tb = 0; tb < TB; ++tb) {
+            if (tb == 0 || tb < tb_used) {
+              acc[rt][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w0, xa[tb][0], acc[rt][tb], 0, 0, 0);
+              acc[rt][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w1, xa[tb][1], acc[rt][tb], 0, 0, 0);
+            }
+          }
         }
       }
     }
   }
 
-  // ---- epilogue (lane: rows 4 g4 + r of each 16-row tile, token l16)
-  if (!xok) return;
+  // ---- epilogue (lane: rows 4 g4 + r of each 16-row tile, token l16 of
+  // each 16-token block)
   const float* sc = a.w_scale ? a.w_scale + static_cast<int64_t>(grp) * a.s_group_stride : nullptr;
-  if (MODE == kGateUp) {
-    const int I = a.N / 2;
 #pragma unroll
-    for (int i = 0; i < RT / 2; ++i) {
-      const int n = tx * (8 * RT) + i * 16 + g4 * 4;
-      float hv[4];
+  for (int tb = 0; tb < TB; ++tb) {
+    if (!xok[tb]) continue;
+    if (MODE == kGateUp) {
+      const int I = a.N / 2;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float sg = sc ? sc[n + r] : 1.f, su = sc ? sc[I + n + r] : 1.f;
-        hv[r] = gelu_erf(acc[i][r] * sg) * (acc[RT / 2 + i][r] * su);
+      for (int i = 0; i < RT / 2; ++i) {
+        const int n = tx * (8 * RT) + i * 16 + g4 * 4;
+        float hv[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float sg = sc ? sc[n + r] : 1.f, su = sc ? sc[I + n + r] : 1.f;
+          hv[r] = gelu_erf(acc[i][tb][r] * sg) * (acc[RT / 2 + i][tb][r] * su);
+        }
+        uint2 pk;
+        pk.x = pack_bf16x2(hv[0], hv[1]);
+        pk.y = pack_bf16x2(hv[2], hv[3]);
+        *reinterpret_cast<uint2*>(static_cast<bf16_t*>(a.out) + static_cast<int64_t>(p_pos[tb]) * I + n) = pk;
       }
-      uint2 pk;
-      pk.x = pack_bf16x2(hv[0], hv[1]);
-      pk.y = pack_bf16x2(hv[2], hv[3]);
-      *reinterpret_cast<uint2*>(static_cast<bf16_t*>(a.out) + static_cast<int64_t>(p_pos) * I + n) = pk;
-    }
-  } else {
-    const int slot = a.sorted_rows[p_pos];
-    const float g = a.gates[slot];
+    } else {
+      const int slot = a.sorted_rows[p_pos[tb]];
+      const float g = a.gates[slot];
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      const int n = tx * (16 * RT) + rt * 16 + g4 * 4;
-      float v[4];
+      for (int rt = 0; rt < RT; ++rt) {
+        const int n = tx * (16 * RT) + rt * 16 + g4 * 4;
+        float v[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) v[r] = g * acc[rt][r] * (sc ? sc[n + r] : 1.f);
-      uint2 pk;
-      pk.x = pack_bf16x2(v[0], v[1]);
-      pk.y = pack_bf16x2(v[2], v[3]);
-      *reinterpret_cast<uint2*>(static_cast<bf16_t*>(a.out) + static_cast<int64_t>(slot) * a.N + n) = pk;
+        for (int r = 0; r < 4; ++r) v[r] = g * acc[rt][tb][r] * (sc ? sc[n + r] : 1.f);
+        uint2 pk;
+        pk.x = pack_bf16x2(v[0], v[1]);
+        pk.y = pack_bf16x2(v[2], v[3]);
+        *reinterpret_cast<uint2*>(static_cast<bf16_t*>(a.out) + static_cast<int64_t>(slot) * a.N + n) = pk;
+      }
     }
   }
 }

@@ -46,6 +46,18 @@ dg_status launch_moe_route(const float* logits, int T, int E, int k, int32_t* to
                            float* gates, int32_t* offsets, int32_t* sorted_rows, void* ws,
                            hipStream_t stream);
 size_t moe_ffn_workspace_bytes(int T, int D, int I, int E, int k, int x_dtype);
+// The expert FFN in three launches (gate/up, down, combine); launch_moe_ffn
+// runs all three with h and y_slot carved from ws.
+dg_status launch_moe_gate_up(const void* x, int x_dtype, const void* w_gate_up, int w_dtype,
+                             int w_layout, const float* s_gate_up, const int32_t* offsets,
+                             const int32_t* sorted_rows, int T, int D, int I, int E, int k,
+                             void* h, hipStream_t stream);
+dg_status launch_moe_down(const void* h, int h_dtype, const void* w_down, int w_dtype,
+                          int w_layout, const float* s_down, const float* gates,
+                          const int32_t* offsets, const int32_t* sorted_rows, int T, int D, int I,
+                          int E, int k, void* y_slot, hipStream_t stream);
+dg_status launch_moe_combine(const void* y_slot, int dtype, int T, int D, int k, float* y,
+                             hipStream_t stream);
 dg_status launch_moe_ffn(const void* x, int x_dtype, const void* w_gate_up, const void* w_down,
                          int w_dtype, int w_layout, const float* s_gate_up, const float* s_down,
                          const int32_t* topk_ids, const float* gates, const int32_t* offsets,

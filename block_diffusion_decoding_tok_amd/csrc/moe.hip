@@ -199,39 +199,56 @@ size_t moe_ffn_workspace_bytes(int T, int D, int I, int E, int k, int x_dtype) {
   return align_up(slots * I * esz, 256) + align_up(slots * D * esz, 256);
 }
 
-constexpr int kMoeNR = 3;      // register ring depth (chunks of 64 k), one-wave kernels
-constexpr int kMoeWaveRT = 8;  // one-wave kernels: 8 tiles of 16 rows per wave
+// one-wave kernels: register ring depth (chunks of 64 k) and weight tiles of
+// 16 rows per item; token tiles of 16 tokens, or of 32 for gate/up when the
+// experts average 20 to 40 tokens (fewer items re-streaming the same rows)
+constexpr int kMoeNR = 3;
+constexpr int kGateRT = 8, kDownRT = 8;
+
+template <int TB, bool FP8, int MODE, bool TILED>
+static void launch_wave(GemmArgs& g, int rows_per_item, int T, int k, int E,
+                        hipStream_t stream) {
+  // grid: an upper bound of the tile count (E + slots / tile size) times the
+  // weight row groups; the kernel deals the live items out itself
+  g.n_tiles_x = (MODE == kGateUp ? g.N / 2 : g.N) / rows_per_item;
+  g.n_tiles_y = E + (T * k + 16 * TB - 1) / (16 * TB);
+  g.n_tiles_total = g.n_tiles_x * g.n_tiles_y;
+  gemm_wave_kernel<(MODE == kGateUp ? kGateRT : kDownRT), TB, kMoeNR, FP8, MODE, TILED>
+      <<<(g.n_tiles_total + 7) / 8 * 8, 64, 0, stream>>>(g);
+}
 
 template <bool FP8, bool TILED>
-static dg_status launch_grouped(const void* x, const void* wgu, const void* wd, const float* sgu,
-                                const float* sd, const float* gates, const int32_t* offsets,
-                                const int32_t* sorted_rows, int T, int D, int I, int E, int k,
-                                bf16_t* h, bf16_t* y_slot, hipStream_t stream) {
-  // few tokens per expert (the canvas of one or two rows): 16-token tiles,
-  // register streaming; more: 64-token tiles staged through LDS
-  const bool small = static_cast<int64_t>(T) * k <= 40ll * E;
-  const int MT = small ? 16 : 16 * kMoeTB;
-  const int max_ty = E + (T * k + MT - 1) / MT;
+static void launch_gate_up_mfma(const void* x, const void* wgu, const float* sgu,
+                                const int32_t* offsets, const int32_t* sorted_rows, int T, int D,
+                                int I, int E, int k, bf16_t* h, hipStream_t stream) {
   GemmArgs g{};
   g.W = wgu; g.w_group_stride = static_cast<int64_t>(2) * I * D;
   g.w_scale = FP8 ? sgu : nullptr; g.s_group_stride = 2 * I;
   g.X = static_cast<const bf16_t*>(x);
   g.N = 2 * I; g.K = D; g.n_groups = E; g.topk = k;
-  g.offsets = offsets; g.sorted_rows = sorted_rows; g.gates = gates;
+  g.offsets = offsets; g.sorted_rows = sorted_rows;
   g.out = h;
-  g.n_tiles_x = I / 64;
-  g.n_tiles_y = max_ty;
-  g.n_tiles_total = g.n_tiles_x * max_ty;
-  g.y_fastest = small;
-  const unsigned gwg = (g.n_tiles_total + 7) / 8 * 8;
-  if (small) {
-    g.n_tiles_x = I / (8 * kMoeWaveRT);
-    g.n_tiles_total = g.n_tiles_x * max_ty;
-    gemm_wave_kernel<kMoeWaveRT, kMoeNR, FP8, kGateUp, TILED>
-        <<<(g.n_tiles_total + 7) / 8 * 8, 64, 0, stream>>>(g);
-  } else
-    gemm_stream_kernel<2, kMoeTB, kMoeKS, kMoePF, FP8, kGateUp, TILED><<<gwg, 256, 0, stream>>>(g);
-  DG_LAUNCH_CHECK();
+  // few tokens per expert (the canvas of one or two rows): one-wave items
+  // streaming registers; more: 64-token tiles staged through LDS
+  const int64_t slots = static_cast<int64_t>(T) * k;
+  if (slots <= 20ll * E) {
+    launch_wave<1, FP8, kGateUp, TILED>(g, 8 * kGateRT, T, k, E, stream);
+  } else if (slots <= 40ll * E) {
+    launch_wave<2, FP8, kGateUp, TILED>(g, 8 * kGateRT, T, k, E, stream);
+  } else {
+    const int MT = 16 * kMoeTB;
+    g.n_tiles_x = I / 64;
+    g.n_tiles_y = E + static_cast<int>((slots + MT - 1) / MT);
+    g.n_tiles_total = g.n_tiles_x * g.n_tiles_y;
+    gemm_stream_kernel<2, kMoeTB, kMoeKS, kMoePF, FP8, kGateUp, TILED>
+        <<<(g.n_tiles_total + 7) / 8 * 8, 256, 0, stream>>>(g);
+  }
+}
+
+template <bool FP8, bool TILED>
+static void launch_down_mfma(const bf16_t* h, const void* wd, const float* sd, const float* gates,
+                             const int32_t* offsets, const int32_t* sorted_rows, int T, int D,
+                             int I, int E, int k, bf16_t* y_slot, hipStream_t stream) {
   GemmArgs d{};
   d.W = wd; d.w_group_stride = static_cast<int64_t>(D) * I;
   d.w_scale = FP8 ? sd : nullptr; d.s_group_stride = D;
@@ -239,18 +256,78 @@ static dg_status launch_grouped(const void* x, const void* wgu, const void* wd, 
   d.N = D; d.K = I; d.n_groups = E; d.topk = k;
   d.offsets = offsets; d.sorted_rows = sorted_rows; d.gates = gates;
   d.out = y_slot;
-  d.n_tiles_x = D / 128;
-  d.n_tiles_y = max_ty;
-  d.n_tiles_total = d.n_tiles_x * max_ty;
-  d.y_fastest = small;
-  const unsigned dwg = (d.n_tiles_total + 7) / 8 * 8;
-  if (small) {
-    d.n_tiles_x = D / (16 * kMoeWaveRT);
-    d.n_tiles_total = d.n_tiles_x * max_ty;
-    gemm_wave_kernel<kMoeWaveRT, kMoeNR, FP8, kDown, TILED>
-        <<<(d.n_tiles_total + 7) / 8 * 8, 64, 0, stream>>>(d);
-  } else
-    gemm_stream_kernel<2, kMoeTB, kMoeKS, kMoePF, FP8, kDown, TILED><<<dwg, 256, 0, stream>>>(d);
+  const int64_t slots = static_cast<int64_t>(T) * k;
+  if (slots <= 40ll * E) {
+    launch_wave<1, FP8, kDown, TILED>(d, 16 * kDownRT, T, k, E, stream);
+  } else {
+    const int MT = 16 * kMoeTB;
+    d.n_tiles_x = D / 128;
+    d.n_tiles_y = E + static_cast<int>((slots + MT - 1) / MT);
+    d.n_tiles_total = d.n_tiles_x * d.n_tiles_y;
+    gemm_stream_kernel<2, kMoeTB, kMoeKS, kMoePF, FP8, kDown, TILED>
+        <<<(d.n_tiles_total + 7) / 8 * 8, 256, 0, stream>>>(d);
+  }
+}
+
+dg_status launch_moe_gate_up(const void* x, int x_dtype, const void* w_gate_up, int w_dtype,
+                             int w_layout, const float* s_gate_up, const int32_t* offsets,
+                             const int32_t* sorted_rows, int T, int D, int I, int E, int k,
+                             void* h, hipStream_t stream) {
+  if (x_dtype == DG_F32) {
+    gateup_f32_kernel<<<T * k, 128, 0, stream>>>(static_cast<const float*>(x),
+                                                 static_cast<const float*>(w_gate_up), offsets,
+                                                 sorted_rows, T * k, E, D, I, k,
+                                                 static_cast<float*>(h));
+    DG_LAUNCH_CHECK();
+    return DG_OK;
+  }
+  const bool tiled = w_layout == DG_LAYOUT_TILED;
+  bf16_t* hb = static_cast<bf16_t*>(h);
+  if (w_dtype == DG_FP8_E4M3) {
+    if (tiled) launch_gate_up_mfma<true, true>(x, w_gate_up, s_gate_up, offsets, sorted_rows, T, D, I, E, k, hb, stream);
+    else launch_gate_up_mfma<true, false>(x, w_gate_up, s_gate_up, offsets, sorted_rows, T, D, I, E, k, hb, stream);
+  } else {
+    if (tiled) launch_gate_up_mfma<false, true>(x, w_gate_up, nullptr, offsets, sorted_rows, T, D, I, E, k, hb, stream);
+    else launch_gate_up_mfma<false, false>(x, w_gate_up, nullptr, offsets, sorted_rows, T, D, I, E, k, hb, stream);
+  }
+  DG_LAUNCH_CHECK();
+  return DG_OK;
+}
+
+dg_status launch_moe_down(const void* h, int h_dtype, const void* w_down, int w_dtype,
+                          int w_layout, const float* s_down, const float* gates,
+                          const int32_t* offsets, const int32_t* sorted_rows, int T, int D, int I,
+                          int E, int k, void* y_slot, hipStream_t stream) {
+  if (h_dtype == DG_F32) {
+    down_f32_kernel<<<T * k, 128, 0, stream>>>(static_cast<const float*>(h),
+                                               static_cast<const float*>(w_down), offsets,
+                                               sorted_rows, gates, T * k, E, D, I,
+                                               static_cast<float*>(y_slot));
+    DG_LAUNCH_CHECK();
+    return DG_OK;
+  }
+  const bool tiled = w_layout == DG_LAYOUT_TILED;
+  const bf16_t* hb = static_cast<const bf16_t*>(h);
+  bf16_t* yb = static_cast<bf16_t*>(y_slot);
+  if (w_dtype == DG_FP8_E4M3) {
+    if (tiled) launch_down_mfma<true, true>(hb, w_down, s_down, gates, offsets, sorted_rows, T, D, I, E, k, yb, stream);
+    else launch_down_mfma<true, false>(hb, w_down, s_down, gates, offsets, sorted_rows, T, D, I, E, k, yb, stream);
+  } else {
+    if (tiled) launch_down_mfma<false, true>(hb, w_down, nullptr, gates, offsets, sorted_rows, T, D, I, E, k, yb, stream);
+    else launch_down_mfma<false, false>(hb, w_down, nullptr, gates, offsets, sorted_rows, T, D, I, E, k, yb, stream);
+  }
+  DG_LAUNCH_CHECK();
+  return DG_OK;
+}
+
+dg_status launch_moe_combine(const void* y_slot, int dtype, int T, int D, int k, float* y,
+                             hipStream_t stream) {
+  const int64_t n4 = static_cast<int64_t>(T) * D / 4;
+  const unsigned cblocks = static_cast<unsigned>((n4 + 255) / 256);
+  if (dtype == DG_F32)
+    combine_kernel<float><<<cblocks, 256, 0, stream>>>(static_cast<const float*>(y_slot), T, D, k, y);
+  else
+    combine_kernel<bf16_t><<<cblocks, 256, 0, stream>>>(static_cast<const bf16_t*>(y_slot), T, D, k, y);
   DG_LAUNCH_CHECK();
   return DG_OK;
 }
@@ -265,41 +342,13 @@ dg_status launch_moe_ffn(const void* x, int x_dtype, const void* w_gate_up, cons
   const size_t esz = x_dtype == DG_F32 ? 4 : 2;
   void* h = w;
   void* y_slot = w + align_up(slots * I * esz, 256);
-  const int64_t n4 = static_cast<int64_t>(T) * D / 4;
-  const unsigned cblocks = static_cast<unsigned>((n4 + 255) / 256);
-  dg_status st = DG_OK;
-  if (x_dtype == DG_F32) {
-    gateup_f32_kernel<<<T * k, 128, 0, stream>>>(static_cast<const float*>(x),
-                                                 static_cast<const float*>(w_gate_up), offsets,
-                                                 sorted_rows, T * k, E, D, I, k,
-                                                 static_cast<float*>(h));
-    DG_LAUNCH_CHECK();
-    down_f32_kernel<<<T * k, 128, 0, stream>>>(static_cast<const float*>(h),
-                                               static_cast<const float*>(w_down), offsets,
-                                               sorted_rows, gates, T * k, E, D, I,
-                                               static_cast<float*>(y_slot));
-    DG_LAUNCH_CHECK();
-    combine_kernel<float><<<cblocks, 256, 0, stream>>>(static_cast<const float*>(y_slot), T, D, k, y);
-    DG_LAUNCH_CHECK();
-    return DG_OK;
-  }
-  const bool tiled = w_layout == DG_LAYOUT_TILED;
-  bf16_t* hb = static_cast<bf16_t*>(h);
-  bf16_t* yb = static_cast<bf16_t*>(y_slot);
-  if (w_dtype == DG_FP8_E4M3)
-    st = tiled ? launch_grouped<true, true>(x, w_gate_up, w_down, s_gate_up, s_down, gates, offsets,
-                                            sorted_rows, T, D, I, E, k, hb, yb, stream)
-               : launch_grouped<true, false>(x, w_gate_up, w_down, s_gate_up, s_down, gates, offsets,
-                                             sorted_rows, T, D, I, E, k, hb, yb, stream);
-  else
-    st = tiled ? launch_grouped<false, true>(x, w_gate_up, w_down, nullptr, nullptr, gates, offsets,
-                                             sorted_rows, T, D, I, E, k, hb, yb, stream)
-               : launch_grouped<false, false>(x, w_gate_up, w_down, nullptr, nullptr, gates, offsets,
-                                              sorted_rows, T, D, I, E, k, hb, yb, stream);
+  dg_status st = launch_moe_gate_up(x, x_dtype, w_gate_up, w_dtype, w_layout, s_gate_up, offsets,
+                                    sorted_rows, T, D, I, E, k, h, stream);
   if (st != DG_OK) return st;
-  combine_kernel<bf16_t><<<cblocks, 256, 0, stream>>>(static_cast<const bf16_t*>(y_slot), T, D, k, y);
-  DG_LAUNCH_CHECK();
-  return DG_OK;
+  st = launch_moe_down(h, x_dtype, w_down, w_dtype, w_layout, s_down, gates, offsets, sorted_rows,
+                       T, D, I, E, k, y_slot, stream);
+  if (st != DG_OK) return st;
+  return launch_moe_combine(y_slot, x_dtype, T, D, k, y, stream);
 }
 
 }  // namespace dg

@@ -83,6 +83,10 @@ _SIGS = {
     "dg_moe_ffn_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I]),
     "dg_moe_ffn": (_I, [_VP, _I, _VP, _VP, _I, _I, _VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _I,
                         _I, _I, _VP, _VP, _SZ, _VP]),
+    "dg_moe_gate_up": (_I, [_VP, _I, _VP, _I, _I, _VP, _VP, _VP, _I, _I, _I, _I, _I, _VP, _VP]),
+    "dg_moe_down": (_I, [_VP, _I, _VP, _I, _I, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _VP,
+                         _VP]),
+    "dg_moe_combine": (_I, [_VP, _I, _I, _I, _I, _VP, _VP]),
     "dg_ctx_workspace_size": (_SZ, [C.POINTER(dg_model_dims), _I, _I]),
     "dg_ctx_create": (_I, [C.POINTER(_VP), C.POINTER(dg_model_dims),
                            C.POINTER(dg_model_weights), _I, _I, _VP, _SZ]),
@@ -293,6 +297,53 @@ def dg_moe_ffn(x, w_gate_up, w_down, s_gate_up, s_down, topk_ids, gates, expert_
         _dev(expert_offsets, "expert_offsets", (torch.int32,)),
         _dev(sorted_rows, "sorted_rows", (torch.int32,)), T, D, I, E, k,
         _dev(y, "y", (torch.float32,)), ws.data_ptr(), ws.numel(), _stream(stream)))
+    return y
+
+
+def _expert_dims(w, E, I, gate_up):
+    if E is None:
+        E = w.shape[0]
+        I = w.shape[1] // 2 if gate_up else w.shape[2]
+    return E, I
+
+
+def dg_moe_gate_up(x, w_gate_up, s_gate_up, expert_offsets, sorted_rows, k, h=None, stream=None,
+                   w_layout=DG_LAYOUT_ROWMAJOR, E=None, I=None):
+    """h [T * k, I] (x's dtype), one row per sorted position."""
+    T, D = x.shape
+    E, I = _expert_dims(w_gate_up, E, I, True)
+    if h is None:
+        h = torch.empty((T * k, I), dtype=x.dtype, device=x.device)
+    _check(lib().dg_moe_gate_up(
+        _dev(x, "x"), _dtype_code(x), _dev(w_gate_up, "w_gate_up"), _dtype_code(w_gate_up),
+        int(w_layout), _dev(s_gate_up, "s_gate_up", (torch.float32,)),
+        _dev(expert_offsets, "expert_offsets", (torch.int32,)),
+        _dev(sorted_rows, "sorted_rows", (torch.int32,)), T, D, I, E, k,
+        _dev(h, "h", (x.dtype,)), _stream(stream)))
+    return h
+
+
+def dg_moe_down(h, w_down, s_down, gates, expert_offsets, sorted_rows, T, D, y_slot=None,
+                stream=None, w_layout=DG_LAYOUT_ROWMAJOR, E=None, I=None):
+    """y_slot [T * k, D] (h's dtype), one gate-weighted row per slot."""
+    E, I = _expert_dims(w_down, E, I, False)
+    k = h.shape[0] // T
+    if y_slot is None:
+        y_slot = torch.empty((T * k, D), dtype=h.dtype, device=h.device)
+    _check(lib().dg_moe_down(
+        _dev(h, "h"), _dtype_code(h), _dev(w_down, "w_down"), _dtype_code(w_down), int(w_layout),
+        _dev(s_down, "s_down", (torch.float32,)), _dev(gates, "gates", (torch.float32,)),
+        _dev(expert_offsets, "expert_offsets", (torch.int32,)),
+        _dev(sorted_rows, "sorted_rows", (torch.int32,)), T, D, I, E, k,
+        _dev(y_slot, "y_slot", (h.dtype,)), _stream(stream)))
+    return y_slot
+
+
+def dg_moe_combine(y_slot, k, y, stream=None):
+    """y [T, D] f32 += sum over each token's k slot rows."""
+    T, D = y.shape
+    _check(lib().dg_moe_combine(_dev(y_slot, "y_slot"), _dtype_code(y_slot), T, D, k,
+                                _dev(y, "y", (torch.float32,)), _stream(stream)))
     return y
 
 

@@ -192,14 +192,40 @@ dg_status dg_moe_route(const float* router_logits, int T, int E, int k, int32_t*
  *   s_gate_up  [E, 2I], s_down [E, D] f32 per-row scales (DG_FP8_E4M3 only;
  *              the weight is byte value * scale); ignored otherwise
  *   routing tables as produced by dg_moe_route; y [T, D] f32, accumulated.
- *   D % 64 == 0 and I % 64 == 0 for the MFMA paths.
- * ws >= dg_moe_ffn_workspace_size(T, D, I, E, k, x_dtype). */
+ *   D % 128 == 0 and I % 64 == 0 for the bf16 / fp8 (MFMA) paths.
+ * ws >= dg_moe_ffn_workspace_size(T, D, I, E, k, x_dtype).  It runs the three
+ * steps below (gate/up, down, combine) with h and y_slot carved from ws. */
 size_t dg_moe_ffn_workspace_size(int T, int D, int I, int E, int k, int x_dtype);
 dg_status dg_moe_ffn(const void* x, int x_dtype, const void* w_gate_up, const void* w_down,
                      int w_dtype, int w_layout, const float* s_gate_up, const float* s_down,
                      const int32_t* topk_ids, const float* gates, const int32_t* expert_offsets,
                      const int32_t* sorted_rows, int T, int D, int I, int E, int k, float* y,
                      void* ws, size_t ws_bytes, void* stream);
+
+/* The expert FFN of dg_moe_ffn as its three steps ([WE0] "26B MoE 설계가
+ * 의미하는 것": each token runs only its selected experts), for callers that
+ * schedule or time them apart.  Arguments, dtypes, layouts and limits as in
+ * dg_moe_ffn; the intermediates are dense device arrays owned by the caller.
+ *
+ * dg_moe_gate_up: for every sorted position p of expert e (expert_offsets[e]
+ *   <= p < expert_offsets[e + 1]) and token t = sorted_rows[p] / k,
+ *   h[p, :] = GELU_erf(x[t] Wg_e^T) * (x[t] Wu_e^T).
+ *   h [T * k, I] in x_dtype.
+ * dg_moe_down: for every sorted position p, slot s = sorted_rows[p],
+ *   y_slot[s, :] = gates[s] * (h[p] Wd_e^T).  h_dtype is x_dtype of the
+ *   gate/up step; y_slot [T * k, D] in h_dtype.
+ * dg_moe_combine: y[t, :] += sum_{j < k} y_slot[t * k + j, :] in slot order.
+ *   y_slot in dtype (DG_BF16 or DG_F32); y [T, D] f32.  D % 4 == 0. */
+dg_status dg_moe_gate_up(const void* x, int x_dtype, const void* w_gate_up, int w_dtype,
+                         int w_layout, const float* s_gate_up, const int32_t* expert_offsets,
+                         const int32_t* sorted_rows, int T, int D, int I, int E, int k, void* h,
+                         void* stream);
+dg_status dg_moe_down(const void* h, int h_dtype, const void* w_down, int w_dtype, int w_layout,
+                      const float* s_down, const float* gates, const int32_t* expert_offsets,
+                      const int32_t* sorted_rows, int T, int D, int I, int E, int k, void* y_slot,
+                      void* stream);
+dg_status dg_moe_combine(const void* y_slot, int dtype, int T, int D, int k, float* y,
+                         void* stream);
 
 /* ----------------------------------------------------------- whole decoder
  * A random-init decoder of n_layers pre-norm layers: RMSNorm (eps 1e-6, unit

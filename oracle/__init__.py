@@ -58,7 +58,7 @@ from .sampler import (SamplerCfg, temperature, position_stats, sampler_step,
                       init_canvas)
 from .attention import rope, attention
 from .moe import (fp8_e4m3fn_decode, moe_route, moe_ffn, moe_ffn_dense_masked,
-                  gelu_erf)
+                  expert_gate_up, gelu_erf)
 from .model import (rmsnorm, TinyModel, layer_forward, model_forward,
                     prefill, denoise_block)
 
@@ -67,6 +67,6 @@ __all__ = [
     "STREAM_GUMBEL", "STREAM_RENOISE", "STREAM_CANVAS",
     "SamplerCfg", "temperature", "position_stats", "sampler_step",
     "init_canvas", "rope", "attention", "fp8_e4m3fn_decode", "moe_route",
-    "moe_ffn", "moe_ffn_dense_masked", "gelu_erf", "rmsnorm", "TinyModel",
+    "moe_ffn", "moe_ffn_dense_masked", "expert_gate_up", "gelu_erf", "rmsnorm", "TinyModel",
     "layer_forward", "model_forward", "prefill", "denoise_block",
 ]

@@ -66,9 +66,15 @@ def moe_route(router_logits, k):
     return ids, gates, offsets, sorted_rows
 
 
+def expert_gate_up(u, wg, wu):
+    """The gated hidden activation of one expert for the rows of u [n, D]:
+    GELU(u Wg^T) * (u Wu^T), [n, I]."""
+    return gelu_erf(u @ wg.T) * (u @ wu.T)
+
+
 def expert_ffn(u, wg, wu, wd):
     """One expert applied to the rows of u [n, D]."""
-    return (gelu_erf(u @ wg.T) * (u @ wu.T)) @ wd.T
+    return expert_gate_up(u, wg, wu) @ wd.T
 
 
 def moe_ffn(u, w_gate_up, w_down, topk_ids, gates):

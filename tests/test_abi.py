@@ -89,6 +89,26 @@ def test_attention_and_moe_reject_bad_shapes(lib):
                           256, 2800, 704, 128, 8, f, f, 1 << 30, None) == -2
 
 
+def test_moe_steps_reject_bad_calls(lib):
+    f = C.c_void_p(256)
+    # gate/up: fp8 without scales; null h; D not a multiple of 128
+    assert lib.dg_moe_gate_up(f, dg.DG_BF16, f, dg.DG_FP8_E4M3, 1, None, f, f,
+                              256, 2816, 704, 128, 8, f, None) == -1
+    assert "scales" in _last_error(lib)
+    assert lib.dg_moe_gate_up(f, dg.DG_BF16, f, dg.DG_BF16, 1, None, f, f,
+                              256, 2816, 704, 128, 8, None, None) == -1
+    assert lib.dg_moe_gate_up(f, dg.DG_BF16, f, dg.DG_BF16, 0, None, f, f,
+                              256, 2880, 704, 128, 8, f, None) == -2
+    # down: null gates; k > 16
+    assert lib.dg_moe_down(f, dg.DG_BF16, f, dg.DG_BF16, 0, None, None, f, f,
+                           256, 2816, 704, 128, 8, f, None) == -1
+    assert lib.dg_moe_down(f, dg.DG_BF16, f, dg.DG_BF16, 0, None, f, f, f,
+                           256, 2816, 704, 128, 17, f, None) == -2
+    # combine: bad dtype; D not a multiple of 4
+    assert lib.dg_moe_combine(f, dg.DG_FP8_E4M3, 256, 2816, 8, f, None) == -1
+    assert lib.dg_moe_combine(f, dg.DG_BF16, 256, 2815, 8, f, None) == -2
+
+
 def test_ctx_validation(lib):
     dims = dg.dg_model_dims(30, 2816, 16, 8, 128, 128, 8, 704, 262144, 10000.0,
                             dg.DG_BF16, dg.DG_FP8_E4M3, dg.DG_LAYOUT_TILED)

@@ -8,7 +8,7 @@ import torch
 
 from block_diffusion_decoding_tok_amd import dg
 from block_diffusion_decoding_tok_amd.inputs import moe_case
-from oracle.moe import moe_route, moe_ffn
+from oracle.moe import moe_route, moe_ffn, expert_gate_up
 from tests.util import ExpertWeights, rel_err_rows, to_f64, pack_tiled
 
 pytestmark = pytest.mark.gpu
@@ -94,10 +94,22 @@ def test_pack_weights_layout(dtype):
     assert np.array_equal(got, ref)
 
 
-def test_moe_ffn_full_size_bs4_fp8_sampled():
+@pytest.mark.parametrize("tiled", [False, True])
+def test_moe_ffn_full_size_bs4_fp8_sampled(tiled):
+    """Above 40 tokens per expert on average: LDS-staged 64-token tiles."""
     case = moe_case(T=1024, w_dtype="fp8", seed=1)
     sample = np.random.default_rng(0).choice(1024, 96, replace=False)
-    err, _ = _ffn_case(case, 8, sample)
+    err, _ = _ffn_case(case, 8, sample, tiled=tiled)
+    assert err < TOL["fp8"], err
+
+
+@pytest.mark.parametrize("tiled", [False, True])
+def test_moe_ffn_full_size_bs2_fp8_sampled(tiled):
+    """Between 20 and 40 tokens per expert on average: one-wave items with
+    32-token tiles for gate/up and 16-token tiles for down."""
+    case = moe_case(T=512, w_dtype="fp8", seed=4)
+    sample = np.random.default_rng(1).choice(512, 96, replace=False)
+    err, _ = _ffn_case(case, 8, sample, tiled=tiled)
     assert err < TOL["fp8"], err
 
 
@@ -129,3 +141,42 @@ def test_moe_ffn_deterministic():
     _, y1 = _ffn_case(case, 4, sample=np.arange(4))
     _, y2 = _ffn_case(case, 4, sample=np.arange(4))
     assert torch.equal(y1, y2)
+
+
+@pytest.mark.parametrize("T", [256, 512])
+def test_moe_steps_compose_to_ffn(T):
+    """gate/up -> down -> combine as three calls equals dg_moe_ffn bit for
+    bit; the hidden rows h and the gate-weighted slot rows of a sample of
+    sorted positions match the oracle's expert steps."""
+    k = 8
+    case = moe_case(T=T, w_dtype="fp8", seed=2)
+    ids, gates, off, rows = _check_route(case.router_logits, k)
+    D, I = case.x.shape[1], case.w_down.shape[2]
+    xd = case.x.to(DEV)
+    wgu, wd = dg.dg_pack_weights(case.w_gate_up.to(DEV)), dg.dg_pack_weights(case.w_down.to(DEV))
+    sgu, sd = case.s_gate_up.to(DEV), case.s_down.to(DEV)
+    t_ids, t_gates = torch.from_numpy(ids).to(DEV), torch.from_numpy(gates).to(DEV)
+    t_off, t_rows = torch.from_numpy(off).to(DEV), torch.from_numpy(rows).to(DEV)
+    kw = dict(w_layout=dg.DG_LAYOUT_TILED, E=case.w_down.shape[0], I=I)
+    y_ffn = torch.zeros((T, D), device=DEV)
+    dg.dg_moe_ffn(xd, wgu, wd, sgu, sd, t_ids, t_gates, t_off, t_rows, y_ffn, **kw)
+    h = dg.dg_moe_gate_up(xd, wgu, sgu, t_off, t_rows, k, **kw)
+    ys = dg.dg_moe_down(h, wd, sd, t_gates, t_off, t_rows, T, D, **kw)
+    y3 = dg.dg_moe_combine(ys, k, torch.zeros((T, D), device=DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(y_ffn, y3)
+
+    wg, wdn = ExpertWeights(case.w_gate_up, case.s_gate_up), ExpertWeights(case.w_down, case.s_down)
+    x64 = to_f64(case.x)
+    h_got = to_f64(h.cpu())
+    ys_got = to_f64(ys.cpu())
+    sample = np.random.default_rng(3).choice(T * k, 48, replace=False)
+    expert_of = np.searchsorted(off, sample, side="right") - 1
+    for e in np.unique(expert_of):
+        ps = sample[expert_of == e]
+        slots = rows[ps]
+        w = wg[e]
+        h_ref = expert_gate_up(x64[slots // k], w[:I], w[I:])
+        assert rel_err_rows(h_got[ps], h_ref) < 1e-2
+        y_ref = gates.reshape(-1)[slots][:, None] * (h_ref @ wdn[e].T)
+        assert rel_err_rows(ys_got[slots], y_ref) < TOL["fp8"]
