@@ -11,13 +11,19 @@
 // Launch sequence:
 //   1. rope_kernel: per token (heads spread over the workgroup's threads),
 //      rotates the block's q (into a packed workspace
-//      [B, Hkv, Lq * G, dh], packed row r = token * G + (head % G)) and k
-//      (into cache slots [P, P + Lq)), copies v into the cache.
-//   2. bf16: attn_mfma_kernel, grid (row tiles of 128, KV splits, B * Hkv);
-//      four waves x 32 packed rows; K tile [64 keys][dh] and V^T tile
-//      [dh][64 keys] staged in LDS (double buffered); S^T = K Q^T and
-//      O^T = V^T P^T on v_mfma_f32_16x16x32_bf16 so that the probabilities
-//      leave the S MFMA already in the B-operand layout of the PV MFMA.
+//      [B, Hkv, Lq * G, dh], packed row r = token * G + (head % G); for the
+//      bf16 path pre-multiplied by log2(e) / sqrt(dh), so that scores come
+//      out of the MFMA in the log2 domain) and k (into cache slots
+//      [P, P + Lq)), copies v into the cache.
+//   2. bf16: attn_mfma_kernel, one workgroup per (row tile of 128, KV split,
+//      b * Hkv), the row tiles of one (split, head) on the same XCD so
+//      that they share its K/V tiles in one L2; eight waves: four row groups
+//      of 32 packed rows x two halves of every 128-key tile (two waves per
+//      SIMD), merged through LDS at the end; K tile [128 keys][dh] (rows in
+//      MFMA order) and V^T tile [dh][128 keys] staged in LDS (double
+//      buffered); S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_16x16x32_bf16
+//      so that the probabilities leave the S MFMA already in the B-operand
+//      layout of the PV MFMA; the running maximum is raised lazily.
 //      f32: attn_f32_kernel, one wave per (query, head) -- parity path.
 //   3. attn_combine_kernel merges the KV splits (online-softmax merge).
 #include "common.h"
@@ -34,7 +40,7 @@ __global__ __launch_bounds__(256) void rope_kernel(
     const T* __restrict__ q, const T* __restrict__ k_new, const T* __restrict__ v_new,
     int64_t q_stride, int64_t kv_stride, T* __restrict__ q_out, T* __restrict__ k_cache,
     T* __restrict__ v_cache, const int32_t* __restrict__ prefix_len, int Lq, int Hq, int Hkv,
-    int dh, int Tmax, float theta) {
+    int dh, int Tmax, float theta, float q_scale) {
   // one workgroup per token; thread (pair j, head lane hl) handles heads
   // hl, hl + lanes, ... of the query heads and then of the KV heads
   const int tok = blockIdx.x;          // b * Lq + i
@@ -55,8 +61,8 @@ __global__ __launch_bounds__(256) void rope_kernel(
       const int g = h / G;
       const int64_t r = static_cast<int64_t>(i) * G + (h % G);
       T* dst = q_out + ((static_cast<int64_t>(b) * Hkv + g) * Lq * G + r) * dh;
-      Elem<T>::store(dst, j, x1 * c - x2 * s);
-      Elem<T>::store(dst, j + half, x2 * c + x1 * s);
+      Elem<T>::store(dst, j, (x1 * c - x2 * s) * q_scale);
+      Elem<T>::store(dst, j + half, (x2 * c + x1 * s) * q_scale);
     }
   }
   const T* kt = k_new + static_cast<int64_t>(tok) * kv_stride;
@@ -82,43 +88,108 @@ __global__ void advance_prefix_kernel(int32_t* prefix_len, int B, int L) {
 }
 
 // ------------------------------------------------------------ bf16 MFMA path
-constexpr int kAttnRows = 128;        // packed rows per workgroup
-constexpr int kAttnKeys = 64;         // keys per LDS tile
+constexpr int kAttnRows = 128;        // packed rows per workgroup (4 row groups of 32)
+constexpr int kAttnKeys = 128;        // keys per LDS tile (2 halves of 64)
 constexpr int kDh = 128;
 constexpr int kKStride = kDh + 8;     // K tile row stride (elements): 272 B
-constexpr int kVStride = kAttnKeys + 8;   // V^T tile row stride: 144 B
+constexpr int kVStride = kAttnKeys + 8;   // V^T tile row stride: 272 B
 constexpr int kKTileElems = kAttnKeys * kKStride;
 constexpr int kVTileElems = kDh * kVStride;
+// A row's running maximum is raised only when a tile's maximum exceeds it by
+// more than this (log2 units): probabilities then stay below 2^8, and the
+// rescale of the output accumulators is skipped on most tiles.
+constexpr float kLazyRescale = 8.f;
 
-// Column of key kappa (0..63) in a V^T tile row: within each 32-key chunk the
-// keys are placed so that the 8 keys a lane feeds to one PV MFMA (4 from each
-// 16-key block, matching the S^T accumulator layout) are contiguous.
-__device__ __forceinline__ int vt_col(int kappa) {
-  const int t = kappa >> 5, w = kappa & 31;
-  return t * 32 + ((w & 15) >> 2) * 8 + ((w >> 4) << 2) + (w & 3);
+// LDS row of key k (0..127) of a K tile.  The S^T MFMA's output row 16 b + 4 g
+// + r (b = 0..3 within a 64-key half, g = lane / 16) must hold key 8 g + 4 (b
+// & 1) + r of the half's 32-key chunk b / 2, so that each lane's eight
+// probabilities of a chunk are eight consecutive keys -- the B-operand layout
+// of the PV MFMA over V^T in natural key order.  Keys are stored in that
+// MFMA row order.
+__device__ __forceinline__ int k_lds_row(int k) {
+  return (k & ~31) | (((k >> 2) & 1) << 4) | (((k >> 3) & 3) << 2) | (k & 3);
 }
 
 struct AttnPartialML { float m, l; };
 
-__global__ __launch_bounds__(256) void attn_mfma_kernel(
+// Staging of one 128-key tile through registers, loads clamped to the last
+// valid key (past it the scores are masked, and the clamped rows hold finite
+// cache data):
+//   K: 128 keys x 16 chunks of 8 dh = 2048 items of 16 B, four per thread,
+//      stored at the key's MFMA row (k_lds_row);
+//   V: a quad of 4 keys (kq) x one chunk of 8 dh (vch) per thread, stored
+//      transposed into V^T [dh][keys] as 8 rows of 4 keys.
+struct AttnStage {
+  uint4 k0, k1, k2, k3, v0, v1, v2, v3;
+};
+
+__device__ __forceinline__ void attn_load_stage(AttnStage& st, const bf16_t* kbase,
+                                                const bf16_t* vbase, int key0, int k_end, int tid,
+                                                int kq, int vch) {
+  auto kload = [&](int it) {
+    const int item = it * 512 + tid;
+    const int gk = min(key0 + (item >> 4), k_end - 1);
+    return *reinterpret_cast<const uint4*>(kbase + static_cast<int64_t>(gk) * kDh + (item & 15) * 8);
+  };
+  auto vload = [&](int kk) {
+    const int gk = min(key0 + kq * 4 + kk, k_end - 1);
+    return *reinterpret_cast<const uint4*>(vbase + static_cast<int64_t>(gk) * kDh + vch * 8);
+  };
+  st.k0 = kload(0); st.k1 = kload(1); st.k2 = kload(2); st.k3 = kload(3);
+  st.v0 = vload(0); st.v1 = vload(1); st.v2 = vload(2); st.v3 = vload(3);
+}
+
+__device__ __forceinline__ uint32_t u4w(const uint4& u, int i) {
+  return i == 0 ? u.x : i == 1 ? u.y : i == 2 ? u.z : u.w;
+}
+
+__device__ __forceinline__ void attn_store_stage(const AttnStage& st, bf16_t* sk, bf16_t* sv,
+                                                 int tid, int kq, int vch) {
+  auto kstore = [&](int it, const uint4& v) {
+    const int item = it * 512 + tid;
+    *reinterpret_cast<uint4*>(&sk[k_lds_row(item >> 4) * kKStride + (item & 15) * 8]) = v;
+  };
+  kstore(0, st.k0); kstore(1, st.k1); kstore(2, st.k2); kstore(3, st.k3);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    // dh element e of the four keys: low or high halves of word e / 2
+    const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+    uint2 pk;
+    pk.x = __builtin_amdgcn_perm(u4w(st.v1, e >> 1), u4w(st.v0, e >> 1), sel);
+    pk.y = __builtin_amdgcn_perm(u4w(st.v3, e >> 1), u4w(st.v2, e >> 1), sel);
+    *reinterpret_cast<uint2*>(&sv[(vch * 8 + e) * kVStride + kq * 4]) = pk;
+  }
+}
+
+__global__ __launch_bounds__(512) void attn_mfma_kernel(
     const bf16_t* __restrict__ qrot, const bf16_t* __restrict__ k_cache,
     const bf16_t* __restrict__ v_cache, const int32_t* __restrict__ prefix_len, int Lq, int G,
-    int Hkv, int Tmax, int chunk, int nsplit, int causal, float scale_log2,
+    int Hkv, int Tmax, int chunk, int ntile_rows, int nsplit, int BH, int causal,
     float* __restrict__ o_part, AttnPartialML* __restrict__ ml_part) {
-  __shared__ __attribute__((aligned(16))) bf16_t s_k[2][kKTileElems];
-  __shared__ __attribute__((aligned(16))) bf16_t s_v[2][kVTileElems];
+  extern __shared__ __attribute__((aligned(16))) bf16_t smem[];
+  // [K tile 0][K tile 1][V^T tile 0][V^T tile 1]
+  auto s_k = [&](int buf) { return smem + buf * kKTileElems; };
+  auto s_v = [&](int buf) { return smem + 2 * kKTileElems + buf * kVTileElems; };
 
-  const int tile = blockIdx.x, split = blockIdx.y, bh = blockIdx.z;
+  // logical index: row tile fastest, then split, then (b, kv head); workgroup
+  // i runs on XCD i % 8, so consecutive logical indices are dealt to one XCD
+  const int total = ntile_rows * nsplit * BH;
+  const int logical = xcd_logical_tile(blockIdx.x, gridDim.x);
+  if (logical >= total) return;
+  const int tile = logical % ntile_rows;
+  const int split = (logical / ntile_rows) % nsplit;
+  const int bh = logical / (ntile_rows * nsplit);
   const int b = bh / Hkv;
   const int rows_total = Lq * G;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g4 = lane >> 4;
+  const int rg = wave & 3, kh = wave >> 2;          // row group, key half
   const int P = prefix_len[b];
   const int n_keys = P + Lq;
-  const int row0 = tile * kAttnRows + wave * 32;   // this wave's first packed row
+  const int row0 = tile * kAttnRows + rg * 32;      // this wave's first packed row
 
   // key range of this split (causal: trimmed to the last row of the tile)
-  int k_begin = split * chunk;
+  const int k_begin = split * chunk;
   int k_end = min(n_keys, k_begin + chunk);
   if (causal) {
     const int last_row = min(rows_total - 1, tile * kAttnRows + kAttnRows - 1);
@@ -127,7 +198,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
   const int ntiles = k_end > k_begin ? (k_end - k_begin + kAttnKeys - 1) / kAttnKeys : 0;
 
   // Q fragments (B operand of S^T = K Q^T): row l16 of each 16-row block,
-  // dh 32c + 8 g4 .. +7
+  // dh 32c + 8 g4 .. +7; q is pre-scaled into the log2 domain
   bf16x8_t qf[2][4];
   const bf16_t* qbase = qrot + static_cast<int64_t>(bh) * rows_total * kDh;
 #pragma unroll
@@ -141,81 +212,38 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
         qf[qb][c] = bf16x8_t{};
     }
   }
-  // token of each of this lane's two rows (for the causal mask)
   int tok_of[2];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) tok_of[qb] = (row0 + qb * 16 + l16) / G;
+  const int wave_tok = row0 / G;   // smallest token of the wave's rows
 
   f32x4_t acc_o[2][8];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
     for (int d = 0; d < 8; ++d) acc_o[qb][d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_run[2] = {-INFINITY, -INFINITY};
+  float m_run[2] = {-INFINITY, -INFINITY};   // exponent base in use (per row)
   float l_run[2] = {0.f, 0.f};
 
   const bf16_t* kbase = k_cache + static_cast<int64_t>(bh) * Tmax * kDh;
   const bf16_t* vbase = v_cache + static_cast<int64_t>(bh) * Tmax * kDh;
 
-  // staging: K tile = 64 keys x 16 chunks of 8 dh (1024 items of 16 B, four
-  // per thread); V tile = 16 quads of 4 keys x 16 chunks of 8 dh (one item
-  // of 4 x 16 B per thread), written transposed into V^T.
-  uint4 kreg[4];
-  uint4 vreg[4];
-  auto load_tile = [&](int t) {
-    const int key0 = k_begin + t * kAttnKeys;
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int item = it * 256 + tid;
-      const int key = item >> 4, ch = item & 15;
-      const int gk = key0 + key;
-      kreg[it] = (gk < k_end) ? *reinterpret_cast<const uint4*>(kbase + static_cast<int64_t>(gk) * kDh + ch * 8)
-                              : make_uint4(0, 0, 0, 0);
-    }
-    {
-      const int kq = tid >> 4, ch = tid & 15;     // 4-key quad kq (0..15), dh chunk ch
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int gk = key0 + kq * 4 + kk;
-        vreg[kk] = (gk < k_end) ? *reinterpret_cast<const uint4*>(vbase + static_cast<int64_t>(gk) * kDh + ch * 8)
-                                : make_uint4(0, 0, 0, 0);
-      }
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int item = it * 256 + tid;
-      const int key = item >> 4, ch = item & 15;
-      *reinterpret_cast<uint4*>(&s_k[buf][key * kKStride + ch * 8]) = kreg[it];
-    }
-    const int kq = tid >> 4, ch = tid & 15;
-    const int col = vt_col(kq * 4);   // 4 consecutive keys -> 4 consecutive columns
-    const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&vreg[0]);
-    const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&vreg[1]);
-    const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&vreg[2]);
-    const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&vreg[3]);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int sh = (e & 1) * 16;
-      const uint32_t a0 = (w0[e >> 1] >> sh) & 0xffffu, a1 = (w1[e >> 1] >> sh) & 0xffffu;
-      const uint32_t a2 = (w2[e >> 1] >> sh) & 0xffffu, a3 = (w3[e >> 1] >> sh) & 0xffffu;
-      uint2 pk;
-      pk.x = a0 | (a1 << 16);
-      pk.y = a2 | (a3 << 16);
-      *reinterpret_cast<uint2*>(&s_v[buf][(ch * 8 + e) * kVStride + col]) = pk;
-    }
-  };
-
-  if (ntiles > 0) load_tile(0);
+  // K/V tiles: register staging (AttnStage), LDS double buffer
+  const int kq = tid & 31, vch = tid >> 5;
+  AttnStage st;
+  if (ntiles > 0) attn_load_stage(st, kbase, vbase, k_begin, k_end, tid, kq, vch);
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t & 1;
-    store_tile(buf);
+    attn_store_stage(st, s_k(buf), s_v(buf), tid, kq, vch);
     __syncthreads();
-    if (t + 1 < ntiles) load_tile(t + 1);
-    const int key0 = k_begin + t * kAttnKeys;
+    if (t + 1 < ntiles)
+      attn_load_stage(st, kbase, vbase, k_begin + (t + 1) * kAttnKeys, k_end, tid, kq, vch);
+    const int hkey0 = k_begin + t * kAttnKeys + kh * 64;   // first key of this wave's half
+    const bf16_t* sk = s_k(buf) + kh * 64 * kKStride;
+    const bf16_t* sv = s_v(buf) + kh * 64;
 
-    // S^T blocks: [kb][qb], keys kb*16 + 4 g4 + r, row l16
+    // S^T blocks [kb][qb]: MFMA row 4 g4 + r of block kb is key
+    // 32 (kb / 2) + 8 g4 + 4 (kb & 1) + r of the half; column = row l16
     f32x4_t s_acc[4][2];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
@@ -224,34 +252,46 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(
-            &s_k[buf][(kb * 16 + l16) * kKStride + c * 32 + g4 * 8]);
+            &sk[(kb * 16 + l16) * kKStride + c * 32 + g4 * 8]);
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
           s_acc[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[qb][c], s_acc[kb][qb], 0, 0, 0);
       }
     }
-    // mask, online softmax (log2 domain), probabilities -> bf16 B operands
+    // keys at or past a row's limit only occur in the split's last tile, or
+    // past the wave's first token under the causal mask
+    const int wave_lim = causal ? min(k_end, P + wave_tok + 1) : k_end;
+    const bool edge = hkey0 + 64 > wave_lim;   // wave-uniform
     bf16x8_t pf[2][2];   // [qb][32-key chunk]
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      const int key_lim = causal ? min(k_end, P + tok_of[qb] + 1) : k_end;
+      if (edge) {
+        const int key_lim = causal ? min(k_end, P + tok_of[qb] + 1) : k_end;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int key = hkey0 + (kb >> 1) * 32 + g4 * 8 + (kb & 1) * 4 + r;
+            if (key >= key_lim) s_acc[kb][qb][r] = -INFINITY;
+          }
+      }
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = key0 + kb * 16 + g4 * 4 + r;
-          float v = s_acc[kb][qb][r] * scale_log2;
-          v = (key < key_lim) ? v : -INFINITY;
-          s_acc[kb][qb][r] = v;
-          mx = fmaxf(mx, v);
-        }
+        mx = fmaxf(mx, fmaxf(fmaxf(s_acc[kb][qb][0], s_acc[kb][qb][1]),
+                             fmaxf(s_acc[kb][qb][2], s_acc[kb][qb][3])));
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run[qb], mx);
-      const float base = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - base);
-      m_run[qb] = m_new;
+      // raise the base only past the lazy margin (wave-uniform decision)
+      if (__any(mx > m_run[qb] + kLazyRescale)) {
+        const float m_new = fmaxf(m_run[qb], mx);
+        const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run[qb] - m_new);
+        m_run[qb] = m_new;
+        l_run[qb] *= alpha;
+#pragma unroll
+        for (int d = 0; d < 8; ++d) acc_o[qb][d] *= alpha;
+      }
+      const float base = (m_run[qb] == -INFINITY) ? 0.f : m_run[qb];
       float rs = 0.f;
       uint32_t pk[2][4];
 #pragma unroll
@@ -265,22 +305,20 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
         pk[kb >> 1][(kb & 1) * 2 + 0] = pack_bf16x2(p[0], p[1]);
         pk[kb >> 1][(kb & 1) * 2 + 1] = pack_bf16x2(p[2], p[3]);
       }
-      l_run[qb] = l_run[qb] * alpha + rs;
-#pragma unroll
-      for (int d = 0; d < 8; ++d) acc_o[qb][d] *= alpha;
+      l_run[qb] += rs;
 #pragma unroll
       for (int ch = 0; ch < 2; ++ch) {
         uint4 u = make_uint4(pk[ch][0], pk[ch][1], pk[ch][2], pk[ch][3]);
         pf[qb][ch] = *reinterpret_cast<bf16x8_t*>(&u);
       }
     }
-    // O^T[d] += V^T[d block] P^T
+    // O^T[d] += V^T[d block][keys] P^T
 #pragma unroll
     for (int ch = 0; ch < 2; ++ch) {
 #pragma unroll
       for (int d = 0; d < 8; ++d) {
         const bf16x8_t va = *reinterpret_cast<const bf16x8_t*>(
-            &s_v[buf][(d * 16 + l16) * kVStride + ch * 32 + g4 * 8]);
+            &sv[(d * 16 + l16) * kVStride + ch * 32 + g4 * 8]);
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
           acc_o[qb][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pf[qb][ch], acc_o[qb][d], 0, 0, 0);
@@ -288,23 +326,54 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
     }
   }
 
-  // write the split's partial: O unnormalized [rows][dh] f32, (m, l) per row
+  // ---- merge the two key halves of each row group through LDS, then write
+  // the split's partial: O unnormalized [rows][dh] f32, (m, l) per row
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    float l = l_run[qb];
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+    l_run[qb] += __shfl_xor(l_run[qb], 16);
+    l_run[qb] += __shfl_xor(l_run[qb], 32);
+  }
+  __syncthreads();                       // every wave is done with the tiles
+  float* s_o = reinterpret_cast<float*>(smem) + rg * (32 * kDh + 64);
+  float* s_ml = s_o + 32 * kDh;
+  if (kh == 1) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+      for (int d = 0; d < 8; ++d)
+        *reinterpret_cast<f32x4_t*>(&s_o[(qb * 16 + l16) * kDh + d * 16 + g4 * 4]) = acc_o[qb][d];
+      if (g4 == 0) {
+        s_ml[(qb * 16 + l16) * 2 + 0] = m_run[qb];
+        s_ml[(qb * 16 + l16) * 2 + 1] = l_run[qb];
+      }
+    }
+  }
+  __syncthreads();
+  if (kh == 1) return;
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const float m1 = s_ml[(qb * 16 + l16) * 2 + 0], l1 = s_ml[(qb * 16 + l16) * 2 + 1];
+    const float M = fmaxf(m_run[qb], m1);
+    const float base = (M == -INFINITY) ? 0.f : M;
+    const float f0 = __builtin_amdgcn_exp2f(m_run[qb] - base), f1 = __builtin_amdgcn_exp2f(m1 - base);
+    const float l = l_run[qb] * f0 + l1 * f1;
     const int r = row0 + qb * 16 + l16;
     if (r >= rows_total) continue;
-    const int64_t prow = (static_cast<int64_t>(split) * gridDim.z + bh) * rows_total + r;
+    const int64_t prow = (static_cast<int64_t>(split) * BH + bh) * rows_total + r;
     float* dst = o_part + prow * kDh;
 #pragma unroll
-    for (int d = 0; d < 8; ++d)
+    for (int d = 0; d < 8; ++d) {
+      const f32x4_t o1 = *reinterpret_cast<const f32x4_t*>(&s_o[(qb * 16 + l16) * kDh + d * 16 + g4 * 4]);
       *reinterpret_cast<float4*>(dst + d * 16 + g4 * 4) =
-          make_float4(acc_o[qb][d][0], acc_o[qb][d][1], acc_o[qb][d][2], acc_o[qb][d][3]);
-    if (g4 == 0) ml_part[prow] = AttnPartialML{m_run[qb], l};
+          make_float4(acc_o[qb][d][0] * f0 + o1[0] * f1, acc_o[qb][d][1] * f0 + o1[1] * f1,
+                      acc_o[qb][d][2] * f0 + o1[2] * f1, acc_o[qb][d][3] * f0 + o1[3] * f1);
+    }
+    if (g4 == 0) ml_part[prow] = AttnPartialML{M, l};
   }
 }
+
+constexpr size_t kAttnSmemBytes = (2 * kKTileElems + 2 * kVTileElems) * sizeof(bf16_t);
+static_assert(4 * (32 * kDh + 64) * sizeof(float) <= kAttnSmemBytes, "merge scratch fits");
 
 // Merge the KV splits of every packed row and write out [B, Lq, Hq, dh].
 template <typename T>
@@ -413,21 +482,28 @@ dg_status launch_attention(const AttnArgs& a, void* ws, hipStream_t stream) {
   char* w = static_cast<char*>(ws);
   void* qrot = w;
   if (a.dtype == DG_BF16) {
+    const float scale_log2 = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(a.dh)));
     rope_kernel<bf16_t><<<a.B * a.Lq, rope_threads(a.dh), 0, stream>>>(
         static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.k_new),
         static_cast<const bf16_t*>(a.v_new), a.q_stride, a.kv_stride,
         static_cast<bf16_t*>(qrot), static_cast<bf16_t*>(a.k_cache),
         static_cast<bf16_t*>(a.v_cache), a.prefix_len, a.Lq, a.Hq, a.Hkv, a.dh, a.Tmax,
-        a.rope_theta);
+        a.rope_theta, scale_log2);
     DG_LAUNCH_CHECK();
     float* o_part = reinterpret_cast<float*>(w + p.q_bytes);
     AttnPartialML* ml = reinterpret_cast<AttnPartialML*>(w + p.q_bytes + p.o_bytes);
-    const float scale_log2 = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(a.dh)));
-    dim3 grid(p.tiles, p.nsplit, a.B * a.Hkv);
-    attn_mfma_kernel<<<grid, 256, 0, stream>>>(
+    const int total = p.tiles * p.nsplit * a.B * a.Hkv;
+    static bool smem_set = false;     // once per process (one device kernel)
+    if (!smem_set) {
+      DG_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(attn_mfma_kernel),
+                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                 static_cast<int>(kAttnSmemBytes)));
+      smem_set = true;
+    }
+    attn_mfma_kernel<<<(total + 7) / 8 * 8, 512, kAttnSmemBytes, stream>>>(
         static_cast<const bf16_t*>(qrot), static_cast<const bf16_t*>(a.k_cache),
         static_cast<const bf16_t*>(a.v_cache), a.prefix_len, a.Lq, G, a.Hkv, a.Tmax, p.chunk,
-        p.nsplit, a.mask_mode == DG_MASK_CAUSAL, scale_log2, o_part, ml);
+        p.tiles, p.nsplit, a.B * a.Hkv, a.mask_mode == DG_MASK_CAUSAL, o_part, ml);
     DG_LAUNCH_CHECK();
     attn_combine_kernel<bf16_t><<<dim3(rows, a.B * a.Hkv), 128, 0, stream>>>(
         o_part, ml, p.nsplit, a.B * a.Hkv, rows, G, a.Hkv, a.Lq, a.dh,
@@ -438,7 +514,7 @@ dg_status launch_attention(const AttnArgs& a, void* ws, hipStream_t stream) {
         static_cast<const float*>(a.q), static_cast<const float*>(a.k_new),
         static_cast<const float*>(a.v_new), a.q_stride, a.kv_stride, static_cast<float*>(qrot),
         static_cast<float*>(a.k_cache), static_cast<float*>(a.v_cache), a.prefix_len, a.Lq,
-        a.Hq, a.Hkv, a.dh, a.Tmax, a.rope_theta);
+        a.Hq, a.Hkv, a.dh, a.Tmax, a.rope_theta, 1.f);
     DG_LAUNCH_CHECK();
     attn_f32_kernel<<<dim3(rows, a.B * a.Hkv), 64, 0, stream>>>(
         static_cast<const float*>(qrot), static_cast<const float*>(a.k_cache),
@@ -457,12 +533,12 @@ dg_status launch_commit(const void* k_new, const void* v_new, int64_t kv_stride,
     rope_kernel<bf16_t><<<B * L, rope_threads(dh), 0, stream>>>(
         nullptr, static_cast<const bf16_t*>(k_new), static_cast<const bf16_t*>(v_new), 0,
         kv_stride, nullptr, static_cast<bf16_t*>(k_cache), static_cast<bf16_t*>(v_cache),
-        prefix_len, L, Hkv, Hkv, dh, Tmax, rope_theta);
+        prefix_len, L, Hkv, Hkv, dh, Tmax, rope_theta, 1.f);
   else
     rope_kernel<float><<<B * L, rope_threads(dh), 0, stream>>>(
         nullptr, static_cast<const float*>(k_new), static_cast<const float*>(v_new), 0,
         kv_stride, nullptr, static_cast<float*>(k_cache), static_cast<float*>(v_cache),
-        prefix_len, L, Hkv, Hkv, dh, Tmax, rope_theta);
+        prefix_len, L, Hkv, Hkv, dh, Tmax, rope_theta, 1.f);
   DG_LAUNCH_CHECK();
   if (advance) return launch_advance_prefix(prefix_len, B, L, stream);
   return DG_OK;

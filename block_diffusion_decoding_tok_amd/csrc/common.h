@@ -33,15 +33,18 @@ typedef uint16_t bf16_t;   // raw bits
 __device__ __forceinline__ float bf16_to_f32(bf16_t h) {
   return __uint_as_float(static_cast<uint32_t>(h) << 16);
 }
-// Round-to-nearest-even float -> bf16 (NaN stays NaN).
-__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x40);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<bf16_t>(u >> 16);
-}
+// Round-to-nearest-even float -> bf16 with the hardware pair conversion
+// (v_cvt_pk_bf16_f32).  Over all 2^32 inputs it equals the integer rule
+// u + 0x7fff + ((u >> 16) & 1) >> 16 for non-NaN u, and (u >> 16) | 0x40 for
+// NaN (quieted, payload kept), denormals included.
+typedef float f32x2_cvt_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_cvt_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+  const f32x2_cvt_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_cvt_t));
+}
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  return __builtin_bit_cast(bf16_t, static_cast<__bf16>(f));
 }
 
 // Element loads/stores for the two activation types.
@@ -79,6 +82,15 @@ __device__ __forceinline__ void rope_cos_sin(int pos, int j, int dh, float theta
   ang -= two_pi * rint(ang / two_pi);
   float a = static_cast<float>(ang);
   sincosf(a, s, c);
+}
+
+// Logical workgroup index for a grid of a multiple of 8 workgroups:
+// hardware deals linear workgroup ids round-robin over the 8 XCDs, so this
+// gives each XCD one contiguous range of logical indices (work items that
+// share operands, placed at adjacent logical indices, share one L2).
+__device__ __forceinline__ int xcd_logical_tile(int linear, int total) {
+  const int per = (total + 7) / 8;
+  return (linear % 8) * per + linear / 8;
 }
 
 }  // namespace dg

@@ -117,14 +117,6 @@ struct WRow {
   __device__ const WT* at(int c) const { return base + c * (TILED ? 1024 : 64); }
 };
 
-// Logical workgroup index: consecutive logical tiles go to the same XCD
-// (hardware dispatches linear workgroup ids round-robin over 8 XCDs), so the
-// row tiles that share a token tile share that XCD's L2.
-__device__ __forceinline__ int xcd_logical_tile(int linear, int total) {
-  const int per = (total + 7) / 8;
-  return (linear % 8) * per + linear / 8;
-}
-
 template <int RT, int TB, int KS, int PF, bool FP8, int MODE, bool TILED>
 __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
   using WT = typename std::conditional<FP8, uint8_t, bf16_t>::type;
