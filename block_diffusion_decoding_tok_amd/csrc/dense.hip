@@ -1,9 +1,10 @@
 // Dense projections (QKV, O, router, LM head), RMSNorm and the embedding
 // gather of the decoder layer.
 //
-//   bf16: gemm_stream_kernel (gemm_mfma.h) in dense mode -- 64 weight rows x
-//         64 tokens per workgroup (16 tokens for narrow outputs), the token
-//         tiles of the same rows adjacent so they share one XCD's L2.
+//   bf16: projections -- gemm_splitk_kernel (gemm_mfma.h), 64 weight rows x
+//         64 (or 16) tokens per workgroup, K split over its four waves;
+//         LM head with tile-packed weights -- gemm_wide_kernel below;
+//         other shapes -- gemm_stream_kernel in dense mode.
 //   f32:  plain SIMT kernels (parity path of the tiny fp32 model).
 // RMSNorm: x / sqrt(mean(x^2) + 1e-6), unit gain, f32 statistics.
 #include "common.h"
@@ -33,6 +34,118 @@ __global__ void gemm_f32_kernel(const float* __restrict__ A, const float* __rest
   for (int k = 0; k < K; ++k) acc = fmaf(a[k], w[k], acc);
   float* c = C + static_cast<int64_t>(m) * N + n;
   *c = accumulate ? *c + acc : acc;
+}
+
+// Vocabulary-sized outputs with tile-packed weights (the LM head): one
+// workgroup of 8 waves computes a 256-row x 256-token block of C^T, the
+// weights read from HBM exactly once.  Per 64-k stage both operands pass
+// through LDS (double buffered, staged in registers one stage ahead): the
+// weight stage is the 16 tiles' packed 2 KB chunks copied as they are (the
+// MFMA A-operand lane order), the token stage is 256 rows of 64 k with a
+// 16-byte pad.  Wave (wr, wt) owns rows 128 wr .. +128 and tokens 64 wt ..
+// +64: 32 accumulator blocks of 16 x 16, 12 KB of LDS reads per 32 MFMAs,
+// below the LDS bandwidth at two waves per SIMD.
+constexpr int kWideRows = 256, kWideTok = 256;
+constexpr int kWideXStride = 64 + 8;                         // elements
+constexpr int kWideWStage = kWideRows * 64;                  // elements
+constexpr int kWideXStage = kWideTok * kWideXStride;         // elements
+constexpr size_t kWideSmemBytes = 2 * (kWideWStage + kWideXStage) * sizeof(bf16_t);
+
+// Registers of one stage: W pieces (four 16-byte pieces of the 16 tiles'
+// packed chunks) and X pieces (token = item / 8, piece = item % 8; rows past
+// M clamped).
+struct WideStage {
+  uint4 w0, w1, w2, w3, x0, x1, x2, x3;
+};
+
+__device__ __forceinline__ void wide_load_stage(WideStage& st, const bf16_t* wsrc,
+                                                const bf16_t* X, int c, int K, int M, int m0,
+                                                int tid) {
+  auto wl = [&](int it) {
+    const int item = it * 512 + tid;                   // 16-byte piece of the stage
+    const int tile = item >> 7, piece = item & 127;    // 128 pieces per 2 KB chunk
+    return *reinterpret_cast<const uint4*>(
+        wsrc + (static_cast<int64_t>(tile) * (K / 64) + c) * 1024 + piece * 8);
+  };
+  auto xl = [&](int it) {
+    const int item = it * 512 + tid;
+    const int tok = min(m0 + (item >> 3), M - 1);
+    return *reinterpret_cast<const uint4*>(X + static_cast<int64_t>(tok) * K + c * 64 + (item & 7) * 8);
+  };
+  st.w0 = wl(0); st.w1 = wl(1); st.w2 = wl(2); st.w3 = wl(3);
+  st.x0 = xl(0); st.x1 = xl(1); st.x2 = xl(2); st.x3 = xl(3);
+}
+
+__device__ __forceinline__ void wide_store_stage(const WideStage& st, bf16_t* sw, bf16_t* sx,
+                                                 int tid) {
+  auto put = [&](int it, const uint4& w, const uint4& x) {
+    const int item = it * 512 + tid;
+    *reinterpret_cast<uint4*>(sw + item * 8) = w;
+    *reinterpret_cast<uint4*>(sx + (item >> 3) * kWideXStride + (item & 7) * 8) = x;
+  };
+  put(0, st.w0, st.x0); put(1, st.w1, st.x1); put(2, st.w2, st.x2); put(3, st.w3, st.x3);
+}
+
+__global__ __launch_bounds__(512) void gemm_wide_kernel(const bf16_t* __restrict__ W,
+                                                        const bf16_t* __restrict__ X,
+                                                        bf16_t* __restrict__ C, int M, int N,
+                                                        int K) {
+  extern __shared__ __attribute__((aligned(16))) bf16_t wsm[];
+  auto s_w = [&](int buf) { return wsm + buf * kWideWStage; };
+  auto s_x = [&](int buf) { return wsm + 2 * kWideWStage + buf * kWideXStage; };
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const int wr = wave & 1, wt = wave >> 1;
+  const int n0 = blockIdx.x * kWideRows;
+  const int m0 = blockIdx.y * kWideTok;
+  const int nchunks = K / 64;
+
+  const bf16_t* wsrc = W + static_cast<int64_t>(n0 / 16) * (K / 64) * 1024;
+  WideStage st;
+  f32x4_v acc[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+
+  wide_load_stage(st, wsrc, X, 0, K, M, m0, tid);
+  for (int c = 0; c < nchunks; ++c) {
+    const int buf = c & 1;
+    wide_store_stage(st, s_w(buf), s_x(buf), tid);
+    __syncthreads();
+    if (c + 1 < nchunks) wide_load_stage(st, wsrc, X, c + 1, K, M, m0, tid);
+    const bf16_t* sw = s_w(buf) + wr * 8 * 1024;
+    const bf16_t* sx = s_x(buf) + (wt * 64) * kWideXStride;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {            // the two 8-value halves of a lane's 16 k
+      bf16x8_v xb[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        xb[j] = *reinterpret_cast<const bf16x8_v*>(sx + (j * 16 + l16) * kWideXStride + g4 * 16 + h * 8);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const bf16x8_v wa = *reinterpret_cast<const bf16x8_v*>(sw + i * 1024 + h * 512 + lane * 8);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, xb[j], acc[i][j], 0, 0, 0);
+      }
+    }
+  }
+
+  // epilogue: lane holds rows 4 g4 + r of row tile i, token l16 of block j
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int m = m0 + wt * 64 + j * 16 + l16;
+    if (m >= M) continue;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int n = n0 + wr * 128 + i * 16 + g4 * 4;
+      uint2 pk;
+      pk.x = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
+      pk.y = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
+      *reinterpret_cast<uint2*>(C + static_cast<int64_t>(m) * N + n) = pk;
+    }
+  }
 }
 
 template <bool TILED>
@@ -66,7 +179,19 @@ dg_status launch_gemm(const void* A, const void* W, void* C, int M, int N, int K
 
 template <bool TILED>
 static void launch_gemm_bf16(GemmArgs& g, int M, int N, int K, hipStream_t stream) {
-  if (N >= 32768) {
+  if (TILED && N >= 32768 && N % kWideRows == 0 && K % 64 == 0 && !g.accumulate &&
+      g.out_dtype == DG_BF16) {
+    static bool smem_set = false;      // once per process
+    if (!smem_set) {
+      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_wide_kernel),
+                                hipFuncAttributeMaxDynamicSharedMemorySize,
+                                static_cast<int>(kWideSmemBytes));
+      smem_set = true;
+    }
+    dim3 grid(N / kWideRows, (M + kWideTok - 1) / kWideTok);
+    gemm_wide_kernel<<<grid, 512, kWideSmemBytes, stream>>>(
+        static_cast<const bf16_t*>(g.W), g.X, static_cast<bf16_t*>(g.out), M, N, K);
+  } else if (N >= 32768) {
     g.n_tiles_x = N / (64 * kWideRT);
     g.n_tiles_y = (M + 16 * kWideTB - 1) / (16 * kWideTB);
     g.n_tiles_total = g.n_tiles_x * g.n_tiles_y;
@@ -93,9 +218,51 @@ static void launch_gemm_bf16(GemmArgs& g, int M, int N, int K, hipStream_t strea
   }
 }
 
+// One row per workgroup; the row stays in registers (float4 pieces) between
+// the sum of squares and the scaled store, so x is read once.
+constexpr int kNormPieces = 4;     // float4 pieces per thread: D <= 4096
+
 template <typename TO>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ x,
                                                       TO* __restrict__ out, int D) {
+  const int row = blockIdx.x;
+  const float4* xr = reinterpret_cast<const float4*>(x + static_cast<int64_t>(row) * D);
+  const int n4 = D / 4;
+  float4 v[kNormPieces];
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < kNormPieces; ++i) {
+    const int p = i * 256 + threadIdx.x;
+    v[i] = p < n4 ? xr[p] : make_float4(0.f, 0.f, 0.f, 0.f);
+    ss = fmaf(v[i].x, v[i].x, fmaf(v[i].y, v[i].y, fmaf(v[i].z, v[i].z, fmaf(v[i].w, v[i].w, ss))));
+  }
+  ss = warp_sum(ss);
+  __shared__ float s_part[4];
+  if ((threadIdx.x & 63) == 0) s_part[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float tot = s_part[0] + s_part[1] + s_part[2] + s_part[3];
+  const float inv = rsqrtf(tot / D + 1e-6f);
+  TO* o = out + static_cast<int64_t>(row) * D;
+#pragma unroll
+  for (int i = 0; i < kNormPieces; ++i) {
+    const int p = i * 256 + threadIdx.x;
+    if (p >= n4) continue;
+    if constexpr (sizeof(TO) == 2) {
+      uint2 pk;
+      pk.x = pack_bf16x2(v[i].x * inv, v[i].y * inv);
+      pk.y = pack_bf16x2(v[i].z * inv, v[i].w * inv);
+      *reinterpret_cast<uint2*>(o + 4 * p) = pk;
+    } else {
+      *reinterpret_cast<float4*>(o + 4 * p) =
+          make_float4(v[i].x * inv, v[i].y * inv, v[i].z * inv, v[i].w * inv);
+    }
+  }
+}
+
+// Rows wider than the register-resident kernel holds, or not a multiple of 4.
+template <typename TO>
+__global__ __launch_bounds__(256) void rmsnorm_wide_kernel(const float* __restrict__ x,
+                                                           TO* __restrict__ out, int D) {
   const int row = blockIdx.x;
   const float* xr = x + static_cast<int64_t>(row) * D;
   float ss = 0.f;
@@ -112,10 +279,14 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
 
 dg_status launch_rmsnorm(const float* x, void* out, int M, int D, int out_dtype,
                          hipStream_t stream) {
-  if (out_dtype == DG_BF16)
-    rmsnorm_kernel<bf16_t><<<M, 256, 0, stream>>>(x, static_cast<bf16_t*>(out), D);
-  else
-    rmsnorm_kernel<float><<<M, 256, 0, stream>>>(x, static_cast<float*>(out), D);
+  const bool regs = D % 4 == 0 && D / 4 <= kNormPieces * 256;
+  if (out_dtype == DG_BF16) {
+    if (regs) rmsnorm_kernel<bf16_t><<<M, 256, 0, stream>>>(x, static_cast<bf16_t*>(out), D);
+    else rmsnorm_wide_kernel<bf16_t><<<M, 256, 0, stream>>>(x, static_cast<bf16_t*>(out), D);
+  } else {
+    if (regs) rmsnorm_kernel<float><<<M, 256, 0, stream>>>(x, static_cast<float*>(out), D);
+    else rmsnorm_wide_kernel<float><<<M, 256, 0, stream>>>(x, static_cast<float*>(out), D);
+  }
   DG_LAUNCH_CHECK();
   return DG_OK;
 }
