@@ -35,4 +35,21 @@ dg_status dg_pack_weights(const void* src, void* dst, int64_t groups, int N, int
                              static_cast<hipStream_t>(stream));
 }
 
+dg_status dg_linear(const void* x, const void* w, void* out, int M, int N, int K, int dtype,
+                    int w_layout, int out_dtype, int accumulate, void* stream) {
+  set_error("");
+  DG_CHECK_ARG(x && w && out, "dg_linear: null pointer");
+  DG_CHECK_ARG(dtype == DG_BF16 || dtype == DG_F32, "dg_linear: dtype must be DG_BF16 or DG_F32");
+  DG_CHECK_ARG(w_layout == DG_LAYOUT_ROWMAJOR || (w_layout == DG_LAYOUT_TILED && dtype == DG_BF16),
+               "dg_linear: bad w_layout (tiled needs bf16)");
+  DG_CHECK_ARG(out_dtype == DG_F32 || (out_dtype == DG_BF16 && dtype == DG_BF16),
+               "dg_linear: out_dtype must be DG_F32, or DG_BF16 with bf16 inputs");
+  DG_CHECK_ARG(!accumulate || out_dtype == DG_F32, "dg_linear: accumulate needs an f32 output");
+  DG_CHECK_SHAPE(M > 0 && N > 0 && K > 0, "dg_linear: sizes must be positive");
+  if (dtype == DG_BF16)
+    DG_CHECK_SHAPE(N % 64 == 0 && K % 64 == 0, "dg_linear: bf16 needs N % 64 == 0 and K % 64 == 0");
+  return launch_gemm(x, w, out, M, N, K, dtype, w_layout, out_dtype,
+                     accumulate ? kAccumulateF32 : kStore, static_cast<hipStream_t>(stream));
+}
+
 }  // extern "C"

@@ -13,8 +13,12 @@
 
 namespace dg {
 
-// projection-sized outputs (QKV, O, router): split-K register streaming
+// projection-sized outputs (QKV, O, router): split-K register streaming,
+// ring of kSplitNR chunks; wide outputs: 16 kProjRT rows x 16 kProjTB tokens
+// per workgroup, K split over kProjNW waves; narrow outputs (router): 32 rows
+// x 16 tokens, K split over eight waves
 constexpr int kSplitNR = 2;
+constexpr int kProjRT = 8, kProjTB = 2, kProjNW = 4;
 // other shapes: 64 rows x 64 tokens per workgroup, LDS-staged tokens
 constexpr int kDenseRT = 1, kDenseTB = 4, kDenseKS = 2, kDensePF = 2;
 // up to 256 tokens: register streaming, 16 tokens per tile, ring of 4 chunks
@@ -191,24 +195,23 @@ static void launch_gemm_bf16(GemmArgs& g, int M, int N, int K, hipStream_t strea
     dim3 grid(N / kWideRows, (M + kWideTok - 1) / kWideTok);
     gemm_wide_kernel<<<grid, 512, kWideSmemBytes, stream>>>(
         static_cast<const bf16_t*>(g.W), g.X, static_cast<bf16_t*>(g.out), M, N, K);
-  } else if (N >= 32768) {
+  } else if (N >= 32768 && N % (64 * kWideRT) == 0) {
     g.n_tiles_x = N / (64 * kWideRT);
     g.n_tiles_y = (M + 16 * kWideTB - 1) / (16 * kWideTB);
     g.n_tiles_total = g.n_tiles_x * g.n_tiles_y;
     gemm_stream_kernel<kWideRT, kWideTB, kWideKS, kWidePF, false, kDense, TILED>
         <<<(g.n_tiles_total + 7) / 8 * 8, 256, 0, stream>>>(g);
-  } else if (K % 256 == 0 && N % 64 == 0) {
-    // projections: 64 rows x 64 tokens per workgroup, K split over its waves
-    // (16-token tiles when the output is too narrow to fill the chip)
+  } else if (K % 64 == 0 && K >= 64 * 8 && N % (16 * kProjRT) == 0 && N % 32 == 0) {
     const bool narrow = N < 1024;
-    g.n_tiles_x = N / 64;
-    g.n_tiles_y = narrow ? (M + 15) / 16 : (M + 63) / 64;
+    g.n_tiles_x = narrow ? N / 32 : N / (16 * kProjRT);
+    g.n_tiles_y = narrow ? (M + 15) / 16 : (M + 16 * kProjTB - 1) / (16 * kProjTB);
     g.n_tiles_total = g.n_tiles_x * g.n_tiles_y;
     const unsigned grid = (g.n_tiles_total + 7) / 8 * 8;
     if (narrow)
-      gemm_splitk_kernel<4, 1, kSplitNR, TILED><<<grid, 256, 0, stream>>>(g);
+      gemm_splitk_kernel<2, 1, kSplitNR, 8, TILED><<<grid, 512, 0, stream>>>(g);
     else
-      gemm_splitk_kernel<4, 4, kSplitNR, TILED><<<grid, 256, 0, stream>>>(g);
+      gemm_splitk_kernel<kProjRT, kProjTB, kSplitNR, kProjNW, TILED>
+          <<<grid, 64 * kProjNW, 0, stream>>>(g);
   } else {
     g.n_tiles_x = N / (64 * kDenseRT);
     g.n_tiles_y = (M + 16 * kDenseTB - 1) / (16 * kDenseTB);

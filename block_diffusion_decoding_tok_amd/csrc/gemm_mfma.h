@@ -549,15 +549,17 @@ namespace dg {
 
 // Dense GEMM for canvas-sized token counts (M <= 1024), bf16 weights:
 // out[m, n] = sum_k X[m, k] W[n, k].  A workgroup owns a tile of 16 * RT
-// weight rows x 16 * TB tokens; its four waves split K into quarters
-// (K % 256 == 0), so a projection with few output tiles still fills the
-// chip, and each wave streams its weight rows and token rows through a
-// register ring of NR chunks (unconditional loads, pinned issue order).  The
-// four partial accumulators are summed through LDS in wave order (fixed
-// order: deterministic), each wave finishing RT / 4 of the row tiles.
-template <int RT, int TB, int NR, bool TILED>
-__global__ __launch_bounds__(256) void gemm_splitk_kernel(GemmArgs a) {
-  static_assert(RT % 4 == 0, "each wave finishes RT / 4 row tiles");
+// weight rows x 16 * TB tokens; its NW waves split the K / 64 chunks into NW
+// contiguous ranges (K % 64 == 0), so a projection with few output tiles
+// still fills the chip, and each wave streams its weight rows and token rows
+// through a register ring of NR chunks (unconditional loads, pinned issue
+// order).  The NW partial accumulators are summed through LDS in wave order
+// (fixed order: deterministic), one thread per (row tile, token block, lane)
+// quad of outputs.
+template <int RT, int TB, int NR, int NW, bool TILED>
+__global__ __launch_bounds__(64 * NW) void gemm_splitk_kernel(GemmArgs a) {
+  static_assert(RT * TB * 64 <= 64 * NW * 4, "at most four output quads per thread");
+  static_assert(NW == 4 || NW == 8, "four or eight waves");
   __shared__ __attribute__((aligned(16))) float s_acc[4][RT * TB * 4][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g4 = lane >> 4;
@@ -567,22 +569,21 @@ __global__ __launch_bounds__(256) void gemm_splitk_kernel(GemmArgs a) {
   const int ty = logical % a.n_tiles_y;
   const int m0 = ty * 16 * TB;
   const int n0 = tx * 16 * RT;
-  const int Kq = a.K / 4;
-  const int k_begin = wave * Kq;
-  const int nchunks = Kq / 64;
+  const int nch_all = a.K / 64;
+  const int c_begin = wave * nch_all / NW;
+  const int nchunks = (wave + 1) * nch_all / NW - c_begin;   // >= 1 when K >= 64 * NW
 
   const bf16_t* W = static_cast<const bf16_t*>(a.W);
   WRow<bf16_t, TILED> wp[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) wp[rt].init(W, n0 + rt * 16, a.K, lane);
-  const int c_begin = k_begin / 64;
   const bf16_t* xp[TB];
   bool xok[TB];
 #pragma unroll
   for (int tb = 0; tb < TB; ++tb) {
     const int m = m0 + tb * 16 + l16;
     xok[tb] = m < a.M;
-    xp[tb] = a.X + static_cast<int64_t>(xok[tb] ? m : m0) * a.K + k_begin + g4 * 16;
+    xp[tb] = a.X + static_cast<int64_t>(xok[tb] ? m : m0) * a.K + c_begin * 64 + g4 * 16;
   }
 
   struct Slot {
@@ -640,43 +641,68 @@ __global__ __launch_bounds__(256) void gemm_splitk_kernel(GemmArgs a) {
     }
   }
 
-  // ---- deterministic split-K reduction through LDS
+  // ---- deterministic split-K reduction through LDS: with eight waves, wave
+  // w + 4 hands its partial to wave w first; then the four partials are
+  // summed in wave order
+  if (NW == 8) {
+    if (wave >= 4) {
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt)
+      for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-    for (int tb = 0; tb < TB; ++tb)
+        for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) s_acc[wave][(rt * TB + tb) * 4 + r][lane] = acc[rt][tb][r];
+          for (int r = 0; r < 4; ++r) s_acc[wave - 4][(rt * TB + tb) * 4 + r][lane] = acc[rt][tb][r];
+    }
+    __syncthreads();
+    if (wave < 4) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[rt][tb][r] += s_acc[wave][(rt * TB + tb) * 4 + r][lane];
+    }
+    __syncthreads();
+  }
+  if (wave < 4) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s_acc[wave][(rt * TB + tb) * 4 + r][lane] = acc[rt][tb][r];
+  }
   __syncthreads();
+  constexpr int kQuads = RT * TB * 64;          // (row tile, token block, lane) quads
 #pragma unroll
-  for (int q = 0; q < RT / 4; ++q) {
-    const int rt = wave * (RT / 4) + q;
-    const int n = n0 + rt * 16 + g4 * 4;
+  for (int q0 = 0; q0 < kQuads; q0 += 64 * NW) {
+    const int q = q0 + tid;
+    if (q >= kQuads) break;
+    const int ql = q & 63, blk = q >> 6;        // blk = rt * TB + tb
+    const int rt = blk / TB, tb = blk % TB;
+    const int n = n0 + rt * 16 + (ql >> 4) * 4;
+    const int m = m0 + tb * 16 + (ql & 15);
+    float v[4];
 #pragma unroll
-    for (int tb = 0; tb < TB; ++tb) {
-      const int m = m0 + tb * 16 + l16;
-      float v[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int idx = (rt * TB + tb) * 4 + r;
-        v[r] = ((s_acc[0][idx][lane] + s_acc[1][idx][lane]) + s_acc[2][idx][lane]) + s_acc[3][idx][lane];
-      }
-      if (m >= a.M) continue;
-      if (a.out_dtype == DG_F32) {
-        float* o = static_cast<float*>(a.out) + static_cast<int64_t>(m) * a.N + n;
-        if (a.accumulate) {
-          const float4 c = *reinterpret_cast<float4*>(o);
-          *reinterpret_cast<float4*>(o) = make_float4(c.x + v[0], c.y + v[1], c.z + v[2], c.w + v[3]);
-        } else {
-          *reinterpret_cast<float4*>(o) = make_float4(v[0], v[1], v[2], v[3]);
-        }
+    for (int r = 0; r < 4; ++r) {
+      v[r] = ((s_acc[0][blk * 4 + r][ql] + s_acc[1][blk * 4 + r][ql]) + s_acc[2][blk * 4 + r][ql]) +
+             s_acc[3][blk * 4 + r][ql];
+    }
+    if (m >= a.M) continue;
+    if (a.out_dtype == DG_F32) {
+      float* o = static_cast<float*>(a.out) + static_cast<int64_t>(m) * a.N + n;
+      if (a.accumulate) {
+        const float4 c = *reinterpret_cast<float4*>(o);
+        *reinterpret_cast<float4*>(o) = make_float4(c.x + v[0], c.y + v[1], c.z + v[2], c.w + v[3]);
       } else {
-        bf16_t* o = static_cast<bf16_t*>(a.out) + static_cast<int64_t>(m) * a.N + n;
-        uint2 pk;
-        pk.x = pack_bf16x2(v[0], v[1]);
-        pk.y = pack_bf16x2(v[2], v[3]);
-        *reinterpret_cast<uint2*>(o) = pk;
+        *reinterpret_cast<float4*>(o) = make_float4(v[0], v[1], v[2], v[3]);
       }
+    } else {
+      bf16_t* o = static_cast<bf16_t*>(a.out) + static_cast<int64_t>(m) * a.N + n;
+      uint2 pk;
+      pk.x = pack_bf16x2(v[0], v[1]);
+      pk.y = pack_bf16x2(v[2], v[3]);
+      *reinterpret_cast<uint2*>(o) = pk;
     }
   }
 }

@@ -87,6 +87,7 @@ _SIGS = {
     "dg_moe_down": (_I, [_VP, _I, _VP, _I, _I, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _VP,
                          _VP]),
     "dg_moe_combine": (_I, [_VP, _I, _I, _I, _I, _VP, _VP]),
+    "dg_linear": (_I, [_VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _I, _VP]),
     "dg_ctx_workspace_size": (_SZ, [C.POINTER(dg_model_dims), _I, _I]),
     "dg_ctx_create": (_I, [C.POINTER(_VP), C.POINTER(dg_model_dims),
                            C.POINTER(dg_model_weights), _I, _I, _VP, _SZ]),
@@ -345,6 +346,21 @@ def dg_moe_combine(y_slot, k, y, stream=None):
     _check(lib().dg_moe_combine(_dev(y_slot, "y_slot"), _dtype_code(y_slot), T, D, k,
                                 _dev(y, "y", (torch.float32,)), _stream(stream)))
     return y
+
+
+def dg_linear(x, w, out=None, out_dtype=None, accumulate=False, stream=None,
+              w_layout=DG_LAYOUT_ROWMAJOR, N=None):
+    """out [M, N] (=|+=) x [M, K] @ w[N, K]^T; w may be tile-packed (pass N
+    or keep w's logical shape)."""
+    M, K = x.shape
+    N = w.shape[0] if N is None else N
+    if out is None:
+        od = out_dtype if out_dtype is not None else x.dtype
+        out = torch.zeros((M, N), dtype=od, device=x.device)
+    _check(lib().dg_linear(_dev(x, "x"), _dev(w, "w"), _dev(out, "out"), M, N, K,
+                           _dtype_code(x), int(w_layout), _dtype_code(out), int(bool(accumulate)),
+                           _stream(stream)))
+    return out
 
 
 # ---------------------------------------------------------- whole decoder

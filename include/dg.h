@@ -309,6 +309,19 @@ dg_status dg_denoise_block(dg_ctx* ctx, const dg_sampler_cfg* cfg, int B, void* 
                            void* const* v_caches, int Tmax, int32_t* prefix_len,
                            int32_t* tokens_out, int32_t* steps_taken, void* stream);
 
+/* dg_linear: the dense projections of a layer and the LM head ([TR]
+ * "DiffusionGemma의 구성": a decoder whose layers project with dense matrices;
+ * [GUIDE] "256토큰 Canvas 병렬 생성": the vocabulary logits of every canvas
+ * position): out[m, n] = sum_k x[m, k] w[n, k], or out += that when
+ * accumulate != 0.  The same kernels the decoder uses (QKV, O, router, LM
+ * head).
+ *   x [M, K] in dtype (DG_BF16 or DG_F32); w [N, K] in dtype and w_layout
+ *   (DG_LAYOUT_TILED only with DG_BF16); out [M, N] in out_dtype: DG_BF16 or
+ *   DG_F32 for bf16 inputs, DG_F32 for f32 inputs; accumulate needs DG_F32.
+ *   bf16 inputs need N % 64 == 0 and K % 64 == 0; fp32 accumulation. */
+dg_status dg_linear(const void* x, const void* w, void* out, int M, int N, int K, int dtype,
+                    int w_layout, int out_dtype, int accumulate, void* stream);
+
 /* ------------------------------------------------------------- utilities
  * Seeded synthetic data and checks used by tests and the benchmark. */
 

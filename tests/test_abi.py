@@ -120,3 +120,12 @@ def test_ctx_validation(lib):
     w = dg.dg_model_weights()
     h = C.c_void_p()
     assert lib.dg_ctx_create(C.byref(h), C.byref(dims), C.byref(w), 1, 256, None, 0) == -1
+
+
+def test_linear_rejects_bad_calls(lib):
+    f = C.c_void_p(256)
+    # tiled layout with f32 inputs; accumulate into bf16; bf16 K not a multiple of 64
+    assert lib.dg_linear(f, f, f, 256, 128, 2816, dg.DG_F32, 1, dg.DG_F32, 0, None) == -1
+    assert lib.dg_linear(f, f, f, 256, 128, 2816, dg.DG_BF16, 0, dg.DG_BF16, 1, None) == -1
+    assert lib.dg_linear(f, f, f, 256, 128, 2800, dg.DG_BF16, 0, dg.DG_F32, 0, None) == -2
+    assert lib.dg_linear(None, f, f, 256, 128, 2816, dg.DG_BF16, 0, dg.DG_F32, 0, None) == -1
