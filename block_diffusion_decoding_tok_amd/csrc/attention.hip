@@ -375,32 +375,44 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(
 constexpr size_t kAttnSmemBytes = (2 * kKTileElems + 2 * kVTileElems) * sizeof(bf16_t);
 static_assert(4 * (32 * kDh + 64) * sizeof(float) <= kAttnSmemBytes, "merge scratch fits");
 
-// Merge the KV splits of every packed row and write out [B, Lq, Hq, dh].
+// Merge the KV splits of every packed row and write out [B, Lq, Hq, dh]:
+// 32 threads per row (4 dh each, 16-byte loads), 8 rows per workgroup.
 template <typename T>
-__global__ void attn_combine_kernel(const float* __restrict__ o_part,
-                                    const AttnPartialML* __restrict__ ml_part, int nsplit,
-                                    int BH, int rows_total, int G, int Hkv, int Lq, int dh,
-                                    T* __restrict__ out) {
-  const int r = blockIdx.x, bh = blockIdx.y;
-  const int d = threadIdx.x;
+__global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ o_part,
+                                                           const AttnPartialML* __restrict__ ml_part,
+                                                           int nsplit, int BH, int rows_total,
+                                                           int G, int Hkv, int Lq,
+                                                           T* __restrict__ out) {
+  const int gr = blockIdx.x * 8 + (threadIdx.x >> 5);      // global packed row index
+  const int d4 = (threadIdx.x & 31) * 4;
+  if (gr >= BH * rows_total) return;
+  const int bh = gr / rows_total, r = gr % rows_total;
   float M = -INFINITY;
-  for (int s = 0; s < nsplit; ++s)
-    M = fmaxf(M, ml_part[(static_cast<int64_t>(s) * BH + bh) * rows_total + r].m);
+  for (int sp = 0; sp < nsplit; ++sp)
+    M = fmaxf(M, ml_part[(static_cast<int64_t>(sp) * BH + bh) * rows_total + r].m);
   const float base = (M == -INFINITY) ? 0.f : M;
-  float L = 0.f, acc = 0.f;
-  for (int s = 0; s < nsplit; ++s) {
-    const int64_t prow = (static_cast<int64_t>(s) * BH + bh) * rows_total + r;
+  float L = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int sp = 0; sp < nsplit; ++sp) {
+    const int64_t prow = (static_cast<int64_t>(sp) * BH + bh) * rows_total + r;
     const AttnPartialML ml = ml_part[prow];
     if (ml.l == 0.f) continue;
     const float f = __builtin_amdgcn_exp2f(ml.m - base);
     L += ml.l * f;
-    if (d < dh) acc += o_part[prow * dh + d] * f;
+    const float4 o = *reinterpret_cast<const float4*>(o_part + prow * kDh + d4);
+    acc.x += o.x * f;
+    acc.y += o.y * f;
+    acc.z += o.z * f;
+    acc.w += o.w * f;
   }
-  if (d >= dh) return;
   const int b = bh / Hkv, g = bh % Hkv;
   const int tok = r / G, h = g * G + r % G;
   const int Hq = Hkv * G;
-  Elem<T>::store(out, ((static_cast<int64_t>(b) * Lq + tok) * Hq + h) * dh + d, acc / L);
+  T* dst = out + ((static_cast<int64_t>(b) * Lq + tok) * Hq + h) * kDh + d4;
+  Elem<T>::store(dst, 0, acc.x / L);
+  Elem<T>::store(dst, 1, acc.y / L);
+  Elem<T>::store(dst, 2, acc.z / L);
+  Elem<T>::store(dst, 3, acc.w / L);
 }
 
 // ------------------------------------------------------------- f32 path
@@ -505,9 +517,8 @@ dg_status launch_attention(const AttnArgs& a, void* ws, hipStream_t stream) {
         static_cast<const bf16_t*>(a.v_cache), a.prefix_len, a.Lq, G, a.Hkv, a.Tmax, p.chunk,
         p.tiles, p.nsplit, a.B * a.Hkv, a.mask_mode == DG_MASK_CAUSAL, o_part, ml);
     DG_LAUNCH_CHECK();
-    attn_combine_kernel<bf16_t><<<dim3(rows, a.B * a.Hkv), 128, 0, stream>>>(
-        o_part, ml, p.nsplit, a.B * a.Hkv, rows, G, a.Hkv, a.Lq, a.dh,
-        static_cast<bf16_t*>(a.out));
+    attn_combine_kernel<bf16_t><<<(a.B * a.Hkv * rows + 7) / 8, 256, 0, stream>>>(
+        o_part, ml, p.nsplit, a.B * a.Hkv, rows, G, a.Hkv, a.Lq, static_cast<bf16_t*>(a.out));
     DG_LAUNCH_CHECK();
   } else {
     rope_kernel<float><<<a.B * a.Lq, rope_threads(a.dh), 0, stream>>>(

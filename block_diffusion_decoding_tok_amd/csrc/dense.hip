@@ -225,18 +225,70 @@ static void launch_gemm_bf16(GemmArgs& g, int M, int N, int K, hipStream_t strea
 // the sum of squares and the scaled store, so x is read once.
 constexpr int kNormPieces = 4;     // float4 pieces per thread: D <= 4096
 
-template <typename TO>
-__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ x,
+// With y_slot, the row first takes the MoE combine: x += sum_j y_slot[row *
+// k + j] in slot order, and the updated row is written back.  Every load is
+// issued unconditionally from a clamped address and masked afterwards, so the
+// loads of a row stay in flight together.
+template <typename TS> struct Slot4;
+template <> struct Slot4<bf16_t> {
+  uint2 u;
+  __device__ void load(const bf16_t* p) { u = *reinterpret_cast<const uint2*>(p); }
+  __device__ float4 get() const {
+    return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                       __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+  }
+};
+template <> struct Slot4<float> {
+  float4 f;
+  __device__ void load(const float* p) { f = *reinterpret_cast<const float4*>(p); }
+  __device__ float4 get() const { return f; }
+};
+
+template <typename TS, typename TO>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const TS* __restrict__ y_slot, int k,
+                                                      float* __restrict__ x,
                                                       TO* __restrict__ out, int D) {
   const int row = blockIdx.x;
-  const float4* xr = reinterpret_cast<const float4*>(x + static_cast<int64_t>(row) * D);
+  float4* xr = reinterpret_cast<float4*>(x + static_cast<int64_t>(row) * D);
   const int n4 = D / 4;
   float4 v[kNormPieces];
+#pragma unroll
+  for (int i = 0; i < kNormPieces; ++i) v[i] = xr[min(i * 256 + static_cast<int>(threadIdx.x), n4 - 1)];
+  if (y_slot) {
+    // slots in groups of 8: loads of a group in flight together, added in order
+    for (int j0 = 0; j0 < k; j0 += 8) {
+      Slot4<TS> sv[kNormPieces][8];
+#pragma unroll
+      for (int i = 0; i < kNormPieces; ++i) {
+        const int p = min(i * 256 + static_cast<int>(threadIdx.x), n4 - 1);
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          sv[i][u].load(y_slot + (static_cast<int64_t>(row) * k + min(j0 + u, k - 1)) * D + 4 * p);
+      }
+#pragma unroll
+      for (int i = 0; i < kNormPieces; ++i)
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          if (j0 + u < k) {
+            const float4 a = sv[i][u].get();
+            v[i].x += a.x;
+            v[i].y += a.y;
+            v[i].z += a.z;
+            v[i].w += a.w;
+          }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < kNormPieces; ++i) {
+      const int p = i * 256 + threadIdx.x;
+      if (p < n4) xr[p] = v[i];
+    }
+  }
   float ss = 0.f;
 #pragma unroll
   for (int i = 0; i < kNormPieces; ++i) {
     const int p = i * 256 + threadIdx.x;
-    v[i] = p < n4 ? xr[p] : make_float4(0.f, 0.f, 0.f, 0.f);
+    if (p >= n4) v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
     ss = fmaf(v[i].x, v[i].x, fmaf(v[i].y, v[i].y, fmaf(v[i].z, v[i].z, fmaf(v[i].w, v[i].w, ss))));
   }
   ss = warp_sum(ss);
@@ -282,13 +334,32 @@ __global__ __launch_bounds__(256) void rmsnorm_wide_kernel(const float* __restri
 
 dg_status launch_rmsnorm(const float* x, void* out, int M, int D, int out_dtype,
                          hipStream_t stream) {
+  return launch_combine_rmsnorm(nullptr, DG_BF16, 0, const_cast<float*>(x), out, M, D, out_dtype,
+                                stream);
+}
+
+dg_status launch_combine_rmsnorm(const void* y_slot, int slot_dtype, int k, float* x, void* out,
+                                 int M, int D, int out_dtype, hipStream_t stream) {
   const bool regs = D % 4 == 0 && D / 4 <= kNormPieces * 256;
+  if (!regs) {
+    dg_status st;
+    if (y_slot && (st = launch_moe_combine(y_slot, slot_dtype, M, D, k, x, stream))) return st;
+    if (out_dtype == DG_BF16)
+      rmsnorm_wide_kernel<bf16_t><<<M, 256, 0, stream>>>(x, static_cast<bf16_t*>(out), D);
+    else
+      rmsnorm_wide_kernel<float><<<M, 256, 0, stream>>>(x, static_cast<float*>(out), D);
+    DG_LAUNCH_CHECK();
+    return DG_OK;
+  }
+  const bool bf = slot_dtype == DG_BF16;
+  const bf16_t* yb = bf ? static_cast<const bf16_t*>(y_slot) : nullptr;
+  const float* yf = bf ? nullptr : static_cast<const float*>(y_slot);
   if (out_dtype == DG_BF16) {
-    if (regs) rmsnorm_kernel<bf16_t><<<M, 256, 0, stream>>>(x, static_cast<bf16_t*>(out), D);
-    else rmsnorm_wide_kernel<bf16_t><<<M, 256, 0, stream>>>(x, static_cast<bf16_t*>(out), D);
+    if (bf) rmsnorm_kernel<bf16_t, bf16_t><<<M, 256, 0, stream>>>(yb, k, x, static_cast<bf16_t*>(out), D);
+    else rmsnorm_kernel<float, bf16_t><<<M, 256, 0, stream>>>(yf, k, x, static_cast<bf16_t*>(out), D);
   } else {
-    if (regs) rmsnorm_kernel<float><<<M, 256, 0, stream>>>(x, static_cast<float*>(out), D);
-    else rmsnorm_wide_kernel<float><<<M, 256, 0, stream>>>(x, static_cast<float*>(out), D);
+    if (bf) rmsnorm_kernel<bf16_t, float><<<M, 256, 0, stream>>>(yb, k, x, static_cast<float*>(out), D);
+    else rmsnorm_kernel<float, float><<<M, 256, 0, stream>>>(yf, k, x, static_cast<float*>(out), D);
   }
   DG_LAUNCH_CHECK();
   return DG_OK;

@@ -370,8 +370,10 @@ namespace dg {
 // unconditional loads in a pinned order; no LDS, no barrier.  (Giving a wave
 // all of an expert's tokens in consecutive passes measured slower: the busy
 // experts' items then take several times longer than the rest.)
-template <int RT, int TB, int NR, bool FP8, int MODE, bool TILED>
-__global__ __launch_bounds__(64) void gemm_wave_kernel(GemmArgs a) {
+constexpr bool kWaveIssueFirst = false;
+
+template <int RT, int TB, int NR, bool FP8, int MODE, bool TILED, int WPE = 1>
+__global__ __launch_bounds__(64, WPE) void gemm_wave_kernel(GemmArgs a) {
   static_assert(MODE == kGateUp || MODE == kDown, "grouped modes only");
   static_assert(MODE != kGateUp || RT % 2 == 0, "gate/up needs paired tiles");
   using WT = typename std::conditional<FP8, uint8_t, bf16_t>::type;
@@ -418,6 +420,9 @@ __global__ __launch_bounds__(64) void gemm_wave_kernel(GemmArgs a) {
       first_tile = __shfl(incl[q] - cnt[q], src_lane);
     }
   }
+  // wave-uniform from here on: keep the expert and tile bases in SGPRs
+  grp = __builtin_amdgcn_readfirstlane(grp);
+  first_tile = __builtin_amdgcn_readfirstlane(first_tile);
   const int base_pos = a.offsets[grp];
   const int m0 = (ty - first_tile) * MT;
   const int m_count = min(MT, a.offsets[grp + 1] - base_pos - m0);
@@ -434,15 +439,21 @@ __global__ __launch_bounds__(64) void gemm_wave_kernel(GemmArgs a) {
     xp[tb] = a.X + static_cast<int64_t>(src) * a.K + g4 * 16;
   }
 
+  // weight tiles: uniform tile bases + one per-lane offset (TILED: the
+  // lane's 16 values of chunk c at c * 1024 + 16 (or 8) * lane elements;
+  // row-major: row lane % 16, k 16 (lane / 16) + 64 c)
   const WT* Wg = static_cast<const WT*>(a.W) + static_cast<int64_t>(grp) * a.w_group_stride;
-  WRow<WT, TILED> wp[RT];
+  const WT* wtile[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const int row0 = (MODE == kGateUp)
                          ? (rt < RT / 2 ? 0 : a.N / 2) + tx * (8 * RT) + (rt % (RT / 2)) * 16
                          : tx * (16 * RT) + rt * 16;
-    wp[rt].init(Wg, row0, a.K, lane);
+    wtile[rt] = TILED ? Wg + static_cast<int64_t>(row0 / 16) * (a.K / 64) * 1024
+                      : Wg + static_cast<int64_t>(row0) * a.K;
   }
+  const int w_lane = TILED ? lane * (sizeof(WT) == 1 ? 16 : 8) : (lane & 15) * a.K + (lane >> 4) * 16;
+  constexpr int kChunk = TILED ? 1024 : 64;
   const int nchunks = a.K / 64;
 
   struct Slot {
@@ -458,7 +469,8 @@ __global__ __launch_bounds__(64) void gemm_wave_kernel(GemmArgs a) {
       sl.x[tb][1] = *reinterpret_cast<const uint4*>(xp[tb] + cc * 64 + 8);
     }
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) sl.w[rt].template load<WRow<WT, TILED>::kSecond>(wp[rt].at(cc));
+    for (int rt = 0; rt < RT; ++rt)
+      sl.w[rt].template load<WRow<WT, TILED>::kSecond>(wtile[rt] + w_lane + cc * kChunk);
   };
   const uint4 zero4 = make_uint4(0, 0, 0, 0);
   f32x4_v acc[RT][TB];
@@ -474,10 +486,15 @@ __global__ __launch_bounds__(64) void gemm_wave_kernel(GemmArgs a) {
   for (int c0 = 0; c0 < nchunks; c0 += NR) {
 #pragma unroll
     for (int p = 0; p < NR; ++p) {
+      // kWaveIssueFirst: refill the slot before its MMAs (one more slot of
+      // registers, loads issued one compute step earlier); otherwise refill
+      // it right after
       const Slot cur = ring[p];
-      __builtin_amdgcn_sched_barrier(0);
-      issue(ring[p], c0 + p + NR);
-      __builtin_amdgcn_sched_barrier(0);
+      if (kWaveIssueFirst) {
+        __builtin_amdgcn_sched_barrier(0);
+        issue(ring[p], c0 + p + NR);
+        __builtin_amdgcn_sched_barrier(0);
+      }
       if (c0 + p < nchunks) {
         bf16x8_v xa[TB][2];
 #pragma unroll
@@ -499,6 +516,11 @@ __global__ __launch_bounds__(64) void gemm_wave_kernel(GemmArgs a) {
             }
           }
         }
+      }
+      if (!kWaveIssueFirst) {
+        __builtin_amdgcn_sched_barrier(0);
+        issue(ring[p], c0 + p + NR);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   }

@@ -58,6 +58,9 @@ dg_status launch_moe_down(const void* h, int h_dtype, const void* w_down, int w_
                           int E, int k, void* y_slot, hipStream_t stream);
 dg_status launch_moe_combine(const void* y_slot, int dtype, int T, int D, int k, float* y,
                              hipStream_t stream);
+// The intermediates launch_moe_ffn carves from its workspace.
+void moe_ffn_workspace_split(void* ws, int T, int I, int k, int x_dtype, void** h,
+                             void** y_slot);
 dg_status launch_moe_ffn(const void* x, int x_dtype, const void* w_gate_up, const void* w_down,
                          int w_dtype, int w_layout, const float* s_gate_up, const float* s_down,
                          const int32_t* topk_ids, const float* gates, const int32_t* offsets,
@@ -73,6 +76,11 @@ dg_status launch_gemm(const void* A, const void* W, void* C, int M, int N, int K
 // RMSNorm of f32 rows x [M, D] (eps 1e-6, unit gain) into out_dtype.
 dg_status launch_rmsnorm(const float* x, void* out, int M, int D, int out_dtype,
                          hipStream_t stream);
+// The MoE combine fused into the next RMSNorm: x[t] += sum_j y_slot[t * k + j]
+// (slot order, as launch_moe_combine), then out = RMSNorm(x).  y_slot may be
+// null (plain RMSNorm); slot_dtype is DG_BF16 or DG_F32.
+dg_status launch_combine_rmsnorm(const void* y_slot, int slot_dtype, int k, float* x, void* out,
+                                 int M, int D, int out_dtype, hipStream_t stream);
 // x[t] = emb[tokens[t]] as f32.
 dg_status launch_embed(const int32_t* tokens, const void* emb, float* x, int M, int D,
                        int dtype, hipStream_t stream);

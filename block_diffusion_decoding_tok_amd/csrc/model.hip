@@ -80,6 +80,9 @@ struct dg_ctx {
   bool use_graphs = true;
   std::map<GraphKey, hipGraphExec_t> graphs;
   std::vector<const float*> router_override;   // empty: the model's own routing
+  // the last MoE layer's gate-weighted slot rows still to be added into x
+  // (host-side enqueue state: the next norm or the end of the forward does it)
+  bool pending_combine = false;
   int router_override_tokens = 0;
 };
 
@@ -169,6 +172,8 @@ dg_status check_dims(const dg_model_dims* d) {
   return DG_OK;
 }
 
+dg_status norm_input(dg_ctx* c, int T, hipStream_t s);
+
 // One decoder layer over T = B * n tokens (residual ctx->x).
 dg_status layer(dg_ctx* c, int l, int B, int n, void* kc, void* vc, int Tmax,
                 const int32_t* prefix_len, int mode, bool kv_only, hipStream_t s) {
@@ -178,7 +183,7 @@ dg_status layer(dg_ctx* c, int l, int B, int n, void* kc, void* vc, int Tmax,
   const int qkv_w = qd + 2 * kd;
   const size_t a = esz(d.act_dtype);
   dg_status st;
-  if ((st = launch_rmsnorm(c->x, c->h, T, d.d_model, d.act_dtype, s))) return st;
+  if ((st = norm_input(c, T, s))) return st;
   if ((st = launch_gemm(c->h, c->wqkv[l], c->qkv, T, qkv_w, d.d_model, d.act_dtype,
                         d.weight_layout, d.act_dtype, kStore, s)))
     return st;
@@ -202,10 +207,41 @@ dg_status layer(dg_ctx* c, int l, int B, int n, void* kc, void* vc, int Tmax,
   if ((st = launch_moe_route(route_in, T, d.n_experts, d.top_k, c->topk_ids, c->gates,
                              c->offsets, c->sorted_rows, c->moe_ws, s)))
     return st;
-  return launch_moe_ffn(c->h, d.act_dtype, c->wgu[l], c->wd[l], d.expert_dtype, d.weight_layout,
-                        c->sgu[l],
-                        c->sd[l], c->topk_ids, c->gates, c->offsets, c->sorted_rows, T, d.d_model,
-                        d.d_ff, d.n_experts, d.top_k, c->x, c->moe_ws, s);
+  // gate/up and down now; the combine into x is left to the next norm
+  void *h_mid, *y_slot;
+  moe_ffn_workspace_split(c->moe_ws, T, d.d_ff, d.top_k, d.act_dtype, &h_mid, &y_slot);
+  if ((st = launch_moe_gate_up(c->h, d.act_dtype, c->wgu[l], d.expert_dtype, d.weight_layout,
+                               c->sgu[l], c->offsets, c->sorted_rows, T, d.d_model, d.d_ff,
+                               d.n_experts, d.top_k, h_mid, s)))
+    return st;
+  if ((st = launch_moe_down(h_mid, d.act_dtype, c->wd[l], d.expert_dtype, d.weight_layout,
+                            c->sd[l], c->gates, c->offsets, c->sorted_rows, T, d.d_model, d.d_ff,
+                            d.n_experts, d.top_k, y_slot, s)))
+    return st;
+  c->pending_combine = true;
+  return DG_OK;
+}
+
+// RMSNorm of the residual stream into c->h, taking a pending MoE combine
+// (the previous layer's expert outputs) into x first.
+dg_status norm_input(dg_ctx* c, int T, hipStream_t s) {
+  const dg_model_dims& d = c->d;
+  void *h_mid, *y_slot = nullptr;
+  if (c->pending_combine)
+    moe_ffn_workspace_split(c->moe_ws, T, d.d_ff, d.top_k, d.act_dtype, &h_mid, &y_slot);
+  c->pending_combine = false;
+  return launch_combine_rmsnorm(y_slot, d.act_dtype, d.top_k, c->x, c->h, T, d.d_model,
+                                d.act_dtype, s);
+}
+
+// Flush a pending MoE combine into x (end of a forward without the LM head).
+dg_status flush_combine(dg_ctx* c, int T, hipStream_t s) {
+  if (!c->pending_combine) return DG_OK;
+  const dg_model_dims& d = c->d;
+  void *h_mid, *y_slot;
+  moe_ffn_workspace_split(c->moe_ws, T, d.d_ff, d.top_k, d.act_dtype, &h_mid, &y_slot);
+  c->pending_combine = false;
+  return launch_moe_combine(y_slot, d.act_dtype, T, d.d_model, d.top_k, c->x, s);
 }
 
 dg_status forward(dg_ctx* c, const int32_t* tokens, int B, int n, int l0, int l1,
@@ -213,14 +249,16 @@ dg_status forward(dg_ctx* c, const int32_t* tokens, int B, int n, int l0, int l1
                   int mode, void* logits, bool commit_only, hipStream_t s) {
   const dg_model_dims& d = c->d;
   dg_status st;
+  c->pending_combine = false;   // a combine is only carried within one forward
   if (tokens && (st = launch_embed(tokens, c->emb, c->x, B * n, d.d_model, d.act_dtype, s)))
     return st;
   for (int l = l0; l < l1; ++l) {
     const bool kv_only = commit_only && l == d.n_layers - 1;
     if ((st = layer(c, l, B, n, kcs[l], vcs[l], Tmax, prefix_len, mode, kv_only, s))) return st;
   }
-  if (logits) {
-    if ((st = launch_rmsnorm(c->x, c->h, B * n, d.d_model, d.act_dtype, s))) return st;
+  if (!logits) return flush_combine(c, B * n, s);
+  {
+    if ((st = norm_input(c, B * n, s))) return st;
     if ((st = launch_gemm(c->h, c->lm, logits, B * n, d.vocab, d.d_model, d.act_dtype,
                           d.weight_layout, d.act_dtype, kStore, s)))
       return st;

@@ -7,7 +7,7 @@
 // output is the gate-weighted sum of its k slots in slot order.
 //
 // Kernels:
-//   route_topk_kernel   one wave per token: k rounds of a wave-wide
+//   route_topk_kernel   16 lanes per token: k rounds of a group-wide
 //                       (logit desc, id asc) max; gates in float.
 //   route_sort_kernel   one 1024-thread workgroup: histogram, exclusive scan
 //                       -> expert_offsets, stable scatter of the slot entries
@@ -23,67 +23,101 @@
 namespace dg {
 
 // ------------------------------------------------------------------ router
-__global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits, int T,
-                                                         int E, int k, int32_t* __restrict__ ids,
-                                                         float* __restrict__ gates) {
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (t >= T) return;
-  constexpr int PER = 4;                 // E <= 256
-  float v[PER];
+// Top-k of one token by a 16-lane group: sub-lane sl holds experts sl,
+// sl + 16, ... (E <= 256); each of the k rounds takes the group-wide
+// (logit desc, id asc) maximum of the experts not yet taken (4 xor-shuffle
+// steps).  Lane j < k of the group writes slot j: its id and its gate, the
+// softmax of the k selected logits (sum in slot order).
+__device__ __forceinline__ void route_topk_group(const float* __restrict__ logits, int t, int E,
+                                                 int k, int sl, int32_t* __restrict__ ids,
+                                                 float* __restrict__ gates) {
+  // all 16 loads issued unconditionally (clamped), masked afterwards
+  float v[16];
 #pragma unroll
-  for (int q = 0; q < PER; ++q) {
-    const int e = q * 64 + lane;
-    v[q] = e < E ? logits[static_cast<int64_t>(t) * E + e] : -INFINITY;
-  }
-  bool taken[PER] = {false, false, false, false};
-  float sel[16];
-  int sel_id[16];
+  for (int q = 0; q < 16; ++q)
+    v[q] = logits[static_cast<int64_t>(t) * E + min(q * 16 + sl, E - 1)];
+#pragma unroll
+  for (int q = 0; q < 16; ++q)
+    if (q * 16 + sl >= E) v[q] = -INFINITY;
+  uint32_t taken = 0;
+  float my_val = 0.f, best0 = 0.f, z = 0.f;
+  int my_id = 0;
   for (int j = 0; j < k; ++j) {
     float best = -INFINITY;
     int bid = 0x7fffffff;
 #pragma unroll
-    for (int q = 0; q < PER; ++q) {
-      const int e = q * 64 + lane;
-      if (e < E && !taken[q] && (v[q] > best || (v[q] == best && e < bid))) { best = v[q]; bid = e; }
+    for (int q = 0; q < 16; ++q) {    // branch-free: compares and selects
+      const int e = q * 16 + sl;
+      const bool ok = (e < E) & !((taken >> q) & 1u);
+      const bool better = ok & ((v[q] > best) | ((v[q] == best) & (e < bid)));
+      best = better ? v[q] : best;
+      bid = better ? e : bid;
     }
-    for (int o = 32; o > 0; o >>= 1) {
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) {
       const float ob = __shfl_xor(best, o);
       const int oi = __shfl_xor(bid, o);
       if (ob > best || (ob == best && oi < bid)) { best = ob; bid = oi; }
     }
-#pragma unroll
-    for (int q = 0; q < PER; ++q)
-      if (q * 64 + lane == bid) taken[q] = true;
-    sel[j] = best;
-    sel_id[j] = bid;
+    if ((bid & 15) == sl) taken |= 1u << (bid >> 4);
+    if (j == 0) best0 = best;
+    z += expf(best - best0);
+    if (sl == j) { my_val = best; my_id = bid; }
   }
-  if (lane == 0) {
-    const float m = sel[0];
-    float z = 0.f;
-    for (int j = 0; j < k; ++j) z += expf(sel[j] - m);
-    for (int j = 0; j < k; ++j) {
-      ids[static_cast<int64_t>(t) * k + j] = sel_id[j];
-      gates[static_cast<int64_t>(t) * k + j] = expf(sel[j] - m) / z;
-    }
+  if (sl < k) {
+    ids[static_cast<int64_t>(t) * k + sl] = my_id;
+    gates[static_cast<int64_t>(t) * k + sl] = expf(my_val - best0) / z;
   }
 }
 
-__global__ __launch_bounds__(1024) void route_sort_kernel(const int32_t* __restrict__ ids, int n,
-                                                          int E, int32_t* __restrict__ offsets,
-                                                          int32_t* __restrict__ sorted_rows) {
-  __shared__ int s_count[256];
-  __shared__ int s_base[256];            // running start of each expert
-  __shared__ int s_wave[16][256];        // per-wave counts in the current chunk
+// Four tokens per one-wave workgroup (spread over many CUs: the rounds are
+// latency-bound).
+__global__ __launch_bounds__(64) void route_topk_kernel(const float* __restrict__ logits, int T,
+                                                        int E, int k, int32_t* __restrict__ ids,
+                                                        float* __restrict__ gates) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 4);
+  if (t >= T) return;
+  route_topk_group(logits, t, E, k, threadIdx.x & 15, ids, gates);
+}
+
+// Stable counting sort of the n = T * k slot entries by expert, by one
+// 1024-thread workgroup: histogram, exclusive scan -> expert_offsets, then
+// chunks of 1024 slots scattered with ballot-based ranks (deterministic).
+struct SortSmem {
+  int count[256];
+  int base[256];          // running start of each expert
+  int wave_cnt[16][256];  // per-wave counts in the current chunk
+};
+
+__device__ void sort_slots(const int* ids, int n, int E, int32_t* __restrict__ offsets,
+                           int32_t* __restrict__ sorted_rows, SortSmem& sm) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (tid < 256) s_count[tid] = 0;
+  if (tid < 256) sm.count[tid] = 0;
   __syncthreads();
-  for (int i = tid; i < n; i += 1024) atomicAdd(&s_count[ids[i]], 1);
+  for (int i = tid; i < n; i += 1024) atomicAdd(&sm.count[ids[i]], 1);
   __syncthreads();
-  if (tid == 0) {
-    int acc = 0;
-    for (int e = 0; e < E; ++e) { s_base[e] = acc; offsets[e] = acc; acc += s_count[e]; }
-    offsets[E] = acc;
+  if (wave == 0) {                       // exclusive scan over E <= 256: 4 per lane
+    int c[4], sum = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = lane * 4 + q;
+      c[q] = e < E ? sm.count[e] : 0;
+      sum += c[q];
+    }
+    int incl = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int tt = __shfl_up(incl, o);
+      if (lane >= o) incl += tt;
+    }
+    int run = incl - sum;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = lane * 4 + q;
+      if (e < E) { sm.base[e] = run; offsets[e] = run; }
+      run += c[q];
+    }
+    if (lane == 63) offsets[E] = incl;
   }
   __syncthreads();
   for (int c0 = 0; c0 < n; c0 += 1024) {
@@ -98,23 +132,30 @@ __global__ __launch_bounds__(1024) void route_sort_kernel(const int32_t* __restr
     }
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     const int rank_in_wave = __popcll(same & below);
-    for (int q = tid; q < 16 * 256; q += 1024) (&s_wave[0][0])[q] = 0;
+    for (int q = tid; q < 16 * 256; q += 1024) (&sm.wave_cnt[0][0])[q] = 0;
     __syncthreads();
-    if (e >= 0 && rank_in_wave == 0) s_wave[wave][e] = __popcll(same);
+    if (e >= 0 && rank_in_wave == 0) sm.wave_cnt[wave][e] = __popcll(same);
     __syncthreads();
     if (e >= 0) {
       int before = 0;
-      for (int w = 0; w < wave; ++w) before += s_wave[w][e];
-      sorted_rows[s_base[e] + before + rank_in_wave] = i;
+      for (int w = 0; w < wave; ++w) before += sm.wave_cnt[w][e];
+      sorted_rows[sm.base[e] + before + rank_in_wave] = i;
     }
     __syncthreads();
     if (tid < E) {
       int tot = 0;
-      for (int w = 0; w < 16; ++w) tot += s_wave[w][tid];
-      s_base[tid] += tot;
+      for (int w = 0; w < 16; ++w) tot += sm.wave_cnt[w][tid];
+      sm.base[tid] += tot;
     }
     __syncthreads();
   }
+}
+
+__global__ __launch_bounds__(1024) void route_sort_kernel(const int32_t* __restrict__ ids, int n,
+                                                          int E, int32_t* __restrict__ offsets,
+                                                          int32_t* __restrict__ sorted_rows) {
+  __shared__ SortSmem sm;
+  sort_slots(ids, n, E, offsets, sorted_rows, sm);
 }
 
 size_t moe_route_workspace_bytes(int, int, int) { return 0; }
@@ -122,7 +163,7 @@ size_t moe_route_workspace_bytes(int, int, int) { return 0; }
 dg_status launch_moe_route(const float* logits, int T, int E, int k, int32_t* topk_ids,
                            float* gates, int32_t* offsets, int32_t* sorted_rows, void*,
                            hipStream_t stream) {
-  route_topk_kernel<<<(T + 3) / 4, 256, 0, stream>>>(logits, T, E, k, topk_ids, gates);
+  route_topk_kernel<<<(T + 3) / 4, 64, 0, stream>>>(logits, T, E, k, topk_ids, gates);
   DG_LAUNCH_CHECK();
   route_sort_kernel<<<1, 1024, 0, stream>>>(topk_ids, T * k, E, offsets, sorted_rows);
   DG_LAUNCH_CHECK();
@@ -202,7 +243,7 @@ size_t moe_ffn_workspace_bytes(int T, int D, int I, int E, int k, int x_dtype) {
 // one-wave kernels: register ring depth (chunks of 64 k) and weight tiles of
 // 16 rows per item; token tiles of 16 tokens, or of 32 for gate/up when the
 // experts average 20 to 40 tokens (fewer items re-streaming the same rows)
-constexpr int kMoeNR = 3;
+constexpr int kMoeNR = 2, kMoeWPE = 3;
 constexpr int kGateRT = 8, kDownRT = 8;
 
 template <int TB, bool FP8, int MODE, bool TILED>
@@ -213,7 +254,8 @@ static void launch_wave(GemmArgs& g, int rows_per_item, int T, int k, int E,
   g.n_tiles_x = (MODE == kGateUp ? g.N / 2 : g.N) / rows_per_item;
   g.n_tiles_y = E + (T * k + 16 * TB - 1) / (16 * TB);
   g.n_tiles_total = g.n_tiles_x * g.n_tiles_y;
-  gemm_wave_kernel<(MODE == kGateUp ? kGateRT : kDownRT), TB, kMoeNR, FP8, MODE, TILED>
+  gemm_wave_kernel<(MODE == kGateUp ? kGateRT : kDownRT), TB, kMoeNR, FP8, MODE, TILED,
+                   (TB == 1 ? kMoeWPE : 1)>
       <<<(g.n_tiles_total + 7) / 8 * 8, 64, 0, stream>>>(g);
 }
 
@@ -332,16 +374,21 @@ dg_status launch_moe_combine(const void* y_slot, int dtype, int T, int D, int k,
   return DG_OK;
 }
 
+void moe_ffn_workspace_split(void* ws, int T, int I, int k, int x_dtype, void** h,
+                             void** y_slot) {
+  const size_t slots = static_cast<size_t>(T) * k;
+  const size_t esz = x_dtype == DG_F32 ? 4 : 2;
+  *h = ws;
+  *y_slot = static_cast<char*>(ws) + align_up(slots * I * esz, 256);
+}
+
 dg_status launch_moe_ffn(const void* x, int x_dtype, const void* w_gate_up, const void* w_down,
                          int w_dtype, int w_layout, const float* s_gate_up, const float* s_down,
                          const int32_t* topk_ids, const float* gates, const int32_t* offsets,
                          const int32_t* sorted_rows, int T, int D, int I, int E, int k, float* y,
                          void* ws, hipStream_t stream) {
-  const size_t slots = static_cast<size_t>(T) * k;
-  char* w = static_cast<char*>(ws);
-  const size_t esz = x_dtype == DG_F32 ? 4 : 2;
-  void* h = w;
-  void* y_slot = w + align_up(slots * I * esz, 256);
+  void *h, *y_slot;
+  moe_ffn_workspace_split(ws, T, I, k, x_dtype, &h, &y_slot);
   dg_status st = launch_moe_gate_up(x, x_dtype, w_gate_up, w_dtype, w_layout, s_gate_up, offsets,
                                     sorted_rows, T, D, I, E, k, h, stream);
   if (st != DG_OK) return st;
