@@ -28,14 +28,14 @@ namespace dg {
 // (logit desc, id asc) maximum of the experts not yet taken (4 xor-shuffle
 // steps).  Lane j < k of the group writes slot j: its id and its gate, the
 // softmax of the k selected logits (sum in slot order).
-__device__ __forceinline__ void route_topk_group(const float* __restrict__ logits, int t, int E,
-                                                 int k, int sl, int32_t* __restrict__ ids,
+__device__ __forceinline__ void route_topk_group(const float* row, int t, int E, int k, int sl,
+                                                 int32_t* __restrict__ ids,
                                                  float* __restrict__ gates) {
-  // all 16 loads issued unconditionally (clamped), masked afterwards
+  // the token's E logits at row (global or LDS); all 16 loads issued
+  // unconditionally (clamped), masked afterwards
   float v[16];
 #pragma unroll
-  for (int q = 0; q < 16; ++q)
-    v[q] = logits[static_cast<int64_t>(t) * E + min(q * 16 + sl, E - 1)];
+  for (int q = 0; q < 16; ++q) v[q] = row[min(q * 16 + sl, E - 1)];
 #pragma unroll
   for (int q = 0; q < 16; ++q)
     if (q * 16 + sl >= E) v[q] = -INFINITY;
@@ -77,7 +77,7 @@ __global__ __launch_bounds__(64) void route_topk_kernel(const float* __restrict_
                                                         float* __restrict__ gates) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 4);
   if (t >= T) return;
-  route_topk_group(logits, t, E, k, threadIdx.x & 15, ids, gates);
+  route_topk_group(logits + static_cast<int64_t>(t) * E, t, E, k, threadIdx.x & 15, ids, gates);
 }
 
 // Stable counting sort of the n = T * k slot entries by expert, by one
@@ -245,6 +245,7 @@ size_t moe_ffn_workspace_bytes(int T, int D, int I, int E, int k, int x_dtype) {
 // experts average 20 to 40 tokens (fewer items re-streaming the same rows)
 constexpr int kMoeNR = 2, kMoeWPE = 3;
 constexpr int kGateRT = 8, kDownRT = 8;
+constexpr int kGateTB1Slots = 20;   // gate/up: 16-token tiles up to this many slots per expert
 
 template <int TB, bool FP8, int MODE, bool TILED>
 static void launch_wave(GemmArgs& g, int rows_per_item, int T, int k, int E,
@@ -273,7 +274,7 @@ static void launch_gate_up_mfma(const void* x, const void* wgu, const float* sgu
   // few tokens per expert (the canvas of one or two rows): one-wave items
   // streaming registers; more: 64-token tiles staged through LDS
   const int64_t slots = static_cast<int64_t>(T) * k;
-  if (slots <= 20ll * E) {
+  if (slots <= kGateTB1Slots * static_cast<int64_t>(E)) {
     launch_wave<1, FP8, kGateUp, TILED>(g, 8 * kGateRT, T, k, E, stream);
   } else if (slots <= 40ll * E) {
     launch_wave<2, FP8, kGateUp, TILED>(g, 8 * kGateRT, T, k, E, stream);
