@@ -38,6 +38,7 @@ METRIC = "canvas denoise steps/s & canvas tok/s (256-tok, bs1); % of MFMA/HBM ro
 HBM_PEAK_GBS = 8000.0
 CANVAS = 256
 PROMPT = 8192
+AR_STEPS = 64
 
 
 def make_weights(d, seed=0):
@@ -246,6 +247,9 @@ def main():
                     help="skip the secondary timing with the random router's own routing")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 256 MiB device copy (scale for byte counters)")
+    ap.add_argument("--no-ar", action="store_true", help="skip the AR-mode decode timing")
+    ap.add_argument("--no-prefill-timing", action="store_true",
+                    help="skip the timed re-encoding of the prompt")
     ap.add_argument("--steps48", action="store_true",
                     help="also time 4 blocks at 48 fixed steps each")
     a = ap.parse_args()
@@ -307,6 +311,39 @@ def main():
         # the stated routing: N(0,1) + planted skew, every expert active
         model.set_router_override(planted_router_logits(d, CANVAS * B))
         elapsed = timed(n_blocks, cfg)
+        # the prompt prefill itself (causal, chunks of 256 tokens, all 30
+        # layers): re-encode the same prompt from position 0, timed
+        prefill_s = None
+        if not a.no_prefill_timing:
+            prompt = prompt_ids(B, PROMPT, d.V, seed=0).to("cuda")
+            Pd.zero_()
+            stream.synchronize()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            dg.dg_prefill(model, prompt, kc, vc, Pd)
+            stream.synchronize()
+            prefill_s = time.perf_counter() - t0
+            assert Pd.cpu().tolist() == [PROMPT] * B
+        # AR-mode decode on the same model: greedy single-token causal steps
+        # from the prompt (one hipGraph of AR_STEPS steps; the cache slots
+        # after the prompt are rewritten)
+        ar_s = None
+        if not a.no_ar:
+            first = torch.zeros(B, dtype=torch.int32, device="cuda")
+            ar_out = torch.empty((B, AR_STEPS), dtype=torch.int32, device="cuda")
+            Pd.fill_(PROMPT)
+            dg.dg_ar_decode(model, first, AR_STEPS, kc, vc, Pd, ar_out)   # capture + warm
+            stream.synchronize()
+            Pd.fill_(PROMPT)
+            stream.synchronize()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            dg.dg_ar_decode(model, first, AR_STEPS, kc, vc, Pd, ar_out)
+            stream.synchronize()
+            ar_s = time.perf_counter() - t0
+            assert Pd.cpu().tolist() == [PROMPT + AR_STEPS] * B
+            Pd.fill_(PROMPT)
+            stream.synchronize()
         t48 = None
         if a.steps48:
             cfg48 = dg.sampler_cfg(CANVAS, 48, 48, seed=0)
@@ -349,6 +386,18 @@ def main():
                     "layer 0, so fewer expert bytes move)"}
     if t48 is not None:
         out["tok_per_s_at_48"] = round(4 * CANVAS * B / t48, 1)
+    if ar_s is not None:
+        out["ar_decode"] = {"steps": AR_STEPS, "ms_per_token": round(1e3 * ar_s / AR_STEPS, 3),
+                            "tok_per_s": round(AR_STEPS * B / ar_s, 1),
+                            "canvas_forward_vs_ar_forward": round(
+                                (1e3 * elapsed / a.steps) / (1e3 * ar_s / AR_STEPS), 2),
+                            "note": "greedy single-token causal steps after the prompt, "
+                                    "one hipGraph, same weights and routing override"}
+    if prefill_s is not None:
+        out["prefill"] = {"tokens": PROMPT * B, "ms": round(1e3 * prefill_s, 2),
+                          "tok_per_s": round(PROMPT * B / prefill_s, 1),
+                          "note": "causal prefill of the prompt, 32 chunks of 256 tokens, eager "
+                                  "launches, host clock around the call"}
     if roof is not None:
         out["roofline"] = {"bound": "hbm", "achieved": round(roof["gbs"], 1), "peak": HBM_PEAK_GBS,
                            "unit": "GB/s", "frac": round(roof["gbs"] / HBM_PEAK_GBS, 4),

@@ -387,23 +387,40 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
   const int d4 = (threadIdx.x & 31) * 4;
   if (gr >= BH * rows_total) return;
   const int bh = gr / rows_total, r = gr % rows_total;
+  // splits in batches of 8: the batch's loads are issued together (clamped
+  // indices, masked afterwards), then merged in split order
+  const int64_t rstride = static_cast<int64_t>(BH) * rows_total;
+  const int64_t r0 = static_cast<int64_t>(bh) * rows_total + r;
   float M = -INFINITY;
-  for (int sp = 0; sp < nsplit; ++sp)
-    M = fmaxf(M, ml_part[(static_cast<int64_t>(sp) * BH + bh) * rows_total + r].m);
+  for (int s0 = 0; s0 < nsplit; s0 += 8) {
+    float mv[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) mv[j] = ml_part[min(s0 + j, nsplit - 1) * rstride + r0].m;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) M = fmaxf(M, mv[j]);       // clamped repeats change nothing
+  }
   const float base = (M == -INFINITY) ? 0.f : M;
   float L = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int sp = 0; sp < nsplit; ++sp) {
-    const int64_t prow = (static_cast<int64_t>(sp) * BH + bh) * rows_total + r;
-    const AttnPartialML ml = ml_part[prow];
-    if (ml.l == 0.f) continue;
-    const float f = __builtin_amdgcn_exp2f(ml.m - base);
-    L += ml.l * f;
-    const float4 o = *reinterpret_cast<const float4*>(o_part + prow * kDh + d4);
-    acc.x += o.x * f;
-    acc.y += o.y * f;
-    acc.z += o.z * f;
-    acc.w += o.w * f;
+  for (int s0 = 0; s0 < nsplit; s0 += 8) {
+    AttnPartialML ml[8];
+    float4 o[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int64_t prow = min(s0 + j, nsplit - 1) * rstride + r0;
+      ml[j] = ml_part[prow];
+      o[j] = *reinterpret_cast<const float4*>(o_part + prow * kDh + d4);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (s0 + j >= nsplit || ml[j].l == 0.f) continue;
+      const float f = __builtin_amdgcn_exp2f(ml[j].m - base);
+      L += ml[j].l * f;
+      acc.x += o[j].x * f;
+      acc.y += o[j].y * f;
+      acc.z += o[j].z * f;
+      acc.w += o[j].w * f;
+    }
   }
   const int b = bh / Hkv, g = bh % Hkv;
   const int tok = r / G, h = g * G + r % G;

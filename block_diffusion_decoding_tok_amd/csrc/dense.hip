@@ -18,7 +18,7 @@ namespace dg {
 // per workgroup, K split over kProjNW waves; narrow outputs (router): 32 rows
 // x 16 tokens, K split over eight waves
 constexpr int kSplitNR = 2;
-constexpr int kProjRT = 8, kProjTB = 2, kProjNW = 4;
+constexpr int kProjRT = 8, kProjTB = 2, kProjNW = 4, kProjWPE = 2;
 // other shapes: 64 rows x 64 tokens per workgroup, LDS-staged tokens
 constexpr int kDenseRT = 1, kDenseTB = 4, kDenseKS = 2, kDensePF = 2;
 // up to 256 tokens: register streaming, 16 tokens per tile, ring of 4 chunks
@@ -152,6 +152,116 @@ __global__ __launch_bounds__(512) void gemm_wide_kernel(const bf16_t* __restrict
   }
 }
 
+// The same block GEMM with both operands copied global -> LDS by the
+// direct-to-LDS 16-byte loads (global_load_lds_dwordx4: lane l of a wave
+// instruction writes LDS bytes [16 l, 16 l + 16) after the instruction's
+// base, from any global address), so no registers hold a stage in flight
+// and the weights run two stages ahead: 3 weight buffers (32 KB each) and 2
+// token buffers (32 KB each, unpadded, 16-byte pieces XOR-swizzled by row so
+// the B-operand reads spread over the banks).
+constexpr int kDlWStages = 3, kDlXStages = 2;
+constexpr bool kWideDirectLds = true;   // LM head: direct-to-LDS form
+constexpr size_t kDlSmemBytes = (kDlWStages * kWideWStage + kDlXStages * kWideTok * 64) * sizeof(bf16_t);
+
+__device__ __forceinline__ int dl_xslot(int row, int piece) { return piece ^ ((row >> 1) & 7); }
+
+// s_waitcnt immediates: vector-memory count <= n (bits 3:0 and 15:14), export
+// and LDS/scalar counts left at their maxima (no wait on them)
+constexpr int waitcnt_vm(int n) { return (n & 0xf) | (0x7 << 4) | (0xf << 8) | (((n >> 4) & 3) << 14); }
+constexpr int kWaitVm4 = waitcnt_vm(4), kWaitVm0 = waitcnt_vm(0);
+
+__global__ __launch_bounds__(512) void gemm_wide_dl_kernel(const bf16_t* __restrict__ W,
+                                                           const bf16_t* __restrict__ X,
+                                                           bf16_t* __restrict__ C, int M, int N,
+                                                           int K) {
+  extern __shared__ __attribute__((aligned(16))) bf16_t dsm[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const int wr = wave & 1, wt = wave >> 1;
+  const int n0 = blockIdx.x * kWideRows;
+  const int m0 = blockIdx.y * kWideTok;
+  const int nchunks = K / 64;
+  const bf16_t* wsrc = W + static_cast<int64_t>(n0 / 16) * (K / 64) * 1024;
+
+  // wave w copies 1 KB blocks 4w .. 4w + 3 of each stage
+  auto issue_w = [&](int c) {            // weight stage c -> buffer c % 3
+    bf16_t* dst = dsm + (c % kDlWStages) * kWideWStage;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int b = wave * 4 + i;         // block: tile b / 2, half b % 2
+      const bf16_t* src = wsrc + (static_cast<int64_t>(b >> 1) * (K / 64) + c) * 1024 +
+                          (b & 1) * 512 + lane * 8;
+      __builtin_amdgcn_global_load_lds(src, dst + b * 512, 16, 0, 0);
+    }
+  };
+  auto issue_x = [&](int c) {            // token stage c -> buffer c % 2
+    bf16_t* dst = dsm + kDlWStages * kWideWStage + (c % kDlXStages) * kWideTok * 64;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int b = wave * 4 + i;         // rows 8 b .. 8 b + 7
+      const int row = b * 8 + (lane >> 3);
+      const int piece = (lane & 7) ^ ((row >> 1) & 7);   // slot lane & 7 holds this piece
+      const int tok = min(m0 + row, M - 1);
+      const bf16_t* src = X + static_cast<int64_t>(tok) * K + c * 64 + piece * 8;
+      __builtin_amdgcn_global_load_lds(src, dst + b * 512, 16, 0, 0);
+    }
+  };
+
+  f32x4_v acc[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+
+  // prologue: W(0), X(0), W(1); iteration c issues X(c + 1), W(c + 2)
+  issue_w(0);
+  issue_x(0);
+  if (nchunks > 1) issue_w(1);
+  for (int c = 0; c < nchunks; ++c) {
+    // stage c's loads are done when at most W(c + 1)'s four are outstanding
+    if (c + 1 < nchunks) __builtin_amdgcn_s_waitcnt(kWaitVm4);
+    else __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    // every wave's copies landed (each waited for its own above); stage c - 1
+    // consumed.  A bare barrier: the fence of __syncthreads would wait for
+    // the stages still in flight as well.
+    __builtin_amdgcn_s_barrier();
+    if (c + 1 < nchunks) issue_x(c + 1);
+    if (c + 2 < nchunks) issue_w(c + 2);
+    const bf16_t* sw = dsm + (c % kDlWStages) * kWideWStage + wr * 8 * 1024;
+    const bf16_t* sx = dsm + kDlWStages * kWideWStage + (c % kDlXStages) * kWideTok * 64;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      bf16x8_v xb[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int row = wt * 64 + j * 16 + l16;
+        xb[j] = *reinterpret_cast<const bf16x8_v*>(sx + row * 64 + dl_xslot(row, g4 * 2 + h) * 8);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const bf16x8_v wa = *reinterpret_cast<const bf16x8_v*>(sw + i * 1024 + h * 512 + lane * 8);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, xb[j], acc[i][j], 0, 0, 0);
+      }
+    }
+  }
+
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int m = m0 + wt * 64 + j * 16 + l16;
+    if (m >= M) continue;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int n = n0 + wr * 128 + i * 16 + g4 * 4;
+      uint2 pk;
+      pk.x = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
+      pk.y = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
+      *reinterpret_cast<uint2*>(C + static_cast<int64_t>(m) * N + n) = pk;
+    }
+  }
+}
+
 template <bool TILED>
 static void launch_gemm_bf16(GemmArgs& g, int M, int N, int K, hipStream_t stream);
 
@@ -190,11 +300,18 @@ static void launch_gemm_bf16(GemmArgs& g, int M, int N, int K, hipStream_t strea
       (void)hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_wide_kernel),
                                 hipFuncAttributeMaxDynamicSharedMemorySize,
                                 static_cast<int>(kWideSmemBytes));
+      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_wide_dl_kernel),
+                                hipFuncAttributeMaxDynamicSharedMemorySize,
+                                static_cast<int>(kDlSmemBytes));
       smem_set = true;
     }
     dim3 grid(N / kWideRows, (M + kWideTok - 1) / kWideTok);
-    gemm_wide_kernel<<<grid, 512, kWideSmemBytes, stream>>>(
-        static_cast<const bf16_t*>(g.W), g.X, static_cast<bf16_t*>(g.out), M, N, K);
+    if (kWideDirectLds)
+      gemm_wide_dl_kernel<<<grid, 512, kDlSmemBytes, stream>>>(
+          static_cast<const bf16_t*>(g.W), g.X, static_cast<bf16_t*>(g.out), M, N, K);
+    else
+      gemm_wide_kernel<<<grid, 512, kWideSmemBytes, stream>>>(
+          static_cast<const bf16_t*>(g.W), g.X, static_cast<bf16_t*>(g.out), M, N, K);
   } else if (N >= 32768 && N % (64 * kWideRT) == 0) {
     g.n_tiles_x = N / (64 * kWideRT);
     g.n_tiles_y = (M + 16 * kWideTB - 1) / (16 * kWideTB);
@@ -202,7 +319,8 @@ static void launch_gemm_bf16(GemmArgs& g, int M, int N, int K, hipStream_t strea
     gemm_stream_kernel<kWideRT, kWideTB, kWideKS, kWidePF, false, kDense, TILED>
         <<<(g.n_tiles_total + 7) / 8 * 8, 256, 0, stream>>>(g);
   } else if (K % 64 == 0 && K >= 64 * 8 && N % (16 * kProjRT) == 0 && N % 32 == 0) {
-    const bool narrow = N < 1024;
+    // narrow outputs, or a handful of tokens (AR decode): more, smaller tiles
+    const bool narrow = N < 1024 || M <= 16;
     g.n_tiles_x = narrow ? N / 32 : N / (16 * kProjRT);
     g.n_tiles_y = narrow ? (M + 15) / 16 : (M + 16 * kProjTB - 1) / (16 * kProjTB);
     g.n_tiles_total = g.n_tiles_x * g.n_tiles_y;
@@ -210,7 +328,7 @@ static void launch_gemm_bf16(GemmArgs& g, int M, int N, int K, hipStream_t strea
     if (narrow)
       gemm_splitk_kernel<2, 1, kSplitNR, 8, TILED><<<grid, 512, 0, stream>>>(g);
     else
-      gemm_splitk_kernel<kProjRT, kProjTB, kSplitNR, kProjNW, TILED>
+      gemm_splitk_kernel<kProjRT, kProjTB, kSplitNR, kProjNW, TILED, kProjWPE>
           <<<grid, 64 * kProjNW, 0, stream>>>(g);
   } else {
     g.n_tiles_x = N / (64 * kDenseRT);

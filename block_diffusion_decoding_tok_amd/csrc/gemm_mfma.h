@@ -578,8 +578,12 @@ namespace dg {
 // order).  The NW partial accumulators are summed through LDS in wave order
 // (fixed order: deterministic), one thread per (row tile, token block, lane)
 // quad of outputs.
-template <int RT, int TB, int NR, int NW, bool TILED>
-__global__ __launch_bounds__(64 * NW) void gemm_splitk_kernel(GemmArgs a) {
+// Refill a ring slot before its MMAs (one more slot of registers, loads one
+// compute step earlier) or right after them.
+constexpr bool kSplitIssueFirst = false;
+
+template <int RT, int TB, int NR, int NW, bool TILED, int WPE = 1>
+__global__ __launch_bounds__(64 * NW, WPE) void gemm_splitk_kernel(GemmArgs a) {
   static_assert(RT * TB * 64 <= 64 * NW * 4, "at most four output quads per thread");
   static_assert(NW == 4 || NW == 8, "four or eight waves");
   __shared__ __attribute__((aligned(16))) float s_acc[4][RT * TB * 4][64];
@@ -595,10 +599,15 @@ __global__ __launch_bounds__(64 * NW) void gemm_splitk_kernel(GemmArgs a) {
   const int c_begin = wave * nch_all / NW;
   const int nchunks = (wave + 1) * nch_all / NW - c_begin;   // >= 1 when K >= 64 * NW
 
+  // uniform tile bases (SGPRs) + one per-lane offset, as in gemm_wave_kernel
   const bf16_t* W = static_cast<const bf16_t*>(a.W);
-  WRow<bf16_t, TILED> wp[RT];
+  const bf16_t* wtile[RT];
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) wp[rt].init(W, n0 + rt * 16, a.K, lane);
+  for (int rt = 0; rt < RT; ++rt)
+    wtile[rt] = TILED ? W + static_cast<int64_t>((n0 + rt * 16) / 16) * (a.K / 64) * 1024
+                      : W + static_cast<int64_t>(n0 + rt * 16) * a.K;
+  const int w_lane = TILED ? lane * 8 : (lane & 15) * a.K + (lane >> 4) * 16;
+  constexpr int kChunk = TILED ? 1024 : 64;
   const bf16_t* xp[TB];
   bool xok[TB];
 #pragma unroll
@@ -617,7 +626,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_splitk_kernel(GemmArgs a) {
     const int cc = min(c, nchunks - 1);
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-      const bf16_t* pw = wp[rt].at(c_begin + cc);
+      const bf16_t* pw = wtile[rt] + w_lane + (c_begin + cc) * kChunk;
       sl.w[rt][0] = *reinterpret_cast<const uint4*>(pw);
       sl.w[rt][1] = *reinterpret_cast<const uint4*>(pw + WRow<bf16_t, TILED>::kSecond);
     }
@@ -641,10 +650,13 @@ __global__ __launch_bounds__(64 * NW) void gemm_splitk_kernel(GemmArgs a) {
   for (int c0 = 0; c0 < nchunks; c0 += NR) {
 #pragma unroll
     for (int p = 0; p < NR; ++p) {
+      // refill the slot before or after its MMAs (see kSplitIssueFirst)
       const Slot cur = ring[p];
-      __builtin_amdgcn_sched_barrier(0);
-      issue(ring[p], c0 + p + NR);
-      __builtin_amdgcn_sched_barrier(0);
+      if (kSplitIssueFirst) {
+        __builtin_amdgcn_sched_barrier(0);
+        issue(ring[p], c0 + p + NR);
+        __builtin_amdgcn_sched_barrier(0);
+      }
       if (c0 + p < nchunks) {
 #pragma unroll
         for (int tb = 0; tb < TB; ++tb) {
@@ -659,6 +671,11 @@ __global__ __launch_bounds__(64 * NW) void gemm_splitk_kernel(GemmArgs a) {
             acc[rt][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w1, x1, acc[rt][tb], 0, 0, 0);
           }
         }
+      }
+      if (!kSplitIssueFirst) {
+        __builtin_amdgcn_sched_barrier(0);
+        issue(ring[p], c0 + p + NR);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   }

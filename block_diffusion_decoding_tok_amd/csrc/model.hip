@@ -27,6 +27,59 @@ __global__ void copy_i32_kernel(const int32_t* s, int32_t* d, int n) {
   if (i < n) d[i] = s[i];
 }
 
+// Greedy token of each row: argmax over V logits (ties to the lowest id),
+// written to tok[b] (the next step's input) and out[b * out_stride + col].
+// One 1024-thread workgroup per row; each thread takes 8 values per 16-byte
+// load, 8 loads in flight per batch (V % 8 == 0; bf16 or f32 logits).
+template <typename T>
+__global__ __launch_bounds__(1024) void argmax_rows_kernel(const T* __restrict__ logits, int V,
+                                                           int32_t* __restrict__ tok,
+                                                           int32_t* __restrict__ out,
+                                                           int out_stride, int col) {
+  constexpr int PER = 16 / sizeof(T);   // values per 16-byte load
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const T* row = logits + static_cast<int64_t>(b) * V;
+  const int npieces = V / PER;
+  float best = -INFINITY;
+  int bid = 0x7fffffff;
+  for (int p0 = tid; p0 < npieces; p0 += 1024 * 8) {
+    uint4 u[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      u[j] = *reinterpret_cast<const uint4*>(row + static_cast<int64_t>(min(p0 + j * 1024, npieces - 1)) * PER);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int p = p0 + j * 1024;
+      if (p >= npieces) continue;
+      const T* e = reinterpret_cast<const T*>(&u[j]);
+#pragma unroll
+      for (int q = 0; q < PER; ++q) {
+        const float x = Elem<T>::load(e, q);
+        const int v = p * PER + q;
+        const bool better = (x > best) | ((x == best) & (v < bid));
+        best = better ? x : best;
+        bid = better ? v : bid;
+      }
+    }
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    const float ob = __shfl_xor(best, o);
+    const int oi = __shfl_xor(bid, o);
+    if (ob > best || (ob == best && oi < bid)) { best = ob; bid = oi; }
+  }
+  __shared__ float s_best[16];
+  __shared__ int s_id[16];
+  if ((tid & 63) == 0) { s_best[tid >> 6] = best; s_id[tid >> 6] = bid; }
+  __syncthreads();
+  if (tid == 0) {
+    for (int w = 1; w < 16; ++w)
+      if (s_best[w] > best || (s_best[w] == best && s_id[w] < bid)) { best = s_best[w]; bid = s_id[w]; }
+    if (bid == 0x7fffffff) bid = 0;     // every logit NaN: id 0
+    tok[b] = bid;
+    out[static_cast<int64_t>(b) * out_stride + col] = bid;
+  }
+}
+
 static dg_status fill_i32(int32_t* p, int n, int v, hipStream_t s) {
   fill_i32_kernel<<<(n + 255) / 256, 256, 0, s>>>(p, n, v);
   DG_LAUNCH_CHECK();
@@ -297,6 +350,31 @@ dg_status enqueue_block(dg_ctx* c, const dg_sampler_cfg& cfg, int B, void* const
   return DG_OK;
 }
 
+// R29: n_steps greedy single-token causal steps; c->tokens holds each row's
+// current input token.
+dg_status enqueue_ar(dg_ctx* c, int B, int n_steps, const int32_t* tokens_in, void* const* kcs,
+                     void* const* vcs, int Tmax, int32_t* prefix_len, int32_t* tokens_out,
+                     hipStream_t s) {
+  const dg_model_dims& d = c->d;
+  copy_i32_kernel<<<(B + 255) / 256, 256, 0, s>>>(tokens_in, c->tokens, B);
+  DG_LAUNCH_CHECK();
+  dg_status st;
+  for (int step = 0; step < n_steps; ++step) {
+    if ((st = forward(c, c->tokens, B, 1, 0, d.n_layers, kcs, vcs, Tmax, prefix_len,
+                      DG_MASK_CAUSAL, c->logits, false, s)))
+      return st;
+    if (d.act_dtype == DG_BF16)
+      argmax_rows_kernel<bf16_t><<<B, 1024, 0, s>>>(static_cast<const bf16_t*>(c->logits),
+                                                    d.vocab, c->tokens, tokens_out, n_steps, step);
+    else
+      argmax_rows_kernel<float><<<B, 1024, 0, s>>>(static_cast<const float*>(c->logits), d.vocab,
+                                                   c->tokens, tokens_out, n_steps, step);
+    DG_LAUNCH_CHECK();
+    if ((st = launch_advance_prefix(prefix_len, B, 1, s))) return st;
+  }
+  return DG_OK;
+}
+
 dg_status check_run(dg_ctx* c, int B, int n, void* const* kcs, void* const* vcs, int Tmax,
                     const int32_t* prefix_len, const char* fn) {
   DG_CHECK_ARG(c != nullptr, std::string(fn) + ": ctx is null");
@@ -456,6 +534,52 @@ dg_status dg_prefill(dg_ctx* ctx, const int32_t* prompt, int B, int n, void* con
       return st;
     if ((st = launch_advance_prefix(prefix_len, B, m, s))) return st;
   }
+  return DG_OK;
+}
+
+dg_status dg_ar_decode(dg_ctx* ctx, int B, int n_steps, const int32_t* tokens_in,
+                       void* const* k_caches, void* const* v_caches, int Tmax,
+                       int32_t* prefix_len, int32_t* tokens_out, void* stream) {
+  set_error("");
+  DG_CHECK_ARG(ctx && tokens_in && tokens_out, "dg_ar_decode: null pointer");
+  DG_CHECK_SHAPE(n_steps >= 1 && n_steps <= Tmax, "dg_ar_decode: n_steps outside [1, Tmax]");
+  DG_CHECK_SHAPE(ctx->d.vocab % 8 == 0, "dg_ar_decode: vocab must be a multiple of 8");
+  dg_status st = check_run(ctx, B, 1, k_caches, v_caches, Tmax, prefix_len, "dg_ar_decode");
+  if (st != DG_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!ctx->use_graphs || s == nullptr)
+    return enqueue_ar(ctx, B, n_steps, tokens_in, k_caches, v_caches, Tmax, prefix_len,
+                      tokens_out, s);
+  // graph key: F = -1 marks the AR loop (block keys have F >= 0)
+  GraphKey key{B, Tmax, 1, n_steps, -1, 0.f, 0.f, 0.f, 0.f, 0.f, 0, {}};
+  for (int l = 0; l < ctx->d.n_layers; ++l) {
+    key.ptrs.push_back(k_caches[l]);
+    key.ptrs.push_back(v_caches[l]);
+  }
+  key.ptrs.push_back(prefix_len);
+  key.ptrs.push_back(const_cast<int32_t*>(tokens_in));
+  key.ptrs.push_back(tokens_out);
+  auto it = ctx->graphs.find(key);
+  if (it == ctx->graphs.end()) {
+    DG_HIP(hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal));
+    st = enqueue_ar(ctx, B, n_steps, tokens_in, k_caches, v_caches, Tmax, prefix_len, tokens_out,
+                    s);
+    hipGraph_t g = nullptr;
+    hipError_t e = hipStreamEndCapture(s, &g);
+    if (st != DG_OK) {
+      if (g) (void)hipGraphDestroy(g);
+      return st;
+    }
+    if (e != hipSuccess)
+      return fail(DG_ERR_HIP, std::string("hipStreamEndCapture: ") + hipGetErrorString(e));
+    hipGraphExec_t exec = nullptr;
+    e = hipGraphInstantiate(&exec, g, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(g);
+    if (e != hipSuccess)
+      return fail(DG_ERR_HIP, std::string("hipGraphInstantiate: ") + hipGetErrorString(e));
+    it = ctx->graphs.emplace(key, exec).first;
+  }
+  DG_HIP(hipGraphLaunch(it->second, s));
   return DG_OK;
 }
 

@@ -246,17 +246,17 @@ size_t moe_ffn_workspace_bytes(int T, int D, int I, int E, int k, int x_dtype) {
 constexpr int kMoeNR = 2, kMoeWPE = 3;
 constexpr int kGateRT = 8, kDownRT = 8;
 constexpr int kGateTB1Slots = 20;   // gate/up: 16-token tiles up to this many slots per expert
+constexpr int kTinySlots = 64;      // up to this many slots in all: half-size items
 
-template <int TB, bool FP8, int MODE, bool TILED>
-static void launch_wave(GemmArgs& g, int rows_per_item, int T, int k, int E,
-                        hipStream_t stream) {
+template <int TB, bool FP8, int MODE, bool TILED, int RT = (MODE == kGateUp ? kGateRT : kDownRT)>
+static void launch_wave(GemmArgs& g, int T, int k, int E, hipStream_t stream) {
   // grid: an upper bound of the tile count (E + slots / tile size) times the
   // weight row groups; the kernel deals the live items out itself
+  const int rows_per_item = MODE == kGateUp ? 8 * RT : 16 * RT;
   g.n_tiles_x = (MODE == kGateUp ? g.N / 2 : g.N) / rows_per_item;
   g.n_tiles_y = E + (T * k + 16 * TB - 1) / (16 * TB);
   g.n_tiles_total = g.n_tiles_x * g.n_tiles_y;
-  gemm_wave_kernel<(MODE == kGateUp ? kGateRT : kDownRT), TB, kMoeNR, FP8, MODE, TILED,
-                   (TB == 1 ? kMoeWPE : 1)>
+  gemm_wave_kernel<RT, TB, kMoeNR, FP8, MODE, TILED, (TB == 1 ? kMoeWPE : 1)>
       <<<(g.n_tiles_total + 7) / 8 * 8, 64, 0, stream>>>(g);
 }
 
@@ -274,10 +274,13 @@ static void launch_gate_up_mfma(const void* x, const void* wgu, const float* sgu
   // few tokens per expert (the canvas of one or two rows): one-wave items
   // streaming registers; more: 64-token tiles staged through LDS
   const int64_t slots = static_cast<int64_t>(T) * k;
-  if (slots <= kGateTB1Slots * static_cast<int64_t>(E)) {
-    launch_wave<1, FP8, kGateUp, TILED>(g, 8 * kGateRT, T, k, E, stream);
+  if (slots <= kTinySlots) {
+    // a few tokens (AR decode): half-size items, twice as many waves
+    launch_wave<1, FP8, kGateUp, TILED, kGateRT / 2>(g, T, k, E, stream);
+  } else if (slots <= kGateTB1Slots * static_cast<int64_t>(E)) {
+    launch_wave<1, FP8, kGateUp, TILED>(g, T, k, E, stream);
   } else if (slots <= 40ll * E) {
-    launch_wave<2, FP8, kGateUp, TILED>(g, 8 * kGateRT, T, k, E, stream);
+    launch_wave<2, FP8, kGateUp, TILED>(g, T, k, E, stream);
   } else {
     const int MT = 16 * kMoeTB;
     g.n_tiles_x = I / 64;
@@ -300,8 +303,10 @@ static void launch_down_mfma(const bf16_t* h, const void* wd, const float* sd, c
   d.offsets = offsets; d.sorted_rows = sorted_rows; d.gates = gates;
   d.out = y_slot;
   const int64_t slots = static_cast<int64_t>(T) * k;
-  if (slots <= 40ll * E) {
-    launch_wave<1, FP8, kDown, TILED>(d, 16 * kDownRT, T, k, E, stream);
+  if (slots <= kTinySlots) {
+    launch_wave<1, FP8, kDown, TILED, kDownRT / 2>(d, T, k, E, stream);
+  } else if (slots <= 40ll * E) {
+    launch_wave<1, FP8, kDown, TILED>(d, T, k, E, stream);
   } else {
     const int MT = 16 * kMoeTB;
     d.n_tiles_x = D / 128;

@@ -88,6 +88,7 @@ _SIGS = {
                          _VP]),
     "dg_moe_combine": (_I, [_VP, _I, _I, _I, _I, _VP, _VP]),
     "dg_linear": (_I, [_VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _I, _VP]),
+    "dg_ar_decode": (_I, [_VP, _I, _I, _VP, C.POINTER(_VP), C.POINTER(_VP), _I, _VP, _VP, _VP]),
     "dg_ctx_workspace_size": (_SZ, [C.POINTER(dg_model_dims), _I, _I]),
     "dg_ctx_create": (_I, [C.POINTER(_VP), C.POINTER(dg_model_dims),
                            C.POINTER(dg_model_weights), _I, _I, _VP, _SZ]),
@@ -426,6 +427,20 @@ def dg_model_forward(model, tokens, x, B, n, layer_begin, layer_end, k_caches, v
         _dev(x, "x", (torch.float32,)), B, n, layer_begin, layer_end, kc, vc,
         k_caches[0].shape[2], _dev(prefix_len, "prefix_len", (torch.int32,)), int(mask_mode),
         None if logits is None else _dev(logits, "logits"), _stream(stream)))
+
+
+def dg_ar_decode(model, tokens_in, n_steps, k_caches, v_caches, prefix_len, tokens_out=None,
+                 stream=None):
+    """Greedy AR decoding: tokens_out [B, n_steps] (prefix_len advances by n_steps)."""
+    B = tokens_in.shape[0]
+    if tokens_out is None:
+        tokens_out = torch.empty((B, n_steps), dtype=torch.int32, device=tokens_in.device)
+    kc, vc = _ptr_array(k_caches), _ptr_array(v_caches)
+    _check(lib().dg_ar_decode(
+        model.ctx, B, n_steps, _dev(tokens_in, "tokens_in", (torch.int32,)), kc, vc,
+        k_caches[0].shape[2], _dev(prefix_len, "prefix_len", (torch.int32,)),
+        _dev(tokens_out, "tokens_out", (torch.int32,)), _stream(stream)))
+    return tokens_out
 
 
 def dg_prefill(model, prompt, k_caches, v_caches, prefix_len, stream=None):

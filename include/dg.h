@@ -309,6 +309,21 @@ dg_status dg_denoise_block(dg_ctx* ctx, const dg_sampler_cfg* cfg, int B, void* 
                            void* const* v_caches, int Tmax, int32_t* prefix_len,
                            int32_t* tokens_out, int32_t* steps_taken, void* stream);
 
+/* dg_ar_decode: autoregressive decoding on the same model, the left-to-right
+ * baseline the canvas is compared with ([JPH] "좌→우 순차 처리와의 대비"; [TR]
+ * "수치").  n_steps single-token steps per row: a causal forward of the row's
+ * current token at position P_b (its rotated K/V of every layer to cache slot
+ * P_b), the final RMSNorm + LM head, then the greedy next token
+ * argmax_v logits (ties to the lowest id; the pages fix no AR sampling rule);
+ * P_b += 1.  The first step's input is tokens_in[b].
+ *   tokens_in [B] i32 device; tokens_out [B, n_steps] i32 device (row-major);
+ *   requires B <= max_batch and P_b + n_steps <= Tmax (the caller guarantees
+ *   the latter).  Captured into one hipGraph per (B, n_steps, buffers) on a
+ *   non-default stream when graphs are enabled. */
+dg_status dg_ar_decode(dg_ctx* ctx, int B, int n_steps, const int32_t* tokens_in,
+                       void* const* k_caches, void* const* v_caches, int Tmax,
+                       int32_t* prefix_len, int32_t* tokens_out, void* stream);
+
 /* dg_linear: the dense projections of a layer and the LM head ([TR]
  * "DiffusionGemma의 구성": a decoder whose layers project with dense matrices;
  * [GUIDE] "256토큰 Canvas 병렬 생성": the vocabulary logits of every canvas

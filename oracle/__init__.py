@@ -50,6 +50,9 @@ pin say "parity unpinned" in their docstring.  Current status:
   model forward   composed from the pinned pieces; the tiny-loop scenario is
                   pinned by its own invariants (re-noise every step at random
                   weights; planted commits; adaptive stop).
+  ar_decode       pinned: the incremental (KV-cache) greedy tokens equal the
+                  argmax of one causal pass over the whole sequence from an
+                  empty cache; equal logits (zero LM head) give id 0.
 """
 
 from .philox import (philox4x32_10, uniform24, gumbel_from_word,
@@ -60,7 +63,7 @@ from .attention import rope, attention
 from .moe import (fp8_e4m3fn_decode, moe_route, moe_ffn, moe_ffn_dense_masked,
                   expert_gate_up, gelu_erf)
 from .model import (rmsnorm, TinyModel, layer_forward, model_forward,
-                    prefill, denoise_block)
+                    prefill, denoise_block, ar_decode)
 
 __all__ = [
     "philox4x32_10", "uniform24", "gumbel_from_word", "uniform_id",
@@ -68,5 +71,5 @@ __all__ = [
     "SamplerCfg", "temperature", "position_stats", "sampler_step",
     "init_canvas", "rope", "attention", "fp8_e4m3fn_decode", "moe_route",
     "moe_ffn", "moe_ffn_dense_masked", "expert_gate_up", "gelu_erf", "rmsnorm", "TinyModel",
-    "layer_forward", "model_forward", "prefill", "denoise_block",
+    "layer_forward", "model_forward", "prefill", "denoise_block", "ar_decode",
 ]

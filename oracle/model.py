@@ -18,6 +18,12 @@ Readings:
   R28 a finished block is committed by one more forward of its final tokens,
       whose rotated keys and values of every layer go to cache slots
       [P, P + L); then P += L.
+  R29 autoregressive (AR) decoding on the same model -- the left-to-right
+      baseline the pages compare the canvas with ([JPH] "좌→우 순차 처리와의
+      대비"; [TR] "수치") -- is a causal forward of one token per row at
+      position P (its K/V to slot P), the final norm and LM head, then the
+      greedy choice argmax_v logits (ties to the lowest id); P += 1.  The
+      pages fix no AR sampling rule; greedy is the plainest.
 """
 
 from dataclasses import dataclass, field
@@ -135,3 +141,19 @@ def denoise_block(m, cfg, k_caches, v_caches, P):
             break
     model_forward(m, tokens, k_caches, v_caches, P, CANVAS, lm_head=False)
     return tokens, steps, trace, np.asarray(P) + L
+
+
+def ar_decode(m, tokens_in, k_caches, v_caches, P, n_steps):
+    """R29: n_steps greedy AR steps from tokens_in [B] at positions P [B].
+
+    Returns (tokens [B, n_steps], new P).  Each step's token is the input of
+    the next; the caches receive one slot per step."""
+    tok = np.asarray(tokens_in, np.int64).copy()
+    P = np.asarray(P, np.int64).copy()
+    out = []
+    for _ in range(n_steps):
+        logits = model_forward(m, tok[:, None], k_caches, v_caches, P, CAUSAL)
+        tok = np.argmax(logits[:, 0], axis=1)          # first maximum: lowest id
+        out.append(tok)
+        P = P + 1
+    return np.stack(out, axis=1), P

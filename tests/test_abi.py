@@ -129,3 +129,8 @@ def test_linear_rejects_bad_calls(lib):
     assert lib.dg_linear(f, f, f, 256, 128, 2816, dg.DG_BF16, 0, dg.DG_BF16, 1, None) == -1
     assert lib.dg_linear(f, f, f, 256, 128, 2800, dg.DG_BF16, 0, dg.DG_F32, 0, None) == -2
     assert lib.dg_linear(None, f, f, 256, 128, 2816, dg.DG_BF16, 0, dg.DG_F32, 0, None) == -1
+
+
+def test_ar_decode_rejects_bad_calls(lib):
+    f = C.c_void_p(256)
+    assert lib.dg_ar_decode(None, 1, 4, f, None, None, 64, f, f, None) == -1

@@ -18,7 +18,7 @@ from block_diffusion_decoding_tok_amd import dg
 from block_diffusion_decoding_tok_amd.inputs import (TINY_DIMS, ModelDims, model_weights,
                                                      prompt_ids)
 from oracle import SamplerCfg, prefill, denoise_block, layer_forward, rmsnorm
-from oracle.attention import CANVAS
+from oracle.attention import CANVAS, CAUSAL
 from block_diffusion_decoding_tok_amd.inputs import router_logits_skewed
 from tests.util import oracle_model, empty_caches, rel_err_rows, to_f64
 
@@ -139,10 +139,12 @@ def full_layers(request):
     return d, w, model
 
 
-@pytest.mark.parametrize("B,P0,planted", [(1, 256, False), (4, 512, False), (1, 256, True)])
-def test_full_width_layers_teacher_forced(full_layers, B, P0, planted):
+@pytest.mark.parametrize("B,P0,planted,mode", [(1, 256, False, CANVAS), (4, 512, False, CANVAS),
+                                               (1, 256, True, CANVAS), (2, 512, True, CAUSAL)])
+def test_full_width_layers_teacher_forced(full_layers, B, P0, planted, mode):
     """planted: the router override supplies N(0,1) + hot-expert-skew logits
-    (the stated MoE routing) instead of the random router's."""
+    (the stated MoE routing) instead of the random router's.  CAUSAL: a
+    256-token prefill chunk at positions [P0, P0 + 256) (the prompt path)."""
     d, w, model = full_layers
     override = None
     if planted:
@@ -166,11 +168,11 @@ def test_full_width_layers_teacher_forced(full_layers, B, P0, planted):
         x_in = x.cpu().double().numpy().reshape(B, 256, d.D)
         cache_k = kc[l].cpu().double().numpy()
         cache_v = vc[l].cpu().double().numpy()
-        dg.dg_model_forward(model, None, x, B, 256, l, l + 1, kc, vc, Pd)
+        dg.dg_model_forward(model, None, x, B, 256, l, l + 1, kc, vc, Pd, mask_mode=mode)
         torch.cuda.synchronize()
         x_out = x.cpu().double().numpy().reshape(B, 256, d.D)
         trace = []
-        ref = layer_forward(m, m.layers[l], x_in, cache_k, cache_v, P_host, CANVAS, trace=trace,
+        ref = layer_forward(m, m.layers[l], x_in, cache_k, cache_v, P_host, mode, trace=trace,
                             router_logits=None if override is None else override[l].numpy())
         got_d = (x_out - x_in).reshape(-1, d.D)
         ref_d = (ref - x_in).reshape(-1, d.D)

@@ -103,6 +103,15 @@ def test_moe_ffn_full_size_bs4_fp8_sampled(tiled):
     assert err < TOL["fp8"], err
 
 
+@pytest.mark.parametrize("T", [1, 3, 8])
+@pytest.mark.parametrize("tiled", [False, True])
+def test_moe_ffn_full_size_few_tokens(T, tiled):
+    """A few tokens (AR decode: T * k <= 64 slots): half-size work items."""
+    case = moe_case(T=T, w_dtype="fp8", seed=20 + T, skew=False)
+    err, _ = _ffn_case(case, 8, tiled=tiled)
+    assert err < TOL["fp8"], err
+
+
 @pytest.mark.parametrize("tiled", [False, True])
 def test_moe_ffn_full_size_bs2_fp8_sampled(tiled):
     """Between 20 and 40 tokens per expert on average: one-wave items with

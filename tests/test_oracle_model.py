@@ -10,7 +10,7 @@ import torch.nn.functional as F
 from block_diffusion_decoding_tok_amd.inputs import (TINY_DIMS, model_weights,
                                                      prompt_ids)
 from oracle import (rmsnorm, SamplerCfg, prefill, denoise_block, model_forward,
-                    layer_forward, init_canvas)
+                    layer_forward, init_canvas, ar_decode)
 from oracle.attention import CAUSAL
 from oracle.philox import renoise_id
 from tests.util import oracle_model, empty_caches
@@ -90,3 +90,33 @@ def test_commit_writes_final_block_kv():
     model_forward(m, tokens, k2, v2, P, 0, lm_head=False)
     assert np.allclose(kc[0][:, :, 32:48], k2[0][:, :, 32:48], atol=1e-12)
     assert np.allclose(vc[0][:, :, 32:48], v2[0][:, :, 32:48], atol=1e-12)
+
+
+def test_ar_decode_equals_one_causal_pass():
+    """KV-cache consistency: the greedy tokens of n incremental steps are the
+    argmax, at each position, of a single causal pass over prompt + inputs
+    from an empty cache (brute force, no cache reuse)."""
+    d = TINY_DIMS
+    m = oracle_model(d, model_weights(d, seed=1))
+    B, P0, n = 2, 20, 6
+    prompt = prompt_ids(B, P0, d.V, seed=3).numpy()
+    kc, vc = empty_caches(d, B, P0 + n + 1)
+    P = prefill(m, prompt, kc, vc)
+    first = np.array([5, 300])
+    toks, P_end = ar_decode(m, first, kc, vc, P, n)
+    assert toks.shape == (B, n) and list(P_end) == [P0 + n] * B
+    seq = np.concatenate([prompt, first[:, None], toks[:, :-1]], axis=1)   # inputs only
+    k2, v2 = empty_caches(d, B, P0 + n + 1)
+    logits = model_forward(m, seq, k2, v2, np.zeros(B, np.int64), CAUSAL)
+    assert np.array_equal(np.argmax(logits[:, P0:], axis=2), toks)
+
+
+def test_ar_decode_ties_go_to_the_lowest_id():
+    """A zero LM head makes every logit equal: the greedy choice is id 0."""
+    d = TINY_DIMS
+    m = oracle_model(d, model_weights(d, seed=0))
+    m.lm = np.zeros_like(m.lm)
+    kc, vc = empty_caches(d, 1, 40)
+    P = prefill(m, prompt_ids(1, 16, d.V, seed=0).numpy(), kc, vc)
+    toks, _ = ar_decode(m, np.array([3]), kc, vc, P, 4)
+    assert np.array_equal(toks, np.zeros((1, 4), np.int64))
