@@ -146,6 +146,62 @@ def moe_roofline(model_w, d, B, reps=20):
                 ffn_ms=ms_ffn, ffn_bytes=ffn_bytes, ffn_gbs=ffn_bytes / (ms_ffn * 1e-3) / 1e9)
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def attention_fraction(d, B, P, reps=20):
+    """dg_canvas_attention (RoPE + split-KV MFMA kernel + merge) on one
+    layer's shapes: 256 canvas queries over P cached keys + the canvas.
+    FLOPs = 4 * Hq * L * (P + L) * dh (QK^T and PV)."""
+    dev = "cuda"
+    g = torch.Generator(device=dev).manual_seed(9)
+    L = CANVAS
+    Tmax = P + L
+    q = (torch.randn((B, L, d.Hq, d.dh), device=dev, generator=g) / d.dh ** 0.5).to(torch.bfloat16)
+    kn = (torch.randn((B, L, d.Hkv, d.dh), device=dev, generator=g) / d.dh ** 0.5).to(torch.bfloat16)
+    vn = torch.randn((B, L, d.Hkv, d.dh), device=dev, generator=g).to(torch.bfloat16)
+    kc = (torch.randn((B, d.Hkv, Tmax, d.dh), device=dev, generator=g) / d.dh ** 0.5).to(torch.bfloat16)
+    vc = torch.randn((B, d.Hkv, Tmax, d.dh), device=dev, generator=g).to(torch.bfloat16)
+    Pd = torch.full((B,), P, dtype=torch.int32, device=dev)
+    out = torch.empty_like(q)
+    ws = torch.empty(dg.lib().dg_attention_workspace_size(B, L, d.Hq, d.Hkv, d.dh, Tmax, dg.DG_BF16),
+                     dtype=torch.uint8, device=dev)
+    ms = _graph_ms(lambda: dg.dg_canvas_attention(q, kn, vn, kc, vc, Pd, out=out, ws=ws), reps)
+    flops = 4.0 * B * d.Hq * L * (P + L) * d.dh
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"op": f"dg_canvas_attention bf16, batch {B}, 256 queries over {P} + 256 keys, 16/8 "
+                  "heads of 128 (RoPE + MFMA kernel + split merge)",
+            "ms_per_call": round(ms, 4), "tflops": round(tf, 1), "bound": "mfma",
+            "peak_tflops": MFMA_BF16_PEAK_TFLOPS, "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
+
+
+def sampler_fraction(d, B, reps=20):
+    """dg_sampler_step on bf16 logits [B, 256, V] (step 0): HBM bytes = the
+    logits read once; also the Gumbel draws per second (VALU-bound: a quarter
+    Philox-10 call and two logarithms per logit)."""
+    dev = "cuda"
+    L = CANVAS
+    logits = torch.empty((B, L, d.V), dtype=torch.bfloat16, device=dev)
+    dg.dg_fill_normal(logits, 2.0, 3, 11)
+    cfg = dg.sampler_cfg(L, 48, 0, seed=0)
+    Pd = torch.full((B,), PROMPT, dtype=torch.int32, device=dev)
+    tok = torch.zeros((B, L), dtype=torch.int32, device=dev)
+    com = torch.zeros((B, L), dtype=torch.uint8, device=dev)
+    ren = torch.zeros_like(com)
+    mp = torch.zeros((B, L), dtype=torch.float32, device=dev)
+    en = torch.zeros_like(mp)
+    me = torch.zeros(B, dtype=torch.float32, device=dev)
+    done = torch.zeros(B, dtype=torch.int32, device=dev)
+    ws = torch.empty(dg.lib().dg_sampler_workspace_size(B, L, d.V), dtype=torch.uint8, device=dev)
+    ms = _graph_ms(lambda: dg.dg_sampler_step(logits, 0, cfg, Pd, tok, com, ren, mp, en, me, done,
+                                              ws=ws), reps)
+    gbs = B * L * d.V * 2 / (ms * 1e-3) / 1e9
+    return {"op": f"dg_sampler_step, bf16 logits [{B}, 256, {d.V}], step 0",
+            "ms_per_call": round(ms, 4), "gbs": round(gbs, 1), "bound": "alu (Philox + 2 ln per logit)",
+            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+            "gumbel_draws_per_s": float(f"{B * L * d.V / (ms * 1e-3):.4g}")}
+
+
 # Sources of the gate/up kernel: a traffic figure taken with byte counters
 # is used only while these files are unchanged.
 _KERNEL_SOURCES = ["block_diffusion_decoding_tok_amd/csrc/gemm_mfma.h",
@@ -351,8 +407,21 @@ def main():
         if a.copy_calibration:
             copy_calibration()
         roof = None
+        extra = {}
         if not a.no_roofline:
             roof = moe_roofline(w, d, B)
+            extra["attention"] = attention_fraction(d, B, PROMPT)
+            extra["sampler"] = sampler_fraction(d, B)
+            # the canvas forward alone (30 layers + LM head, no sampler),
+            # 10 forwards captured in one graph on the bench stream
+            fw_tok = prompt_ids(B, CANVAS, d.V, seed=42).to("cuda")
+            fw_x = torch.empty((B * CANVAS, d.D), dtype=torch.float32, device="cuda")
+            fw_logits = torch.empty((B, CANVAS, d.V), dtype=torch.bfloat16, device="cuda")
+            Pd.fill_(PROMPT)
+            stream.synchronize()
+            extra["ms_per_canvas_forward"] = round(_graph_ms(
+                lambda: dg.dg_model_forward(model, fw_tok, fw_x, B, CANVAS, 0, d.NL, kc, vc, Pd,
+                                            logits=fw_logits), 10), 3)
     steps_per_s = a.steps / elapsed
     out = {
         "metric": METRIC,
@@ -386,6 +455,10 @@ def main():
                     "layer 0, so fewer expert bytes move)"}
     if t48 is not None:
         out["tok_per_s_at_48"] = round(4 * CANVAS * B / t48, 1)
+    if roof is not None:
+        out["ms_per_canvas_forward"] = extra["ms_per_canvas_forward"]
+        out["kernel_fractions"] = {"moe_gate_up": {"frac_hbm": round(roof["gbs"] / HBM_PEAK_GBS, 4)},
+                                   "attention": extra["attention"], "sampler": extra["sampler"]}
     if ar_s is not None:
         out["ar_decode"] = {"steps": AR_STEPS, "ms_per_token": round(1e3 * ar_s / AR_STEPS, 3),
                             "tok_per_s": round(AR_STEPS * B / ar_s, 1),
