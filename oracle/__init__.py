@@ -28,7 +28,7 @@ Pages cited (by title; section names are the pages' own headings):
           section "좌→우 순차 처리와의 대비"
 
 Where the pages leave a step open, the module docstrings state the reading
-taken (R1..R28 in the design notes).
+taken (R1..R30 in the design notes).
 
 Parity pins: every function has at least one pin in ``tests/test_oracle_*.py``
 that checks it against something other than itself (closed forms, brute
@@ -50,6 +50,9 @@ pin say "parity unpinned" in their docstring.  Current status:
   model forward   composed from the pinned pieces; the tiny-loop scenario is
                   pinned by its own invariants (re-noise every step at random
                   weights; planted commits; adaptive stop).
+  mxfp4           pinned: torch's e4m3fn and e8m0 decoders on the same bit
+                  fields, worked round-to-nearest-even and saturation cases,
+                  brute-force nearest value, exact round trips, error bound.
   ar_decode       pinned: the incremental (KV-cache) greedy tokens equal the
                   argmax of one causal pass over the whole sequence from an
                   empty cache; equal logits (zero LM head) give id 0.
@@ -62,6 +65,7 @@ from .sampler import (SamplerCfg, temperature, position_stats, sampler_step,
 from .attention import rope, attention
 from .moe import (fp8_e4m3fn_decode, moe_route, moe_ffn, moe_ffn_dense_masked,
                   expert_gate_up, gelu_erf)
+from .mxfp4 import e2m1_decode, e8m0_decode, quantize_mxfp4, dequantize_mxfp4
 from .model import (rmsnorm, TinyModel, layer_forward, model_forward,
                     prefill, denoise_block, ar_decode)
 
@@ -72,4 +76,5 @@ __all__ = [
     "init_canvas", "rope", "attention", "fp8_e4m3fn_decode", "moe_route",
     "moe_ffn", "moe_ffn_dense_masked", "expert_gate_up", "gelu_erf", "rmsnorm", "TinyModel",
     "layer_forward", "model_forward", "prefill", "denoise_block", "ar_decode",
+    "e2m1_decode", "e8m0_decode", "quantize_mxfp4", "dequantize_mxfp4",
 ]
