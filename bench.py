@@ -75,6 +75,26 @@ def make_weights(d, seed=0):
     return w
 
 
+def make_mxfp4_experts(d, w, seed=0):
+    """The same model with MXFP4 experts: the experts' float32 draws (same
+    Philox streams as the fp8 experts) quantized on the device to OCP MXFP4
+    and tile-packed; the dense weights are shared with w."""
+    dev = "cuda"
+    out = {k: v for k, v in w.items() if not k.startswith(("wgu.", "wd.", "sgu.", "sd."))}
+    tmp = torch.empty((d.E, 2 * d.I, d.D), dtype=torch.float32, device=dev)
+    for l in range(d.NL):
+        base = 16 + 16 * l
+        for name, shape, sid in (("gu", (d.E, 2 * d.I, d.D), base + 3), ("d", (d.E, d.D, d.I), base + 4)):
+            src = tmp.view(-1)[: int(np.prod(shape))].view(shape)
+            dg.dg_fill_normal(src, 0.02, seed, sid)
+            codes, scales = dg.dg_quantize_mxfp4(src)
+            out[f"w{name}.{l}"] = dg.dg_pack_mxfp4(codes, scales)
+            del codes, scales
+    torch.cuda.synchronize()
+    del tmp
+    return out
+
+
 def planted_router_logits(d, T, seed=100):
     """Per-layer router logits with the stated MoE routing: N(0, 1) plus a
     planted skew so that 13 of 128 experts take 40% of the top-8 assignments
@@ -105,7 +125,7 @@ def _graph_ms(fn, reps):
     return start.elapsed_time(end) / reps
 
 
-def moe_roofline(model_w, d, B, reps=20):
+def moe_roofline(model_w, d, B, reps=20, mxfp4=False):
     """The dominant kernel of the step, the experts' gate/up GEMM
     (dg_moe_gate_up), timed on a middle layer's experts for the canvas tokens
     with that layer's planted routing (every expert active).  Algorithmic
@@ -125,23 +145,28 @@ def moe_roofline(model_w, d, B, reps=20):
     ws = torch.empty(dg.lib().dg_moe_ffn_workspace_size(T, d.D, d.I, d.E, d.k, dg.DG_BF16),
                      dtype=torch.uint8, device=dev)
     wgu, wd = model_w[f"wgu.{layer}"], model_w[f"wd.{layer}"]
-    sgu, sd = model_w[f"sgu.{layer}"], model_w[f"sd.{layer}"]
+    sgu, sd = model_w.get(f"sgu.{layer}"), model_w.get(f"sd.{layer}")
     kw = dict(w_layout=dg.DG_LAYOUT_TILED, E=d.E, I=d.I)
+    if mxfp4:
+        kw["w_dtype"] = dg.DG_MXFP4
     ms_gu = _graph_ms(lambda: dg.dg_moe_gate_up(x, wgu, sgu, off, rows, d.k, h=h, **kw), reps)
     ms_ffn = _graph_ms(lambda: dg.dg_moe_ffn(x, wgu, wd, sgu, sd, ids, gates, off, rows, y,
                                              ws=ws, **kw), reps)
     route_bytes = (d.E + 1) * 4 + slots * 4
-    gu_bytes = (d.E * 2 * d.I * d.D            # fp8 gate/up rows
-                + d.E * 2 * d.I * 4            # their scales
+
+    def wbytes(rows, K):                       # weight rows with their scales
+        return rows * K // 2 + rows * K // 32 if mxfp4 else rows * K + 4 * rows
+    gu_bytes = (wbytes(d.E * 2 * d.I, d.D)     # gate/up rows + scales
                 + T * d.D * 2                  # token rows (bf16)
                 + slots * d.I * 2              # hidden rows written (bf16)
                 + route_bytes)
     # whole FFN: + down rows and scales, h read, gate-weighted slot rows
     # written + read (bf16), y read + written (f32)
-    ffn_bytes = (gu_bytes + d.E * d.D * d.I + d.E * d.D * 4 + slots * d.I * 2
+    ffn_bytes = (gu_bytes + wbytes(d.E * d.D, d.I) + slots * d.I * 2
                  + slots * d.D * 2 * 2 + T * d.D * 4 * 2 + slots * 4)
+    fmt = "MXFP4" if mxfp4 else "fp8"
     return dict(kernel=(f"gemm_wave_kernel (dg_moe_gate_up): experts of layer {layer}, {T} "
-                        "tokens, fp8 tiled weights, planted routing (all 128 experts active)"),
+                        f"tokens, {fmt} tiled weights, planted routing (all 128 experts active)"),
                 ms=ms_gu, algo_bytes=gu_bytes, gbs=gu_bytes / (ms_gu * 1e-3) / 1e9,
                 ffn_ms=ms_ffn, ffn_bytes=ffn_bytes, ffn_gbs=ffn_bytes / (ms_ffn * 1e-3) / 1e9)
 
@@ -306,6 +331,8 @@ def main():
     ap.add_argument("--no-ar", action="store_true", help="skip the AR-mode decode timing")
     ap.add_argument("--no-prefill-timing", action="store_true",
                     help="skip the timed re-encoding of the prompt")
+    ap.add_argument("--no-mxfp4", action="store_true",
+                    help="skip the timing of the same model with MXFP4 experts")
     ap.add_argument("--steps48", action="store_true",
                     help="also time 4 blocks at 48 fixed steps each")
     a = ap.parse_args()
@@ -338,19 +365,19 @@ def main():
         assert Pd.cpu().tolist() == [PROMPT] * B
         cfg = dg.sampler_cfg(CANVAS, 48, a.block_steps, seed=0)
 
-        def run_blocks(nb, c):
+        def run_blocks(nb, c, m):
             for _ in range(nb):
-                dg.dg_denoise_block(model, c, B, kc, vc, Pd, tok, steps_taken)
+                dg.dg_denoise_block(m, c, B, kc, vc, Pd, tok, steps_taken)
 
-        def timed(nb, c):
+        def timed(nb, c, m=model):
             """Warm up (captures the graph), rewind, time nb blocks."""
-            run_blocks(max(1, a.warmup // a.block_steps), c)
+            run_blocks(max(1, a.warmup // a.block_steps), c, m)
             stream.synchronize()
             Pd.fill_(PROMPT)
             stream.synchronize()
             torch.cuda.synchronize()
             t0 = time.perf_counter()
-            run_blocks(nb, c)
+            run_blocks(nb, c, m)
             stream.synchronize()
             torch.cuda.synchronize()
             el = time.perf_counter() - t0
@@ -404,6 +431,28 @@ def main():
         if a.steps48:
             cfg48 = dg.sampler_cfg(CANVAS, 48, 48, seed=0)
             t48 = timed(4, cfg48)
+        # the same step with MXFP4 experts (same draws, quantized on the
+        # device), planted routing, same prompt cache
+        mx = None
+        if not a.no_mxfp4:
+            w_mx = make_mxfp4_experts(d, w)
+            model_mx = dg.DGModel(d, w_mx, B, CANVAS, dg.DG_BF16, dg.DG_MXFP4,
+                                  weight_layout=dg.DG_LAYOUT_TILED)
+            model_mx.set_router_override(planted_router_logits(d, CANVAS * B))
+            el_mx = timed(n_blocks, cfg, model_mx)
+            mx = {"steps_per_s": round(a.steps / el_mx, 3),
+                  "ms_per_step": round(1e3 * el_mx / a.steps, 3),
+                  "canvas_tok_per_s": round(CANVAS * B * a.steps / el_mx, 1)}
+            if not a.no_roofline:
+                r = moe_roofline(w_mx, d, B, mxfp4=True)
+                mx["gate_up"] = {"kernel": r["kernel"], "ms": round(r["ms"], 4),
+                                 "algo_bytes": r["algo_bytes"], "gbs": round(r["gbs"], 1),
+                                 "hbm_frac": round(r["gbs"] / HBM_PEAK_GBS, 4)}
+                mx["ffn"] = {"ms": round(r["ffn_ms"], 4), "algo_bytes": r["ffn_bytes"],
+                             "gbs": round(r["ffn_gbs"], 1),
+                             "hbm_frac": round(r["ffn_gbs"] / HBM_PEAK_GBS, 4)}
+            model_mx.close()
+            del w_mx
         if a.copy_calibration:
             copy_calibration()
         roof = None
@@ -455,6 +504,10 @@ def main():
                     "layer 0, so fewer expert bytes move)"}
     if t48 is not None:
         out["tok_per_s_at_48"] = round(4 * CANVAS * B / t48, 1)
+    if mx is not None:
+        mx["note"] = ("the same step with OCP MXFP4 experts (E2M1, one E8M0 scale per 32 k) "
+                      "quantized on the device from the same draws, planted routing")
+        out["mxfp4_experts"] = mx
     if roof is not None:
         out["ms_per_canvas_forward"] = extra["ms_per_canvas_forward"]
         out["kernel_fractions"] = {"moe_gate_up": {"frac_hbm": round(roof["gbs"] / HBM_PEAK_GBS, 4)},

@@ -45,8 +45,10 @@ static dg_status check_ffn(const char* fn, int x_dtype, int w_dtype, int w_layou
   };
   if (!(x_dtype == DG_BF16 || x_dtype == DG_F32))
     return bad(DG_ERR_INVALID_ARG, "activation dtype must be DG_BF16 or DG_F32");
-  if (!(w_dtype == DG_BF16 || w_dtype == DG_F32 || w_dtype == DG_FP8_E4M3))
+  if (!(w_dtype == DG_BF16 || w_dtype == DG_F32 || w_dtype == DG_FP8_E4M3 || w_dtype == DG_MXFP4))
     return bad(DG_ERR_INVALID_ARG, "bad w_dtype");
+  if (w_dtype == DG_MXFP4 && w_layout != DG_LAYOUT_TILED)
+    return bad(DG_ERR_INVALID_ARG, "MXFP4 weights must be tile-packed (DG_LAYOUT_TILED)");
   if ((x_dtype == DG_F32) != (w_dtype == DG_F32))
     return bad(DG_ERR_INVALID_ARG, "f32 activations go with f32 weights only");
   if (!(w_layout == DG_LAYOUT_ROWMAJOR || w_layout == DG_LAYOUT_TILED))

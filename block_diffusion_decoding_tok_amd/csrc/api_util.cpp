@@ -35,6 +35,31 @@ dg_status dg_pack_weights(const void* src, void* dst, int64_t groups, int N, int
                              static_cast<hipStream_t>(stream));
 }
 
+dg_status dg_quantize_mxfp4(const float* src, uint8_t* codes, uint8_t* scales, int64_t rows,
+                            int cols, void* stream) {
+  set_error("");
+  DG_CHECK_ARG(rows == 0 || (src && codes && scales), "dg_quantize_mxfp4: null pointer");
+  DG_CHECK_SHAPE(rows >= 0 && cols > 0 && cols % 32 == 0,
+                 "dg_quantize_mxfp4: need rows >= 0 and cols % 32 == 0");
+  DG_CHECK_SHAPE(rows * static_cast<int64_t>(cols) / 256 < (1ll << 31),
+                 "dg_quantize_mxfp4: tensor too large");
+  return launch_quantize_mxfp4(src, codes, scales, rows * static_cast<int64_t>(cols),
+                               static_cast<hipStream_t>(stream));
+}
+
+dg_status dg_pack_mxfp4(const uint8_t* codes, const uint8_t* scales, void* dst, int64_t groups,
+                        int N, int K, void* stream) {
+  set_error("");
+  DG_CHECK_ARG(codes && scales && dst && static_cast<const void*>(codes) != dst &&
+                   static_cast<const void*>(scales) != dst,
+               "dg_pack_mxfp4: null or aliased pointer");
+  DG_CHECK_SHAPE(groups > 0 && N > 0 && K > 0 && N % 16 == 0 && K % 64 == 0,
+                 "dg_pack_mxfp4: need N % 16 == 0 and K % 64 == 0");
+  DG_CHECK_SHAPE(groups * N * static_cast<int64_t>(K) / 1024 < (1ll << 31),
+                 "dg_pack_mxfp4: tensor too large");
+  return launch_pack_mxfp4(codes, scales, dst, groups, N, K, static_cast<hipStream_t>(stream));
+}
+
 dg_status dg_linear(const void* x, const void* w, void* out, int M, int N, int K, int dtype,
                     int w_layout, int out_dtype, int accumulate, void* stream) {
   set_error("");

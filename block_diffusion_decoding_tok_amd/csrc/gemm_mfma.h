@@ -79,15 +79,20 @@ __device__ __forceinline__ void fp8x16_to_bf16(const uint4& q, bf16x8_v& lo, bf1
   hi = bf16x8_v{p[4][0], p[4][1], p[5][0], p[5][1], p[6][0], p[6][1], p[7][0], p[7][1]};
 }
 
-template <bool FP8> struct WChunk;
-template <> struct WChunk<true> {
+// Weight formats of the streamed A operand.
+constexpr int kWBf16 = 0;   // bf16 values
+constexpr int kWFp8 = 1;    // OCP e4m3fn bytes, per-row scale in the epilogue
+constexpr int kWMx4 = 2;    // OCP MXFP4: E2M1 pairs per byte + an E8M0 scale per 32 k
+
+template <int WF> struct WChunk;
+template <> struct WChunk<kWFp8> {
   uint4 q;
   template <int SECOND = 0>
   __device__ void load(const uint8_t* p) { q = *reinterpret_cast<const uint4*>(p); }
   __device__ void zero() { q = make_uint4(0, 0, 0, 0); }
   __device__ void get(bf16x8_v& a, bf16x8_v& b) const { fp8x16_to_bf16(q, a, b); }
 };
-template <> struct WChunk<false> {
+template <> struct WChunk<kWBf16> {
   uint4 q0, q1;
   template <int SECOND = 8>
   __device__ void load(const bf16_t* p) {
@@ -100,6 +105,38 @@ template <> struct WChunk<false> {
     b = *reinterpret_cast<const bf16x8_v*>(&q1);
   }
 };
+// A lane's 16 k of MXFP4 (8 bytes, the lower k in the low nibble) and the
+// E8M0 scale byte of their 32-k block.  The conversion multiplies by the
+// scale 2^(e - 127) (built as the float with exponent field e), so the bf16
+// values are the exact weights for scale bytes 1..254 (E2M1 has 2 significant
+// bits; the quantizer keeps every product a normal bf16 or zero).
+template <> struct WChunk<kWMx4> {
+  uint2 q;
+  uint32_t s;
+  __device__ void load_mx(const uint8_t* codes, const uint8_t* scale) {
+    q = *reinterpret_cast<const uint2*>(codes);
+    s = *scale;
+  }
+  __device__ void get(bf16x8_v& a, bf16x8_v& b) const {
+    const float sc = __uint_as_float(s << 23);
+    bf16x2_v p[8];
+    p[0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q.x, sc, 0);
+    p[1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q.x, sc, 1);
+    p[2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q.x, sc, 2);
+    p[3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q.x, sc, 3);
+    p[4] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q.y, sc, 0);
+    p[5] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q.y, sc, 1);
+    p[6] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q.y, sc, 2);
+    p[7] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q.y, sc, 3);
+    a = bf16x8_v{p[0][0], p[0][1], p[1][0], p[1][1], p[2][0], p[2][1], p[3][0], p[3][1]};
+    b = bf16x8_v{p[4][0], p[4][1], p[5][0], p[5][1], p[6][0], p[6][1], p[7][0], p[7][1]};
+  }
+};
+
+// Bytes of one tiled MXFP4 block (16 rows x 64 k): 512 code bytes in lane
+// order (lane r + 16 q: row r, k 16 q .. 16 q + 15) and 32 scale bytes
+// (16 h + r: row r, k half h).
+constexpr int kMx4Block = 544;
 
 // Address of a lane's 16 k-values of chunk c (64 k) of a 16-row weight tile,
 // row-major or tile-packed (DG_LAYOUT_TILED: the tile's chunk c is one
@@ -204,10 +241,10 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
   const int nstages = (nchunks + KS - 1) / KS;
 
   // weight ring: PF stages of KS chunks in flight per wave
-  WChunk<FP8> wr[PF][KS][RT];
+  WChunk<FP8 ? kWFp8 : kWBf16> wr[PF][KS][RT];
   // unconditional loads (clamped chunk; rows are in range by contract) keep
   // the compiler's memory-counter waits precise
-  auto load_w = [&](int stage, WChunk<FP8> (&slot)[KS][RT]) {
+  auto load_w = [&](int stage, WChunk<FP8 ? kWFp8 : kWBf16> (&slot)[KS][RT]) {
 #pragma unroll
     for (int j = 0; j < KS; ++j) {
       const int c = min(stage * KS + j, nchunks - 1);
@@ -372,11 +409,12 @@ namespace dg {
 // experts' items then take several times longer than the rest.)
 constexpr bool kWaveIssueFirst = false;
 
-template <int RT, int TB, int NR, bool FP8, int MODE, bool TILED, int WPE = 1>
+template <int RT, int TB, int NR, int WF, int MODE, bool TILED, int WPE = 1>
 __global__ __launch_bounds__(64, WPE) void gemm_wave_kernel(GemmArgs a) {
   static_assert(MODE == kGateUp || MODE == kDown, "grouped modes only");
   static_assert(MODE != kGateUp || RT % 2 == 0, "gate/up needs paired tiles");
-  using WT = typename std::conditional<FP8, uint8_t, bf16_t>::type;
+  static_assert(WF != kWMx4 || TILED, "MXFP4 weights are always tile-packed");
+  using WT = typename std::conditional<WF == kWBf16, bf16_t, uint8_t>::type;
   constexpr int MT = 16 * TB;
   const int lane = threadIdx.x;
   const int l16 = lane & 15, g4 = lane >> 4;
@@ -441,24 +479,29 @@ __global__ __launch_bounds__(64, WPE) void gemm_wave_kernel(GemmArgs a) {
 
   // weight tiles: uniform tile bases + one per-lane offset (TILED: the
   // lane's 16 values of chunk c at c * 1024 + 16 (or 8) * lane elements;
-  // row-major: row lane % 16, k 16 (lane / 16) + 64 c)
+  // MXFP4: codes at c * 544 + 8 * lane bytes, the scale of its 32-k half at
+  // c * 544 + 512 + 16 (q / 2) + r; row-major: row lane % 16, k 16 (lane / 16)
+  // + 64 c)
   const WT* Wg = static_cast<const WT*>(a.W) + static_cast<int64_t>(grp) * a.w_group_stride;
+  constexpr int kChunk = WF == kWMx4 ? kMx4Block : (TILED ? 1024 : 64);
   const WT* wtile[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const int row0 = (MODE == kGateUp)
                          ? (rt < RT / 2 ? 0 : a.N / 2) + tx * (8 * RT) + (rt % (RT / 2)) * 16
                          : tx * (16 * RT) + rt * 16;
-    wtile[rt] = TILED ? Wg + static_cast<int64_t>(row0 / 16) * (a.K / 64) * 1024
+    wtile[rt] = TILED ? Wg + static_cast<int64_t>(row0 / 16) * (a.K / 64) * (WF == kWMx4 ? kMx4Block : 1024)
                       : Wg + static_cast<int64_t>(row0) * a.K;
   }
-  const int w_lane = TILED ? lane * (sizeof(WT) == 1 ? 16 : 8) : (lane & 15) * a.K + (lane >> 4) * 16;
-  constexpr int kChunk = TILED ? 1024 : 64;
+  const int w_lane = WF == kWMx4 ? lane * 8
+                     : TILED     ? lane * (sizeof(WT) == 1 ? 16 : 8)
+                                 : (lane & 15) * a.K + (lane >> 4) * 16;
+  const int s_lane = 512 + 16 * (g4 >> 1) + l16;   // MXFP4 only
   const int nchunks = a.K / 64;
 
   struct Slot {
     uint4 x[TB][2];
-    WChunk<FP8> w[RT];
+    WChunk<WF> w[RT];
   };
   Slot ring[NR];
   auto issue = [&](Slot& sl, int c) {
@@ -469,8 +512,12 @@ __global__ __launch_bounds__(64, WPE) void gemm_wave_kernel(GemmArgs a) {
       sl.x[tb][1] = *reinterpret_cast<const uint4*>(xp[tb] + cc * 64 + 8);
     }
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-      sl.w[rt].template load<WRow<WT, TILED>::kSecond>(wtile[rt] + w_lane + cc * kChunk);
+    for (int rt = 0; rt < RT; ++rt) {
+      if constexpr (WF == kWMx4)
+        sl.w[rt].load_mx(wtile[rt] + w_lane + cc * kChunk, wtile[rt] + s_lane + cc * kChunk);
+      else
+        sl.w[rt].template load<WRow<WT, TILED>::kSecond>(wtile[rt] + w_lane + cc * kChunk);
+    }
   };
   const uint4 zero4 = make_uint4(0, 0, 0, 0);
   f32x4_v acc[RT][TB];

@@ -5,6 +5,7 @@
 //   quantize: scale = max|row| / 448; byte = e4m3fn round-to-nearest-even of
 //   x / scale, saturated to +-448.
 //   pack: row-major weights -> DG_LAYOUT_TILED.
+//   MXFP4: OCP block quantization (32 k per E8M0 scale) and its tiled pack.
 #include "common.h"
 #include "kernels.h"
 #include "philox.h"
@@ -116,6 +117,86 @@ dg_status launch_quantize_fp8_rows(const float* src, uint8_t* q, float* scale, i
                                    int cols, hipStream_t stream) {
   if (rows == 0) return DG_OK;
   quantize_rows_kernel<<<static_cast<unsigned>(rows), 256, 0, stream>>>(src, q, scale, cols);
+  DG_LAUNCH_CHECK();
+  return DG_OK;
+}
+
+// ------------------------------------------------------------------ MXFP4
+// One lane per element, 32 consecutive lanes per block: the block's amax by a
+// max over the magnitudes' bit patterns (ordered like the values for
+// non-negative floats), shared exponent floor(log2 amax) - 2 from amax's
+// exponent field (a zero or subnormal amax falls to the clamp), then the
+// element's E2M1 magnitude by counting the grid midpoints it passes: at a
+// midpoint the comparison is strict where the lower neighbour has the even
+// mantissa and inclusive where the upper one does (round half to even);
+// beyond 5 everything saturates to 6.  v * 2^-shared is exact (a power of two
+// within the normal range), so the decisions are exact.
+__global__ __launch_bounds__(256) void quantize_mxfp4_kernel(const float* __restrict__ src,
+                                                             uint8_t* __restrict__ codes,
+                                                             uint8_t* __restrict__ scales,
+                                                             int64_t n) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const bool ok = i < n;                      // n % 32 == 0: a block is all in or all out
+  const float v = src[ok ? i : 0];
+  uint32_t m = __float_as_uint(v) & 0x7fffffffu;
+#pragma unroll
+  for (int o = 16; o > 0; o >>= 1) m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), o)));
+  const int shared = min(max(static_cast<int>(m >> 23) - 127 - 2, -125), 127);
+  const float a = fabsf(v) * __uint_as_float(static_cast<uint32_t>(127 - shared) << 23);
+  const uint32_t mag = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) +
+                       (a >= 3.5f) + (a > 5.0f);
+  const uint32_t code = mag | ((__float_as_uint(v) >> 31) << 3);
+  const uint32_t hi = static_cast<uint32_t>(__shfl_down(static_cast<int>(code), 1));
+  if (ok && (threadIdx.x & 1) == 0) codes[i / 2] = static_cast<uint8_t>(code | (hi << 4));
+  if (ok && (threadIdx.x & 31) == 0) scales[i / 32] = static_cast<uint8_t>(shared + 127);
+}
+
+dg_status launch_quantize_mxfp4(const float* src, uint8_t* codes, uint8_t* scales, int64_t n,
+                                hipStream_t stream) {
+  if (n == 0) return DG_OK;
+  quantize_mxfp4_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, stream>>>(src, codes,
+                                                                                   scales, n);
+  DG_LAUNCH_CHECK();
+  return DG_OK;
+}
+
+// Row-major codes [G, N, K / 2] + scales [G, N, K / 32] -> tiled MXFP4 blocks
+// of 544 bytes (16 rows x 64 k); one thread per 8-byte word of the
+// destination: words 0..63 are lane r + 16 q's codes (row r, k 16 q ..
+// 16 q + 15), words 64..67 the 32 scale bytes (16 h + r: row r, half h).
+__global__ void pack_mxfp4_kernel(const uint8_t* __restrict__ codes,
+                                  const uint8_t* __restrict__ scales, uint2* __restrict__ dst,
+                                  int64_t words, int N, int K) {
+  const int64_t w = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (w >= words) return;
+  const int64_t blk = w / 68;
+  const int within = static_cast<int>(w % 68);
+  const int64_t NC = K / 64, NT = N / 16;
+  const int64_t c = blk % NC;
+  const int64_t gt = blk / NC;                          // g * NT + t
+  const int64_t g = gt / NT, t = gt % NT;
+  const int64_t row0 = g * N + 16 * t;                  // first row of the tile
+  if (within < 64) {
+    const int r = within % 16, q = within / 16;
+    dst[w] = *reinterpret_cast<const uint2*>(codes + (row0 + r) * (K / 2) + 32 * c + 8 * q);
+  } else {
+    uint32_t b[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int byte = 8 * (within - 64) + j, h = byte / 16, r = byte % 16;
+      b[j] = scales[(row0 + r) * (K / 32) + 2 * c + h];
+    }
+    dst[w] = make_uint2(b[0] | b[1] << 8 | b[2] << 16 | b[3] << 24,
+                        b[4] | b[5] << 8 | b[6] << 16 | b[7] << 24);
+  }
+}
+
+dg_status launch_pack_mxfp4(const uint8_t* codes, const uint8_t* scales, void* dst,
+                            int64_t groups, int N, int K, hipStream_t stream) {
+  const int64_t words = groups * (N / 16) * static_cast<int64_t>(K / 64) * 68;
+  if (words == 0) return DG_OK;
+  pack_mxfp4_kernel<<<static_cast<unsigned>((words + 255) / 256), 256, 0, stream>>>(
+      codes, scales, static_cast<uint2*>(dst), words, N, K);
   DG_LAUNCH_CHECK();
   return DG_OK;
 }

@@ -92,5 +92,9 @@ dg_status launch_quantize_fp8_rows(const float* src, uint8_t* q, float* scale, i
                                    int cols, hipStream_t stream);
 dg_status launch_pack_weights(const void* src, void* dst, int64_t groups, int N, int K,
                               int elem_bytes, hipStream_t stream);
+dg_status launch_quantize_mxfp4(const float* src, uint8_t* codes, uint8_t* scales, int64_t n,
+                                hipStream_t stream);
+dg_status launch_pack_mxfp4(const uint8_t* codes, const uint8_t* scales, void* dst,
+                            int64_t groups, int N, int K, hipStream_t stream);
 
 }  // namespace dg

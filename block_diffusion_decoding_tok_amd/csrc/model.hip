@@ -207,8 +207,9 @@ dg_status check_dims(const dg_model_dims* d) {
                    (d->weight_layout == DG_LAYOUT_TILED && d->act_dtype == DG_BF16),
                "weight_layout must be row-major, or tiled with bf16 activations");
   if (d->act_dtype == DG_BF16) {
-    DG_CHECK_ARG(d->expert_dtype == DG_BF16 || d->expert_dtype == DG_FP8_E4M3,
-                 "bf16 activations need bf16 or fp8 experts");
+    DG_CHECK_ARG(d->expert_dtype == DG_BF16 || d->expert_dtype == DG_FP8_E4M3 ||
+                     (d->expert_dtype == DG_MXFP4 && d->weight_layout == DG_LAYOUT_TILED),
+                 "bf16 activations need bf16, fp8 or (tiled) MXFP4 experts");
     DG_CHECK_SHAPE(d->head_dim == 128, "the bf16 path needs head_dim 128");
     const int qkv_n = (d->n_heads + 2 * d->n_kv_heads) * d->head_dim;
     DG_CHECK_SHAPE(d->d_model % 128 == 0 && qkv_n % 128 == 0 && d->n_experts % 128 == 0 &&

@@ -248,7 +248,11 @@ constexpr int kGateRT = 8, kDownRT = 8;
 constexpr int kGateTB1Slots = 20;   // gate/up: 16-token tiles up to this many slots per expert
 constexpr int kTinySlots = 64;      // up to this many slots in all: half-size items
 
-template <int TB, bool FP8, int MODE, bool TILED, int RT = (MODE == kGateUp ? kGateRT : kDownRT)>
+// MXFP4 weights: a chunk of a tile is half the bytes of fp8, so the ring
+// holds more chunks to keep as many bytes in flight
+constexpr int kMx4NR = 2, kMx4WPE = 3;
+
+template <int TB, int WF, int MODE, bool TILED, int RT = (MODE == kGateUp ? kGateRT : kDownRT)>
 static void launch_wave(GemmArgs& g, int T, int k, int E, hipStream_t stream) {
   // grid: an upper bound of the tile count (E + slots / tile size) times the
   // weight row groups; the kernel deals the live items out itself
@@ -256,63 +260,78 @@ static void launch_wave(GemmArgs& g, int T, int k, int E, hipStream_t stream) {
   g.n_tiles_x = (MODE == kGateUp ? g.N / 2 : g.N) / rows_per_item;
   g.n_tiles_y = E + (T * k + 16 * TB - 1) / (16 * TB);
   g.n_tiles_total = g.n_tiles_x * g.n_tiles_y;
-  gemm_wave_kernel<RT, TB, kMoeNR, FP8, MODE, TILED, (TB == 1 ? kMoeWPE : 1)>
-      <<<(g.n_tiles_total + 7) / 8 * 8, 64, 0, stream>>>(g);
+  const unsigned grid = static_cast<unsigned>((g.n_tiles_total + 7) / 8 * 8);
+  if constexpr (WF == kWMx4)
+    gemm_wave_kernel<RT, TB, kMx4NR, WF, MODE, TILED, (TB == 1 ? kMx4WPE : 1)><<<grid, 64, 0, stream>>>(g);
+  else
+    gemm_wave_kernel<RT, TB, kMoeNR, WF, MODE, TILED, (TB == 1 ? kMoeWPE : 1)><<<grid, 64, 0, stream>>>(g);
 }
 
-template <bool FP8, bool TILED>
+// Bytes of one expert's weights [N, K] in format WF.
+template <int WF>
+static int64_t expert_bytes(int N, int K) {
+  const int64_t nk = static_cast<int64_t>(N) * K;
+  return WF == kWMx4 ? nk / 2 + nk / 32 : (WF == kWFp8 ? nk : 2 * nk);
+}
+
+template <int WF, bool TILED>
 static void launch_gate_up_mfma(const void* x, const void* wgu, const float* sgu,
                                 const int32_t* offsets, const int32_t* sorted_rows, int T, int D,
                                 int I, int E, int k, bf16_t* h, hipStream_t stream) {
   GemmArgs g{};
-  g.W = wgu; g.w_group_stride = static_cast<int64_t>(2) * I * D;
-  g.w_scale = FP8 ? sgu : nullptr; g.s_group_stride = 2 * I;
+  g.W = wgu;
+  g.w_group_stride = WF == kWBf16 ? static_cast<int64_t>(2) * I * D : expert_bytes<WF>(2 * I, D);
+  g.w_scale = WF == kWFp8 ? sgu : nullptr; g.s_group_stride = 2 * I;
   g.X = static_cast<const bf16_t*>(x);
   g.N = 2 * I; g.K = D; g.n_groups = E; g.topk = k;
   g.offsets = offsets; g.sorted_rows = sorted_rows;
   g.out = h;
   // few tokens per expert (the canvas of one or two rows): one-wave items
-  // streaming registers; more: 64-token tiles staged through LDS
+  // streaming registers; more: 64-token tiles staged through LDS (bf16 and
+  // fp8; MXFP4 keeps one-wave items of 32 tokens)
   const int64_t slots = static_cast<int64_t>(T) * k;
   if (slots <= kTinySlots) {
     // a few tokens (AR decode): half-size items, twice as many waves
-    launch_wave<1, FP8, kGateUp, TILED, kGateRT / 2>(g, T, k, E, stream);
+    launch_wave<1, WF, kGateUp, TILED, kGateRT / 2>(g, T, k, E, stream);
   } else if (slots <= kGateTB1Slots * static_cast<int64_t>(E)) {
-    launch_wave<1, FP8, kGateUp, TILED>(g, T, k, E, stream);
-  } else if (slots <= 40ll * E) {
-    launch_wave<2, FP8, kGateUp, TILED>(g, T, k, E, stream);
-  } else {
+    launch_wave<1, WF, kGateUp, TILED>(g, T, k, E, stream);
+  } else if (slots <= 40ll * E || WF == kWMx4) {
+    launch_wave<2, WF, kGateUp, TILED>(g, T, k, E, stream);
+  } else if constexpr (WF != kWMx4) {
     const int MT = 16 * kMoeTB;
     g.n_tiles_x = I / 64;
     g.n_tiles_y = E + static_cast<int>((slots + MT - 1) / MT);
     g.n_tiles_total = g.n_tiles_x * g.n_tiles_y;
-    gemm_stream_kernel<2, kMoeTB, kMoeKS, kMoePF, FP8, kGateUp, TILED>
+    gemm_stream_kernel<2, kMoeTB, kMoeKS, kMoePF, WF == kWFp8, kGateUp, TILED>
         <<<(g.n_tiles_total + 7) / 8 * 8, 256, 0, stream>>>(g);
   }
 }
 
-template <bool FP8, bool TILED>
+template <int WF, bool TILED>
 static void launch_down_mfma(const bf16_t* h, const void* wd, const float* sd, const float* gates,
                              const int32_t* offsets, const int32_t* sorted_rows, int T, int D,
                              int I, int E, int k, bf16_t* y_slot, hipStream_t stream) {
   GemmArgs d{};
-  d.W = wd; d.w_group_stride = static_cast<int64_t>(D) * I;
-  d.w_scale = FP8 ? sd : nullptr; d.s_group_stride = D;
+  d.W = wd;
+  d.w_group_stride = WF == kWBf16 ? static_cast<int64_t>(D) * I : expert_bytes<WF>(D, I);
+  d.w_scale = WF == kWFp8 ? sd : nullptr; d.s_group_stride = D;
   d.X = h;
   d.N = D; d.K = I; d.n_groups = E; d.topk = k;
   d.offsets = offsets; d.sorted_rows = sorted_rows; d.gates = gates;
   d.out = y_slot;
   const int64_t slots = static_cast<int64_t>(T) * k;
   if (slots <= kTinySlots) {
-    launch_wave<1, FP8, kDown, TILED, kDownRT / 2>(d, T, k, E, stream);
+    launch_wave<1, WF, kDown, TILED, kDownRT / 2>(d, T, k, E, stream);
   } else if (slots <= 40ll * E) {
-    launch_wave<1, FP8, kDown, TILED>(d, T, k, E, stream);
+    launch_wave<1, WF, kDown, TILED>(d, T, k, E, stream);
+  } else if constexpr (WF == kWMx4) {
+    launch_wave<2, WF, kDown, TILED>(d, T, k, E, stream);
   } else {
     const int MT = 16 * kMoeTB;
     d.n_tiles_x = D / 128;
     d.n_tiles_y = E + static_cast<int>((slots + MT - 1) / MT);
     d.n_tiles_total = d.n_tiles_x * d.n_tiles_y;
-    gemm_stream_kernel<2, kMoeTB, kMoeKS, kMoePF, FP8, kDown, TILED>
+    gemm_stream_kernel<2, kMoeTB, kMoeKS, kMoePF, WF == kWFp8, kDown, TILED>
         <<<(d.n_tiles_total + 7) / 8 * 8, 256, 0, stream>>>(d);
   }
 }
@@ -331,12 +350,14 @@ dg_status launch_moe_gate_up(const void* x, int x_dtype, const void* w_gate_up, 
   }
   const bool tiled = w_layout == DG_LAYOUT_TILED;
   bf16_t* hb = static_cast<bf16_t*>(h);
-  if (w_dtype == DG_FP8_E4M3) {
-    if (tiled) launch_gate_up_mfma<true, true>(x, w_gate_up, s_gate_up, offsets, sorted_rows, T, D, I, E, k, hb, stream);
-    else launch_gate_up_mfma<true, false>(x, w_gate_up, s_gate_up, offsets, sorted_rows, T, D, I, E, k, hb, stream);
+  if (w_dtype == DG_MXFP4) {
+    launch_gate_up_mfma<kWMx4, true>(x, w_gate_up, nullptr, offsets, sorted_rows, T, D, I, E, k, hb, stream);
+  } else if (w_dtype == DG_FP8_E4M3) {
+    if (tiled) launch_gate_up_mfma<kWFp8, true>(x, w_gate_up, s_gate_up, offsets, sorted_rows, T, D, I, E, k, hb, stream);
+    else launch_gate_up_mfma<kWFp8, false>(x, w_gate_up, s_gate_up, offsets, sorted_rows, T, D, I, E, k, hb, stream);
   } else {
-    if (tiled) launch_gate_up_mfma<false, true>(x, w_gate_up, nullptr, offsets, sorted_rows, T, D, I, E, k, hb, stream);
-    else launch_gate_up_mfma<false, false>(x, w_gate_up, nullptr, offsets, sorted_rows, T, D, I, E, k, hb, stream);
+    if (tiled) launch_gate_up_mfma<kWBf16, true>(x, w_gate_up, nullptr, offsets, sorted_rows, T, D, I, E, k, hb, stream);
+    else launch_gate_up_mfma<kWBf16, false>(x, w_gate_up, nullptr, offsets, sorted_rows, T, D, I, E, k, hb, stream);
   }
   DG_LAUNCH_CHECK();
   return DG_OK;
@@ -357,12 +378,14 @@ dg_status launch_moe_down(const void* h, int h_dtype, const void* w_down, int w_
   const bool tiled = w_layout == DG_LAYOUT_TILED;
   const bf16_t* hb = static_cast<const bf16_t*>(h);
   bf16_t* yb = static_cast<bf16_t*>(y_slot);
-  if (w_dtype == DG_FP8_E4M3) {
-    if (tiled) launch_down_mfma<true, true>(hb, w_down, s_down, gates, offsets, sorted_rows, T, D, I, E, k, yb, stream);
-    else launch_down_mfma<true, false>(hb, w_down, s_down, gates, offsets, sorted_rows, T, D, I, E, k, yb, stream);
+  if (w_dtype == DG_MXFP4) {
+    launch_down_mfma<kWMx4, true>(hb, w_down, nullptr, gates, offsets, sorted_rows, T, D, I, E, k, yb, stream);
+  } else if (w_dtype == DG_FP8_E4M3) {
+    if (tiled) launch_down_mfma<kWFp8, true>(hb, w_down, s_down, gates, offsets, sorted_rows, T, D, I, E, k, yb, stream);
+    else launch_down_mfma<kWFp8, false>(hb, w_down, s_down, gates, offsets, sorted_rows, T, D, I, E, k, yb, stream);
   } else {
-    if (tiled) launch_down_mfma<false, true>(hb, w_down, nullptr, gates, offsets, sorted_rows, T, D, I, E, k, yb, stream);
-    else launch_down_mfma<false, false>(hb, w_down, nullptr, gates, offsets, sorted_rows, T, D, I, E, k, yb, stream);
+    if (tiled) launch_down_mfma<kWBf16, true>(hb, w_down, nullptr, gates, offsets, sorted_rows, T, D, I, E, k, yb, stream);
+    else launch_down_mfma<kWBf16, false>(hb, w_down, nullptr, gates, offsets, sorted_rows, T, D, I, E, k, yb, stream);
   }
   DG_LAUNCH_CHECK();
   return DG_OK;

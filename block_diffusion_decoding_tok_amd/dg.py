@@ -14,7 +14,7 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libdg.so")
 
-DG_F32, DG_BF16, DG_FP8_E4M3 = 0, 1, 2
+DG_F32, DG_BF16, DG_FP8_E4M3, DG_MXFP4 = 0, 1, 2, 3
 DG_MASK_CANVAS, DG_MASK_CAUSAL = 0, 1
 DG_LAYOUT_ROWMAJOR, DG_LAYOUT_TILED = 0, 1
 STATUS_NONFINITE_LOGITS = 1
@@ -103,6 +103,8 @@ _SIGS = {
     "dg_fill_normal": (_I, [_VP, _I, _SZ, _F, _U64, C.c_uint32, _VP]),
     "dg_quantize_fp8_rows": (_I, [_VP, _VP, _VP, _I64, _I, _VP]),
     "dg_pack_weights": (_I, [_VP, _VP, _I64, _I, _I, _I, _VP]),
+    "dg_quantize_mxfp4": (_I, [_VP, _VP, _VP, _I64, _I, _VP]),
+    "dg_pack_mxfp4": (_I, [_VP, _VP, _VP, _I64, _I, _I, _VP]),
     "dg_philox": (_I, [_VP, _I64, _U64, _VP, _VP]),
     "dg_gumbel": (_I, [_VP, _I64, _VP, _VP]),
 }
@@ -280,16 +282,19 @@ def dg_moe_route(router_logits, k, topk_ids=None, gates=None, expert_offsets=Non
 
 
 def dg_moe_ffn(x, w_gate_up, w_down, s_gate_up, s_down, topk_ids, gates, expert_offsets,
-               sorted_rows, y, ws=None, stream=None, w_layout=DG_LAYOUT_ROWMAJOR, E=None, I=None):
+               sorted_rows, y, ws=None, stream=None, w_layout=DG_LAYOUT_ROWMAJOR, E=None, I=None,
+               w_dtype=None):
     """w_gate_up / w_down: [E, 2I, D] / [E, D, I] row-major, or the same bytes
-    in DG_LAYOUT_TILED (then pass E and I, or keep the logical shape)."""
+    in DG_LAYOUT_TILED (then pass E and I, or keep the logical shape).  MXFP4
+    weights (from dg_pack_mxfp4) need w_dtype=DG_MXFP4, the tiled layout, E
+    and I."""
     T, D = x.shape
     if E is None:
         E, I2 = w_gate_up.shape[0], w_gate_up.shape[1]
         I = I2 // 2
     k = topk_ids.shape[1]
     xd = _dtype_code(x)
-    wd = _dtype_code(w_gate_up)
+    wd = _dtype_code(w_gate_up) if w_dtype is None else int(w_dtype)
     if ws is None:
         ws = _workspace(lib().dg_moe_ffn_workspace_size(T, D, I, E, k, xd), x.device)
     _check(lib().dg_moe_ffn(
@@ -310,14 +315,15 @@ def _expert_dims(w, E, I, gate_up):
 
 
 def dg_moe_gate_up(x, w_gate_up, s_gate_up, expert_offsets, sorted_rows, k, h=None, stream=None,
-                   w_layout=DG_LAYOUT_ROWMAJOR, E=None, I=None):
+                   w_layout=DG_LAYOUT_ROWMAJOR, E=None, I=None, w_dtype=None):
     """h [T * k, I] (x's dtype), one row per sorted position."""
     T, D = x.shape
     E, I = _expert_dims(w_gate_up, E, I, True)
     if h is None:
         h = torch.empty((T * k, I), dtype=x.dtype, device=x.device)
     _check(lib().dg_moe_gate_up(
-        _dev(x, "x"), _dtype_code(x), _dev(w_gate_up, "w_gate_up"), _dtype_code(w_gate_up),
+        _dev(x, "x"), _dtype_code(x), _dev(w_gate_up, "w_gate_up"),
+        _dtype_code(w_gate_up) if w_dtype is None else int(w_dtype),
         int(w_layout), _dev(s_gate_up, "s_gate_up", (torch.float32,)),
         _dev(expert_offsets, "expert_offsets", (torch.int32,)),
         _dev(sorted_rows, "sorted_rows", (torch.int32,)), T, D, I, E, k,
@@ -326,14 +332,15 @@ def dg_moe_gate_up(x, w_gate_up, s_gate_up, expert_offsets, sorted_rows, k, h=No
 
 
 def dg_moe_down(h, w_down, s_down, gates, expert_offsets, sorted_rows, T, D, y_slot=None,
-                stream=None, w_layout=DG_LAYOUT_ROWMAJOR, E=None, I=None):
+                stream=None, w_layout=DG_LAYOUT_ROWMAJOR, E=None, I=None, w_dtype=None):
     """y_slot [T * k, D] (h's dtype), one gate-weighted row per slot."""
     E, I = _expert_dims(w_down, E, I, False)
     k = h.shape[0] // T
     if y_slot is None:
         y_slot = torch.empty((T * k, D), dtype=h.dtype, device=h.device)
     _check(lib().dg_moe_down(
-        _dev(h, "h"), _dtype_code(h), _dev(w_down, "w_down"), _dtype_code(w_down), int(w_layout),
+        _dev(h, "h"), _dtype_code(h), _dev(w_down, "w_down"),
+        _dtype_code(w_down) if w_dtype is None else int(w_dtype), int(w_layout),
         _dev(s_down, "s_down", (torch.float32,)), _dev(gates, "gates", (torch.float32,)),
         _dev(expert_offsets, "expert_offsets", (torch.int32,)),
         _dev(sorted_rows, "sorted_rows", (torch.int32,)), T, D, I, E, k,
@@ -479,6 +486,41 @@ def dg_pack_weights(src, dst=None, stream=None):
     _check(lib().dg_pack_weights(_dev(src, "src", (torch.bfloat16, torch.uint8)),
                                  _dev(dst, "dst", (torch.bfloat16, torch.uint8)), groups, N, K,
                                  code, _stream(stream)))
+    return dst
+
+
+def dg_quantize_mxfp4(src, codes=None, scales=None, stream=None):
+    """OCP MXFP4 of f32 src [..., K] (K % 32 == 0): codes [..., K / 2] and
+    E8M0 scales [..., K / 32], both uint8, row-major."""
+    K = src.shape[-1]
+    rows = src.numel() // K
+    if codes is None:
+        codes = torch.empty(src.shape[:-1] + (K // 2,), dtype=torch.uint8, device=src.device)
+    if scales is None:
+        scales = torch.empty(src.shape[:-1] + (K // 32,), dtype=torch.uint8, device=src.device)
+    _check(lib().dg_quantize_mxfp4(_dev(src, "src", (torch.float32,)),
+                                   _dev(codes, "codes", (torch.uint8,)),
+                                   _dev(scales, "scales", (torch.uint8,)), rows, K,
+                                   _stream(stream)))
+    return codes, scales
+
+
+def mxfp4_tiled_bytes(groups, N, K):
+    return groups * N * K * 17 // 32
+
+
+def dg_pack_mxfp4(codes, scales, dst=None, stream=None):
+    """Row-major MXFP4 codes [.., N, K / 2] + scales [.., N, K / 32] -> the
+    tiled MXFP4 layout (flat uint8, groups * N * K * 17 / 32 bytes)."""
+    N, K = codes.shape[-2], 2 * codes.shape[-1]
+    groups = codes.numel() // (N * K // 2)
+    if tuple(scales.shape[:-1]) != tuple(codes.shape[:-1]) or scales.shape[-1] * 32 != K:
+        raise ValueError("dg_pack_mxfp4: codes and scales shapes disagree")
+    if dst is None:
+        dst = torch.empty(mxfp4_tiled_bytes(groups, N, K), dtype=torch.uint8, device=codes.device)
+    _check(lib().dg_pack_mxfp4(_dev(codes, "codes", (torch.uint8,)),
+                               _dev(scales, "scales", (torch.uint8,)),
+                               _dev(dst, "dst", (torch.uint8,)), groups, N, K, _stream(stream)))
     return dst
 
 

@@ -20,7 +20,8 @@ vocabulary of 2^18, 30-layer MoE decoder with 128 experts, top-8):
   moe_case        MoE FFN on 256*B tokens, D 2816, 128 experts top-8, FFN 704,
                   hidden N(0, 1), router logits N(0, 1) plus a planted skew so
                   that 10% of experts (13) receive 40% of the assignments,
-                  weights N(0, 0.02) in bf16 or fp8-e4m3 with per-row scales.
+                  weights N(0, 0.02) in bf16 or fp8-e4m3 with per-row scales,
+                  or random MXFP4 codes (see mxfp4_random).
   sampler_case    logits [B, 256, 2^18] N(0, 2) in bf16 with a +12 peak at a
                   random id on 60% of positions (154 of 256).
 """
@@ -183,6 +184,18 @@ def _normal_f32(rng, shape, std, chunk=1 << 24):
     return out.reshape(shape)
 
 
+def mxfp4_random(rng, shape, scale_byte=120, spread=1):
+    """Random OCP MXFP4 weights of logical shape [..., N, K]: code bytes
+    uniform over 0..255 (two E2M1 elements each), E8M0 scale bytes uniform in
+    scale_byte +- spread (2^-7, the scale that N(0, 0.02) weights take).
+    Returns (codes [..., N, K / 2], scales [..., N, K / 32]) uint8 tensors."""
+    *lead, K = shape
+    codes = rng.integers(0, 256, tuple(lead) + (K // 2,), dtype=np.uint8)
+    scales = rng.integers(scale_byte - spread, scale_byte + spread + 1,
+                          tuple(lead) + (K // 32,), dtype=np.uint8)
+    return torch.from_numpy(codes), torch.from_numpy(scales)
+
+
 def moe_case(T=256, D=2816, E=128, k=8, I=704, w_dtype="bf16", seed=0,
              w_std=0.02, skew=True):
     r = _rngs(seed, ["x", "router", "wgu", "wd"])
@@ -192,6 +205,11 @@ def moe_case(T=256, D=2816, E=128, k=8, I=704, w_dtype="bf16", seed=0,
     else:
         logits = r["router"].standard_normal((T, E), dtype=np.float32)
         hot, beta = np.zeros(0, np.int64), 0.0
+    if w_dtype == "mxfp4":
+        qgu, sgu = mxfp4_random(r["wgu"], (E, 2 * I, D))
+        qd, sd = mxfp4_random(r["wd"], (E, D, I))
+        return MoECase(to_bf16(x), torch.from_numpy(logits), qgu, qd, sgu, sd, hot, beta,
+                       "mxfp4")
     wgu = _normal_f32(r["wgu"], (E, 2 * I, D), w_std)
     wd = _normal_f32(r["wd"], (E, D, I), w_std)
     if w_dtype == "fp8":

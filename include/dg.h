@@ -43,7 +43,11 @@ typedef enum {
   DG_ERR_NONFINITE = -6      /* reserved: non-finite input detected */
 } dg_status;
 
-typedef enum { DG_F32 = 0, DG_BF16 = 1, DG_FP8_E4M3 = 2 /* OCP e4m3fn */ } dg_dtype;
+/* DG_MXFP4: OCP Microscaling MXFP4 (FP4 E2M1 elements, blocks of 32 along K
+ * sharing one E8M0 scale 2^(e - 127)); expert weights only, tile-packed with
+ * their scales (see dg_layout; the 4-bit counterpart of the NVFP4 weights the
+ * GeekNews page's "최적화와 실행 환경" names). */
+typedef enum { DG_F32 = 0, DG_BF16 = 1, DG_FP8_E4M3 = 2 /* OCP e4m3fn */, DG_MXFP4 = 3 } dg_dtype;
 
 typedef enum { DG_MASK_CANVAS = 0, DG_MASK_CAUSAL = 1 } dg_mask_mode;
 
@@ -56,7 +60,14 @@ typedef enum { DG_MASK_CANVAS = 0, DG_MASK_CAUSAL = 1 } dg_mask_mode;
  *                       2-byte types: half h = (k % 16) / 8 at h * 512 + lane * 8.
  *                       It is the order in which a 64-lane wave loads an MFMA
  *                       A-operand tile, so every load reads 1 KB contiguous.
- *                       Needs N % 16 == 0 and K % 64 == 0 (dg_pack_weights). */
+ *                       Needs N % 16 == 0 and K % 64 == 0 (dg_pack_weights).
+ *   DG_MXFP4 weights are always tile-packed (dg_pack_mxfp4), in blocks of
+ *   16 rows x 64 k of 544 bytes, block (g, n / 16, k / 64) at byte
+ *   ((g * N / 16 + n / 16) * K / 64 + k / 64) * 544; inside a block, with
+ *   r = n % 16, q = (k % 64) / 16: bytes 8 (r + 16 q) .. +7 hold the codes of
+ *   k % 64 = 16 q .. 16 q + 15 (two per byte, the lower k in the low nibble),
+ *   byte 512 + 16 h + r the E8M0 scale of row r, k % 64 in [32 h, 32 h + 32).
+ *   A tensor [G, N, K] takes G * N * K * 17 / 32 bytes. */
 typedef enum { DG_LAYOUT_ROWMAJOR = 0, DG_LAYOUT_TILED = 1 } dg_layout;
 
 /* Device status-word bits. */
@@ -185,10 +196,12 @@ dg_status dg_moe_route(const float* router_logits, int T, int E, int k, int32_t*
 
 /* dg_moe_ffn: y[t] += sum_j gates[t, j] * FFN_{topk_ids[t, j]}(x[t]) with
  * FFN_e(u) = (GELU_erf(u Wg_e^T) * (u Wu_e^T)) Wd_e^T, summed in slot order.
- *   x          [T, D] DG_BF16 (with DG_BF16 / DG_FP8_E4M3 weights) or DG_F32
- *              (with DG_F32 weights)
+ *   x          [T, D] DG_BF16 (with DG_BF16 / DG_FP8_E4M3 / DG_MXFP4 weights)
+ *              or DG_F32 (with DG_F32 weights)
  *   w_gate_up  [E, 2I, D]: rows 0..I-1 gate, I..2I-1 up;  w_down [E, D, I];
- *              in w_layout (DG_LAYOUT_TILED only with DG_BF16 / DG_FP8_E4M3)
+ *              in w_layout (DG_LAYOUT_TILED only with DG_BF16 / DG_FP8_E4M3;
+ *              DG_MXFP4 weights must be DG_LAYOUT_TILED: the tiled MXFP4
+ *              layout with the block scales inside, from dg_pack_mxfp4)
  *   s_gate_up  [E, 2I], s_down [E, D] f32 per-row scales (DG_FP8_E4M3 only;
  *              the weight is byte value * scale); ignored otherwise
  *   routing tables as produced by dg_moe_route; y [T, D] f32, accumulated.
@@ -232,8 +245,8 @@ dg_status dg_moe_combine(const void* y_slot, int dtype, int T, int D, int k, flo
  * gain) -> fused QKV -> canvas attention -> O projection + residual -> RMSNorm
  * -> router -> top-k MoE + residual; final RMSNorm -> untied LM head.  Dense
  * weights and activations use act_dtype (DG_BF16 or DG_F32); experts use
- * expert_dtype (DG_BF16, DG_FP8_E4M3, or DG_F32 with DG_F32 activations).
- * The residual stream is f32.  Weight shapes: emb, lm_head [V, D]; wqkv
+ * expert_dtype (DG_BF16, DG_FP8_E4M3, DG_MXFP4 with the tiled layout, or
+ * DG_F32 with DG_F32 activations).  The residual stream is f32.  Weight shapes: emb, lm_head [V, D]; wqkv
  * [(Hq + 2 Hkv) dh, D] (rows q | k | v); wo [D, Hq dh]; wr [E, D]; experts as
  * in dg_moe_ffn.  emb is always row-major; every other weight is in
  * weight_layout (DG_LAYOUT_TILED only with bf16 activations).  KV caches: per
@@ -352,6 +365,19 @@ dg_status dg_quantize_fp8_rows(const float* src, uint8_t* q, float* scale, int64
  * not alias src).  dtype: DG_BF16 or DG_FP8_E4M3 (any 1-byte type). */
 dg_status dg_pack_weights(const void* src, void* dst, int64_t groups, int N, int K, int dtype,
                           void* stream);
+/* OCP MXFP4 quantization of src [rows, cols] f32 (cols % 32 == 0; finite
+ * values), row-major: codes [rows, cols / 2] (element 2j in the low nibble of
+ * byte j), scales [rows, cols / 32] E8M0.  Per block of 32: shared exponent
+ * floor(log2 amax) - 2 clamped to [-125, 127] (an all-zero block takes -125),
+ * elements round to the nearest E2M1 value of v / 2^shared, ties to the even
+ * mantissa, saturating at 6, sign kept (OCP Microscaling v1.0 conversion). */
+dg_status dg_quantize_mxfp4(const float* src, uint8_t* codes, uint8_t* scales, int64_t rows,
+                            int cols, void* stream);
+/* Pack row-major MXFP4 codes [groups, N, K / 2] and scales [groups, N, K / 32]
+ * into the tiled MXFP4 layout (dst: groups * N * K * 17 / 32 bytes, not
+ * aliasing the inputs).  Needs N % 16 == 0 and K % 64 == 0. */
+dg_status dg_pack_mxfp4(const uint8_t* codes, const uint8_t* scales, void* dst, int64_t groups,
+                        int N, int K, void* stream);
 /* Philox4x32-10 words for n counters: out[4i..4i+3] = Philox(ctr[4i..4i+3], seed). */
 dg_status dg_philox(const uint32_t* counters, int64_t n, uint64_t seed, uint32_t* out,
                     void* stream);

@@ -134,3 +134,23 @@ def test_linear_rejects_bad_calls(lib):
 def test_ar_decode_rejects_bad_calls(lib):
     f = C.c_void_p(256)
     assert lib.dg_ar_decode(None, 1, 4, f, None, None, 64, f, f, None) == -1
+
+
+def test_mxfp4_rejects_bad_calls(lib):
+    f = C.c_void_p(256)
+    # MXFP4 experts must be tile-packed; f32 activations cannot take them
+    assert lib.dg_moe_ffn(f, dg.DG_BF16, f, f, dg.DG_MXFP4, 0, None, None, f, f, f, f,
+                          256, 2816, 704, 128, 8, f, f, 1 << 30, None) == -1
+    assert "tile" in _last_error(lib)
+    assert lib.dg_moe_gate_up(f, dg.DG_F32, f, dg.DG_MXFP4, 1, None, f, f,
+                              256, 2816, 704, 128, 8, f, None) == -1
+    # quantize: cols % 32; pack: K % 64, aliasing
+    assert lib.dg_quantize_mxfp4(f, f, f, 4, 48, None) == -2
+    assert lib.dg_pack_mxfp4(f, C.c_void_p(512), C.c_void_p(1024), 1, 16, 96, None) == -2
+    assert lib.dg_pack_mxfp4(f, C.c_void_p(512), f, 1, 16, 128, None) == -1
+    # a model with MXFP4 experts needs the tiled layout
+    dims = dg.dg_model_dims(30, 2816, 16, 8, 128, 128, 8, 704, 262144, 10000.0,
+                            dg.DG_BF16, dg.DG_MXFP4, dg.DG_LAYOUT_ROWMAJOR)
+    assert lib.dg_ctx_workspace_size(C.byref(dims), 1, 256) == 0
+    dims.weight_layout = dg.DG_LAYOUT_TILED
+    assert lib.dg_ctx_workspace_size(C.byref(dims), 1, 256) > 0

@@ -4,7 +4,7 @@ float64 model, and the comparison rules used by the parity tests."""
 import numpy as np
 import torch
 
-from oracle import TinyModel, fp8_e4m3fn_decode
+from oracle import TinyModel, fp8_e4m3fn_decode, dequantize_mxfp4
 
 
 def to_f64(t):
@@ -85,6 +85,35 @@ class ExpertWeights:
         if self.w.dtype == torch.uint8:
             return _FP8_TABLE[self.w[e].numpy()] * self.s[e].to(torch.float64).numpy()[:, None]
         return to_f64(self.w[e])
+
+
+class Mx4ExpertWeights:
+    """Per-expert float64 view of row-major MXFP4 expert weights: codes
+    [E, N, K / 2] and E8M0 scales [E, N, K / 32] (uint8 tensors), decoded by
+    the oracle one expert at a time."""
+
+    def __init__(self, codes, scales):
+        self.codes, self.scales = codes, scales
+        self.shape = tuple(codes.shape[:-1]) + (2 * codes.shape[-1],)
+
+    def __getitem__(self, e):
+        return dequantize_mxfp4(self.codes[e].numpy(), self.scales[e].numpy())
+
+
+def pack_mxfp4_tiled(codes, scales):
+    """Row-major MXFP4 codes [.., N, K / 2] and scales [.., N, K / 32] -> the
+    tiled MXFP4 byte order (flat): per block of 16 rows x 64 k, 512 code
+    bytes (lane r + 16 q: row r, bytes 8 q .. 8 q + 7 of the block's 32) then
+    32 scale bytes (16 h + r: row r, block half h)."""
+    c = np.asarray(codes)
+    s = np.asarray(scales)
+    N, K = c.shape[-2], 2 * c.shape[-1]
+    G = c.size // (N * K // 2)
+    cb = c.reshape(G, N // 16, 16, K // 64, 4, 8)           # g, t, r, c, q, byte
+    cb = cb.transpose(0, 1, 3, 4, 2, 5).reshape(G, N // 16, K // 64, 512)
+    sb = s.reshape(G, N // 16, 16, K // 64, 2)               # g, t, r, c, h
+    sb = sb.transpose(0, 1, 3, 4, 2).reshape(G, N // 16, K // 64, 32)
+    return np.ascontiguousarray(np.concatenate([cb, sb], axis=-1)).reshape(-1)
 
 
 # value of every e4m3fn byte, from the oracle's decoder
