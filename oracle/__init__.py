@@ -28,7 +28,7 @@ Pages cited (by title; section names are the pages' own headings):
           section "좌→우 순차 처리와의 대비"
 
 Where the pages leave a step open, the module docstrings state the reading
-taken (R1..R30 in the design notes).
+taken (R1..R32 in the design notes).
 
 Parity pins: every function has at least one pin in ``tests/test_oracle_*.py``
 that checks it against something other than itself (closed forms, brute
@@ -40,7 +40,9 @@ pin say "parity unpinned" in their docstring.  Current status:
   sampler_step    pinned: closed-form two-level softmax values, uniform-logit
                   entropy, temperature schedule closed form, Gumbel-max
                   frequencies vs softmax (chi-square), planted commit/re-noise/
-                  stop scenarios.
+                  stop scenarios; the entropy-bound selection against a
+                  brute-force search over all subsets, planted entropy-bound
+                  steps (two-level closed form), bound 0 and unbounded cases.
   attention       pinned: torch scaled_dot_product_attention (fp64, CPU),
                   prompt-row independence, permutation equivariance, RoPE
                   shift invariance, equal-score mean.
@@ -53,6 +55,9 @@ pin say "parity unpinned" in their docstring.  Current status:
   mxfp4           pinned: torch's e4m3fn and e8m0 decoders on the same bit
                   fields, worked round-to-nearest-even and saturation cases,
                   brute-force nearest value, exact round trips, error bound.
+  generate        pinned: no EOS reproduces consecutive single blocks; an EOS
+                  first produced in a row's second block stops that row
+                  there (prefix frozen) and leaves the other row unchanged.
   ar_decode       pinned: the incremental (KV-cache) greedy tokens equal the
                   argmax of one causal pass over the whole sequence from an
                   empty cache; equal logits (zero LM head) give id 0.
@@ -61,13 +66,13 @@ pin say "parity unpinned" in their docstring.  Current status:
 from .philox import (philox4x32_10, uniform24, gumbel_from_word,
                      uniform_id, STREAM_GUMBEL, STREAM_RENOISE, STREAM_CANVAS)
 from .sampler import (SamplerCfg, temperature, position_stats, sampler_step,
-                      init_canvas)
+                      init_canvas, entropy_bound_select)
 from .attention import rope, attention
 from .moe import (fp8_e4m3fn_decode, moe_route, moe_ffn, moe_ffn_dense_masked,
                   expert_gate_up, gelu_erf)
 from .mxfp4 import e2m1_decode, e8m0_decode, quantize_mxfp4, dequantize_mxfp4
 from .model import (rmsnorm, TinyModel, layer_forward, model_forward,
-                    prefill, denoise_block, ar_decode)
+                    prefill, denoise_block, ar_decode, generate)
 
 __all__ = [
     "philox4x32_10", "uniform24", "gumbel_from_word", "uniform_id",
@@ -77,4 +82,5 @@ __all__ = [
     "moe_ffn", "moe_ffn_dense_masked", "expert_gate_up", "gelu_erf", "rmsnorm", "TinyModel",
     "layer_forward", "model_forward", "prefill", "denoise_block", "ar_decode",
     "e2m1_decode", "e8m0_decode", "quantize_mxfp4", "dequantize_mxfp4",
+    "entropy_bound_select", "generate",
 ]

@@ -24,6 +24,13 @@ Readings:
       position P (its K/V to slot P), the final norm and LM head, then the
       greedy choice argmax_v logits (ties to the lowest id); P += 1.  The
       pages fix no AR sampling rule; greedy is the plainest.
+  R32 EOS-terminated multi-block decode ([TR] "DiffusionGemma의 구성",
+      flowchart: after a block is committed, the loop ends if EOS was reached,
+      else a new canvas starts): a row ends after the first committed block
+      that holds the EOS id anywhere, or after max_blocks blocks.  Rows run as
+      one batch; a row that has ended rides along in later blocks with its
+      prefix length frozen (its canvas and cache slots past the prefix are
+      scratch), and its later output blocks are -1.
 """
 
 from dataclasses import dataclass, field
@@ -157,3 +164,27 @@ def ar_decode(m, tokens_in, k_caches, v_caches, P, n_steps):
         out.append(tok)
         P = P + 1
     return np.stack(out, axis=1), P
+
+
+def generate(m, cfg, k_caches, v_caches, P, eos_id, max_blocks):
+    """R32: blocks until every row has produced a block holding eos_id, or
+    max_blocks blocks.  Returns (tokens [B, max_blocks, L] with -1 after a
+    row's last block, n_blocks [B], final P [B])."""
+    P = np.array(P, np.int64)
+    B, L = len(P), cfg.canvas_len
+    out = np.full((B, max_blocks, L), -1, np.int64)
+    n_blocks = np.zeros(B, np.int64)
+    active = np.ones(B, bool)
+    for blk in range(max_blocks):
+        if not active.any():
+            break
+        tokens, _, _, P_next = denoise_block(m, cfg, k_caches, v_caches, P)
+        for b in range(B):
+            if not active[b]:
+                continue
+            out[b, blk] = tokens[b]
+            n_blocks[b] = blk + 1
+            P[b] = P_next[b]
+            if np.any(tokens[b] == eos_id):
+                active[b] = False
+    return out, n_blocks, P

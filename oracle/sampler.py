@@ -23,6 +23,16 @@ Readings where the pages are silent (numbering as in the design notes):
   R9  otherwise the position takes the Gumbel sample.
   R10 sample = argmax_v (z_v + g_v), ties to the lowest v.
   R14 fixed_steps > 0 disables the adaptive stop; the schedule stays over S.
+  R31 the entropy-bound commit policy (the serving configuration's
+      "entropy_bound" sampler with bound 0.1: a confidence-based early exit;
+      developer guide, "vLLM으로 서빙하기"), read as entropy-bounded
+      unmasking (Ben-Hamu et al., "Accelerated Sampling from Masked Diffusion
+      Models via Entropy Bounded Unmasking", 2025) carried over to the
+      uniform-state canvas: at each step the uncommitted positions are ranked
+      by entropy (ties to the lower position) and the longest prefix U of that
+      ranking with sum_U H - max_U H <= bound is committed with its samples
+      (at least one position per step); the rest follow R7 and R9.  In the
+      adaptive mode the block also ends once every position is committed.
 Rows already done on entry are left untouched.
 """
 
@@ -44,6 +54,29 @@ class SamplerCfg:
     commit_prob: float = 0.9
     renoise_prob: float = 0.1
     seed: int = 0
+    commit_policy: int = 0        # 0: maxprob >= commit_prob (R6); 1: entropy bound (R31)
+    entropy_bound: float = 0.1
+
+
+COMMIT_MAXPROB = 0
+COMMIT_ENTROPY_BOUND = 1
+
+
+def entropy_bound_select(entropy, committed, bound):
+    """R31: the positions to commit this step.  Candidates are the
+    uncommitted positions ranked by (entropy, position); the longest prefix
+    whose entropies sum, minus their maximum (the last one), to at most
+    ``bound`` is selected.  Returns a boolean mask."""
+    order = sorted((i for i in range(len(entropy)) if not committed[i]),
+                   key=lambda i: (entropy[i], i))
+    sel = np.zeros(len(entropy), bool)
+    total = 0.0                    # sum of the prefix before the candidate
+    for i in order:
+        if total > bound:
+            break
+        sel[i] = True
+        total += entropy[i]
+    return sel
 
 
 def temperature(step, max_steps, t0=0.8, t1=0.4):
@@ -116,16 +149,22 @@ def sampler_step(logits, step, cfg, prefix_pos, tokens, committed, done,
             rest = np.delete(score, v)
             gap[b, i] = score[v] - rest.max() if rest.size else np.inf
         ment[b] = ent[b].mean()
+        if cfg.commit_policy == COMMIT_ENTROPY_BOUND:
+            commit = entropy_bound_select(ent[b], com[b], cfg.entropy_bound)
+        else:
+            commit = mp[b] >= cfg.commit_prob
         if cfg.fixed_steps > 0:
             end = step == cfg.fixed_steps - 1
         else:
             end = (ment[b] < cfg.stop_entropy) or (step == S - 1)
+            if cfg.commit_policy == COMMIT_ENTROPY_BOUND:
+                end = end or bool(np.all(com[b] | commit))
         ends[b] = int(end)
         for i in range(L):
             ren[b, i] = 0
             if com[b, i]:
                 continue
-            if mp[b, i] >= cfg.commit_prob:
+            if commit[i]:
                 tok[b, i] = sample[b, i]
                 com[b, i] = 1
             elif mp[b, i] < cfg.renoise_prob and not end:

@@ -120,3 +120,38 @@ def test_ar_decode_ties_go_to_the_lowest_id():
     P = prefill(m, prompt_ids(1, 16, d.V, seed=0).numpy(), kc, vc)
     toks, _ = ar_decode(m, np.array([3]), kc, vc, P, 4)
     assert np.array_equal(toks, np.zeros((1, 4), np.int64))
+
+
+def test_generate_stops_rows_at_their_eos_block():
+    """R32 on the tiny model: with an EOS id that row 0 first produces in its
+    second block, row 0 stops after two blocks (prefix frozen, later blocks
+    -1) while row 1 runs on unchanged; without EOS every row runs max_blocks
+    blocks, each equal to consecutive single blocks."""
+    from oracle import generate
+    d = TINY_DIMS
+    m = oracle_model(d, model_weights(d, seed=0))
+    B, L, nb = 2, 16, 3
+    prompt = prompt_ids(B, 32, d.V, seed=0).numpy()
+    cfg = SamplerCfg(canvas_len=L, max_steps=4, seed=0)
+
+    def fresh():
+        kc, vc = empty_caches(d, B, 32 + nb * L)
+        return kc, vc, prefill(m, prompt, kc, vc)
+    kc, vc, P = fresh()
+    ref = []
+    for _ in range(nb):
+        t, _, _, P = denoise_block(m, cfg, kc, vc, P)
+        ref.append(t)
+    ref = np.stack(ref, axis=1)                              # [B, nb, L]
+    kc, vc, P = fresh()
+    out, n_blocks, P_end = generate(m, cfg, kc, vc, P, eos_id=-5, max_blocks=nb)
+    assert np.array_equal(out, ref) and list(n_blocks) == [nb, nb]
+    assert list(P_end) == [32 + nb * L] * B
+    cand = [v for v in ref[0, 1] if v not in ref[0, 0] and v not in ref[1].ravel()]
+    assert cand, "no token unique to row 0's second block"
+    kc, vc, P = fresh()
+    out, n_blocks, P_end = generate(m, cfg, kc, vc, P, eos_id=cand[0], max_blocks=nb)
+    assert list(n_blocks) == [2, nb]
+    assert list(P_end) == [32 + 2 * L, 32 + nb * L]
+    assert np.array_equal(out[0, :2], ref[0, :2]) and (out[0, 2] == -1).all()
+    assert np.array_equal(out[1], ref[1])

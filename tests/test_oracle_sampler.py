@@ -234,3 +234,85 @@ def test_init_canvas_uses_stream2():
         for i in range(4):
             assert tok[b, i] == canvas_id(0, P + i, b, 512)
     assert tok.min() >= 0 and tok.max() < 512
+
+
+# ---------------------------------------------------- entropy-bound policy (R31)
+
+def test_entropy_bound_select_is_the_largest_feasible_set():
+    """Brute force over every subset of the uncommitted positions: the
+    selection has the largest size among the sets with sum - max <= bound,
+    and it holds the lowest-entropy positions (ties to the lower position)."""
+    from itertools import combinations
+    from oracle.sampler import entropy_bound_select
+    rng = np.random.default_rng(8)
+    for trial in range(60):
+        L = 7
+        h = rng.exponential(0.08, L) if trial % 3 else np.round(rng.exponential(0.08, L), 2)
+        com = rng.random(L) < 0.25
+        bound = [0.0, 0.05, 0.1, 0.3][trial % 4]
+        sel = entropy_bound_select(h, com, bound)
+        free = [i for i in range(L) if not com[i]]
+        assert not np.any(sel & com)
+        best = 0
+        for n in range(1, len(free) + 1):
+            # sum - max as the sum of all but the largest (no cancellation)
+            if any(sum(sorted(h[list(c)])[:-1]) <= bound for c in combinations(free, n)):
+                best = n
+        assert sel.sum() == best
+        if best:
+            ranked = sorted(free, key=lambda i: (h[i], i))
+            assert set(np.flatnonzero(sel)) == set(ranked[:best])
+
+
+def _eb_cfg(**kw):
+    return SamplerCfg(commit_policy=1, **kw)
+
+
+def test_entropy_bound_step_planted():
+    """Three confident positions (entropy about 1e-3 each, from the two-level
+    closed form) and five flat ones: the three plus the lowest flat position
+    commit (the largest entropy of the set is not counted against the bound);
+    the other flat ones are re-noised (maxprob 1/V < 0.1)."""
+    V, S, L = 512, 8, 8
+    cfg = _eb_cfg(canvas_len=L, max_steps=S, seed=5)
+    T = temperature(0, S)
+    x = np.zeros((1, L, V))
+    x[0, 2, 7] = x[0, 5, 11] = x[0, 6, 3] = 16.0 * T
+    r = _one_step(x, 0, cfg)
+    W = np.exp(16.0) + V - 1
+    h_conf = np.log(W) - np.exp(16.0) / W * 16.0
+    assert np.allclose(r["entropy"][0, [2, 5, 6]], h_conf, rtol=1e-12)
+    assert 3 * h_conf < cfg.entropy_bound
+    assert list(r["committed"][0]) == [1, 0, 1, 0, 0, 1, 1, 0]
+    assert list(r["renoised"][0]) == [0, 1, 0, 1, 1, 0, 0, 1]
+    assert r["done"][0] == 0
+
+
+def test_entropy_bound_commits_all_and_ends():
+    V, S, L = 512, 8, 6
+    x = np.random.default_rng(1).standard_normal((1, L, V))
+    r = _one_step(x, 0, _eb_cfg(canvas_len=L, max_steps=S, seed=2, entropy_bound=1e9))
+    assert r["committed"].all() and r["done"][0] == 1 and r["renoised"].sum() == 0
+    assert np.array_equal(r["tokens"], r["sample"])
+    # fixed steps: no early end
+    r = _one_step(x, 0, _eb_cfg(canvas_len=L, max_steps=S, seed=2, entropy_bound=1e9,
+                                fixed_steps=4))
+    assert r["committed"].all() and r["done"][0] == 0
+
+
+def test_entropy_bound_zero_commits_one_per_step():
+    V, S, L = 512, 8, 5
+    cfg = _eb_cfg(canvas_len=L, max_steps=S, seed=3, entropy_bound=0.0, renoise_prob=0.0)
+    rng = np.random.default_rng(4)
+    tokens = np.zeros((1, L), np.int64)
+    committed = np.zeros((1, L), np.int64)
+    done = np.zeros(1, np.int64)
+    for s in range(L):
+        x = rng.standard_normal((1, L, V)) * 3
+        r = sampler_step(x, s, cfg, np.zeros(1, np.int64), tokens, committed, done)
+        new = r["committed"][0] - committed[0]
+        assert new.sum() == 1
+        free = np.flatnonzero(committed[0] == 0)
+        assert np.flatnonzero(new)[0] == free[np.argmin(r["entropy"][0, free])]
+        tokens, committed, done = r["tokens"], r["committed"], r["done"]
+        assert done[0] == (1 if s == L - 1 else 0)          # all committed -> ends
