@@ -1,4 +1,6 @@
 // C ABI: sampler step, canvas init, Philox and Gumbel test hooks.
+#include <cmath>
+
 #include "kernels.h"
 
 using namespace dg;
@@ -32,6 +34,10 @@ dg_status dg_sampler_step(const void* logits, int logit_dtype, int B, int L, int
   DG_CHECK_SHAPE(step >= 0 && step < limit, "dg_sampler_step: step outside the schedule");
   DG_CHECK_ARG(cfg->temp_start > 0.f && cfg->temp_end > 0.f,
                "dg_sampler_step: temperatures must be positive");
+  DG_CHECK_ARG(cfg->commit_policy == DG_COMMIT_MAXPROB ||
+                   (cfg->commit_policy == DG_COMMIT_ENTROPY_BOUND && cfg->entropy_bound >= 0.f &&
+                    cfg->entropy_bound < INFINITY),
+               "dg_sampler_step: bad commit_policy / entropy_bound");
   if (ws_bytes < sampler_workspace_bytes(B, L, V) || ws == nullptr)
     return fail(DG_ERR_WORKSPACE, "dg_sampler_step: workspace too small");
   return launch_sampler(logits, logit_dtype, B, L, V, step, *cfg, prefix_len, tokens, committed,

@@ -94,10 +94,14 @@ struct GraphKey {
   int B, Tmax, L, S, F;
   float t0, t1, eps, tc, tr;
   uint64_t seed;
+  int policy;
+  float bound;
+  int part;                 // which piece of a block (adaptive mode: chunks of steps)
   std::vector<void*> ptrs;
   bool operator<(const GraphKey& o) const {
-    return std::tie(B, Tmax, L, S, F, t0, t1, eps, tc, tr, seed, ptrs) <
-           std::tie(o.B, o.Tmax, o.L, o.S, o.F, o.t0, o.t1, o.eps, o.tc, o.tr, o.seed, o.ptrs);
+    return std::tie(B, Tmax, L, S, F, t0, t1, eps, tc, tr, seed, policy, bound, part, ptrs) <
+           std::tie(o.B, o.Tmax, o.L, o.S, o.F, o.t0, o.t1, o.eps, o.tc, o.tr, o.seed, o.policy,
+                    o.bound, o.part, o.ptrs);
   }
 };
 
@@ -130,6 +134,9 @@ struct dg_ctx {
   float* mean_entropy = nullptr;
   int32_t* done = nullptr;
   int32_t* status = nullptr;
+  int32_t* active = nullptr;       // dg_generate: rows that have not met EOS
+  int32_t* blk_tokens = nullptr;   // dg_generate: the current block's tokens [B, L]
+  int32_t* blk_steps = nullptr;    // dg_generate: the current block's steps [B]
   bool use_graphs = true;
   std::map<GraphKey, hipGraphExec_t> graphs;
   std::vector<const float*> router_override;   // empty: the model's own routing
@@ -144,7 +151,7 @@ namespace {
 struct Layout {
   size_t x, h, qkv, attn_out, router, topk_ids, gates, offsets, sorted_rows, attn_ws, moe_ws,
       logits, samp_ws, tokens, committed, renoised, maxprob, entropy, mean_entropy, done, status,
-      total;
+      active, blk_tokens, blk_steps, total;
 };
 
 size_t esz(int dt) { return dt == DG_F32 ? 4 : 2; }
@@ -188,6 +195,9 @@ Layout layout(const dg_model_dims& d, int maxB, int maxT) {
   L.mean_entropy = take(maxB * 4);
   L.done = take(maxB * 4);
   L.status = take(4);
+  L.active = take(maxB * 4);
+  L.blk_tokens = take(T * 4);
+  L.blk_steps = take(maxB * 4);
   L.total = off;
   return L;
 }
@@ -320,19 +330,25 @@ dg_status forward(dg_ctx* c, const int32_t* tokens, int B, int n, int l0, int l1
   return DG_OK;
 }
 
-dg_status enqueue_block(dg_ctx* c, const dg_sampler_cfg& cfg, int B, void* const* kcs,
-                        void* const* vcs, int Tmax, int32_t* prefix_len, int32_t* tokens_out,
-                        int32_t* steps_taken, hipStream_t s) {
-  const dg_model_dims& d = c->d;
-  const int L = cfg.canvas_len;
-  const int n_steps = cfg.fixed_steps > 0 ? cfg.fixed_steps : cfg.max_steps;
+// A block in three pieces: begin (canvas init), steps [s0, s1) (forward +
+// LM head + sampler each), end (commit forward, prefix advance, tokens out).
+dg_status enqueue_block_begin(dg_ctx* c, const dg_sampler_cfg& cfg, int B,
+                              const int32_t* prefix_len, int32_t* steps_taken, hipStream_t s) {
   dg_status st;
-  if ((st = launch_init_canvas(prefix_len, B, L, d.vocab, cfg.seed, c->tokens, c->committed,
-                               c->done, s)))
+  if ((st = launch_init_canvas(prefix_len, B, cfg.canvas_len, c->d.vocab, cfg.seed, c->tokens,
+                               c->committed, c->done, s)))
     return st;
   if ((st = fill_i32(steps_taken, B, 0, s))) return st;
-  if ((st = fill_i32(c->status, 1, 0, s))) return st;
-  for (int step = 0; step < n_steps; ++step) {
+  return fill_i32(c->status, 1, 0, s);
+}
+
+dg_status enqueue_block_steps(dg_ctx* c, const dg_sampler_cfg& cfg, int B, void* const* kcs,
+                              void* const* vcs, int Tmax, int32_t* prefix_len,
+                              int32_t* steps_taken, int s0, int s1, hipStream_t s) {
+  const dg_model_dims& d = c->d;
+  const int L = cfg.canvas_len;
+  dg_status st;
+  for (int step = s0; step < s1; ++step) {
     if ((st = forward(c, c->tokens, B, L, 0, d.n_layers, kcs, vcs, Tmax, prefix_len,
                       DG_MASK_CANVAS, c->logits, false, s)))
       return st;
@@ -341,14 +357,33 @@ dg_status enqueue_block(dg_ctx* c, const dg_sampler_cfg& cfg, int B, void* const
                              c->mean_entropy, c->done, c->status, steps_taken, c->samp_ws, s)))
       return st;
   }
+  return DG_OK;
+}
+
+dg_status enqueue_block_end(dg_ctx* c, const dg_sampler_cfg& cfg, int B, void* const* kcs,
+                            void* const* vcs, int Tmax, int32_t* prefix_len, int32_t* tokens_out,
+                            hipStream_t s) {
+  const int L = cfg.canvas_len;
+  dg_status st;
   // commit: the final tokens' K/V of every layer into slots [P, P + L)
-  if ((st = forward(c, c->tokens, B, L, 0, d.n_layers, kcs, vcs, Tmax, prefix_len,
+  if ((st = forward(c, c->tokens, B, L, 0, c->d.n_layers, kcs, vcs, Tmax, prefix_len,
                     DG_MASK_CANVAS, nullptr, true, s)))
     return st;
   if ((st = launch_advance_prefix(prefix_len, B, L, s))) return st;
   copy_i32_kernel<<<(B * L + 255) / 256, 256, 0, s>>>(c->tokens, tokens_out, B * L);
   DG_LAUNCH_CHECK();
   return DG_OK;
+}
+
+dg_status enqueue_block(dg_ctx* c, const dg_sampler_cfg& cfg, int B, void* const* kcs,
+                        void* const* vcs, int Tmax, int32_t* prefix_len, int32_t* tokens_out,
+                        int32_t* steps_taken, hipStream_t s) {
+  const int n_steps = cfg.fixed_steps > 0 ? cfg.fixed_steps : cfg.max_steps;
+  dg_status st;
+  if ((st = enqueue_block_begin(c, cfg, B, prefix_len, steps_taken, s))) return st;
+  if ((st = enqueue_block_steps(c, cfg, B, kcs, vcs, Tmax, prefix_len, steps_taken, 0, n_steps, s)))
+    return st;
+  return enqueue_block_end(c, cfg, B, kcs, vcs, Tmax, prefix_len, tokens_out, s);
 }
 
 // R29: n_steps greedy single-token causal steps; c->tokens holds each row's
@@ -389,6 +424,123 @@ dg_status check_run(dg_ctx* c, int B, int n, void* const* kcs, void* const* vcs,
                  std::string(fn) + ": more tokens than the router override holds");
   return DG_OK;
 }
+
+// Launch what enq(stream) enqueues: captured once per key into a hipGraph
+// and replayed when graphs are on and the stream is not the null stream,
+// else enqueued directly.
+template <typename F>
+dg_status run_graph(dg_ctx* ctx, const GraphKey& key, hipStream_t s, F&& enq) {
+  if (!ctx->use_graphs || s == nullptr) return enq(s);
+  auto it = ctx->graphs.find(key);
+  if (it == ctx->graphs.end()) {
+    DG_HIP(hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal));
+    const dg_status st = enq(s);
+    hipGraph_t g = nullptr;
+    hipError_t e = hipStreamEndCapture(s, &g);
+    if (st != DG_OK) {
+      if (g) (void)hipGraphDestroy(g);
+      return st;
+    }
+    if (e != hipSuccess)
+      return fail(DG_ERR_HIP, std::string("hipStreamEndCapture: ") + hipGetErrorString(e));
+    hipGraphExec_t exec = nullptr;
+    e = hipGraphInstantiate(&exec, g, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(g);
+    if (e != hipSuccess)
+      return fail(DG_ERR_HIP, std::string("hipGraphInstantiate: ") + hipGetErrorString(e));
+    it = ctx->graphs.emplace(key, exec).first;
+  }
+  DG_HIP(hipGraphLaunch(it->second, s));
+  return DG_OK;
+}
+
+dg_status check_block_cfg(const dg_sampler_cfg* cfg, const char* fn) {
+  DG_CHECK_SHAPE(cfg->max_steps >= 1 && cfg->fixed_steps >= 0 && cfg->fixed_steps <= cfg->max_steps,
+                 std::string(fn) + ": bad step settings");
+  DG_CHECK_ARG(cfg->temp_start > 0.f && cfg->temp_end > 0.f, std::string(fn) + ": bad temperatures");
+  DG_CHECK_ARG(cfg->commit_policy == DG_COMMIT_MAXPROB ||
+                   (cfg->commit_policy == DG_COMMIT_ENTROPY_BOUND && cfg->entropy_bound >= 0.f &&
+                    cfg->entropy_bound < INFINITY),
+               std::string(fn) + ": bad commit_policy / entropy_bound");
+  return DG_OK;
+}
+
+// Steps per captured piece in the adaptive mode: the host reads the rows'
+// done flags after each piece and stops once every row is done.
+constexpr int kAdaptiveChunk = 4;
+
+// One block (see dg_denoise_block).  part keys: 0 the whole fixed-steps
+// block; 1 + s0 the adaptive piece of steps [s0, s0 + chunk) (with the
+// canvas init when s0 == 0); -2 the commit.
+dg_status run_block(dg_ctx* c, const dg_sampler_cfg& cfg, int B, void* const* kcs,
+                    void* const* vcs, int Tmax, int32_t* prefix_len, int32_t* tokens_out,
+                    int32_t* steps_taken, hipStream_t s) {
+  GraphKey key{B, Tmax, cfg.canvas_len, cfg.max_steps, cfg.fixed_steps, cfg.temp_start,
+               cfg.temp_end, cfg.stop_entropy, cfg.commit_prob, cfg.renoise_prob, cfg.seed,
+               cfg.commit_policy, cfg.entropy_bound, 0, {}};
+  for (int l = 0; l < c->d.n_layers; ++l) {
+    key.ptrs.push_back(kcs[l]);
+    key.ptrs.push_back(vcs[l]);
+  }
+  key.ptrs.push_back(prefix_len);
+  key.ptrs.push_back(tokens_out);
+  key.ptrs.push_back(steps_taken);
+  if (cfg.fixed_steps > 0)
+    return run_graph(c, key, s, [&](hipStream_t q) {
+      return enqueue_block(c, cfg, B, kcs, vcs, Tmax, prefix_len, tokens_out, steps_taken, q);
+    });
+  const int S = cfg.max_steps;
+  std::vector<int32_t> done(B);
+  dg_status st;
+  for (int s0 = 0; s0 < S; s0 += kAdaptiveChunk) {
+    const int s1 = std::min(S, s0 + kAdaptiveChunk);
+    key.part = 1 + s0;
+    st = run_graph(c, key, s, [&](hipStream_t q) {
+      dg_status r = DG_OK;
+      if (s0 == 0 && (r = enqueue_block_begin(c, cfg, B, prefix_len, steps_taken, q))) return r;
+      return enqueue_block_steps(c, cfg, B, kcs, vcs, Tmax, prefix_len, steps_taken, s0, s1, q);
+    });
+    if (st != DG_OK) return st;
+    if (s1 == S) break;
+    DG_HIP(hipMemcpyAsync(done.data(), c->done, B * sizeof(int32_t), hipMemcpyDeviceToHost, s));
+    DG_HIP(hipStreamSynchronize(s));
+    bool all = true;
+    for (int b = 0; b < B; ++b) all = all && done[b] != 0;
+    if (all) break;
+  }
+  key.part = -2;
+  return run_graph(c, key, s, [&](hipStream_t q) {
+    return enqueue_block_end(c, cfg, B, kcs, vcs, Tmax, prefix_len, tokens_out, q);
+  });
+}
+
+// After a block of dg_generate: an active row copies the block out, counts
+// it and ends if it holds eos_id; a row that had ended undoes the block's
+// prefix advance (it rode along).  One workgroup per row.
+__global__ __launch_bounds__(256) void eos_block_kernel(
+    const int32_t* __restrict__ blk_tokens, const int32_t* __restrict__ blk_steps, int L,
+    int eos_id, int blk, int max_blocks, int32_t* __restrict__ active,
+    int32_t* __restrict__ prefix_len, int32_t* __restrict__ tokens_out,
+    int32_t* __restrict__ n_blocks, int32_t* __restrict__ steps_out) {
+  const int b = blockIdx.x;
+  if (!active[b]) {
+    if (threadIdx.x == 0) prefix_len[b] -= L;
+    return;
+  }
+  int hit = 0;
+  for (int i = threadIdx.x; i < L; i += 256) {
+    const int32_t t = blk_tokens[static_cast<size_t>(b) * L + i];
+    tokens_out[(static_cast<size_t>(b) * max_blocks + blk) * L + i] = t;
+    hit |= t == eos_id;
+  }
+  hit = __syncthreads_or(hit);
+  if (threadIdx.x == 0) {
+    n_blocks[b] = blk + 1;
+    steps_out[static_cast<size_t>(b) * max_blocks + blk] = blk_steps[b];
+    if (hit) active[b] = 0;
+  }
+}
+
 
 }  // namespace
 
@@ -456,6 +608,9 @@ dg_status dg_ctx_create(dg_ctx** out, const dg_model_dims* dims, const dg_model_
   c->mean_entropy = reinterpret_cast<float*>(b + L.mean_entropy);
   c->done = reinterpret_cast<int32_t*>(b + L.done);
   c->status = reinterpret_cast<int32_t*>(b + L.status);
+  c->active = reinterpret_cast<int32_t*>(b + L.active);
+  c->blk_tokens = reinterpret_cast<int32_t*>(b + L.blk_tokens);
+  c->blk_steps = reinterpret_cast<int32_t*>(b + L.blk_steps);
   *out = c;
   return DG_OK;
 }
@@ -547,12 +702,8 @@ dg_status dg_ar_decode(dg_ctx* ctx, int B, int n_steps, const int32_t* tokens_in
   DG_CHECK_SHAPE(ctx->d.vocab % 8 == 0, "dg_ar_decode: vocab must be a multiple of 8");
   dg_status st = check_run(ctx, B, 1, k_caches, v_caches, Tmax, prefix_len, "dg_ar_decode");
   if (st != DG_OK) return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (!ctx->use_graphs || s == nullptr)
-    return enqueue_ar(ctx, B, n_steps, tokens_in, k_caches, v_caches, Tmax, prefix_len,
-                      tokens_out, s);
   // graph key: F = -1 marks the AR loop (block keys have F >= 0)
-  GraphKey key{B, Tmax, 1, n_steps, -1, 0.f, 0.f, 0.f, 0.f, 0.f, 0, {}};
+  GraphKey key{B, Tmax, 1, n_steps, -1, 0.f, 0.f, 0.f, 0.f, 0.f, 0, 0, 0.f, 0, {}};
   for (int l = 0; l < ctx->d.n_layers; ++l) {
     key.ptrs.push_back(k_caches[l]);
     key.ptrs.push_back(v_caches[l]);
@@ -560,28 +711,10 @@ dg_status dg_ar_decode(dg_ctx* ctx, int B, int n_steps, const int32_t* tokens_in
   key.ptrs.push_back(prefix_len);
   key.ptrs.push_back(const_cast<int32_t*>(tokens_in));
   key.ptrs.push_back(tokens_out);
-  auto it = ctx->graphs.find(key);
-  if (it == ctx->graphs.end()) {
-    DG_HIP(hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal));
-    st = enqueue_ar(ctx, B, n_steps, tokens_in, k_caches, v_caches, Tmax, prefix_len, tokens_out,
-                    s);
-    hipGraph_t g = nullptr;
-    hipError_t e = hipStreamEndCapture(s, &g);
-    if (st != DG_OK) {
-      if (g) (void)hipGraphDestroy(g);
-      return st;
-    }
-    if (e != hipSuccess)
-      return fail(DG_ERR_HIP, std::string("hipStreamEndCapture: ") + hipGetErrorString(e));
-    hipGraphExec_t exec = nullptr;
-    e = hipGraphInstantiate(&exec, g, nullptr, nullptr, 0);
-    (void)hipGraphDestroy(g);
-    if (e != hipSuccess)
-      return fail(DG_ERR_HIP, std::string("hipGraphInstantiate: ") + hipGetErrorString(e));
-    it = ctx->graphs.emplace(key, exec).first;
-  }
-  DG_HIP(hipGraphLaunch(it->second, s));
-  return DG_OK;
+  return run_graph(ctx, key, static_cast<hipStream_t>(stream), [&](hipStream_t q) {
+    return enqueue_ar(ctx, B, n_steps, tokens_in, k_caches, v_caches, Tmax, prefix_len,
+                      tokens_out, q);
+  });
 }
 
 dg_status dg_denoise_block(dg_ctx* ctx, const dg_sampler_cfg* cfg, int B, void* const* k_caches,
@@ -589,47 +722,51 @@ dg_status dg_denoise_block(dg_ctx* ctx, const dg_sampler_cfg* cfg, int B, void* 
                            int32_t* tokens_out, int32_t* steps_taken, void* stream) {
   set_error("");
   DG_CHECK_ARG(ctx && cfg && tokens_out && steps_taken, "dg_denoise_block: null pointer");
-  DG_CHECK_SHAPE(cfg->max_steps >= 1 && cfg->fixed_steps >= 0 && cfg->fixed_steps <= cfg->max_steps,
-                 "dg_denoise_block: bad step settings");
-  DG_CHECK_ARG(cfg->temp_start > 0.f && cfg->temp_end > 0.f, "dg_denoise_block: bad temperatures");
-  dg_status st = check_run(ctx, B, cfg->canvas_len, k_caches, v_caches, Tmax, prefix_len,
-                           "dg_denoise_block");
+  dg_status st = check_block_cfg(cfg, "dg_denoise_block");
   if (st != DG_OK) return st;
+  st = check_run(ctx, B, cfg->canvas_len, k_caches, v_caches, Tmax, prefix_len,
+                 "dg_denoise_block");
+  if (st != DG_OK) return st;
+  return run_block(ctx, *cfg, B, k_caches, v_caches, Tmax, prefix_len, tokens_out, steps_taken,
+                   static_cast<hipStream_t>(stream));
+}
+
+dg_status dg_generate(dg_ctx* ctx, const dg_sampler_cfg* cfg, int B, void* const* k_caches,
+                      void* const* v_caches, int Tmax, int32_t* prefix_len, int32_t eos_id,
+                      int max_blocks, int32_t* tokens_out, int32_t* n_blocks,
+                      int32_t* steps_taken, void* stream) {
+  set_error("");
+  DG_CHECK_ARG(ctx && cfg && tokens_out && n_blocks && steps_taken, "dg_generate: null pointer");
+  dg_status st = check_block_cfg(cfg, "dg_generate");
+  if (st != DG_OK) return st;
+  st = check_run(ctx, B, cfg->canvas_len, k_caches, v_caches, Tmax, prefix_len, "dg_generate");
+  if (st != DG_OK) return st;
+  const int L = cfg->canvas_len;
+  DG_CHECK_SHAPE(max_blocks >= 1 && static_cast<int64_t>(max_blocks) * L <= Tmax,
+                 "dg_generate: need 1 <= max_blocks and max_blocks * L <= Tmax");
+  DG_CHECK_SHAPE(static_cast<int64_t>(B) * max_blocks * L < (1ll << 31),
+                 "dg_generate: B * max_blocks * L too large");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (!ctx->use_graphs || s == nullptr)
-    return enqueue_block(ctx, *cfg, B, k_caches, v_caches, Tmax, prefix_len, tokens_out,
-                         steps_taken, s);
-  GraphKey key{B, Tmax, cfg->canvas_len, cfg->max_steps, cfg->fixed_steps, cfg->temp_start,
-               cfg->temp_end, cfg->stop_entropy, cfg->commit_prob, cfg->renoise_prob, cfg->seed,
-               {}};
-  for (int l = 0; l < ctx->d.n_layers; ++l) {
-    key.ptrs.push_back(k_caches[l]);
-    key.ptrs.push_back(v_caches[l]);
+  const int n_out = B * max_blocks * L;
+  if ((st = fill_i32(tokens_out, n_out, -1, s))) return st;
+  if ((st = fill_i32(n_blocks, B, 0, s))) return st;
+  if ((st = fill_i32(steps_taken, B * max_blocks, 0, s))) return st;
+  if ((st = fill_i32(ctx->active, B, 1, s))) return st;
+  std::vector<int32_t> act(B);
+  for (int blk = 0; blk < max_blocks; ++blk) {
+    st = run_block(ctx, *cfg, B, k_caches, v_caches, Tmax, prefix_len, ctx->blk_tokens,
+                   ctx->blk_steps, s);
+    if (st != DG_OK) return st;
+    eos_block_kernel<<<B, 256, 0, s>>>(ctx->blk_tokens, ctx->blk_steps, L, eos_id, blk,
+                                       max_blocks, ctx->active, prefix_len, tokens_out, n_blocks,
+                                       steps_taken);
+    DG_LAUNCH_CHECK();
+    DG_HIP(hipMemcpyAsync(act.data(), ctx->active, B * sizeof(int32_t), hipMemcpyDeviceToHost, s));
+    DG_HIP(hipStreamSynchronize(s));
+    bool any = false;
+    for (int b = 0; b < B; ++b) any = any || act[b] != 0;
+    if (!any) break;
   }
-  key.ptrs.push_back(prefix_len);
-  key.ptrs.push_back(tokens_out);
-  key.ptrs.push_back(steps_taken);
-  auto it = ctx->graphs.find(key);
-  if (it == ctx->graphs.end()) {
-    DG_HIP(hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal));
-    st = enqueue_block(ctx, *cfg, B, k_caches, v_caches, Tmax, prefix_len, tokens_out,
-                       steps_taken, s);
-    hipGraph_t g = nullptr;
-    hipError_t e = hipStreamEndCapture(s, &g);
-    if (st != DG_OK) {
-      if (g) (void)hipGraphDestroy(g);
-      return st;
-    }
-    if (e != hipSuccess)
-      return fail(DG_ERR_HIP, std::string("hipStreamEndCapture: ") + hipGetErrorString(e));
-    hipGraphExec_t exec = nullptr;
-    e = hipGraphInstantiate(&exec, g, nullptr, nullptr, 0);
-    (void)hipGraphDestroy(g);
-    if (e != hipSuccess)
-      return fail(DG_ERR_HIP, std::string("hipGraphInstantiate: ") + hipGetErrorString(e));
-    it = ctx->graphs.emplace(key, exec).first;
-  }
-  DG_HIP(hipGraphLaunch(it->second, s));
   return DG_OK;
 }
 

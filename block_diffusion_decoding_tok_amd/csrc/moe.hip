@@ -248,11 +248,18 @@ constexpr int kGateRT = 8, kDownRT = 8;
 constexpr int kGateTB1Slots = 20;   // gate/up: 16-token tiles up to this many slots per expert
 constexpr int kTinySlots = 64;      // up to this many slots in all: half-size items
 
-// MXFP4 weights: a chunk of a tile is half the bytes of fp8, so the ring
-// holds more chunks to keep as many bytes in flight
+// MXFP4 weights: a chunk of a tile is half the bytes of fp8 (ring depth,
+// waves per SIMD and weight tiles per item are set on their own)
 constexpr int kMx4NR = 2, kMx4WPE = 3;
+constexpr int kMx4GateRT = 8, kMx4DownRT = 8;
 
-template <int TB, int WF, int MODE, bool TILED, int RT = (MODE == kGateUp ? kGateRT : kDownRT)>
+template <int WF, int MODE>
+constexpr int item_tiles() {
+  return WF == kWMx4 ? (MODE == kGateUp ? kMx4GateRT : kMx4DownRT)
+                     : (MODE == kGateUp ? kGateRT : kDownRT);
+}
+
+template <int TB, int WF, int MODE, bool TILED, int RT = item_tiles<WF, MODE>()>
 static void launch_wave(GemmArgs& g, int T, int k, int E, hipStream_t stream) {
   // grid: an upper bound of the tile count (E + slots / tile size) times the
   // weight row groups; the kernel deals the live items out itself
@@ -261,8 +268,12 @@ static void launch_wave(GemmArgs& g, int T, int k, int E, hipStream_t stream) {
   g.n_tiles_y = E + (T * k + 16 * TB - 1) / (16 * TB);
   g.n_tiles_total = g.n_tiles_x * g.n_tiles_y;
   const unsigned grid = static_cast<unsigned>((g.n_tiles_total + 7) / 8 * 8);
+  // bf16 chunks are twice the registers of fp8: two waves per SIMD (three
+  // would spill the ring)
   if constexpr (WF == kWMx4)
     gemm_wave_kernel<RT, TB, kMx4NR, WF, MODE, TILED, (TB == 1 ? kMx4WPE : 1)><<<grid, 64, 0, stream>>>(g);
+  else if constexpr (WF == kWBf16)
+    gemm_wave_kernel<RT, TB, kMoeNR, WF, MODE, TILED, (TB == 1 ? 2 : 1)><<<grid, 64, 0, stream>>>(g);
   else
     gemm_wave_kernel<RT, TB, kMoeNR, WF, MODE, TILED, (TB == 1 ? kMoeWPE : 1)><<<grid, 64, 0, stream>>>(g);
 }
@@ -292,7 +303,7 @@ static void launch_gate_up_mfma(const void* x, const void* wgu, const float* sgu
   const int64_t slots = static_cast<int64_t>(T) * k;
   if (slots <= kTinySlots) {
     // a few tokens (AR decode): half-size items, twice as many waves
-    launch_wave<1, WF, kGateUp, TILED, kGateRT / 2>(g, T, k, E, stream);
+    launch_wave<1, WF, kGateUp, TILED, item_tiles<WF, kGateUp>() / 2>(g, T, k, E, stream);
   } else if (slots <= kGateTB1Slots * static_cast<int64_t>(E)) {
     launch_wave<1, WF, kGateUp, TILED>(g, T, k, E, stream);
   } else if (slots <= 40ll * E || WF == kWMx4) {
@@ -321,7 +332,7 @@ static void launch_down_mfma(const bf16_t* h, const void* wd, const float* sd, c
   d.out = y_slot;
   const int64_t slots = static_cast<int64_t>(T) * k;
   if (slots <= kTinySlots) {
-    launch_wave<1, WF, kDown, TILED, kDownRT / 2>(d, T, k, E, stream);
+    launch_wave<1, WF, kDown, TILED, item_tiles<WF, kDown>() / 2>(d, T, k, E, stream);
   } else if (slots <= 40ll * E) {
     launch_wave<1, WF, kDown, TILED>(d, T, k, E, stream);
   } else if constexpr (WF == kWMx4) {

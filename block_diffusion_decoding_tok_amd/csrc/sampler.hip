@@ -192,7 +192,8 @@ constexpr int kFinishThreads = 256;
 __global__ __launch_bounds__(kFinishThreads) void sampler_finish_kernel(
     const SamplerPartial* __restrict__ part, int L, int V, int nsplit, float invT, int step,
     int ends_at_step, int adaptive, float stop_entropy, float commit_prob, float renoise_prob,
-    uint32_t k0, uint32_t k1, const int32_t* __restrict__ prefix_len,
+    int policy, float entropy_bound, uint32_t k0, uint32_t k1,
+    const int32_t* __restrict__ prefix_len,
     int32_t* __restrict__ tokens, uint8_t* __restrict__ committed,
     uint8_t* __restrict__ renoised, float* __restrict__ maxprob, float* __restrict__ entropy,
     float* __restrict__ mean_entropy, int32_t* __restrict__ done, int32_t* __restrict__ status,
@@ -202,7 +203,9 @@ __global__ __launch_bounds__(kFinishThreads) void sampler_finish_kernel(
   const int tid = threadIdx.x;
   extern __shared__ unsigned char smem_raw[];
   double* s_mp = reinterpret_cast<double*>(smem_raw);        // [L]
-  int32_t* s_sample = reinterpret_cast<int32_t*>(s_mp + L);  // [L]
+  double* s_h = s_mp + L;                                    // [L]
+  int32_t* s_sample = reinterpret_cast<int32_t*>(s_h + L);   // [L]
+  uint8_t* s_flag = reinterpret_cast<uint8_t*>(s_sample + L);   // [L] bit 0: uncommitted
   __shared__ double s_red[kFinishThreads / 64];
   __shared__ int s_nf[kFinishThreads / 64];
 
@@ -232,7 +235,9 @@ __global__ __launch_bounds__(kFinishThreads) void sampler_finish_kernel(
     const double mp = 1.0 / Z;
     const double H = log(Z) - A / Z;
     s_mp[i] = mp;
+    s_h[i] = H;
     s_sample[i] = best_v;
+    s_flag[i] = committed[static_cast<size_t>(b) * L + i] ? 0 : 1;
     maxprob[static_cast<size_t>(b) * L + i] = static_cast<float>(mp);
     entropy[static_cast<size_t>(b) * L + i] = static_cast<float>(H);
     hsum += H;
@@ -245,7 +250,28 @@ __global__ __launch_bounds__(kFinishThreads) void sampler_finish_kernel(
   int anynf = 0;
   for (int w = 0; w < kFinishThreads / 64; ++w) { tot += s_red[w]; anynf |= s_nf[w]; }
   const double hbar = tot / L;
-  const bool ends = adaptive ? (hbar < static_cast<double>(stop_entropy) || step == ends_at_step)
+  // entropy-bound policy: an uncommitted position commits when the
+  // entropies of the uncommitted positions ranked below it, by (entropy,
+  // position), sum to at most the bound -- the longest ranked prefix whose
+  // sum minus its largest term is within the bound (O(L^2) broadcast reads)
+  bool all_committed = false;
+  if (policy == DG_COMMIT_ENTROPY_BOUND) {
+    int left = 0;                      // uncommitted positions that stay so
+    for (int i = tid; i < L; i += kFinishThreads) {
+      if (!(s_flag[i] & 1)) continue;
+      const double hi = s_h[i];
+      double below = 0.0;
+      for (int j = 0; j < L; ++j) {
+        const double hj = s_h[j];
+        if ((s_flag[j] & 1) && (hj < hi || (hj == hi && j < i))) below += hj;
+      }
+      if (below <= static_cast<double>(entropy_bound)) s_flag[i] |= 2;
+      else left = 1;
+    }
+    all_committed = __syncthreads_or(left) == 0;
+  }
+  const bool ends = adaptive ? (hbar < static_cast<double>(stop_entropy) || step == ends_at_step ||
+                                all_committed)
                              : (step == ends_at_step);
   if (tid == 0) {
     mean_entropy[b] = static_cast<float>(hbar);
@@ -259,7 +285,10 @@ __global__ __launch_bounds__(kFinishThreads) void sampler_finish_kernel(
     uint8_t ren = 0;
     if (!committed[o]) {
       const double mpd = s_mp[i];   // thresholds compared in double
-      if (mpd >= static_cast<double>(commit_prob)) {
+      const bool commit = policy == DG_COMMIT_ENTROPY_BOUND
+                              ? (s_flag[i] & 2) != 0
+                              : mpd >= static_cast<double>(commit_prob);
+      if (commit) {
         tokens[o] = s_sample[i];
         committed[o] = 1;
       } else if (mpd < static_cast<double>(renoise_prob) && !ends) {
@@ -301,11 +330,17 @@ dg_status launch_sampler(const void* logits, int logit_dtype, int B, int L, int 
   DG_LAUNCH_CHECK();
   const int adaptive = cfg.fixed_steps > 0 ? 0 : 1;
   const int ends_at = cfg.fixed_steps > 0 ? cfg.fixed_steps - 1 : S - 1;
-  const size_t smem = static_cast<size_t>(L) * (sizeof(double) + sizeof(int32_t));
+  const size_t smem = static_cast<size_t>(L) * (2 * sizeof(double) + sizeof(int32_t) + 1);
+  static bool smem_set = false;        // up to 4096 positions: 86 KB of LDS
+  if (!smem_set) {
+    DG_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(sampler_finish_kernel),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, 4096 * 21));
+    smem_set = true;
+  }
   sampler_finish_kernel<<<B, kFinishThreads, smem, stream>>>(
       part, L, V, nsplit, invT, step, ends_at, adaptive, cfg.stop_entropy, cfg.commit_prob,
-      cfg.renoise_prob, k0, k1, prefix_len, tokens, committed, renoised, maxprob, entropy,
-      mean_entropy, done, status, steps_taken);
+      cfg.renoise_prob, cfg.commit_policy, cfg.entropy_bound, k0, k1, prefix_len, tokens,
+      committed, renoised, maxprob, entropy, mean_entropy, done, status, steps_taken);
   DG_LAUNCH_CHECK();
   return DG_OK;
 }

@@ -35,15 +35,20 @@ class dg_sampler_cfg(C.Structure):
                 ("fixed_steps", C.c_int32), ("temp_start", C.c_float),
                 ("temp_end", C.c_float), ("stop_entropy", C.c_float),
                 ("commit_prob", C.c_float), ("renoise_prob", C.c_float),
-                ("seed", C.c_uint64)]
+                ("seed", C.c_uint64), ("commit_policy", C.c_int32),
+                ("entropy_bound", C.c_float)]
+
+
+DG_COMMIT_MAXPROB, DG_COMMIT_ENTROPY_BOUND = 0, 1
 
 
 def sampler_cfg(canvas_len=256, max_steps=48, fixed_steps=0, temp_start=0.8,
                 temp_end=0.4, stop_entropy=0.005, commit_prob=0.9,
-                renoise_prob=0.1, seed=0):
+                renoise_prob=0.1, seed=0, commit_policy=DG_COMMIT_MAXPROB,
+                entropy_bound=0.1):
     return dg_sampler_cfg(canvas_len, max_steps, fixed_steps, temp_start,
                           temp_end, stop_entropy, commit_prob, renoise_prob,
-                          seed)
+                          seed, commit_policy, entropy_bound)
 
 
 class dg_model_dims(C.Structure):
@@ -100,6 +105,8 @@ _SIGS = {
     "dg_prefill": (_I, [_VP, _VP, _I, _I, C.POINTER(_VP), C.POINTER(_VP), _I, _VP, _VP]),
     "dg_denoise_block": (_I, [_VP, C.POINTER(dg_sampler_cfg), _I, C.POINTER(_VP),
                               C.POINTER(_VP), _I, _VP, _VP, _VP, _VP]),
+    "dg_generate": (_I, [_VP, C.POINTER(dg_sampler_cfg), _I, C.POINTER(_VP), C.POINTER(_VP),
+                         _I, _VP, C.c_int32, _I, _VP, _VP, _VP, _VP]),
     "dg_fill_normal": (_I, [_VP, _I, _SZ, _F, _U64, C.c_uint32, _VP]),
     "dg_quantize_fp8_rows": (_I, [_VP, _VP, _VP, _I64, _I, _VP]),
     "dg_pack_weights": (_I, [_VP, _VP, _I64, _I, _I, _I, _VP]),
@@ -466,6 +473,28 @@ def dg_denoise_block(model, cfg, B, k_caches, v_caches, prefix_len, tokens_out, 
         _dev(prefix_len, "prefix_len", (torch.int32,)),
         _dev(tokens_out, "tokens_out", (torch.int32,)),
         _dev(steps_taken, "steps_taken", (torch.int32,)), _stream(stream)))
+
+
+def dg_generate(model, cfg, B, k_caches, v_caches, prefix_len, eos_id, max_blocks,
+                tokens_out=None, n_blocks=None, steps_taken=None, stream=None):
+    """EOS-terminated multi-block decode; returns (tokens_out [B, max_blocks,
+    L], n_blocks [B], steps_taken [B, max_blocks])."""
+    dev = prefix_len.device
+    L = cfg.canvas_len
+    if tokens_out is None:
+        tokens_out = torch.empty((B, max_blocks, L), dtype=torch.int32, device=dev)
+    if n_blocks is None:
+        n_blocks = torch.empty(B, dtype=torch.int32, device=dev)
+    if steps_taken is None:
+        steps_taken = torch.empty((B, max_blocks), dtype=torch.int32, device=dev)
+    kc, vc = _ptr_array(k_caches), _ptr_array(v_caches)
+    _check(lib().dg_generate(
+        model.ctx, C.byref(cfg), B, kc, vc, k_caches[0].shape[2],
+        _dev(prefix_len, "prefix_len", (torch.int32,)), int(eos_id), int(max_blocks),
+        _dev(tokens_out, "tokens_out", (torch.int32,)),
+        _dev(n_blocks, "n_blocks", (torch.int32,)),
+        _dev(steps_taken, "steps_taken", (torch.int32,)), _stream(stream)))
+    return tokens_out, n_blocks, steps_taken
 
 
 # ------------------------------------------------------------ utilities

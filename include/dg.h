@@ -82,7 +82,18 @@ typedef enum { DG_LAYOUT_ROWMAJOR = 0, DG_LAYOUT_TILED = 1 } dg_layout;
  *   max_steps     S, step cap; the temperature schedule runs over S
  *   fixed_steps   0 = adaptive stop; F > 0 = exactly F steps, no stop test
  *   seed          Philox4x32-10 key (lo, hi words)
+ *   commit_policy DG_COMMIT_MAXPROB: an uncommitted position commits when its
+ *                 maxprob >= commit_prob.  DG_COMMIT_ENTROPY_BOUND: the
+ *                 serving configuration's "entropy_bound" sampler (developer
+ *                 guide, "vLLM으로 서빙하기": bound 0.1, a confidence-based
+ *                 early exit), read as entropy-bounded unmasking: the
+ *                 uncommitted positions ranked by (entropy, position), the
+ *                 longest prefix whose entropies sum, minus their maximum, to
+ *                 at most entropy_bound commits (at least one per step); in
+ *                 the adaptive mode the block also ends when all committed.
+ *   entropy_bound the bound in nats (>= 0), DG_COMMIT_ENTROPY_BOUND only
  */
+typedef enum { DG_COMMIT_MAXPROB = 0, DG_COMMIT_ENTROPY_BOUND = 1 } dg_commit_policy;
 typedef struct {
   int32_t canvas_len;
   int32_t max_steps;
@@ -93,6 +104,8 @@ typedef struct {
   float commit_prob;
   float renoise_prob;
   uint64_t seed;
+  int32_t commit_policy;
+  float entropy_bound;
 } dg_sampler_cfg;
 
 /* Library version (major * 10000 + minor * 100 + patch). */
@@ -317,10 +330,30 @@ dg_status dg_prefill(dg_ctx* ctx, const int32_t* prompt, int B, int n, void* con
  * row is done (adaptive) or fixed_steps; then one more forward of the final
  * tokens commits every layer's K/V to slots [P_b, P_b + L) and prefix_len += L.
  *   tokens_out [B, L] i32; steps_taken [B] i32 (steps each row ran).
- *   requires B <= max_batch, L <= max_tokens, P_b + L <= Tmax. */
+ *   requires B <= max_batch, L <= max_tokens, P_b + L <= Tmax.
+ * With fixed_steps the block is one asynchronous hipGraph (graphs on).  In
+ * the adaptive mode the steps run in chunks of a few steps and the call
+ * waits on the stream after each chunk to read the rows' done flags, so it
+ * stops as soon as every row is done; it returns once the block is queued
+ * behind the last chunk. */
 dg_status dg_denoise_block(dg_ctx* ctx, const dg_sampler_cfg* cfg, int B, void* const* k_caches,
                            void* const* v_caches, int Tmax, int32_t* prefix_len,
                            int32_t* tokens_out, int32_t* steps_taken, void* stream);
+
+/* dg_generate: EOS-terminated multi-block decode ([TR] "DiffusionGemma의
+ * 구성", flowchart: after each committed block, stop at EOS, else start the
+ * next canvas).  Blocks as in dg_denoise_block, one after another; a row ends
+ * after the first block holding eos_id, or after max_blocks blocks.  Rows
+ * that ended ride along in later blocks with prefix_len frozen (their cache
+ * slots past the prefix are scratch).  The call waits on the stream after
+ * each block and returns when every row ended.
+ *   tokens_out [B, max_blocks, L] i32 (-1 after a row's last block);
+ *   n_blocks [B] i32 (blocks each row produced); steps_taken [B, max_blocks]
+ *   i32 (0 after a row's last block); requires P_b + max_blocks * L <= Tmax. */
+dg_status dg_generate(dg_ctx* ctx, const dg_sampler_cfg* cfg, int B, void* const* k_caches,
+                      void* const* v_caches, int Tmax, int32_t* prefix_len, int32_t eos_id,
+                      int max_blocks, int32_t* tokens_out, int32_t* n_blocks,
+                      int32_t* steps_taken, void* stream);
 
 /* dg_ar_decode: autoregressive decoding on the same model, the left-to-right
  * baseline the canvas is compared with ([JPH] "좌→우 순차 처리와의 대비"; [TR]

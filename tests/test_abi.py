@@ -154,3 +154,15 @@ def test_mxfp4_rejects_bad_calls(lib):
     assert lib.dg_ctx_workspace_size(C.byref(dims), 1, 256) == 0
     dims.weight_layout = dg.DG_LAYOUT_TILED
     assert lib.dg_ctx_workspace_size(C.byref(dims), 1, 256) > 0
+
+
+def test_generate_and_policy_reject_bad_calls(lib):
+    f = C.c_void_p(256)
+    cfg = dg.sampler_cfg(commit_policy=7)
+    args = [f, dg.DG_BF16, 1, 256, 262144, 0, C.byref(cfg)] + [f] * 9 + [f, 1 << 30, None]
+    assert lib.dg_sampler_step(*args) == -1 and "commit_policy" in _last_error(lib)
+    cfg = dg.sampler_cfg(commit_policy=dg.DG_COMMIT_ENTROPY_BOUND, entropy_bound=-1.0)
+    args[6] = C.byref(cfg)
+    assert lib.dg_sampler_step(*args) == -1
+    assert lib.dg_generate(None, C.byref(dg.sampler_cfg()), 1, None, None, 64, f, 1, 2,
+                           f, f, f, None) == -1

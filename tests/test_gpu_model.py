@@ -45,6 +45,8 @@ def _tiny_block(cfg_kw, boost_rows=0, boost=1.0, B=2, graphs=True):
     # oracle
     okc, ovc = empty_caches(d, B, Tmax)
     P = prefill(m, prompt.numpy(), okc, ovc)
+    if "entropy_bound" in cfg_kw:            # the device holds the bound in float32
+        cfg_kw = dict(cfg_kw, entropy_bound=float(np.float32(cfg_kw["entropy_bound"])))
     ocfg = SamplerCfg(canvas_len=16, max_steps=8, **cfg_kw)
     o_tok, o_steps, trace, o_P = denoise_block(m, ocfg, okc, ovc, P)
     # device
@@ -59,7 +61,8 @@ def _tiny_block(cfg_kw, boost_rows=0, boost=1.0, B=2, graphs=True):
         assert Pd.cpu().tolist() == [32] * B
         pre = [k.cpu().double().numpy() for k in kc]
         assert rel_err_rows(pre[0][:, :, :32], okc[0][:, :, :32]) < 1e-5
-        gcfg = dg.sampler_cfg(16, 8, ocfg.fixed_steps, seed=ocfg.seed)
+        gcfg = dg.sampler_cfg(16, 8, ocfg.fixed_steps, seed=ocfg.seed,
+                              commit_policy=ocfg.commit_policy, entropy_bound=ocfg.entropy_bound)
         tok = torch.full((B, 16), -1, dtype=torch.int32, device=DEV)
         steps = torch.full((B,), -1, dtype=torch.int32, device=DEV)
         dg.dg_denoise_block(model, gcfg, B, kc, vc, Pd, tok, steps)
@@ -100,6 +103,61 @@ def test_tiny_loop_fixed_steps_and_second_block():
     r = _tiny_block(dict(fixed_steps=3, seed=5))
     assert list(r["steps"]) == [3, 3]
     _assert_block_parity(r)
+
+
+@pytest.mark.parametrize("graphs", [True, False])
+def test_tiny_loop_entropy_bound_random_weights(graphs):
+    """Entropy-bound policy at random weights (entropy about 6.2 per
+    position): one commit per step, the block runs to the cap."""
+    r = _tiny_block(dict(commit_policy=1, entropy_bound=0.1), graphs=graphs)
+    assert list(r["steps"]) == [8, 8]
+    assert all(tr["committed"].sum() == 2 * (tr["step"] + 1) for tr in r["trace"])
+    _assert_block_parity(r)
+
+
+def test_tiny_loop_entropy_bound_planted_early_exit():
+    r = _tiny_block(dict(commit_policy=1, entropy_bound=0.1), boost_rows=4, boost=400.0)
+    assert (r["steps"] < 8).all()
+    _assert_block_parity(r)
+
+
+def test_generate_eos_tiny():
+    """EOS-terminated multi-block decode against the oracle: the EOS id is one
+    that row 0 first produces in its second block, so row 0 stops after two
+    blocks and row 1 runs all three; tokens, block counts, steps and the
+    final prefix lengths bit-exact."""
+    from oracle import generate
+    d = TINY_DIMS
+    B, L, nb = 2, 16, 3
+    w = model_weights(d, seed=0)
+    m = oracle_model(d, w)
+    prompt = prompt_ids(B, 32, d.V, seed=0)
+    Tmax = 32 + nb * L
+    cfg = SamplerCfg(canvas_len=L, max_steps=4, seed=0)
+
+    def oracle_run(eos):
+        okc, ovc = empty_caches(d, B, Tmax)
+        P = prefill(m, prompt.numpy(), okc, ovc)
+        return generate(m, cfg, okc, ovc, P, eos, nb)
+    ref, _, _ = oracle_run(-5)
+    cand = [v for v in ref[0, 1] if v not in ref[0, 0] and v not in ref[1].ravel()]
+    eos = int(cand[0])
+    o_out, o_n, o_P = oracle_run(eos)
+    assert list(o_n) == [2, nb]
+
+    model = dg.DGModel(d, _dev_weights(w), B, L, dg.DG_F32, dg.DG_F32)
+    kc, vc = _caches(d, B, Tmax, torch.float32)
+    Pd = torch.zeros(B, dtype=torch.int32, device=DEV)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        dg.dg_prefill(model, prompt.to(DEV), kc, vc, Pd)
+        gcfg = dg.sampler_cfg(L, 4, 0, seed=0)
+        out, n, steps = dg.dg_generate(model, gcfg, B, kc, vc, Pd, eos, nb)
+        stream.synchronize()
+    assert np.array_equal(out.cpu().numpy(), o_out)
+    assert np.array_equal(n.cpu().numpy(), o_n)
+    assert np.array_equal(Pd.cpu().numpy(), o_P)
+    assert steps.cpu().numpy().tolist() == [[4, 4, 0], [4, 4, 4]]
 
 
 def test_graph_replay_matches_eager():

@@ -16,9 +16,12 @@ DEV = "cuda"
 
 
 def _cfg_pair(**kw):
+    if "entropy_bound" in kw:               # the device holds the bound in float32
+        kw["entropy_bound"] = float(np.float32(kw["entropy_bound"]))
     o = SamplerCfg(**kw)
     g = dg.sampler_cfg(o.canvas_len, o.max_steps, o.fixed_steps, o.temp_start, o.temp_end,
-                       o.stop_entropy, o.commit_prob, o.renoise_prob, o.seed)
+                       o.stop_entropy, o.commit_prob, o.renoise_prob, o.seed, o.commit_policy,
+                       o.entropy_bound)
     return o, g
 
 
@@ -93,7 +96,7 @@ def _run_and_compare(logits_dev, logits_host_f64, ocfg, gcfg, steps, P, state=No
         assert np.allclose(got["maxprob"][act], ref["maxprob"][act], rtol=2e-6, atol=1e-9)
         assert np.allclose(got["entropy"][act], ref["entropy"][act], rtol=2e-6, atol=2e-6)
         assert np.allclose(got["mean_entropy"][act], ref["mean_entropy"][act], rtol=2e-6, atol=1e-6)
-        excl, row_excl = sampler_exclusions(ref, ocfg)
+        excl, row_excl = sampler_exclusions(ref, ocfg, before["committed"])
         keep = ~excl
         for key in ("tokens", "committed", "renoised"):
             assert np.array_equal(got[key][keep], ref[key][keep]), (key, s)
@@ -172,3 +175,46 @@ def test_sampler_deterministic():
         outs.append(st.host())
     for k in outs[0]:
         assert np.array_equal(outs[0][k], outs[1][k]), k
+
+
+# ------------------------------------------------ entropy-bound commit policy
+
+def test_sampler_entropy_bound_full_size_bs1():
+    """The planted workload at steps 0, 23, 46, 47 of the schedule (the
+    device state carried between them): at least one commit per step, more
+    once the planted peaks sharpen as T falls to 0.4."""
+    case = sampler_case(B=1, L=256, V=262144, seed=0)
+    ocfg, gcfg = _cfg_pair(canvas_len=256, max_steps=48, seed=0, commit_policy=1,
+                           entropy_bound=0.1)
+    x64 = case.logits.to(torch.float64).numpy()
+    st, excl = _run_and_compare(case.logits.to(DEV), x64, ocfg, gcfg, [0, 23, 46, 47], [0])
+    assert excl <= 3
+    h = st.host()
+    assert h["committed"].sum() >= 4
+
+
+def test_sampler_entropy_bound_batch_and_bounds():
+    """Four rows of different peak heights; bounds 0 (one commit per step),
+    0.1 and 5 (many per step); reduced canvas length."""
+    B, L, V = 4, 40, 20000
+    for bound, seed in ((0.0, 3), (0.1, 4), (5.0, 5)):
+        case = sampler_case(B=B, L=L, V=V, seed=seed, dtype=torch.float32, peak=9.0)
+        ocfg, gcfg = _cfg_pair(canvas_len=L, max_steps=8, seed=seed, commit_policy=1,
+                               entropy_bound=bound)
+        x64 = case.logits.to(torch.float64).numpy()
+        st, _ = _run_and_compare(case.logits.to(DEV), x64, ocfg, gcfg, list(range(8)),
+                                 [0, 100, 7, 4096])
+        h = st.host()
+        assert h["done"].all()
+
+
+def test_sampler_entropy_bound_all_committed_ends_block():
+    B, L, V = 2, 16, 4096
+    x = torch.zeros((B, L, V))
+    x[0, :, 5] = 30.0                  # every position sure: all commit at step 0
+    ocfg, gcfg = _cfg_pair(canvas_len=L, max_steps=8, seed=2, commit_policy=1,
+                           entropy_bound=0.1, stop_entropy=0.0)
+    st, _ = _run_and_compare(x.to(DEV), x.double().numpy(), ocfg, gcfg, [0], [0, 0])
+    h = st.host()
+    assert h["committed"][0].all() and list(h["done"]) == [1, 0]
+    assert h["committed"][1].sum() == 1          # flat row: exactly one commit

@@ -62,11 +62,36 @@ def gumbel_band(top_score):
     return 1e-6 * np.maximum(1.0, np.abs(top_score))
 
 
-def sampler_exclusions(ref, cfg):
+EB_BAND = 1e-5           # entropy-bound sums / rank gaps closer than this: row excluded
+
+
+def entropy_bound_ambiguous(h, committed, bound):
+    """True when the entropy-bound selection of a row could flip between the
+    device's and the oracle's entropies: a ranked prefix sum within EB_BAND of
+    the bound, or the two positions that straddle the cut within EB_BAND of
+    each other."""
+    free = sorted((i for i in range(len(h)) if not committed[i]), key=lambda i: (h[i], i))
+    if len(free) < 2:
+        return False
+    hs = np.array([h[i] for i in free])
+    csum = np.cumsum(hs)[:-1]
+    if np.any(np.abs(csum - bound) < EB_BAND):
+        return True
+    n_sel = 1 + int(np.sum(csum <= bound))
+    return n_sel < len(hs) and hs[n_sel] - hs[n_sel - 1] < EB_BAND
+
+
+def sampler_exclusions(ref, cfg, committed_before=None):
     """Boolean [B, L] mask of positions whose integer outputs are excluded from
     the bit-exact comparison, and [B] mask of rows whose stop decision is."""
     mp = ref["maxprob"]
     near_tau = (np.abs(mp - cfg.commit_prob) < TAU_BAND) | (np.abs(mp - cfg.renoise_prob) < TAU_BAND)
+    if getattr(cfg, "commit_policy", 0) == 1:
+        near_tau = np.abs(mp - cfg.renoise_prob) < TAU_BAND
+        for b in range(mp.shape[0]):
+            if committed_before is not None and entropy_bound_ambiguous(
+                    ref["entropy"][b], committed_before[b], cfg.entropy_bound):
+                near_tau[b] = True
     near_tie = ref["gap"] < gumbel_band(ref["top_score"])
     row = np.abs(ref["mean_entropy"] - cfg.stop_entropy) < STOP_BAND
     return near_tau | near_tie | row[:, None], row
