@@ -95,6 +95,72 @@ def make_mxfp4_experts(d, w, seed=0):
     return out
 
 
+def entropy_bound_timing(d, w, model, B, kc, vc, Pd, stream):
+    """The entropy-bound commit policy (bound 0.1, adaptive mode):
+      * one block on the random-init model, whose positions stay uncertain
+        (entropy about 12 nats): one commit per step, so it runs to the cap
+        of 48 steps in chunks of 4 with a host check of the done flags between
+        chunks -- set against the same 48 steps as one graph (fixed mode);
+      * dg_generate with EOS on a copy of the model whose first 16 LM-head
+        rows are scaled by 400 (a planted confident head): every position
+        fits the bound at once, so a block ends after one step; 4 blocks
+        without EOS, then with the EOS id set to a token of the first block.
+    The prompt cache is reused; the prefix is rewound after each run."""
+    eb_cfg = dg.sampler_cfg(CANVAS, 48, 0, seed=0, commit_policy=dg.DG_COMMIT_ENTROPY_BOUND,
+                            entropy_bound=0.1)
+    fixed = dg.sampler_cfg(CANVAS, 48, 48, seed=0)
+    tok = torch.empty((B, CANVAS), dtype=torch.int32, device="cuda")
+    steps = torch.empty(B, dtype=torch.int32, device="cuda")
+
+    def one_block(m, c):
+        Pd.fill_(PROMPT)
+        dg.dg_denoise_block(m, c, B, kc, vc, Pd, tok, steps)      # capture + warm
+        stream.synchronize()
+        Pd.fill_(PROMPT)
+        stream.synchronize()
+        t0 = time.perf_counter()
+        dg.dg_denoise_block(m, c, B, kc, vc, Pd, tok, steps)
+        stream.synchronize()
+        return 1e3 * (time.perf_counter() - t0), steps.cpu().tolist()
+    ms_eb, st_eb = one_block(model, eb_cfg)
+    ms_fx, _ = one_block(model, fixed)
+    out = {"bound": 0.1,
+           "random_init_block": {"steps": st_eb, "ms": round(ms_eb, 2),
+                                 "fixed_48_step_graph_ms": round(ms_fx, 2),
+                                 "chunk_check_overhead_frac": round(ms_eb / ms_fx - 1, 4)}}
+    lm = w["lm"].clone()
+    lm[: (d.D // 64) * 1024] *= 400.0                        # tile 0: LM rows 0..15
+    w_pl = dict(w)
+    w_pl["lm"] = lm
+    m_pl = dg.DGModel(d, w_pl, B, CANVAS, dg.DG_BF16, dg.DG_FP8_E4M3,
+                      weight_layout=dg.DG_LAYOUT_TILED)
+    m_pl.set_router_override(planted_router_logits(d, CANVAS * B))
+
+    def gen(eos):
+        Pd.fill_(PROMPT)
+        dg.dg_generate(m_pl, eb_cfg, B, kc, vc, Pd, eos, 4)       # capture + warm
+        stream.synchronize()
+        Pd.fill_(PROMPT)
+        stream.synchronize()
+        t0 = time.perf_counter()
+        toks, nb, st = dg.dg_generate(m_pl, eb_cfg, B, kc, vc, Pd, eos, 4)
+        stream.synchronize()
+        el = time.perf_counter() - t0
+        n_tok = int(nb.sum().item()) * CANVAS
+        return dict(ms=round(1e3 * el, 2), n_blocks=nb.cpu().tolist(),
+                    steps=st.cpu().tolist(), tok_per_s=round(n_tok / el, 1)), toks
+    g_noeos, toks = gen(-1)
+    eos = int(toks[0, 0, 0].item())
+    g_eos, _ = gen(eos)
+    g_eos["eos_id"] = eos
+    out["planted_confident_generate"] = {"no_eos": g_noeos, "eos": g_eos}
+    m_pl.close()
+    del lm, w_pl
+    Pd.fill_(PROMPT)
+    stream.synchronize()
+    return out
+
+
 def planted_router_logits(d, T, seed=100):
     """Per-layer router logits with the stated MoE routing: N(0, 1) plus a
     planted skew so that 13 of 128 experts take 40% of the top-8 assignments
@@ -221,8 +287,16 @@ def sampler_fraction(d, B, reps=20):
     ms = _graph_ms(lambda: dg.dg_sampler_step(logits, 0, cfg, Pd, tok, com, ren, mp, en, me, done,
                                               ws=ws), reps)
     gbs = B * L * d.V * 2 / (ms * 1e-3) / 1e9
+    # the entropy-bound commit policy on the same logits (its ranked
+    # selection runs in the per-row finishing kernel)
+    cfg_eb = dg.sampler_cfg(L, 48, 0, seed=0, commit_policy=dg.DG_COMMIT_ENTROPY_BOUND,
+                            entropy_bound=0.1)
+    com.zero_()
+    ms_eb = _graph_ms(lambda: dg.dg_sampler_step(logits, 0, cfg_eb, Pd, tok, com, ren, mp, en, me,
+                                                 done, ws=ws), reps)
     return {"op": f"dg_sampler_step, bf16 logits [{B}, 256, {d.V}], step 0",
-            "ms_per_call": round(ms, 4), "gbs": round(gbs, 1), "bound": "alu (Philox + 2 ln per logit)",
+            "ms_per_call": round(ms, 4), "ms_per_call_entropy_bound": round(ms_eb, 4),
+            "gbs": round(gbs, 1), "bound": "alu (Philox + 2 ln per logit)",
             "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
             "gumbel_draws_per_s": float(f"{B * L * d.V / (ms * 1e-3):.4g}")}
 
@@ -333,6 +407,8 @@ def main():
                     help="skip the timed re-encoding of the prompt")
     ap.add_argument("--no-mxfp4", action="store_true",
                     help="skip the timing of the same model with MXFP4 experts")
+    ap.add_argument("--no-eb", action="store_true",
+                    help="skip the entropy-bound policy / EOS generate timings")
     ap.add_argument("--steps48", action="store_true",
                     help="also time 4 blocks at 48 fixed steps each")
     a = ap.parse_args()
@@ -431,6 +507,11 @@ def main():
         if a.steps48:
             cfg48 = dg.sampler_cfg(CANVAS, 48, 48, seed=0)
             t48 = timed(4, cfg48)
+        # entropy-bound commit policy (adaptive blocks, early exit) and
+        # EOS-terminated generate
+        eb = None
+        if not a.no_eb:
+            eb = entropy_bound_timing(d, w, model, B, kc, vc, Pd, stream)
         # the same step with MXFP4 experts (same draws, quantized on the
         # device), planted routing, same prompt cache
         mx = None
@@ -504,6 +585,8 @@ def main():
                     "layer 0, so fewer expert bytes move)"}
     if t48 is not None:
         out["tok_per_s_at_48"] = round(4 * CANVAS * B / t48, 1)
+    if eb is not None:
+        out["entropy_bound"] = eb
     if mx is not None:
         mx["note"] = ("the same step with OCP MXFP4 experts (E2M1, one E8M0 scale per 32 k) "
                       "quantized on the device from the same draws, planted routing")

@@ -256,17 +256,31 @@ __global__ __launch_bounds__(kFinishThreads) void sampler_finish_kernel(
   // sum minus its largest term is within the bound (O(L^2) broadcast reads)
   bool all_committed = false;
   if (policy == DG_COMMIT_ENTROPY_BOUND) {
+    // ranking keys: committed positions take +inf and never rank below
+    for (int i = tid; i < L; i += kFinishThreads)
+      if (!(s_flag[i] & 1)) s_h[i] = INFINITY;
+    __syncthreads();
     int left = 0;                      // uncommitted positions that stay so
     for (int i = tid; i < L; i += kFinishThreads) {
       if (!(s_flag[i] & 1)) continue;
       const double hi = s_h[i];
-      double below = 0.0;
-      for (int j = 0; j < L; ++j) {
-        const double hj = s_h[j];
-        if ((s_flag[j] & 1) && (hj < hi || (hj == hi && j < i))) below += hj;
+      double below[4] = {0.0, 0.0, 0.0, 0.0};   // independent partial sums
+      int j = 0;
+      for (; j + 4 <= L; j += 4) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const double hj = s_h[j + u];
+          below[u] += (hj < hi || (hj == hi && j + u < i)) ? hj : 0.0;
+        }
       }
-      if (below <= static_cast<double>(entropy_bound)) s_flag[i] |= 2;
-      else left = 1;
+      for (; j < L; ++j) {
+        const double hj = s_h[j];
+        below[0] += (hj < hi || (hj == hi && j < i)) ? hj : 0.0;
+      }
+      if ((below[0] + below[1]) + (below[2] + below[3]) <= static_cast<double>(entropy_bound))
+        s_flag[i] |= 2;
+      else
+        left = 1;
     }
     all_committed = __syncthreads_or(left) == 0;
   }
