@@ -9,7 +9,8 @@
 // positions, rotated keys in the cache.
 //
 // Launch sequence:
-//   1. rope_kernel: per token (heads spread over the workgroup's threads),
+//   1. rope_kernel (unless the QKV projection already did it in its
+//      epilogue): per token (heads spread over the workgroup's threads),
 //      rotates the block's q (into a packed workspace
 //      [B, Hkv, Lq * G, dh], packed row r = token * G + (head % G); for the
 //      bf16 path pre-multiplied by log2(e) / sqrt(dh), so that scores come
@@ -511,14 +512,15 @@ dg_status launch_attention(const AttnArgs& a, void* ws, hipStream_t stream) {
   char* w = static_cast<char*>(ws);
   void* qrot = w;
   if (a.dtype == DG_BF16) {
-    const float scale_log2 = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(a.dh)));
-    rope_kernel<bf16_t><<<a.B * a.Lq, rope_threads(a.dh), 0, stream>>>(
-        static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.k_new),
-        static_cast<const bf16_t*>(a.v_new), a.q_stride, a.kv_stride,
-        static_cast<bf16_t*>(qrot), static_cast<bf16_t*>(a.k_cache),
-        static_cast<bf16_t*>(a.v_cache), a.prefix_len, a.Lq, a.Hq, a.Hkv, a.dh, a.Tmax,
-        a.rope_theta, scale_log2);
-    DG_LAUNCH_CHECK();
+    if (!a.q_ready) {
+      rope_kernel<bf16_t><<<a.B * a.Lq, rope_threads(a.dh), 0, stream>>>(
+          static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.k_new),
+          static_cast<const bf16_t*>(a.v_new), a.q_stride, a.kv_stride,
+          static_cast<bf16_t*>(qrot), static_cast<bf16_t*>(a.k_cache),
+          static_cast<bf16_t*>(a.v_cache), a.prefix_len, a.Lq, a.Hq, a.Hkv, a.dh, a.Tmax,
+          a.rope_theta, attn_q_scale(a.dh));
+      DG_LAUNCH_CHECK();
+    }
     float* o_part = reinterpret_cast<float*>(w + p.q_bytes);
     AttnPartialML* ml = reinterpret_cast<AttnPartialML*>(w + p.q_bytes + p.o_bytes);
     const int total = p.tiles * p.nsplit * a.B * a.Hkv;

@@ -74,14 +74,22 @@ __device__ __forceinline__ double warp_sum_d(double v) {
 
 // RoPE angle for (position, pair j) reduced to [-pi, pi] in double, then
 // evaluated in float: pos * theta^(-2j/dh).
-__device__ __forceinline__ void rope_cos_sin(int pos, int j, int dh, float theta, float* c,
-                                             float* s) {
-  double inv = exp(-2.0 * static_cast<double>(j) / dh * log(static_cast<double>(theta)));
+// RoPE frequency of pair j: theta^(-2 j / dh), in double.
+__device__ __forceinline__ double rope_inv_freq(int j, int dh, float theta) {
+  return exp(-2.0 * static_cast<double>(j) / dh * log(static_cast<double>(theta)));
+}
+
+// cos / sin of the angle pos * inv, reduced to [-pi, pi] in double first.
+__device__ __forceinline__ void rope_cos_sin_at(int pos, double inv, float* c, float* s) {
   double ang = static_cast<double>(pos) * inv;
   const double two_pi = 6.283185307179586476925286766559;
   ang -= two_pi * rint(ang / two_pi);
-  float a = static_cast<float>(ang);
-  sincosf(a, s, c);
+  sincosf(static_cast<float>(ang), s, c);
+}
+
+__device__ __forceinline__ void rope_cos_sin(int pos, int j, int dh, float theta, float* c,
+                                             float* s) {
+  rope_cos_sin_at(pos, rope_inv_freq(j, dh, theta), c, s);
 }
 
 // Logical workgroup index for a grid of a multiple of 8 workgroups:

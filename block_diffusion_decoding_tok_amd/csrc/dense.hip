@@ -291,6 +291,41 @@ dg_status launch_gemm(const void* A, const void* W, void* C, int M, int N, int K
   return DG_OK;
 }
 
+dg_status launch_qkv_rope(const void* A, const void* W, int K, int w_layout, const QkvRope& r,
+                          hipStream_t stream) {
+  const int M = r.B * r.Lq;
+  const int N = (r.Hq + 2 * r.Hkv) * r.dh;
+  // the wide split-K tiles: 16 kProjRT = 128 rows = one head of 128
+  if (!(r.dh == 128 && kProjRT == 8 && M > 16 && N >= 1024 && K % 64 == 0 && K >= 64 * 8 &&
+        r.Hq % r.Hkv == 0))
+    return DG_ERR_UNSUPPORTED;
+  GemmArgs g{};
+  g.W = W; g.X = static_cast<const bf16_t*>(A);
+  g.N = N; g.K = K; g.M = M; g.n_groups = 1;
+  g.out_dtype = DG_BF16;
+  g.y_fastest = 1;
+  g.rope = 1;
+  g.prefix_len = r.prefix_len;
+  g.Lq = r.Lq; g.Hq = r.Hq; g.Hkv = r.Hkv; g.Tmax = r.Tmax;
+  g.theta = r.theta;
+  g.q_scale = attn_q_scale(r.dh);
+  g.q_out = static_cast<bf16_t*>(r.q_out);
+  g.k_cache = static_cast<bf16_t*>(r.k_cache);
+  g.v_cache = static_cast<bf16_t*>(r.v_cache);
+  g.n_tiles_x = N / (16 * kProjRT);
+  g.n_tiles_y = (M + 16 * kProjTB - 1) / (16 * kProjTB);
+  g.n_tiles_total = g.n_tiles_x * g.n_tiles_y;
+  const unsigned grid = (g.n_tiles_total + 7) / 8 * 8;
+  if (w_layout == DG_LAYOUT_TILED)
+    gemm_splitk_kernel<kProjRT, kProjTB, kSplitNR, kProjNW, true, kProjWPE>
+        <<<grid, 64 * kProjNW, 0, stream>>>(g);
+  else
+    gemm_splitk_kernel<kProjRT, kProjTB, kSplitNR, kProjNW, false, kProjWPE>
+        <<<grid, 64 * kProjNW, 0, stream>>>(g);
+  DG_LAUNCH_CHECK();
+  return DG_OK;
+}
+
 template <bool TILED>
 static void launch_gemm_bf16(GemmArgs& g, int M, int N, int K, hipStream_t stream) {
   if (TILED && N >= 32768 && N % kWideRows == 0 && K % 64 == 0 && !g.accumulate &&

@@ -60,6 +60,16 @@ struct GemmArgs {
   int n_tiles_y;            // token-tile slots
   int n_tiles_total;        // logical workgroups (x * y)
   int y_fastest;            // dense: logical order with token tiles of the same rows adjacent
+  // dense QKV projection with the RoPE epilogue (gemm_splitk_kernel, 128-row
+  // tiles = one head of 128): out is unused; q (rotated, scaled by q_scale)
+  // goes to the packed attention layout, k (rotated) and v to the caches
+  int rope;
+  const int32_t* prefix_len;
+  int Lq, Hq, Hkv, Tmax;
+  float theta, q_scale;
+  bf16_t* q_out;
+  bf16_t* k_cache;
+  bf16_t* v_cache;
 };
 
 __device__ __forceinline__ float gelu_erf(float x) {
@@ -634,10 +644,12 @@ __global__ __launch_bounds__(64 * NW, WPE) void gemm_splitk_kernel(GemmArgs a) {
   static_assert(RT * TB * 64 <= 64 * NW * 4, "at most four output quads per thread");
   static_assert(NW == 4 || NW == 8, "four or eight waves");
   __shared__ __attribute__((aligned(16))) float s_acc[4][RT * TB * 4][64];
+  __shared__ double s_inv[64];                  // RoPE epilogue: frequencies of the 64 pairs
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g4 = lane >> 4;
   const int logical = xcd_logical_tile(blockIdx.x, gridDim.x);
   if (logical >= a.n_tiles_total) return;
+  if (RT == 8 && a.rope && tid < 64) s_inv[tid] = rope_inv_freq(tid, 128, a.theta);
   const int tx = logical / a.n_tiles_y;       // row tile (token tiles adjacent)
   const int ty = logical % a.n_tiles_y;
   const int m0 = ty * 16 * TB;
@@ -759,6 +771,63 @@ __global__ __launch_bounds__(64 * NW, WPE) void gemm_splitk_kernel(GemmArgs a) {
         for (int r = 0; r < 4; ++r) s_acc[wave][(rt * TB + tb) * 4 + r][lane] = acc[rt][tb][r];
   }
   __syncthreads();
+  if constexpr (RT == 8) {
+    if (a.rope) {
+      // RoPE pairs (d, d + 64) of the tile's head: the quads of row tiles rt
+      // and rt + 4 (rt < 4); rotation as in the separate RoPE kernel
+      constexpr int kPairs = (RT / 2) * TB * 64;
+#pragma unroll
+      for (int q0 = 0; q0 < kPairs; q0 += 64 * NW) {
+        const int q = q0 + tid;
+        if (q >= kPairs) break;
+        const int ql = q & 63, blk = q >> 6;    // blk = rt * TB + tb, rt < 4
+        const int rt = blk / TB, tb = blk % TB;
+        const int blk2 = blk + (RT / 2) * TB;
+        float v1[4], v2[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          v1[r] = ((s_acc[0][blk * 4 + r][ql] + s_acc[1][blk * 4 + r][ql]) + s_acc[2][blk * 4 + r][ql]) +
+                  s_acc[3][blk * 4 + r][ql];
+          v2[r] = ((s_acc[0][blk2 * 4 + r][ql] + s_acc[1][blk2 * 4 + r][ql]) + s_acc[2][blk2 * 4 + r][ql]) +
+                  s_acc[3][blk2 * 4 + r][ql];
+        }
+        const int m = m0 + tb * 16 + (ql & 15);
+        if (m >= a.M) continue;
+        const int head = n0 / 128;
+        const int d0 = rt * 16 + (ql >> 4) * 4;  // < 64
+        const int b = m / a.Lq, i = m % a.Lq;
+        const int pos = a.prefix_len[b] + i;
+        float o1[4], o2[4];
+        bf16_t* dst;
+        if (head < a.Hq + a.Hkv) {
+          const float sc = head < a.Hq ? a.q_scale : 1.f;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float c, sn;
+            rope_cos_sin_at(pos, s_inv[d0 + r], &c, &sn);
+            o1[r] = (v1[r] * c - v2[r] * sn) * sc;
+            o2[r] = (v2[r] * c + v1[r] * sn) * sc;
+          }
+          if (head < a.Hq) {
+            const int G = a.Hq / a.Hkv;
+            const int64_t row = static_cast<int64_t>(i) * G + head % G;
+            dst = a.q_out + ((static_cast<int64_t>(b) * a.Hkv + head / G) * a.Lq * G + row) * 128;
+          } else {
+            dst = a.k_cache + ((static_cast<int64_t>(b) * a.Hkv + (head - a.Hq)) * a.Tmax + pos) * 128;
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) { o1[r] = v1[r]; o2[r] = v2[r]; }
+          dst = a.v_cache +
+                ((static_cast<int64_t>(b) * a.Hkv + (head - a.Hq - a.Hkv)) * a.Tmax + pos) * 128;
+        }
+        *reinterpret_cast<uint2*>(dst + d0) = make_uint2(pack_bf16x2(o1[0], o1[1]), pack_bf16x2(o1[2], o1[3]));
+        *reinterpret_cast<uint2*>(dst + d0 + 64) =
+            make_uint2(pack_bf16x2(o2[0], o2[1]), pack_bf16x2(o2[2], o2[3]));
+      }
+      return;
+    }
+  }
   constexpr int kQuads = RT * TB * 64;          // (row tile, token block, lane) quads
 #pragma unroll
   for (int q0 = 0; q0 < kQuads; q0 += 64 * NW) {

@@ -32,7 +32,13 @@ struct AttnArgs {
   float rope_theta;
   int dtype;
   void* out;                          // [B, Lq, Hq, dh] dense
+  int q_ready = 0;                    // q already rotated in the workspace, k/v in the caches
 };
+// Scale of the packed q of the bf16 attention kernel: log2(e) / sqrt(dh), so
+// that scores come out of the MFMA in the log2 domain.
+inline float attn_q_scale(int dh) {
+  return static_cast<float>(1.4426950408889634 / __builtin_sqrt(static_cast<double>(dh)));
+}
 size_t attention_workspace_bytes(int B, int Lq, int Hq, int Hkv, int dh, int Tmax, int dtype);
 dg_status launch_attention(const AttnArgs& a, void* ws, hipStream_t stream);
 dg_status launch_commit(const void* k_new, const void* v_new, int64_t kv_stride, void* k_cache,
@@ -73,6 +79,20 @@ dg_status launch_moe_ffn(const void* x, int x_dtype, const void* w_gate_up, cons
 enum GemmEpilogue { kStore = 0, kAccumulateF32 = 1 };
 dg_status launch_gemm(const void* A, const void* W, void* C, int M, int N, int K, int dtype,
                       int w_layout, int out_dtype, GemmEpilogue ep, hipStream_t stream);
+// The bf16 QKV projection with RoPE in its epilogue: q rotated and scaled
+// into the attention workspace's packed q (its first bytes), k rotated and v
+// into the caches at [P, P + Lq).  DG_ERR_UNSUPPORTED when the shape does not
+// take the fused path (then run the projection and the attention's own RoPE).
+struct QkvRope {
+  const int32_t* prefix_len;
+  int B, Lq, Hq, Hkv, dh, Tmax;
+  float theta;
+  void* q_out;
+  void* k_cache;
+  void* v_cache;
+};
+dg_status launch_qkv_rope(const void* A, const void* W, int K, int w_layout, const QkvRope& r,
+                          hipStream_t stream);
 // RMSNorm of f32 rows x [M, D] (eps 1e-6, unit gain) into out_dtype.
 dg_status launch_rmsnorm(const float* x, void* out, int M, int D, int out_dtype,
                          hipStream_t stream);

@@ -237,6 +237,7 @@ dg_status check_dims(const dg_model_dims* d) {
 }
 
 dg_status norm_input(dg_ctx* c, int T, hipStream_t s);
+dg_status layer_tail(dg_ctx* c, int l, int B, int n, hipStream_t s);
 
 // One decoder layer over T = B * n tokens (residual ctx->x).
 dg_status layer(dg_ctx* c, int l, int B, int n, void* kc, void* vc, int Tmax,
@@ -248,6 +249,21 @@ dg_status layer(dg_ctx* c, int l, int B, int n, void* kc, void* vc, int Tmax,
   const size_t a = esz(d.act_dtype);
   dg_status st;
   if ((st = norm_input(c, T, s))) return st;
+  // bf16: the projection rotates q and k in its epilogue and writes q to the
+  // attention workspace, k and v to the caches (one launch less per layer)
+  if (d.act_dtype == DG_BF16) {
+    const QkvRope r{prefix_len, B, n, d.n_heads, d.n_kv_heads, d.head_dim, Tmax, d.rope_theta,
+                    c->attn_ws, kc, vc};
+    st = launch_qkv_rope(c->h, c->wqkv[l], d.d_model, d.weight_layout, r, s);
+    if (st == DG_OK) {
+      if (kv_only) return DG_OK;
+      AttnArgs aa{nullptr, nullptr, nullptr, 0, 0, kc, vc, prefix_len, B, n, d.n_heads,
+                  d.n_kv_heads, d.head_dim, Tmax, mode, d.rope_theta, d.act_dtype, c->attn_out, 1};
+      if ((st = launch_attention(aa, c->attn_ws, s))) return st;
+      return layer_tail(c, l, B, n, s);
+    }
+    if (st != DG_ERR_UNSUPPORTED) return st;
+  }
   if ((st = launch_gemm(c->h, c->wqkv[l], c->qkv, T, qkv_w, d.d_model, d.act_dtype,
                         d.weight_layout, d.act_dtype, kStore, s)))
     return st;
@@ -260,6 +276,17 @@ dg_status layer(dg_ctx* c, int l, int B, int n, void* kc, void* vc, int Tmax,
               d.n_heads, d.n_kv_heads, d.head_dim, Tmax, mode, d.rope_theta, d.act_dtype,
               c->attn_out};
   if ((st = launch_attention(aa, c->attn_ws, s))) return st;
+  return layer_tail(c, l, B, n, s);
+}
+
+// The rest of a layer after attention: O projection + residual, RMSNorm,
+// router, routing, expert gate/up and down (the combine waits for the next
+// norm).
+dg_status layer_tail(dg_ctx* c, int l, int B, int n, hipStream_t s) {
+  const dg_model_dims& d = c->d;
+  const int T = B * n;
+  const int qd = d.n_heads * d.head_dim;
+  dg_status st;
   if ((st = launch_gemm(c->attn_out, c->wo[l], c->x, T, d.d_model, qd, d.act_dtype,
                         d.weight_layout, DG_F32, kAccumulateF32, s)))
     return st;
