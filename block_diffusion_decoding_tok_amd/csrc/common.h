@@ -72,9 +72,9 @@ __device__ __forceinline__ double warp_sum_d(double v) {
   return v;
 }
 
-// RoPE angle for (position, pair j) reduced to [-pi, pi] in double, then
-// evaluated in float: pos * theta^(-2j/dh).
-// RoPE frequency of pair j: theta^(-2 j / dh), in double.
+// RoPE: the angle pos * theta^(-2j/dh) of pair j, reduced to [-pi, pi] in
+// double, then evaluated in float.
+// Frequency of pair j: theta^(-2 j / dh), in double.
 __device__ __forceinline__ double rope_inv_freq(int j, int dh, float theta) {
   return exp(-2.0 * static_cast<double>(j) / dh * log(static_cast<double>(theta)));
 }

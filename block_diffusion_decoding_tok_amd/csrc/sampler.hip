@@ -82,17 +82,28 @@ __global__ __launch_bounds__(kSampThreads) void sampler_partial_kernel(
     if (valid[g]) vals[g].load(row + v0);
   }
 
-  // pass 1: max (and finiteness)
+  // pass 1: max and Gumbel-max over the slice (increasing v per thread)
+  const uint32_t pos = static_cast<uint32_t>(prefix_len[b] + i);
+  const uint32_t c3 = (kStreamGumbel << 24) | static_cast<uint32_t>(b);
   float lmax = -INFINITY;
-  bool nonfinite = false;
+  float best = -INFINITY;
+  int best_v = 0x7fffffff;
 #pragma unroll
   for (int g = 0; g < kSampGroups; ++g) {
     if (!valid[g]) continue;
+    const int v0 = v_begin + (g * kSampThreads + tid) * 8;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float x = vals[g].get(j);
-      nonfinite |= !isfinite(x);
-      lmax = fmaxf(lmax, x);
+    for (int h = 0; h < 2; ++h) {
+      const Philox4 r = philox4x32_10(static_cast<uint32_t>((v0 >> 2) + h), pos,
+                                      static_cast<uint32_t>(step), c3, k0, k1);
+      const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float x = vals[g].get(4 * h + q);
+        lmax = fmaxf(lmax, x);
+        const float sc = __builtin_fmaf(x, invT, gumbel_from_word(w[q]));
+        if (sc > best) { best = sc; best_v = v0 + 4 * h + q; }
+      }
     }
   }
 
@@ -114,28 +125,13 @@ __global__ __launch_bounds__(kSampThreads) void sampler_partial_kernel(
     Z += zs;
     A2 += as;
   }
-
-  // pass 3: Gumbel-max over the slice (increasing v per thread)
-  const uint32_t pos = static_cast<uint32_t>(prefix_len[b] + i);
-  const uint32_t c3 = (kStreamGumbel << 24) | static_cast<uint32_t>(b);
-  float best = -INFINITY;
-  int best_v = 0x7fffffff;
+  // a non-finite logit shows in the sums: NaN propagates through the
+  // differences, +inf makes lmax infinite (and inf - inf NaN), -inf gives
+  // 0 * -inf = NaN in A
+  bool any_valid = false;
 #pragma unroll
-  for (int g = 0; g < kSampGroups; ++g) {
-    if (!valid[g]) continue;
-    const int v0 = v_begin + (g * kSampThreads + tid) * 8;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const Philox4 r = philox4x32_10(static_cast<uint32_t>((v0 >> 2) + h), pos,
-                                      static_cast<uint32_t>(step), c3, k0, k1);
-      const uint32_t w[4] = {r.x, r.y, r.z, r.w};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float s = __builtin_fmaf(vals[g].get(4 * h + q), invT, gumbel_from_word(w[q]));
-        if (s > best) { best = s; best_v = v0 + 4 * h + q; }
-      }
-    }
-  }
+  for (int g = 0; g < kSampGroups; ++g) any_valid |= valid[g];
+  const bool nonfinite = any_valid && !(isfinite(lmax) && isfinite(Z) && isfinite(A2));
 
   // workgroup merge: max, then rescale (double), then Gumbel best
   __shared__ float s_max[kSampThreads / 64];
@@ -187,12 +183,18 @@ __global__ __launch_bounds__(kSampThreads) void sampler_partial_kernel(
   }
 }
 
-constexpr int kFinishThreads = 256;
+constexpr int kFinishThreads = 1024;
 
+// One workgroup per row.  Merge: 16 lanes per position (lane sl takes
+// splits sl, sl + 16, ...), shuffle reductions in a fixed order.  The
+// entropy-bound ranking sorts (entropy, position) keys with a bitonic sort in
+// LDS (committed positions and the padding up to npow2 take +inf), then each
+// thread walks a contiguous segment of the sorted keys with its exclusive
+// prefix sum (segment sums scanned across the workgroup).
 __global__ __launch_bounds__(kFinishThreads) void sampler_finish_kernel(
-    const SamplerPartial* __restrict__ part, int L, int V, int nsplit, float invT, int step,
-    int ends_at_step, int adaptive, float stop_entropy, float commit_prob, float renoise_prob,
-    int policy, float entropy_bound, uint32_t k0, uint32_t k1,
+    const SamplerPartial* __restrict__ part, int L, int npow2, int V, int nsplit, float invT,
+    int step, int ends_at_step, int adaptive, float stop_entropy, float commit_prob,
+    float renoise_prob, int policy, float entropy_bound, uint32_t k0, uint32_t k1,
     const int32_t* __restrict__ prefix_len,
     int32_t* __restrict__ tokens, uint8_t* __restrict__ committed,
     uint8_t* __restrict__ renoised, float* __restrict__ maxprob, float* __restrict__ entropy,
@@ -202,23 +204,32 @@ __global__ __launch_bounds__(kFinishThreads) void sampler_finish_kernel(
   if (done[b]) return;
   const int tid = threadIdx.x;
   extern __shared__ unsigned char smem_raw[];
-  double* s_mp = reinterpret_cast<double*>(smem_raw);        // [L]
-  double* s_h = s_mp + L;                                    // [L]
-  int32_t* s_sample = reinterpret_cast<int32_t*>(s_h + L);   // [L]
-  uint8_t* s_flag = reinterpret_cast<uint8_t*>(s_sample + L);   // [L] bit 0: uncommitted
-  __shared__ double s_red[kFinishThreads / 64];
-  __shared__ int s_nf[kFinishThreads / 64];
+  double* s_mp = reinterpret_cast<double*>(smem_raw);           // [L]
+  double* s_key = s_mp + L;                                     // [npow2] entropies
+  int32_t* s_sample = reinterpret_cast<int32_t*>(s_key + npow2);   // [L]
+  int32_t* s_idx = s_sample + L;                                // [npow2]
+  uint8_t* s_flag = reinterpret_cast<uint8_t*>(s_idx + npow2);  // [L] bit 0: uncommitted
+  constexpr int kWaves = kFinishThreads / 64;
+  __shared__ double s_red[kWaves];
+  __shared__ int s_nf[kWaves];
 
+  // ---- per-position merge of the slice partials
+  const int sl = tid & 15, grp = tid >> 4;
+  constexpr int kGroups = kFinishThreads / 16;
   double hsum = 0.0;
   int nf = 0;
-  for (int i = tid; i < L; i += kFinishThreads) {
-    const SamplerPartial* p = part + (static_cast<size_t>(b) * L + i) * nsplit;
+  for (int i0 = 0; i0 < L; i0 += kGroups) {
+    const int i = i0 + grp;
+    const bool act = i < L;                      // uniform in the 16-lane group
+    const SamplerPartial* p = part + (static_cast<size_t>(b) * L + (act ? i : 0)) * nsplit;
     float M = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, p[s].lmax);
+    for (int s = sl; s < nsplit; s += 16) M = fmaxf(M, p[s].lmax);
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
     double Z = 0.0, A = 0.0;
     float best = -INFINITY;
     int best_v = 0x7fffffff;
-    for (int s = 0; s < nsplit; ++s) {
+    for (int s = sl; s < nsplit; s += 16) {
       const SamplerPartial q = p[s];
       nf |= q.flags;
       if (q.Z > 0.0) {
@@ -232,15 +243,25 @@ __global__ __launch_bounds__(kFinishThreads) void sampler_finish_kernel(
         best_v = q.best_v;
       }
     }
-    const double mp = 1.0 / Z;
-    const double H = log(Z) - A / Z;
-    s_mp[i] = mp;
-    s_h[i] = H;
-    s_sample[i] = best_v;
-    s_flag[i] = committed[static_cast<size_t>(b) * L + i] ? 0 : 1;
-    maxprob[static_cast<size_t>(b) * L + i] = static_cast<float>(mp);
-    entropy[static_cast<size_t>(b) * L + i] = static_cast<float>(H);
-    hsum += H;
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) {
+      Z += __shfl_xor(Z, o);
+      A += __shfl_xor(A, o);
+      const float ob = __shfl_xor(best, o);
+      const int ov = __shfl_xor(best_v, o);
+      if (ob > best || (ob == best && ov < best_v)) { best = ob; best_v = ov; }
+    }
+    if (act && sl == 0) {
+      const double mp = 1.0 / Z;
+      const double H = log(Z) - A / Z;
+      s_mp[i] = mp;
+      s_key[i] = H;
+      s_sample[i] = best_v;
+      s_flag[i] = committed[static_cast<size_t>(b) * L + i] ? 0 : 1;
+      maxprob[static_cast<size_t>(b) * L + i] = static_cast<float>(mp);
+      entropy[static_cast<size_t>(b) * L + i] = static_cast<float>(H);
+      hsum += H;
+    }
   }
   hsum = warp_sum_d(hsum);
   nf = __any(nf) ? 1 : 0;
@@ -248,39 +269,65 @@ __global__ __launch_bounds__(kFinishThreads) void sampler_finish_kernel(
   __syncthreads();
   double tot = 0.0;
   int anynf = 0;
-  for (int w = 0; w < kFinishThreads / 64; ++w) { tot += s_red[w]; anynf |= s_nf[w]; }
+  for (int w = 0; w < kWaves; ++w) { tot += s_red[w]; anynf |= s_nf[w]; }
   const double hbar = tot / L;
-  // entropy-bound policy: an uncommitted position commits when the
+
+  // ---- entropy-bound policy: an uncommitted position commits when the
   // entropies of the uncommitted positions ranked below it, by (entropy,
-  // position), sum to at most the bound -- the longest ranked prefix whose
-  // sum minus its largest term is within the bound (O(L^2) broadcast reads)
+  // position), sum to at most the bound (the longest ranked prefix whose sum
+  // minus its largest term is within the bound)
   bool all_committed = false;
   if (policy == DG_COMMIT_ENTROPY_BOUND) {
-    // ranking keys: committed positions take +inf and never rank below
-    for (int i = tid; i < L; i += kFinishThreads)
-      if (!(s_flag[i] & 1)) s_h[i] = INFINITY;
+    for (int r = tid; r < npow2; r += kFinishThreads) {
+      if (!(r < L && (s_flag[r] & 1))) s_key[r] = INFINITY;
+      s_idx[r] = r;
+    }
     __syncthreads();
-    int left = 0;                      // uncommitted positions that stay so
-    for (int i = tid; i < L; i += kFinishThreads) {
-      if (!(s_flag[i] & 1)) continue;
-      const double hi = s_h[i];
-      double below[4] = {0.0, 0.0, 0.0, 0.0};   // independent partial sums
-      int j = 0;
-      for (; j + 4 <= L; j += 4) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const double hj = s_h[j + u];
-          below[u] += (hj < hi || (hj == hi && j + u < i)) ? hj : 0.0;
+    for (int k = 2; k <= npow2; k <<= 1) {
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        for (int t = tid; t < npow2; t += kFinishThreads) {
+          const int u = t ^ j;
+          if (u > t) {
+            const double ka = s_key[t], kb = s_key[u];
+            const int ia = s_idx[t], ib = s_idx[u];
+            const bool a_after = ka > kb || (ka == kb && ia > ib);
+            if (a_after == ((t & k) == 0)) {       // ascending runs where (t & k) == 0
+              s_key[t] = kb; s_key[u] = ka;
+              s_idx[t] = ib; s_idx[u] = ia;
+            }
+          }
         }
+        __syncthreads();
       }
-      for (; j < L; ++j) {
-        const double hj = s_h[j];
-        below[0] += (hj < hi || (hj == hi && j < i)) ? hj : 0.0;
-      }
-      if ((below[0] + below[1]) + (below[2] + below[3]) <= static_cast<double>(entropy_bound))
-        s_flag[i] |= 2;
-      else
-        left = 1;
+    }
+    // exclusive prefix sums of the sorted finite keys: thread segments of
+    // seg keys, segment totals scanned through the waves
+    const int seg = (npow2 + kFinishThreads - 1) / kFinishThreads;
+    const int r0 = min(tid * seg, npow2), r1 = min(r0 + seg, npow2);
+    double part_sum = 0.0;
+    for (int r = r0; r < r1; ++r) {
+      const double kv = s_key[r];
+      if (kv < INFINITY) part_sum += kv;
+    }
+    const int lane = tid & 63, wv = tid >> 6;
+    double incl = part_sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const double t2 = __shfl_up(incl, o);
+      if (lane >= o) incl += t2;
+    }
+    __syncthreads();                     // s_red reused for the wave totals
+    if (lane == 63) s_red[wv] = incl;
+    __syncthreads();
+    double run = incl - part_sum;
+    for (int w = 0; w < wv; ++w) run += s_red[w];
+    int left = 0;                        // uncommitted positions that stay so
+    for (int r = r0; r < r1; ++r) {
+      const double kv = s_key[r];
+      if (!(kv < INFINITY)) continue;
+      if (run <= static_cast<double>(entropy_bound)) s_flag[s_idx[r]] |= 2;
+      else left = 1;
+      run += kv;
     }
     all_committed = __syncthreads_or(left) == 0;
   }
@@ -293,6 +340,7 @@ __global__ __launch_bounds__(kFinishThreads) void sampler_finish_kernel(
     if (steps_taken) steps_taken[b] += 1;
     if (anynf && status) atomicOr(status, DG_STATUS_NONFINITE_LOGITS);
   }
+  __syncthreads();                       // s_flag complete before the update
   const uint32_t c3r = (kStreamRenoise << 24) | static_cast<uint32_t>(b);
   for (int i = tid; i < L; i += kFinishThreads) {
     const size_t o = static_cast<size_t>(b) * L + i;
@@ -344,15 +392,18 @@ dg_status launch_sampler(const void* logits, int logit_dtype, int B, int L, int 
   DG_LAUNCH_CHECK();
   const int adaptive = cfg.fixed_steps > 0 ? 0 : 1;
   const int ends_at = cfg.fixed_steps > 0 ? cfg.fixed_steps - 1 : S - 1;
-  const size_t smem = static_cast<size_t>(L) * (2 * sizeof(double) + sizeof(int32_t) + 1);
-  static bool smem_set = false;        // up to 4096 positions: 86 KB of LDS
+  int npow2 = 1;
+  while (npow2 < L) npow2 <<= 1;
+  const size_t smem = static_cast<size_t>(L) * (sizeof(double) + sizeof(int32_t) + 1) +
+                      static_cast<size_t>(npow2) * (sizeof(double) + sizeof(int32_t));
+  static bool smem_set = false;        // up to 4096 positions: 100 KB of LDS
   if (!smem_set) {
     DG_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(sampler_finish_kernel),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, 4096 * 21));
+                               hipFuncAttributeMaxDynamicSharedMemorySize, 4096 * 25));
     smem_set = true;
   }
   sampler_finish_kernel<<<B, kFinishThreads, smem, stream>>>(
-      part, L, V, nsplit, invT, step, ends_at, adaptive, cfg.stop_entropy, cfg.commit_prob,
+      part, L, npow2, V, nsplit, invT, step, ends_at, adaptive, cfg.stop_entropy, cfg.commit_prob,
       cfg.renoise_prob, cfg.commit_policy, cfg.entropy_bound, k0, k1, prefix_len, tokens,
       committed, renoised, maxprob, entropy, mean_entropy, done, status, steps_taken);
   DG_LAUNCH_CHECK();
