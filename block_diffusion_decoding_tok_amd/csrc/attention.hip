@@ -335,14 +335,17 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(
     l_run[qb] += __shfl_xor(l_run[qb], 32);
   }
   __syncthreads();                       // every wave is done with the tiles
-  float* s_o = reinterpret_cast<float*>(smem) + rg * (32 * kDh + 64);
-  float* s_ml = s_o + 32 * kDh;
+  // rows padded by 4 floats: the 16 rows a 16-lane group touches start on
+  // different banks
+  constexpr int kOStride = kDh + 4;
+  float* s_o = reinterpret_cast<float*>(smem) + rg * (32 * kOStride + 64);
+  float* s_ml = s_o + 32 * kOStride;
   if (kh == 1) {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
 #pragma unroll
       for (int d = 0; d < 8; ++d)
-        *reinterpret_cast<f32x4_t*>(&s_o[(qb * 16 + l16) * kDh + d * 16 + g4 * 4]) = acc_o[qb][d];
+        *reinterpret_cast<f32x4_t*>(&s_o[(qb * 16 + l16) * kOStride + d * 16 + g4 * 4]) = acc_o[qb][d];
       if (g4 == 0) {
         s_ml[(qb * 16 + l16) * 2 + 0] = m_run[qb];
         s_ml[(qb * 16 + l16) * 2 + 1] = l_run[qb];
@@ -364,7 +367,7 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(
     float* dst = o_part + prow * kDh;
 #pragma unroll
     for (int d = 0; d < 8; ++d) {
-      const f32x4_t o1 = *reinterpret_cast<const f32x4_t*>(&s_o[(qb * 16 + l16) * kDh + d * 16 + g4 * 4]);
+      const f32x4_t o1 = *reinterpret_cast<const f32x4_t*>(&s_o[(qb * 16 + l16) * kOStride + d * 16 + g4 * 4]);
       *reinterpret_cast<float4*>(dst + d * 16 + g4 * 4) =
           make_float4(acc_o[qb][d][0] * f0 + o1[0] * f1, acc_o[qb][d][1] * f0 + o1[1] * f1,
                       acc_o[qb][d][2] * f0 + o1[2] * f1, acc_o[qb][d][3] * f0 + o1[3] * f1);
@@ -374,7 +377,7 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(
 }
 
 constexpr size_t kAttnSmemBytes = (2 * kKTileElems + 2 * kVTileElems) * sizeof(bf16_t);
-static_assert(4 * (32 * kDh + 64) * sizeof(float) <= kAttnSmemBytes, "merge scratch fits");
+static_assert(4 * (32 * (kDh + 4) + 64) * sizeof(float) <= kAttnSmemBytes, "merge scratch fits");
 
 // Merge the KV splits of every packed row and write out [B, Lq, Hq, dh]:
 // 32 threads per row (4 dh each, 16-byte loads), 8 rows per workgroup.
