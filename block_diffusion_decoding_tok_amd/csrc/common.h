@@ -72,6 +72,25 @@ __device__ __forceinline__ double warp_sum_d(double v) {
   return v;
 }
 
+// All-reduce over each 16-lane row of (value, index) pairs: the largest
+// value, the lowest index among equals, in every lane of the row.  Four DPP
+// moves (xor 1 and xor 2 inside quads, then the 8-lane and 16-lane mirrors)
+// instead of LDS-routed shuffles.
+template <int CTRL>
+__device__ __forceinline__ void dpp_max_step(float& v, int& id) {
+  const float ov = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+  const int oi = __builtin_amdgcn_mov_dpp(id, CTRL, 0xF, 0xF, false);
+  const bool take = (ov > v) | ((ov == v) & (oi < id));
+  v = take ? ov : v;
+  id = take ? oi : id;
+}
+__device__ __forceinline__ void row16_max_lowid(float& v, int& id) {
+  dpp_max_step<0xB1>(v, id);    // quad_perm [1, 0, 3, 2]
+  dpp_max_step<0x4E>(v, id);    // quad_perm [2, 3, 0, 1]
+  dpp_max_step<0x141>(v, id);   // row_half_mirror
+  dpp_max_step<0x140>(v, id);   // row_mirror
+}
+
 // RoPE: the angle pos * theta^(-2j/dh) of pair j, reduced to [-pi, pi] in
 // double, then evaluated in float.
 // Frequency of pair j: theta^(-2 j / dh), in double.

@@ -25,7 +25,7 @@ namespace dg {
 // ------------------------------------------------------------------ router
 // Top-k of one token by a 16-lane group: sub-lane sl holds experts sl,
 // sl + 16, ... (E <= 256); each of the k rounds takes the group-wide
-// (logit desc, id asc) maximum of the experts not yet taken (4 xor-shuffle
+// (logit desc, id asc) maximum of the experts not yet taken (four DPP
 // steps).  Lane j < k of the group writes slot j: its id and its gate, the
 // softmax of the k selected logits (sum in slot order).
 __device__ __forceinline__ void route_topk_group(const float* row, int t, int E, int k, int sl,
@@ -53,12 +53,7 @@ __device__ __forceinline__ void route_topk_group(const float* row, int t, int E,
       best = better ? v[q] : best;
       bid = better ? e : bid;
     }
-#pragma unroll
-    for (int o = 8; o > 0; o >>= 1) {
-      const float ob = __shfl_xor(best, o);
-      const int oi = __shfl_xor(bid, o);
-      if (ob > best || (ob == best && oi < bid)) { best = ob; bid = oi; }
-    }
+    row16_max_lowid(best, bid);
     if ((bid & 15) == sl) taken |= 1u << (bid >> 4);
     if (j == 0) best0 = best;
     z += expf(best - best0);
