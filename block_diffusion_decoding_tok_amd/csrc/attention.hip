@@ -391,19 +391,12 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
   const int d4 = (threadIdx.x & 31) * 4;
   if (gr >= BH * rows_total) return;
   const int bh = gr / rows_total, r = gr % rows_total;
-  // splits in batches of 8: the batch's loads are issued together (clamped
-  // indices, masked afterwards), then merged in split order
+  // splits in batches of 8: a batch's (m, l) and O loads are issued together
+  // (clamped indices, masked afterwards), then merged in split order with an
+  // online rescale when a batch raises the running maximum (one pass)
   const int64_t rstride = static_cast<int64_t>(BH) * rows_total;
   const int64_t r0 = static_cast<int64_t>(bh) * rows_total + r;
   float M = -INFINITY;
-  for (int s0 = 0; s0 < nsplit; s0 += 8) {
-    float mv[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) mv[j] = ml_part[min(s0 + j, nsplit - 1) * rstride + r0].m;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) M = fmaxf(M, mv[j]);       // clamped repeats change nothing
-  }
-  const float base = (M == -INFINITY) ? 0.f : M;
   float L = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int s0 = 0; s0 < nsplit; s0 += 8) {
@@ -415,10 +408,20 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
       ml[j] = ml_part[prow];
       o[j] = *reinterpret_cast<const float4*>(o_part + prow * kDh + d4);
     }
+    float mb = M;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (s0 + j < nsplit && ml[j].l != 0.f) mb = fmaxf(mb, ml[j].m);
+    if (mb > M) {                     // raise the base: rescale what is summed so far
+      const float f = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(M - mb);
+      L *= f;
+      acc.x *= f; acc.y *= f; acc.z *= f; acc.w *= f;
+      M = mb;
+    }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       if (s0 + j >= nsplit || ml[j].l == 0.f) continue;
-      const float f = __builtin_amdgcn_exp2f(ml[j].m - base);
+      const float f = __builtin_amdgcn_exp2f(ml[j].m - M);
       L += ml[j].l * f;
       acc.x += o[j].x * f;
       acc.y += o[j].y * f;

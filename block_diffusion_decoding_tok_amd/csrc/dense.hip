@@ -15,8 +15,8 @@ namespace dg {
 
 // projection-sized outputs (QKV, O, router): split-K register streaming,
 // ring of kSplitNR chunks; wide outputs: 16 kProjRT rows x 16 kProjTB tokens
-// per workgroup, K split over kProjNW waves; narrow outputs (router): 32 rows
-// x 16 tokens, K split over eight waves
+// per workgroup, K split over kProjNW waves; narrow outputs: 16 rows (router)
+// or 32 rows (a handful of tokens) x 16 tokens, K split over eight waves
 constexpr int kSplitNR = 2;
 constexpr int kProjRT = 8, kProjTB = 2, kProjNW = 4, kProjWPE = 2;
 // other shapes: 64 rows x 64 tokens per workgroup, LDS-staged tokens
@@ -355,12 +355,16 @@ static void launch_gemm_bf16(GemmArgs& g, int M, int N, int K, hipStream_t strea
         <<<(g.n_tiles_total + 7) / 8 * 8, 256, 0, stream>>>(g);
   } else if (K % 64 == 0 && K >= 64 * 8 && N % (16 * kProjRT) == 0 && N % 32 == 0) {
     // narrow outputs, or a handful of tokens (AR decode): more, smaller tiles
+    // (router outputs: 16-row tiles; a few tokens: 32-row tiles)
     const bool narrow = N < 1024 || M <= 16;
-    g.n_tiles_x = narrow ? N / 32 : N / (16 * kProjRT);
+    const int narrow_rows = N < 1024 ? 16 : 32;
+    g.n_tiles_x = narrow ? N / narrow_rows : N / (16 * kProjRT);
     g.n_tiles_y = narrow ? (M + 15) / 16 : (M + 16 * kProjTB - 1) / (16 * kProjTB);
     g.n_tiles_total = g.n_tiles_x * g.n_tiles_y;
     const unsigned grid = (g.n_tiles_total + 7) / 8 * 8;
-    if (narrow)
+    if (narrow && narrow_rows == 16)
+      gemm_splitk_kernel<1, 1, kSplitNR, 8, TILED><<<grid, 512, 0, stream>>>(g);
+    else if (narrow)
       gemm_splitk_kernel<2, 1, kSplitNR, 8, TILED><<<grid, 512, 0, stream>>>(g);
     else
       gemm_splitk_kernel<kProjRT, kProjTB, kSplitNR, kProjNW, TILED, kProjWPE>
