@@ -238,7 +238,7 @@ size_t moe_ffn_workspace_bytes(int T, int D, int I, int E, int k, int x_dtype) {
 // one-wave kernels: register ring depth (chunks of 64 k) and weight tiles of
 // 16 rows per item; token tiles of 16 tokens, or of 32 for gate/up when the
 // experts average 20 to 40 tokens (fewer items re-streaming the same rows)
-constexpr int kMoeNR = 2, kMoeWPE = 3, kDownWPE = 3;
+constexpr int kMoeNR = 2, kMoeWPE = 3, kDownNR = 2, kDownWPE = 3;
 constexpr int kGateRT = 8, kDownRT = 8;
 constexpr int kGateTB1Slots = 20;   // gate/up: 16-token tiles up to this many slots per expert
 constexpr int kTinySlots = 64;      // up to this many slots in all: half-size items
@@ -270,7 +270,7 @@ static void launch_wave(GemmArgs& g, int T, int k, int E, hipStream_t stream) {
   else if constexpr (WF == kWBf16)
     gemm_wave_kernel<RT, TB, kMoeNR, WF, MODE, TILED, (TB == 1 ? 2 : 1)><<<grid, 64, 0, stream>>>(g);
   else
-    gemm_wave_kernel<RT, TB, kMoeNR, WF, MODE, TILED,
+    gemm_wave_kernel<RT, TB, (MODE == kDown ? kDownNR : kMoeNR), WF, MODE, TILED,
                      (TB == 1 ? (MODE == kDown ? kDownWPE : kMoeWPE) : 1)><<<grid, 64, 0, stream>>>(g);
 }
 
