@@ -254,7 +254,11 @@ constexpr int item_tiles() {
                      : (MODE == kGateUp ? kGateRT : kDownRT);
 }
 
-template <int TB, int WF, int MODE, bool TILED, int RT = item_tiles<WF, MODE>()>
+// a handful of tokens (AR decode): few items, so each wave keeps a deeper ring
+// of fewer weight tiles in flight
+constexpr int kTinyRT = 2, kTinyNR = 4;
+
+template <int TB, int WF, int MODE, bool TILED, int RT = item_tiles<WF, MODE>(), int NRT = 0>
 static void launch_wave(GemmArgs& g, int T, int k, int E, hipStream_t stream) {
   // grid: an upper bound of the tile count (E + slots / tile size) times the
   // weight row groups; the kernel deals the live items out itself
@@ -265,7 +269,9 @@ static void launch_wave(GemmArgs& g, int T, int k, int E, hipStream_t stream) {
   const unsigned grid = static_cast<unsigned>((g.n_tiles_total + 7) / 8 * 8);
   // bf16 chunks are twice the registers of fp8: two waves per SIMD (three
   // would spill the ring)
-  if constexpr (WF == kWMx4)
+  if constexpr (NRT > 0)
+    gemm_wave_kernel<RT, TB, NRT, WF, MODE, TILED, 1><<<grid, 64, 0, stream>>>(g);
+  else if constexpr (WF == kWMx4)
     gemm_wave_kernel<RT, TB, kMx4NR, WF, MODE, TILED, (TB == 1 ? kMx4WPE : 1)><<<grid, 64, 0, stream>>>(g);
   else if constexpr (WF == kWBf16)
     gemm_wave_kernel<RT, TB, kMoeNR, WF, MODE, TILED, (TB == 1 ? 2 : 1)><<<grid, 64, 0, stream>>>(g);
@@ -299,7 +305,7 @@ static void launch_gate_up_mfma(const void* x, const void* wgu, const float* sgu
   const int64_t slots = static_cast<int64_t>(T) * k;
   if (slots <= kTinySlots) {
     // a few tokens (AR decode): half-size items, twice as many waves
-    launch_wave<1, WF, kGateUp, TILED, item_tiles<WF, kGateUp>() / 2>(g, T, k, E, stream);
+    launch_wave<1, WF, kGateUp, TILED, kTinyRT, kTinyNR>(g, T, k, E, stream);
   } else if (slots <= kGateTB1Slots * static_cast<int64_t>(E)) {
     launch_wave<1, WF, kGateUp, TILED>(g, T, k, E, stream);
   } else if (slots <= 40ll * E || WF == kWMx4) {
@@ -328,7 +334,7 @@ static void launch_down_mfma(const bf16_t* h, const void* wd, const float* sd, c
   d.out = y_slot;
   const int64_t slots = static_cast<int64_t>(T) * k;
   if (slots <= kTinySlots) {
-    launch_wave<1, WF, kDown, TILED, item_tiles<WF, kDown>() / 2>(d, T, k, E, stream);
+    launch_wave<1, WF, kDown, TILED, kTinyRT, kTinyNR>(d, T, k, E, stream);
   } else if (slots <= 40ll * E) {
     launch_wave<1, WF, kDown, TILED>(d, T, k, E, stream);
   } else if constexpr (WF == kWMx4) {
