@@ -166,3 +166,21 @@ def test_generate_and_policy_reject_bad_calls(lib):
     assert lib.dg_sampler_step(*args) == -1
     assert lib.dg_generate(None, C.byref(dg.sampler_cfg()), 1, None, None, 64, f, 1, 2,
                            f, f, f, None) == -1
+
+
+def test_zero_and_degenerate_sizes_rejected(lib):
+    f = C.c_void_p(256)
+    cfg = dg.sampler_cfg()
+    # no tokens / no rows / no positions
+    assert lib.dg_moe_route(f, 0, 128, 8, f, f, f, f, f, 1 << 20, None) == -2
+    assert lib.dg_moe_ffn(f, dg.DG_BF16, f, f, dg.DG_BF16, 0, None, None, f, f, f, f,
+                          0, 2816, 704, 128, 8, f, f, 1 << 30, None) == -2
+    args = [f, dg.DG_BF16, 0, 256, 262144, 0, C.byref(cfg)] + [f] * 9 + [f, 1 << 30, None]
+    assert lib.dg_sampler_step(*args) == -2
+    args[2], args[3] = 1, 0
+    assert lib.dg_sampler_step(*args) == -2
+    args[3] = 4097                       # above the largest canvas
+    assert lib.dg_sampler_step(*args) == -2
+    # empty quantize / fill calls are no-ops
+    assert lib.dg_quantize_mxfp4(None, None, None, 0, 32, None) == 0
+    assert lib.dg_quantize_fp8_rows(None, None, None, 0, 16, None) == 0

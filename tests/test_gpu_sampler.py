@@ -218,3 +218,18 @@ def test_sampler_entropy_bound_all_committed_ends_block():
     h = st.host()
     assert h["committed"][0].all() and list(h["done"]) == [1, 0]
     assert h["committed"][1].sum() == 1          # flat row: exactly one commit
+
+
+@pytest.mark.parametrize("L", [300, 4096])
+def test_sampler_entropy_bound_long_and_ragged_canvas(L):
+    """The ranking's bitonic sort over a padded power of two (300 -> 512) and
+    at the largest canvas (4096 positions, 100 KB of LDS); small vocabulary so
+    the oracle stays quick; bounds that select many positions per step."""
+    B, V = 2, 512
+    case = sampler_case(B=B, L=L, V=V, seed=L, dtype=torch.float32, peak=9.0)
+    ocfg, gcfg = _cfg_pair(canvas_len=L, max_steps=8, seed=3, commit_policy=1,
+                           entropy_bound=2.0)
+    x64 = case.logits.to(torch.float64).numpy()
+    st, _ = _run_and_compare(case.logits.to(DEV), x64, ocfg, gcfg, [0, 5, 7], [0, 17])
+    h = st.host()
+    assert h["committed"].sum() > 3 * B
