@@ -379,13 +379,14 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(
 constexpr size_t kAttnSmemBytes = (2 * kKTileElems + 2 * kVTileElems) * sizeof(bf16_t);
 static_assert(4 * (32 * (kDh + 4) + 64) * sizeof(float) <= kAttnSmemBytes, "merge scratch fits");
 
-// Merge the KV splits of every packed row and write out [B, Lq, Hq, dh]:
+// Merge the KV splits of every packed row and write out [B, Lq, Hq, dh]
+// (row-major, or with tiled the tiled activation layout of [B Lq, Hq dh]):
 // 32 threads per row (4 dh each, 16-byte loads), 8 rows per workgroup.
 template <typename T>
 __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ o_part,
                                                            const AttnPartialML* __restrict__ ml_part,
                                                            int nsplit, int BH, int rows_total,
-                                                           int G, int Hkv, int Lq,
+                                                           int G, int Hkv, int Lq, int tiled,
                                                            T* __restrict__ out) {
   const int gr = blockIdx.x * 8 + (threadIdx.x >> 5);      // global packed row index
   const int d4 = (threadIdx.x & 31) * 4;
@@ -432,7 +433,8 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
   const int b = bh / Hkv, g = bh % Hkv;
   const int tok = r / G, h = g * G + r % G;
   const int Hq = Hkv * G;
-  T* dst = out + ((static_cast<int64_t>(b) * Lq + tok) * Hq + h) * kDh + d4;
+  const int64_t m = static_cast<int64_t>(b) * Lq + tok;
+  T* dst = tiled ? out + xtile_offset(m, h * kDh + d4, Hq * kDh) : out + (m * Hq + h) * kDh + d4;
   Elem<T>::store(dst, 0, acc.x / L);
   Elem<T>::store(dst, 1, acc.y / L);
   Elem<T>::store(dst, 2, acc.z / L);
@@ -543,7 +545,8 @@ dg_status launch_attention(const AttnArgs& a, void* ws, hipStream_t stream) {
         p.tiles, p.nsplit, a.B * a.Hkv, a.mask_mode == DG_MASK_CAUSAL, o_part, ml);
     DG_LAUNCH_CHECK();
     attn_combine_kernel<bf16_t><<<(a.B * a.Hkv * rows + 7) / 8, 256, 0, stream>>>(
-        o_part, ml, p.nsplit, a.B * a.Hkv, rows, G, a.Hkv, a.Lq, static_cast<bf16_t*>(a.out));
+        o_part, ml, p.nsplit, a.B * a.Hkv, rows, G, a.Hkv, a.Lq, a.out_tiled,
+        static_cast<bf16_t*>(a.out));
     DG_LAUNCH_CHECK();
   } else {
     rope_kernel<float><<<a.B * a.Lq, rope_threads(a.dh), 0, stream>>>(

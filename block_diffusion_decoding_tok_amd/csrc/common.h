@@ -27,6 +27,19 @@ dg_status fail(dg_status st, const std::string& msg);
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// The tiled activation layout of a bf16 matrix [M, K] (K % 64 == 0) that the
+// dense projections can read: one 2 KB block per 16 tokens x 64 k, blocks in
+// (token block, k block) order, and inside a block the operand lane order of
+// the 16x16x32 MFMA: element (m, k) at (k / 8 % 2) * 512 + ((k / 16 % 4) * 16
+// + m % 16) * 8 + k % 8.  Four consecutive k from a multiple of 4 stay
+// contiguous.  Storage: ceil(M / 16) * 16 * K elements; rows past M in the
+// last block are never written and never used.
+__host__ __device__ inline int64_t xtile_offset(int64_t m, int k, int K) {
+  const int kk = k & 63;
+  return ((m >> 4) * (K >> 6) + (k >> 6)) * 1024 + ((kk >> 3) & 1) * 512 +
+         ((kk >> 4) * 16 + (m & 15)) * 8 + (kk & 7);
+}
+
 // ------------------------------------------------------------ bf16 helpers
 typedef uint16_t bf16_t;   // raw bits
 

@@ -1,8 +1,9 @@
 // Dense projections (QKV, O, router, LM head), RMSNorm and the embedding
 // gather of the decoder layer.
 //
-//   bf16: projections -- gemm_splitk_kernel (gemm_mfma.h), 64 weight rows x
-//         64 (or 16) tokens per workgroup, K split over its four waves;
+//   bf16: projections -- gemm_splitk_kernel (gemm_mfma.h), 128 weight rows x
+//         32 tokens per workgroup (64 x 64 with tiled activations), K split
+//         over its four waves;
 //         LM head with tile-packed weights -- gemm_wide_kernel below;
 //         other shapes -- gemm_stream_kernel in dense mode.
 //   f32:  plain SIMT kernels (parity path of the tiny fp32 model).
@@ -19,6 +20,10 @@ namespace dg {
 // or 32 rows (a handful of tokens) x 16 tokens, K split over eight waves
 constexpr int kSplitNR = 2;
 constexpr int kProjRT = 8, kProjTB = 2, kProjNW = 4, kProjWPE = 2;
+// tiled activations: 64 rows x 64 tokens per workgroup (the least bytes per
+// compute unit for these shapes: 720 KB against 900 KB at 256 tokens; QKV
+// 14.4 -> 12.7 us, O 11.0 -> 9.3 us measured)
+constexpr int kXtRT = 4, kXtTB = 4;
 // other shapes: 64 rows x 64 tokens per workgroup, LDS-staged tokens
 constexpr int kDenseRT = 1, kDenseTB = 4, kDenseKS = 2, kDensePF = 2;
 // up to 256 tokens: register streaming, 16 tokens per tile, ring of 4 chunks
@@ -291,13 +296,24 @@ dg_status launch_gemm(const void* A, const void* W, void* C, int M, int N, int K
   return DG_OK;
 }
 
+bool qkv_rope_supported(const QkvRope& r, int K) {
+  const int M = r.B * r.Lq;
+  const int N = (r.Hq + 2 * r.Hkv) * r.dh;
+  // the wide split-K tiles: 16 kProjRT = 128 rows = one head of 128 (tiled
+  // activations: 64-row tiles, half a head's rotated pairs each)
+  return r.dh == 128 && kProjRT == 8 && kXtRT == 4 && M > 16 && N >= 1024 && K % 64 == 0 &&
+         K >= 64 * 8 && r.Hq % r.Hkv == 0;
+}
+
+bool dense_xt_supported(int M, int N, int K) {
+  return M > 16 && N % (16 * kXtRT) == 0 && K % 64 == 0 && K >= 64 * 8;
+}
+
 dg_status launch_qkv_rope(const void* A, const void* W, int K, int w_layout, const QkvRope& r,
                           hipStream_t stream) {
   const int M = r.B * r.Lq;
   const int N = (r.Hq + 2 * r.Hkv) * r.dh;
-  // the wide split-K tiles: 16 kProjRT = 128 rows = one head of 128
-  if (!(r.dh == 128 && kProjRT == 8 && M > 16 && N >= 1024 && K % 64 == 0 && K >= 64 * 8 &&
-        r.Hq % r.Hkv == 0))
+  if (!qkv_rope_supported(r, K) || (r.x_tiled && w_layout != DG_LAYOUT_TILED))
     return DG_ERR_UNSUPPORTED;
   GemmArgs g{};
   g.W = W; g.X = static_cast<const bf16_t*>(A);
@@ -312,16 +328,42 @@ dg_status launch_qkv_rope(const void* A, const void* W, int K, int w_layout, con
   g.q_out = static_cast<bf16_t*>(r.q_out);
   g.k_cache = static_cast<bf16_t*>(r.k_cache);
   g.v_cache = static_cast<bf16_t*>(r.v_cache);
-  g.n_tiles_x = N / (16 * kProjRT);
-  g.n_tiles_y = (M + 16 * kProjTB - 1) / (16 * kProjTB);
+  g.x_tiled = r.x_tiled;
+  const int rt = r.x_tiled ? kXtRT : kProjRT, tb = r.x_tiled ? kXtTB : kProjTB;
+  g.n_tiles_x = N / (16 * rt);
+  g.n_tiles_y = (M + 16 * tb - 1) / (16 * tb);
   g.n_tiles_total = g.n_tiles_x * g.n_tiles_y;
   const unsigned grid = (g.n_tiles_total + 7) / 8 * 8;
-  if (w_layout == DG_LAYOUT_TILED)
+  if (r.x_tiled)
+    gemm_splitk_kernel<kXtRT, kXtTB, kSplitNR, kProjNW, true, kProjWPE>
+        <<<grid, 64 * kProjNW, 0, stream>>>(g);
+  else if (w_layout == DG_LAYOUT_TILED)
     gemm_splitk_kernel<kProjRT, kProjTB, kSplitNR, kProjNW, true, kProjWPE>
         <<<grid, 64 * kProjNW, 0, stream>>>(g);
   else
     gemm_splitk_kernel<kProjRT, kProjTB, kSplitNR, kProjNW, false, kProjWPE>
         <<<grid, 64 * kProjNW, 0, stream>>>(g);
+  DG_LAUNCH_CHECK();
+  return DG_OK;
+}
+
+dg_status launch_gemm_xt(const void* A, const void* W, void* C, int M, int N, int K,
+                         int out_dtype, GemmEpilogue ep, hipStream_t stream) {
+  if (!dense_xt_supported(M, N, K) || (out_dtype != DG_BF16 && out_dtype != DG_F32) ||
+      (ep == kAccumulateF32 && out_dtype != DG_F32))
+    return DG_ERR_UNSUPPORTED;
+  GemmArgs g{};
+  g.W = W; g.X = static_cast<const bf16_t*>(A); g.out = C;
+  g.N = N; g.K = K; g.M = M; g.n_groups = 1;
+  g.out_dtype = out_dtype;
+  g.accumulate = ep == kAccumulateF32;
+  g.y_fastest = 1;
+  g.x_tiled = 1;
+  g.n_tiles_x = N / (16 * kXtRT);
+  g.n_tiles_y = (M + 16 * kXtTB - 1) / (16 * kXtTB);
+  g.n_tiles_total = g.n_tiles_x * g.n_tiles_y;
+  gemm_splitk_kernel<kXtRT, kXtTB, kSplitNR, kProjNW, true, kProjWPE>
+      <<<(g.n_tiles_total + 7) / 8 * 8, 64 * kProjNW, 0, stream>>>(g);
   DG_LAUNCH_CHECK();
   return DG_OK;
 }
@@ -407,7 +449,7 @@ template <> struct Slot4<float> {
 template <typename TS, typename TO>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const TS* __restrict__ y_slot, int k,
                                                       float* __restrict__ x,
-                                                      TO* __restrict__ out, int D) {
+                                                      TO* __restrict__ out, int D, int tiled) {
   const int row = blockIdx.x;
   float4* xr = reinterpret_cast<float4*>(x + static_cast<int64_t>(row) * D);
   const int n4 = D / 4;
@@ -466,7 +508,8 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const TS* __restrict__ y_s
       uint2 pk;
       pk.x = pack_bf16x2(v[i].x * inv, v[i].y * inv);
       pk.y = pack_bf16x2(v[i].z * inv, v[i].w * inv);
-      *reinterpret_cast<uint2*>(o + 4 * p) = pk;
+      TO* dst = tiled ? out + xtile_offset(row, 4 * p, D) : o + 4 * p;
+      *reinterpret_cast<uint2*>(dst) = pk;
     } else {
       *reinterpret_cast<float4*>(o + 4 * p) =
           make_float4(v[i].x * inv, v[i].y * inv, v[i].z * inv, v[i].w * inv);
@@ -499,8 +542,10 @@ dg_status launch_rmsnorm(const float* x, void* out, int M, int D, int out_dtype,
 }
 
 dg_status launch_combine_rmsnorm(const void* y_slot, int slot_dtype, int k, float* x, void* out,
-                                 int M, int D, int out_dtype, hipStream_t stream) {
+                                 int M, int D, int out_dtype, hipStream_t stream, bool out_tiled) {
   const bool regs = D % 4 == 0 && D / 4 <= kNormPieces * 256;
+  if (out_tiled && !(regs && D % 64 == 0 && out_dtype == DG_BF16)) return DG_ERR_UNSUPPORTED;
+  const int tl = out_tiled ? 1 : 0;
   if (!regs) {
     dg_status st;
     if (y_slot && (st = launch_moe_combine(y_slot, slot_dtype, M, D, k, x, stream))) return st;
@@ -515,11 +560,11 @@ dg_status launch_combine_rmsnorm(const void* y_slot, int slot_dtype, int k, floa
   const bf16_t* yb = bf ? static_cast<const bf16_t*>(y_slot) : nullptr;
   const float* yf = bf ? nullptr : static_cast<const float*>(y_slot);
   if (out_dtype == DG_BF16) {
-    if (bf) rmsnorm_kernel<bf16_t, bf16_t><<<M, 256, 0, stream>>>(yb, k, x, static_cast<bf16_t*>(out), D);
-    else rmsnorm_kernel<float, bf16_t><<<M, 256, 0, stream>>>(yf, k, x, static_cast<bf16_t*>(out), D);
+    if (bf) rmsnorm_kernel<bf16_t, bf16_t><<<M, 256, 0, stream>>>(yb, k, x, static_cast<bf16_t*>(out), D, tl);
+    else rmsnorm_kernel<float, bf16_t><<<M, 256, 0, stream>>>(yf, k, x, static_cast<bf16_t*>(out), D, tl);
   } else {
-    if (bf) rmsnorm_kernel<bf16_t, float><<<M, 256, 0, stream>>>(yb, k, x, static_cast<float*>(out), D);
-    else rmsnorm_kernel<float, float><<<M, 256, 0, stream>>>(yf, k, x, static_cast<float*>(out), D);
+    if (bf) rmsnorm_kernel<bf16_t, float><<<M, 256, 0, stream>>>(yb, k, x, static_cast<float*>(out), D, 0);
+    else rmsnorm_kernel<float, float><<<M, 256, 0, stream>>>(yf, k, x, static_cast<float*>(out), D, 0);
   }
   DG_LAUNCH_CHECK();
   return DG_OK;

@@ -60,9 +60,12 @@ struct GemmArgs {
   int n_tiles_y;            // token-tile slots
   int n_tiles_total;        // logical workgroups (x * y)
   int y_fastest;            // dense: logical order with token tiles of the same rows adjacent
-  // dense QKV projection with the RoPE epilogue (gemm_splitk_kernel, 128-row
-  // tiles = one head of 128): out is unused; q (rotated, scaled by q_scale)
-  // goes to the packed attention layout, k (rotated) and v to the caches
+  int x_tiled;              // dense: X in the tiled activation layout (xtile_offset)
+  // dense QKV projection with the RoPE epilogue (gemm_splitk_kernel; a
+  // 128-row tile is one head of 128, a 64-row tile the row pairs (d, d + 64)
+  // of d in [0, 32) or [32, 64) of one head): out is unused; q (rotated,
+  // scaled by q_scale) goes to the packed attention layout, k (rotated) and v
+  // to the caches
   int rope;
   const int32_t* prefix_len;
   int Lq, Hq, Hkv, Tmax;
@@ -649,7 +652,8 @@ __global__ __launch_bounds__(64 * NW, WPE) void gemm_splitk_kernel(GemmArgs a) {
   const int l16 = lane & 15, g4 = lane >> 4;
   const int logical = xcd_logical_tile(blockIdx.x, gridDim.x);
   if (logical >= a.n_tiles_total) return;
-  if (RT == 8 && a.rope && tid < 64) s_inv[tid] = rope_inv_freq(tid, 128, a.theta);
+  constexpr bool kRopeTile = RT == 8 || RT == 4;
+  if (kRopeTile && a.rope && tid < 64) s_inv[tid] = rope_inv_freq(tid, 128, a.theta);
   const int tx = logical / a.n_tiles_y;       // row tile (token tiles adjacent)
   const int ty = logical % a.n_tiles_y;
   const int m0 = ty * 16 * TB;
@@ -657,23 +661,39 @@ __global__ __launch_bounds__(64 * NW, WPE) void gemm_splitk_kernel(GemmArgs a) {
   const int nch_all = a.K / 64;
   const int c_begin = wave * nch_all / NW;
   const int nchunks = (wave + 1) * nch_all / NW - c_begin;   // >= 1 when K >= 64 * NW
+  // 16-row tile of the weights behind accumulator row tile rt: consecutive,
+  // except 64-row RoPE tiles, which take row tiles {0, 1, 4, 5} or {2, 3, 6, 7}
+  // of head tx / 2 so that both rows of every rotated pair are here
+  auto row16 = [&](int rt) {
+    if (RT == 4 && a.rope) return (tx >> 1) * 8 + (tx & 1) * 2 + (rt & 1) + (rt >> 1) * 4;
+    return n0 / 16 + rt;
+  };
 
   // uniform tile bases (SGPRs) + one per-lane offset, as in gemm_wave_kernel
   const bf16_t* W = static_cast<const bf16_t*>(a.W);
   const bf16_t* wtile[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt)
-    wtile[rt] = TILED ? W + static_cast<int64_t>((n0 + rt * 16) / 16) * (a.K / 64) * 1024
-                      : W + static_cast<int64_t>(n0 + rt * 16) * a.K;
+    wtile[rt] = TILED ? W + static_cast<int64_t>(row16(rt)) * (a.K / 64) * 1024
+                      : W + static_cast<int64_t>(row16(rt)) * 16 * a.K;
   const int w_lane = TILED ? lane * 8 : (lane & 15) * a.K + (lane >> 4) * 16;
   constexpr int kChunk = TILED ? 1024 : 64;
+  // activations: row-major (16 token rows x 16 bytes per load) or tiled (one
+  // 1 KB block per load; token blocks past the last one are clamped to it,
+  // their rows masked below)
+  const int x_chunk = a.x_tiled ? 1024 : 64, x_second = a.x_tiled ? 512 : 8;
   const bf16_t* xp[TB];
   bool xok[TB];
 #pragma unroll
   for (int tb = 0; tb < TB; ++tb) {
     const int m = m0 + tb * 16 + l16;
     xok[tb] = m < a.M;
-    xp[tb] = a.X + static_cast<int64_t>(xok[tb] ? m : m0) * a.K + c_begin * 64 + g4 * 16;
+    if (a.x_tiled) {
+      const int blk = min(m0 / 16 + tb, (a.M + 15) / 16 - 1);
+      xp[tb] = a.X + (static_cast<int64_t>(blk) * (a.K / 64) + c_begin) * 1024 + lane * 8;
+    } else {
+      xp[tb] = a.X + static_cast<int64_t>(xok[tb] ? m : m0) * a.K + c_begin * 64 + g4 * 16;
+    }
   }
 
   struct Slot {
@@ -691,8 +711,8 @@ __global__ __launch_bounds__(64 * NW, WPE) void gemm_splitk_kernel(GemmArgs a) {
     }
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) {
-      sl.x[tb][0] = *reinterpret_cast<const uint4*>(xp[tb] + cc * 64);
-      sl.x[tb][1] = *reinterpret_cast<const uint4*>(xp[tb] + cc * 64 + 8);
+      sl.x[tb][0] = *reinterpret_cast<const uint4*>(xp[tb] + cc * x_chunk);
+      sl.x[tb][1] = *reinterpret_cast<const uint4*>(xp[tb] + cc * x_chunk + x_second);
     }
   };
   const uint4 zero4 = make_uint4(0, 0, 0, 0);
@@ -771,10 +791,10 @@ __global__ __launch_bounds__(64 * NW, WPE) void gemm_splitk_kernel(GemmArgs a) {
         for (int r = 0; r < 4; ++r) s_acc[wave][(rt * TB + tb) * 4 + r][lane] = acc[rt][tb][r];
   }
   __syncthreads();
-  if constexpr (RT == 8) {
+  if constexpr (kRopeTile) {
     if (a.rope) {
       // RoPE pairs (d, d + 64) of the tile's head: the quads of row tiles rt
-      // and rt + 4 (rt < 4); rotation as in the separate RoPE kernel
+      // and rt + RT / 2 (rt < RT / 2); rotation as in the separate RoPE kernel
       constexpr int kPairs = (RT / 2) * TB * 64;
 #pragma unroll
       for (int q0 = 0; q0 < kPairs; q0 += 64 * NW) {
@@ -793,8 +813,8 @@ __global__ __launch_bounds__(64 * NW, WPE) void gemm_splitk_kernel(GemmArgs a) {
         }
         const int m = m0 + tb * 16 + (ql & 15);
         if (m >= a.M) continue;
-        const int head = n0 / 128;
-        const int d0 = rt * 16 + (ql >> 4) * 4;  // < 64
+        const int head = row16(0) / 8;
+        const int d0 = (row16(rt) % 8) * 16 + (ql >> 4) * 4;  // < 64
         const int b = m / a.Lq, i = m % a.Lq;
         const int pos = a.prefix_len[b] + i;
         float o1[4], o2[4];

@@ -33,6 +33,7 @@ struct AttnArgs {
   int dtype;
   void* out;                          // [B, Lq, Hq, dh] dense
   int q_ready = 0;                    // q already rotated in the workspace, k/v in the caches
+  int out_tiled = 0;                  // bf16 out in the tiled activation layout (xtile_offset)
 };
 // Scale of the packed q of the bf16 attention kernel: log2(e) / sqrt(dh), so
 // that scores come out of the MFMA in the log2 domain.
@@ -83,6 +84,7 @@ dg_status launch_gemm(const void* A, const void* W, void* C, int M, int N, int K
 // into the attention workspace's packed q (its first bytes), k rotated and v
 // into the caches at [P, P + Lq).  DG_ERR_UNSUPPORTED when the shape does not
 // take the fused path (then run the projection and the attention's own RoPE).
+// x_tiled: A in the tiled activation layout (tiled weights only).
 struct QkvRope {
   const int32_t* prefix_len;
   int B, Lq, Hq, Hkv, dh, Tmax;
@@ -90,17 +92,27 @@ struct QkvRope {
   void* q_out;
   void* k_cache;
   void* v_cache;
+  int x_tiled;
 };
+bool qkv_rope_supported(const QkvRope& r, int K);
 dg_status launch_qkv_rope(const void* A, const void* W, int K, int w_layout, const QkvRope& r,
                           hipStream_t stream);
+// C (=|+=) A W^T with A bf16 in the tiled activation layout and W tiled bf16
+// (the O projection over more than 16 tokens); dense_xt_supported says which
+// shapes run.
+bool dense_xt_supported(int M, int N, int K);
+dg_status launch_gemm_xt(const void* A, const void* W, void* C, int M, int N, int K,
+                         int out_dtype, GemmEpilogue ep, hipStream_t stream);
 // RMSNorm of f32 rows x [M, D] (eps 1e-6, unit gain) into out_dtype.
 dg_status launch_rmsnorm(const float* x, void* out, int M, int D, int out_dtype,
                          hipStream_t stream);
 // The MoE combine fused into the next RMSNorm: x[t] += sum_j y_slot[t * k + j]
 // (slot order, as launch_moe_combine), then out = RMSNorm(x).  y_slot may be
-// null (plain RMSNorm); slot_dtype is DG_BF16 or DG_F32.
+// null (plain RMSNorm); slot_dtype is DG_BF16 or DG_F32.  out_tiled: bf16
+// out in the tiled activation layout (D % 64 == 0, D <= 4096).
 dg_status launch_combine_rmsnorm(const void* y_slot, int slot_dtype, int k, float* x, void* out,
-                                 int M, int D, int out_dtype, hipStream_t stream);
+                                 int M, int D, int out_dtype, hipStream_t stream,
+                                 bool out_tiled = false);
 // x[t] = emb[tokens[t]] as f32.
 dg_status launch_embed(const int32_t* tokens, const void* emb, float* x, int M, int D,
                        int dtype, hipStream_t stream);

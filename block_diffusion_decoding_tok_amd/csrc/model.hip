@@ -172,10 +172,11 @@ Layout layout(const dg_model_dims& d, int maxB, int maxT) {
   const size_t a = esz(d.act_dtype);
   size_t off = 0;
   auto take = [&](size_t bytes) { const size_t o = off; off += align_up(bytes, 256); return o; };
+  const size_t T16 = align_up(T, 16);     // the tiled activation layout's whole token blocks
   L.x = take(T * d.d_model * 4);
-  L.h = take(T * d.d_model * a);
+  L.h = take(T16 * d.d_model * a);
   L.qkv = take(T * qkv_w * a);
-  L.attn_out = take(T * d.n_heads * d.head_dim * a);
+  L.attn_out = take(T16 * d.n_heads * d.head_dim * a);
   L.router = take(T * d.n_experts * 4);
   L.topk_ids = take(T * d.top_k * 4);
   L.gates = take(T * d.top_k * 4);
@@ -236,8 +237,18 @@ dg_status check_dims(const dg_model_dims* d) {
   return DG_OK;
 }
 
-dg_status norm_input(dg_ctx* c, int T, hipStream_t s);
-dg_status layer_tail(dg_ctx* c, int l, int B, int n, hipStream_t s);
+dg_status norm_input(dg_ctx* c, int T, hipStream_t s, bool tiled = false);
+dg_status layer_tail(dg_ctx* c, int l, int B, int n, bool xt, hipStream_t s);
+
+// Whether a layer over T tokens runs its dense projections on the tiled
+// activation layout: the fused QKV + RoPE projection and the O projection
+// both take it (bf16, tiled weights, heads of 128, more than 16 tokens).
+bool tiled_acts(const dg_model_dims& d, const QkvRope& r) {
+  const int qd = d.n_heads * d.head_dim;
+  return d.act_dtype == DG_BF16 && d.weight_layout == DG_LAYOUT_TILED && d.d_model % 64 == 0 &&
+         d.d_model / 4 <= 1024 && qkv_rope_supported(r, d.d_model) &&
+         dense_xt_supported(r.B * r.Lq, d.d_model, qd);
+}
 
 // One decoder layer over T = B * n tokens (residual ctx->x).
 dg_status layer(dg_ctx* c, int l, int B, int n, void* kc, void* vc, int Tmax,
@@ -248,21 +259,24 @@ dg_status layer(dg_ctx* c, int l, int B, int n, void* kc, void* vc, int Tmax,
   const int qkv_w = qd + 2 * kd;
   const size_t a = esz(d.act_dtype);
   dg_status st;
-  if ((st = norm_input(c, T, s))) return st;
+  QkvRope r{prefix_len, B, n, d.n_heads, d.n_kv_heads, d.head_dim, Tmax, d.rope_theta,
+            c->attn_ws, kc, vc, 0};
+  const bool xt = tiled_acts(d, r);
+  r.x_tiled = xt ? 1 : 0;
+  if ((st = norm_input(c, T, s, xt))) return st;
   // bf16: the projection rotates q and k in its epilogue and writes q to the
   // attention workspace, k and v to the caches (one launch less per layer)
   if (d.act_dtype == DG_BF16) {
-    const QkvRope r{prefix_len, B, n, d.n_heads, d.n_kv_heads, d.head_dim, Tmax, d.rope_theta,
-                    c->attn_ws, kc, vc};
     st = launch_qkv_rope(c->h, c->wqkv[l], d.d_model, d.weight_layout, r, s);
     if (st == DG_OK) {
       if (kv_only) return DG_OK;
       AttnArgs aa{nullptr, nullptr, nullptr, 0, 0, kc, vc, prefix_len, B, n, d.n_heads,
-                  d.n_kv_heads, d.head_dim, Tmax, mode, d.rope_theta, d.act_dtype, c->attn_out, 1};
+                  d.n_kv_heads, d.head_dim, Tmax, mode, d.rope_theta, d.act_dtype, c->attn_out, 1,
+                  xt ? 1 : 0};
       if ((st = launch_attention(aa, c->attn_ws, s))) return st;
-      return layer_tail(c, l, B, n, s);
+      return layer_tail(c, l, B, n, xt, s);
     }
-    if (st != DG_ERR_UNSUPPORTED) return st;
+    if (st != DG_ERR_UNSUPPORTED || xt) return st;
   }
   if ((st = launch_gemm(c->h, c->wqkv[l], c->qkv, T, qkv_w, d.d_model, d.act_dtype,
                         d.weight_layout, d.act_dtype, kStore, s)))
@@ -276,20 +290,25 @@ dg_status layer(dg_ctx* c, int l, int B, int n, void* kc, void* vc, int Tmax,
               d.n_heads, d.n_kv_heads, d.head_dim, Tmax, mode, d.rope_theta, d.act_dtype,
               c->attn_out};
   if ((st = launch_attention(aa, c->attn_ws, s))) return st;
-  return layer_tail(c, l, B, n, s);
+  return layer_tail(c, l, B, n, false, s);
 }
 
 // The rest of a layer after attention: O projection + residual, RMSNorm,
 // router, routing, expert gate/up and down (the combine waits for the next
-// norm).
-dg_status layer_tail(dg_ctx* c, int l, int B, int n, hipStream_t s) {
+// norm).  xt: the attention output is in the tiled activation layout.
+dg_status layer_tail(dg_ctx* c, int l, int B, int n, bool xt, hipStream_t s) {
   const dg_model_dims& d = c->d;
   const int T = B * n;
   const int qd = d.n_heads * d.head_dim;
   dg_status st;
-  if ((st = launch_gemm(c->attn_out, c->wo[l], c->x, T, d.d_model, qd, d.act_dtype,
-                        d.weight_layout, DG_F32, kAccumulateF32, s)))
+  if (xt) {
+    if ((st = launch_gemm_xt(c->attn_out, c->wo[l], c->x, T, d.d_model, qd, DG_F32,
+                             kAccumulateF32, s)))
+      return st;
+  } else if ((st = launch_gemm(c->attn_out, c->wo[l], c->x, T, d.d_model, qd, d.act_dtype,
+                               d.weight_layout, DG_F32, kAccumulateF32, s))) {
     return st;
+  }
   if ((st = launch_rmsnorm(c->x, c->h, T, d.d_model, d.act_dtype, s))) return st;
   if ((st = launch_gemm(c->h, c->wr[l], c->router, T, d.n_experts, d.d_model, d.act_dtype,
                         d.weight_layout, DG_F32, kStore, s)))
@@ -313,16 +332,17 @@ dg_status layer_tail(dg_ctx* c, int l, int B, int n, hipStream_t s) {
   return DG_OK;
 }
 
-// RMSNorm of the residual stream into c->h, taking a pending MoE combine
-// (the previous layer's expert outputs) into x first.
-dg_status norm_input(dg_ctx* c, int T, hipStream_t s) {
+// RMSNorm of the residual stream into c->h (tiled: in the tiled activation
+// layout), taking a pending MoE combine (the previous layer's expert outputs)
+// into x first.
+dg_status norm_input(dg_ctx* c, int T, hipStream_t s, bool tiled) {
   const dg_model_dims& d = c->d;
   void *h_mid, *y_slot = nullptr;
   if (c->pending_combine)
     moe_ffn_workspace_split(c->moe_ws, T, d.d_ff, d.top_k, d.act_dtype, &h_mid, &y_slot);
   c->pending_combine = false;
   return launch_combine_rmsnorm(y_slot, d.act_dtype, d.top_k, c->x, c->h, T, d.d_model,
-                                d.act_dtype, s);
+                                d.act_dtype, s, tiled);
 }
 
 // Flush a pending MoE combine into x (end of a forward without the LM head).

@@ -197,38 +197,46 @@ def full_layers(request):
     return d, w, model
 
 
-@pytest.mark.parametrize("B,P0,planted,mode", [(1, 256, False, CANVAS), (4, 512, False, CANVAS),
-                                               (1, 256, True, CANVAS), (2, 512, True, CAUSAL)])
-def test_full_width_layers_teacher_forced(full_layers, B, P0, planted, mode):
+@pytest.mark.parametrize("B,P0,planted,mode,n", [(1, 256, False, CANVAS, 256),
+                                                 (4, 512, False, CANVAS, 256),
+                                                 (1, 256, True, CANVAS, 256),
+                                                 (2, 512, True, CAUSAL, 256),
+                                                 (1, 300, False, CANVAS, 200),
+                                                 (3, 40, True, CAUSAL, 40),
+                                                 (1, 64, False, CAUSAL, 17)])
+def test_full_width_layers_teacher_forced(full_layers, B, P0, planted, mode, n):
     """planted: the router override supplies N(0,1) + hot-expert-skew logits
-    (the stated MoE routing) instead of the random router's.  CAUSAL: a
-    256-token prefill chunk at positions [P0, P0 + 256) (the prompt path)."""
+    (the stated MoE routing) instead of the random router's.  CAUSAL: an
+    n-token prefill chunk at positions [P0, P0 + n) (the prompt path).  Token
+    counts off the 16- and 64-token tiles (200, 3 x 40, 17) end in partial
+    token blocks of the tiled activation layout; 300 prompt tokens prefill as
+    256 + 44."""
     d, w, model = full_layers
     override = None
     if planted:
-        override = [torch.from_numpy(router_logits_skewed(B * 256, d.E, d.k, seed=40 + l)[0])
+        override = [torch.from_numpy(router_logits_skewed(B * n, d.E, d.k, seed=40 + l)[0])
                     for l in range(d.NL)]
         model.set_router_override([o.to(DEV) for o in override])
     else:
         model.set_router_override(None)
     m = oracle_model(d, w)
-    Tmax = P0 + 256
+    Tmax = P0 + n
     kc, vc = _caches(d, B, Tmax, torch.bfloat16)
     Pd = torch.zeros(B, dtype=torch.int32, device=DEV)
     prompt = prompt_ids(B, P0, d.V, seed=B).to(DEV)
     dg.dg_prefill(model, prompt, kc, vc, Pd)
-    canvas = prompt_ids(B, 256, d.V, seed=100 + B).to(DEV)
-    x = torch.empty((B * 256, d.D), dtype=torch.float32, device=DEV)
+    canvas = prompt_ids(B, n, d.V, seed=100 + B).to(DEV)
+    x = torch.empty((B * n, d.D), dtype=torch.float32, device=DEV)
     P_host = Pd.cpu().numpy()
     assert list(P_host) == [P0] * B
-    dg.dg_model_forward(model, canvas, x, B, 256, 0, 0, kc, vc, Pd)       # embed only
+    dg.dg_model_forward(model, canvas, x, B, n, 0, 0, kc, vc, Pd)         # embed only
     for l in range(d.NL):
-        x_in = x.cpu().double().numpy().reshape(B, 256, d.D)
+        x_in = x.cpu().double().numpy().reshape(B, n, d.D)
         cache_k = kc[l].cpu().double().numpy()
         cache_v = vc[l].cpu().double().numpy()
-        dg.dg_model_forward(model, None, x, B, 256, l, l + 1, kc, vc, Pd, mask_mode=mode)
+        dg.dg_model_forward(model, None, x, B, n, l, l + 1, kc, vc, Pd, mask_mode=mode)
         torch.cuda.synchronize()
-        x_out = x.cpu().double().numpy().reshape(B, 256, d.D)
+        x_out = x.cpu().double().numpy().reshape(B, n, d.D)
         trace = []
         ref = layer_forward(m, m.layers[l], x_in, cache_k, cache_v, P_host, mode, trace=trace,
                             router_logits=None if override is None else override[l].numpy())
@@ -249,12 +257,12 @@ def test_full_width_layers_teacher_forced(full_layers, B, P0, planted, mode):
         if planted:                      # identical routing inputs: no exceptions
             assert not bad.any()
         # the canvas K/V written by the device vs the oracle's (same inputs)
-        got_k = kc[l].cpu().double().numpy()[:, :, P0:P0 + 256]
-        assert rel_err_rows(got_k, cache_k[:, :, P0:P0 + 256]) < 3e-2
+        got_k = kc[l].cpu().double().numpy()[:, :, P0:P0 + n]
+        assert rel_err_rows(got_k, cache_k[:, :, P0:P0 + n]) < 3e-2
     # final norm + LM head on the last layer's output
-    logits = torch.empty((B, 256, d.V), dtype=torch.bfloat16, device=DEV)
+    logits = torch.empty((B, n, d.V), dtype=torch.bfloat16, device=DEV)
     x_last = x.cpu().double().numpy()
-    dg.dg_model_forward(model, None, x, B, 256, d.NL, d.NL, kc, vc, Pd, logits=logits)
+    dg.dg_model_forward(model, None, x, B, n, d.NL, d.NL, kc, vc, Pd, logits=logits)
     torch.cuda.synchronize()
     ref = rmsnorm(x_last) @ to_f64(w["lm"]).T
     assert rel_err_rows(logits.cpu().double().numpy().reshape(-1, d.V), ref) < 2e-2
