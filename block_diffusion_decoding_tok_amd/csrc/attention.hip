@@ -189,9 +189,14 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(
   const int n_keys = P + Lq;
   const int row0 = tile * kAttnRows + rg * 32;      // this wave's first packed row
 
-  // key range of this split (causal: trimmed to the last row of the tile)
-  const int k_begin = split * chunk;
-  int k_end = min(n_keys, k_begin + chunk);
+  // key range of this split: the row's keys [0, P + Lq) dealt out evenly in
+  // whole tiles (P is read on the device, so a captured graph replayed at a
+  // larger prefix still balances its splits; chunk * nsplit covers Tmax);
+  // causal: trimmed to the last row of the tile
+  const int even = ((n_keys + nsplit - 1) / nsplit + kAttnKeys - 1) / kAttnKeys * kAttnKeys;
+  const int split_keys = min(chunk, even);
+  const int k_begin = split * split_keys;
+  int k_end = min(n_keys, k_begin + split_keys);
   if (causal) {
     const int last_row = min(rows_total - 1, tile * kAttnRows + kAttnRows - 1);
     k_end = min(k_end, P + last_row / G + 1);

@@ -207,7 +207,10 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
     }
     // the grid is an upper bound of the item count: the live items are dealt
     // out evenly over the 8 XCDs (workgroup i runs on XCD i % 8) in
-    // contiguous ranges with the token tiles of a row tile adjacent
+    // contiguous ranges with the row tiles of a token tile adjacent, so that
+    // a token tile's rows are fetched into one L2 once (at a thousand tokens
+    // the gathered rows outgrow an L2) and an expert's consecutive token
+    // tiles still share its weight rows there
     const int n_tiles = s_scan[E - 1];
     const int live = n_tiles * a.n_tiles_x;
     const int per_xcd = (live + 7) / 8;
@@ -215,8 +218,8 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
     if (slot >= per_xcd) return;
     const int item = (blockIdx.x % 8) * per_xcd + slot;
     if (item >= live) return;
-    tx = item / n_tiles;
-    ty = item % n_tiles;
+    tx = item % a.n_tiles_x;
+    ty = item / a.n_tiles_x;
     int lo = 0, hi = E - 1;                    // first e with scan[e] > ty
     while (lo < hi) {
       const int mid = (lo + hi) >> 1;

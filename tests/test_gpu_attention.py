@@ -68,6 +68,14 @@ def test_canvas_attention_bf16_ragged_rows():
     _check(case, [77, 700, 0], 1000, CANVAS, torch.bfloat16)
 
 
+def test_canvas_attention_bf16_spare_cache():
+    """A cache sized for far more keys than the rows hold (the splits are
+    balanced over each row's own key count on the device): two rows with
+    different prefixes in a cache of 8192 slots."""
+    case = attention_case(B=2, Lq=256, P=3000, seed=31)
+    _check(case, [1500, 3000], 8192, CANVAS, torch.bfloat16)
+
+
 @pytest.mark.parametrize("P", [0, 64, 300])
 def test_causal_prefill_bf16(P):
     case = attention_case(B=2, Lq=200, P=max(P, 1), seed=20 + P)
