@@ -33,7 +33,7 @@ def _check_route(logits, k):
 
 
 @pytest.mark.parametrize("T,E,k", [(256, 128, 8), (1024, 128, 8), (37, 5, 2), (300, 256, 16),
-                                   (64, 1, 1), (10, 200, 3)])
+                                   (64, 1, 1), (10, 200, 3), (130, 128, 8)])
 def test_route_matches_oracle(T, E, k):
     rng = np.random.default_rng(T + E + k)
     logits = torch.from_numpy(rng.standard_normal((T, E)).astype(np.float32))
