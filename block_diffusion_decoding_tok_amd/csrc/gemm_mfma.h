@@ -41,6 +41,14 @@ enum GemmMode { kGateUp = 0, kDown = 1, kDense = 2 };
 struct GemmArgs {
   const void* W;            // weights (bf16 or fp8 bytes)
   int64_t w_group_stride;   // elements between experts
+  // tiled 16 x 64 blocks (bf16 / fp8): elements between the blocks of
+  // consecutive 16-row tiles and between consecutive 64-k chunks of a tile.
+  // w_chunk_stride == 0: one matrix, each tile's chunks contiguous (tile
+  // stride K / 64 * 1024, chunk stride 1024); a stack of experts stores the
+  // chunk c of every expert's tiles together (tile stride 1024, chunk stride
+  // E * N / 16 * 1024)
+  int64_t w_tile_stride;
+  int64_t w_chunk_stride;
   const float* w_scale;     // per-row scale (fp8) or null
   int64_t s_group_stride;
   const bf16_t* X;          // activations [rows, K] bf16
@@ -157,14 +165,19 @@ constexpr int kMx4Block = 544;
 template <typename WT, bool TILED>
 struct WRow {
   const WT* base;
+  int64_t cstride;
   static constexpr int kSecond = TILED ? 512 : 8;   // 2-byte types: values 8..15
-  __device__ void init(const WT* Wg, int row0, int K, int lane) {
-    if (TILED)
-      base = Wg + static_cast<int64_t>(row0 / 16) * (K / 64) * 1024 + lane * (sizeof(WT) == 1 ? 16 : 8);
-    else
+  __device__ void init(const WT* Wg, int row0, int K, int lane, const GemmArgs& a) {
+    if (TILED) {
+      const int64_t ts = a.w_chunk_stride ? a.w_tile_stride : static_cast<int64_t>(K / 64) * 1024;
+      cstride = a.w_chunk_stride ? a.w_chunk_stride : 1024;
+      base = Wg + static_cast<int64_t>(row0 / 16) * ts + lane * (sizeof(WT) == 1 ? 16 : 8);
+    } else {
+      cstride = 64;
       base = Wg + static_cast<int64_t>(row0 + (lane & 15)) * K + (lane >> 4) * 16;
+    }
   }
-  __device__ const WT* at(int c) const { return base + c * (TILED ? 1024 : 64); }
+  __device__ const WT* at(int c) const { return base + c * cstride; }
 };
 
 template <int RT, int TB, int KS, int PF, bool FP8, int MODE, bool TILED>
@@ -251,7 +264,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
   for (int rt = 0; rt < RT; ++rt) {
     const int row0 = (MODE == kGateUp) ? (rt == 0 ? 0 : a.N / 2) + tx * 64 + wave * 16
                                        : tx * (64 * RT) + wave * (16 * RT) + rt * 16;
-    wr_at[rt].init(Wg, row0, a.K, lane);
+    wr_at[rt].init(Wg, row0, a.K, lane, a);
   }
   const int nchunks = (a.K + 63) / 64;
   const int nstages = (nchunks + KS - 1) / KS;
@@ -499,14 +512,19 @@ __global__ __launch_bounds__(64, WPE) void gemm_wave_kernel(GemmArgs a) {
   // c * 544 + 512 + 16 (q / 2) + r; row-major: row lane % 16, k 16 (lane / 16)
   // + 64 c)
   const WT* Wg = static_cast<const WT*>(a.W) + static_cast<int64_t>(grp) * a.w_group_stride;
-  constexpr int kChunk = WF == kWMx4 ? kMx4Block : (TILED ? 1024 : 64);
+  // elements between a tile's consecutive 64-k chunks, and between tiles
+  const int64_t kChunk = WF == kWMx4 ? kMx4Block
+                         : TILED     ? (a.w_chunk_stride ? a.w_chunk_stride : 1024)
+                                     : 64;
+  const int64_t tile_stride = WF == kWMx4 ? static_cast<int64_t>(a.K / 64) * kMx4Block
+                              : (a.w_chunk_stride ? a.w_tile_stride : static_cast<int64_t>(a.K / 64) * 1024);
   const WT* wtile[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const int row0 = (MODE == kGateUp)
                          ? (rt < RT / 2 ? 0 : a.N / 2) + tx * (8 * RT) + (rt % (RT / 2)) * 16
                          : tx * (16 * RT) + rt * 16;
-    wtile[rt] = TILED ? Wg + static_cast<int64_t>(row0 / 16) * (a.K / 64) * (WF == kWMx4 ? kMx4Block : 1024)
+    wtile[rt] = TILED ? Wg + static_cast<int64_t>(row0 / 16) * tile_stride
                       : Wg + static_cast<int64_t>(row0) * a.K;
   }
   const int w_lane = WF == kWMx4 ? lane * 8

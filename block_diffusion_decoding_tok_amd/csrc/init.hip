@@ -70,9 +70,11 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const float* __restr
 }
 
 // Row-major [G, N, K] -> tile-packed (16 rows x 64 k blocks in wave-load
-// order); one thread per 16-byte piece of the destination.
+// order; one matrix: a tile's blocks contiguous, block (t, c) at t K/64 + c; a
+// stack of G > 1: block (g, t, c) at (c G + g) N/16 + t, every expert's k
+// chunk c together); one thread per 16-byte piece of the destination.
 __global__ void pack_weights_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
-                                    int64_t pieces, int N, int K, int elem_bytes) {
+                                    int64_t pieces, int64_t G, int N, int K, int elem_bytes) {
   const int64_t q = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (q >= pieces) return;
   const int per_block = 1024 * elem_bytes / 16;        // 64 (1-byte) or 128 (2-byte) pieces
@@ -81,9 +83,14 @@ __global__ void pack_weights_kernel(const uint4* __restrict__ src, uint4* __rest
   const int lane = within % 64, h = within / 64;
   const int r = lane % 16, g4 = lane / 16;
   const int64_t NC = K / 64, NT = N / 16;
-  const int64_t c = blk % NC;
-  const int64_t gt = blk / NC;                          // g * NT + t
-  const int64_t g = gt / NT, t = gt % NT;
+  int64_t g, t, c;
+  if (G == 1) {
+    g = 0; t = blk / NC; c = blk % NC;
+  } else {
+    t = blk % NT;
+    const int64_t cg = blk / NT;                        // c * G + g
+    g = cg % G; c = cg / G;
+  }
   const int vals = 16 / elem_bytes;                     // values per piece
   const int64_t elem = (g * N + 16 * t + r) * static_cast<int64_t>(K) + 64 * c + 16 * g4 + vals * h;
   dst[q] = src[elem * elem_bytes / 16];
@@ -94,7 +101,7 @@ dg_status launch_pack_weights(const void* src, void* dst, int64_t groups, int N,
   const int64_t pieces = groups * N * static_cast<int64_t>(K) * elem_bytes / 16;
   if (pieces == 0) return DG_OK;
   pack_weights_kernel<<<static_cast<unsigned>((pieces + 255) / 256), 256, 0, stream>>>(
-      static_cast<const uint4*>(src), static_cast<uint4*>(dst), pieces, N, K, elem_bytes);
+      static_cast<const uint4*>(src), static_cast<uint4*>(dst), pieces, groups, N, K, elem_bytes);
   DG_LAUNCH_CHECK();
   return DG_OK;
 }

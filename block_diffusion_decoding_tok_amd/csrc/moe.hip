@@ -311,6 +311,15 @@ static void launch_wave(GemmArgs& g, int T, int k, int E, hipStream_t stream) {
                      (TB == 1 ? (MODE == kDown ? kDownWPE : kMoeWPE) : 1)><<<grid, 64, 0, stream>>>(g);
 }
 
+// A tile-packed stack of E > 1 experts [E, N, K] (bf16 / fp8) keeps the k
+// chunk c of every expert's 16-row tiles together: items streaming the same
+// k range of different experts read neighbouring addresses.
+static void stack_strides(GemmArgs& g, int N, int K, int E) {
+  g.w_group_stride = static_cast<int64_t>(N / 16) * 1024;
+  g.w_tile_stride = 1024;
+  g.w_chunk_stride = static_cast<int64_t>(E) * (N / 16) * 1024;
+}
+
 // Bytes of one expert's weights [N, K] in format WF.
 template <int WF>
 static int64_t expert_bytes(int N, int K) {
@@ -325,6 +334,7 @@ static void launch_gate_up_mfma(const void* x, const void* wgu, const float* sgu
   GemmArgs g{};
   g.W = wgu;
   g.w_group_stride = WF == kWBf16 ? static_cast<int64_t>(2) * I * D : expert_bytes<WF>(2 * I, D);
+  if (TILED && WF != kWMx4 && E > 1) stack_strides(g, 2 * I, D, E);
   g.w_scale = WF == kWFp8 ? sgu : nullptr; g.s_group_stride = 2 * I;
   g.X = static_cast<const bf16_t*>(x);
   g.N = 2 * I; g.K = D; g.n_groups = E; g.topk = k;
@@ -358,6 +368,7 @@ static void launch_down_mfma(const bf16_t* h, const void* wd, const float* sd, c
   GemmArgs d{};
   d.W = wd;
   d.w_group_stride = WF == kWBf16 ? static_cast<int64_t>(D) * I : expert_bytes<WF>(D, I);
+  if (TILED && WF != kWMx4 && E > 1) stack_strides(d, D, I, E);
   d.w_scale = WF == kWFp8 ? sd : nullptr; d.s_group_stride = D;
   d.X = h;
   d.N = D; d.K = I; d.n_groups = E; d.topk = k;

@@ -53,9 +53,14 @@ typedef enum { DG_MASK_CANVAS = 0, DG_MASK_CAUSAL = 1 } dg_mask_mode;
 
 /* Weight layouts for [G, N, K] weight tensors (G groups, e.g. experts).
  *   DG_LAYOUT_ROWMAJOR  element (g, n, k) at (g * N + n) * K + k.
- *   DG_LAYOUT_TILED     blocks of 16 rows x 64 k, block (g, n / 16, k / 64) at
- *                       ((g * N / 16 + n / 16) * K / 64 + k / 64) * 1024 elements;
- *                       inside a block, with r = n % 16, q = (k % 64) / 16:
+ *   DG_LAYOUT_TILED     blocks of 16 rows x 64 k.  One matrix (G = 1): block
+ *                       (n / 16, k / 64) at (n / 16 * K / 64 + k / 64) * 1024
+ *                       elements (a 16-row tile contiguous).  A stack of G > 1
+ *                       (experts): block (g, n / 16, k / 64) at
+ *                       ((k / 64 * G + g) * N / 16 + n / 16) * 1024 elements
+ *                       (the k chunk of every expert's tiles together, so the
+ *                       waves streaming different experts read neighbouring
+ *                       addresses); inside a block, with r = n % 16, q = (k % 64) / 16:
  *                       1-byte types: lane = r + 16 q holds k % 16 at lane * 16;
  *                       2-byte types: half h = (k % 16) / 8 at h * 512 + lane * 8.
  *                       It is the order in which a 64-lane wave loads an MFMA

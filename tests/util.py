@@ -147,7 +147,9 @@ _FP8_TABLE = fp8_e4m3fn_decode(np.arange(256, dtype=np.uint8))
 
 def pack_tiled(w):
     """Row-major [.., N, K] -> the DG_LAYOUT_TILED element order (numpy view of
-    the same shape): blocks of 16 rows x 64 k in wave-load order."""
+    the same shape): blocks of 16 rows x 64 k in wave-load order; one matrix
+    keeps a tile's blocks together (t, c), a stack of G > 1 matrices keeps the
+    k chunk c of every matrix's tiles together (c, g, t)."""
     a = np.asarray(w)
     N, K = a.shape[-2], a.shape[-1]
     G = a.size // (N * K)
@@ -157,4 +159,7 @@ def pack_tiled(w):
     else:
         x = x.reshape(G, N // 16, 16, K // 64, 4, 2, 8)     # g, t, r, c, q, h, j
         out = x.transpose(0, 1, 3, 5, 4, 2, 6)               # g, t, c, h, q, r, j
+    if G > 1:                                                # block order c, g, t
+        blocks = np.ascontiguousarray(out).reshape(G, N // 16, K // 64, -1)
+        out = blocks.transpose(2, 0, 1, 3)
     return np.ascontiguousarray(out).reshape(a.shape)
