@@ -256,9 +256,13 @@ __global__ void down_f32_kernel(const float* __restrict__ h, const float* __rest
 }
 
 // ------------------------------------------------------------- launchers
+// LDS-staged 64-token tiles (a thousand tokens and more): stages of 64 k, two
+// in flight, so that four waves per SIMD stay resident (measured at 1024
+// tokens: gate/up 190 -> 156 us, down 131 -> 94 us against 128 k x 3 stages
+// at two waves per SIMD)
 constexpr int kMoeTB = 4;      // 64 tokens per tile
-constexpr int kMoeKS = 2;      // 128 k per LDS stage
-constexpr int kMoePF = 3;      // weight stages in flight
+constexpr int kMoeKS = 1;      // 64 k per LDS stage
+constexpr int kMoePF = 2;      // weight stages in flight
 
 size_t moe_ffn_workspace_bytes(int T, int D, int I, int E, int k, int x_dtype) {
   const size_t slots = static_cast<size_t>(T) * k;
