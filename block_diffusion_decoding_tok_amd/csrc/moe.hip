@@ -12,7 +12,6 @@
 //   route_sort_kernel   one 1024-thread workgroup: histogram, exclusive scan
 //                       -> expert_offsets, stable scatter of the slot entries
 //                       t * k + j by expert (ballot-based ranks, deterministic).
-//   route_fused_kernel  both in one workgroup for up to 2048 slots.
 //   gemm_stream_kernel  (gemm_mfma.h) gate/up + GELU*up -> h [T*k, I] bf16 in
 //                       sorted order; down + gate -> y_slot [T*k, D] bf16.
 //   combine_kernel      y[t] += sum_j y_slot[t*k + j] in slot order.
@@ -28,12 +27,10 @@ namespace dg {
 // sl + 16, ... (E <= 256); each of the k rounds takes the group-wide
 // (logit desc, id asc) maximum of the experts not yet taken (four DPP
 // steps).  Lane j < k of the group writes slot j: its id and its gate, the
-// softmax of the k selected logits (sum in slot order).  With s_ids the ids
-// are also kept in LDS for a sort in the same workgroup.
+// softmax of the k selected logits (sum in slot order).
 __device__ __forceinline__ void route_topk_group(const float* row, int t, int E, int k, int sl,
                                                  int32_t* __restrict__ ids,
-                                                 float* __restrict__ gates,
-                                                 int* s_ids = nullptr) {
+                                                 float* __restrict__ gates) {
   // the token's E logits at row (global or LDS); all 16 loads issued
   // unconditionally (clamped), masked afterwards
   float v[16];
@@ -65,7 +62,6 @@ __device__ __forceinline__ void route_topk_group(const float* row, int t, int E,
   if (sl < k) {
     ids[static_cast<int64_t>(t) * k + sl] = my_id;
     gates[static_cast<int64_t>(t) * k + sl] = expf(my_val - best0) / z;
-    if (s_ids) s_ids[t * k + sl] = my_id;
   }
 }
 
@@ -157,38 +153,11 @@ __global__ __launch_bounds__(1024) void route_sort_kernel(const int32_t* __restr
   sort_slots(ids, n, E, offsets, sorted_rows, sm);
 }
 
-// A canvas-sized router (T * k <= kFusedRouteSlots): the top-k of every
-// token (64 tokens at a time, one per 16-lane group) and the stable sort in
-// one 1024-thread workgroup, the ids passed between them in LDS -- one launch
-// instead of two, the same arithmetic and results.
-constexpr int kFusedRouteSlots = 2048;
-
-__global__ __launch_bounds__(1024) void route_fused_kernel(const float* __restrict__ logits,
-                                                           int T, int E, int k,
-                                                           int32_t* __restrict__ ids,
-                                                           float* __restrict__ gates,
-                                                           int32_t* __restrict__ offsets,
-                                                           int32_t* __restrict__ sorted_rows) {
-  __shared__ SortSmem sm;
-  __shared__ int s_ids[kFusedRouteSlots];
-  const int group = threadIdx.x >> 4, sl = threadIdx.x & 15;
-  for (int t = group; t < T; t += 64)     // a group's 16 lanes share t
-    route_topk_group(logits + static_cast<int64_t>(t) * E, t, E, k, sl, ids, gates, s_ids);
-  __syncthreads();
-  sort_slots(s_ids, T * k, E, offsets, sorted_rows, sm);
-}
-
 size_t moe_route_workspace_bytes(int, int, int) { return 0; }
 
 dg_status launch_moe_route(const float* logits, int T, int E, int k, int32_t* topk_ids,
                            float* gates, int32_t* offsets, int32_t* sorted_rows, void*,
                            hipStream_t stream) {
-  if (static_cast<int64_t>(T) * k <= kFusedRouteSlots) {
-    route_fused_kernel<<<1, 1024, 0, stream>>>(logits, T, E, k, topk_ids, gates, offsets,
-                                               sorted_rows);
-    DG_LAUNCH_CHECK();
-    return DG_OK;
-  }
   route_topk_kernel<<<(T + 3) / 4, 64, 0, stream>>>(logits, T, E, k, topk_ids, gates);
   DG_LAUNCH_CHECK();
   route_sort_kernel<<<1, 1024, 0, stream>>>(topk_ids, T * k, E, offsets, sorted_rows);
