@@ -76,27 +76,67 @@ __global__ __launch_bounds__(64) void route_topk_kernel(const float* __restrict_
 }
 
 // Stable counting sort of the n = T * k slot entries by expert, by one
-// 1024-thread workgroup: histogram, exclusive scan -> expert_offsets, then
-// chunks of 1024 slots scattered with ballot-based ranks (deterministic).
+// 1024-thread workgroup.  Wave w owns the contiguous range of entries
+// [w R, (w + 1) R), R = ceil(n / 16), and walks it in chunks of 64 twice:
+// first counting its entries per expert, then -- after the counts are turned
+// into each (wave, expert)'s first output position (experts ascending, waves
+// ascending within an expert) -- placing every entry at that position plus
+// its rank among the same expert's entries of the chunk (ballot-based).  Waves
+// own ascending ranges and walk them in order, so equal experts keep the
+// entry order t * k + j: the result is unique (deterministic).  Three barriers
+// in all (the previous form took five per chunk of 1024 entries).
 struct SortSmem {
-  int count[256];
-  int base[256];          // running start of each expert
-  int wave_cnt[16][256];  // per-wave counts in the current chunk
+  int cnt[16][256];       // per wave: entries per expert, then the running position
 };
+
+// Lanes of this wave whose expert equals mine (empty for an inactive lane).
+__device__ __forceinline__ uint64_t same_expert_lanes(int e, bool active) {
+  uint64_t same = __ballot(active);
+#pragma unroll
+  for (int bit = 0; bit < 8; ++bit) {
+    const uint64_t bal = __ballot(active && ((e >> bit) & 1));
+    same &= ((e >> bit) & 1) ? bal : ~bal;
+  }
+  return active ? same : 0ull;
+}
 
 __device__ void sort_slots(const int* ids, int n, int E, int32_t* __restrict__ offsets,
                            int32_t* __restrict__ sorted_rows, SortSmem& sm) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (tid < 256) sm.count[tid] = 0;
+  for (int q = tid; q < 16 * 256; q += 1024) (&sm.cnt[0][0])[q] = 0;
   __syncthreads();
-  for (int i = tid; i < n; i += 1024) atomicAdd(&sm.count[ids[i]], 1);
+  const int R = (n + 15) / 16;
+  const int r0 = wave * R, r1 = min(n, r0 + R);
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  // pass 1: per-wave counts (one leader lane per distinct expert of a chunk)
+  for (int c0 = r0; c0 < r1; c0 += 64) {
+    const int i = c0 + lane;
+    const bool act = i < r1;
+    const int e = act ? ids[i] : 0;
+    const uint64_t same = same_expert_lanes(e, act);
+    if (act && __popcll(same & below) == 0) sm.cnt[wave][e] += __popcll(same);
+  }
   __syncthreads();
-  if (wave == 0) {                       // exclusive scan over E <= 256: 4 per lane
+  // positions: thread e < E turns its column into exclusive prefixes over the
+  // waves; wave 0 then scans the experts' totals (4 per lane)
+  int total = 0;
+  if (tid < E) {
+#pragma unroll
+    for (int w = 0; w < 16; ++w) {
+      const int c = sm.cnt[w][tid];
+      sm.cnt[w][tid] = total;
+      total += c;
+    }
+  }
+  __shared__ int s_total[256];
+  if (tid < 256) s_total[tid] = tid < E ? total : 0;
+  __syncthreads();
+  __shared__ int s_off[256];
+  if (wave == 0) {
     int c[4], sum = 0;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int e = lane * 4 + q;
-      c[q] = e < E ? sm.count[e] : 0;
+      c[q] = s_total[lane * 4 + q];
       sum += c[q];
     }
     int incl = sum;
@@ -109,40 +149,24 @@ __device__ void sort_slots(const int* ids, int n, int E, int32_t* __restrict__ o
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int e = lane * 4 + q;
-      if (e < E) { sm.base[e] = run; offsets[e] = run; }
+      if (e < E) { s_off[e] = run; offsets[e] = run; }
       run += c[q];
     }
     if (lane == 63) offsets[E] = incl;
   }
   __syncthreads();
-  for (int c0 = 0; c0 < n; c0 += 1024) {
-    const int i = c0 + tid;
-    const int e = i < n ? ids[i] : -1;
-    // lanes of this wave with the same expert
-    uint64_t same = __ballot(i < n);
-#pragma unroll
-    for (int bit = 0; bit < 8; ++bit) {
-      const uint64_t bal = __ballot(e >= 0 && ((e >> bit) & 1));
-      same &= ((e >> bit) & 1) ? bal : ~bal;
-    }
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    const int rank_in_wave = __popcll(same & below);
-    for (int q = tid; q < 16 * 256; q += 1024) (&sm.wave_cnt[0][0])[q] = 0;
-    __syncthreads();
-    if (e >= 0 && rank_in_wave == 0) sm.wave_cnt[wave][e] = __popcll(same);
-    __syncthreads();
-    if (e >= 0) {
-      int before = 0;
-      for (int w = 0; w < wave; ++w) before += sm.wave_cnt[w][e];
-      sorted_rows[sm.base[e] + before + rank_in_wave] = i;
-    }
-    __syncthreads();
-    if (tid < E) {
-      int tot = 0;
-      for (int w = 0; w < 16; ++w) tot += sm.wave_cnt[w][tid];
-      sm.base[tid] += tot;
-    }
-    __syncthreads();
+  // pass 2: place the entries; the chunk's leader of each expert then moves
+  // the wave's running position past the chunk's entries of that expert
+  // (one wave's LDS accesses complete in issue order)
+  for (int c0 = r0; c0 < r1; c0 += 64) {
+    const int i = c0 + lane;
+    const bool act = i < r1;
+    const int e = act ? ids[i] : 0;
+    const uint64_t same = same_expert_lanes(e, act);
+    const int rank = __popcll(same & below);
+    const int pos = act ? s_off[e] + sm.cnt[wave][e] + rank : 0;
+    if (act) sorted_rows[pos] = i;
+    if (act && rank == 0) sm.cnt[wave][e] += __popcll(same);
   }
 }
 
