@@ -232,8 +232,8 @@ def moe_roofline(model_w, d, B, reps=20, mxfp4=False):
                  + slots * d.D * 2 * 2 + T * d.D * 4 * 2 + slots * 4)
     fmt = "MXFP4" if mxfp4 else "fp8"
     # the library's dispatch: one-wave items up to 40 slots per expert on
-    # average (always for MXFP4), LDS-staged 64-token tiles above
-    kname = "gemm_wave_kernel" if (mxfp4 or slots <= 40 * d.E) else "gemm_stream_kernel"
+    # average, LDS-staged 64-token tiles above
+    kname = "gemm_wave_kernel" if slots <= 40 * d.E else "gemm_stream_kernel"
     return dict(kernel=(f"{kname} (dg_moe_gate_up): experts of layer {layer}, {T} "
                         f"tokens, {fmt} tiled weights, planted routing (all 128 experts active)"),
                 ms=ms_gu, algo_bytes=gu_bytes, gbs=gu_bytes / (ms_gu * 1e-3) / 1e9,

@@ -396,7 +396,7 @@ static void launch_gemm_bf16(GemmArgs& g, int M, int N, int K, hipStream_t strea
     g.n_tiles_x = N / (64 * kWideRT);
     g.n_tiles_y = (M + 16 * kWideTB - 1) / (16 * kWideTB);
     g.n_tiles_total = g.n_tiles_x * g.n_tiles_y;
-    gemm_stream_kernel<kWideRT, kWideTB, kWideKS, kWidePF, false, kDense, TILED>
+    gemm_stream_kernel<kWideRT, kWideTB, kWideKS, kWidePF, kWBf16, kDense, TILED>
         <<<(g.n_tiles_total + 7) / 8 * 8, 256, 0, stream>>>(g);
   } else if (K % 64 == 0 && K >= 64 * 8 && N % (16 * kProjRT) == 0 && N % 32 == 0) {
     // narrow outputs, or a handful of tokens (AR decode): more, smaller tiles
@@ -418,7 +418,7 @@ static void launch_gemm_bf16(GemmArgs& g, int M, int N, int K, hipStream_t strea
     g.n_tiles_x = N / (64 * kDenseRT);
     g.n_tiles_y = (M + 16 * kDenseTB - 1) / (16 * kDenseTB);
     g.n_tiles_total = g.n_tiles_x * g.n_tiles_y;
-    gemm_stream_kernel<kDenseRT, kDenseTB, kDenseKS, kDensePF, false, kDense, TILED>
+    gemm_stream_kernel<kDenseRT, kDenseTB, kDenseKS, kDensePF, kWBf16, kDense, TILED>
         <<<(g.n_tiles_total + 7) / 8 * 8, 256, 0, stream>>>(g);
   }
 }

@@ -180,9 +180,10 @@ struct WRow {
   __device__ const WT* at(int c) const { return base + c * cstride; }
 };
 
-template <int RT, int TB, int KS, int PF, bool FP8, int MODE, bool TILED>
+template <int RT, int TB, int KS, int PF, int WF, int MODE, bool TILED>
 __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
-  using WT = typename std::conditional<FP8, uint8_t, bf16_t>::type;
+  static_assert(WF != kWMx4 || TILED, "MXFP4 weights are always tile-packed");
+  using WT = typename std::conditional<WF == kWBf16, bf16_t, uint8_t>::type;
   constexpr int MT = 16 * TB;           // tokens per tile
   constexpr int SK = 64 * KS;           // k per LDS stage
   constexpr int XS = SK + 8;            // LDS row stride (elements)
@@ -266,20 +267,40 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
                                        : tx * (64 * RT) + wave * (16 * RT) + rt * 16;
     wr_at[rt].init(Wg, row0, a.K, lane, a);
   }
+  // MXFP4: tile blocks of 544 bytes (a tile's chunks contiguous); the lane's
+  // 8 code bytes at 8 lane, the scale of its 32-k half at 512 + 16 (g4 / 2) + r
+  const uint8_t* mx_codes[RT];
+  const uint8_t* mx_scale[RT];
+  if constexpr (WF == kWMx4) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const int row0 = (MODE == kGateUp) ? (rt == 0 ? 0 : a.N / 2) + tx * 64 + wave * 16
+                                         : tx * (64 * RT) + wave * (16 * RT) + rt * 16;
+      const uint8_t* tile = reinterpret_cast<const uint8_t*>(Wg) +
+                            static_cast<int64_t>(row0 / 16) * (a.K / 64) * kMx4Block;
+      mx_codes[rt] = tile + lane * 8;
+      mx_scale[rt] = tile + 512 + 16 * (g4 >> 1) + l16;
+    }
+  }
+  auto load_chunk = [&](WChunk<WF>& w, int rt, int c) {
+    if constexpr (WF == kWMx4)
+      w.load_mx(mx_codes[rt] + c * kMx4Block, mx_scale[rt] + c * kMx4Block);
+    else
+      w.template load<WRow<WT, TILED>::kSecond>(wr_at[rt].at(c));
+  };
   const int nchunks = (a.K + 63) / 64;
   const int nstages = (nchunks + KS - 1) / KS;
 
   // weight ring: PF stages of KS chunks in flight per wave
-  WChunk<FP8 ? kWFp8 : kWBf16> wr[PF][KS][RT];
+  WChunk<WF> wr[PF][KS][RT];
   // unconditional loads (clamped chunk; rows are in range by contract) keep
   // the compiler's memory-counter waits precise
-  auto load_w = [&](int stage, WChunk<FP8 ? kWFp8 : kWBf16> (&slot)[KS][RT]) {
+  auto load_w = [&](int stage, WChunk<WF> (&slot)[KS][RT]) {
 #pragma unroll
     for (int j = 0; j < KS; ++j) {
       const int c = min(stage * KS + j, nchunks - 1);
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
-        slot[j][rt].template load<WRow<WT, TILED>::kSecond>(wr_at[rt].at(c));
+      for (int rt = 0; rt < RT; ++rt) load_chunk(slot[j][rt], rt, c);
     }
   };
   // token rows: a stage of MT rows x SK k of bf16 = PIECES 16-byte pieces,
@@ -342,8 +363,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
         for (int rt = 0; rt < RT; ++rt) wr[p][j][rt].get(wa[rt][0], wa[rt][1]);
         const int c = min((s + PF) * KS + j, nchunks - 1);
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-          wr[p][j][rt].template load<WRow<WT, TILED>::kSecond>(wr_at[rt].at(c));
+        for (int rt = 0; rt < RT; ++rt) load_chunk(wr[p][j][rt], rt, c);
         if (s * KS + j >= nchunks) continue;
 #pragma unroll
         for (int tb = 0; tb < TB; ++tb) {

@@ -338,22 +338,22 @@ static void launch_gate_up_mfma(const void* x, const void* wgu, const float* sgu
   g.offsets = offsets; g.sorted_rows = sorted_rows;
   g.out = h;
   // few tokens per expert (the canvas of one or two rows): one-wave items
-  // streaming registers; more: 64-token tiles staged through LDS (bf16 and
-  // fp8; MXFP4 keeps one-wave items of 32 tokens)
+  // streaming registers; more: 64-token tiles staged through LDS (every
+  // weight format)
   const int64_t slots = static_cast<int64_t>(T) * k;
   if (slots <= kTinySlots) {
     // a few tokens (AR decode): half-size items, twice as many waves
     launch_wave<1, WF, kGateUp, TILED, kTinyRT, kTinyNR>(g, T, k, E, stream);
   } else if (slots <= kGateTB1Slots * static_cast<int64_t>(E)) {
     launch_wave<1, WF, kGateUp, TILED>(g, T, k, E, stream);
-  } else if (slots <= 40ll * E || WF == kWMx4) {
+  } else if (slots <= 40ll * E) {
     launch_wave<2, WF, kGateUp, TILED>(g, T, k, E, stream);
-  } else if constexpr (WF != kWMx4) {
+  } else {
     const int MT = 16 * kMoeTB;
     g.n_tiles_x = I / 64;
     g.n_tiles_y = E + static_cast<int>((slots + MT - 1) / MT);
     g.n_tiles_total = g.n_tiles_x * g.n_tiles_y;
-    gemm_stream_kernel<2, kMoeTB, kMoeKS, kMoePF, WF == kWFp8, kGateUp, TILED>
+    gemm_stream_kernel<2, kMoeTB, kMoeKS, kMoePF, WF, kGateUp, TILED>
         <<<(g.n_tiles_total + 7) / 8 * 8, 256, 0, stream>>>(g);
   }
 }
@@ -376,14 +376,12 @@ static void launch_down_mfma(const bf16_t* h, const void* wd, const float* sd, c
     launch_wave<1, WF, kDown, TILED, kTinyRT, kTinyNR>(d, T, k, E, stream);
   } else if (slots <= 40ll * E) {
     launch_wave<1, WF, kDown, TILED>(d, T, k, E, stream);
-  } else if constexpr (WF == kWMx4) {
-    launch_wave<2, WF, kDown, TILED>(d, T, k, E, stream);
   } else {
     const int MT = 16 * kMoeTB;
     d.n_tiles_x = D / 128;
     d.n_tiles_y = E + static_cast<int>((slots + MT - 1) / MT);
     d.n_tiles_total = d.n_tiles_x * d.n_tiles_y;
-    gemm_stream_kernel<2, kMoeTB, kMoeKS, kMoePF, WF == kWFp8, kDown, TILED>
+    gemm_stream_kernel<2, kMoeTB, kMoeKS, kMoePF, WF, kDown, TILED>
         <<<(d.n_tiles_total + 7) / 8 * 8, 256, 0, stream>>>(d);
   }
 }

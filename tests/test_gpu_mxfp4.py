@@ -100,7 +100,7 @@ def test_moe_ffn_mxfp4_full_size_bs1():
 @pytest.mark.parametrize("T", [512, 1024])
 def test_moe_ffn_mxfp4_full_size_sampled(T):
     """bs2 (32-token gate/up tiles) and bs4 (above 40 tokens per expert:
-    32-token tiles for both GEMMs)."""
+    LDS-staged 64-token tiles for both GEMMs)."""
     case = moe_case(T=T, w_dtype="mxfp4", seed=T)
     sample = np.random.default_rng(T).choice(T, 96, replace=False)
     err, _ = _ffn_case_mx4(case, 8, sample)
@@ -117,6 +117,14 @@ def test_moe_ffn_mxfp4_few_tokens(T):
 def test_moe_ffn_mxfp4_ragged_small():
     """Few tokens, experts with 0 and > 64 tokens, several row tiles."""
     case = moe_case(T=70, D=256, E=6, k=2, I=128, w_dtype="mxfp4", seed=5, skew=False)
+    err, _ = _ffn_case_mx4(case, 2)
+    assert err < TOL, err
+
+
+def test_moe_ffn_mxfp4_many_tokens_per_expert():
+    """Above 40 slots per expert (LDS-staged 64-token tiles) at small widths,
+    with ragged token tiles per expert."""
+    case = moe_case(T=400, D=256, E=6, k=2, I=128, w_dtype="mxfp4", seed=6, skew=False)
     err, _ = _ffn_case_mx4(case, 2)
     assert err < TOL, err
 
