@@ -109,10 +109,12 @@ __device__ void sort_slots(const int* ids, int n, int E, int32_t* __restrict__ o
   const int r0 = wave * R, r1 = min(n, r0 + R);
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   // pass 1: per-wave counts (one leader lane per distinct expert of a chunk)
+  // (ids are clamped to [0, E): an id out of range can only misplace entries,
+  // never address memory outside the tables)
   for (int c0 = r0; c0 < r1; c0 += 64) {
     const int i = c0 + lane;
     const bool act = i < r1;
-    const int e = act ? ids[i] : 0;
+    const int e = act ? min(max(ids[i], 0), E - 1) : 0;
     const uint64_t same = same_expert_lanes(e, act);
     if (act && __popcll(same & below) == 0) sm.cnt[wave][e] += __popcll(same);
   }
@@ -161,11 +163,11 @@ __device__ void sort_slots(const int* ids, int n, int E, int32_t* __restrict__ o
   for (int c0 = r0; c0 < r1; c0 += 64) {
     const int i = c0 + lane;
     const bool act = i < r1;
-    const int e = act ? ids[i] : 0;
+    const int e = act ? min(max(ids[i], 0), E - 1) : 0;
     const uint64_t same = same_expert_lanes(e, act);
     const int rank = __popcll(same & below);
     const int pos = act ? s_off[e] + sm.cnt[wave][e] + rank : 0;
-    if (act) sorted_rows[pos] = i;
+    if (act && pos < n) sorted_rows[pos] = i;
     if (act && rank == 0) sm.cnt[wave][e] += __popcll(same);
   }
 }
