@@ -183,8 +183,15 @@ __global__ __launch_bounds__(512) void gemm_wide_dl_kernel(const bf16_t* __restr
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g4 = lane >> 4;
   const int wr = wave & 1, wt = wave >> 1;
-  const int n0 = blockIdx.x * kWideRows;
-  const int m0 = blockIdx.y * kWideTok;
+  // logical tile: token tiles of one row tile adjacent, and each XCD a
+  // contiguous range, so the token tiles of a weight tile (more than 256
+  // tokens) read it into one L2 once
+  const int mt = (M + kWideTok - 1) / kWideTok;
+  const int total = (N / kWideRows) * mt;
+  const int logical = xcd_logical_tile(blockIdx.x, gridDim.x);
+  if (logical >= total) return;
+  const int n0 = (logical / mt) * kWideRows;
+  const int m0 = (logical % mt) * kWideTok;
   const int nchunks = K / 64;
   const bf16_t* wsrc = W + static_cast<int64_t>(n0 / 16) * (K / 64) * 1024;
 
@@ -386,8 +393,9 @@ static void launch_gemm_bf16(GemmArgs& g, int M, int N, int K, hipStream_t strea
       smem_set = true;
     }
     dim3 grid(N / kWideRows, (M + kWideTok - 1) / kWideTok);
+    const unsigned dl_grid = (grid.x * grid.y + 7) / 8 * 8;
     if (kWideDirectLds)
-      gemm_wide_dl_kernel<<<grid, 512, kDlSmemBytes, stream>>>(
+      gemm_wide_dl_kernel<<<dl_grid, 512, kDlSmemBytes, stream>>>(
           static_cast<const bf16_t*>(g.W), g.X, static_cast<bf16_t*>(g.out), M, N, K);
     else
       gemm_wide_kernel<<<grid, 512, kWideSmemBytes, stream>>>(
