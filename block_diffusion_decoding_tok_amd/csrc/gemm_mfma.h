@@ -648,19 +648,49 @@ __global__ __launch_bounds__(64, WPE) void gemm_wave_kernel(GemmArgs a) {
         pk.y = pack_bf16x2(hv[2], hv[3]);
         *reinterpret_cast<uint2*>(static_cast<bf16_t*>(a.out) + static_cast<int64_t>(p_pos[tb]) * I + n) = pk;
       }
-    } else {
-      const int slot = a.sorted_rows[p_pos[tb]];
-      const float g = a.gates[slot];
+    }
+  }
+  if constexpr (MODE == kDown) {
+    // The item's 16 TB slot rows x 16 RT columns go through LDS, so that the
+    // stores leave as runs of 32 RT bytes per slot row (16 bytes per lane)
+    // instead of 8-byte pieces: first each lane puts its gate- and
+    // scale-weighted values of token l16 (rows 4 g4 .. 4 g4 + 3 of every
+    // tile) into row tb * 16 + l16; then lane l copies 16-byte pieces.
+    constexpr int NC = 16 * RT;              // columns of the item
+    constexpr int YS = NC + 8;               // LDS row stride (elements)
+    __shared__ __attribute__((aligned(16))) bf16_t s_y[16 * TB * YS];
+    __shared__ int s_slot[16 * TB];
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+      const int row = tb * 16 + l16;
+      const int slot = xok[tb] ? a.sorted_rows[p_pos[tb]] : -1;
+      const float g = xok[tb] ? a.gates[slot] : 0.f;
+      if (g4 == 0) s_slot[row] = slot;
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
-        const int n = tx * (16 * RT) + rt * 16 + g4 * 4;
+        const int n = tx * NC + rt * 16 + g4 * 4;
         float v[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) v[r] = g * acc[rt][tb][r] * (sc ? sc[n + r] : 1.f);
         uint2 pk;
         pk.x = pack_bf16x2(v[0], v[1]);
         pk.y = pack_bf16x2(v[2], v[3]);
-        *reinterpret_cast<uint2*>(static_cast<bf16_t*>(a.out) + static_cast<int64_t>(slot) * a.N + n) = pk;
+        *reinterpret_cast<uint2*>(&s_y[row * YS + rt * 16 + g4 * 4]) = pk;
+      }
+    }
+    __syncthreads();                         // one wave: orders the LDS writes and reads
+    constexpr int PR = NC / 8;               // 16-byte pieces per row
+    constexpr int PIECES = 16 * TB * PR;
+#pragma unroll
+    for (int it = 0; it < (PIECES + 63) / 64; ++it) {
+      const int q = it * 64 + lane;
+      if (q < PIECES) {
+        const int row = q / PR, c8 = q % PR;
+        const int slot = s_slot[row];
+        const uint4 v = *reinterpret_cast<const uint4*>(&s_y[row * YS + c8 * 8]);
+        if (slot >= 0)
+          *reinterpret_cast<uint4*>(static_cast<bf16_t*>(a.out) + static_cast<int64_t>(slot) * a.N +
+                                    tx * NC + c8 * 8) = v;
       }
     }
   }
