@@ -629,14 +629,20 @@ __global__ __launch_bounds__(64, WPE) void gemm_wave_kernel(GemmArgs a) {
   // ---- epilogue (lane: rows 4 g4 + r of each 16-row tile, token l16 of
   // each 16-token block)
   const float* sc = a.w_scale ? a.w_scale + static_cast<int64_t>(grp) * a.s_group_stride : nullptr;
+  if constexpr (MODE == kGateUp) {
+    // h = GELU(gate) * up for the item's 16 TB sorted positions (consecutive
+    // rows of h) x 8 RT columns, staged through LDS like the down epilogue
+    // below so that each row leaves as one run of 16 RT bytes
+    const int I = a.N / 2;
+    constexpr int NC = 8 * RT;               // columns of the item
+    constexpr int HS = NC + 8;               // LDS row stride (elements)
+    __shared__ __attribute__((aligned(16))) bf16_t s_h[16 * TB * HS];
 #pragma unroll
-  for (int tb = 0; tb < TB; ++tb) {
-    if (!xok[tb]) continue;
-    if (MODE == kGateUp) {
-      const int I = a.N / 2;
+    for (int tb = 0; tb < TB; ++tb) {
+      const int row = tb * 16 + l16;
 #pragma unroll
       for (int i = 0; i < RT / 2; ++i) {
-        const int n = tx * (8 * RT) + i * 16 + g4 * 4;
+        const int n = tx * NC + i * 16 + g4 * 4;
         float hv[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -646,7 +652,20 @@ __global__ __launch_bounds__(64, WPE) void gemm_wave_kernel(GemmArgs a) {
         uint2 pk;
         pk.x = pack_bf16x2(hv[0], hv[1]);
         pk.y = pack_bf16x2(hv[2], hv[3]);
-        *reinterpret_cast<uint2*>(static_cast<bf16_t*>(a.out) + static_cast<int64_t>(p_pos[tb]) * I + n) = pk;
+        *reinterpret_cast<uint2*>(&s_h[row * HS + i * 16 + g4 * 4]) = pk;
+      }
+    }
+    __syncthreads();                         // one wave: orders the LDS writes and reads
+    constexpr int PR = NC / 8;               // 16-byte pieces per row
+    constexpr int PIECES = 16 * TB * PR;
+#pragma unroll
+    for (int it = 0; it < (PIECES + 63) / 64; ++it) {
+      const int q = it * 64 + lane;
+      const int row = q / PR, c8 = q % PR;
+      if (q < PIECES && row < m_count) {
+        const uint4 v = *reinterpret_cast<const uint4*>(&s_h[row * HS + c8 * 8]);
+        *reinterpret_cast<uint4*>(static_cast<bf16_t*>(a.out) +
+                                  static_cast<int64_t>(base_pos + m0 + row) * I + tx * NC + c8 * 8) = v;
       }
     }
   }
