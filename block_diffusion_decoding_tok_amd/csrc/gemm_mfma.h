@@ -384,6 +384,61 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
 
   // ---- epilogue: lane holds rows 4 g4 + r of each 16-row tile, token l16
   const float* sc = a.w_scale ? a.w_scale + static_cast<int64_t>(grp) * a.s_group_stride : nullptr;
+  if constexpr (MODE != kDense) {
+    // expert modes: the workgroup's MT rows x NC columns go through LDS (the
+    // token stages are free once every wave is past the last one), so that
+    // each destination row leaves as one run of 16-byte pieces
+    constexpr int NC = MODE == kGateUp ? 64 : 64 * RT;
+    constexpr int OS = NC + 8;
+    static_assert(MT * OS <= 2 * MT * XS, "output tile fits the token stages");
+    bf16_t* s_o = &s_x[0][0];
+    const int I = a.N / 2;
+    __syncthreads();
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+      const int t = tb * 16 + l16;
+      if (MODE == kGateUp) {
+        const int n = tx * 64 + wave * 16 + g4 * 4;
+        float hv[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float sg = sc ? sc[n + r] : 1.f, su = sc ? sc[I + n + r] : 1.f;
+          hv[r] = gelu_erf(acc[0][tb][r] * sg) * (acc[1][tb][r] * su);
+        }
+        uint2 pk;
+        pk.x = pack_bf16x2(hv[0], hv[1]);
+        pk.y = pack_bf16x2(hv[2], hv[3]);
+        *reinterpret_cast<uint2*>(&s_o[t * OS + wave * 16 + g4 * 4]) = pk;
+      } else {
+        const float g = t < m_count ? a.gates[s_dst[t]] : 0.f;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          const int nl = wave * (16 * RT) + rt * 16 + g4 * 4;
+          const int n = tx * NC + nl;
+          float v[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[r] = g * acc[rt][tb][r] * (sc ? sc[n + r] : 1.f);
+          uint2 pk;
+          pk.x = pack_bf16x2(v[0], v[1]);
+          pk.y = pack_bf16x2(v[2], v[3]);
+          *reinterpret_cast<uint2*>(&s_o[t * OS + nl]) = pk;
+        }
+      }
+    }
+    __syncthreads();
+    constexpr int PR = NC / 8;               // 16-byte pieces per row
+    const int ld = MODE == kGateUp ? I : a.N;
+#pragma unroll
+    for (int it = 0; it < (MT * PR + 255) / 256; ++it) {
+      const int q = it * 256 + tid;
+      const int row = q / PR, c8 = q % PR;
+      if (q < MT * PR && row < m_count)
+        *reinterpret_cast<uint4*>(static_cast<bf16_t*>(a.out) + static_cast<int64_t>(s_dst[row]) * ld +
+                                  tx * NC + c8 * 8) =
+            *reinterpret_cast<const uint4*>(&s_o[row * OS + c8 * 8]);
+    }
+    return;
+  }
 #pragma unroll
   for (int tb = 0; tb < TB; ++tb) {
     const int t = tb * 16 + l16;
