@@ -131,6 +131,17 @@ def test_moe_ffn_ragged_small(w_dtype, tiled):
     assert err < TOL[w_dtype], err
 
 
+@pytest.mark.parametrize("w_dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("T", [30, 200])
+def test_moe_ffn_single_expert_tiled(w_dtype, T):
+    """One expert (a stack of one matrix keeps each tile's chunks together,
+    unlike a stack of several): one-wave items at 30 slots, LDS-staged tiles
+    at 200."""
+    case = moe_case(T=T, D=256, E=1, k=1, I=128, w_dtype=w_dtype, seed=70 + T, skew=False)
+    err, _ = _ffn_case(case, 1, tiled=True)
+    assert err < TOL[w_dtype], err
+
+
 @pytest.mark.parametrize("tiled", [False, True])
 def test_moe_ffn_many_tokens_per_expert(tiled):
     """Above 40 tokens per expert the LDS-staged 64-token tiles take over."""
