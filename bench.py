@@ -448,18 +448,27 @@ def main():
             for _ in range(nb):
                 dg.dg_denoise_block(m, c, B, kc, vc, Pd, tok, steps_taken)
 
+        block_ms = []     # device time of each block of the last timed() call
+
         def timed(nb, c, m=model):
-            """Warm up (captures the graph), rewind, time nb blocks."""
+            """Warm up (captures the graph), rewind, time nb blocks (host clock
+            around all of them; HIP events on the bench stream between blocks
+            give each block's device time)."""
             run_blocks(max(1, a.warmup // a.block_steps), c, m)
             stream.synchronize()
             Pd.fill_(PROMPT)
             stream.synchronize()
             torch.cuda.synchronize()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(nb + 1)]
             t0 = time.perf_counter()
-            run_blocks(nb, c, m)
+            ev[0].record(stream)
+            for i in range(nb):
+                run_blocks(1, c, m)
+                ev[i + 1].record(stream)
             stream.synchronize()
             torch.cuda.synchronize()
             el = time.perf_counter() - t0
+            block_ms[:] = [ev[i].elapsed_time(ev[i + 1]) for i in range(nb)]
             assert Pd.cpu().tolist() == [PROMPT + CANVAS * nb] * B
             assert steps_taken.cpu().tolist() == [a.block_steps if c is cfg else 48] * B
             Pd.fill_(PROMPT)
@@ -473,6 +482,7 @@ def main():
         # the stated routing: N(0,1) + planted skew, every expert active
         model.set_router_override(planted_router_logits(d, CANVAS * B))
         elapsed = timed(n_blocks, cfg)
+        planted_block_ms = list(block_ms)
         # the prompt prefill itself (causal, chunks of 256 tokens, all 30
         # layers): re-encode the same prompt from position 0, timed
         prefill_s = None
@@ -579,6 +589,11 @@ def main():
                    "block_steps": a.block_steps, "parallelism": "single GPU"},
         "canvas_tok_per_s": round(steps_per_s * CANVAS * B, 1),
         "tok_per_s_at_block_steps": round(n_blocks * CANVAS * B / elapsed, 1),
+        # each timed block's device time (HIP events on the bench stream; the
+        # block's steps and its commit), over the n blocks of the run
+        "block_ms": {"n": len(planted_block_ms), "min": round(min(planted_block_ms), 3),
+                     "median": round(float(np.median(planted_block_ms)), 3),
+                     "max": round(max(planted_block_ms), 3)},
     }
     if elapsed_natural is not None:
         out["natural_routing"] = {
