@@ -27,17 +27,19 @@ namespace dg {
 // sl + 16, ... (E <= 256); each of the k rounds takes the group-wide
 // (logit desc, id asc) maximum of the experts not yet taken (four DPP
 // steps).  Lane j < k of the group writes slot j: its id and its gate, the
-// softmax of the k selected logits (sum in slot order).
+// softmax of the k selected logits (sum in slot order).  QN = 16-lane rows of
+// experts held per lane: 8 for E <= 128, else 16.
+template <int QN>
 __device__ __forceinline__ void route_topk_group(const float* row, int t, int E, int k, int sl,
                                                  int32_t* __restrict__ ids,
                                                  float* __restrict__ gates) {
-  // the token's E logits at row (global or LDS); all 16 loads issued
+  // the token's E logits at row (global or LDS); all QN loads issued
   // unconditionally (clamped), masked afterwards
-  float v[16];
+  float v[QN];
 #pragma unroll
-  for (int q = 0; q < 16; ++q) v[q] = row[min(q * 16 + sl, E - 1)];
+  for (int q = 0; q < QN; ++q) v[q] = row[min(q * 16 + sl, E - 1)];
 #pragma unroll
-  for (int q = 0; q < 16; ++q)
+  for (int q = 0; q < QN; ++q)
     if (q * 16 + sl >= E) v[q] = -INFINITY;
   uint32_t taken = 0;
   float my_val = 0.f, best0 = 0.f, z = 0.f;
@@ -46,7 +48,7 @@ __device__ __forceinline__ void route_topk_group(const float* row, int t, int E,
     float best = -INFINITY;
     int bid = 0x7fffffff;
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {    // branch-free: compares and selects
+    for (int q = 0; q < QN; ++q) {    // branch-free: compares and selects
       const int e = q * 16 + sl;
       const bool ok = (e < E) & !((taken >> q) & 1u);
       const bool better = ok & ((v[q] > best) | ((v[q] == best) & (e < bid)));
@@ -67,12 +69,14 @@ __device__ __forceinline__ void route_topk_group(const float* row, int t, int E,
 
 // Four tokens per one-wave workgroup (spread over many CUs: the rounds are
 // latency-bound).
+template <int QN>
 __global__ __launch_bounds__(64) void route_topk_kernel(const float* __restrict__ logits, int T,
                                                         int E, int k, int32_t* __restrict__ ids,
                                                         float* __restrict__ gates) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 4);
   if (t >= T) return;
-  route_topk_group(logits + static_cast<int64_t>(t) * E, t, E, k, threadIdx.x & 15, ids, gates);
+  route_topk_group<QN>(logits + static_cast<int64_t>(t) * E, t, E, k, threadIdx.x & 15, ids,
+                       gates);
 }
 
 // Stable counting sort of the n = T * k slot entries by expert, by one
@@ -184,7 +188,10 @@ size_t moe_route_workspace_bytes(int, int, int) { return 0; }
 dg_status launch_moe_route(const float* logits, int T, int E, int k, int32_t* topk_ids,
                            float* gates, int32_t* offsets, int32_t* sorted_rows, void*,
                            hipStream_t stream) {
-  route_topk_kernel<<<(T + 3) / 4, 64, 0, stream>>>(logits, T, E, k, topk_ids, gates);
+  if (E <= 128)
+    route_topk_kernel<8><<<(T + 3) / 4, 64, 0, stream>>>(logits, T, E, k, topk_ids, gates);
+  else
+    route_topk_kernel<16><<<(T + 3) / 4, 64, 0, stream>>>(logits, T, E, k, topk_ids, gates);
   DG_LAUNCH_CHECK();
   route_sort_kernel<<<1, 1024, 0, stream>>>(topk_ids, T * k, E, offsets, sorted_rows);
   DG_LAUNCH_CHECK();
