@@ -49,9 +49,12 @@ pin say "parity unpinned" in their docstring.  Current status:
   moe_route       pinned: brute-force stable sort, gate sums, k = E dense mix.
   moe_ffn         pinned: dense masked every-expert sum, E = k = 1 textbook FFN,
                   token permutation equivariance, torch float8_e4m3fn decode.
-  model forward   composed from the pinned pieces; the tiny-loop scenario is
-                  pinned by its own invariants (re-noise every step at random
-                  weights; planted commits; adaptive stop).
+  model forward   pinned: an independently composed float64 torch layer
+                  (rms_norm, SDPA with repeated KV heads, complex-rotation
+                  RoPE, topk, erf GELU) at 1e-12; zero-sublayer closed forms
+                  (identity; x + o Wo^T).  The tiny-loop scenario is pinned by
+                  its own invariants (re-noise every step at random weights;
+                  planted commits; adaptive stop).
   mxfp4           pinned: torch's e4m3fn and e8m0 decoders on the same bit
                   fields, worked round-to-nearest-even and saturation cases,
                   brute-force nearest value, exact round trips, error bound.

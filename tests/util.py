@@ -4,13 +4,8 @@ float64 model, and the comparison rules used by the parity tests."""
 import numpy as np
 import torch
 
-from oracle import TinyModel, fp8_e4m3fn_decode, dequantize_mxfp4
-
-
-def to_f64(t):
-    """Exact float64 value of a host tensor (bf16 / f32 / e4m3fn bytes need a
-    scale, see ``expert_f64``)."""
-    return t.to(torch.float64).numpy()
+from oracle import fp8_e4m3fn_decode, dequantize_mxfp4
+from oracle.host_weights import ExpertWeights, oracle_model, to_f64  # noqa: F401
 
 
 def expert_f64(w, s):
@@ -19,20 +14,6 @@ def expert_f64(w, s):
     if w.dtype == torch.uint8:
         return fp8_e4m3fn_decode(w.numpy()) * s.to(torch.float64).numpy()[..., None]
     return to_f64(w)
-
-
-def oracle_model(dims, weights, layers=None):
-    nl = dims.NL if layers is None else layers
-    m = TinyModel(D=dims.D, Hq=dims.Hq, Hkv=dims.Hkv, dh=dims.dh, E=dims.E,
-                  k=dims.k, I=dims.I, V=dims.V, emb=to_f64(weights["emb"]),
-                  lm=to_f64(weights["lm"]))
-    for l in range(nl):
-        m.layers.append(dict(
-            wqkv=to_f64(weights[f"wqkv.{l}"]), wo=to_f64(weights[f"wo.{l}"]),
-            wr=to_f64(weights[f"wr.{l}"]),
-            w_gate_up=ExpertWeights(weights[f"wgu.{l}"], weights[f"sgu.{l}"]),
-            w_down=ExpertWeights(weights[f"wd.{l}"], weights[f"sd.{l}"])))
-    return m
 
 
 def empty_caches(dims, B, Tmax, layers=None):
@@ -97,21 +78,6 @@ def sampler_exclusions(ref, cfg, committed_before=None):
     return near_tau | near_tie | row[:, None], row
 
 
-class ExpertWeights:
-    """Per-expert float64 view of host expert weights (bf16/f32 values, or
-    e4m3fn bytes times per-row scales), dequantized one expert at a time so
-    the full tensor never exists in float64."""
-
-    def __init__(self, w, s=None):
-        self.w, self.s = w, s
-        self.shape = tuple(w.shape)
-
-    def __getitem__(self, e):
-        if self.w.dtype == torch.uint8:
-            return _FP8_TABLE[self.w[e].numpy()] * self.s[e].to(torch.float64).numpy()[:, None]
-        return to_f64(self.w[e])
-
-
 class Mx4ExpertWeights:
     """Per-expert float64 view of row-major MXFP4 expert weights: codes
     [E, N, K / 2] and E8M0 scales [E, N, K / 32] (uint8 tensors), decoded by
@@ -139,10 +105,6 @@ def pack_mxfp4_tiled(codes, scales):
     sb = s.reshape(G, N // 16, 16, K // 64, 2)               # g, t, r, c, h
     sb = sb.transpose(0, 1, 3, 4, 2).reshape(G, N // 16, K // 64, 32)
     return np.ascontiguousarray(np.concatenate([cb, sb], axis=-1)).reshape(-1)
-
-
-# value of every e4m3fn byte, from the oracle's decoder
-_FP8_TABLE = fp8_e4m3fn_decode(np.arange(256, dtype=np.uint8))
 
 
 def pack_tiled(w):
