@@ -68,6 +68,7 @@ __global__ __launch_bounds__(256) void rope_kernel(
   }
   const T* kt = k_new + static_cast<int64_t>(tok) * kv_stride;
   const T* vt = v_new + static_cast<int64_t>(tok) * kv_stride;
+  if (pos >= Tmax) return;             // past the cache: nothing is written
   for (int g = hl; g < Hkv; g += lanes) {
     const float x1 = Elem<T>::load(kt, g * dh + j), x2 = Elem<T>::load(kt, g * dh + j + half);
     const int64_t o = ((static_cast<int64_t>(b) * Hkv + g) * Tmax + pos) * dh;
@@ -186,7 +187,7 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(
   const int l16 = lane & 15, g4 = lane >> 4;
   const int rg = wave & 3, kh = wave >> 2;          // row group, key half
   const int P = prefix_len[b];
-  const int n_keys = P + Lq;
+  const int n_keys = min(P + Lq, Tmax);             // never read past the cache
   const int row0 = tile * kAttnRows + rg * 32;      // this wave's first packed row
 
   // key range of this split: the row's keys [0, P + Lq) dealt out evenly in
@@ -459,7 +460,7 @@ __global__ void attn_f32_kernel(const float* __restrict__ qrot, const float* __r
   const int rows_total = Lq * G;
   const int tok = r / G;
   const int P = prefix_len[b];
-  const int n_keys = causal ? P + tok + 1 : P + Lq;
+  const int n_keys = min(causal ? P + tok + 1 : P + Lq, Tmax);   // never past the cache
   const float* qr = qrot + (static_cast<int64_t>(bh) * rows_total + r) * dh;
   const float q0 = lane < dh ? qr[lane] : 0.f;
   const float q1 = lane + 64 < dh ? qr[lane + 64] : 0.f;
@@ -537,13 +538,9 @@ dg_status launch_attention(const AttnArgs& a, void* ws, hipStream_t stream) {
     float* o_part = reinterpret_cast<float*>(w + p.q_bytes);
     AttnPartialML* ml = reinterpret_cast<AttnPartialML*>(w + p.q_bytes + p.o_bytes);
     const int total = p.tiles * p.nsplit * a.B * a.Hkv;
-    static bool smem_set = false;     // once per process (one device kernel)
-    if (!smem_set) {
-      DG_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(attn_mfma_kernel),
-                                 hipFuncAttributeMaxDynamicSharedMemorySize,
-                                 static_cast<int>(kAttnSmemBytes)));
-      smem_set = true;
-    }
+    dg_status lst = ensure_lds_limit(reinterpret_cast<const void*>(attn_mfma_kernel),
+                                     static_cast<int>(kAttnSmemBytes));
+    if (lst != DG_OK) return lst;
     attn_mfma_kernel<<<(total + 7) / 8 * 8, 512, kAttnSmemBytes, stream>>>(
         static_cast<const bf16_t*>(qrot), static_cast<const bf16_t*>(a.k_cache),
         static_cast<const bf16_t*>(a.v_cache), a.prefix_len, a.Lq, G, a.Hkv, a.Tmax, p.chunk,

@@ -27,6 +27,10 @@ dg_status fail(dg_status st, const std::string& msg);
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Raises a kernel's dynamic LDS limit to bytes on the current device, once
+// per (kernel, device); safe to call from several threads.
+dg_status ensure_lds_limit(const void* kernel, int bytes);
+
 // The tiled activation layout of a bf16 matrix [M, K] (K % 64 == 0) that the
 // dense projections can read: one 2 KB block per 16 tokens x 64 k, blocks in
 // (token block, k block) order, and inside a block the operand lane order of

@@ -275,7 +275,7 @@ __global__ __launch_bounds__(512) void gemm_wide_dl_kernel(const bf16_t* __restr
 }
 
 template <bool TILED>
-static void launch_gemm_bf16(GemmArgs& g, int M, int N, int K, hipStream_t stream);
+static dg_status launch_gemm_bf16(GemmArgs& g, int M, int N, int K, hipStream_t stream);
 
 dg_status launch_gemm(const void* A, const void* W, void* C, int M, int N, int K, int dtype,
                       int w_layout, int out_dtype, GemmEpilogue ep, hipStream_t stream) {
@@ -295,10 +295,9 @@ dg_status launch_gemm(const void* A, const void* W, void* C, int M, int N, int K
   g.out_dtype = ep == kAccumulateF32 ? DG_F32 : out_dtype;
   g.accumulate = ep == kAccumulateF32;
   g.y_fastest = 1;
-  if (w_layout == DG_LAYOUT_TILED)
-    launch_gemm_bf16<true>(g, M, N, K, stream);
-  else
-    launch_gemm_bf16<false>(g, M, N, K, stream);
+  const dg_status st = w_layout == DG_LAYOUT_TILED ? launch_gemm_bf16<true>(g, M, N, K, stream)
+                                                    : launch_gemm_bf16<false>(g, M, N, K, stream);
+  if (st != DG_OK) return st;
   DG_LAUNCH_CHECK();
   return DG_OK;
 }
@@ -376,22 +375,18 @@ dg_status launch_gemm_xt(const void* A, const void* W, void* C, int M, int N, in
 }
 
 template <bool TILED>
-static void launch_gemm_bf16(GemmArgs& g, int M, int N, int K, hipStream_t stream) {
+static dg_status launch_gemm_bf16(GemmArgs& g, int M, int N, int K, hipStream_t stream) {
   // wide outputs (the LM head) over many tokens: 256 x 256 tiles staged
   // through LDS; over a handful of tokens (AR decode) the split-K streaming
   // tiles below move the weights faster (6.0 against 3.7 TB/s at one token)
   if (TILED && M > 16 && N >= 32768 && N % kWideRows == 0 && K % 64 == 0 && !g.accumulate &&
       g.out_dtype == DG_BF16) {
-    static bool smem_set = false;      // once per process
-    if (!smem_set) {
-      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_wide_kernel),
-                                hipFuncAttributeMaxDynamicSharedMemorySize,
-                                static_cast<int>(kWideSmemBytes));
-      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_wide_dl_kernel),
-                                hipFuncAttributeMaxDynamicSharedMemorySize,
-                                static_cast<int>(kDlSmemBytes));
-      smem_set = true;
-    }
+    dg_status lst = ensure_lds_limit(reinterpret_cast<const void*>(gemm_wide_kernel),
+                                     static_cast<int>(kWideSmemBytes));
+    if (lst == DG_OK)
+      lst = ensure_lds_limit(reinterpret_cast<const void*>(gemm_wide_dl_kernel),
+                             static_cast<int>(kDlSmemBytes));
+    if (lst != DG_OK) return lst;
     dim3 grid(N / kWideRows, (M + kWideTok - 1) / kWideTok);
     const unsigned dl_grid = (grid.x * grid.y + 7) / 8 * 8;
     if (kWideDirectLds)
@@ -429,6 +424,7 @@ static void launch_gemm_bf16(GemmArgs& g, int M, int N, int K, hipStream_t strea
     gemm_stream_kernel<kDenseRT, kDenseTB, kDenseKS, kDensePF, kWBf16, kDense, TILED>
         <<<(g.n_tiles_total + 7) / 8 * 8, 256, 0, stream>>>(g);
   }
+  return DG_OK;
 }
 
 // One row per workgroup; the row stays in registers (float4 pieces) between

@@ -962,6 +962,7 @@ __global__ __launch_bounds__(64 * NW, WPE) void gemm_splitk_kernel(GemmArgs a) {
         const int d0 = (row16(rt) % 8) * 16 + (ql >> 4) * 4;  // < 64
         const int b = m / a.Lq, i = m % a.Lq;
         const int pos = a.prefix_len[b] + i;
+        if (head >= a.Hq && pos >= a.Tmax) continue;   // past the cache: not written
         float o1[4], o2[4];
         bf16_t* dst;
         if (head < a.Hq + a.Hkv) {

@@ -31,17 +31,20 @@ __global__ void copy_i32_kernel(const int32_t* s, int32_t* d, int n) {
 // written to tok[b] (the next step's input) and out[b * out_stride + col].
 // One 1024-thread workgroup per row; each thread takes 8 values per 16-byte
 // load, 8 loads in flight per batch (V % 8 == 0; bf16 or f32 logits).
+// A NaN or infinite logit sets DG_STATUS_NONFINITE_LOGITS in *status.
 template <typename T>
 __global__ __launch_bounds__(1024) void argmax_rows_kernel(const T* __restrict__ logits, int V,
                                                            int32_t* __restrict__ tok,
                                                            int32_t* __restrict__ out,
-                                                           int out_stride, int col) {
+                                                           int out_stride, int col,
+                                                           int32_t* __restrict__ status) {
   constexpr int PER = 16 / sizeof(T);   // values per 16-byte load
   const int b = blockIdx.x, tid = threadIdx.x;
   const T* row = logits + static_cast<int64_t>(b) * V;
   const int npieces = V / PER;
   float best = -INFINITY;
   int bid = 0x7fffffff;
+  bool finite = true;
   for (int p0 = tid; p0 < npieces; p0 += 1024 * 8) {
     uint4 u[8];
 #pragma unroll
@@ -56,6 +59,7 @@ __global__ __launch_bounds__(1024) void argmax_rows_kernel(const T* __restrict__
       for (int q = 0; q < PER; ++q) {
         const float x = Elem<T>::load(e, q);
         const int v = p * PER + q;
+        finite &= isfinite(x);
         const bool better = (x > best) | ((x == best) & (v < bid));
         best = better ? x : best;
         bid = better ? v : bid;
@@ -67,6 +71,7 @@ __global__ __launch_bounds__(1024) void argmax_rows_kernel(const T* __restrict__
     const int oi = __shfl_xor(bid, o);
     if (ob > best || (ob == best && oi < bid)) { best = ob; bid = oi; }
   }
+  const bool nonfinite = __syncthreads_or(!finite);
   __shared__ float s_best[16];
   __shared__ int s_id[16];
   if ((tid & 63) == 0) { s_best[tid >> 6] = best; s_id[tid >> 6] = bid; }
@@ -77,7 +82,17 @@ __global__ __launch_bounds__(1024) void argmax_rows_kernel(const T* __restrict__
     if (bid == 0x7fffffff) bid = 0;     // every logit NaN: id 0
     tok[b] = bid;
     out[static_cast<int64_t>(b) * out_stride + col] = bid;
+    if (nonfinite) atomicOr(status, DG_STATUS_NONFINITE_LOGITS);
   }
+}
+
+// Publishes the device status word of a block or AR run to the context's
+// host-visible word (pinned host memory): a non-zero status is stored there,
+// where the host finds it on a later call without synchronizing.
+__global__ void publish_status_kernel(const int32_t* __restrict__ status,
+                                      int32_t* __restrict__ host_word) {
+  const int32_t v = *status;
+  if (v) __hip_atomic_store(host_word, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
 static dg_status fill_i32(int32_t* p, int n, int v, hipStream_t s) {
@@ -137,6 +152,10 @@ struct dg_ctx {
   int32_t* active = nullptr;       // dg_generate: rows that have not met EOS
   int32_t* blk_tokens = nullptr;   // dg_generate: the current block's tokens [B, L]
   int32_t* blk_steps = nullptr;    // dg_generate: the current block's steps [B]
+  // host-visible status word (pinned host memory): the device stores a
+  // non-zero block status there; the host reads and clears it
+  int32_t* host_status = nullptr;
+  int32_t* host_status_dev = nullptr;    // its device-side address
   bool use_graphs = true;
   std::map<GraphKey, hipGraphExec_t> graphs;
   std::vector<const float*> router_override;   // empty: the model's own routing
@@ -377,6 +396,12 @@ dg_status forward(dg_ctx* c, const int32_t* tokens, int B, int n, int l0, int l1
   return DG_OK;
 }
 
+dg_status publish_status(dg_ctx* c, hipStream_t s) {
+  publish_status_kernel<<<1, 1, 0, s>>>(c->status, c->host_status_dev);
+  DG_LAUNCH_CHECK();
+  return DG_OK;
+}
+
 // A block in three pieces: begin (canvas init), steps [s0, s1) (forward +
 // LM head + sampler each), end (commit forward, prefix advance, tokens out).
 dg_status enqueue_block_begin(dg_ctx* c, const dg_sampler_cfg& cfg, int B,
@@ -419,7 +444,7 @@ dg_status enqueue_block_end(dg_ctx* c, const dg_sampler_cfg& cfg, int B, void* c
   if ((st = launch_advance_prefix(prefix_len, B, L, s))) return st;
   copy_i32_kernel<<<(B * L + 255) / 256, 256, 0, s>>>(c->tokens, tokens_out, B * L);
   DG_LAUNCH_CHECK();
-  return DG_OK;
+  return publish_status(c, s);
 }
 
 dg_status enqueue_block(dg_ctx* c, const dg_sampler_cfg& cfg, int B, void* const* kcs,
@@ -442,19 +467,33 @@ dg_status enqueue_ar(dg_ctx* c, int B, int n_steps, const int32_t* tokens_in, vo
   copy_i32_kernel<<<(B + 255) / 256, 256, 0, s>>>(tokens_in, c->tokens, B);
   DG_LAUNCH_CHECK();
   dg_status st;
+  if ((st = fill_i32(c->status, 1, 0, s))) return st;
   for (int step = 0; step < n_steps; ++step) {
     if ((st = forward(c, c->tokens, B, 1, 0, d.n_layers, kcs, vcs, Tmax, prefix_len,
                       DG_MASK_CAUSAL, c->logits, false, s)))
       return st;
     if (d.act_dtype == DG_BF16)
       argmax_rows_kernel<bf16_t><<<B, 1024, 0, s>>>(static_cast<const bf16_t*>(c->logits),
-                                                    d.vocab, c->tokens, tokens_out, n_steps, step);
+                                                    d.vocab, c->tokens, tokens_out, n_steps, step,
+                                                    c->status);
     else
       argmax_rows_kernel<float><<<B, 1024, 0, s>>>(static_cast<const float*>(c->logits), d.vocab,
-                                                   c->tokens, tokens_out, n_steps, step);
+                                                   c->tokens, tokens_out, n_steps, step,
+                                                   c->status);
     DG_LAUNCH_CHECK();
     if ((st = launch_advance_prefix(prefix_len, B, 1, s))) return st;
   }
+  return publish_status(c, s);
+}
+
+// Reports (and clears) a non-finite status the device stored in the
+// context's host word: DG_ERR_NONFINITE, else DG_OK.  No synchronization.
+dg_status take_status(dg_ctx* c, const char* fn) {
+  const int32_t v = __atomic_exchange_n(c->host_status, 0, __ATOMIC_ACQ_REL);
+  if (v & DG_STATUS_NONFINITE_LOGITS)
+    return fail(DG_ERR_NONFINITE, std::string(fn) +
+                                      ": non-finite logits (NaN or Inf) in a block or AR run "
+                                      "queued earlier on this context");
   return DG_OK;
 }
 
@@ -545,12 +584,15 @@ dg_status run_block(dg_ctx* c, const dg_sampler_cfg& cfg, int B, void* const* kc
     st = run_graph(c, key, s, [&](hipStream_t q) {
       dg_status r = DG_OK;
       if (s0 == 0 && (r = enqueue_block_begin(c, cfg, B, prefix_len, steps_taken, q))) return r;
-      return enqueue_block_steps(c, cfg, B, kcs, vcs, Tmax, prefix_len, steps_taken, s0, s1, q);
+      if ((r = enqueue_block_steps(c, cfg, B, kcs, vcs, Tmax, prefix_len, steps_taken, s0, s1, q)))
+        return r;
+      return publish_status(c, q);
     });
     if (st != DG_OK) return st;
     if (s1 == S) break;
     DG_HIP(hipMemcpyAsync(done.data(), c->done, B * sizeof(int32_t), hipMemcpyDeviceToHost, s));
     DG_HIP(hipStreamSynchronize(s));
+    if ((st = take_status(c, "dg_denoise_block"))) return st;
     bool all = true;
     for (int b = 0; b < B; ++b) all = all && done[b] != 0;
     if (all) break;
@@ -618,7 +660,20 @@ dg_status dg_ctx_create(dg_ctx** out, const dg_model_dims* dims, const dg_model_
   }
   const Layout L = layout(*dims, max_batch, max_tokens);
   if (!ws || ws_bytes < L.total) return fail(DG_ERR_WORKSPACE, "dg_ctx_create: workspace too small");
+  int32_t* host_word = nullptr;
+  DG_HIP(hipHostMalloc(reinterpret_cast<void**>(&host_word), sizeof(int32_t),
+                       hipHostMallocMapped | hipHostMallocCoherent));
+  *host_word = 0;
+  void* host_word_dev = nullptr;
+  const hipError_t he = hipHostGetDevicePointer(&host_word_dev, host_word, 0);
+  if (he != hipSuccess) {
+    (void)hipHostFree(host_word);
+    return fail(DG_ERR_HIP, std::string("dg_ctx_create: hipHostGetDevicePointer: ") +
+                                hipGetErrorString(he));
+  }
   dg_ctx* c = new dg_ctx();
+  c->host_status = host_word;
+  c->host_status_dev = static_cast<int32_t*>(host_word_dev);
   c->d = *dims;
   c->emb = w->emb;
   c->lm = w->lm_head;
@@ -665,8 +720,16 @@ dg_status dg_ctx_create(dg_ctx** out, const dg_model_dims* dims, const dg_model_
 dg_status dg_ctx_destroy(dg_ctx* ctx) {
   if (!ctx) return DG_OK;
   for (auto& kv : ctx->graphs) (void)hipGraphExecDestroy(kv.second);
+  if (ctx->host_status) (void)hipHostFree(ctx->host_status);
   delete ctx;
   return DG_OK;
+}
+
+dg_status dg_ctx_check_status(dg_ctx* ctx, void* stream) {
+  set_error("");
+  DG_CHECK_ARG(ctx != nullptr, "dg_ctx_check_status: ctx is null");
+  DG_HIP(hipStreamSynchronize(static_cast<hipStream_t>(stream)));
+  return take_status(ctx, "dg_ctx_check_status");
 }
 
 dg_status dg_ctx_set_graphs(dg_ctx* ctx, int use_graphs) {
@@ -749,6 +812,7 @@ dg_status dg_ar_decode(dg_ctx* ctx, int B, int n_steps, const int32_t* tokens_in
   DG_CHECK_SHAPE(ctx->d.vocab % 8 == 0, "dg_ar_decode: vocab must be a multiple of 8");
   dg_status st = check_run(ctx, B, 1, k_caches, v_caches, Tmax, prefix_len, "dg_ar_decode");
   if (st != DG_OK) return st;
+  if ((st = take_status(ctx, "dg_ar_decode"))) return st;
   // graph key: F = -1 marks the AR loop (block keys have F >= 0)
   GraphKey key{B, Tmax, 1, n_steps, -1, 0.f, 0.f, 0.f, 0.f, 0.f, 0, 0, 0.f, 0, {}};
   for (int l = 0; l < ctx->d.n_layers; ++l) {
@@ -774,6 +838,7 @@ dg_status dg_denoise_block(dg_ctx* ctx, const dg_sampler_cfg* cfg, int B, void* 
   st = check_run(ctx, B, cfg->canvas_len, k_caches, v_caches, Tmax, prefix_len,
                  "dg_denoise_block");
   if (st != DG_OK) return st;
+  if ((st = take_status(ctx, "dg_denoise_block"))) return st;
   return run_block(ctx, *cfg, B, k_caches, v_caches, Tmax, prefix_len, tokens_out, steps_taken,
                    static_cast<hipStream_t>(stream));
 }
@@ -788,6 +853,7 @@ dg_status dg_generate(dg_ctx* ctx, const dg_sampler_cfg* cfg, int B, void* const
   if (st != DG_OK) return st;
   st = check_run(ctx, B, cfg->canvas_len, k_caches, v_caches, Tmax, prefix_len, "dg_generate");
   if (st != DG_OK) return st;
+  if ((st = take_status(ctx, "dg_generate"))) return st;
   const int L = cfg->canvas_len;
   DG_CHECK_SHAPE(max_blocks >= 1 && static_cast<int64_t>(max_blocks) * L <= Tmax,
                  "dg_generate: need 1 <= max_blocks and max_blocks * L <= Tmax");
@@ -810,6 +876,7 @@ dg_status dg_generate(dg_ctx* ctx, const dg_sampler_cfg* cfg, int B, void* const
     DG_LAUNCH_CHECK();
     DG_HIP(hipMemcpyAsync(act.data(), ctx->active, B * sizeof(int32_t), hipMemcpyDeviceToHost, s));
     DG_HIP(hipStreamSynchronize(s));
+    if ((st = take_status(ctx, "dg_generate"))) return st;
     bool any = false;
     for (int b = 0; b < B; ++b) any = any || act[b] != 0;
     if (!any) break;

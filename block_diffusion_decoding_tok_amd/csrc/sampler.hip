@@ -396,12 +396,10 @@ dg_status launch_sampler(const void* logits, int logit_dtype, int B, int L, int 
   while (npow2 < L) npow2 <<= 1;
   const size_t smem = static_cast<size_t>(L) * (sizeof(double) + sizeof(int32_t) + 1) +
                       static_cast<size_t>(npow2) * (sizeof(double) + sizeof(int32_t));
-  static bool smem_set = false;        // up to 4096 positions: 100 KB of LDS
-  if (!smem_set) {
-    DG_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(sampler_finish_kernel),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, 4096 * 25));
-    smem_set = true;
-  }
+  // up to 4096 positions: 100 KB of LDS
+  const dg_status lst =
+      ensure_lds_limit(reinterpret_cast<const void*>(sampler_finish_kernel), 4096 * 25);
+  if (lst != DG_OK) return lst;
   sampler_finish_kernel<<<B, kFinishThreads, smem, stream>>>(
       part, L, npow2, V, nsplit, invT, step, ends_at, adaptive, cfg.stop_entropy, cfg.commit_prob,
       cfg.renoise_prob, cfg.commit_policy, cfg.entropy_bound, k0, k1, prefix_len, tokens,

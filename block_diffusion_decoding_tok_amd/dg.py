@@ -99,6 +99,7 @@ _SIGS = {
                            C.POINTER(dg_model_weights), _I, _I, _VP, _SZ]),
     "dg_ctx_destroy": (_I, [_VP]),
     "dg_ctx_set_graphs": (_I, [_VP, _I]),
+    "dg_ctx_check_status": (_I, [_VP, _VP]),
     "dg_ctx_set_router_override": (_I, [_VP, C.POINTER(_VP), _I]),
     "dg_model_forward": (_I, [_VP, _VP, _VP, _I, _I, _I, _I, C.POINTER(_VP), C.POINTER(_VP),
                               _I, _VP, _I, _VP, _VP]),
@@ -420,6 +421,11 @@ class DGModel:
 
     def set_graphs(self, on):
         _check(lib().dg_ctx_set_graphs(self.ctx, int(bool(on))))
+
+    def check_status(self, stream=None):
+        """dg_ctx_check_status: wait for the stream; raise DGError
+        (DG_ERR_NONFINITE) if a finished decoder call met NaN/Inf logits."""
+        _check(lib().dg_ctx_check_status(self.ctx, _stream(stream)))
 
     def set_router_override(self, logits_per_layer):
         """Route with the given per-layer f32 [n_tokens, E] logits (None: the

@@ -8,6 +8,7 @@
  *   [GUIDE] aisparkup "diffusion-gemma tutorial / developer guide"
  *   [GN]    "DiffusionGemma: 4배 빠른 텍스트 생성" (GeekNews)
  *   [WE0]   test.we0.ai article on DiffusionGemma
+ *   [JPH]   "구글, 순차 처리 탈피한 확산 기반 AI 모델 디퓨전젬마 공개"
  *
  * Conventions for every entry point
  *   - All tensor arguments are DEVICE pointers owned by the caller, row-major,
@@ -21,7 +22,8 @@
  *     invalid call returns a negative dg_status and launches nothing.  The
  *     message of the last failure on the calling thread is dg_last_error().
  *   - Device-side conditions (non-finite logits) are reported through a
- *     caller-provided device status word (see dg_sampler_step).
+ *     caller-provided device status word (see dg_sampler_step); the decoder
+ *     calls report them as DG_ERR_NONFINITE (see dg_ctx_check_status).
  */
 #ifndef DG_H_
 #define DG_H_
@@ -40,7 +42,7 @@ typedef enum {
   DG_ERR_UNSUPPORTED = -3,   /* valid but not implemented combination */
   DG_ERR_WORKSPACE = -4,     /* workspace missing or too small */
   DG_ERR_HIP = -5,           /* a HIP runtime call failed (see dg_last_error) */
-  DG_ERR_NONFINITE = -6      /* reserved: non-finite input detected */
+  DG_ERR_NONFINITE = -6      /* NaN / Inf logits met by a decoder call (see dg_ctx_check_status) */
 } dg_status;
 
 /* DG_MXFP4: OCP Microscaling MXFP4 (FP4 E2M1 elements, blocks of 32 along K
@@ -303,6 +305,24 @@ dg_status dg_ctx_create(dg_ctx** out, const dg_model_dims* dims, const dg_model_
 dg_status dg_ctx_destroy(dg_ctx* ctx);
 /* use_graphs != 0 (default): dg_denoise_block replays a captured hipGraph. */
 dg_status dg_ctx_set_graphs(dg_ctx* ctx, int use_graphs);
+/* Non-finite logits (the failure the sampler and the AR argmax detect: a NaN
+ * or Inf anywhere in a row's logits) in the decoder calls.  Each block and
+ * each AR run clears the context's device status word when it starts; the
+ * sampler steps (and the AR argmax) OR in DG_STATUS_NONFINITE_LOGITS; the end
+ * of the block (of each adaptive chunk, of the AR run) stores a non-zero word
+ * into a host-visible word of the context (pinned host memory, allocated by
+ * dg_ctx_create).  Every decoder call (dg_denoise_block, dg_generate,
+ * dg_ar_decode) first takes that word: if it is set, the call clears it and
+ * returns DG_ERR_NONFINITE without launching anything.  Calls that wait on
+ * the stream anyway (the adaptive mode after each chunk, dg_generate after
+ * each block) return DG_ERR_NONFINITE as soon as they see it, leaving the
+ * block uncommitted (prefix_len not advanced).  An asynchronous call (fixed
+ * steps with graphs, dg_ar_decode) returns DG_OK and its non-finite logits
+ * are reported by the next call on the context that runs after the device
+ * finished it, or by dg_ctx_check_status.
+ * dg_ctx_check_status: waits for stream, then returns DG_ERR_NONFINITE (and
+ * clears the word) if a finished call met non-finite logits, else DG_OK. */
+dg_status dg_ctx_check_status(dg_ctx* ctx, void* stream);
 /* Benchmarking hook: route every forward with caller-supplied router logits
  * instead of the router projection's output (the projection still runs).
  * logits: host array [n_layers] of device pointers to f32 [n_tokens, E]; a
@@ -340,7 +360,8 @@ dg_status dg_prefill(dg_ctx* ctx, const int32_t* prompt, int B, int n, void* con
  * the adaptive mode the steps run in chunks of a few steps and the call
  * waits on the stream after each chunk to read the rows' done flags, so it
  * stops as soon as every row is done; it returns once the block is queued
- * behind the last chunk. */
+ * behind the last chunk.  Non-finite logits: DG_ERR_NONFINITE, as described
+ * at dg_ctx_check_status. */
 dg_status dg_denoise_block(dg_ctx* ctx, const dg_sampler_cfg* cfg, int B, void* const* k_caches,
                            void* const* v_caches, int Tmax, int32_t* prefix_len,
                            int32_t* tokens_out, int32_t* steps_taken, void* stream);

@@ -187,14 +187,37 @@ def _packed(w):
 
 @pytest.fixture(scope="module", params=["rowmajor", "tiled"])
 def full_layers(request):
+    """The model, and the same model with every expert weight zero: its layer
+    output is the residual stream after the attention branch, from which the
+    device's own router logits are recomputed exactly (measured routing)."""
     d = FULL_LAYER
     w = model_weights(d, seed=3, expert_dtype="fp8", dense_dtype="bf16")
+    w0 = dict(w)
+    for l in range(d.NL):
+        w0[f"wgu.{l}"] = torch.zeros_like(w[f"wgu.{l}"])
+        w0[f"wd.{l}"] = torch.zeros_like(w[f"wd.{l}"])
     if request.param == "tiled":
         model = dg.DGModel(d, _packed(w), 4, 256, dg.DG_BF16, dg.DG_FP8_E4M3,
                            weight_layout=dg.DG_LAYOUT_TILED)
+        model0 = dg.DGModel(d, _packed(w0), 4, 256, dg.DG_BF16, dg.DG_FP8_E4M3,
+                            weight_layout=dg.DG_LAYOUT_TILED)
     else:
         model = dg.DGModel(d, _dev_weights(w), 4, 256, dg.DG_BF16, dg.DG_FP8_E4M3)
-    return d, w, model
+        model0 = dg.DGModel(d, _dev_weights(w0), 4, 256, dg.DG_BF16, dg.DG_FP8_E4M3)
+    return d, w, model, model0
+
+
+def _device_router_logits(x_attn, wr):
+    """The router logits the device computes from its post-attention stream
+    x_attn [T, D] (f32): RMSNorm rounded to bf16 (the router GEMM's input),
+    times the bf16 router weights, in float64 (the device accumulates in f32)."""
+    h = torch.from_numpy(rmsnorm(x_attn)).to(torch.bfloat16).double().numpy()
+    return h @ to_f64(wr).T
+
+
+def _topk_gap(r, k):
+    s = np.sort(r, axis=1)[:, ::-1]
+    return s[:, k - 1] - s[:, k]
 
 
 @pytest.mark.parametrize("B,P0,planted,mode,n", [(1, 256, False, CANVAS, 256),
@@ -206,12 +229,17 @@ def full_layers(request):
                                                  (1, 64, False, CAUSAL, 17)])
 def test_full_width_layers_teacher_forced(full_layers, B, P0, planted, mode, n):
     """planted: the router override supplies N(0,1) + hot-expert-skew logits
-    (the stated MoE routing) instead of the random router's.  CAUSAL: an
-    n-token prefill chunk at positions [P0, P0 + n) (the prompt path).  Token
-    counts off the 16- and 64-token tiles (200, 3 x 40, 17) end in partial
-    token blocks of the tiled activation layout; 300 prompt tokens prefill as
-    256 + 44."""
-    d, w, model = full_layers
+    (the stated MoE routing) instead of the random router's, so both sides
+    route on identical logits.  Natural routing: the device's own router
+    logits are measured (from the zero-expert model's post-attention stream)
+    and the oracle layer is evaluated once with its own routing and once with
+    the device's; every token must match the latter within the fp8
+    tolerance, and the tokens whose routing differs must be near-ties within
+    the measured router-logit error.  CAUSAL: an n-token prefill chunk at
+    positions [P0, P0 + n) (the prompt path).  Token counts off the 16- and
+    64-token tiles (200, 3 x 40, 17) end in partial token blocks of the tiled
+    activation layout; 300 prompt tokens prefill as 256 + 44."""
+    d, w, model, model0 = full_layers
     override = None
     if planted:
         override = [torch.from_numpy(router_logits_skewed(B * n, d.E, d.k, seed=40 + l)[0])
@@ -234,31 +262,58 @@ def test_full_width_layers_teacher_forced(full_layers, B, P0, planted, mode, n):
         x_in = x.cpu().double().numpy().reshape(B, n, d.D)
         cache_k = kc[l].cpu().double().numpy()
         cache_v = vc[l].cpu().double().numpy()
+        if not planted:
+            # the same layer with zero experts: x_in + attention branch
+            x0 = x.clone()
+            dg.dg_model_forward(model0, None, x0, B, n, l, l + 1, kc, vc, Pd, mask_mode=mode)
         dg.dg_model_forward(model, None, x, B, n, l, l + 1, kc, vc, Pd, mask_mode=mode)
         torch.cuda.synchronize()
         x_out = x.cpu().double().numpy().reshape(B, n, d.D)
         trace = []
-        ref = layer_forward(m, m.layers[l], x_in, cache_k, cache_v, P_host, mode, trace=trace,
+        ck, cv = cache_k.copy(), cache_v.copy()
+        ref = layer_forward(m, m.layers[l], x_in, ck, cv, P_host, mode, trace=trace,
                             router_logits=None if override is None else override[l].numpy())
         got_d = (x_out - x_in).reshape(-1, d.D)
-        ref_d = (ref - x_in).reshape(-1, d.D)
-        err = np.linalg.norm(got_d - ref_d, axis=1) / np.linalg.norm(ref_d, axis=1)
-        # bf16 activations move the router logits by ~1e-3, so a token whose
-        # k-th and (k+1)-th logits are closer than that may legitimately pick
-        # another expert.  Every token outside the tolerance must be such a
-        # near-tie, and they must be a small minority.
-        r = np.sort(trace[0]["router_logits"], axis=1)[:, ::-1]
-        gap = r[:, d.k - 1] - r[:, d.k]
-        bad = err >= 5e-2
-        print(f"layer {l}: max err {err.max():.3g}, out-of-tolerance tokens {bad.sum()} "
-              f"(gaps {np.sort(gap[bad])[:8]}), max err of the others {err[~bad].max():.3g}")
-        assert np.all(gap[bad] < 2e-2), (l, gap[bad].max())
-        assert bad.mean() < 0.1, (l, bad.mean())
         if planted:                      # identical routing inputs: no exceptions
-            assert not bad.any()
+            ref_d = (ref - x_in).reshape(-1, d.D)
+            err = np.linalg.norm(got_d - ref_d, axis=1) / np.linalg.norm(ref_d, axis=1)
+            print(f"layer {l}: max err {err.max():.3g}")
+            assert err.max() < 5e-2, (l, err.max())
+        else:
+            r_ref = trace[0]["router_logits"]
+            r_dev = _device_router_logits(x0.cpu().double().numpy(), w[f"wr.{l}"])
+            dr = np.abs(r_dev - r_ref).max()
+            ref_dev = layer_forward(m, m.layers[l], x_in, cache_k.copy(), cache_v.copy(), P_host,
+                                    mode, router_logits=r_dev)
+            ref_d = (ref_dev - x_in).reshape(-1, d.D)
+            err = np.linalg.norm(got_d - ref_d, axis=1) / np.linalg.norm(ref_d, axis=1)
+            # r_dev recomputes the device's f32 RMSNorm in float64 before the
+            # bf16 rounding and sums in float64: it can order two logits
+            # differently from the device only when they are within ~1e-4
+            amb = _topk_gap(r_dev, d.k) < 1e-4
+            flipped = np.any(np.sort(trace[0]["topk_ids"], axis=1) !=
+                             np.sort(np.argsort(-r_dev, axis=1, kind="stable")[:, :d.k], axis=1),
+                             axis=1)
+            gap = _topk_gap(r_ref, d.k)
+            print(f"layer {l}: router-logit error max {dr:.3g}; {flipped.sum()} of {B * n} tokens "
+                  f"route differently (k/k+1 gaps {np.sort(gap[flipped])[:6]}); max err against "
+                  f"the device routing {err[~amb].max():.3g}; {amb.sum()} ambiguous")
+            assert err[~amb].max() < 5e-2, (l, err[~amb].max())
+            # a routing difference needs a k / k+1 gap within twice the
+            # measured router-logit error
+            assert np.all(gap[flipped] <= 2 * dr), (l, gap[flipped].max(), dr)
+            # the router logits themselves are a bf16-path output: per token
+            # within the bf16 relative bar
+            er = rel_err_rows(r_dev, r_ref)
+            print(f"layer {l}: router logits relative error per token max {er:.3g}")
+            assert er < 2e-2, er
         # the canvas K/V written by the device vs the oracle's (same inputs)
         got_k = kc[l].cpu().double().numpy()[:, :, P0:P0 + n]
-        assert rel_err_rows(got_k, cache_k[:, :, P0:P0 + n]) < 3e-2
+        got_v = vc[l].cpu().double().numpy()[:, :, P0:P0 + n]
+        ek = rel_err_rows(got_k, ck[:, :, P0:P0 + n])
+        ev = rel_err_rows(got_v, cv[:, :, P0:P0 + n])
+        print(f"layer {l}: cache K err {ek:.3g}, V err {ev:.3g}")
+        assert ek < 2e-2 and ev < 2e-2, (ek, ev)
     # final norm + LM head on the last layer's output
     logits = torch.empty((B, n, d.V), dtype=torch.bfloat16, device=DEV)
     x_last = x.cpu().double().numpy()
@@ -292,3 +347,82 @@ def test_full_vocab_lm_head_sampled():
     got = logits[0].cpu().double().numpy()[sel]
     assert rel_err_rows(got, ref) < 2e-2
     assert np.allclose(x.cpu().double().numpy()[sel], xr)
+
+
+# ----------------------------------------------------------- non-finite logits
+
+def _nan_head_model(B, graphs=True):
+    """The tiny f32 model with a NaN in one LM-head row: every position's
+    logit of id 5 is NaN."""
+    d = TINY_DIMS
+    w = model_weights(d, seed=0)
+    w["lm"] = w["lm"].clone()
+    w["lm"][5, 3] = float("nan")
+    model = dg.DGModel(d, _dev_weights(w), B, 16, dg.DG_F32, dg.DG_F32)
+    model.set_graphs(graphs)
+    kc, vc = _caches(d, B, 32 + 4 * 16, torch.float32)
+    Pd = torch.zeros(B, dtype=torch.int32, device=DEV)
+    return d, model, kc, vc, Pd
+
+
+def _expect_nonfinite(fn):
+    with pytest.raises(dg.DGError) as ei:
+        fn()
+    assert ei.value.code == -6, ei.value
+
+
+def test_nonfinite_logits_fixed_graph_reported_later():
+    """Fixed steps with graphs: the call is asynchronous and returns; the
+    context's status is reported by dg_ctx_check_status (once), and a clean
+    model's block reports nothing."""
+    B = 2
+    d, model, kc, vc, Pd = _nan_head_model(B)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        dg.dg_prefill(model, prompt_ids(B, 32, d.V, seed=0).to(DEV), kc, vc, Pd)
+        cfg = dg.sampler_cfg(16, 8, 3, seed=0)
+        tok = torch.empty((B, 16), dtype=torch.int32, device=DEV)
+        steps = torch.empty(B, dtype=torch.int32, device=DEV)
+        dg.dg_denoise_block(model, cfg, B, kc, vc, Pd, tok, steps)
+        _expect_nonfinite(lambda: model.check_status(stream))
+        model.check_status(stream)                     # reported once, then clear
+        # the next call after a finished bad block refuses to run
+        dg.dg_denoise_block(model, cfg, B, kc, vc, Pd, tok, steps)
+        stream.synchronize()
+        _expect_nonfinite(lambda: dg.dg_denoise_block(model, cfg, B, kc, vc, Pd, tok, steps))
+        stream.synchronize()
+    # a finite model: nothing reported
+    r = _tiny_block(dict(fixed_steps=3, seed=5))
+    r["model"].check_status()
+
+
+def test_nonfinite_logits_adaptive_and_generate_return_error():
+    """The adaptive mode and dg_generate wait on the stream anyway: they
+    return DG_ERR_NONFINITE themselves, and leave the prefix unadvanced."""
+    B = 2
+    d, model, kc, vc, Pd = _nan_head_model(B)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        dg.dg_prefill(model, prompt_ids(B, 32, d.V, seed=0).to(DEV), kc, vc, Pd)
+        stream.synchronize()
+        cfg = dg.sampler_cfg(16, 8, 0, seed=0)
+        tok = torch.empty((B, 16), dtype=torch.int32, device=DEV)
+        steps = torch.empty(B, dtype=torch.int32, device=DEV)
+        _expect_nonfinite(lambda: dg.dg_denoise_block(model, cfg, B, kc, vc, Pd, tok, steps))
+        stream.synchronize()
+        assert Pd.cpu().tolist() == [32] * B
+        _expect_nonfinite(lambda: dg.dg_generate(model, cfg, B, kc, vc, Pd, -1, 2))
+        stream.synchronize()
+        model.check_status(stream)
+
+
+def test_nonfinite_logits_ar_decode():
+    B = 2
+    d, model, kc, vc, Pd = _nan_head_model(B)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        dg.dg_prefill(model, prompt_ids(B, 32, d.V, seed=0).to(DEV), kc, vc, Pd)
+        first = torch.zeros(B, dtype=torch.int32, device=DEV)
+        dg.dg_ar_decode(model, first, 3, kc, vc, Pd)
+        _expect_nonfinite(lambda: model.check_status(stream))
+        model.check_status(stream)

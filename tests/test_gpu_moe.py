@@ -94,13 +94,16 @@ def test_pack_weights_layout(dtype):
     assert np.array_equal(got, ref)
 
 
+@pytest.mark.parametrize("w_dtype", ["bf16", "fp8"])
 @pytest.mark.parametrize("tiled", [False, True])
-def test_moe_ffn_full_size_bs4_fp8_sampled(tiled):
-    """Above 40 tokens per expert on average: LDS-staged 64-token tiles."""
-    case = moe_case(T=1024, w_dtype="fp8", seed=1)
+def test_moe_ffn_full_size_bs4_sampled(w_dtype, tiled):
+    """Batch 4 of the MoE workload (1024 tokens, 128 experts, top-8): above 40
+    tokens per expert on average, the LDS-staged 64-token tiles over the
+    multi-expert (chunk-column) stack; 96 sampled tokens."""
+    case = moe_case(T=1024, w_dtype=w_dtype, seed=1)
     sample = np.random.default_rng(0).choice(1024, 96, replace=False)
     err, _ = _ffn_case(case, 8, sample, tiled=tiled)
-    assert err < TOL["fp8"], err
+    assert err < TOL[w_dtype], err
 
 
 @pytest.mark.parametrize("T", [1, 3, 8])

@@ -115,6 +115,17 @@ def test_sampler_config_full_size_bs1():
     assert excl <= 3
 
 
+def test_sampler_config_full_size_bs4():
+    """Batch 4 of the sampler workload at full size ([4, 256, 2^18] bf16
+    logits): the first and the last step of the schedule."""
+    case = sampler_case(B=4, L=256, V=262144, seed=2)
+    ocfg, gcfg = _cfg_pair(canvas_len=256, max_steps=48, seed=3)
+    x64 = case.logits.to(torch.float64).numpy()
+    _, excl = _run_and_compare(case.logits.to(DEV), x64, ocfg, gcfg, [0, 47],
+                               [0, 256, 4096, 8192])
+    assert excl <= 4
+
+
 def test_sampler_batch4_reduced_length():
     case = sampler_case(B=4, L=40, V=262144, seed=1)
     ocfg, gcfg = _cfg_pair(canvas_len=40, max_steps=48, seed=7)
