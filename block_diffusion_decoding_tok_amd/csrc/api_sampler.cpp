@@ -12,12 +12,16 @@ size_t dg_sampler_workspace_size(int B, int L, int V) {
   return sampler_workspace_bytes(B, L, V);
 }
 
-dg_status dg_sampler_step(const void* logits, int logit_dtype, int B, int L, int V, int step,
-                          const dg_sampler_cfg* cfg, const int32_t* prefix_len, int32_t* tokens,
-                          uint8_t* committed, uint8_t* renoised, float* maxprob, float* entropy,
-                          float* mean_entropy, int32_t* done, int32_t* status, void* ws,
-                          size_t ws_bytes, void* stream) {
-  set_error("");
+}  // extern "C"
+
+namespace dg {
+// Host checks of one sampler step (everything but the workspace).
+dg_status check_sampler_step(const void* logits, int logit_dtype, int B, int L, int V, int step,
+                             const dg_sampler_cfg* cfg, const int32_t* prefix_len,
+                             const int32_t* tokens, const uint8_t* committed,
+                             const uint8_t* renoised, const float* maxprob,
+                             const float* entropy, const float* mean_entropy,
+                             const int32_t* done) {
   DG_CHECK_ARG(cfg != nullptr, "dg_sampler_step: cfg is null");
   DG_CHECK_ARG(logits && prefix_len && tokens && committed && renoised && maxprob && entropy &&
                    mean_entropy && done,
@@ -38,6 +42,22 @@ dg_status dg_sampler_step(const void* logits, int logit_dtype, int B, int L, int
                    (cfg->commit_policy == DG_COMMIT_ENTROPY_BOUND && cfg->entropy_bound >= 0.f &&
                     cfg->entropy_bound < INFINITY),
                "dg_sampler_step: bad commit_policy / entropy_bound");
+  return DG_OK;
+}
+}  // namespace dg
+
+extern "C" {
+
+dg_status dg_sampler_step(const void* logits, int logit_dtype, int B, int L, int V, int step,
+                          const dg_sampler_cfg* cfg, const int32_t* prefix_len, int32_t* tokens,
+                          uint8_t* committed, uint8_t* renoised, float* maxprob, float* entropy,
+                          float* mean_entropy, int32_t* done, int32_t* status, void* ws,
+                          size_t ws_bytes, void* stream) {
+  set_error("");
+  const dg_status st = check_sampler_step(logits, logit_dtype, B, L, V, step, cfg, prefix_len,
+                                          tokens, committed, renoised, maxprob, entropy,
+                                          mean_entropy, done);
+  if (st != DG_OK) return st;
   if (ws_bytes < sampler_workspace_bytes(B, L, V) || ws == nullptr)
     return fail(DG_ERR_WORKSPACE, "dg_sampler_step: workspace too small");
   return launch_sampler(logits, logit_dtype, B, L, V, step, *cfg, prefix_len, tokens, committed,

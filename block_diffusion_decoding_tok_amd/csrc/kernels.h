@@ -8,6 +8,13 @@ namespace dg {
 
 // sampler.hip
 size_t sampler_workspace_bytes(int B, int L, int V);
+// api_sampler.cpp: host checks of dg_sampler_step's arguments (not the workspace)
+dg_status check_sampler_step(const void* logits, int logit_dtype, int B, int L, int V, int step,
+                             const dg_sampler_cfg* cfg, const int32_t* prefix_len,
+                             const int32_t* tokens, const uint8_t* committed,
+                             const uint8_t* renoised, const float* maxprob,
+                             const float* entropy, const float* mean_entropy,
+                             const int32_t* done);
 dg_status launch_sampler(const void* logits, int logit_dtype, int B, int L, int V, int step,
                          const dg_sampler_cfg& cfg, const int32_t* prefix_len, int32_t* tokens,
                          uint8_t* committed, uint8_t* renoised, float* maxprob, float* entropy,

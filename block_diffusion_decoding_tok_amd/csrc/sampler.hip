@@ -19,6 +19,8 @@
 // Kernel 2 (finish): one workgroup per row merges the nsplit partials of each
 // position, computes maxprob / entropy / the row's mean entropy, decides
 // whether this step ends the row, and applies the update.
+#include <mutex>
+
 #include "common.h"
 #include "philox.h"
 #include "kernels.h"
@@ -413,6 +415,35 @@ size_t sampler_workspace_bytes(int B, int L, int V) {
   return align_up(static_cast<size_t>(B) * L * nsplit * sizeof(SamplerPartial), 256);
 }
 
+// ------------------------------------------------- library-owned scratch
+// The workspace of dg_sampler_step_noalloc: one array per GPU the library
+// runs on, held until the process ends.  Host code never uses the array's
+// name as an address: the device address comes from hipGetSymbolAddress,
+// taken once per device with that device current.
+constexpr size_t kSamplerScratchBytes = size_t(1) << 20;
+static_assert(kSamplerScratchBytes == DG_SAMPLER_SCRATCH_BYTES, "scratch size");
+static __device__ __align__(256) unsigned char scratch[kSamplerScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array.
+static dg_status scratch_ptr(void** out) {
+  int dev = 0;
+  DG_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return fail(DG_ERR_UNSUPPORTED, "device index out of range");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    DG_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p) return fail(DG_ERR_HIP, "hipGetSymbolAddress returned a null scratch address");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return DG_OK;
+}
+
 // ------------------------------------------------------------ init canvas
 __global__ void init_canvas_kernel(const int32_t* __restrict__ prefix_len, int B, int L, int V,
                                    uint32_t k0, uint32_t k1, int32_t* __restrict__ tokens,
@@ -469,3 +500,27 @@ dg_status launch_gumbel(const uint32_t* w, int64_t n, float* out, hipStream_t st
 }
 
 }  // namespace dg
+
+extern "C" dg_status dg_sampler_step_noalloc(const void* logits, int logit_dtype, int B, int L,
+                                             int V, int step, const dg_sampler_cfg* cfg,
+                                             const int32_t* prefix_len, int32_t* tokens,
+                                             uint8_t* committed, uint8_t* renoised,
+                                             float* maxprob, float* entropy, float* mean_entropy,
+                                             int32_t* done, int32_t* status, void* stream) {
+  using namespace dg;
+  set_error("");
+  dg_status st = check_sampler_step(logits, logit_dtype, B, L, V, step, cfg, prefix_len, tokens,
+                                    committed, renoised, maxprob, entropy, mean_entropy, done);
+  if (st != DG_OK) return st;
+  if (sampler_workspace_bytes(B, L, V) > kSamplerScratchBytes)
+    return fail(DG_ERR_WORKSPACE,
+                "dg_sampler_step_noalloc: B * L * ceil(V / 16384) * 32 bytes exceed the "
+                "library's 1 MiB scratch");
+  void* ws = nullptr;
+  if ((st = scratch_ptr(&ws))) return st;
+  // every partial the finishing kernel reads is written earlier in the same
+  // call, so the scratch needs no clearing
+  return launch_sampler(logits, logit_dtype, B, L, V, step, *cfg, prefix_len, tokens, committed,
+                        renoised, maxprob, entropy, mean_entropy, done, status, nullptr, ws,
+                        static_cast<hipStream_t>(stream));
+}

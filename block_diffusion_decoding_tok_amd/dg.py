@@ -78,6 +78,8 @@ _SIGS = {
     "dg_sampler_workspace_size": (_SZ, [_I, _I, _I]),
     "dg_sampler_step": (_I, [_VP, _I, _I, _I, _I, _I, C.POINTER(dg_sampler_cfg), _VP, _VP,
                              _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
+    "dg_sampler_step_noalloc": (_I, [_VP, _I, _I, _I, _I, _I, C.POINTER(dg_sampler_cfg), _VP,
+                                     _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
     "dg_init_canvas": (_I, [_VP, _I, _I, _I, _U64, _VP, _VP, _VP, _VP]),
     "dg_attention_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I, _I]),
     "dg_canvas_attention": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _I,
@@ -206,6 +208,21 @@ def dg_sampler_step(logits, step, cfg, prefix_len, tokens, committed, renoised,
         _dev(mean_entropy, "mean_entropy", (torch.float32,)),
         _dev(done, "done", (torch.int32,)), _dev(status, "status", (torch.int32,)),
         ws.data_ptr(), ws.numel(), _stream(stream)))
+
+
+def dg_sampler_step_noalloc(logits, step, cfg, prefix_len, tokens, committed, renoised,
+                            maxprob, entropy, mean_entropy, done, status=None, stream=None):
+    """dg_sampler_step on the library's own scratch (no workspace argument)."""
+    B, L, V = logits.shape
+    _check(lib().dg_sampler_step_noalloc(
+        _dev(logits, "logits", (torch.bfloat16, torch.float32)), _dtype_code(logits),
+        B, L, V, int(step), C.byref(cfg), _dev(prefix_len, "prefix_len", (torch.int32,)),
+        _dev(tokens, "tokens", (torch.int32,)), _dev(committed, "committed", (torch.uint8,)),
+        _dev(renoised, "renoised", (torch.uint8,)), _dev(maxprob, "maxprob", (torch.float32,)),
+        _dev(entropy, "entropy", (torch.float32,)),
+        _dev(mean_entropy, "mean_entropy", (torch.float32,)),
+        _dev(done, "done", (torch.int32,)), _dev(status, "status", (torch.int32,)),
+        _stream(stream)))
 
 
 def dg_init_canvas(prefix_len, L, V, seed, tokens, committed, done, stream=None):

@@ -155,6 +155,24 @@ dg_status dg_sampler_step(const void* logits, int logit_dtype, int B, int L, int
                           int32_t* done, int32_t* status, void* ws, size_t ws_bytes,
                           void* stream);
 
+/* dg_sampler_step_noalloc: dg_sampler_step for callers that cannot allocate
+ * device memory or pass a workspace (code under hipGraph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).  Same arguments, results
+ * and errors as dg_sampler_step, without ws / ws_bytes: the workspace is a
+ * library-owned device array of DG_SAMPLER_SCRATCH_BYTES on each GPU the call
+ * runs on (held until the process ends).  Calls with
+ * dg_sampler_workspace_size(B, L, V) > DG_SAMPLER_SCRATCH_BYTES (e.g. more
+ * than 2048 positions at V = 2^18) return DG_ERR_WORKSPACE and launch
+ * nothing.  It allocates nothing.  Every call on a GPU shares that GPU's
+ * array: calls that overlap on one GPU (several streams, several host
+ * threads) race and must be serialized by the caller. */
+#define DG_SAMPLER_SCRATCH_BYTES (1u << 20)
+dg_status dg_sampler_step_noalloc(const void* logits, int logit_dtype, int B, int L, int V,
+                                  int step, const dg_sampler_cfg* cfg, const int32_t* prefix_len,
+                                  int32_t* tokens, uint8_t* committed, uint8_t* renoised,
+                                  float* maxprob, float* entropy, float* mean_entropy,
+                                  int32_t* done, int32_t* status, void* stream);
+
 /* dg_init_canvas: the block's starting canvas ([GN] "텍스트 확산의 작동 방식";
  * [GUIDE] "Uniform State Diffusion": random placeholder tokens).
  * tokens[b, i] = uniform id in [0, V) from Philox counter
