@@ -131,7 +131,7 @@ def entropy_bound_timing(d, w, model, B, kc, vc, Pd, stream):
     out = {"bound": 0.1,
            "random_init_block": {"steps": st_eb, "ms": round(ms_eb, 2),
                                  "fixed_48_step_graph_ms": round(ms_fx, 2),
-                                 "chunk_check_overhead_frac": round(ms_eb / ms_fx - 1, 4)}}
+                                 "adaptive_overhead_frac": round(ms_eb / ms_fx - 1, 4)}}
     lm = w["lm"].clone()
     lm[: (d.D // 64) * 1024] *= 400.0                        # tile 0: LM rows 0..15
     w_pl = dict(w)
@@ -157,6 +157,19 @@ def entropy_bound_timing(d, w, model, B, kc, vc, Pd, stream):
     eos = int(toks[0, 0, 0].item())
     g_eos, _ = gen(eos)
     g_eos["eos_id"] = eos
+    # what the blocks would take with no step beyond each block's end: the
+    # steps taken at the fixed-graph step time, plus one commit per block
+    # (step and commit times from the 48-step and 12-step fixed blocks)
+    fixed12 = dg.sampler_cfg(CANVAS, 48, 12, seed=0)
+    ms_12, _ = one_block(model, fixed12)
+    step_ms = (ms_fx - ms_12) / 36
+    commit_ms = ms_12 - 12 * step_ms
+    for g in (g_noeos, g_eos):
+        n_steps = sum(sum(r) for r in g["steps"])
+        n_blk = sum(g["n_blocks"])
+        g["steps_plus_commits_ms"] = round(n_steps * step_ms + n_blk * commit_ms, 2)
+    out["step_ms"] = round(step_ms, 3)
+    out["commit_ms"] = round(commit_ms, 3)
     out["planted_confident_generate"] = {"no_eos": g_noeos, "eos": g_eos}
     m_pl.close()
     del lm, w_pl

@@ -167,7 +167,8 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(
     const bf16_t* __restrict__ qrot, const bf16_t* __restrict__ k_cache,
     const bf16_t* __restrict__ v_cache, const int32_t* __restrict__ prefix_len, int Lq, int G,
     int Hkv, int Tmax, int chunk, int ntile_rows, int nsplit, int BH, int causal,
-    float* __restrict__ o_part, AttnPartialML* __restrict__ ml_part) {
+    float* __restrict__ o_part, AttnPartialML* __restrict__ ml_part, const int32_t* gate,
+    int gate_n, const int32_t* __restrict__ row_done) {
   extern __shared__ __attribute__((aligned(16))) bf16_t smem[];
   // [K tile 0][K tile 1][V^T tile 0][V^T tile 1]
   auto s_k = [&](int buf) { return smem + buf * kKTileElems; };
@@ -182,6 +183,8 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(
   const int split = (logical / ntile_rows) % nsplit;
   const int bh = logical / (ntile_rows * nsplit);
   const int b = bh / Hkv;
+  // the adaptive loop's gate: every row stopped, or this row stopped
+  if (step_gate_closed(gate, gate_n) || (row_done && row_done[b])) return;
   const int rows_total = Lq * G;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g4 = lane >> 4;
@@ -393,11 +396,14 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
                                                            const AttnPartialML* __restrict__ ml_part,
                                                            int nsplit, int BH, int rows_total,
                                                            int G, int Hkv, int Lq, int tiled,
-                                                           T* __restrict__ out) {
+                                                           T* __restrict__ out,
+                                                           const int32_t* gate, int gate_n,
+                                                           const int32_t* __restrict__ row_done) {
   const int gr = blockIdx.x * 8 + (threadIdx.x >> 5);      // global packed row index
   const int d4 = (threadIdx.x & 31) * 4;
-  if (gr >= BH * rows_total) return;
+  if (gr >= BH * rows_total || step_gate_closed(gate, gate_n)) return;
   const int bh = gr / rows_total, r = gr % rows_total;
+  if (row_done && row_done[bh / Hkv]) return;
   // splits in batches of 8: a batch's (m, l) and O loads are issued together
   // (clamped indices, masked afterwards), then merged in split order with an
   // online rescale when a batch raises the running maximum (one pass)
@@ -544,11 +550,12 @@ dg_status launch_attention(const AttnArgs& a, void* ws, hipStream_t stream) {
     attn_mfma_kernel<<<(total + 7) / 8 * 8, 512, kAttnSmemBytes, stream>>>(
         static_cast<const bf16_t*>(qrot), static_cast<const bf16_t*>(a.k_cache),
         static_cast<const bf16_t*>(a.v_cache), a.prefix_len, a.Lq, G, a.Hkv, a.Tmax, p.chunk,
-        p.tiles, p.nsplit, a.B * a.Hkv, a.mask_mode == DG_MASK_CAUSAL, o_part, ml);
+        p.tiles, p.nsplit, a.B * a.Hkv, a.mask_mode == DG_MASK_CAUSAL, o_part, ml,
+        a.gate.n_done, a.gate.n, a.gate.row_done);
     DG_LAUNCH_CHECK();
     attn_combine_kernel<bf16_t><<<(a.B * a.Hkv * rows + 7) / 8, 256, 0, stream>>>(
         o_part, ml, p.nsplit, a.B * a.Hkv, rows, G, a.Hkv, a.Lq, a.out_tiled,
-        static_cast<bf16_t*>(a.out));
+        static_cast<bf16_t*>(a.out), a.gate.n_done, a.gate.n, a.gate.row_done);
     DG_LAUNCH_CHECK();
   } else {
     rope_kernel<float><<<a.B * a.Lq, rope_threads(a.dh), 0, stream>>>(

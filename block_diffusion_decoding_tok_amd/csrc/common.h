@@ -128,6 +128,14 @@ __device__ __forceinline__ void rope_cos_sin(int pos, int j, int dh, float theta
   rope_cos_sin_at(pos, rope_inv_freq(j, dh, theta), c, s);
 }
 
+// Step gate of the adaptive block loop: a kernel handed a non-null n_done
+// returns at once when n_done[0] >= n, i.e. every row of the batch has
+// stopped (the steps the host queued ahead of its done check then cost only
+// their launches).  The count is read once per workgroup, through lane 0.
+__device__ __forceinline__ bool step_gate_closed(const int32_t* n_done, int n) {
+  return n_done != nullptr && __builtin_amdgcn_readfirstlane(*n_done) >= n;
+}
+
 // Logical workgroup index for a grid of a multiple of 8 workgroups:
 // hardware deals linear workgroup ids round-robin over the 8 XCDs, so this
 // gives each XCD one contiguous range of logical indices (work items that

@@ -178,8 +178,10 @@ constexpr int kWaitVm4 = waitcnt_vm(4), kWaitVm0 = waitcnt_vm(0);
 __global__ __launch_bounds__(512) void gemm_wide_dl_kernel(const bf16_t* __restrict__ W,
                                                            const bf16_t* __restrict__ X,
                                                            bf16_t* __restrict__ C, int M, int N,
-                                                           int K) {
+                                                           int K, const int32_t* gate,
+                                                           int gate_n) {
   extern __shared__ __attribute__((aligned(16))) bf16_t dsm[];
+  if (step_gate_closed(gate, gate_n)) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g4 = lane >> 4;
   const int wr = wave & 1, wt = wave >> 1;
@@ -278,7 +280,8 @@ template <bool TILED>
 static dg_status launch_gemm_bf16(GemmArgs& g, int M, int N, int K, hipStream_t stream);
 
 dg_status launch_gemm(const void* A, const void* W, void* C, int M, int N, int K, int dtype,
-                      int w_layout, int out_dtype, GemmEpilogue ep, hipStream_t stream) {
+                      int w_layout, int out_dtype, GemmEpilogue ep, hipStream_t stream,
+                      const StepGate& gate) {
   if (dtype == DG_F32) {
     dim3 grid((N + 127) / 128, M);
     gemm_f32_kernel<<<grid, 128, 0, stream>>>(static_cast<const float*>(A),
@@ -295,6 +298,8 @@ dg_status launch_gemm(const void* A, const void* W, void* C, int M, int N, int K
   g.out_dtype = ep == kAccumulateF32 ? DG_F32 : out_dtype;
   g.accumulate = ep == kAccumulateF32;
   g.y_fastest = 1;
+  g.gate = gate.n_done;
+  g.gate_n = gate.n;
   const dg_status st = w_layout == DG_LAYOUT_TILED ? launch_gemm_bf16<true>(g, M, N, K, stream)
                                                     : launch_gemm_bf16<false>(g, M, N, K, stream);
   if (st != DG_OK) return st;
@@ -316,7 +321,7 @@ bool dense_xt_supported(int M, int N, int K) {
 }
 
 dg_status launch_qkv_rope(const void* A, const void* W, int K, int w_layout, const QkvRope& r,
-                          hipStream_t stream) {
+                          hipStream_t stream, const StepGate& gate) {
   const int M = r.B * r.Lq;
   const int N = (r.Hq + 2 * r.Hkv) * r.dh;
   if (!qkv_rope_supported(r, K) || (r.x_tiled && w_layout != DG_LAYOUT_TILED))
@@ -335,6 +340,8 @@ dg_status launch_qkv_rope(const void* A, const void* W, int K, int w_layout, con
   g.k_cache = static_cast<bf16_t*>(r.k_cache);
   g.v_cache = static_cast<bf16_t*>(r.v_cache);
   g.x_tiled = r.x_tiled;
+  g.gate = gate.n_done;
+  g.gate_n = gate.n;
   const int rt = r.x_tiled ? kXtRT : kProjRT, tb = r.x_tiled ? kXtTB : kProjTB;
   g.n_tiles_x = N / (16 * rt);
   g.n_tiles_y = (M + 16 * tb - 1) / (16 * tb);
@@ -354,7 +361,8 @@ dg_status launch_qkv_rope(const void* A, const void* W, int K, int w_layout, con
 }
 
 dg_status launch_gemm_xt(const void* A, const void* W, void* C, int M, int N, int K,
-                         int out_dtype, GemmEpilogue ep, hipStream_t stream) {
+                         int out_dtype, GemmEpilogue ep, hipStream_t stream,
+                         const StepGate& gate) {
   if (!dense_xt_supported(M, N, K) || (out_dtype != DG_BF16 && out_dtype != DG_F32) ||
       (ep == kAccumulateF32 && out_dtype != DG_F32))
     return DG_ERR_UNSUPPORTED;
@@ -365,6 +373,8 @@ dg_status launch_gemm_xt(const void* A, const void* W, void* C, int M, int N, in
   g.accumulate = ep == kAccumulateF32;
   g.y_fastest = 1;
   g.x_tiled = 1;
+  g.gate = gate.n_done;
+  g.gate_n = gate.n;
   g.n_tiles_x = N / (16 * kXtRT);
   g.n_tiles_y = (M + 16 * kXtTB - 1) / (16 * kXtTB);
   g.n_tiles_total = g.n_tiles_x * g.n_tiles_y;
@@ -391,7 +401,8 @@ static dg_status launch_gemm_bf16(GemmArgs& g, int M, int N, int K, hipStream_t 
     const unsigned dl_grid = (grid.x * grid.y + 7) / 8 * 8;
     if (kWideDirectLds)
       gemm_wide_dl_kernel<<<dl_grid, 512, kDlSmemBytes, stream>>>(
-          static_cast<const bf16_t*>(g.W), g.X, static_cast<bf16_t*>(g.out), M, N, K);
+          static_cast<const bf16_t*>(g.W), g.X, static_cast<bf16_t*>(g.out), M, N, K, g.gate,
+          g.gate_n);
     else
       gemm_wide_kernel<<<grid, 512, kWideSmemBytes, stream>>>(
           static_cast<const bf16_t*>(g.W), g.X, static_cast<bf16_t*>(g.out), M, N, K);

@@ -81,6 +81,9 @@ struct GemmArgs {
   bf16_t* q_out;
   bf16_t* k_cache;
   bf16_t* v_cache;
+  // step gate (step_gate_closed): null outside the adaptive block loop
+  const int32_t* gate;
+  int gate_n;
 };
 
 __device__ __forceinline__ float gelu_erf(float x) {
@@ -183,6 +186,7 @@ struct WRow {
 template <int RT, int TB, int KS, int PF, int WF, int MODE, bool TILED>
 __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
   static_assert(WF != kWMx4 || TILED, "MXFP4 weights are always tile-packed");
+  if (step_gate_closed(a.gate, a.gate_n)) return;
   using WT = typename std::conditional<WF == kWBf16, bf16_t, uint8_t>::type;
   constexpr int MT = 16 * TB;           // tokens per tile
   constexpr int SK = 64 * KS;           // k per LDS stage
@@ -520,6 +524,7 @@ __global__ __launch_bounds__(64, WPE) void gemm_wave_kernel(GemmArgs a) {
   static_assert(WF != kWMx4 || TILED, "MXFP4 weights are always tile-packed");
   using WT = typename std::conditional<WF == kWBf16, bf16_t, uint8_t>::type;
   constexpr int MT = 16 * TB;
+  if (step_gate_closed(a.gate, a.gate_n)) return;
   const int lane = threadIdx.x;
   const int l16 = lane & 15, g4 = lane >> 4;
 
@@ -796,7 +801,7 @@ __global__ __launch_bounds__(64 * NW, WPE) void gemm_splitk_kernel(GemmArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g4 = lane >> 4;
   const int logical = xcd_logical_tile(blockIdx.x, gridDim.x);
-  if (logical >= a.n_tiles_total) return;
+  if (logical >= a.n_tiles_total || step_gate_closed(a.gate, a.gate_n)) return;
   constexpr bool kRopeTile = RT == 8 || RT == 4;
   if (kRopeTile && a.rope && tid < 64) s_inv[tid] = rope_inv_freq(tid, 128, a.theta);
   const int tx = logical / a.n_tiles_y;       // row tile (token tiles adjacent)

@@ -6,6 +6,15 @@
 
 namespace dg {
 
+// The adaptive block loop's step gate (see step_gate_closed): gated kernels
+// skip their work once n_done[0] >= n; row_done[b] != 0 lets per-row kernels
+// (attention) skip a row that has stopped.  Default: no gate.
+struct StepGate {
+  const int32_t* n_done = nullptr;
+  int n = 0;
+  const int32_t* row_done = nullptr;
+};
+
 // sampler.hip
 size_t sampler_workspace_bytes(int B, int L, int V);
 // api_sampler.cpp: host checks of dg_sampler_step's arguments (not the workspace)
@@ -15,11 +24,13 @@ dg_status check_sampler_step(const void* logits, int logit_dtype, int B, int L, 
                              const uint8_t* renoised, const float* maxprob,
                              const float* entropy, const float* mean_entropy,
                              const int32_t* done);
+// n_done (optional): incremented once by each row in the step that ends it.
 dg_status launch_sampler(const void* logits, int logit_dtype, int B, int L, int V, int step,
                          const dg_sampler_cfg& cfg, const int32_t* prefix_len, int32_t* tokens,
                          uint8_t* committed, uint8_t* renoised, float* maxprob, float* entropy,
                          float* mean_entropy, int32_t* done, int32_t* status,
-                         int32_t* steps_taken, void* ws, hipStream_t stream);
+                         int32_t* steps_taken, void* ws, hipStream_t stream,
+                         int32_t* n_done = nullptr);
 dg_status launch_init_canvas(const int32_t* prefix_len, int B, int L, int V, uint64_t seed,
                              int32_t* tokens, uint8_t* committed, int32_t* done,
                              hipStream_t stream);
@@ -41,6 +52,7 @@ struct AttnArgs {
   void* out;                          // [B, Lq, Hq, dh] dense
   int q_ready = 0;                    // q already rotated in the workspace, k/v in the caches
   int out_tiled = 0;                  // bf16 out in the tiled activation layout (xtile_offset)
+  StepGate gate = {};
 };
 // Scale of the packed q of the bf16 attention kernel: log2(e) / sqrt(dh), so
 // that scores come out of the MFMA in the log2 domain.
@@ -65,11 +77,12 @@ size_t moe_ffn_workspace_bytes(int T, int D, int I, int E, int k, int x_dtype);
 dg_status launch_moe_gate_up(const void* x, int x_dtype, const void* w_gate_up, int w_dtype,
                              int w_layout, const float* s_gate_up, const int32_t* offsets,
                              const int32_t* sorted_rows, int T, int D, int I, int E, int k,
-                             void* h, hipStream_t stream);
+                             void* h, hipStream_t stream, const StepGate& gate = {});
 dg_status launch_moe_down(const void* h, int h_dtype, const void* w_down, int w_dtype,
                           int w_layout, const float* s_down, const float* gates,
                           const int32_t* offsets, const int32_t* sorted_rows, int T, int D, int I,
-                          int E, int k, void* y_slot, hipStream_t stream);
+                          int E, int k, void* y_slot, hipStream_t stream,
+                          const StepGate& gate = {});
 dg_status launch_moe_combine(const void* y_slot, int dtype, int T, int D, int k, float* y,
                              hipStream_t stream);
 // The intermediates launch_moe_ffn carves from its workspace.
@@ -86,7 +99,8 @@ dg_status launch_moe_ffn(const void* x, int x_dtype, const void* w_gate_up, cons
 // in out_dtype, or add into f32 C.
 enum GemmEpilogue { kStore = 0, kAccumulateF32 = 1 };
 dg_status launch_gemm(const void* A, const void* W, void* C, int M, int N, int K, int dtype,
-                      int w_layout, int out_dtype, GemmEpilogue ep, hipStream_t stream);
+                      int w_layout, int out_dtype, GemmEpilogue ep, hipStream_t stream,
+                      const StepGate& gate = {});
 // The bf16 QKV projection with RoPE in its epilogue: q rotated and scaled
 // into the attention workspace's packed q (its first bytes), k rotated and v
 // into the caches at [P, P + Lq).  DG_ERR_UNSUPPORTED when the shape does not
@@ -103,13 +117,14 @@ struct QkvRope {
 };
 bool qkv_rope_supported(const QkvRope& r, int K);
 dg_status launch_qkv_rope(const void* A, const void* W, int K, int w_layout, const QkvRope& r,
-                          hipStream_t stream);
+                          hipStream_t stream, const StepGate& gate = {});
 // C (=|+=) A W^T with A bf16 in the tiled activation layout and W tiled bf16
 // (the O projection over more than 16 tokens); dense_xt_supported says which
 // shapes run.
 bool dense_xt_supported(int M, int N, int K);
 dg_status launch_gemm_xt(const void* A, const void* W, void* C, int M, int N, int K,
-                         int out_dtype, GemmEpilogue ep, hipStream_t stream);
+                         int out_dtype, GemmEpilogue ep, hipStream_t stream,
+                         const StepGate& gate = {});
 // RMSNorm of f32 rows x [M, D] (eps 1e-6, unit gain) into out_dtype.
 dg_status launch_rmsnorm(const float* x, void* out, int M, int D, int out_dtype,
                          hipStream_t stream);

@@ -149,6 +149,7 @@ struct dg_ctx {
   float* mean_entropy = nullptr;
   int32_t* done = nullptr;
   int32_t* status = nullptr;
+  int32_t* n_done = nullptr;       // rows of the current block that have stopped
   int32_t* active = nullptr;       // dg_generate: rows that have not met EOS
   int32_t* blk_tokens = nullptr;   // dg_generate: the current block's tokens [B, L]
   int32_t* blk_steps = nullptr;    // dg_generate: the current block's steps [B]
@@ -156,6 +157,14 @@ struct dg_ctx {
   // non-zero block status there; the host reads and clears it
   int32_t* host_status = nullptr;
   int32_t* host_status_dev = nullptr;    // its device-side address
+  // host-visible copy of n_done, written at the end of each adaptive step
+  int32_t* host_ndone = nullptr;
+  int32_t* host_ndone_dev = nullptr;
+  // the step gate of the steps being enqueued (adaptive mode only)
+  StepGate gate;
+  // graphs are captured on this private stream, never on the caller's
+  hipStream_t cap_stream = nullptr;
+  hipEvent_t step_ev[2] = {nullptr, nullptr};   // adaptive mode: steps in flight
   bool use_graphs = true;
   std::map<GraphKey, hipGraphExec_t> graphs;
   std::vector<const float*> router_override;   // empty: the model's own routing
@@ -170,7 +179,7 @@ namespace {
 struct Layout {
   size_t x, h, qkv, attn_out, router, topk_ids, gates, offsets, sorted_rows, attn_ws, moe_ws,
       logits, samp_ws, tokens, committed, renoised, maxprob, entropy, mean_entropy, done, status,
-      active, blk_tokens, blk_steps, total;
+      n_done, active, blk_tokens, blk_steps, total;
 };
 
 size_t esz(int dt) { return dt == DG_F32 ? 4 : 2; }
@@ -215,6 +224,7 @@ Layout layout(const dg_model_dims& d, int maxB, int maxT) {
   L.mean_entropy = take(maxB * 4);
   L.done = take(maxB * 4);
   L.status = take(4);
+  L.n_done = take(4);
   L.active = take(maxB * 4);
   L.blk_tokens = take(T * 4);
   L.blk_steps = take(maxB * 4);
@@ -286,12 +296,12 @@ dg_status layer(dg_ctx* c, int l, int B, int n, void* kc, void* vc, int Tmax,
   // bf16: the projection rotates q and k in its epilogue and writes q to the
   // attention workspace, k and v to the caches (one launch less per layer)
   if (d.act_dtype == DG_BF16) {
-    st = launch_qkv_rope(c->h, c->wqkv[l], d.d_model, d.weight_layout, r, s);
+    st = launch_qkv_rope(c->h, c->wqkv[l], d.d_model, d.weight_layout, r, s, c->gate);
     if (st == DG_OK) {
       if (kv_only) return DG_OK;
       AttnArgs aa{nullptr, nullptr, nullptr, 0, 0, kc, vc, prefix_len, B, n, d.n_heads,
                   d.n_kv_heads, d.head_dim, Tmax, mode, d.rope_theta, d.act_dtype, c->attn_out, 1,
-                  xt ? 1 : 0};
+                  xt ? 1 : 0, c->gate};
       if ((st = launch_attention(aa, c->attn_ws, s))) return st;
       return layer_tail(c, l, B, n, xt, s);
     }
@@ -307,7 +317,7 @@ dg_status layer(dg_ctx* c, int l, int B, int n, void* kc, void* vc, int Tmax,
                          d.rope_theta, d.act_dtype, false, s);
   AttnArgs aa{qkv, qkv + qd * a, qkv + (qd + kd) * a, qkv_w, qkv_w, kc, vc, prefix_len, B, n,
               d.n_heads, d.n_kv_heads, d.head_dim, Tmax, mode, d.rope_theta, d.act_dtype,
-              c->attn_out};
+              c->attn_out, 0, 0, c->gate};
   if ((st = launch_attention(aa, c->attn_ws, s))) return st;
   return layer_tail(c, l, B, n, false, s);
 }
@@ -322,15 +332,15 @@ dg_status layer_tail(dg_ctx* c, int l, int B, int n, bool xt, hipStream_t s) {
   dg_status st;
   if (xt) {
     if ((st = launch_gemm_xt(c->attn_out, c->wo[l], c->x, T, d.d_model, qd, DG_F32,
-                             kAccumulateF32, s)))
+                             kAccumulateF32, s, c->gate)))
       return st;
   } else if ((st = launch_gemm(c->attn_out, c->wo[l], c->x, T, d.d_model, qd, d.act_dtype,
-                               d.weight_layout, DG_F32, kAccumulateF32, s))) {
+                               d.weight_layout, DG_F32, kAccumulateF32, s, c->gate))) {
     return st;
   }
   if ((st = launch_rmsnorm(c->x, c->h, T, d.d_model, d.act_dtype, s))) return st;
   if ((st = launch_gemm(c->h, c->wr[l], c->router, T, d.n_experts, d.d_model, d.act_dtype,
-                        d.weight_layout, DG_F32, kStore, s)))
+                        d.weight_layout, DG_F32, kStore, s, c->gate)))
     return st;
   const float* route_in = c->router_override.empty() ? c->router : c->router_override[l];
   if ((st = launch_moe_route(route_in, T, d.n_experts, d.top_k, c->topk_ids, c->gates,
@@ -341,11 +351,11 @@ dg_status layer_tail(dg_ctx* c, int l, int B, int n, bool xt, hipStream_t s) {
   moe_ffn_workspace_split(c->moe_ws, T, d.d_ff, d.top_k, d.act_dtype, &h_mid, &y_slot);
   if ((st = launch_moe_gate_up(c->h, d.act_dtype, c->wgu[l], d.expert_dtype, d.weight_layout,
                                c->sgu[l], c->offsets, c->sorted_rows, T, d.d_model, d.d_ff,
-                               d.n_experts, d.top_k, h_mid, s)))
+                               d.n_experts, d.top_k, h_mid, s, c->gate)))
     return st;
   if ((st = launch_moe_down(h_mid, d.act_dtype, c->wd[l], d.expert_dtype, d.weight_layout,
                             c->sd[l], c->gates, c->offsets, c->sorted_rows, T, d.d_model, d.d_ff,
-                            d.n_experts, d.top_k, y_slot, s)))
+                            d.n_experts, d.top_k, y_slot, s, c->gate)))
     return st;
   c->pending_combine = true;
   return DG_OK;
@@ -390,10 +400,16 @@ dg_status forward(dg_ctx* c, const int32_t* tokens, int B, int n, int l0, int l1
   {
     if ((st = norm_input(c, B * n, s))) return st;
     if ((st = launch_gemm(c->h, c->lm, logits, B * n, d.vocab, d.d_model, d.act_dtype,
-                          d.weight_layout, d.act_dtype, kStore, s)))
+                          d.weight_layout, d.act_dtype, kStore, s, c->gate)))
       return st;
   }
   return DG_OK;
+}
+
+// Copies the count of stopped rows to the context's host-visible word.
+__global__ void publish_count_kernel(const int32_t* __restrict__ n_done,
+                                     int32_t* __restrict__ host_word) {
+  __hip_atomic_store(host_word, *n_done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
 dg_status publish_status(dg_ctx* c, hipStream_t s) {
@@ -411,6 +427,7 @@ dg_status enqueue_block_begin(dg_ctx* c, const dg_sampler_cfg& cfg, int B,
                                c->committed, c->done, s)))
     return st;
   if ((st = fill_i32(steps_taken, B, 0, s))) return st;
+  if ((st = fill_i32(c->n_done, 1, 0, s))) return st;
   return fill_i32(c->status, 1, 0, s);
 }
 
@@ -426,7 +443,8 @@ dg_status enqueue_block_steps(dg_ctx* c, const dg_sampler_cfg& cfg, int B, void*
       return st;
     if ((st = launch_sampler(c->logits, d.act_dtype, B, L, d.vocab, step, cfg, prefix_len,
                              c->tokens, c->committed, c->renoised, c->maxprob, c->entropy,
-                             c->mean_entropy, c->done, c->status, steps_taken, c->samp_ws, s)))
+                             c->mean_entropy, c->done, c->status, steps_taken, c->samp_ws, s,
+                             c->n_done)))
       return st;
   }
   return DG_OK;
@@ -512,17 +530,19 @@ dg_status check_run(dg_ctx* c, int B, int n, void* const* kcs, void* const* vcs,
 }
 
 // Launch what enq(stream) enqueues: captured once per key into a hipGraph
-// and replayed when graphs are on and the stream is not the null stream,
-// else enqueued directly.
+// (on the context's private capture stream, so the caller's stream and the
+// work already queued on it are never part of a capture) and replayed on s
+// when graphs are on and s is not the null stream, else enqueued directly.
 template <typename F>
 dg_status run_graph(dg_ctx* ctx, const GraphKey& key, hipStream_t s, F&& enq) {
   if (!ctx->use_graphs || s == nullptr) return enq(s);
   auto it = ctx->graphs.find(key);
   if (it == ctx->graphs.end()) {
-    DG_HIP(hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal));
-    const dg_status st = enq(s);
+    hipStream_t cs = ctx->cap_stream;
+    DG_HIP(hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal));
+    const dg_status st = enq(cs);
     hipGraph_t g = nullptr;
-    hipError_t e = hipStreamEndCapture(s, &g);
+    hipError_t e = hipStreamEndCapture(cs, &g);
     if (st != DG_OK) {
       if (g) (void)hipGraphDestroy(g);
       return st;
@@ -551,13 +571,15 @@ dg_status check_block_cfg(const dg_sampler_cfg* cfg, const char* fn) {
   return DG_OK;
 }
 
-// Steps per captured piece in the adaptive mode: the host reads the rows'
-// done flags after each piece and stops once every row is done.
-constexpr int kAdaptiveChunk = 4;
+// Adaptive mode: steps the host keeps queued beyond the one whose done
+// count it waits for.  The device gates every heavy kernel of a queued step
+// on that count, so a step queued after the block ended costs only its
+// launches.
+constexpr int kAdaptiveLookahead = 1;
 
 // One block (see dg_denoise_block).  part keys: 0 the whole fixed-steps
-// block; 1 + s0 the adaptive piece of steps [s0, s0 + chunk) (with the
-// canvas init when s0 == 0); -2 the commit.
+// block; 1 + s the adaptive step s (with the canvas init when s == 0); -2
+// the commit.
 dg_status run_block(dg_ctx* c, const dg_sampler_cfg& cfg, int B, void* const* kcs,
                     void* const* vcs, int Tmax, int32_t* prefix_len, int32_t* tokens_out,
                     int32_t* steps_taken, hipStream_t s) {
@@ -575,27 +597,43 @@ dg_status run_block(dg_ctx* c, const dg_sampler_cfg& cfg, int B, void* const* kc
     return run_graph(c, key, s, [&](hipStream_t q) {
       return enqueue_block(c, cfg, B, kcs, vcs, Tmax, prefix_len, tokens_out, steps_taken, q);
     });
+  // Adaptive: one graph per step, each gated on the device by the count of
+  // stopped rows (and attention per row by the row's done flag) and ending
+  // with that count copied to a host-visible word.  The host keeps
+  // kAdaptiveLookahead steps queued beyond the one it waits for (an event
+  // after each step), so the device never idles on the host's check; the
+  // steps queued past the block's end run gated.
   const int S = cfg.max_steps;
-  std::vector<int32_t> done(B);
   dg_status st;
-  for (int s0 = 0; s0 < S; s0 += kAdaptiveChunk) {
-    const int s1 = std::min(S, s0 + kAdaptiveChunk);
-    key.part = 1 + s0;
-    st = run_graph(c, key, s, [&](hipStream_t q) {
-      dg_status r = DG_OK;
-      if (s0 == 0 && (r = enqueue_block_begin(c, cfg, B, prefix_len, steps_taken, q))) return r;
-      if ((r = enqueue_block_steps(c, cfg, B, kcs, vcs, Tmax, prefix_len, steps_taken, s0, s1, q)))
-        return r;
-      return publish_status(c, q);
+  auto launch_step = [&](int step) -> dg_status {
+    key.part = 1 + step;
+    dg_status r = run_graph(c, key, s, [&](hipStream_t q) {
+      dg_status e = DG_OK;
+      if (step == 0 && (e = enqueue_block_begin(c, cfg, B, prefix_len, steps_taken, q))) return e;
+      c->gate = StepGate{c->n_done, B, c->done};
+      e = enqueue_block_steps(c, cfg, B, kcs, vcs, Tmax, prefix_len, steps_taken, step, step + 1,
+                              q);
+      c->gate = StepGate{};
+      if (e != DG_OK) return e;
+      if ((e = publish_status(c, q))) return e;
+      publish_count_kernel<<<1, 1, 0, q>>>(c->n_done, c->host_ndone_dev);
+      DG_LAUNCH_CHECK();
+      return DG_OK;
     });
-    if (st != DG_OK) return st;
-    if (s1 == S) break;
-    DG_HIP(hipMemcpyAsync(done.data(), c->done, B * sizeof(int32_t), hipMemcpyDeviceToHost, s));
-    DG_HIP(hipStreamSynchronize(s));
+    if (r != DG_OK) return r;
+    DG_HIP(hipEventRecord(c->step_ev[step % 2], s));
+    return DG_OK;
+  };
+  static_assert(kAdaptiveLookahead == 1, "two step events in flight");
+  *c->host_ndone = 0;
+  for (int step = 0; step <= std::min(kAdaptiveLookahead, S - 1); ++step)
+    if ((st = launch_step(step))) return st;
+  for (int step = 0; step < S; ++step) {
+    DG_HIP(hipEventSynchronize(c->step_ev[step % 2]));
     if ((st = take_status(c, "dg_denoise_block"))) return st;
-    bool all = true;
-    for (int b = 0; b < B; ++b) all = all && done[b] != 0;
-    if (all) break;
+    if (__atomic_load_n(c->host_ndone, __ATOMIC_ACQUIRE) >= B) break;
+    const int next = step + 1 + kAdaptiveLookahead;
+    if (next < S && (st = launch_step(next))) return st;
   }
   key.part = -2;
   return run_graph(c, key, s, [&](hipStream_t q) {
@@ -660,10 +698,10 @@ dg_status dg_ctx_create(dg_ctx** out, const dg_model_dims* dims, const dg_model_
   }
   const Layout L = layout(*dims, max_batch, max_tokens);
   if (!ws || ws_bytes < L.total) return fail(DG_ERR_WORKSPACE, "dg_ctx_create: workspace too small");
-  int32_t* host_word = nullptr;
-  DG_HIP(hipHostMalloc(reinterpret_cast<void**>(&host_word), sizeof(int32_t),
+  int32_t* host_word = nullptr;     // [0] status, [1] stopped-row count
+  DG_HIP(hipHostMalloc(reinterpret_cast<void**>(&host_word), 2 * sizeof(int32_t),
                        hipHostMallocMapped | hipHostMallocCoherent));
-  *host_word = 0;
+  host_word[0] = host_word[1] = 0;
   void* host_word_dev = nullptr;
   const hipError_t he = hipHostGetDevicePointer(&host_word_dev, host_word, 0);
   if (he != hipSuccess) {
@@ -671,9 +709,25 @@ dg_status dg_ctx_create(dg_ctx** out, const dg_model_dims* dims, const dg_model_
     return fail(DG_ERR_HIP, std::string("dg_ctx_create: hipHostGetDevicePointer: ") +
                                 hipGetErrorString(he));
   }
+  hipStream_t cap = nullptr;
+  hipEvent_t ev0 = nullptr, ev1 = nullptr;
+  hipError_t ce = hipStreamCreateWithFlags(&cap, hipStreamNonBlocking);
+  if (ce == hipSuccess) ce = hipEventCreateWithFlags(&ev0, hipEventDisableTiming);
+  if (ce == hipSuccess) ce = hipEventCreateWithFlags(&ev1, hipEventDisableTiming);
+  if (ce != hipSuccess) {
+    if (ev0) (void)hipEventDestroy(ev0);
+    if (cap) (void)hipStreamDestroy(cap);
+    (void)hipHostFree(host_word);
+    return fail(DG_ERR_HIP, std::string("dg_ctx_create: stream / event: ") + hipGetErrorString(ce));
+  }
   dg_ctx* c = new dg_ctx();
   c->host_status = host_word;
   c->host_status_dev = static_cast<int32_t*>(host_word_dev);
+  c->host_ndone = host_word + 1;
+  c->host_ndone_dev = static_cast<int32_t*>(host_word_dev) + 1;
+  c->cap_stream = cap;
+  c->step_ev[0] = ev0;
+  c->step_ev[1] = ev1;
   c->d = *dims;
   c->emb = w->emb;
   c->lm = w->lm_head;
@@ -710,6 +764,7 @@ dg_status dg_ctx_create(dg_ctx** out, const dg_model_dims* dims, const dg_model_
   c->mean_entropy = reinterpret_cast<float*>(b + L.mean_entropy);
   c->done = reinterpret_cast<int32_t*>(b + L.done);
   c->status = reinterpret_cast<int32_t*>(b + L.status);
+  c->n_done = reinterpret_cast<int32_t*>(b + L.n_done);
   c->active = reinterpret_cast<int32_t*>(b + L.active);
   c->blk_tokens = reinterpret_cast<int32_t*>(b + L.blk_tokens);
   c->blk_steps = reinterpret_cast<int32_t*>(b + L.blk_steps);
@@ -720,6 +775,9 @@ dg_status dg_ctx_create(dg_ctx** out, const dg_model_dims* dims, const dg_model_
 dg_status dg_ctx_destroy(dg_ctx* ctx) {
   if (!ctx) return DG_OK;
   for (auto& kv : ctx->graphs) (void)hipGraphExecDestroy(kv.second);
+  for (hipEvent_t e : ctx->step_ev)
+    if (e) (void)hipEventDestroy(e);
+  if (ctx->cap_stream) (void)hipStreamDestroy(ctx->cap_stream);
   if (ctx->host_status) (void)hipHostFree(ctx->host_status);
   delete ctx;
   return DG_OK;

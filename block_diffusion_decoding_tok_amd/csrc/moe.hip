@@ -339,8 +339,11 @@ static int64_t expert_bytes(int N, int K) {
 template <int WF, bool TILED>
 static void launch_gate_up_mfma(const void* x, const void* wgu, const float* sgu,
                                 const int32_t* offsets, const int32_t* sorted_rows, int T, int D,
-                                int I, int E, int k, bf16_t* h, hipStream_t stream) {
+                                int I, int E, int k, bf16_t* h, hipStream_t stream,
+                                const StepGate& gate) {
   GemmArgs g{};
+  g.gate = gate.n_done;
+  g.gate_n = gate.n;
   g.W = wgu;
   g.w_group_stride = WF == kWBf16 ? static_cast<int64_t>(2) * I * D : expert_bytes<WF>(2 * I, D);
   if (TILED && WF != kWMx4 && E > 1) stack_strides(g, 2 * I, D, E);
@@ -373,8 +376,11 @@ static void launch_gate_up_mfma(const void* x, const void* wgu, const float* sgu
 template <int WF, bool TILED>
 static void launch_down_mfma(const bf16_t* h, const void* wd, const float* sd, const float* gates,
                              const int32_t* offsets, const int32_t* sorted_rows, int T, int D,
-                             int I, int E, int k, bf16_t* y_slot, hipStream_t stream) {
+                             int I, int E, int k, bf16_t* y_slot, hipStream_t stream,
+                             const StepGate& gate) {
   GemmArgs d{};
+  d.gate = gate.n_done;
+  d.gate_n = gate.n;
   d.W = wd;
   d.w_group_stride = WF == kWBf16 ? static_cast<int64_t>(D) * I : expert_bytes<WF>(D, I);
   if (TILED && WF != kWMx4 && E > 1) stack_strides(d, D, I, E);
@@ -401,7 +407,7 @@ static void launch_down_mfma(const bf16_t* h, const void* wd, const float* sd, c
 dg_status launch_moe_gate_up(const void* x, int x_dtype, const void* w_gate_up, int w_dtype,
                              int w_layout, const float* s_gate_up, const int32_t* offsets,
                              const int32_t* sorted_rows, int T, int D, int I, int E, int k,
-                             void* h, hipStream_t stream) {
+                             void* h, hipStream_t stream, const StepGate& gate) {
   if (x_dtype == DG_F32) {
     gateup_f32_kernel<<<T * k, 128, 0, stream>>>(static_cast<const float*>(x),
                                                  static_cast<const float*>(w_gate_up), offsets,
@@ -413,13 +419,13 @@ dg_status launch_moe_gate_up(const void* x, int x_dtype, const void* w_gate_up, 
   const bool tiled = w_layout == DG_LAYOUT_TILED;
   bf16_t* hb = static_cast<bf16_t*>(h);
   if (w_dtype == DG_MXFP4) {
-    launch_gate_up_mfma<kWMx4, true>(x, w_gate_up, nullptr, offsets, sorted_rows, T, D, I, E, k, hb, stream);
+    launch_gate_up_mfma<kWMx4, true>(x, w_gate_up, nullptr, offsets, sorted_rows, T, D, I, E, k, hb, stream, gate);
   } else if (w_dtype == DG_FP8_E4M3) {
-    if (tiled) launch_gate_up_mfma<kWFp8, true>(x, w_gate_up, s_gate_up, offsets, sorted_rows, T, D, I, E, k, hb, stream);
-    else launch_gate_up_mfma<kWFp8, false>(x, w_gate_up, s_gate_up, offsets, sorted_rows, T, D, I, E, k, hb, stream);
+    if (tiled) launch_gate_up_mfma<kWFp8, true>(x, w_gate_up, s_gate_up, offsets, sorted_rows, T, D, I, E, k, hb, stream, gate);
+    else launch_gate_up_mfma<kWFp8, false>(x, w_gate_up, s_gate_up, offsets, sorted_rows, T, D, I, E, k, hb, stream, gate);
   } else {
-    if (tiled) launch_gate_up_mfma<kWBf16, true>(x, w_gate_up, nullptr, offsets, sorted_rows, T, D, I, E, k, hb, stream);
-    else launch_gate_up_mfma<kWBf16, false>(x, w_gate_up, nullptr, offsets, sorted_rows, T, D, I, E, k, hb, stream);
+    if (tiled) launch_gate_up_mfma<kWBf16, true>(x, w_gate_up, nullptr, offsets, sorted_rows, T, D, I, E, k, hb, stream, gate);
+    else launch_gate_up_mfma<kWBf16, false>(x, w_gate_up, nullptr, offsets, sorted_rows, T, D, I, E, k, hb, stream, gate);
   }
   DG_LAUNCH_CHECK();
   return DG_OK;
@@ -428,7 +434,7 @@ dg_status launch_moe_gate_up(const void* x, int x_dtype, const void* w_gate_up, 
 dg_status launch_moe_down(const void* h, int h_dtype, const void* w_down, int w_dtype,
                           int w_layout, const float* s_down, const float* gates,
                           const int32_t* offsets, const int32_t* sorted_rows, int T, int D, int I,
-                          int E, int k, void* y_slot, hipStream_t stream) {
+                          int E, int k, void* y_slot, hipStream_t stream, const StepGate& gate) {
   if (h_dtype == DG_F32) {
     down_f32_kernel<<<T * k, 128, 0, stream>>>(static_cast<const float*>(h),
                                                static_cast<const float*>(w_down), offsets,
@@ -441,13 +447,13 @@ dg_status launch_moe_down(const void* h, int h_dtype, const void* w_down, int w_
   const bf16_t* hb = static_cast<const bf16_t*>(h);
   bf16_t* yb = static_cast<bf16_t*>(y_slot);
   if (w_dtype == DG_MXFP4) {
-    launch_down_mfma<kWMx4, true>(hb, w_down, nullptr, gates, offsets, sorted_rows, T, D, I, E, k, yb, stream);
+    launch_down_mfma<kWMx4, true>(hb, w_down, nullptr, gates, offsets, sorted_rows, T, D, I, E, k, yb, stream, gate);
   } else if (w_dtype == DG_FP8_E4M3) {
-    if (tiled) launch_down_mfma<kWFp8, true>(hb, w_down, s_down, gates, offsets, sorted_rows, T, D, I, E, k, yb, stream);
-    else launch_down_mfma<kWFp8, false>(hb, w_down, s_down, gates, offsets, sorted_rows, T, D, I, E, k, yb, stream);
+    if (tiled) launch_down_mfma<kWFp8, true>(hb, w_down, s_down, gates, offsets, sorted_rows, T, D, I, E, k, yb, stream, gate);
+    else launch_down_mfma<kWFp8, false>(hb, w_down, s_down, gates, offsets, sorted_rows, T, D, I, E, k, yb, stream, gate);
   } else {
-    if (tiled) launch_down_mfma<kWBf16, true>(hb, w_down, nullptr, gates, offsets, sorted_rows, T, D, I, E, k, yb, stream);
-    else launch_down_mfma<kWBf16, false>(hb, w_down, nullptr, gates, offsets, sorted_rows, T, D, I, E, k, yb, stream);
+    if (tiled) launch_down_mfma<kWBf16, true>(hb, w_down, nullptr, gates, offsets, sorted_rows, T, D, I, E, k, yb, stream, gate);
+    else launch_down_mfma<kWBf16, false>(hb, w_down, nullptr, gates, offsets, sorted_rows, T, D, I, E, k, yb, stream, gate);
   }
   DG_LAUNCH_CHECK();
   return DG_OK;

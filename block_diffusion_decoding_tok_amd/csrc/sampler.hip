@@ -201,7 +201,7 @@ __global__ __launch_bounds__(kFinishThreads) void sampler_finish_kernel(
     int32_t* __restrict__ tokens, uint8_t* __restrict__ committed,
     uint8_t* __restrict__ renoised, float* __restrict__ maxprob, float* __restrict__ entropy,
     float* __restrict__ mean_entropy, int32_t* __restrict__ done, int32_t* __restrict__ status,
-    int32_t* __restrict__ steps_taken) {
+    int32_t* __restrict__ steps_taken, int32_t* __restrict__ n_done) {
   const int b = blockIdx.x;
   if (done[b]) return;
   const int tid = threadIdx.x;
@@ -339,6 +339,7 @@ __global__ __launch_bounds__(kFinishThreads) void sampler_finish_kernel(
   if (tid == 0) {
     mean_entropy[b] = static_cast<float>(hbar);
     done[b] = ends ? 1 : 0;
+    if (ends && n_done) atomicAdd(n_done, 1);
     if (steps_taken) steps_taken[b] += 1;
     if (anynf && status) atomicOr(status, DG_STATUS_NONFINITE_LOGITS);
   }
@@ -372,7 +373,7 @@ dg_status launch_sampler(const void* logits, int logit_dtype, int B, int L, int 
                          const dg_sampler_cfg& cfg, const int32_t* prefix_len, int32_t* tokens,
                          uint8_t* committed, uint8_t* renoised, float* maxprob, float* entropy,
                          float* mean_entropy, int32_t* done, int32_t* status,
-                         int32_t* steps_taken, void* ws, hipStream_t stream) {
+                         int32_t* steps_taken, void* ws, hipStream_t stream, int32_t* n_done) {
   const int nsplit = (V + kSampSlice - 1) / kSampSlice;
   const int slice = ((V + nsplit - 1) / nsplit + 7) / 8 * 8;
   const int S = cfg.max_steps;
@@ -405,7 +406,7 @@ dg_status launch_sampler(const void* logits, int logit_dtype, int B, int L, int 
   sampler_finish_kernel<<<B, kFinishThreads, smem, stream>>>(
       part, L, npow2, V, nsplit, invT, step, ends_at, adaptive, cfg.stop_entropy, cfg.commit_prob,
       cfg.renoise_prob, cfg.commit_policy, cfg.entropy_bound, k0, k1, prefix_len, tokens,
-      committed, renoised, maxprob, entropy, mean_entropy, done, status, steps_taken);
+      committed, renoised, maxprob, entropy, mean_entropy, done, status, steps_taken, n_done);
   DG_LAUNCH_CHECK();
   return DG_OK;
 }

@@ -375,11 +375,15 @@ dg_status dg_prefill(dg_ctx* ctx, const int32_t* prompt, int B, int n, void* con
  *   tokens_out [B, L] i32; steps_taken [B] i32 (steps each row ran).
  *   requires B <= max_batch, L <= max_tokens, P_b + L <= Tmax.
  * With fixed_steps the block is one asynchronous hipGraph (graphs on).  In
- * the adaptive mode the steps run in chunks of a few steps and the call
- * waits on the stream after each chunk to read the rows' done flags, so it
- * stops as soon as every row is done; it returns once the block is queued
- * behind the last chunk.  Non-finite logits: DG_ERR_NONFINITE, as described
- * at dg_ctx_check_status. */
+ * the adaptive mode each step is its own graph: the sampler counts the rows
+ * that stopped on the device, and every heavy kernel of a step (projections,
+ * attention -- also per stopped row --, experts, LM head, sampler) returns
+ * at once when that count equals B.  The host keeps one step queued beyond
+ * the step it waits for (an event per step, no stream synchronization) and
+ * reads the count from a host-visible word after that step; once every row
+ * stopped it queues the commit, so at most one step after the end runs, and
+ * that one gated.  The call returns once the commit is queued.  Non-finite
+ * logits: DG_ERR_NONFINITE, as described at dg_ctx_check_status. */
 dg_status dg_denoise_block(dg_ctx* ctx, const dg_sampler_cfg* cfg, int B, void* const* k_caches,
                            void* const* v_caches, int Tmax, int32_t* prefix_len,
                            int32_t* tokens_out, int32_t* steps_taken, void* stream);
