@@ -127,6 +127,7 @@ struct dg_ctx {
   std::vector<const void*> wqkv, wo, wr, wgu, wd;
   std::vector<const float*> sgu, sd;
   int max_batch = 0, max_tokens = 0;
+  int max_prefill = 0;             // tokens (all rows) per prefill forward
   // workspace carve-up
   float* x = nullptr;
   void* h = nullptr;
@@ -184,18 +185,24 @@ struct Layout {
 
 size_t esz(int dt) { return dt == DG_F32 ? 4 : 2; }
 
-size_t attn_ws_max(const dg_model_dims& d, int maxB, int maxT) {
+// The attention workspace of any forward the context runs: B <= maxB rows of
+// n <= maxT tokens (canvas, AR, small prefill chunks) or of n <= maxP / B
+// tokens (prefill chunks).
+size_t attn_ws_max(const dg_model_dims& d, int maxB, int maxT, int maxP) {
   size_t m = 0;
   for (int B = 1; B <= maxB; ++B)
-    for (int n = 1; n <= maxT; ++n)
+    for (int n = 1; n <= std::max(maxT, maxP / B); ++n)
       m = std::max(m, attention_workspace_bytes(B, n, d.n_heads, d.n_kv_heads, d.head_dim,
                                                 1 << 30, d.act_dtype));
   return m;
 }
 
-Layout layout(const dg_model_dims& d, int maxB, int maxT) {
+// maxP: tokens (all rows) of one prefill forward; the activation buffers
+// hold max(maxB * maxT, maxP) tokens, the canvas state and logits maxB * maxT.
+Layout layout(const dg_model_dims& d, int maxB, int maxT, int maxP) {
   Layout L{};
-  const size_t T = static_cast<size_t>(maxB) * maxT;
+  const size_t Tc = static_cast<size_t>(maxB) * maxT;
+  const size_t T = std::max(Tc, static_cast<size_t>(maxP));
   const size_t qkv_w = static_cast<size_t>(d.n_heads + 2 * d.n_kv_heads) * d.head_dim;
   const size_t a = esz(d.act_dtype);
   size_t off = 0;
@@ -210,23 +217,23 @@ Layout layout(const dg_model_dims& d, int maxB, int maxT) {
   L.gates = take(T * d.top_k * 4);
   L.offsets = take((d.n_experts + 1) * 4);
   L.sorted_rows = take(T * d.top_k * 4);
-  L.attn_ws = take(attn_ws_max(d, maxB, maxT));
+  L.attn_ws = take(attn_ws_max(d, maxB, maxT, maxP));
   L.moe_ws = take(std::max(moe_ffn_workspace_bytes(static_cast<int>(T), d.d_model, d.d_ff,
                                                    d.n_experts, d.top_k, d.act_dtype),
                            moe_route_workspace_bytes(static_cast<int>(T), d.n_experts, d.top_k)));
-  L.logits = take(T * d.vocab * a);
+  L.logits = take(Tc * d.vocab * a);
   L.samp_ws = take(sampler_workspace_bytes(maxB, maxT, d.vocab));
-  L.tokens = take(T * 4);
-  L.committed = take(T);
-  L.renoised = take(T);
-  L.maxprob = take(T * 4);
-  L.entropy = take(T * 4);
+  L.tokens = take(T * 4);            // also stages a prefill chunk's ids
+  L.committed = take(Tc);
+  L.renoised = take(Tc);
+  L.maxprob = take(Tc * 4);
+  L.entropy = take(Tc * 4);
   L.mean_entropy = take(maxB * 4);
   L.done = take(maxB * 4);
   L.status = take(4);
   L.n_done = take(4);
   L.active = take(maxB * 4);
-  L.blk_tokens = take(T * 4);
+  L.blk_tokens = take(Tc * 4);
   L.blk_steps = take(maxB * 4);
   L.total = off;
   return L;
@@ -516,13 +523,14 @@ dg_status take_status(dg_ctx* c, const char* fn) {
 }
 
 dg_status check_run(dg_ctx* c, int B, int n, void* const* kcs, void* const* vcs, int Tmax,
-                    const int32_t* prefix_len, const char* fn) {
+                    const int32_t* prefix_len, const char* fn, int max_n = 0) {
+  if (max_n == 0 && c) max_n = c->max_tokens;
   DG_CHECK_ARG(c != nullptr, std::string(fn) + ": ctx is null");
   DG_CHECK_ARG(kcs && vcs && prefix_len, std::string(fn) + ": null pointer");
   for (int l = 0; l < c->d.n_layers; ++l)
     DG_CHECK_ARG(kcs[l] && vcs[l], std::string(fn) + ": null cache pointer");
   DG_CHECK_SHAPE(B > 0 && B <= c->max_batch, std::string(fn) + ": B outside [1, max_batch]");
-  DG_CHECK_SHAPE(n > 0 && n <= c->max_tokens, std::string(fn) + ": n outside [1, max_tokens]");
+  DG_CHECK_SHAPE(n > 0 && n <= max_n, std::string(fn) + ": n outside [1, max_tokens]");
   DG_CHECK_SHAPE(Tmax >= n, std::string(fn) + ": Tmax smaller than the block");
   DG_CHECK_SHAPE(c->router_override.empty() || B * n <= c->router_override_tokens,
                  std::string(fn) + ": more tokens than the router override holds");
@@ -673,19 +681,25 @@ __global__ __launch_bounds__(256) void eos_block_kernel(
 
 extern "C" {
 
-size_t dg_ctx_workspace_size(const dg_model_dims* dims, int max_batch, int max_tokens) {
-  if (!dims || max_batch <= 0 || max_tokens <= 0 || check_dims(dims) != DG_OK) return 0;
-  return layout(*dims, max_batch, max_tokens).total;
+size_t dg_ctx_workspace_size(const dg_model_dims* dims, int max_batch, int max_tokens,
+                             int max_prefill_tokens) {
+  if (!dims || max_batch <= 0 || max_tokens <= 0 || max_prefill_tokens < 0 ||
+      max_prefill_tokens > (1 << 16) || check_dims(dims) != DG_OK)
+    return 0;
+  return layout(*dims, max_batch, max_tokens, max_prefill_tokens).total;
 }
 
 dg_status dg_ctx_create(dg_ctx** out, const dg_model_dims* dims, const dg_model_weights* w,
-                        int max_batch, int max_tokens, void* ws, size_t ws_bytes) {
+                        int max_batch, int max_tokens, int max_prefill_tokens, void* ws,
+                        size_t ws_bytes) {
   set_error("");
   DG_CHECK_ARG(out && w, "dg_ctx_create: null pointer");
   dg_status st = check_dims(dims);
   if (st != DG_OK) return st;
   DG_CHECK_SHAPE(max_batch > 0 && max_batch < (1 << 24) && max_tokens > 0 && max_tokens <= 4096,
                  "dg_ctx_create: bad max_batch / max_tokens");
+  DG_CHECK_SHAPE(max_prefill_tokens >= 0 && max_prefill_tokens <= (1 << 16),
+                 "dg_ctx_create: max_prefill_tokens outside [0, 65536]");
   const int nl = dims->n_layers;
   DG_CHECK_ARG(w->emb && w->lm_head && w->wqkv && w->wo && w->wr && w->w_gate_up && w->w_down,
                "dg_ctx_create: null weight pointer");
@@ -696,7 +710,7 @@ dg_status dg_ctx_create(dg_ctx** out, const dg_model_dims* dims, const dg_model_
       DG_CHECK_ARG(w->s_gate_up && w->s_down && w->s_gate_up[l] && w->s_down[l],
                    "dg_ctx_create: fp8 experts need scales");
   }
-  const Layout L = layout(*dims, max_batch, max_tokens);
+  const Layout L = layout(*dims, max_batch, max_tokens, max_prefill_tokens);
   if (!ws || ws_bytes < L.total) return fail(DG_ERR_WORKSPACE, "dg_ctx_create: workspace too small");
   int32_t* host_word = nullptr;     // [0] status, [1] stopped-row count
   DG_HIP(hipHostMalloc(reinterpret_cast<void**>(&host_word), 2 * sizeof(int32_t),
@@ -742,6 +756,7 @@ dg_status dg_ctx_create(dg_ctx** out, const dg_model_dims* dims, const dg_model_
   }
   c->max_batch = max_batch;
   c->max_tokens = max_tokens;
+  c->max_prefill = max_prefill_tokens;
   char* b = static_cast<char*>(ws);
   c->x = reinterpret_cast<float*>(b + L.x);
   c->h = b + L.h;
@@ -818,7 +833,10 @@ dg_status dg_model_forward(dg_ctx* ctx, const int32_t* tokens, float* x, int B, 
                            void* const* v_caches, int Tmax, const int32_t* prefix_len,
                            int mask_mode, void* logits, void* stream) {
   set_error("");
-  dg_status st = check_run(ctx, B, n, k_caches, v_caches, Tmax, prefix_len, "dg_model_forward");
+  // token counts up to a prefill chunk (the activation buffers hold it)
+  const int max_n = ctx ? std::max(ctx->max_tokens, B > 0 ? ctx->max_prefill / B : 0) : 0;
+  dg_status st = check_run(ctx, B, n, k_caches, v_caches, Tmax, prefix_len, "dg_model_forward",
+                           max_n);
   if (st != DG_OK) return st;
   DG_CHECK_ARG(x != nullptr, "dg_model_forward: x is null");
   DG_CHECK_ARG(mask_mode == DG_MASK_CANVAS || mask_mode == DG_MASK_CAUSAL,
@@ -843,9 +861,12 @@ dg_status dg_prefill(dg_ctx* ctx, const int32_t* prompt, int B, int n, void* con
   set_error("");
   DG_CHECK_ARG(ctx && prompt, "dg_prefill: null pointer");
   DG_CHECK_SHAPE(n > 0 && n <= Tmax, "dg_prefill: n outside [1, Tmax]");
-  const int chunk = ctx->max_tokens;
+  DG_CHECK_SHAPE(B > 0 && B <= ctx->max_batch, "dg_prefill: B outside [1, max_batch]");
+  // tokens per row of one chunk: the larger of the canvas limit and the
+  // prefill limit shared by the rows
+  const int chunk = std::max(ctx->max_tokens, ctx->max_prefill / B);
   dg_status st = check_run(ctx, B, std::min(n, chunk), k_caches, v_caches, Tmax, prefix_len,
-                           "dg_prefill");
+                           "dg_prefill", chunk);
   if (st != DG_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   // the chunk's token ids, contiguous per row, staged in the canvas buffer

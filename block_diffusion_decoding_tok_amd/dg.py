@@ -96,9 +96,9 @@ _SIGS = {
     "dg_moe_combine": (_I, [_VP, _I, _I, _I, _I, _VP, _VP]),
     "dg_linear": (_I, [_VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _I, _VP]),
     "dg_ar_decode": (_I, [_VP, _I, _I, _VP, C.POINTER(_VP), C.POINTER(_VP), _I, _VP, _VP, _VP]),
-    "dg_ctx_workspace_size": (_SZ, [C.POINTER(dg_model_dims), _I, _I]),
+    "dg_ctx_workspace_size": (_SZ, [C.POINTER(dg_model_dims), _I, _I, _I]),
     "dg_ctx_create": (_I, [C.POINTER(_VP), C.POINTER(dg_model_dims),
-                           C.POINTER(dg_model_weights), _I, _I, _VP, _SZ]),
+                           C.POINTER(dg_model_weights), _I, _I, _I, _VP, _SZ]),
     "dg_ctx_destroy": (_I, [_VP]),
     "dg_ctx_set_graphs": (_I, [_VP, _I]),
     "dg_ctx_check_status": (_I, [_VP, _VP]),
@@ -404,7 +404,8 @@ class DGModel:
     workspace outlive the context."""
 
     def __init__(self, dims, weights, max_batch, max_tokens, act_dtype, expert_dtype,
-                 rope_theta=10000.0, device="cuda", weight_layout=DG_LAYOUT_ROWMAJOR):
+                 rope_theta=10000.0, device="cuda", weight_layout=DG_LAYOUT_ROWMAJOR,
+                 max_prefill_tokens=0):
         self.dims = dims
         self.weights = weights
         nl = dims.NL
@@ -418,11 +419,13 @@ class DGModel:
         self.cw = dg_model_weights(weights["emb"].data_ptr(), weights["lm"].data_ptr(),
                                    a["wqkv"], a["wo"], a["wr"], a["wgu"], a["wd"], a["sgu"],
                                    a["sd"])
-        nbytes = lib().dg_ctx_workspace_size(C.byref(self.cdims), max_batch, max_tokens)
+        nbytes = lib().dg_ctx_workspace_size(C.byref(self.cdims), max_batch, max_tokens,
+                                             max_prefill_tokens)
         self.ws = _workspace(nbytes, device)
         h = C.c_void_p()
         _check(lib().dg_ctx_create(C.byref(h), C.byref(self.cdims), C.byref(self.cw),
-                                   max_batch, max_tokens, self.ws.data_ptr(), self.ws.numel()))
+                                   max_batch, max_tokens, max_prefill_tokens,
+                                   self.ws.data_ptr(), self.ws.numel()))
         self.ctx = h
 
     def close(self):

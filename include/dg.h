@@ -314,12 +314,21 @@ typedef struct {
 typedef struct dg_ctx dg_ctx;
 
 /* Workspace for a context serving up to max_batch rows of max_tokens tokens
- * per forward (the canvas length, also the prefill chunk). */
-size_t dg_ctx_workspace_size(const dg_model_dims* dims, int max_batch, int max_tokens);
+ * per forward (the canvas length, the AR and model-forward limit) and prefill
+ * forwards of up to max_prefill_tokens tokens over all rows (a row's prefill
+ * chunk is max(max_tokens, max_prefill_tokens / B) tokens; 0: chunks of
+ * max_tokens).  Only the activation buffers grow with max_prefill_tokens
+ * (about 80 KB per token at the decoder's full width), not the logits and
+ * sampler buffers.  max_prefill_tokens <= 65536.  0 on invalid input. */
+size_t dg_ctx_workspace_size(const dg_model_dims* dims, int max_batch, int max_tokens,
+                             int max_prefill_tokens);
 /* Creates a context holding the dims, copies of the weight pointers (not the
- * weights) and the workspace pointer; the caller keeps every buffer alive. */
+ * weights) and the workspace pointer; the caller keeps every buffer alive.
+ * Also allocates the context's own small host state: a pinned host word
+ * pair (status and stopped-row count), a capture stream and two events. */
 dg_status dg_ctx_create(dg_ctx** out, const dg_model_dims* dims, const dg_model_weights* w,
-                        int max_batch, int max_tokens, void* ws, size_t ws_bytes);
+                        int max_batch, int max_tokens, int max_prefill_tokens, void* ws,
+                        size_t ws_bytes);
 dg_status dg_ctx_destroy(dg_ctx* ctx);
 /* use_graphs != 0 (default): dg_denoise_block replays a captured hipGraph. */
 dg_status dg_ctx_set_graphs(dg_ctx* ctx, int use_graphs);
@@ -350,8 +359,8 @@ dg_status dg_ctx_check_status(dg_ctx* ctx, void* stream);
  * instead of the one its random weights produce. */
 dg_status dg_ctx_set_router_override(dg_ctx* ctx, const float* const* logits, int n_tokens);
 
-/* dg_model_forward: one forward over n tokens per row at cache positions
- * [P_b, P_b + n).  If tokens != NULL the residual x is first set to the
+/* dg_model_forward: one forward over n tokens per row (n <= max(max_tokens,
+ * max_prefill_tokens / B)) at cache positions [P_b, P_b + n).  If tokens != NULL the residual x is first set to the
  * embeddings; layers [layer_begin, layer_end) are applied to x [B * n, D] f32
  * in place (each writes its rotated K/V to its cache at [P_b, P_b + n)); if
  * logits != NULL (requires layer_end == n_layers) the final RMSNorm + LM head
@@ -362,8 +371,11 @@ dg_status dg_model_forward(dg_ctx* ctx, const int32_t* tokens, float* x, int B, 
                            int mask_mode, void* logits, void* stream);
 
 /* dg_prefill: encode a prompt into the KV cache ([TR] "DiffusionGemma의 구성",
- * flowchart: prompt -> KV cache) with a causal mask, in chunks of at most
- * max_tokens, starting at prefix_len[b] and advancing it by n. */
+ * flowchart: prompt -> KV cache; [GUIDE] "vLLM으로 서빙하기": chunked
+ * prefill) with a causal mask, in chunks of max(max_tokens,
+ * max_prefill_tokens / B) tokens per row (large chunks stream each layer's
+ * expert weights once per chunk instead of once per canvas-sized chunk),
+ * starting at prefix_len[b] and advancing it by n.  prompt [B, n] i32. */
 dg_status dg_prefill(dg_ctx* ctx, const int32_t* prompt, int B, int n, void* const* k_caches,
                      void* const* v_caches, int Tmax, int32_t* prefix_len, void* stream);
 

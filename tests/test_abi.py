@@ -112,14 +112,19 @@ def test_moe_steps_reject_bad_calls(lib):
 def test_ctx_validation(lib):
     dims = dg.dg_model_dims(30, 2816, 16, 8, 128, 128, 8, 704, 262144, 10000.0,
                             dg.DG_BF16, dg.DG_FP8_E4M3, dg.DG_LAYOUT_TILED)
-    n = lib.dg_ctx_workspace_size(C.byref(dims), 1, 256)
+    n = lib.dg_ctx_workspace_size(C.byref(dims), 1, 256, 0)
     assert n > 256 * 262144 * 2           # holds at least the logits
+    # a prefill limit grows the activation buffers only (not the logits)
+    n2 = lib.dg_ctx_workspace_size(C.byref(dims), 1, 256, 2048)
+    assert n < n2 < n + 2048 * 200 * 1024
+    assert lib.dg_ctx_workspace_size(C.byref(dims), 1, 256, -1) == 0
+    assert lib.dg_ctx_workspace_size(C.byref(dims), 1, 256, (1 << 16) + 1) == 0
     bad = dg.dg_model_dims(30, 2816, 16, 8, 64, 128, 8, 704, 262144, 10000.0,
                            dg.DG_BF16, dg.DG_FP8_E4M3, 0)
-    assert lib.dg_ctx_workspace_size(C.byref(bad), 1, 256) == 0
+    assert lib.dg_ctx_workspace_size(C.byref(bad), 1, 256, 0) == 0
     w = dg.dg_model_weights()
     h = C.c_void_p()
-    assert lib.dg_ctx_create(C.byref(h), C.byref(dims), C.byref(w), 1, 256, None, 0) == -1
+    assert lib.dg_ctx_create(C.byref(h), C.byref(dims), C.byref(w), 1, 256, 0, None, 0) == -1
 
 
 def test_linear_rejects_bad_calls(lib):
@@ -151,9 +156,9 @@ def test_mxfp4_rejects_bad_calls(lib):
     # a model with MXFP4 experts needs the tiled layout
     dims = dg.dg_model_dims(30, 2816, 16, 8, 128, 128, 8, 704, 262144, 10000.0,
                             dg.DG_BF16, dg.DG_MXFP4, dg.DG_LAYOUT_ROWMAJOR)
-    assert lib.dg_ctx_workspace_size(C.byref(dims), 1, 256) == 0
+    assert lib.dg_ctx_workspace_size(C.byref(dims), 1, 256, 0) == 0
     dims.weight_layout = dg.DG_LAYOUT_TILED
-    assert lib.dg_ctx_workspace_size(C.byref(dims), 1, 256) > 0
+    assert lib.dg_ctx_workspace_size(C.byref(dims), 1, 256, 0) > 0
 
 
 def test_generate_and_policy_reject_bad_calls(lib):

@@ -196,15 +196,17 @@ def full_layers(request):
     for l in range(d.NL):
         w0[f"wgu.{l}"] = torch.zeros_like(w[f"wgu.{l}"])
         w0[f"wd.{l}"] = torch.zeros_like(w[f"wd.{l}"])
+    # activations for prefill forwards of up to 2048 tokens
+    kw = dict(max_prefill_tokens=2048)
     if request.param == "tiled":
         model = dg.DGModel(d, _packed(w), 4, 256, dg.DG_BF16, dg.DG_FP8_E4M3,
-                           weight_layout=dg.DG_LAYOUT_TILED)
+                           weight_layout=dg.DG_LAYOUT_TILED, **kw)
         model0 = dg.DGModel(d, _packed(w0), 4, 256, dg.DG_BF16, dg.DG_FP8_E4M3,
-                            weight_layout=dg.DG_LAYOUT_TILED)
+                            weight_layout=dg.DG_LAYOUT_TILED, **kw)
     else:
-        model = dg.DGModel(d, _dev_weights(w), 4, 256, dg.DG_BF16, dg.DG_FP8_E4M3)
-        model0 = dg.DGModel(d, _dev_weights(w0), 4, 256, dg.DG_BF16, dg.DG_FP8_E4M3)
-    return d, w, model, model0
+        model = dg.DGModel(d, _dev_weights(w), 4, 256, dg.DG_BF16, dg.DG_FP8_E4M3, **kw)
+        model0 = dg.DGModel(d, _dev_weights(w0), 4, 256, dg.DG_BF16, dg.DG_FP8_E4M3, **kw)
+    return d, w, model, model0, request.param
 
 
 def _device_router_logits(x_attn, wr):
@@ -226,7 +228,9 @@ def _topk_gap(r, k):
                                                  (2, 512, True, CAUSAL, 256),
                                                  (1, 300, False, CANVAS, 200),
                                                  (3, 40, True, CAUSAL, 40),
-                                                 (1, 64, False, CAUSAL, 17)])
+                                                 (1, 64, False, CAUSAL, 17),
+                                                 (1, 256, True, CAUSAL, 2048),
+                                                 (2, 100, True, CAUSAL, 1000)])
 def test_full_width_layers_teacher_forced(full_layers, B, P0, planted, mode, n):
     """planted: the router override supplies N(0,1) + hot-expert-skew logits
     (the stated MoE routing) instead of the random router's, so both sides
@@ -238,13 +242,20 @@ def test_full_width_layers_teacher_forced(full_layers, B, P0, planted, mode, n):
     the measured router-logit error.  CAUSAL: an n-token prefill chunk at
     positions [P0, P0 + n) (the prompt path).  Token counts off the 16- and
     64-token tiles (200, 3 x 40, 17) end in partial token blocks of the tiled
-    activation layout; 300 prompt tokens prefill as 256 + 44."""
-    d, w, model, model0 = full_layers
+    activation layout; 300 prompt tokens prefill as 256 + 44.  2048 and
+    2 x 1000 tokens: the large prefill chunks (tiled weights only)."""
+    d, w, model, model0, layout = full_layers
+    if n > 256 and layout != "tiled":
+        pytest.skip("large prefill chunks: checked on the tiled layout")
     override = None
     if planted:
-        override = [torch.from_numpy(router_logits_skewed(B * n, d.E, d.k, seed=40 + l)[0])
+        # enough rows for the prompt's prefill chunks too; a forward over
+        # B * n tokens routes with the first B * n rows
+        t_ov = max(B * n, 2048)
+        override = [torch.from_numpy(router_logits_skewed(t_ov, d.E, d.k, seed=40 + l)[0])
                     for l in range(d.NL)]
         model.set_router_override([o.to(DEV) for o in override])
+        override = [o[:B * n] for o in override]
     else:
         model.set_router_override(None)
     m = oracle_model(d, w)
@@ -321,6 +332,40 @@ def test_full_width_layers_teacher_forced(full_layers, B, P0, planted, mode, n):
     torch.cuda.synchronize()
     ref = rmsnorm(x_last) @ to_f64(w["lm"]).T
     assert rel_err_rows(logits.cpu().double().numpy().reshape(-1, d.V), ref) < 2e-2
+
+
+def test_prefill_large_chunks_layer0_cache():
+    """dg_prefill of a 2304-token prompt in chunks of 2048 + 256 tokens
+    (max_prefill_tokens 2048): the prefix advances by the whole prompt and
+    layer 0's cache -- the keys and values of the embedded prompt, causal --
+    matches the oracle's layer 0 over the same prompt from position 0; a
+    second prefill with canvas-sized chunks gives the same layer-0 cache."""
+    d = FULL_LAYER
+    w = model_weights(d, seed=3, expert_dtype="fp8", dense_dtype="bf16")
+    pw = _packed(w)
+    n = 2304
+    prompt = prompt_ids(1, n, d.V, seed=9)
+    out = []
+    for maxp in (2048, 0):
+        model = dg.DGModel(d, pw, 1, 256, dg.DG_BF16, dg.DG_FP8_E4M3,
+                           weight_layout=dg.DG_LAYOUT_TILED, max_prefill_tokens=maxp)
+        kc, vc = _caches(d, 1, n, torch.bfloat16)
+        Pd = torch.zeros(1, dtype=torch.int32, device=DEV)
+        dg.dg_prefill(model, prompt.to(DEV), kc, vc, Pd)
+        torch.cuda.synchronize()
+        assert Pd.cpu().tolist() == [n]
+        out.append((kc[0].cpu().double().numpy(), vc[0].cpu().double().numpy()))
+        model.close()
+    m = oracle_model(d, w, layers=1)
+    x = to_f64(w["emb"])[prompt.numpy()]
+    ok, ov = empty_caches(d, 1, n, layers=1)
+    layer_forward(m, m.layers[0], x, ok[0], ov[0], np.zeros(1, np.int64), CAUSAL)
+    for k_got, v_got in out:
+        ek, ev = rel_err_rows(k_got, ok[0]), rel_err_rows(v_got, ov[0])
+        print(f"layer 0 cache over {n} prompt tokens: K err {ek:.3g}, V err {ev:.3g}")
+        assert ek < 2e-2 and ev < 2e-2
+    # layer 0's K/V depend only on the embeddings: the same bits either way
+    assert np.array_equal(out[0][0], out[1][0]) and np.array_equal(out[0][1], out[1][1])
 
 
 def test_full_vocab_lm_head_sampled():
