@@ -103,6 +103,30 @@ __device__ __forceinline__ void fp8x16_to_bf16(const uint4& q, bf16x8_v& lo, bf1
   hi = bf16x8_v{p[4][0], p[4][1], p[5][0], p[5][1], p[6][0], p[6][1], p[7][0], p[7][1]};
 }
 
+// Cache policy of the weight streams.  The one-wave expert kernel
+// (gemm_wave_kernel) loads its weights with the nontemporal hint, so that
+// weights read once per launch do not displace what the step reuses from the
+// caches (activations, routing tables, the KV cache): the 30-layer step at
+// 256 tokens runs 2.3% faster.  The LDS-staged expert tiles (more tokens per
+// expert, several token tiles reading one weight tile through L2) and the
+// dense projections keep the default policy: with the hint they measured
+// 1.7% (a thousand tokens) and 1% slower.
+constexpr bool kNtWaveW = true;
+__device__ __forceinline__ uint4 load_nt16(const void* p) {
+  typedef unsigned int u32x4_nt __attribute__((ext_vector_type(4)));
+  const u32x4_nt t = __builtin_nontemporal_load(static_cast<const u32x4_nt*>(p));
+  return make_uint4(t[0], t[1], t[2], t[3]);
+}
+__device__ __forceinline__ uint2 load_nt8(const void* p) {
+  typedef unsigned int u32x2_nt __attribute__((ext_vector_type(2)));
+  const u32x2_nt t = __builtin_nontemporal_load(static_cast<const u32x2_nt*>(p));
+  return make_uint2(t[0], t[1]);
+}
+template <bool NT>
+__device__ __forceinline__ uint4 load_w16(const void* p) {
+  return NT ? load_nt16(p) : *static_cast<const uint4*>(p);
+}
+
 // Weight formats of the streamed A operand.
 constexpr int kWBf16 = 0;   // bf16 values
 constexpr int kWFp8 = 1;    // OCP e4m3fn bytes, per-row scale in the epilogue
@@ -111,17 +135,17 @@ constexpr int kWMx4 = 2;    // OCP MXFP4: E2M1 pairs per byte + an E8M0 scale pe
 template <int WF> struct WChunk;
 template <> struct WChunk<kWFp8> {
   uint4 q;
-  template <int SECOND = 0>
-  __device__ void load(const uint8_t* p) { q = *reinterpret_cast<const uint4*>(p); }
+  template <int SECOND = 0, bool NT = false>
+  __device__ void load(const uint8_t* p) { q = load_w16<NT>(p); }
   __device__ void zero() { q = make_uint4(0, 0, 0, 0); }
   __device__ void get(bf16x8_v& a, bf16x8_v& b) const { fp8x16_to_bf16(q, a, b); }
 };
 template <> struct WChunk<kWBf16> {
   uint4 q0, q1;
-  template <int SECOND = 8>
+  template <int SECOND = 8, bool NT = false>
   __device__ void load(const bf16_t* p) {
-    q0 = *reinterpret_cast<const uint4*>(p);
-    q1 = *reinterpret_cast<const uint4*>(p + SECOND);
+    q0 = load_w16<NT>(p);
+    q1 = load_w16<NT>(p + SECOND);
   }
   __device__ void zero() { q0 = q1 = make_uint4(0, 0, 0, 0); }
   __device__ void get(bf16x8_v& a, bf16x8_v& b) const {
@@ -137,8 +161,9 @@ template <> struct WChunk<kWBf16> {
 template <> struct WChunk<kWMx4> {
   uint2 q;
   uint32_t s;
+  template <bool NT = false>
   __device__ void load_mx(const uint8_t* codes, const uint8_t* scale) {
-    q = *reinterpret_cast<const uint2*>(codes);
+    q = NT ? load_nt8(codes) : *reinterpret_cast<const uint2*>(codes);
     s = *scale;
   }
   __device__ void get(bf16x8_v& a, bf16x8_v& b) const {
@@ -628,9 +653,10 @@ __global__ __launch_bounds__(64, WPE) void gemm_wave_kernel(GemmArgs a) {
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       if constexpr (WF == kWMx4)
-        sl.w[rt].load_mx(wtile[rt] + w_lane + cc * kChunk, wtile[rt] + s_lane + cc * kChunk);
+        sl.w[rt].template load_mx<kNtWaveW>(wtile[rt] + w_lane + cc * kChunk,
+                                            wtile[rt] + s_lane + cc * kChunk);
       else
-        sl.w[rt].template load<WRow<WT, TILED>::kSecond>(wtile[rt] + w_lane + cc * kChunk);
+        sl.w[rt].template load<WRow<WT, TILED>::kSecond, kNtWaveW>(wtile[rt] + w_lane + cc * kChunk);
     }
   };
   const uint4 zero4 = make_uint4(0, 0, 0, 0);
