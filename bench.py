@@ -340,6 +340,20 @@ _KERNEL_SOURCES = ["block_diffusion_decoding_tok_amd/csrc/gemm_mfma.h",
 _COUNTER_FILE = os.path.join(ROOT, "profiles", "moe_gate_up_counters_canvas256.md")
 
 
+def forward_floor_bytes(d, B, n, P, experts_touched):
+    """Bytes one forward of n tokens per row (B rows, P cached keys per row)
+    has to move at the least: every layer's dense weights, the fp8 rows and
+    scales of the experts its tokens touch, the K/V cache it attends over
+    (read) and the new keys' K/V (written); the LM head's weights and the
+    logits (written, then read by the sampler or argmax).  Activations are
+    left out (a few MB per layer)."""
+    dense = ((d.Hq + 2 * d.Hkv) * d.dh * d.D + d.D * d.Hq * d.dh + d.E * d.D) * 2
+    experts = experts_touched * ((2 * d.I * d.D + d.D * d.I) + (2 * d.I + d.D) * 4)
+    kv = B * 2 * d.Hkv * d.dh * 2 * ((P + n) + n)
+    head = d.V * d.D * 2 + 2 * B * n * d.V * 2
+    return d.NL * (dense + experts + kv) + head
+
+
 def kernel_source_hash():
     import hashlib
     hsh = hashlib.sha256()
@@ -677,13 +691,29 @@ def main():
         out["ms_per_canvas_forward"] = extra["ms_per_canvas_forward"]
         out["kernel_fractions"] = {"moe_gate_up": {"frac_hbm": round(roof["gbs"] / HBM_PEAK_GBS, 4)},
                                    "attention": extra["attention"], "sampler": extra["sampler"]}
+    # HBM floors (forward_floor_bytes at 8 TB/s): the canvas forward touches
+    # every expert (planted routing), an AR token at most B * k of them
+    canvas_floor_ms = forward_floor_bytes(d, B, CANVAS, PROMPT, d.E) / (HBM_PEAK_GBS * 1e6)
+    out["step_hbm_floor"] = {"ms": round(canvas_floor_ms, 3),
+                             "frac_of_step": round(canvas_floor_ms / (1e3 * elapsed / a.steps), 3),
+                             "note": "weights, K/V cache and logits one canvas forward must move, "
+                                     "at 8 TB/s, against the measured ms per step"}
     if ar_s is not None:
-        out["ar_decode"] = {"steps": AR_STEPS, "ms_per_token": round(1e3 * ar_s / AR_STEPS, 3),
+        ar_ms = 1e3 * ar_s / AR_STEPS
+        ar_floor_ms = forward_floor_bytes(d, B, 1, PROMPT + AR_STEPS // 2,
+                                          min(d.E, B * d.k)) / (HBM_PEAK_GBS * 1e6)
+        out["ar_decode"] = {"steps": AR_STEPS, "ms_per_token": round(ar_ms, 3),
                             "tok_per_s": round(AR_STEPS * B / ar_s, 1),
+                            "hbm_floor_ms_per_token": round(ar_floor_ms, 3),
+                            "frac_of_floor": round(ar_floor_ms / ar_ms, 3),
                             "canvas_forward_vs_ar_forward": round(
-                                (1e3 * elapsed / a.steps) / (1e3 * ar_s / AR_STEPS), 2),
+                                (1e3 * elapsed / a.steps) / ar_ms, 2),
+                            "canvas_forward_vs_ar_forward_at_floors": round(
+                                canvas_floor_ms / ar_floor_ms, 2),
                             "note": "greedy single-token causal steps after the prompt, "
-                                    "one hipGraph, same weights and routing override"}
+                                    "one hipGraph, same weights and routing override; the "
+                                    "ratios compare one canvas step with one AR token, measured "
+                                    "and at the two HBM floors"}
     if prefill_s is not None:
         out["prefill"] = {"tokens": PROMPT * B, "ms": round(1e3 * prefill_s, 2),
                           "tok_per_s": round(PROMPT * B / prefill_s, 1),

@@ -508,6 +508,8 @@ static AttnPlan plan_attention(int B, int Lq, int Hq, int Hkv, int dh, int Tmax,
   if (dtype == DG_BF16) {
     p.tiles = (rows + kAttnRows - 1) / kAttnRows;
     const int base = p.tiles * B * Hkv;
+    // one workgroup per CU (its LDS): more splits than that only add rounds
+    // (a few query rows at 1024 workgroups: 14.2 -> 20.6 us, merge 4.8 -> 9.8)
     const int target = 256;
     int ns = (target + base - 1) / base;
     const int max_ns = (Tmax + kAttnKeys - 1) / kAttnKeys;

@@ -103,14 +103,18 @@ __device__ __forceinline__ void fp8x16_to_bf16(const uint4& q, bf16x8_v& lo, bf1
   hi = bf16x8_v{p[4][0], p[4][1], p[5][0], p[5][1], p[6][0], p[6][1], p[7][0], p[7][1]};
 }
 
-// Cache policy of the weight streams.  The one-wave expert kernel
-// (gemm_wave_kernel) loads its weights with the nontemporal hint, so that
-// weights read once per launch do not displace what the step reuses from the
-// caches (activations, routing tables, the KV cache): the 30-layer step at
-// 256 tokens runs 2.3% faster.  The LDS-staged expert tiles (more tokens per
-// expert, several token tiles reading one weight tile through L2) and the
-// dense projections keep the default policy: with the hint they measured
-// 1.7% (a thousand tokens) and 1% slower.
+// Cache policy of the weight streams.  In the one-wave expert kernel
+// (gemm_wave_kernel) the item that is its expert's last token tile loads the
+// weights with the nontemporal hint, so that rows read for the last time in
+// the launch do not displace what the step reuses from the caches
+// (activations, routing tables, the KV cache); an expert's earlier token
+// tiles load them with the default policy and leave them in L2 for the later
+// ones.  Measured on the 30-layer step at 256 tokens: the hint on every item
+// +2.3% against no hint, but 16% of the weight bytes fetched twice; the hint
+// on last tiles only a further +1.4%; on single-tile experts only, -2%.  The
+// LDS-staged expert tiles (more tokens per expert) and the dense projections
+// keep the default policy: with the hint they measured 1.7% (a thousand
+// tokens) and 1% slower.
 constexpr bool kNtWaveW = true;
 __device__ __forceinline__ uint4 load_nt16(const void* p) {
   typedef unsigned int u32x4_nt __attribute__((ext_vector_type(4)));
@@ -642,75 +646,86 @@ __global__ __launch_bounds__(64, WPE) void gemm_wave_kernel(GemmArgs a) {
     uint4 x[TB][2];
     WChunk<WF> w[RT];
   };
-  Slot ring[NR];
-  auto issue = [&](Slot& sl, int c) {
-    const int cc = min(c, nchunks - 1);
-#pragma unroll
-    for (int tb = 0; tb < TB; ++tb) {
-      sl.x[tb][0] = *reinterpret_cast<const uint4*>(xp[tb] + cc * 64);
-      sl.x[tb][1] = *reinterpret_cast<const uint4*>(xp[tb] + cc * 64 + 8);
-    }
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      if constexpr (WF == kWMx4)
-        sl.w[rt].template load_mx<kNtWaveW>(wtile[rt] + w_lane + cc * kChunk,
-                                            wtile[rt] + s_lane + cc * kChunk);
-      else
-        sl.w[rt].template load<WRow<WT, TILED>::kSecond, kNtWaveW>(wtile[rt] + w_lane + cc * kChunk);
-    }
-  };
+  // cache policy of this item's weight loads (wave-uniform): the hint on
+  // the expert's last token tile only
+  const int grp_tiles = (a.offsets[grp + 1] - base_pos + MT - 1) / MT;
+  const bool item_nt = kNtWaveW && ty - first_tile == grp_tiles - 1;
   const uint4 zero4 = make_uint4(0, 0, 0, 0);
   f32x4_v acc[RT][TB];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) acc[rt][tb] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+  auto stream_k = [&](auto nt_tag) {
+    constexpr bool NT = decltype(nt_tag)::value;
+    Slot ring[NR];
+    auto issue = [&](Slot& sl, int c) {
+      const int cc = min(c, nchunks - 1);
 #pragma unroll
-  for (int p = 0; p < NR; ++p) {
-    issue(ring[p], p);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  for (int c0 = 0; c0 < nchunks; c0 += NR) {
+      for (int tb = 0; tb < TB; ++tb) {
+        sl.x[tb][0] = *reinterpret_cast<const uint4*>(xp[tb] + cc * 64);
+        sl.x[tb][1] = *reinterpret_cast<const uint4*>(xp[tb] + cc * 64 + 8);
+      }
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        if constexpr (WF == kWMx4)
+          sl.w[rt].template load_mx<NT>(wtile[rt] + w_lane + cc * kChunk,
+                                        wtile[rt] + s_lane + cc * kChunk);
+        else
+          sl.w[rt].template load<WRow<WT, TILED>::kSecond, NT>(wtile[rt] + w_lane + cc * kChunk);
+      }
+    };
 #pragma unroll
     for (int p = 0; p < NR; ++p) {
-      // kWaveIssueFirst: refill the slot before its MMAs (one more slot of
-      // registers, loads issued one compute step earlier); otherwise refill
-      // it right after
-      const Slot cur = ring[p];
-      if (kWaveIssueFirst) {
-        __builtin_amdgcn_sched_barrier(0);
-        issue(ring[p], c0 + p + NR);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      if (c0 + p < nchunks) {
-        bf16x8_v xa[TB][2];
+      issue(ring[p], p);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    for (int c0 = 0; c0 < nchunks; c0 += NR) {
 #pragma unroll
-        for (int tb = 0; tb < TB; ++tb) {
-          const uint4 u0 = xok[tb] ? cur.x[tb][0] : zero4;
-          const uint4 u1 = xok[tb] ? cur.x[tb][1] : zero4;
-          xa[tb][0] = *reinterpret_cast<const bf16x8_v*>(&u0);
-          xa[tb][1] = *reinterpret_cast<const bf16x8_v*>(&u1);
+      for (int p = 0; p < NR; ++p) {
+        // kWaveIssueFirst: refill the slot before its MMAs (one more slot of
+        // registers, loads issued one compute step earlier); otherwise refill
+        // it right after
+        const Slot cur = ring[p];
+        if (kWaveIssueFirst) {
+          __builtin_amdgcn_sched_barrier(0);
+          issue(ring[p], c0 + p + NR);
+          __builtin_amdgcn_sched_barrier(0);
         }
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-          bf16x8_v w0, w1;
-          cur.w[rt].get(w0, w1);
+        if (c0 + p < nchunks) {
+          bf16x8_v xa[TB][2];
 #pragma unroll
           for (int tb = 0; tb < TB; ++tb) {
-            if (tb == 0 || tb < tb_used) {
-              acc[rt][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w0, xa[tb][0], acc[rt][tb], 0, 0, 0);
-              acc[rt][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w1, xa[tb][1], acc[rt][tb], 0, 0, 0);
+            const uint4 u0 = xok[tb] ? cur.x[tb][0] : zero4;
+            const uint4 u1 = xok[tb] ? cur.x[tb][1] : zero4;
+            xa[tb][0] = *reinterpret_cast<const bf16x8_v*>(&u0);
+            xa[tb][1] = *reinterpret_cast<const bf16x8_v*>(&u1);
+          }
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) {
+            bf16x8_v w0, w1;
+            cur.w[rt].get(w0, w1);
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb) {
+              if (tb == 0 || tb < tb_used) {
+                acc[rt][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w0, xa[tb][0], acc[rt][tb], 0, 0, 0);
+                acc[rt][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w1, xa[tb][1], acc[rt][tb], 0, 0, 0);
+              }
             }
           }
         }
-      }
-      if (!kWaveIssueFirst) {
-        __builtin_amdgcn_sched_barrier(0);
-        issue(ring[p], c0 + p + NR);
-        __builtin_amdgcn_sched_barrier(0);
+        if (!kWaveIssueFirst) {
+          __builtin_amdgcn_sched_barrier(0);
+          issue(ring[p], c0 + p + NR);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
-  }
+  };
+  if (item_nt)
+    stream_k(std::integral_constant<bool, true>{});
+  else
+    stream_k(std::integral_constant<bool, false>{});
 
   // ---- epilogue (lane: rows 4 g4 + r of each 16-row tile, token l16 of
   // each 16-token block)

@@ -16,6 +16,8 @@
 //                       sorted order; down + gate -> y_slot [T*k, D] bf16.
 //   combine_kernel      y[t] += sum_j y_slot[t*k + j] in slot order.
 //   f32 path            plain SIMT kernels over the same tables (parity path).
+#include <algorithm>
+
 #include "common.h"
 #include "gemm_mfma.h"
 #include "kernels.h"
@@ -300,11 +302,12 @@ constexpr int kTinyRT = 2, kTinyNR = 4;
 
 template <int TB, int WF, int MODE, bool TILED, int RT = item_tiles<WF, MODE>(), int NRT = 0>
 static void launch_wave(GemmArgs& g, int T, int k, int E, hipStream_t stream) {
-  // grid: an upper bound of the tile count (E + slots / tile size) times the
-  // weight row groups; the kernel deals the live items out itself
+  // grid: an upper bound of the tile count times the weight row groups (an
+  // expert with tokens has at most one partial tile, and at most min(E, T k)
+  // experts have tokens); the kernel deals the live items out itself
   const int rows_per_item = MODE == kGateUp ? 8 * RT : 16 * RT;
   g.n_tiles_x = (MODE == kGateUp ? g.N / 2 : g.N) / rows_per_item;
-  g.n_tiles_y = E + (T * k + 16 * TB - 1) / (16 * TB);
+  g.n_tiles_y = std::min(E, T * k) + (T * k + 16 * TB - 1) / (16 * TB);
   g.n_tiles_total = g.n_tiles_x * g.n_tiles_y;
   const unsigned grid = static_cast<unsigned>((g.n_tiles_total + 7) / 8 * 8);
   // bf16 chunks are twice the registers of fp8: two waves per SIMD (three

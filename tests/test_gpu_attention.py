@@ -76,6 +76,16 @@ def test_canvas_attention_bf16_spare_cache():
     _check(case, [1500, 3000], 8192, CANVAS, torch.bfloat16)
 
 
+@pytest.mark.parametrize("Lq", [1, 5, 16])
+@pytest.mark.parametrize("mode", [CANVAS, CAUSAL])
+def test_attention_bf16_few_queries(Lq, mode):
+    """A few query tokens per row (AR decode): one row tile per KV head and
+    the cache split over many workgroups, most of them empty past the short
+    row's keys; rows with 8000 and 333 cached keys in 8448 slots."""
+    case = attention_case(B=2, Lq=Lq, P=8000, seed=40 + Lq)
+    _check(case, [8000, 333], 8448, mode, torch.bfloat16)
+
+
 @pytest.mark.parametrize("P", [0, 64, 300])
 def test_causal_prefill_bf16(P):
     case = attention_case(B=2, Lq=200, P=max(P, 1), seed=20 + P)
