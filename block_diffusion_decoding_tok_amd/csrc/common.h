@@ -136,6 +136,10 @@ __device__ __forceinline__ bool step_gate_closed(const int32_t* n_done, int n) {
   return n_done != nullptr && __builtin_amdgcn_readfirstlane(*n_done) >= n;
 }
 
+// s_waitcnt immediates: vector-memory count <= n (bits 3:0 and 15:14), export
+// and LDS/scalar counts left at their maxima (no wait on them)
+constexpr int waitcnt_vm(int n) { return (n & 0xf) | (0x7 << 4) | (0xf << 8) | (((n >> 4) & 3) << 14); }
+
 // Logical workgroup index for a grid of a multiple of 8 workgroups:
 // hardware deals linear workgroup ids round-robin over the 8 XCDs, so this
 // gives each XCD one contiguous range of logical indices (work items that

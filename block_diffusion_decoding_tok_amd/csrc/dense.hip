@@ -170,9 +170,6 @@ constexpr size_t kDlSmemBytes = (kDlWStages * kWideWStage + kDlXStages * kWideTo
 
 __device__ __forceinline__ int dl_xslot(int row, int piece) { return piece ^ ((row >> 1) & 7); }
 
-// s_waitcnt immediates: vector-memory count <= n (bits 3:0 and 15:14), export
-// and LDS/scalar counts left at their maxima (no wait on them)
-constexpr int waitcnt_vm(int n) { return (n & 0xf) | (0x7 << 4) | (0xf << 8) | (((n >> 4) & 3) << 14); }
 constexpr int kWaitVm4 = waitcnt_vm(4), kWaitVm0 = waitcnt_vm(0);
 
 __global__ __launch_bounds__(512) void gemm_wide_dl_kernel(const bf16_t* __restrict__ W,
@@ -307,6 +304,30 @@ dg_status launch_gemm(const void* A, const void* W, void* C, int M, int N, int K
   return DG_OK;
 }
 
+// A thousand tokens and more with tiled activations: 128 x 128 tiles staged
+// through LDS (gemm_dl128_kernel).  Stages in flight: 2 (64 KB of LDS, two
+// workgroups per CU) once the grid fills the chip twice, else 4 (measured at
+// 2048 / 1024 tokens: QKV 111 -> 52 / 48 -> 33 us, O 64 -> 38 / 30 -> 29 us).
+constexpr int kDl128MinTokens = 1024;
+
+static dg_status launch_dl128(GemmArgs& g, int M, int N, hipStream_t stream) {
+  g.n_tiles_x = N / 128;
+  g.n_tiles_y = (M + 127) / 128;
+  g.n_tiles_total = g.n_tiles_x * g.n_tiles_y;
+  const unsigned grid = (g.n_tiles_total + 7) / 8 * 8;
+  if (g.n_tiles_total >= 512) {
+    constexpr int kBytes = 2 * kDl128Stage * static_cast<int>(sizeof(bf16_t));
+    gemm_dl128_kernel<2><<<grid, 256, kBytes, stream>>>(g);
+  } else {
+    constexpr int kBytes = 4 * kDl128Stage * static_cast<int>(sizeof(bf16_t));
+    const dg_status st = ensure_lds_limit(reinterpret_cast<const void*>(gemm_dl128_kernel<4>), kBytes);
+    if (st != DG_OK) return st;
+    gemm_dl128_kernel<4><<<grid, 256, kBytes, stream>>>(g);
+  }
+  DG_LAUNCH_CHECK();
+  return DG_OK;
+}
+
 bool qkv_rope_supported(const QkvRope& r, int K) {
   const int M = r.B * r.Lq;
   const int N = (r.Hq + 2 * r.Hkv) * r.dh;
@@ -326,6 +347,7 @@ dg_status launch_qkv_rope(const void* A, const void* W, int K, int w_layout, con
   const int N = (r.Hq + 2 * r.Hkv) * r.dh;
   if (!qkv_rope_supported(r, K) || (r.x_tiled && w_layout != DG_LAYOUT_TILED))
     return DG_ERR_UNSUPPORTED;
+  if (!r.rope_tab) return DG_ERR_INVALID_ARG;
   GemmArgs g{};
   g.W = W; g.X = static_cast<const bf16_t*>(A);
   g.N = N; g.K = K; g.M = M; g.n_groups = 1;
@@ -334,14 +356,15 @@ dg_status launch_qkv_rope(const void* A, const void* W, int K, int w_layout, con
   g.rope = 1;
   g.prefix_len = r.prefix_len;
   g.Lq = r.Lq; g.Hq = r.Hq; g.Hkv = r.Hkv; g.Tmax = r.Tmax;
-  g.theta = r.theta;
   g.q_scale = attn_q_scale(r.dh);
+  g.rope_tab = r.rope_tab;
   g.q_out = static_cast<bf16_t*>(r.q_out);
   g.k_cache = static_cast<bf16_t*>(r.k_cache);
   g.v_cache = static_cast<bf16_t*>(r.v_cache);
   g.x_tiled = r.x_tiled;
   g.gate = gate.n_done;
   g.gate_n = gate.n;
+  if (r.x_tiled && M >= kDl128MinTokens) return launch_dl128(g, M, N, stream);
   const int rt = r.x_tiled ? kXtRT : kProjRT, tb = r.x_tiled ? kXtTB : kProjTB;
   g.n_tiles_x = N / (16 * rt);
   g.n_tiles_y = (M + 16 * tb - 1) / (16 * tb);
@@ -375,6 +398,7 @@ dg_status launch_gemm_xt(const void* A, const void* W, void* C, int M, int N, in
   g.x_tiled = 1;
   g.gate = gate.n_done;
   g.gate_n = gate.n;
+  if (M >= kDl128MinTokens && N % 128 == 0) return launch_dl128(g, M, N, stream);
   g.n_tiles_x = N / (16 * kXtRT);
   g.n_tiles_y = (M + 16 * kXtTB - 1) / (16 * kXtTB);
   g.n_tiles_total = g.n_tiles_x * g.n_tiles_y;
@@ -461,11 +485,23 @@ template <> struct Slot4<float> {
   __device__ float4 get() const { return f; }
 };
 
+// (cos, sin) of row `row`'s RoPE pairs into rt.tab (threads j < rt.pairs)
+__device__ __forceinline__ void rope_table_row(const RopeTable& rt, int row) {
+  const int j = threadIdx.x;
+  if (rt.tab == nullptr || j >= rt.pairs) return;
+  const int pos = rt.prefix_len[row / rt.Lq] + row % rt.Lq;
+  float c, s;
+  rope_cos_sin(pos, j, 2 * rt.pairs, rt.theta, &c, &s);
+  rt.tab[static_cast<int64_t>(row) * rt.pairs + j] = make_float2(c, s);
+}
+
 template <typename TS, typename TO>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const TS* __restrict__ y_slot, int k,
                                                       float* __restrict__ x,
-                                                      TO* __restrict__ out, int D, int tiled) {
+                                                      TO* __restrict__ out, int D, int tiled,
+                                                      RopeTable rt) {
   const int row = blockIdx.x;
+  rope_table_row(rt, row);
   float4* xr = reinterpret_cast<float4*>(x + static_cast<int64_t>(row) * D);
   const int n4 = D / 4;
   float4 v[kNormPieces];
@@ -535,8 +571,10 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const TS* __restrict__ y_s
 // Rows wider than the register-resident kernel holds, or not a multiple of 4.
 template <typename TO>
 __global__ __launch_bounds__(256) void rmsnorm_wide_kernel(const float* __restrict__ x,
-                                                           TO* __restrict__ out, int D) {
+                                                           TO* __restrict__ out, int D,
+                                                           RopeTable rt) {
   const int row = blockIdx.x;
+  rope_table_row(rt, row);
   const float* xr = x + static_cast<int64_t>(row) * D;
   float ss = 0.f;
   for (int d = threadIdx.x; d < D; d += blockDim.x) ss = fmaf(xr[d], xr[d], ss);
@@ -557,7 +595,10 @@ dg_status launch_rmsnorm(const float* x, void* out, int M, int D, int out_dtype,
 }
 
 dg_status launch_combine_rmsnorm(const void* y_slot, int slot_dtype, int k, float* x, void* out,
-                                 int M, int D, int out_dtype, hipStream_t stream, bool out_tiled) {
+                                 int M, int D, int out_dtype, hipStream_t stream, bool out_tiled,
+                                 const RopeTable& rope) {
+  if (rope.tab && (rope.pairs <= 0 || rope.pairs > 256 || rope.Lq <= 0 || !rope.prefix_len))
+    return DG_ERR_INVALID_ARG;
   const bool regs = D % 4 == 0 && D / 4 <= kNormPieces * 256;
   if (out_tiled && !(regs && D % 64 == 0 && out_dtype == DG_BF16)) return DG_ERR_UNSUPPORTED;
   const int tl = out_tiled ? 1 : 0;
@@ -565,9 +606,9 @@ dg_status launch_combine_rmsnorm(const void* y_slot, int slot_dtype, int k, floa
     dg_status st;
     if (y_slot && (st = launch_moe_combine(y_slot, slot_dtype, M, D, k, x, stream))) return st;
     if (out_dtype == DG_BF16)
-      rmsnorm_wide_kernel<bf16_t><<<M, 256, 0, stream>>>(x, static_cast<bf16_t*>(out), D);
+      rmsnorm_wide_kernel<bf16_t><<<M, 256, 0, stream>>>(x, static_cast<bf16_t*>(out), D, rope);
     else
-      rmsnorm_wide_kernel<float><<<M, 256, 0, stream>>>(x, static_cast<float*>(out), D);
+      rmsnorm_wide_kernel<float><<<M, 256, 0, stream>>>(x, static_cast<float*>(out), D, rope);
     DG_LAUNCH_CHECK();
     return DG_OK;
   }
@@ -575,11 +616,11 @@ dg_status launch_combine_rmsnorm(const void* y_slot, int slot_dtype, int k, floa
   const bf16_t* yb = bf ? static_cast<const bf16_t*>(y_slot) : nullptr;
   const float* yf = bf ? nullptr : static_cast<const float*>(y_slot);
   if (out_dtype == DG_BF16) {
-    if (bf) rmsnorm_kernel<bf16_t, bf16_t><<<M, 256, 0, stream>>>(yb, k, x, static_cast<bf16_t*>(out), D, tl);
-    else rmsnorm_kernel<float, bf16_t><<<M, 256, 0, stream>>>(yf, k, x, static_cast<bf16_t*>(out), D, tl);
+    if (bf) rmsnorm_kernel<bf16_t, bf16_t><<<M, 256, 0, stream>>>(yb, k, x, static_cast<bf16_t*>(out), D, tl, rope);
+    else rmsnorm_kernel<float, bf16_t><<<M, 256, 0, stream>>>(yf, k, x, static_cast<bf16_t*>(out), D, tl, rope);
   } else {
-    if (bf) rmsnorm_kernel<bf16_t, float><<<M, 256, 0, stream>>>(yb, k, x, static_cast<float*>(out), D, 0);
-    else rmsnorm_kernel<float, float><<<M, 256, 0, stream>>>(yf, k, x, static_cast<float*>(out), D, 0);
+    if (bf) rmsnorm_kernel<bf16_t, float><<<M, 256, 0, stream>>>(yb, k, x, static_cast<float*>(out), D, 0, rope);
+    else rmsnorm_kernel<float, float><<<M, 256, 0, stream>>>(yf, k, x, static_cast<float*>(out), D, 0, rope);
   }
   DG_LAUNCH_CHECK();
   return DG_OK;

@@ -75,9 +75,10 @@ struct GemmArgs {
   // scaled by q_scale) goes to the packed attention layout, k (rotated) and v
   // to the caches
   int rope;
+  const float2* rope_tab;   // (cos, sin) [M, 64] of the tokens' positions (RopeTable)
   const int32_t* prefix_len;
   int Lq, Hq, Hkv, Tmax;
-  float theta, q_scale;
+  float q_scale;
   bf16_t* q_out;
   bf16_t* k_cache;
   bf16_t* v_cache;
@@ -838,13 +839,11 @@ __global__ __launch_bounds__(64 * NW, WPE) void gemm_splitk_kernel(GemmArgs a) {
   static_assert(RT * TB * 64 <= 64 * NW * 4, "at most four output quads per thread");
   static_assert(NW == 4 || NW == 8, "four or eight waves");
   __shared__ __attribute__((aligned(16))) float s_acc[4][RT * TB * 4][64];
-  __shared__ double s_inv[64];                  // RoPE epilogue: frequencies of the 64 pairs
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g4 = lane >> 4;
   const int logical = xcd_logical_tile(blockIdx.x, gridDim.x);
   if (logical >= a.n_tiles_total || step_gate_closed(a.gate, a.gate_n)) return;
   constexpr bool kRopeTile = RT == 8 || RT == 4;
-  if (kRopeTile && a.rope && tid < 64) s_inv[tid] = rope_inv_freq(tid, 128, a.theta);
   const int tx = logical / a.n_tiles_y;       // row tile (token tiles adjacent)
   const int ty = logical % a.n_tiles_y;
   const int m0 = ty * 16 * TB;
@@ -1013,10 +1012,10 @@ __global__ __launch_bounds__(64 * NW, WPE) void gemm_splitk_kernel(GemmArgs a) {
         bf16_t* dst;
         if (head < a.Hq + a.Hkv) {
           const float sc = head < a.Hq ? a.q_scale : 1.f;
+          const float2* cs = a.rope_tab + static_cast<int64_t>(m) * 64 + d0;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            float c, sn;
-            rope_cos_sin_at(pos, s_inv[d0 + r], &c, &sn);
+            const float c = cs[r].x, sn = cs[r].y;
             o1[r] = (v1[r] * c - v2[r] * sn) * sc;
             o2[r] = (v2[r] * c + v1[r] * sn) * sc;
           }
@@ -1070,6 +1069,176 @@ __global__ __launch_bounds__(64 * NW, WPE) void gemm_splitk_kernel(GemmArgs a) {
       pk.x = pack_bf16x2(v[0], v[1]);
       pk.y = pack_bf16x2(v[2], v[3]);
       *reinterpret_cast<uint2*>(o) = pk;
+    }
+  }
+}
+
+}  // namespace dg
+
+namespace dg {
+
+// Dense GEMM for a thousand tokens and more (prefill chunks, the canvas of
+// several rows) over tiled weights and tiled activations:
+// out[m, n] = sum_k X[m, k] W[n, k].  A workgroup of four waves owns 128
+// weight rows x 128 tokens over the whole K, so each operand byte it moves
+// serves 128 outputs (the split-K tiles above move 720 KB per 64 x 64 tile at
+// 256 tokens; here a 2048-token QKV projection moves half the bytes per
+// output and runs in 52 against 111 us).  Per 64-k stage the 8 weight tiles'
+// and the 8 token blocks' 2 KB chunks are copied into LDS unchanged by
+// direct-to-LDS 16-byte loads (both tiled layouts already hold the MFMA
+// operand lane order); NS stages are in flight.  Wave (wr, wt) owns rows
+// 64 wr .. +64 and tokens 64 wt .. +64 (16 accumulator blocks).
+// Epilogues: bf16 or f32 stores, f32 accumulate, or (a.rope) the QKV form:
+// a 128-row tile is one head, wave wr = 1 hands its rows (d + 64) to wave
+// wr = 0 through LDS, which rotates the pairs (angles from a.rope_tab) and
+// writes q / k / v.
+constexpr int kDl128Stage = 16384;               // elements per stage (32 KB)
+
+template <int NS>
+__global__ __launch_bounds__(256, 2) void gemm_dl128_kernel(GemmArgs a) {
+  static_assert(NS >= 2 && NS * kDl128Stage * 2 >= 32 * 1024, "the RoPE hand-over fits a stage");
+  extern __shared__ __attribute__((aligned(16))) bf16_t dl128_smem[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const int logical = xcd_logical_tile(blockIdx.x, gridDim.x);
+  if (logical >= a.n_tiles_total || step_gate_closed(a.gate, a.gate_n)) return;
+  const int tx = logical / a.n_tiles_y, ty = logical % a.n_tiles_y;
+  const int n0 = tx * 128, m0 = ty * 128;
+  const int nch = a.K / 64;
+  const int wr = wave & 1, wt = wave >> 1;
+  const bf16_t* W = static_cast<const bf16_t*>(a.W);
+  const int mblocks = (a.M + 15) / 16;
+  // this wave's eight 1 KB blocks of every stage: block b = 8 wave + i is
+  // half b % 2 of weight tile b / 2 (b < 16) or of token block (b - 16) / 2;
+  // token blocks past the last one are clamped to it (their rows are masked
+  // in the epilogue)
+  const bf16_t* src[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int b = wave * 8 + i;
+    if (b < 16) {
+      src[i] = W + static_cast<int64_t>(n0 / 16 + (b >> 1)) * nch * 1024 + (b & 1) * 512 + lane * 8;
+    } else {
+      const int blk = min(m0 / 16 + ((b - 16) >> 1), mblocks - 1);
+      src[i] = a.X + static_cast<int64_t>(blk) * nch * 1024 + (b & 1) * 512 + lane * 8;
+    }
+  }
+  auto issue = [&](int c) {
+    bf16_t* dst = dl128_smem + (c % NS) * kDl128Stage + wave * 8 * 512;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) __builtin_amdgcn_global_load_lds(src[i] + c * 1024, dst + i * 512, 16, 0, 0);
+  };
+  f32x4_v acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < NS - 1; ++c)
+    if (c < nch) issue(c);
+  for (int c = 0; c < nch; ++c) {
+    // stage c's copies have landed when at most the later stages' (8 each)
+    // are outstanding; then every wave's have (barrier), and every wave is
+    // done with stage c - 1, whose buffer the next issue refills.  A bare
+    // barrier: the fence of __syncthreads would wait for every copy in flight
+    if (c + NS - 2 < nch) __builtin_amdgcn_s_waitcnt(waitcnt_vm((NS - 2) * 8));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __builtin_amdgcn_s_barrier();
+    if (c + NS - 1 < nch) issue(c + NS - 1);
+    const bf16_t* st = dl128_smem + (c % NS) * kDl128Stage;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      bf16x8_v wa[4], xb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        wa[i] = *reinterpret_cast<const bf16x8_v*>(st + ((wr * 4 + i) * 2 + h) * 512 + lane * 8);
+        xb[i] = *reinterpret_cast<const bf16x8_v*>(st + (16 + (wt * 4 + i) * 2 + h) * 512 + lane * 8);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[i], xb[j], acc[i][j], 0, 0, 0);
+    }
+  }
+
+  // lane: rows 4 g4 + r of row block i, token l16 of token block j
+  if (a.rope) {
+    // hand rows 64 .. 127 (the d + 64 halves of the head's pairs) to wave wr = 0
+    __syncthreads();                             // every wave is done with the stages
+    f32x4_v* s_x = reinterpret_cast<f32x4_v*>(dl128_smem);
+    if (wr == 1) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) s_x[((wt * 4 + i) * 4 + j) * 64 + lane] = acc[i][j];
+    }
+    __syncthreads();
+    if (wr == 1) return;
+    const int head = tx;
+    const int G = a.Hq / a.Hkv;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int m = m0 + (wt * 4 + j) * 16 + l16;
+      if (m >= a.M) continue;
+      const int b = m / a.Lq, i_tok = m % a.Lq;
+      const int pos = a.prefix_len[b] + i_tok;
+      if (head >= a.Hq && pos >= a.Tmax) continue;   // past the cache: not written
+      bf16_t* dst;
+      if (head < a.Hq) {
+        const int64_t row = static_cast<int64_t>(i_tok) * G + head % G;
+        dst = a.q_out + ((static_cast<int64_t>(b) * a.Hkv + head / G) * a.Lq * G + row) * 128;
+      } else if (head < a.Hq + a.Hkv) {
+        dst = a.k_cache + ((static_cast<int64_t>(b) * a.Hkv + (head - a.Hq)) * a.Tmax + pos) * 128;
+      } else {
+        dst = a.v_cache + ((static_cast<int64_t>(b) * a.Hkv + (head - a.Hq - a.Hkv)) * a.Tmax + pos) * 128;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f32x4_v v1 = acc[i][j];
+        const f32x4_v v2 = s_x[((wt * 4 + i) * 4 + j) * 64 + lane];
+        const int d0 = i * 16 + g4 * 4;            // < 64
+        float o1[4], o2[4];
+        if (head < a.Hq + a.Hkv) {
+          const float sc = head < a.Hq ? a.q_scale : 1.f;
+          const float2* cs = a.rope_tab + static_cast<int64_t>(m) * 64 + d0;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float c = cs[r].x, sn = cs[r].y;
+            o1[r] = (v1[r] * c - v2[r] * sn) * sc;
+            o2[r] = (v2[r] * c + v1[r] * sn) * sc;
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) { o1[r] = v1[r]; o2[r] = v2[r]; }
+        }
+        *reinterpret_cast<uint2*>(dst + d0) = make_uint2(pack_bf16x2(o1[0], o1[1]), pack_bf16x2(o1[2], o1[3]));
+        *reinterpret_cast<uint2*>(dst + d0 + 64) =
+            make_uint2(pack_bf16x2(o2[0], o2[1]), pack_bf16x2(o2[2], o2[3]));
+      }
+    }
+    return;
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int m = m0 + (wt * 4 + j) * 16 + l16;
+    if (m >= a.M) continue;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int n = n0 + (wr * 4 + i) * 16 + g4 * 4;
+      const f32x4_v v = acc[i][j];
+      if (a.out_dtype == DG_F32) {
+        float* o = static_cast<float*>(a.out) + static_cast<int64_t>(m) * a.N + n;
+        if (a.accumulate) {
+          const float4 c4 = *reinterpret_cast<const float4*>(o);
+          *reinterpret_cast<float4*>(o) = make_float4(c4.x + v[0], c4.y + v[1], c4.z + v[2], c4.w + v[3]);
+        } else {
+          *reinterpret_cast<float4*>(o) = make_float4(v[0], v[1], v[2], v[3]);
+        }
+      } else {
+        bf16_t* o = static_cast<bf16_t*>(a.out) + static_cast<int64_t>(m) * a.N + n;
+        *reinterpret_cast<uint2*>(o) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+      }
     }
   }
 }

@@ -114,6 +114,9 @@ struct QkvRope {
   void* k_cache;
   void* v_cache;
   int x_tiled;
+  // (cos, sin) of every (token, pair) of the forward [B * Lq, dh / 2], as
+  // RopeTable below writes it (the input RMSNorm of the layer)
+  const float2* rope_tab;
 };
 bool qkv_rope_supported(const QkvRope& r, int K);
 dg_status launch_qkv_rope(const void* A, const void* W, int K, int w_layout, const QkvRope& r,
@@ -128,13 +131,24 @@ dg_status launch_gemm_xt(const void* A, const void* W, void* C, int M, int N, in
 // RMSNorm of f32 rows x [M, D] (eps 1e-6, unit gain) into out_dtype.
 dg_status launch_rmsnorm(const float* x, void* out, int M, int D, int out_dtype,
                          hipStream_t stream);
+// RoPE angles of a forward's tokens: with tab set, row t (token t % Lq of
+// batch row t / Lq, position prefix_len[t / Lq] + t % Lq) also writes
+// tab[t * pairs + j] = (cos, sin) of position * theta^(-2 j / (2 pairs)) for
+// the pairs j < pairs, the angle reduced to [-pi, pi] in double first.
+struct RopeTable {
+  const int32_t* prefix_len = nullptr;
+  int Lq = 1, pairs = 0;
+  float theta = 0.f;
+  float2* tab = nullptr;
+};
 // The MoE combine fused into the next RMSNorm: x[t] += sum_j y_slot[t * k + j]
 // (slot order, as launch_moe_combine), then out = RMSNorm(x).  y_slot may be
 // null (plain RMSNorm); slot_dtype is DG_BF16 or DG_F32.  out_tiled: bf16
-// out in the tiled activation layout (D % 64 == 0, D <= 4096).
+// out in the tiled activation layout (D % 64 == 0, D <= 4096).  rope: the
+// RoPE table of the rows (pairs <= 256), written alongside.
 dg_status launch_combine_rmsnorm(const void* y_slot, int slot_dtype, int k, float* x, void* out,
                                  int M, int D, int out_dtype, hipStream_t stream,
-                                 bool out_tiled = false);
+                                 bool out_tiled = false, const RopeTable& rope = {});
 // x[t] = emb[tokens[t]] as f32.
 dg_status launch_embed(const int32_t* tokens, const void* emb, float* x, int M, int D,
                        int dtype, hipStream_t stream);

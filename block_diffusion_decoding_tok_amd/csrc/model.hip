@@ -154,6 +154,7 @@ struct dg_ctx {
   int32_t* active = nullptr;       // dg_generate: rows that have not met EOS
   int32_t* blk_tokens = nullptr;   // dg_generate: the current block's tokens [B, L]
   int32_t* blk_steps = nullptr;    // dg_generate: the current block's steps [B]
+  float2* rope_tab = nullptr;      // (cos, sin) of a forward's tokens x pairs
   // host-visible status word (pinned host memory): the device stores a
   // non-zero block status there; the host reads and clears it
   int32_t* host_status = nullptr;
@@ -180,7 +181,7 @@ namespace {
 struct Layout {
   size_t x, h, qkv, attn_out, router, topk_ids, gates, offsets, sorted_rows, attn_ws, moe_ws,
       logits, samp_ws, tokens, committed, renoised, maxprob, entropy, mean_entropy, done, status,
-      n_done, active, blk_tokens, blk_steps, total;
+      n_done, active, blk_tokens, blk_steps, rope_tab, total;
 };
 
 size_t esz(int dt) { return dt == DG_F32 ? 4 : 2; }
@@ -235,6 +236,7 @@ Layout layout(const dg_model_dims& d, int maxB, int maxT, int maxP) {
   L.active = take(maxB * 4);
   L.blk_tokens = take(Tc * 4);
   L.blk_steps = take(maxB * 4);
+  L.rope_tab = take(T * (d.head_dim / 2) * sizeof(float2));   // RoPE table of a forward
   L.total = off;
   return L;
 }
@@ -273,7 +275,8 @@ dg_status check_dims(const dg_model_dims* d) {
   return DG_OK;
 }
 
-dg_status norm_input(dg_ctx* c, int T, hipStream_t s, bool tiled = false);
+dg_status norm_input(dg_ctx* c, int T, hipStream_t s, bool tiled = false,
+                     const RopeTable& rope = {});
 dg_status layer_tail(dg_ctx* c, int l, int B, int n, bool xt, hipStream_t s);
 
 // Whether a layer over T tokens runs its dense projections on the tiled
@@ -296,10 +299,14 @@ dg_status layer(dg_ctx* c, int l, int B, int n, void* kc, void* vc, int Tmax,
   const size_t a = esz(d.act_dtype);
   dg_status st;
   QkvRope r{prefix_len, B, n, d.n_heads, d.n_kv_heads, d.head_dim, Tmax, d.rope_theta,
-            c->attn_ws, kc, vc, 0};
+            c->attn_ws, kc, vc, 0, c->rope_tab};
   const bool xt = tiled_acts(d, r);
   r.x_tiled = xt ? 1 : 0;
-  if ((st = norm_input(c, T, s, xt))) return st;
+  // the input norm also writes the RoPE angles the fused QKV projection reads
+  RopeTable rt;
+  if (d.act_dtype == DG_BF16 && qkv_rope_supported(r, d.d_model))
+    rt = RopeTable{prefix_len, n, d.head_dim / 2, d.rope_theta, c->rope_tab};
+  if ((st = norm_input(c, T, s, xt, rt))) return st;
   // bf16: the projection rotates q and k in its epilogue and writes q to the
   // attention workspace, k and v to the caches (one launch less per layer)
   if (d.act_dtype == DG_BF16) {
@@ -371,14 +378,14 @@ dg_status layer_tail(dg_ctx* c, int l, int B, int n, bool xt, hipStream_t s) {
 // RMSNorm of the residual stream into c->h (tiled: in the tiled activation
 // layout), taking a pending MoE combine (the previous layer's expert outputs)
 // into x first.
-dg_status norm_input(dg_ctx* c, int T, hipStream_t s, bool tiled) {
+dg_status norm_input(dg_ctx* c, int T, hipStream_t s, bool tiled, const RopeTable& rope) {
   const dg_model_dims& d = c->d;
   void *h_mid, *y_slot = nullptr;
   if (c->pending_combine)
     moe_ffn_workspace_split(c->moe_ws, T, d.d_ff, d.top_k, d.act_dtype, &h_mid, &y_slot);
   c->pending_combine = false;
   return launch_combine_rmsnorm(y_slot, d.act_dtype, d.top_k, c->x, c->h, T, d.d_model,
-                                d.act_dtype, s, tiled);
+                                d.act_dtype, s, tiled, rope);
 }
 
 // Flush a pending MoE combine into x (end of a forward without the LM head).
@@ -783,6 +790,7 @@ dg_status dg_ctx_create(dg_ctx** out, const dg_model_dims* dims, const dg_model_
   c->active = reinterpret_cast<int32_t*>(b + L.active);
   c->blk_tokens = reinterpret_cast<int32_t*>(b + L.blk_tokens);
   c->blk_steps = reinterpret_cast<int32_t*>(b + L.blk_steps);
+  c->rope_tab = reinterpret_cast<float2*>(b + L.rope_tab);
   *out = c;
   return DG_OK;
 }

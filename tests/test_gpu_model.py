@@ -230,7 +230,8 @@ def _topk_gap(r, k):
                                                  (3, 40, True, CAUSAL, 40),
                                                  (1, 64, False, CAUSAL, 17),
                                                  (1, 256, True, CAUSAL, 2048),
-                                                 (2, 100, True, CAUSAL, 1000)])
+                                                 (2, 100, True, CAUSAL, 1000),
+                                                 (2, 64, True, CAUSAL, 600)])
 def test_full_width_layers_teacher_forced(full_layers, B, P0, planted, mode, n):
     """planted: the router override supplies N(0,1) + hot-expert-skew logits
     (the stated MoE routing) instead of the random router's, so both sides
@@ -242,8 +243,11 @@ def test_full_width_layers_teacher_forced(full_layers, B, P0, planted, mode, n):
     the measured router-logit error.  CAUSAL: an n-token prefill chunk at
     positions [P0, P0 + n) (the prompt path).  Token counts off the 16- and
     64-token tiles (200, 3 x 40, 17) end in partial token blocks of the tiled
-    activation layout; 300 prompt tokens prefill as 256 + 44.  2048 and
-    2 x 1000 tokens: the large prefill chunks (tiled weights only)."""
+    activation layout; 300 prompt tokens prefill as 256 + 44.  2048, 2 x 1000
+    and 2 x 600 tokens: the large prefill chunks (tiled weights only), whose
+    projections run the 128 x 128 LDS-staged tiles with two stages in flight
+    (2048, 2000 tokens: 512 tiles) or four (1200 tokens, a partial last tile;
+    also 4 x 256 canvas tokens)."""
     d, w, model, model0, layout = full_layers
     if n > 256 and layout != "tiled":
         pytest.skip("large prefill chunks: checked on the tiled layout")
@@ -339,7 +343,8 @@ def test_prefill_large_chunks_layer0_cache():
     (max_prefill_tokens 2048): the prefix advances by the whole prompt and
     layer 0's cache -- the keys and values of the embedded prompt, causal --
     matches the oracle's layer 0 over the same prompt from position 0; a
-    second prefill with canvas-sized chunks gives the same layer-0 cache."""
+    second prefill with canvas-sized chunks gives the same layer-0 cache up
+    to a bf16 rounding step per row."""
     d = FULL_LAYER
     w = model_weights(d, seed=3, expert_dtype="fp8", dense_dtype="bf16")
     pw = _packed(w)
@@ -364,8 +369,14 @@ def test_prefill_large_chunks_layer0_cache():
         ek, ev = rel_err_rows(k_got, ok[0]), rel_err_rows(v_got, ov[0])
         print(f"layer 0 cache over {n} prompt tokens: K err {ek:.3g}, V err {ev:.3g}")
         assert ek < 2e-2 and ev < 2e-2
-    # layer 0's K/V depend only on the embeddings: the same bits either way
-    assert np.array_equal(out[0][0], out[1][0]) and np.array_equal(out[0][1], out[1][1])
+    # layer 0's K/V depend only on the embeddings; the 2048-token chunk runs
+    # the 128 x 128 projection tiles (one K order) and the 256-token chunks
+    # the split-K tiles (four K ranges summed), so the two f32 sums differ in
+    # rounding order only: per (head, position) row of 128 the two caches
+    # are within a bf16 rounding step (2^-8 relative; the rotation can cancel
+    # single elements, so the bound is on the row)
+    for a_, b_ in ((out[0][0], out[1][0]), (out[0][1], out[1][1])):
+        assert rel_err_rows(a_, b_) < 2.0 ** -7
 
 
 def test_full_vocab_lm_head_sampled():
