@@ -305,9 +305,11 @@ dg_status launch_gemm(const void* A, const void* W, void* C, int M, int N, int K
 }
 
 // A thousand tokens and more with tiled activations: 128 x 128 tiles staged
-// through LDS (gemm_dl128_kernel).  Stages in flight: 2 (64 KB of LDS, two
-// workgroups per CU) once the grid fills the chip twice, else 4 (measured at
-// 2048 / 1024 tokens: QKV 111 -> 52 / 48 -> 33 us, O 64 -> 38 / 30 -> 29 us).
+// through LDS (gemm_dl128_kernel).  Stages in flight: 4 (128 KB of LDS, one
+// workgroup per CU) while the grid fits the 256 CUs once, else 2 (64 KB, two
+// workgroups per CU).  Measured at 2048 / 1024 tokens against the split-K
+// tiles: QKV 111 -> 52 / 48 -> 33 us, O 64 -> 38 / 30 -> 29 us (O at 2048
+// tokens, 352 tiles: 54 us with four stages).
 constexpr int kDl128MinTokens = 1024;
 
 static dg_status launch_dl128(GemmArgs& g, int M, int N, hipStream_t stream) {
@@ -315,7 +317,7 @@ static dg_status launch_dl128(GemmArgs& g, int M, int N, hipStream_t stream) {
   g.n_tiles_y = (M + 127) / 128;
   g.n_tiles_total = g.n_tiles_x * g.n_tiles_y;
   const unsigned grid = (g.n_tiles_total + 7) / 8 * 8;
-  if (g.n_tiles_total >= 512) {
+  if (g.n_tiles_total > 256) {
     constexpr int kBytes = 2 * kDl128Stage * static_cast<int>(sizeof(bf16_t));
     gemm_dl128_kernel<2><<<grid, 256, kBytes, stream>>>(g);
   } else {

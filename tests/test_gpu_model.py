@@ -245,9 +245,10 @@ def test_full_width_layers_teacher_forced(full_layers, B, P0, planted, mode, n):
     64-token tiles (200, 3 x 40, 17) end in partial token blocks of the tiled
     activation layout; 300 prompt tokens prefill as 256 + 44.  2048, 2 x 1000
     and 2 x 600 tokens: the large prefill chunks (tiled weights only), whose
-    projections run the 128 x 128 LDS-staged tiles with two stages in flight
-    (2048, 2000 tokens: 512 tiles) or four (1200 tokens, a partial last tile;
-    also 4 x 256 canvas tokens)."""
+    projections run the 128 x 128 LDS-staged tiles, with two stages in flight
+    when the tiles outnumber the CUs (QKV at all three sizes, O at 2048 and
+    2000) and four otherwise (O at 1200 tokens, and both projections over
+    4 x 256 canvas tokens); 1200 tokens end in a partial tile."""
     d, w, model, model0, layout = full_layers
     if n > 256 and layout != "tiled":
         pytest.skip("large prefill chunks: checked on the tiled layout")
