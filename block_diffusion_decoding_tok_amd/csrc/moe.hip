@@ -276,18 +276,22 @@ size_t moe_ffn_workspace_bytes(int T, int D, int I, int E, int k, int x_dtype) {
 
 // one-wave kernels: register ring depth (chunks of 64 k) and weight tiles of
 // 16 rows per item; token tiles of 16 tokens, or of 32 for gate/up when the
-// experts average 20 to 40 tokens (fewer items re-streaming the same rows)
-constexpr int kMoeNR = 2, kMoeWPE = 3, kDownNR = 2, kDownWPE = 2;
+// experts average 20 to 40 tokens (fewer items re-streaming the same rows).
+// fp8 over 16-token tiles: one chunk in flight at four waves per SIMD, for
+// gate/up (116 VGPRs; the 30-layer step +1.6% over two chunks at three waves)
+// and down (128 rows per item, 118 VGPRs; the step +2.1% over 256 rows with
+// two chunks at two waves)
+constexpr int kMoeNR = 2, kMoeWPE = 3, kDownNR = 1, kDownWPE = 4;
+constexpr int kGateNR = 1, kGateWPE = 4;
 constexpr int kGateRT = 8;
-// down: 256 output rows per fp8 item (two waves per SIMD; 63.3 against 64.7 us
-// for 128 rows at three, the step +0.35%); bf16 rows are twice the registers
-constexpr int kDownRT = 16, kDownRTBf16 = 8;
+constexpr int kDownRT = 8, kDownRTBf16 = 8;
 constexpr int kGateTB1Slots = 20;   // gate/up: 16-token tiles up to this many slots per expert
 constexpr int kTinySlots = 64;      // up to this many slots in all: half-size items
 
 // MXFP4 weights: a chunk of a tile is half the bytes of fp8 (ring depth,
-// waves per SIMD and weight tiles per item are set on their own)
-constexpr int kMx4NR = 2, kMx4WPE = 3;
+// waves per SIMD and weight tiles per item are set on their own; one chunk in
+// flight at four waves per SIMD: the MXFP4 step +0.9% over two at three)
+constexpr int kMx4NR = 1, kMx4WPE = 4;
 constexpr int kMx4GateRT = 8, kMx4DownRT = 8;
 
 template <int WF, int MODE>
@@ -319,8 +323,8 @@ static void launch_wave(GemmArgs& g, int T, int k, int E, hipStream_t stream) {
   else if constexpr (WF == kWBf16)
     gemm_wave_kernel<RT, TB, kMoeNR, WF, MODE, TILED, (TB == 1 ? 2 : 1)><<<grid, 64, 0, stream>>>(g);
   else
-    gemm_wave_kernel<RT, TB, (MODE == kDown ? kDownNR : kMoeNR), WF, MODE, TILED,
-                     (TB == 1 ? (MODE == kDown ? kDownWPE : kMoeWPE) : 1)><<<grid, 64, 0, stream>>>(g);
+    gemm_wave_kernel<RT, TB, (MODE == kDown ? kDownNR : TB == 1 ? kGateNR : kMoeNR), WF, MODE, TILED,
+                     (TB == 1 ? (MODE == kDown ? kDownWPE : kGateWPE) : 1)><<<grid, 64, 0, stream>>>(g);
 }
 
 // A tile-packed stack of E > 1 experts [E, N, K] (bf16 / fp8) keeps the k
