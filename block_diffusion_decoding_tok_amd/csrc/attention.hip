@@ -101,6 +101,12 @@ constexpr int kVTileElems = kDh * kVStride;
 // more than this (log2 units): probabilities then stay below 2^8, and the
 // rescale of the output accumulators is skipped on most tiles.
 constexpr float kLazyRescale = 8.f;
+// The row sums of P come from two more MFMAs per tile against a block of
+// ones (the sum of the bf16 P the PV product uses) instead of 32 vector adds
+// per lane and two cross-lane sums (calls 2% faster at batch 1 and 4;
+// starting the S accumulators at minus the exponent base, to save the 32
+// subtractions too, measured no faster).
+constexpr bool kAttnMfmaRowSum = true;
 
 // LDS row of key k (0..127) of a K tile.  The S^T MFMA's output row 16 b + 4 g
 // + r (b = 0..3 within a 64-key half, g = lane / 16) must hold key 8 g + 4 (b
@@ -234,6 +240,10 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(
     for (int d = 0; d < 8; ++d) acc_o[qb][d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_run[2] = {-INFINITY, -INFINITY};   // exponent base in use (per row)
   float l_run[2] = {0.f, 0.f};
+  f32x4_t acc_l[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+  bf16x8_t ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = static_cast<__bf16>(1.0f);
 
   const bf16_t* kbase = k_cache + static_cast<int64_t>(bh) * Tmax * kDh;
   const bf16_t* vbase = v_cache + static_cast<int64_t>(bh) * Tmax * kDh;
@@ -287,9 +297,10 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(
       }
       float mx = -INFINITY;
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-        mx = fmaxf(mx, fmaxf(fmaxf(s_acc[kb][qb][0], s_acc[kb][qb][1]),
-                             fmaxf(s_acc[kb][qb][2], s_acc[kb][qb][3])));
+      for (int kb = 0; kb < 4; ++kb) {
+        mx = fmaxf(mx, fmaxf(s_acc[kb][qb][0], s_acc[kb][qb][1]));
+        mx = fmaxf(mx, fmaxf(s_acc[kb][qb][2], s_acc[kb][qb][3]));
+      }
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       // raise the base only past the lazy margin (wave-uniform decision)
@@ -298,6 +309,7 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(
         const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run[qb] - m_new);
         m_run[qb] = m_new;
         l_run[qb] *= alpha;
+        acc_l[qb] *= alpha;
 #pragma unroll
         for (int d = 0; d < 8; ++d) acc_o[qb][d] *= alpha;
       }
@@ -310,12 +322,12 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           p[r] = __builtin_amdgcn_exp2f(s_acc[kb][qb][r] - base);
-          rs += p[r];
+          if (!kAttnMfmaRowSum) rs += p[r];
         }
         pk[kb >> 1][(kb & 1) * 2 + 0] = pack_bf16x2(p[0], p[1]);
         pk[kb >> 1][(kb & 1) * 2 + 1] = pack_bf16x2(p[2], p[3]);
       }
-      l_run[qb] += rs;
+      if (!kAttnMfmaRowSum) l_run[qb] += rs;
 #pragma unroll
       for (int ch = 0; ch < 2; ++ch) {
         uint4 u = make_uint4(pk[ch][0], pk[ch][1], pk[ch][2], pk[ch][3]);
@@ -333,6 +345,12 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(
         for (int qb = 0; qb < 2; ++qb)
           acc_o[qb][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pf[qb][ch], acc_o[qb][d], 0, 0, 0);
       }
+      // row sums of P: every output row of ones . P^T is the column sum
+      if (kAttnMfmaRowSum) {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          acc_l[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[qb][ch], acc_l[qb], 0, 0, 0);
+      }
     }
   }
 
@@ -340,8 +358,12 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(
   // the split's partial: O unnormalized [rows][dh] f32, (m, l) per row
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    l_run[qb] += __shfl_xor(l_run[qb], 16);
-    l_run[qb] += __shfl_xor(l_run[qb], 32);
+    if (kAttnMfmaRowSum) {
+      l_run[qb] = acc_l[qb][0];            // the whole half's sum for row l16
+    } else {
+      l_run[qb] += __shfl_xor(l_run[qb], 16);
+      l_run[qb] += __shfl_xor(l_run[qb], 32);
+    }
   }
   __syncthreads();                       // every wave is done with the tiles
   // rows padded by 4 floats: the 16 rows a 16-lane group touches start on
