@@ -213,8 +213,8 @@ struct WRow {
   __device__ const WT* at(int c) const { return base + c * cstride; }
 };
 
-template <int RT, int TB, int KS, int PF, int WF, int MODE, bool TILED>
-__global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
+template <int RT, int TB, int KS, int PF, int WF, int MODE, bool TILED, int MINWG = 1>
+__global__ __launch_bounds__(256, MINWG) void gemm_stream_kernel(GemmArgs a) {
   static_assert(WF != kWMx4 || TILED, "MXFP4 weights are always tile-packed");
   if (step_gate_closed(a.gate, a.gate_n)) return;
   using WT = typename std::conditional<WF == kWBf16, bf16_t, uint8_t>::type;

@@ -260,13 +260,17 @@ __global__ void down_f32_kernel(const float* __restrict__ h, const float* __rest
 }
 
 // ------------------------------------------------------------- launchers
-// LDS-staged 64-token tiles (a thousand tokens and more): stages of 64 k, two
-// in flight, so that four waves per SIMD stay resident (measured at 1024
-// tokens: gate/up 190 -> 156 us, down 131 -> 94 us against 128 k x 3 stages
-// at two waves per SIMD)
+// LDS-staged 64-token tiles (a thousand tokens and more): stages of 64 k, few
+// in flight, so that many waves per SIMD stay resident (measured at 1024
+// tokens: gate/up 190 -> 156 us, down 131 -> 94 us for two stages at four
+// waves per SIMD against 128 k x 3 stages at two).  fp8 and MXFP4 weights:
+// one weight stage in flight at five workgroups (20 waves) per CU, 96 VGPRs
+// (prefill +1.8%, the batch-4 step +0.3% against two stages at four); bf16
+// weights keep two stages at four (at five they spill).
 constexpr int kMoeTB = 4;      // 64 tokens per tile
 constexpr int kMoeKS = 1;      // 64 k per LDS stage
-constexpr int kMoePF = 2;      // weight stages in flight
+template <int WF> constexpr int moe_stream_pf() { return WF == kWBf16 ? 2 : 1; }
+template <int WF> constexpr int moe_stream_minwg() { return WF == kWBf16 ? 1 : 5; }
 
 size_t moe_ffn_workspace_bytes(int T, int D, int I, int E, int k, int x_dtype) {
   const size_t slots = static_cast<size_t>(T) * k;
@@ -375,7 +379,7 @@ static void launch_gate_up_mfma(const void* x, const void* wgu, const float* sgu
     g.n_tiles_x = I / 64;
     g.n_tiles_y = E + static_cast<int>((slots + MT - 1) / MT);
     g.n_tiles_total = g.n_tiles_x * g.n_tiles_y;
-    gemm_stream_kernel<2, kMoeTB, kMoeKS, kMoePF, WF, kGateUp, TILED>
+    gemm_stream_kernel<2, kMoeTB, kMoeKS, moe_stream_pf<WF>(), WF, kGateUp, TILED, moe_stream_minwg<WF>()>
         <<<(g.n_tiles_total + 7) / 8 * 8, 256, 0, stream>>>(g);
   }
 }
@@ -406,7 +410,7 @@ static void launch_down_mfma(const bf16_t* h, const void* wd, const float* sd, c
     d.n_tiles_x = D / 128;
     d.n_tiles_y = E + static_cast<int>((slots + MT - 1) / MT);
     d.n_tiles_total = d.n_tiles_x * d.n_tiles_y;
-    gemm_stream_kernel<2, kMoeTB, kMoeKS, kMoePF, WF, kDown, TILED>
+    gemm_stream_kernel<2, kMoeTB, kMoeKS, moe_stream_pf<WF>(), WF, kDown, TILED, moe_stream_minwg<WF>()>
         <<<(d.n_tiles_total + 7) / 8 * 8, 256, 0, stream>>>(d);
   }
 }
