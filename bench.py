@@ -11,10 +11,12 @@ A "step" is one canvas denoise step: the forward over the canvas (all 30
 layers, canvas attention over the cache, MoE), the LM head and the sampler.
 ``--steps K`` steps are timed as consecutive fixed-step blocks: K // block_steps
 blocks of block_steps steps, then one block of the remaining K % block_steps
-steps (each block one hipGraph replay, its commit included), bracketed by
-device synchronization.  ``--warmup W`` steps run the same way, untimed,
-before; every block shape that is timed is also run once untimed, so no
-graph capture falls inside the timed region.
+steps, bracketed by device synchronization.  Each block is one hipGraph
+replay of dg_denoise_block_deferred: a block's commit forward (the K/V of its
+final tokens) runs fused into the next block's first step, and the last
+block's by dg_commit_pending, inside the timed region.  ``--warmup W`` steps
+run the same way, untimed, before, and then the timed sequence once more, so
+no graph capture falls inside the timed region.
 
 Printed: one JSON line with steps/s (value), canvas tok/s, ms per step,
 tok/s at 12 steps per block, the roofline of the dominant kernel (the experts'
@@ -503,24 +505,37 @@ def main():
 
         block_ms = []     # device time of each block of the last timed() call
 
+        def run_blocks(m, blocks, ev=None):
+            # consecutive blocks, each block's commit forward fused into the
+            # next block's first step (dg_denoise_block_deferred); the last
+            # block's commit by dg_commit_pending
+            for i, f in enumerate(blocks):
+                dg.dg_denoise_block_deferred(m, cfg_of(f), B, kc, vc, Pd, tok, steps_taken)
+                if ev is not None and i + 1 < len(blocks):
+                    ev[i + 1].record(stream)
+            dg.dg_commit_pending(m, B, kc, vc, Pd)
+            if ev is not None:
+                ev[len(blocks)].record(stream)
+
         def timed(blocks, warm, m=model):
-            """Run the warm blocks (untimed; they capture the graphs), rewind
-            the prefix, then time the blocks (host clock around all of them;
-            HIP events on the bench stream between blocks give each block's
-            device time).  blocks, warm: fixed step counts per block."""
-            for f in warm:
-                dg.dg_denoise_block(m, cfg_of(f), B, kc, vc, Pd, tok, steps_taken)
-            stream.synchronize()
-            Pd.fill_(PROMPT)
-            stream.synchronize()
+            """Run the warm blocks and then the timed sequence once, untimed
+            (they capture every graph the timed run replays), rewinding the
+            prefix after each; then time the blocks (host clock around all of
+            them; HIP events on the bench stream between blocks give each
+            block's device time, the last block's with the final commit).
+            blocks, warm: fixed step counts per block."""
+            for seq in (warm, blocks):
+                if seq:
+                    run_blocks(m, seq)
+                stream.synchronize()
+                Pd.fill_(PROMPT)
+                stream.synchronize()
             torch.cuda.synchronize()
             nb = len(blocks)
             ev = [torch.cuda.Event(enable_timing=True) for _ in range(nb + 1)]
             t0 = time.perf_counter()
             ev[0].record(stream)
-            for i, f in enumerate(blocks):
-                dg.dg_denoise_block(m, cfg_of(f), B, kc, vc, Pd, tok, steps_taken)
-                ev[i + 1].record(stream)
+            run_blocks(m, blocks, ev)
             stream.synchronize()
             torch.cuda.synchronize()
             el = time.perf_counter() - t0
@@ -602,9 +617,12 @@ def main():
         mx = None
         if not a.no_mxfp4:
             w_mx = make_mxfp4_experts(d, w)
+            # (the fused first step of a deferred block runs 2 canvases per
+            # row: the context's prefill limit and the override hold them)
             model_mx = dg.DGModel(d, w_mx, B, CANVAS, dg.DG_BF16, dg.DG_MXFP4,
-                                  weight_layout=dg.DG_LAYOUT_TILED)
-            model_mx.set_router_override(planted_router_logits(d, CANVAS * B))
+                                  weight_layout=dg.DG_LAYOUT_TILED,
+                                  max_prefill_tokens=2 * CANVAS * B)
+            model_mx.set_router_override(planted_router_logits(d, 2 * CANVAS * B))
             el_mx = timed(plan, warm_plan, model_mx)
             mx = {"steps_per_s": round(a.steps / el_mx, 3),
                   "ms_per_step": round(1e3 * el_mx / a.steps, 3),

@@ -108,6 +108,12 @@ constexpr float kLazyRescale = 8.f;
 // subtractions too, measured no faster).
 constexpr bool kAttnMfmaRowSum = true;
 
+// Block-causal masks: token i of a block of Lq sees the cache and the block's
+// tokens up to the end of its own group of mask_blk (1: causal).
+__device__ __forceinline__ int attn_block_end(int tok, int mask_blk, int Lq) {
+  return min(Lq, (tok / mask_blk + 1) * mask_blk);
+}
+
 // LDS row of key k (0..127) of a K tile.  The S^T MFMA's output row 16 b + 4 g
 // + r (b = 0..3 within a 64-key half, g = lane / 16) must hold key 8 g + 4 (b
 // & 1) + r of the half's 32-key chunk b / 2, so that each lane's eight
@@ -172,7 +178,7 @@ __device__ __forceinline__ void attn_store_stage(const AttnStage& st, bf16_t* sk
 __global__ __launch_bounds__(512) void attn_mfma_kernel(
     const bf16_t* __restrict__ qrot, const bf16_t* __restrict__ k_cache,
     const bf16_t* __restrict__ v_cache, const int32_t* __restrict__ prefix_len, int Lq, int G,
-    int Hkv, int Tmax, int chunk, int ntile_rows, int nsplit, int BH, int causal,
+    int Hkv, int Tmax, int chunk, int ntile_rows, int nsplit, int BH, int mask_blk,
     float* __restrict__ o_part, AttnPartialML* __restrict__ ml_part, const int32_t* gate,
     int gate_n, const int32_t* __restrict__ row_done) {
   extern __shared__ __attribute__((aligned(16))) bf16_t smem[];
@@ -202,14 +208,14 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(
   // key range of this split: the row's keys [0, P + Lq) dealt out evenly in
   // whole tiles (P is read on the device, so a captured graph replayed at a
   // larger prefix still balances its splits; chunk * nsplit covers Tmax);
-  // causal: trimmed to the last row of the tile
+  // block-causal (mask_blk > 0): trimmed to the last row of the tile
   const int even = ((n_keys + nsplit - 1) / nsplit + kAttnKeys - 1) / kAttnKeys * kAttnKeys;
   const int split_keys = min(chunk, even);
   const int k_begin = split * split_keys;
   int k_end = min(n_keys, k_begin + split_keys);
-  if (causal) {
+  if (mask_blk) {
     const int last_row = min(rows_total - 1, tile * kAttnRows + kAttnRows - 1);
-    k_end = min(k_end, P + last_row / G + 1);
+    k_end = min(k_end, P + attn_block_end(last_row / G, mask_blk, Lq));
   }
   const int ntiles = k_end > k_begin ? (k_end - k_begin + kAttnKeys - 1) / kAttnKeys : 0;
 
@@ -279,14 +285,14 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(
       }
     }
     // keys at or past a row's limit only occur in the split's last tile, or
-    // past the wave's first token under the causal mask
-    const int wave_lim = causal ? min(k_end, P + wave_tok + 1) : k_end;
+    // past the wave's first token's block under a block-causal mask
+    const int wave_lim = mask_blk ? min(k_end, P + attn_block_end(wave_tok, mask_blk, Lq)) : k_end;
     const bool edge = hkey0 + 64 > wave_lim;   // wave-uniform
     bf16x8_t pf[2][2];   // [qb][32-key chunk]
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       if (edge) {
-        const int key_lim = causal ? min(k_end, P + tok_of[qb] + 1) : k_end;
+        const int key_lim = mask_blk ? min(k_end, P + attn_block_end(tok_of[qb], mask_blk, Lq)) : k_end;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
@@ -480,7 +486,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
 __global__ void attn_f32_kernel(const float* __restrict__ qrot, const float* __restrict__ k_cache,
                                 const float* __restrict__ v_cache,
                                 const int32_t* __restrict__ prefix_len, int Lq, int G, int Hkv,
-                                int Tmax, int dh, int causal, float scale,
+                                int Tmax, int dh, int mask_blk, float scale,
                                 float* __restrict__ out) {
   const int r = blockIdx.x, bh = blockIdx.y;
   const int b = bh / Hkv, g = bh % Hkv;
@@ -488,7 +494,7 @@ __global__ void attn_f32_kernel(const float* __restrict__ qrot, const float* __r
   const int rows_total = Lq * G;
   const int tok = r / G;
   const int P = prefix_len[b];
-  const int n_keys = min(causal ? P + tok + 1 : P + Lq, Tmax);   // never past the cache
+  const int n_keys = min(P + (mask_blk ? attn_block_end(tok, mask_blk, Lq) : Lq), Tmax);   // never past the cache
   const float* qr = qrot + (static_cast<int64_t>(bh) * rows_total + r) * dh;
   const float q0 = lane < dh ? qr[lane] : 0.f;
   const float q1 = lane + 64 < dh ? qr[lane + 64] : 0.f;
@@ -516,6 +522,13 @@ __global__ void attn_f32_kernel(const float* __restrict__ qrot, const float* __r
 }
 
 // ------------------------------------------------------------- launchers
+// Group size of the block-causal mask: 0 for the canvas mask (the whole
+// block), 1 causal, or the AttnArgs' own mask_blk.
+static int attn_mask_blk(const AttnArgs& a) {
+  if (a.mask_blk > 0) return a.mask_blk;
+  return a.mask_mode == DG_MASK_CAUSAL ? 1 : 0;
+}
+
 struct AttnPlan {
   int tiles, nsplit, chunk;
   size_t q_bytes, o_bytes, ml_bytes;
@@ -574,7 +587,7 @@ dg_status launch_attention(const AttnArgs& a, void* ws, hipStream_t stream) {
     attn_mfma_kernel<<<(total + 7) / 8 * 8, 512, kAttnSmemBytes, stream>>>(
         static_cast<const bf16_t*>(qrot), static_cast<const bf16_t*>(a.k_cache),
         static_cast<const bf16_t*>(a.v_cache), a.prefix_len, a.Lq, G, a.Hkv, a.Tmax, p.chunk,
-        p.tiles, p.nsplit, a.B * a.Hkv, a.mask_mode == DG_MASK_CAUSAL, o_part, ml,
+        p.tiles, p.nsplit, a.B * a.Hkv, attn_mask_blk(a), o_part, ml,
         a.gate.n_done, a.gate.n, a.gate.row_done);
     DG_LAUNCH_CHECK();
     attn_combine_kernel<bf16_t><<<(a.B * a.Hkv * rows + 7) / 8, 256, 0, stream>>>(
@@ -591,7 +604,7 @@ dg_status launch_attention(const AttnArgs& a, void* ws, hipStream_t stream) {
     attn_f32_kernel<<<dim3(rows, a.B * a.Hkv), 64, 0, stream>>>(
         static_cast<const float*>(qrot), static_cast<const float*>(a.k_cache),
         static_cast<const float*>(a.v_cache), a.prefix_len, a.Lq, G, a.Hkv, a.Tmax, a.dh,
-        a.mask_mode == DG_MASK_CAUSAL, static_cast<float>(1.0 / sqrt(static_cast<double>(a.dh))),
+        attn_mask_blk(a), static_cast<float>(1.0 / sqrt(static_cast<double>(a.dh))),
         static_cast<float*>(a.out));
     DG_LAUNCH_CHECK();
   }

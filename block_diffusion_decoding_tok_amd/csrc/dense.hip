@@ -497,12 +497,17 @@ __device__ __forceinline__ void rope_table_row(const RopeTable& rt, int row) {
   rt.tab[static_cast<int64_t>(row) * rt.pairs + j] = make_float2(c, s);
 }
 
+__device__ __forceinline__ int norm_in_row(const NormRows& nr, int r) {
+  return nr.blk > 0 ? (r / nr.blk) * nr.in_blk + nr.in_off + r % nr.blk : r;
+}
+
 template <typename TS, typename TO>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const TS* __restrict__ y_slot, int k,
                                                       float* __restrict__ x,
                                                       TO* __restrict__ out, int D, int tiled,
-                                                      RopeTable rt) {
-  const int row = blockIdx.x;
+                                                      RopeTable rt, NormRows nr) {
+  const int orow = blockIdx.x;                  // output row
+  const int row = norm_in_row(nr, orow);        // input row of x (and y_slot)
   rope_table_row(rt, row);
   float4* xr = reinterpret_cast<float4*>(x + static_cast<int64_t>(row) * D);
   const int n4 = D / 4;
@@ -552,7 +557,7 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const TS* __restrict__ y_s
   __syncthreads();
   const float tot = s_part[0] + s_part[1] + s_part[2] + s_part[3];
   const float inv = rsqrtf(tot / D + 1e-6f);
-  TO* o = out + static_cast<int64_t>(row) * D;
+  TO* o = out + static_cast<int64_t>(orow) * D;
 #pragma unroll
   for (int i = 0; i < kNormPieces; ++i) {
     const int p = i * 256 + threadIdx.x;
@@ -561,7 +566,7 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const TS* __restrict__ y_s
       uint2 pk;
       pk.x = pack_bf16x2(v[i].x * inv, v[i].y * inv);
       pk.y = pack_bf16x2(v[i].z * inv, v[i].w * inv);
-      TO* dst = tiled ? out + xtile_offset(row, 4 * p, D) : o + 4 * p;
+      TO* dst = tiled ? out + xtile_offset(orow, 4 * p, D) : o + 4 * p;
       *reinterpret_cast<uint2*>(dst) = pk;
     } else {
       *reinterpret_cast<float4*>(o + 4 * p) =
@@ -574,8 +579,9 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const TS* __restrict__ y_s
 template <typename TO>
 __global__ __launch_bounds__(256) void rmsnorm_wide_kernel(const float* __restrict__ x,
                                                            TO* __restrict__ out, int D,
-                                                           RopeTable rt) {
-  const int row = blockIdx.x;
+                                                           RopeTable rt, NormRows nr) {
+  const int orow = blockIdx.x;
+  const int row = norm_in_row(nr, orow);
   rope_table_row(rt, row);
   const float* xr = x + static_cast<int64_t>(row) * D;
   float ss = 0.f;
@@ -586,7 +592,7 @@ __global__ __launch_bounds__(256) void rmsnorm_wide_kernel(const float* __restri
   __syncthreads();
   const float tot = s_part[0] + s_part[1] + s_part[2] + s_part[3];
   const float inv = rsqrtf(tot / D + 1e-6f);
-  TO* o = out + static_cast<int64_t>(row) * D;
+  TO* o = out + static_cast<int64_t>(orow) * D;
   for (int d = threadIdx.x; d < D; d += blockDim.x) Elem<TO>::store(o, d, xr[d] * inv);
 }
 
@@ -598,19 +604,22 @@ dg_status launch_rmsnorm(const float* x, void* out, int M, int D, int out_dtype,
 
 dg_status launch_combine_rmsnorm(const void* y_slot, int slot_dtype, int k, float* x, void* out,
                                  int M, int D, int out_dtype, hipStream_t stream, bool out_tiled,
-                                 const RopeTable& rope) {
+                                 const RopeTable& rope, const NormRows& rows) {
   if (rope.tab && (rope.pairs <= 0 || rope.pairs > 256 || rope.Lq <= 0 || !rope.prefix_len))
+    return DG_ERR_INVALID_ARG;
+  if (rows.blk < 0 || (rows.blk > 0 && (rows.in_off < 0 || rows.in_off + rows.blk > rows.in_blk)))
     return DG_ERR_INVALID_ARG;
   const bool regs = D % 4 == 0 && D / 4 <= kNormPieces * 256;
   if (out_tiled && !(regs && D % 64 == 0 && out_dtype == DG_BF16)) return DG_ERR_UNSUPPORTED;
   const int tl = out_tiled ? 1 : 0;
   if (!regs) {
+    if (rows.blk > 0) return DG_ERR_UNSUPPORTED;   // the row map needs the fused combine
     dg_status st;
     if (y_slot && (st = launch_moe_combine(y_slot, slot_dtype, M, D, k, x, stream))) return st;
     if (out_dtype == DG_BF16)
-      rmsnorm_wide_kernel<bf16_t><<<M, 256, 0, stream>>>(x, static_cast<bf16_t*>(out), D, rope);
+      rmsnorm_wide_kernel<bf16_t><<<M, 256, 0, stream>>>(x, static_cast<bf16_t*>(out), D, rope, rows);
     else
-      rmsnorm_wide_kernel<float><<<M, 256, 0, stream>>>(x, static_cast<float*>(out), D, rope);
+      rmsnorm_wide_kernel<float><<<M, 256, 0, stream>>>(x, static_cast<float*>(out), D, rope, rows);
     DG_LAUNCH_CHECK();
     return DG_OK;
   }
@@ -618,11 +627,11 @@ dg_status launch_combine_rmsnorm(const void* y_slot, int slot_dtype, int k, floa
   const bf16_t* yb = bf ? static_cast<const bf16_t*>(y_slot) : nullptr;
   const float* yf = bf ? nullptr : static_cast<const float*>(y_slot);
   if (out_dtype == DG_BF16) {
-    if (bf) rmsnorm_kernel<bf16_t, bf16_t><<<M, 256, 0, stream>>>(yb, k, x, static_cast<bf16_t*>(out), D, tl, rope);
-    else rmsnorm_kernel<float, bf16_t><<<M, 256, 0, stream>>>(yf, k, x, static_cast<bf16_t*>(out), D, tl, rope);
+    if (bf) rmsnorm_kernel<bf16_t, bf16_t><<<M, 256, 0, stream>>>(yb, k, x, static_cast<bf16_t*>(out), D, tl, rope, rows);
+    else rmsnorm_kernel<float, bf16_t><<<M, 256, 0, stream>>>(yf, k, x, static_cast<bf16_t*>(out), D, tl, rope, rows);
   } else {
-    if (bf) rmsnorm_kernel<bf16_t, float><<<M, 256, 0, stream>>>(yb, k, x, static_cast<float*>(out), D, 0, rope);
-    else rmsnorm_kernel<float, float><<<M, 256, 0, stream>>>(yf, k, x, static_cast<float*>(out), D, 0, rope);
+    if (bf) rmsnorm_kernel<bf16_t, float><<<M, 256, 0, stream>>>(yb, k, x, static_cast<float*>(out), D, 0, rope, rows);
+    else rmsnorm_kernel<float, float><<<M, 256, 0, stream>>>(yf, k, x, static_cast<float*>(out), D, 0, rope, rows);
   }
   DG_LAUNCH_CHECK();
   return DG_OK;

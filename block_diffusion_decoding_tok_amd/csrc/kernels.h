@@ -53,6 +53,10 @@ struct AttnArgs {
   int q_ready = 0;                    // q already rotated in the workspace, k/v in the caches
   int out_tiled = 0;                  // bf16 out in the tiled activation layout (xtile_offset)
   StepGate gate = {};
+  // > 0: block-causal mask with groups of mask_blk tokens (a token sees the
+  // cache and its block's tokens up to the end of its own group), in place
+  // of mask_mode
+  int mask_blk = 0;
 };
 // Scale of the packed q of the bf16 attention kernel: log2(e) / sqrt(dh), so
 // that scores come out of the MFMA in the log2 domain.
@@ -141,14 +145,22 @@ struct RopeTable {
   float theta = 0.f;
   float2* tab = nullptr;
 };
+// Rows of a norm that reads a subset of x: with blk > 0, output row r reads
+// input row (r / blk) * in_blk + in_off + r % blk (e.g. the last L of every
+// 2L-token row of a forward); blk == 0: output row r reads row r.
+struct NormRows {
+  int blk = 0, in_blk = 0, in_off = 0;
+};
 // The MoE combine fused into the next RMSNorm: x[t] += sum_j y_slot[t * k + j]
 // (slot order, as launch_moe_combine), then out = RMSNorm(x).  y_slot may be
 // null (plain RMSNorm); slot_dtype is DG_BF16 or DG_F32.  out_tiled: bf16
 // out in the tiled activation layout (D % 64 == 0, D <= 4096).  rope: the
-// RoPE table of the rows (pairs <= 256), written alongside.
+// RoPE table of the rows (pairs <= 256), written alongside.  rows: M output
+// rows read (and combine into) the input rows NormRows maps them to.
 dg_status launch_combine_rmsnorm(const void* y_slot, int slot_dtype, int k, float* x, void* out,
                                  int M, int D, int out_dtype, hipStream_t stream,
-                                 bool out_tiled = false, const RopeTable& rope = {});
+                                 bool out_tiled = false, const RopeTable& rope = {},
+                                 const NormRows& rows = {});
 // x[t] = emb[tokens[t]] as f32.
 dg_status launch_embed(const int32_t* tokens, const void* emb, float* x, int M, int D,
                        int dtype, hipStream_t stream);

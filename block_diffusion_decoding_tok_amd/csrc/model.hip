@@ -155,6 +155,15 @@ struct dg_ctx {
   int32_t* blk_tokens = nullptr;   // dg_generate: the current block's tokens [B, L]
   int32_t* blk_steps = nullptr;    // dg_generate: the current block's steps [B]
   float2* rope_tab = nullptr;      // (cos, sin) of a forward's tokens x pairs
+  // deferred commit (dg_denoise_block_deferred): the last block's final
+  // tokens, whose K/V the next deferred block's first step (or
+  // dg_commit_pending) writes into the cache slots [P - L, P)
+  int32_t* pending_tok = nullptr;  // [maxB, maxT]
+  int32_t* fused_tok = nullptr;    // [maxB, 2 maxT]: each row's pending block, then its canvas
+  int32_t* prefix_back = nullptr;  // [maxB]: prefix - L, the pending block's first position
+  bool pending = false;            // host-side enqueue state
+  int pending_B = 0, pending_L = 0, pending_Tmax = 0;
+  std::vector<void*> pending_ptrs; // the caches and prefix array it belongs to
   // host-visible status word (pinned host memory): the device stores a
   // non-zero block status there; the host reads and clears it
   int32_t* host_status = nullptr;
@@ -181,7 +190,8 @@ namespace {
 struct Layout {
   size_t x, h, qkv, attn_out, router, topk_ids, gates, offsets, sorted_rows, attn_ws, moe_ws,
       logits, samp_ws, tokens, committed, renoised, maxprob, entropy, mean_entropy, done, status,
-      n_done, active, blk_tokens, blk_steps, rope_tab, total;
+      n_done, active, blk_tokens, blk_steps, rope_tab, pending_tok, fused_tok, prefix_back,
+      total;
 };
 
 size_t esz(int dt) { return dt == DG_F32 ? 4 : 2; }
@@ -237,6 +247,9 @@ Layout layout(const dg_model_dims& d, int maxB, int maxT, int maxP) {
   L.blk_tokens = take(Tc * 4);
   L.blk_steps = take(maxB * 4);
   L.rope_tab = take(T * (d.head_dim / 2) * sizeof(float2));   // RoPE table of a forward
+  L.pending_tok = take(Tc * 4);
+  L.fused_tok = take(2 * Tc * 4);
+  L.prefix_back = take(maxB * 4);
   L.total = off;
   return L;
 }
@@ -276,7 +289,7 @@ dg_status check_dims(const dg_model_dims* d) {
 }
 
 dg_status norm_input(dg_ctx* c, int T, hipStream_t s, bool tiled = false,
-                     const RopeTable& rope = {});
+                     const RopeTable& rope = {}, const NormRows& rows = {}, int m_out = 0);
 dg_status layer_tail(dg_ctx* c, int l, int B, int n, bool xt, hipStream_t s);
 
 // Whether a layer over T tokens runs its dense projections on the tiled
@@ -291,7 +304,8 @@ bool tiled_acts(const dg_model_dims& d, const QkvRope& r) {
 
 // One decoder layer over T = B * n tokens (residual ctx->x).
 dg_status layer(dg_ctx* c, int l, int B, int n, void* kc, void* vc, int Tmax,
-                const int32_t* prefix_len, int mode, bool kv_only, hipStream_t s) {
+                const int32_t* prefix_len, int mode, bool kv_only, hipStream_t s,
+                int mask_blk = 0) {
   const dg_model_dims& d = c->d;
   const int T = B * n;
   const int qd = d.n_heads * d.head_dim, kd = d.n_kv_heads * d.head_dim;
@@ -315,7 +329,7 @@ dg_status layer(dg_ctx* c, int l, int B, int n, void* kc, void* vc, int Tmax,
       if (kv_only) return DG_OK;
       AttnArgs aa{nullptr, nullptr, nullptr, 0, 0, kc, vc, prefix_len, B, n, d.n_heads,
                   d.n_kv_heads, d.head_dim, Tmax, mode, d.rope_theta, d.act_dtype, c->attn_out, 1,
-                  xt ? 1 : 0, c->gate};
+                  xt ? 1 : 0, c->gate, mask_blk};
       if ((st = launch_attention(aa, c->attn_ws, s))) return st;
       return layer_tail(c, l, B, n, xt, s);
     }
@@ -331,7 +345,7 @@ dg_status layer(dg_ctx* c, int l, int B, int n, void* kc, void* vc, int Tmax,
                          d.rope_theta, d.act_dtype, false, s);
   AttnArgs aa{qkv, qkv + qd * a, qkv + (qd + kd) * a, qkv_w, qkv_w, kc, vc, prefix_len, B, n,
               d.n_heads, d.n_kv_heads, d.head_dim, Tmax, mode, d.rope_theta, d.act_dtype,
-              c->attn_out, 0, 0, c->gate};
+              c->attn_out, 0, 0, c->gate, mask_blk};
   if ((st = launch_attention(aa, c->attn_ws, s))) return st;
   return layer_tail(c, l, B, n, false, s);
 }
@@ -378,14 +392,18 @@ dg_status layer_tail(dg_ctx* c, int l, int B, int n, bool xt, hipStream_t s) {
 // RMSNorm of the residual stream into c->h (tiled: in the tiled activation
 // layout), taking a pending MoE combine (the previous layer's expert outputs)
 // into x first.
-dg_status norm_input(dg_ctx* c, int T, hipStream_t s, bool tiled, const RopeTable& rope) {
+// The norm of a forward's T tokens into c->h (m_out rows through `rows` when
+// set), with the last MoE layer's pending combine.
+dg_status norm_input(dg_ctx* c, int T, hipStream_t s, bool tiled, const RopeTable& rope,
+                     const NormRows& rows, int m_out) {
   const dg_model_dims& d = c->d;
   void *h_mid, *y_slot = nullptr;
   if (c->pending_combine)
     moe_ffn_workspace_split(c->moe_ws, T, d.d_ff, d.top_k, d.act_dtype, &h_mid, &y_slot);
   c->pending_combine = false;
-  return launch_combine_rmsnorm(y_slot, d.act_dtype, d.top_k, c->x, c->h, T, d.d_model,
-                                d.act_dtype, s, tiled, rope);
+  return launch_combine_rmsnorm(y_slot, d.act_dtype, d.top_k, c->x, c->h,
+                                m_out > 0 ? m_out : T, d.d_model, d.act_dtype, s, tiled, rope,
+                                rows);
 }
 
 // Flush a pending MoE combine into x (end of a forward without the LM head).
@@ -398,9 +416,13 @@ dg_status flush_combine(dg_ctx* c, int T, hipStream_t s) {
   return launch_moe_combine(y_slot, d.act_dtype, T, d.d_model, d.top_k, c->x, s);
 }
 
+// mask_blk > 0: block-causal attention over the n tokens of each row in
+// groups of mask_blk; lm_rows: the rows of each batch row the LM head takes
+// (logits [B * lm_rows.blk] when set, else all B * n).
 dg_status forward(dg_ctx* c, const int32_t* tokens, int B, int n, int l0, int l1,
                   void* const* kcs, void* const* vcs, int Tmax, const int32_t* prefix_len,
-                  int mode, void* logits, bool commit_only, hipStream_t s) {
+                  int mode, void* logits, bool commit_only, hipStream_t s, int mask_blk = 0,
+                  const NormRows& lm_rows = {}) {
   const dg_model_dims& d = c->d;
   dg_status st;
   c->pending_combine = false;   // a combine is only carried within one forward
@@ -408,16 +430,14 @@ dg_status forward(dg_ctx* c, const int32_t* tokens, int B, int n, int l0, int l1
     return st;
   for (int l = l0; l < l1; ++l) {
     const bool kv_only = commit_only && l == d.n_layers - 1;
-    if ((st = layer(c, l, B, n, kcs[l], vcs[l], Tmax, prefix_len, mode, kv_only, s))) return st;
-  }
-  if (!logits) return flush_combine(c, B * n, s);
-  {
-    if ((st = norm_input(c, B * n, s))) return st;
-    if ((st = launch_gemm(c->h, c->lm, logits, B * n, d.vocab, d.d_model, d.act_dtype,
-                          d.weight_layout, d.act_dtype, kStore, s, c->gate)))
+    if ((st = layer(c, l, B, n, kcs[l], vcs[l], Tmax, prefix_len, mode, kv_only, s, mask_blk)))
       return st;
   }
-  return DG_OK;
+  if (!logits) return flush_combine(c, B * n, s);
+  const int m = lm_rows.blk > 0 ? B * lm_rows.blk : B * n;
+  if ((st = norm_input(c, B * n, s, false, {}, lm_rows, m))) return st;
+  return launch_gemm(c->h, c->lm, logits, m, d.vocab, d.d_model, d.act_dtype, d.weight_layout,
+                     d.act_dtype, kStore, s, c->gate);
 }
 
 // Copies the count of stopped rows to the context's host-visible word.
@@ -473,6 +493,86 @@ dg_status enqueue_block_end(dg_ctx* c, const dg_sampler_cfg& cfg, int B, void* c
   if ((st = forward(c, c->tokens, B, L, 0, c->d.n_layers, kcs, vcs, Tmax, prefix_len,
                     DG_MASK_CANVAS, nullptr, true, s)))
     return st;
+  if ((st = launch_advance_prefix(prefix_len, B, L, s))) return st;
+  copy_i32_kernel<<<(B * L + 255) / 256, 256, 0, s>>>(c->tokens, tokens_out, B * L);
+  DG_LAUNCH_CHECK();
+  return publish_status(c, s);
+}
+
+// Deferred commit: row b's pending block then its canvas, [B, 2L]; and the
+// pending block's first position, prefix - L.
+__global__ void assemble_fused_kernel(const int32_t* __restrict__ pending,
+                                      const int32_t* __restrict__ canvas, int B, int L,
+                                      int32_t* __restrict__ fused) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= B * 2 * L) return;
+  const int b = i / (2 * L), j = i % (2 * L);
+  fused[i] = j < L ? pending[b * L + j] : canvas[b * L + j - L];
+}
+
+__global__ void prefix_back_kernel(const int32_t* __restrict__ prefix_len, int B, int L,
+                                   int32_t* __restrict__ back) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b < B) back[b] = prefix_len[b] - L;
+}
+
+// The first step of a deferred block with a commit pending: one forward over
+// each row's pending block (positions [P - L, P)) followed by its canvas
+// ([P, P + L)), the pending block attending to the cache before it and to
+// itself, the canvas to both blocks and itself (block-causal groups of L).
+// It writes the pending block's K/V into the cache as its commit forward
+// would, and the canvas rows' logits as the step's own forward would; then
+// the step's sampler.
+dg_status enqueue_fused_first_step(dg_ctx* c, const dg_sampler_cfg& cfg, int B, void* const* kcs,
+                                   void* const* vcs, int Tmax, int32_t* prefix_len,
+                                   int32_t* steps_taken, hipStream_t s) {
+  const dg_model_dims& d = c->d;
+  const int L = cfg.canvas_len;
+  assemble_fused_kernel<<<(2 * B * L + 255) / 256, 256, 0, s>>>(c->pending_tok, c->tokens, B, L,
+                                                                c->fused_tok);
+  DG_LAUNCH_CHECK();
+  prefix_back_kernel<<<(B + 63) / 64, 64, 0, s>>>(prefix_len, B, L, c->prefix_back);
+  DG_LAUNCH_CHECK();
+  dg_status st;
+  if ((st = forward(c, c->fused_tok, B, 2 * L, 0, d.n_layers, kcs, vcs, Tmax, c->prefix_back,
+                    DG_MASK_CANVAS, c->logits, false, s, L, NormRows{L, 2 * L, L})))
+    return st;
+  return launch_sampler(c->logits, d.act_dtype, B, L, d.vocab, 0, cfg, prefix_len, c->tokens,
+                        c->committed, c->renoised, c->maxprob, c->entropy, c->mean_entropy,
+                        c->done, c->status, steps_taken, c->samp_ws, s, c->n_done);
+}
+
+// The commit forward of the pending block alone (positions [P - L, P)).
+dg_status enqueue_commit_pending(dg_ctx* c, int B, int L, void* const* kcs, void* const* vcs,
+                                 int Tmax, const int32_t* prefix_len, hipStream_t s) {
+  prefix_back_kernel<<<(B + 63) / 64, 64, 0, s>>>(prefix_len, B, L, c->prefix_back);
+  DG_LAUNCH_CHECK();
+  return forward(c, c->pending_tok, B, L, 0, c->d.n_layers, kcs, vcs, Tmax, c->prefix_back,
+                 DG_MASK_CANVAS, nullptr, true, s);
+}
+
+// A fixed-steps block whose commit is deferred: its first step fused with
+// the previous block's commit when one is pending; at the end the final
+// tokens become the pending block and the prefix advances by L.
+dg_status enqueue_block_deferred(dg_ctx* c, const dg_sampler_cfg& cfg, int B, void* const* kcs,
+                                 void* const* vcs, int Tmax, int32_t* prefix_len,
+                                 int32_t* tokens_out, int32_t* steps_taken, bool fused,
+                                 hipStream_t s) {
+  const int L = cfg.canvas_len;
+  const int n_steps = cfg.fixed_steps;
+  dg_status st;
+  if ((st = enqueue_block_begin(c, cfg, B, prefix_len, steps_taken, s))) return st;
+  int first = 0;
+  if (fused) {
+    if ((st = enqueue_fused_first_step(c, cfg, B, kcs, vcs, Tmax, prefix_len, steps_taken, s)))
+      return st;
+    first = 1;
+  }
+  if ((st = enqueue_block_steps(c, cfg, B, kcs, vcs, Tmax, prefix_len, steps_taken, first,
+                                n_steps, s)))
+    return st;
+  copy_i32_kernel<<<(B * L + 255) / 256, 256, 0, s>>>(c->tokens, c->pending_tok, B * L);
+  DG_LAUNCH_CHECK();
   if ((st = launch_advance_prefix(prefix_len, B, L, s))) return st;
   copy_i32_kernel<<<(B * L + 255) / 256, 256, 0, s>>>(c->tokens, tokens_out, B * L);
   DG_LAUNCH_CHECK();
@@ -584,6 +684,28 @@ dg_status check_block_cfg(const dg_sampler_cfg* cfg, const char* fn) {
                     cfg->entropy_bound < INFINITY),
                std::string(fn) + ": bad commit_policy / entropy_bound");
   return DG_OK;
+}
+
+// Every entry point but the deferred block and dg_commit_pending refuses to
+// run while a deferred commit is pending (its K/V are not in the cache yet).
+dg_status check_no_pending(dg_ctx* c, const char* fn) {
+  if (c && c->pending)
+    return fail(DG_ERR_INVALID_ARG, std::string(fn) +
+                                        ": a deferred block commit is pending on this context "
+                                        "(call dg_commit_pending first)");
+  return DG_OK;
+}
+
+// The caches, prefix array, B, L and Tmax a pending commit belongs to.
+std::vector<void*> pending_key_ptrs(dg_ctx* c, void* const* kcs, void* const* vcs,
+                                    const int32_t* prefix_len) {
+  std::vector<void*> v;
+  for (int l = 0; l < c->d.n_layers; ++l) {
+    v.push_back(kcs[l]);
+    v.push_back(vcs[l]);
+  }
+  v.push_back(const_cast<int32_t*>(prefix_len));
+  return v;
 }
 
 // Adaptive mode: steps the host keeps queued beyond the one whose done
@@ -791,6 +913,9 @@ dg_status dg_ctx_create(dg_ctx** out, const dg_model_dims* dims, const dg_model_
   c->blk_tokens = reinterpret_cast<int32_t*>(b + L.blk_tokens);
   c->blk_steps = reinterpret_cast<int32_t*>(b + L.blk_steps);
   c->rope_tab = reinterpret_cast<float2*>(b + L.rope_tab);
+  c->pending_tok = reinterpret_cast<int32_t*>(b + L.pending_tok);
+  c->fused_tok = reinterpret_cast<int32_t*>(b + L.fused_tok);
+  c->prefix_back = reinterpret_cast<int32_t*>(b + L.prefix_back);
   *out = c;
   return DG_OK;
 }
@@ -845,7 +970,7 @@ dg_status dg_model_forward(dg_ctx* ctx, const int32_t* tokens, float* x, int B, 
   const int max_n = ctx ? std::max(ctx->max_tokens, B > 0 ? ctx->max_prefill / B : 0) : 0;
   dg_status st = check_run(ctx, B, n, k_caches, v_caches, Tmax, prefix_len, "dg_model_forward",
                            max_n);
-  if (st != DG_OK) return st;
+  if (st != DG_OK || (st = check_no_pending(ctx, "dg_model_forward"))) return st;
   DG_CHECK_ARG(x != nullptr, "dg_model_forward: x is null");
   DG_CHECK_ARG(mask_mode == DG_MASK_CANVAS || mask_mode == DG_MASK_CAUSAL,
                "dg_model_forward: bad mask_mode");
@@ -875,7 +1000,7 @@ dg_status dg_prefill(dg_ctx* ctx, const int32_t* prompt, int B, int n, void* con
   const int chunk = std::max(ctx->max_tokens, ctx->max_prefill / B);
   dg_status st = check_run(ctx, B, std::min(n, chunk), k_caches, v_caches, Tmax, prefix_len,
                            "dg_prefill", chunk);
-  if (st != DG_OK) return st;
+  if (st != DG_OK || (st = check_no_pending(ctx, "dg_prefill"))) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   // the chunk's token ids, contiguous per row, staged in the canvas buffer
   for (int c0 = 0; c0 < n; c0 += chunk) {
@@ -898,7 +1023,7 @@ dg_status dg_ar_decode(dg_ctx* ctx, int B, int n_steps, const int32_t* tokens_in
   DG_CHECK_SHAPE(n_steps >= 1 && n_steps <= Tmax, "dg_ar_decode: n_steps outside [1, Tmax]");
   DG_CHECK_SHAPE(ctx->d.vocab % 8 == 0, "dg_ar_decode: vocab must be a multiple of 8");
   dg_status st = check_run(ctx, B, 1, k_caches, v_caches, Tmax, prefix_len, "dg_ar_decode");
-  if (st != DG_OK) return st;
+  if (st != DG_OK || (st = check_no_pending(ctx, "dg_ar_decode"))) return st;
   if ((st = take_status(ctx, "dg_ar_decode"))) return st;
   // graph key: F = -1 marks the AR loop (block keys have F >= 0)
   GraphKey key{B, Tmax, 1, n_steps, -1, 0.f, 0.f, 0.f, 0.f, 0.f, 0, 0, 0.f, 0, {}};
@@ -924,10 +1049,77 @@ dg_status dg_denoise_block(dg_ctx* ctx, const dg_sampler_cfg* cfg, int B, void* 
   if (st != DG_OK) return st;
   st = check_run(ctx, B, cfg->canvas_len, k_caches, v_caches, Tmax, prefix_len,
                  "dg_denoise_block");
-  if (st != DG_OK) return st;
+  if (st != DG_OK || (st = check_no_pending(ctx, "dg_denoise_block"))) return st;
   if ((st = take_status(ctx, "dg_denoise_block"))) return st;
   return run_block(ctx, *cfg, B, k_caches, v_caches, Tmax, prefix_len, tokens_out, steps_taken,
                    static_cast<hipStream_t>(stream));
+}
+
+dg_status dg_denoise_block_deferred(dg_ctx* ctx, const dg_sampler_cfg* cfg, int B,
+                                    void* const* k_caches, void* const* v_caches, int Tmax,
+                                    int32_t* prefix_len, int32_t* tokens_out,
+                                    int32_t* steps_taken, void* stream) {
+  set_error("");
+  const char* fn = "dg_denoise_block_deferred";
+  DG_CHECK_ARG(ctx && cfg && tokens_out && steps_taken, std::string(fn) + ": null pointer");
+  dg_status st = check_block_cfg(cfg, fn);
+  if (st != DG_OK) return st;
+  if (cfg->fixed_steps <= 0)
+    return fail(DG_ERR_UNSUPPORTED, std::string(fn) + ": needs fixed_steps > 0");
+  const int L = cfg->canvas_len;
+  st = check_run(ctx, B, L, k_caches, v_caches, Tmax, prefix_len, fn);
+  if (st != DG_OK) return st;
+  // the fused first step runs 2L tokens per row: the activation and
+  // attention buffers hold them when 2L fits the canvas or the prefill limit
+  DG_CHECK_SHAPE(2 * L <= std::max(ctx->max_tokens, ctx->max_prefill / B),
+                 std::string(fn) + ": needs 2 canvas_len <= max(max_tokens, max_prefill_tokens / B)");
+  DG_CHECK_SHAPE(ctx->router_override.empty() || 2 * B * L <= ctx->router_override_tokens,
+                 std::string(fn) + ": the router override must hold 2 B canvas_len tokens");
+  DG_CHECK_SHAPE(Tmax >= 2 * L, std::string(fn) + ": Tmax smaller than two blocks");
+  const std::vector<void*> ptrs = pending_key_ptrs(ctx, k_caches, v_caches, prefix_len);
+  const bool fused = ctx->pending;
+  if (fused)
+    DG_CHECK_ARG(B == ctx->pending_B && L == ctx->pending_L && Tmax == ctx->pending_Tmax &&
+                     ptrs == ctx->pending_ptrs,
+                 std::string(fn) + ": the pending commit belongs to other caches or shapes");
+  if ((st = take_status(ctx, fn))) return st;
+  GraphKey key{B, Tmax, L, cfg->max_steps, cfg->fixed_steps, cfg->temp_start, cfg->temp_end,
+               cfg->stop_entropy, cfg->commit_prob, cfg->renoise_prob, cfg->seed,
+               cfg->commit_policy, cfg->entropy_bound, fused ? 11 : 10, ptrs};
+  key.ptrs.push_back(tokens_out);
+  key.ptrs.push_back(steps_taken);
+  st = run_graph(ctx, key, static_cast<hipStream_t>(stream), [&](hipStream_t q) {
+    return enqueue_block_deferred(ctx, *cfg, B, k_caches, v_caches, Tmax, prefix_len, tokens_out,
+                                  steps_taken, fused, q);
+  });
+  if (st != DG_OK) return st;
+  ctx->pending = true;
+  ctx->pending_B = B;
+  ctx->pending_L = L;
+  ctx->pending_Tmax = Tmax;
+  ctx->pending_ptrs = ptrs;
+  return DG_OK;
+}
+
+dg_status dg_commit_pending(dg_ctx* ctx, int B, void* const* k_caches, void* const* v_caches,
+                            int Tmax, const int32_t* prefix_len, void* stream) {
+  set_error("");
+  const char* fn = "dg_commit_pending";
+  DG_CHECK_ARG(ctx != nullptr, std::string(fn) + ": ctx is null");
+  if (!ctx->pending) return DG_OK;
+  dg_status st = check_run(ctx, B, ctx->pending_L, k_caches, v_caches, Tmax, prefix_len, fn);
+  if (st != DG_OK) return st;
+  const std::vector<void*> ptrs = pending_key_ptrs(ctx, k_caches, v_caches, prefix_len);
+  DG_CHECK_ARG(B == ctx->pending_B && Tmax == ctx->pending_Tmax && ptrs == ctx->pending_ptrs,
+               std::string(fn) + ": the pending commit belongs to other caches or shapes");
+  // graph key: F = -3 marks the commit of a deferred block
+  GraphKey key{B, Tmax, ctx->pending_L, 0, -3, 0.f, 0.f, 0.f, 0.f, 0.f, 0, 0, 0.f, 0, ptrs};
+  st = run_graph(ctx, key, static_cast<hipStream_t>(stream), [&](hipStream_t q) {
+    return enqueue_commit_pending(ctx, B, ctx->pending_L, k_caches, v_caches, Tmax, prefix_len, q);
+  });
+  if (st != DG_OK) return st;
+  ctx->pending = false;
+  return DG_OK;
 }
 
 dg_status dg_generate(dg_ctx* ctx, const dg_sampler_cfg* cfg, int B, void* const* k_caches,
@@ -939,7 +1131,7 @@ dg_status dg_generate(dg_ctx* ctx, const dg_sampler_cfg* cfg, int B, void* const
   dg_status st = check_block_cfg(cfg, "dg_generate");
   if (st != DG_OK) return st;
   st = check_run(ctx, B, cfg->canvas_len, k_caches, v_caches, Tmax, prefix_len, "dg_generate");
-  if (st != DG_OK) return st;
+  if (st != DG_OK || (st = check_no_pending(ctx, "dg_generate"))) return st;
   if ((st = take_status(ctx, "dg_generate"))) return st;
   const int L = cfg->canvas_len;
   DG_CHECK_SHAPE(max_blocks >= 1 && static_cast<int64_t>(max_blocks) * L <= Tmax,

@@ -110,6 +110,9 @@ _SIGS = {
                               C.POINTER(_VP), _I, _VP, _VP, _VP, _VP]),
     "dg_generate": (_I, [_VP, C.POINTER(dg_sampler_cfg), _I, C.POINTER(_VP), C.POINTER(_VP),
                          _I, _VP, C.c_int32, _I, _VP, _VP, _VP, _VP]),
+    "dg_denoise_block_deferred": (_I, [_VP, C.POINTER(dg_sampler_cfg), _I, C.POINTER(_VP),
+                                       C.POINTER(_VP), _I, _VP, _VP, _VP, _VP]),
+    "dg_commit_pending": (_I, [_VP, _I, C.POINTER(_VP), C.POINTER(_VP), _I, _VP, _VP]),
     "dg_fill_normal": (_I, [_VP, _I, _SZ, _F, _U64, C.c_uint32, _VP]),
     "dg_quantize_fp8_rows": (_I, [_VP, _VP, _VP, _I64, _I, _VP]),
     "dg_pack_weights": (_I, [_VP, _VP, _I64, _I, _I, _I, _VP]),
@@ -499,6 +502,23 @@ def dg_denoise_block(model, cfg, B, k_caches, v_caches, prefix_len, tokens_out, 
         _dev(prefix_len, "prefix_len", (torch.int32,)),
         _dev(tokens_out, "tokens_out", (torch.int32,)),
         _dev(steps_taken, "steps_taken", (torch.int32,)), _stream(stream)))
+
+
+def dg_denoise_block_deferred(model, cfg, B, k_caches, v_caches, prefix_len, tokens_out,
+                              steps_taken, stream=None):
+    kc, vc = _ptr_array(k_caches), _ptr_array(v_caches)
+    _check(lib().dg_denoise_block_deferred(
+        model.ctx, C.byref(cfg), B, kc, vc, k_caches[0].shape[2],
+        _dev(prefix_len, "prefix_len", (torch.int32,)),
+        _dev(tokens_out, "tokens_out", (torch.int32,)),
+        _dev(steps_taken, "steps_taken", (torch.int32,)), _stream(stream)))
+
+
+def dg_commit_pending(model, B, k_caches, v_caches, prefix_len, stream=None):
+    kc, vc = _ptr_array(k_caches), _ptr_array(v_caches)
+    _check(lib().dg_commit_pending(
+        model.ctx, B, kc, vc, k_caches[0].shape[2],
+        _dev(prefix_len, "prefix_len", (torch.int32,)), _stream(stream)))
 
 
 def dg_generate(model, cfg, B, k_caches, v_caches, prefix_len, eos_id, max_blocks,

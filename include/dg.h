@@ -415,6 +415,40 @@ dg_status dg_generate(dg_ctx* ctx, const dg_sampler_cfg* cfg, int B, void* const
                       int max_blocks, int32_t* tokens_out, int32_t* n_blocks,
                       int32_t* steps_taken, void* stream);
 
+/* dg_denoise_block_deferred: dg_denoise_block (fixed_steps > 0 only) with its
+ * commit forward deferred into the next block ([TR] "DiffusionGemma의 구성",
+ * flowchart: a finished block enters the KV cache before the next block
+ * denoises).  At the end the block's final tokens become the context's
+ * pending block: tokens_out is written and prefix_len += L as with
+ * dg_denoise_block, but the cache slots [P_b - L, P_b) do not hold the final
+ * tokens' K/V yet.  The next dg_denoise_block_deferred (same B, L, Tmax,
+ * caches and prefix_len array) runs its first step as one forward over each
+ * row's pending block (positions [P_b - L, P_b)) followed by its new canvas
+ * ([P_b, P_b + L)) with a block-causal mask: the pending block attends to the
+ * cache before it and to itself, exactly as its commit forward would (and
+ * writes the same K/V), the canvas to the cache, the pending block and
+ * itself, as its first step would; logits are taken for the canvas rows
+ * only.  Each layer's expert weights then stream once for both.  The last
+ * pending block is committed by dg_commit_pending.  While a commit is pending
+ * every other decoder call on the context (dg_model_forward, dg_prefill,
+ * dg_ar_decode, dg_denoise_block, dg_generate) fails with DG_ERR_INVALID_ARG.
+ *   requires 2 L <= max(max_tokens, max_prefill_tokens / B) (the fused step's
+ *   2L tokens per row), Tmax >= 2 L, and a router override (if set) of at
+ *   least 2 B L tokens.  Errors: DG_ERR_UNSUPPORTED for the adaptive mode;
+ *   DG_ERR_INVALID_ARG when a pending commit belongs to other caches, shapes
+ *   or prefix array. */
+dg_status dg_denoise_block_deferred(dg_ctx* ctx, const dg_sampler_cfg* cfg, int B,
+                                    void* const* k_caches, void* const* v_caches, int Tmax,
+                                    int32_t* prefix_len, int32_t* tokens_out,
+                                    int32_t* steps_taken, void* stream);
+/* dg_commit_pending: the commit forward of the context's pending block (its
+ * K/V into slots [P_b - L, P_b); prefix_len is not changed, it was advanced
+ * when the block ran).  DG_OK and nothing launched when none is pending;
+ * DG_ERR_INVALID_ARG when the arguments are not the ones the pending block
+ * ran with. */
+dg_status dg_commit_pending(dg_ctx* ctx, int B, void* const* k_caches, void* const* v_caches,
+                            int Tmax, const int32_t* prefix_len, void* stream);
+
 /* dg_ar_decode: autoregressive decoding on the same model, the left-to-right
  * baseline the canvas is compared with ([JPH] "좌→우 순차 처리와의 대비"; [TR]
  * "수치").  n_steps single-token steps per row: a causal forward of the row's
