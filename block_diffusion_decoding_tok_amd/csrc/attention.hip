@@ -126,6 +126,21 @@ __device__ __forceinline__ int k_lds_row(int k) {
 
 struct AttnPartialML { float m, l; };
 
+// Maximum of x over the four lanes l16 + 16 g (g = 0..3) that hold one row's
+// scores: a swap across the two 32-lane halves, then across neighbouring
+// 16-lane rows (VALU lane swaps; a shuffle would take two LDS round trips).
+// The NaN-propagating maximum needs no operand canonicalization (the
+// number-preferring one doubles the VALU count on scores fresh from the MFMA).
+__device__ __forceinline__ float fmax2(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float max_over_g4(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto h = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const float a = fmax2(__uint_as_float(h[0]), __uint_as_float(h[1]));
+  const unsigned ua = __float_as_uint(a);
+  const auto r = __builtin_amdgcn_permlane16_swap(ua, ua, false, false);
+  return fmax2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // Staging of one 128-key tile through registers, loads clamped to the last
 // valid key (past it the scores are masked, and the clamped rows hold finite
 // cache data):
@@ -304,11 +319,10 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        mx = fmaxf(mx, fmaxf(s_acc[kb][qb][0], s_acc[kb][qb][1]));
-        mx = fmaxf(mx, fmaxf(s_acc[kb][qb][2], s_acc[kb][qb][3]));
+        mx = fmax2(fmax2(mx, s_acc[kb][qb][0]), s_acc[kb][qb][1]);
+        mx = fmax2(fmax2(mx, s_acc[kb][qb][2]), s_acc[kb][qb][3]);
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = max_over_g4(mx);
       // raise the base only past the lazy margin (wave-uniform decision)
       if (__any(mx > m_run[qb] + kLazyRescale)) {
         const float m_new = fmaxf(m_run[qb], mx);

@@ -12,6 +12,7 @@
 //   route_sort_kernel   one 1024-thread workgroup: histogram, exclusive scan
 //                       -> expert_offsets, stable scatter of the slot entries
 //                       t * k + j by expert (ballot-based ranks, deterministic).
+//   route_fused_kernel  both in one workgroup, up to 64 tokens.
 //   gemm_stream_kernel  (gemm_mfma.h) gate/up + GELU*up -> h [T*k, I] bf16 in
 //                       sorted order; down + gate -> y_slot [T*k, D] bf16.
 //   combine_kernel      y[t] += sum_j y_slot[t*k + j] in slot order.
@@ -32,14 +33,17 @@ namespace dg {
 // softmax of the k selected logits (sum in slot order).  QN = 16-lane rows of
 // experts held per lane: 8 for E <= 128, else 16.
 template <int QN>
-__device__ __forceinline__ void route_topk_group(const float* row, int t, int E, int k, int sl,
-                                                 int32_t* __restrict__ ids,
-                                                 float* __restrict__ gates) {
-  // the token's E logits at row (global or LDS); all QN loads issued
-  // unconditionally (clamped), masked afterwards
-  float v[QN];
+__device__ __forceinline__ void route_load_logits(const float* row, int E, int sl, float (&v)[QN]) {
 #pragma unroll
   for (int q = 0; q < QN; ++q) v[q] = row[min(q * 16 + sl, E - 1)];
+}
+
+// Ranks the logits v (as loaded by route_load_logits) of token t; with
+// ids_lds the slot ids are also written there.
+template <int QN>
+__device__ __forceinline__ void route_rank(float (&v)[QN], int t, int E, int k, int sl,
+                                           int32_t* __restrict__ ids, float* __restrict__ gates,
+                                           int* ids_lds = nullptr) {
 #pragma unroll
   for (int q = 0; q < QN; ++q)
     if (q * 16 + sl >= E) v[q] = -INFINITY;
@@ -66,7 +70,19 @@ __device__ __forceinline__ void route_topk_group(const float* row, int t, int E,
   if (sl < k) {
     ids[static_cast<int64_t>(t) * k + sl] = my_id;
     gates[static_cast<int64_t>(t) * k + sl] = expf(my_val - best0) / z;
+    if (ids_lds) ids_lds[t * k + sl] = my_id;
   }
+}
+
+template <int QN>
+__device__ __forceinline__ void route_topk_group(const float* row, int t, int E, int k, int sl,
+                                                 int32_t* __restrict__ ids,
+                                                 float* __restrict__ gates) {
+  // the token's E logits; all QN loads issued unconditionally (clamped),
+  // masked afterwards
+  float v[QN];
+  route_load_logits<QN>(row, E, sl, v);
+  route_rank<QN>(v, t, E, k, sl, ids, gates);
 }
 
 // Four tokens per one-wave workgroup (spread over many CUs: the rounds are
@@ -185,11 +201,55 @@ __global__ __launch_bounds__(1024) void route_sort_kernel(const int32_t* __restr
   sort_slots(ids, n, E, offsets, sorted_rows, sm);
 }
 
+// The top-k and the sort in one 1024-thread workgroup, for up to
+// kRouteFusedMaxTokens tokens (AR decode, small batches): 64 groups of 16
+// lanes take the tokens g, g + 64, ..., the slot ids go to LDS as well, and
+// the counting sort reads them there.  One launch instead of two.  The top-k
+// rounds are VALU work (about 500 wave instructions per token): one CU takes
+// the 256 tokens of a canvas step in ~15 us against ~1 us spread over 64 CUs,
+// so canvas-sized and larger token counts keep the two launches.
+constexpr int kRouteFusedMaxTokens = 64;
+constexpr int kRouteFusedMax = kRouteFusedMaxTokens * 16;   // slot entries (k <= 16)
+
+template <int QN>
+__global__ __launch_bounds__(1024) void route_fused_kernel(const float* __restrict__ logits, int T,
+                                                           int E, int k, int32_t* __restrict__ ids,
+                                                           float* __restrict__ gates,
+                                                           int32_t* __restrict__ offsets,
+                                                           int32_t* __restrict__ sorted_rows) {
+  __shared__ SortSmem sm;
+  __shared__ int s_ids[kRouteFusedMax];
+  const int g = threadIdx.x >> 4, sl = threadIdx.x & 15;
+  if (g < T) {
+    float v[QN];
+    route_load_logits<QN>(logits + static_cast<int64_t>(g) * E, E, sl, v);
+    for (int t = g; t < T; t += 64) {
+      float cur[QN];
+#pragma unroll
+      for (int q = 0; q < QN; ++q) cur[q] = v[q];
+      if (t + 64 < T) route_load_logits<QN>(logits + static_cast<int64_t>(t + 64) * E, E, sl, v);
+      route_rank<QN>(cur, t, E, k, sl, ids, gates, s_ids);
+    }
+  }
+  __syncthreads();
+  sort_slots(s_ids, T * k, E, offsets, sorted_rows, sm);
+}
+
 size_t moe_route_workspace_bytes(int, int, int) { return 0; }
 
 dg_status launch_moe_route(const float* logits, int T, int E, int k, int32_t* topk_ids,
                            float* gates, int32_t* offsets, int32_t* sorted_rows, void*,
                            hipStream_t stream) {
+  if (T <= kRouteFusedMaxTokens) {
+    if (E <= 128)
+      route_fused_kernel<8><<<1, 1024, 0, stream>>>(logits, T, E, k, topk_ids, gates, offsets,
+                                                    sorted_rows);
+    else
+      route_fused_kernel<16><<<1, 1024, 0, stream>>>(logits, T, E, k, topk_ids, gates, offsets,
+                                                     sorted_rows);
+    DG_LAUNCH_CHECK();
+    return DG_OK;
+  }
   if (E <= 128)
     route_topk_kernel<8><<<(T + 3) / 4, 64, 0, stream>>>(logits, T, E, k, topk_ids, gates);
   else

@@ -32,8 +32,12 @@ def _check_route(logits, k):
     return ids, gates, off, rows
 
 
+# up to 64 tokens the top-k and the sort run in one workgroup
+# (route_fused_kernel), above that in two launches: both sides of the bound,
+# one token (AR decode) and E > 128 on both paths
 @pytest.mark.parametrize("T,E,k", [(256, 128, 8), (1024, 128, 8), (37, 5, 2), (300, 256, 16),
-                                   (64, 1, 1), (10, 200, 3), (130, 128, 8)])
+                                   (64, 1, 1), (10, 200, 3), (130, 128, 8), (64, 128, 8),
+                                   (65, 128, 8), (1, 128, 8), (64, 256, 16), (2, 3, 3)])
 def test_route_matches_oracle(T, E, k):
     rng = np.random.default_rng(T + E + k)
     logits = torch.from_numpy(rng.standard_normal((T, E)).astype(np.float32))
