@@ -93,8 +93,8 @@ __global__ void advance_prefix_kernel(int32_t* prefix_len, int B, int L) {
 constexpr int kAttnRows = 128;        // packed rows per workgroup (4 row groups of 32)
 constexpr int kAttnKeys = 128;        // keys per LDS tile (2 halves of 64)
 constexpr int kDh = 128;
-constexpr int kKStride = kDh + 8;     // K tile row stride (elements): 272 B
-constexpr int kVStride = kAttnKeys + 8;   // V^T tile row stride: 272 B
+constexpr int kKStride = kDh + 16;    // K tile row stride (elements): 288 B
+constexpr int kVStride = kAttnKeys + 16;  // V^T tile row stride: 288 B
 constexpr int kKTileElems = kAttnKeys * kKStride;
 constexpr int kVTileElems = kDh * kVStride;
 // A row's running maximum is raised only when a tile's maximum exceeds it by

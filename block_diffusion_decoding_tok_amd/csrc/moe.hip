@@ -99,29 +99,34 @@ __global__ __launch_bounds__(64) void route_topk_kernel(const float* __restrict_
 
 // Stable counting sort of the n = T * k slot entries by expert, by one
 // 1024-thread workgroup.  Wave w owns the contiguous range of entries
-// [w R, (w + 1) R), R = ceil(n / 16), and walks it in chunks of 64 twice:
-// first counting its entries per expert, then -- after the counts are turned
-// into each (wave, expert)'s first output position (experts ascending, waves
-// ascending within an expert) -- placing every entry at that position plus
-// its rank among the same expert's entries of the chunk (ballot-based).  Waves
-// own ascending ranges and walk them in order, so equal experts keep the
-// entry order t * k + j: the result is unique (deterministic).  Three barriers
-// in all (the previous form took five per chunk of 1024 entries).
+// [w R, (w + 1) R), R = ceil(n / 16): it first counts its entries per expert
+// (LDS atomic adds: the counts do not depend on the order), then -- after
+// the counts are turned into each (wave, expert)'s first output position
+// (experts ascending, waves ascending within an expert) -- walks its range
+// in chunks of 64 and places every entry at that position plus its rank
+// among the same expert's entries of the chunk (ballot-based).  Waves own
+// ascending ranges and walk them in order, so equal experts keep the entry
+// order t * k + j: the result is unique (deterministic).  The ballot match
+// is the costly part (it runs on one CU), so it runs in the placement pass
+// only, over the BITS bits that hold an id below E.
 struct SortSmem {
   int cnt[16][256];       // per wave: entries per expert, then the running position
 };
 
-// Lanes of this wave whose expert equals mine (empty for an inactive lane).
+// Lanes of this wave whose expert equals mine (empty for an inactive lane);
+// e < 2^BITS.
+template <int BITS>
 __device__ __forceinline__ uint64_t same_expert_lanes(int e, bool active) {
   uint64_t same = __ballot(active);
 #pragma unroll
-  for (int bit = 0; bit < 8; ++bit) {
+  for (int bit = 0; bit < BITS; ++bit) {
     const uint64_t bal = __ballot(active && ((e >> bit) & 1));
     same &= ((e >> bit) & 1) ? bal : ~bal;
   }
   return active ? same : 0ull;
 }
 
+template <int BITS>
 __device__ void sort_slots(const int* ids, int n, int E, int32_t* __restrict__ offsets,
                            int32_t* __restrict__ sorted_rows, SortSmem& sm) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -130,16 +135,10 @@ __device__ void sort_slots(const int* ids, int n, int E, int32_t* __restrict__ o
   const int R = (n + 15) / 16;
   const int r0 = wave * R, r1 = min(n, r0 + R);
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  // pass 1: per-wave counts (one leader lane per distinct expert of a chunk)
+  // pass 1: per-wave counts
   // (ids are clamped to [0, E): an id out of range can only misplace entries,
   // never address memory outside the tables)
-  for (int c0 = r0; c0 < r1; c0 += 64) {
-    const int i = c0 + lane;
-    const bool act = i < r1;
-    const int e = act ? min(max(ids[i], 0), E - 1) : 0;
-    const uint64_t same = same_expert_lanes(e, act);
-    if (act && __popcll(same & below) == 0) sm.cnt[wave][e] += __popcll(same);
-  }
+  for (int i = r0 + lane; i < r1; i += 64) atomicAdd(&sm.cnt[wave][min(max(ids[i], 0), E - 1)], 1);
   __syncthreads();
   // positions: thread e < E turns its column into exclusive prefixes over the
   // waves; wave 0 then scans the experts' totals (4 per lane)
@@ -186,7 +185,7 @@ __device__ void sort_slots(const int* ids, int n, int E, int32_t* __restrict__ o
     const int i = c0 + lane;
     const bool act = i < r1;
     const int e = act ? min(max(ids[i], 0), E - 1) : 0;
-    const uint64_t same = same_expert_lanes(e, act);
+    const uint64_t same = same_expert_lanes<BITS>(e, act);
     const int rank = __popcll(same & below);
     const int pos = act ? s_off[e] + sm.cnt[wave][e] + rank : 0;
     if (act && pos < n) sorted_rows[pos] = i;
@@ -194,11 +193,37 @@ __device__ void sort_slots(const int* ids, int n, int E, int32_t* __restrict__ o
   }
 }
 
+// Up to kSortStage entries the ids are first copied into LDS, every thread
+// issuing all its loads at once: the two passes then read LDS instead of
+// paying a global-load latency per 64-entry chunk (15.7 -> 4 us at 8192
+// entries).
+constexpr int kSortStage = 16384;
+constexpr int kSortStagePerThread = kSortStage / 1024;
+
 __global__ __launch_bounds__(1024) void route_sort_kernel(const int32_t* __restrict__ ids, int n,
                                                           int E, int32_t* __restrict__ offsets,
                                                           int32_t* __restrict__ sorted_rows) {
   __shared__ SortSmem sm;
-  sort_slots(ids, n, E, offsets, sorted_rows, sm);
+  if (n <= kSortStage) {
+    __shared__ int s_ids[kSortStage];
+    const int tid = threadIdx.x;
+    int v[kSortStagePerThread];
+#pragma unroll
+    for (int j = 0; j < kSortStagePerThread; ++j) v[j] = ids[min(tid + j * 1024, n - 1)];
+#pragma unroll
+    for (int j = 0; j < kSortStagePerThread; ++j)
+      if (tid + j * 1024 < n) s_ids[tid + j * 1024] = v[j];
+    __syncthreads();
+    if (E <= 128)
+      sort_slots<7>(s_ids, n, E, offsets, sorted_rows, sm);
+    else
+      sort_slots<8>(s_ids, n, E, offsets, sorted_rows, sm);
+  } else {
+    if (E <= 128)
+      sort_slots<7>(ids, n, E, offsets, sorted_rows, sm);
+    else
+      sort_slots<8>(ids, n, E, offsets, sorted_rows, sm);
+  }
 }
 
 // The top-k and the sort in one 1024-thread workgroup, for up to
@@ -232,7 +257,10 @@ __global__ __launch_bounds__(1024) void route_fused_kernel(const float* __restri
     }
   }
   __syncthreads();
-  sort_slots(s_ids, T * k, E, offsets, sorted_rows, sm);
+  if (E <= 128)
+    sort_slots<7>(s_ids, T * k, E, offsets, sorted_rows, sm);
+  else
+    sort_slots<8>(s_ids, T * k, E, offsets, sorted_rows, sm);
 }
 
 size_t moe_route_workspace_bytes(int, int, int) { return 0; }
