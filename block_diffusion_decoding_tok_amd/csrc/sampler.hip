@@ -12,7 +12,8 @@
 // vocabulary slice of one position.  Each thread keeps its slice (up to 8
 // groups of 8 logits, 16-byte loads, coalesced across the workgroup) in
 // registers and walks it three times: max; exp-sum and entropy accumulator
-// relative to its own max (float terms, double accumulation); Gumbel-max.
+// relative to its own max (float terms, double accumulation); Gumbel-max
+// (skipped for a committed position, whose token stays).
 // The workgroup merges the per-thread statistics (online-softmax rescaling in
 // double) and writes one 32-byte partial.  HBM traffic: the logits once.
 //
@@ -67,9 +68,13 @@ template <typename T>
 __global__ __launch_bounds__(kSampThreads) void sampler_partial_kernel(
     const T* __restrict__ logits, int L, int V, int slice, int nsplit, float invT,
     uint32_t k0, uint32_t k1, int step, const int32_t* __restrict__ prefix_len,
-    const int32_t* __restrict__ done, SamplerPartial* __restrict__ part) {
+    const int32_t* __restrict__ done, const uint8_t* __restrict__ committed,
+    SamplerPartial* __restrict__ part) {
   const int split = blockIdx.x, i = blockIdx.y, b = blockIdx.z;
   if (done[b]) return;
+  // a committed position keeps its token: only its maxprob and entropy are
+  // needed, so its slices skip the Gumbel draws (workgroup-uniform)
+  const bool want_sample = !committed[static_cast<size_t>(b) * L + i];
   const int tid = threadIdx.x;
   const int v_begin = split * slice;
   const int v_end = min(V, v_begin + slice);
@@ -90,6 +95,14 @@ __global__ __launch_bounds__(kSampThreads) void sampler_partial_kernel(
   float lmax = -INFINITY;
   float best = -INFINITY;
   int best_v = 0x7fffffff;
+  if (!want_sample) {
+#pragma unroll
+    for (int g = 0; g < kSampGroups; ++g) {
+      if (!valid[g]) continue;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) lmax = fmaxf(lmax, vals[g].get(j));
+    }
+  } else {
 #pragma unroll
   for (int g = 0; g < kSampGroups; ++g) {
     if (!valid[g]) continue;
@@ -107,6 +120,7 @@ __global__ __launch_bounds__(kSampThreads) void sampler_partial_kernel(
         if (sc > best) { best = sc; best_v = v0 + 4 * h + q; }
       }
     }
+  }
   }
 
   // pass 2: Z and A relative to the thread's own max, in units of log2
@@ -387,11 +401,11 @@ dg_status launch_sampler(const void* logits, int logit_dtype, int B, int L, int 
   if (logit_dtype == DG_BF16)
     sampler_partial_kernel<bf16_t><<<grid, kSampThreads, 0, stream>>>(
         static_cast<const bf16_t*>(logits), L, V, slice, nsplit, invT, k0, k1, step, prefix_len,
-        done, part);
+        done, committed, part);
   else
     sampler_partial_kernel<float><<<grid, kSampThreads, 0, stream>>>(
         static_cast<const float*>(logits), L, V, slice, nsplit, invT, k0, k1, step, prefix_len,
-        done, part);
+        done, committed, part);
   DG_LAUNCH_CHECK();
   const int adaptive = cfg.fixed_steps > 0 ? 0 : 1;
   const int ends_at = cfg.fixed_steps > 0 ? cfg.fixed_steps - 1 : S - 1;
