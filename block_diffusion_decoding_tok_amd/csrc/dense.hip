@@ -334,9 +334,10 @@ bool qkv_rope_supported(const QkvRope& r, int K) {
   const int M = r.B * r.Lq;
   const int N = (r.Hq + 2 * r.Hkv) * r.dh;
   // the wide split-K tiles: 16 kProjRT = 128 rows = one head of 128 (tiled
-  // activations: 64-row tiles, half a head's rotated pairs each)
-  return r.dh == 128 && kProjRT == 8 && kXtRT == 4 && M > 16 && N >= 1024 && K % 64 == 0 &&
-         K >= 64 * 8 && r.Hq % r.Hkv == 0;
+  // activations: 64-row tiles, half a head's rotated pairs each); a handful
+  // of tokens (AR decode): 32-row tiles, a quarter of a head's pairs each
+  return r.dh == 128 && kProjRT == 8 && kXtRT == 4 && M >= 1 && N >= 1024 && K % 64 == 0 &&
+         K >= 64 * 8 && r.Hq % r.Hkv == 0 && (M > 16 || !r.x_tiled);
 }
 
 bool dense_xt_supported(int M, int N, int K) {
@@ -367,6 +368,20 @@ dg_status launch_qkv_rope(const void* A, const void* W, int K, int w_layout, con
   g.gate = gate.n_done;
   g.gate_n = gate.n;
   if (r.x_tiled && M >= kDl128MinTokens) return launch_dl128(g, M, N, stream);
+  if (M <= 16) {
+    // the narrow split-K tiles of a handful of tokens (32 weight rows, eight
+    // waves over K), RoPE in their epilogue instead of a separate kernel
+    g.n_tiles_x = N / 32;
+    g.n_tiles_y = 1;
+    g.n_tiles_total = g.n_tiles_x;
+    const unsigned grid = (g.n_tiles_total + 7) / 8 * 8;
+    if (w_layout == DG_LAYOUT_TILED)
+      gemm_splitk_kernel<2, 1, kSplitNR, 8, true><<<grid, 512, 0, stream>>>(g);
+    else
+      gemm_splitk_kernel<2, 1, kSplitNR, 8, false><<<grid, 512, 0, stream>>>(g);
+    DG_LAUNCH_CHECK();
+    return DG_OK;
+  }
   const int rt = r.x_tiled ? kXtRT : kProjRT, tb = r.x_tiled ? kXtTB : kProjTB;
   g.n_tiles_x = N / (16 * rt);
   g.n_tiles_y = (M + 16 * tb - 1) / (16 * tb);

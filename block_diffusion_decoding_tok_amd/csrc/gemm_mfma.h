@@ -843,7 +843,7 @@ __global__ __launch_bounds__(64 * NW, WPE) void gemm_splitk_kernel(GemmArgs a) {
   const int l16 = lane & 15, g4 = lane >> 4;
   const int logical = xcd_logical_tile(blockIdx.x, gridDim.x);
   if (logical >= a.n_tiles_total || step_gate_closed(a.gate, a.gate_n)) return;
-  constexpr bool kRopeTile = RT == 8 || RT == 4;
+  constexpr bool kRopeTile = RT == 8 || RT == 4 || RT == 2;
   const int tx = logical / a.n_tiles_y;       // row tile (token tiles adjacent)
   const int ty = logical % a.n_tiles_y;
   const int m0 = ty * 16 * TB;
@@ -852,10 +852,12 @@ __global__ __launch_bounds__(64 * NW, WPE) void gemm_splitk_kernel(GemmArgs a) {
   const int c_begin = wave * nch_all / NW;
   const int nchunks = (wave + 1) * nch_all / NW - c_begin;   // >= 1 when K >= 64 * NW
   // 16-row tile of the weights behind accumulator row tile rt: consecutive,
-  // except 64-row RoPE tiles, which take row tiles {0, 1, 4, 5} or {2, 3, 6, 7}
-  // of head tx / 2 so that both rows of every rotated pair are here
+  // except RoPE tiles of 64 rows, which take row tiles {0, 1, 4, 5} or
+  // {2, 3, 6, 7} of head tx / 2, and of 32 rows, row tiles {j, j + 4} of head
+  // tx / 4 (j = tx % 4), so that both rows of every rotated pair are here
   auto row16 = [&](int rt) {
     if (RT == 4 && a.rope) return (tx >> 1) * 8 + (tx & 1) * 2 + (rt & 1) + (rt >> 1) * 4;
+    if (RT == 2 && a.rope) return (tx >> 2) * 8 + (tx & 3) + rt * 4;
     return n0 / 16 + rt;
   };
 

@@ -82,8 +82,9 @@ def test_full_width_ar_teacher_forced():
     """2 full-width layers (D 2816, fp8 experts, V 4096), tile-packed weights,
     batch 2 over a 256-token prompt: 4 single steps, each fed the oracle's
     previous token.  The device's greedy token must be a maximal logit of the
-    oracle's to within the bf16 error of the logits; the K/V slot each step
-    writes must match."""
+    oracle's to within the bf16 error of the logits; the K and V slots each
+    step writes (the QKV projection's RoPE epilogue at one token per row)
+    must match."""
     d = ModelDims(NL=2, D=2816, Hq=16, Hkv=8, dh=128, E=128, k=8, I=704, V=4096)
     w = model_weights(d, seed=5, expert_dtype="fp8", dense_dtype="bf16")
     m = oracle_model(d, w)
@@ -115,5 +116,7 @@ def test_full_width_ar_teacher_forced():
         assert Pd.cpu().tolist() == list(P + 1)
         for l in range(d.NL):
             slot_k = kc[l].cpu().double().numpy()[:, :, P[0]]
+            slot_v = vc[l].cpu().double().numpy()[:, :, P[0]]
             assert rel_err_rows(slot_k, okc[l][:, :, P[0]]) < 3e-2
+            assert rel_err_rows(slot_v, ovc[l][:, :, P[0]]) < 3e-2
         tok = np.argmax(logits, axis=1)                    # teacher forcing
