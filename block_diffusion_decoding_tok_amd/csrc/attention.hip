@@ -430,6 +430,200 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(
 constexpr size_t kAttnSmemBytes = (2 * kKTileElems + 2 * kVTileElems) * sizeof(bf16_t);
 static_assert(4 * (32 * (kDh + 4) + 64) * sizeof(float) <= kAttnSmemBytes, "merge scratch fits");
 
+// ------------------------------------------------ few query rows (AR decode)
+// Up to kDecRows packed rows per KV head (one token: the G heads of a group):
+// the 128-row tiles above would be almost all padding, and their key tiles
+// pass through LDS one after another.  Here a 512-thread workgroup owns an
+// even share (a multiple of 64 keys) of one (b, kv head)'s keys; per chunk
+// of kDecKeys each of its eight waves takes 64 keys and issues all of their
+// K and V loads at once (pinned ahead of the arithmetic):
+//   S^T = K Q^T on v_mfma_f32_16x16x32_bf16, the K rows straight from memory
+//   as the A operand (lane (l16, g4): key l16 of a 16-key block, dh
+//   32 c + 8 g4 .. + 7), q padded to 16 rows as B; lane (l16, g4) then holds
+//   the scores of keys 16 kb + 4 g4 + r of row l16;
+//   online softmax per row (maximum over the lane's 16 scores, then over the
+//   four g4 lanes by lane swaps; the row's rescale factor broadcast from its
+//   lane);
+//   P V on the VALU: lane (l16, g4) accumulates dh 8 l16 .. + 7 of every row
+//   over the keys 4 i + g4 (i = 0..15), the probabilities read from LDS;
+// at the end the four g4 partial sums are added by lane swaps, the eight
+// waves merge through LDS (online-softmax rescale) and the workgroup writes
+// the split's partial in the layout attn_combine_kernel reads.
+constexpr int kDecWaves = 8;
+constexpr int kDecKeys = 64 * kDecWaves;   // keys per chunk (64 per wave)
+constexpr int kDecRows = 4;
+constexpr int kDecTargetWgs = 256;         // workgroups per launch (one per CU)
+
+__device__ __forceinline__ float sum_over_g4(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto h = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const float a = __uint_as_float(h[0]) + __uint_as_float(h[1]);
+  const unsigned ua = __float_as_uint(a);
+  const auto r = __builtin_amdgcn_permlane16_swap(ua, ua, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <int RP>   // rows computed (>= the real row count R)
+__global__ __launch_bounds__(64 * kDecWaves) void attn_decode_kernel(
+    const bf16_t* __restrict__ qrot, const bf16_t* __restrict__ k_cache,
+    const bf16_t* __restrict__ v_cache, const int32_t* __restrict__ prefix_len, int Lq, int G,
+    int Hkv, int Tmax, int nsplit, int BH, int mask_blk, float* __restrict__ o_part,
+    AttnPartialML* __restrict__ ml_part, const int32_t* gate, int gate_n,
+    const int32_t* __restrict__ row_done) {
+  static_assert(RP <= kDecRows, "rows");
+  const int split = blockIdx.x % nsplit, bh = blockIdx.x / nsplit;
+  if (bh >= BH) return;
+  const int b = bh / Hkv;
+  if (step_gate_closed(gate, gate_n) || (row_done && row_done[b])) return;
+  const int R = Lq * G;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const int P = prefix_len[b];
+  const int n_keys = min(P + Lq, Tmax);
+  // keys any row of this head sees (block-causal: up to the last token's
+  // block), dealt out evenly in whole chunks (P is read on the device, so a
+  // captured graph replayed at a larger prefix still balances its splits)
+  const int k_all = mask_blk ? min(n_keys, P + attn_block_end(Lq - 1, mask_blk, Lq)) : n_keys;
+  const int share = ((k_all + nsplit - 1) / nsplit + 63) / 64 * 64;
+  const int k_begin = split * share;
+  const int k_end = min(k_all, k_begin + share);
+  // this lane's row (rows past R repeat row R - 1's limit; they are not written)
+  const int key_lim_row =
+      mask_blk ? min(k_end, P + attn_block_end(min(l16, R - 1) / G, mask_blk, Lq)) : k_end;
+
+  const bf16_t* kbase = k_cache + static_cast<int64_t>(bh) * Tmax * kDh;
+  const bf16_t* vbase = v_cache + static_cast<int64_t>(bh) * Tmax * kDh;
+  const bf16_t* qbase = qrot + static_cast<int64_t>(bh) * R * kDh;
+  bf16x8_t qf[4];
+  const int qrow = l16 < R ? l16 : 0;
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    qf[c] = *reinterpret_cast<const bf16x8_t*>(qbase + static_cast<int64_t>(qrow) * kDh + c * 32 + g4 * 8);
+  if (l16 >= R) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) qf[c] = bf16x8_t{};
+  }
+
+  __shared__ float s_p[kDecWaves][64][RP];
+  float m_run = -INFINITY;   // row l16's exponent base (log2 domain)
+  float l_run = 0.f;         // this lane's share of row l16's sum
+  float o[RP][8];
+#pragma unroll
+  for (int j = 0; j < RP; ++j)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[j][e] = 0.f;
+
+  for (int kc = k_begin; kc < k_end; kc += kDecKeys) {
+    const int k0 = kc + wave * 64;
+    const int kw_end = min(k_end, k0 + 64);            // this wave's keys [k0, kw_end)
+    const int k_last = max(min(kw_end, Tmax) - 1, 0);  // loads past it are clamped to it
+    bf16x8_t kf[4][4];
+    uint4 vr[16];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const int key = min(k0 + kb * 16 + l16, k_last);
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        kf[kb][c] = *reinterpret_cast<const bf16x8_t*>(kbase + static_cast<int64_t>(key) * kDh + c * 32 + g4 * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int key = min(k0 + 4 * i + g4, k_last);
+      vr[i] = *reinterpret_cast<const uint4*>(vbase + static_cast<int64_t>(key) * kDh + l16 * 8);
+    }
+    __builtin_amdgcn_sched_barrier(0);   // every load of the chunk issued first
+    // scores (log2 domain: q carries log2(e) / sqrt(dh))
+    f32x4_t sc[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      sc[kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        sc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb][c], qf[c], sc[kb], 0, 0, 0);
+    }
+    const int key_lim = min(kw_end, key_lim_row);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (k0 + kb * 16 + 4 * g4 + r >= key_lim) sc[kb][r] = -INFINITY;
+        mx = fmax2(mx, sc[kb][r]);
+      }
+    mx = max_over_g4(mx);
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    const float base = (m_new == -INFINITY) ? 0.f : m_new;
+    l_run *= alpha;
+#pragma unroll
+    for (int j = 0; j < RP; ++j) {
+      // row j's factor, from a lane that holds row j
+      const float aj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), j));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[j][e] *= aj;
+    }
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float pv = __builtin_amdgcn_exp2f(sc[kb][r] - base);
+        l_run += pv;
+        if (l16 < RP) s_p[wave][kb * 16 + 4 * g4 + r][l16] = pv;
+      }
+    // (one wave's LDS writes complete before its later reads)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float vf[8];
+      const uint32_t w[4] = {vr[i].x, vr[i].y, vr[i].z, vr[i].w};
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        vf[2 * h] = __uint_as_float(w[h] << 16);
+        vf[2 * h + 1] = __uint_as_float(w[h] & 0xffff0000u);
+      }
+#pragma unroll
+      for (int j = 0; j < RP; ++j) {
+        const float pj = s_p[wave][4 * i + g4][j];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[j][e] = __builtin_fmaf(pj, vf[e], o[j][e]);
+      }
+    }
+  }
+  l_run = sum_over_g4(l_run);
+#pragma unroll
+  for (int j = 0; j < RP; ++j)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[j][e] = sum_over_g4(o[j][e]);
+
+  // merge the waves: row j's base and sum sit in lanes l16 = j
+  __shared__ float s_m[kDecWaves][RP], s_l[kDecWaves][RP];
+  __shared__ float s_o[kDecWaves][RP][kDh];
+  if (g4 == 0) {
+    if (l16 < RP) { s_m[wave][l16] = m_run; s_l[wave][l16] = l_run; }
+#pragma unroll
+    for (int j = 0; j < RP; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s_o[wave][j][l16 * 8 + e] = o[j][e];
+  }
+  __syncthreads();
+  for (int q = tid; q < R * kDh; q += 64 * kDecWaves) {
+    const int j = q / kDh, d = q % kDh;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w2 = 0; w2 < kDecWaves; ++w2) M = fmaxf(M, s_m[w2][j]);
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int w2 = 0; w2 < kDecWaves; ++w2) {
+      const float f = s_m[w2][j] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s_m[w2][j] - M);
+      L += s_l[w2][j] * f;
+      O += s_o[w2][j][d] * f;
+    }
+    const int64_t prow = (static_cast<int64_t>(split) * BH + bh) * R + j;
+    o_part[prow * kDh + d] = O;
+    if (d == 0) ml_part[prow] = AttnPartialML{M, L};
+  }
+}
+
 // Merge the KV splits of every packed row and write out [B, Lq, Hq, dh]
 // (row-major, or with tiled the tiled activation layout of [B Lq, Hq dh]):
 // 32 threads per row (4 dh each, 16-byte loads), 8 rows per workgroup.
@@ -495,6 +689,78 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
   Elem<T>::store(dst, 3, acc.w / L);
 }
 
+// The same merge for the decode kernel's few rows: one workgroup per packed
+// row, its eight groups of 32 threads (4 dh each) take the splits g, g + 8,
+// ... (loads issued together, online rescale), then the groups merge through
+// LDS.  (With 32 threads per row the whole merge of one token ran on two
+// workgroups, one split after another.)
+template <typename T>
+__global__ __launch_bounds__(256) void attn_combine_few_kernel(
+    const float* __restrict__ o_part, const AttnPartialML* __restrict__ ml_part, int nsplit,
+    int BH, int rows_total, int G, int Hkv, int Lq, int tiled, T* __restrict__ out,
+    const int32_t* gate, int gate_n, const int32_t* __restrict__ row_done) {
+  const int gr = blockIdx.x;                        // packed row (bh, r)
+  if (gr >= BH * rows_total || step_gate_closed(gate, gate_n)) return;
+  const int bh = gr / rows_total, r = gr % rows_total;
+  if (row_done && row_done[bh / Hkv]) return;
+  const int grp = threadIdx.x >> 5, d4 = (threadIdx.x & 31) * 4;
+  const int64_t rstride = static_cast<int64_t>(BH) * rows_total;
+  const int64_t r0 = static_cast<int64_t>(bh) * rows_total + r;
+  float M = -INFINITY, L = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s0 = grp; s0 < nsplit; s0 += 32) {
+    AttnPartialML ml[4];
+    float4 o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t prow = min(s0 + 8 * j, nsplit - 1) * rstride + r0;
+      ml[j] = ml_part[prow];
+      o[j] = *reinterpret_cast<const float4*>(o_part + prow * kDh + d4);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (s0 + 8 * j >= nsplit || ml[j].l == 0.f) continue;
+      const float mb = fmaxf(M, ml[j].m);
+      const float f0 = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(M - mb);
+      const float f1 = __builtin_amdgcn_exp2f(ml[j].m - mb);
+      L = L * f0 + ml[j].l * f1;
+      acc.x = acc.x * f0 + o[j].x * f1;
+      acc.y = acc.y * f0 + o[j].y * f1;
+      acc.z = acc.z * f0 + o[j].z * f1;
+      acc.w = acc.w * f0 + o[j].w * f1;
+      M = mb;
+    }
+  }
+  __shared__ float s_m[8], s_l[8];
+  __shared__ float4 s_acc[8][32];
+  if ((threadIdx.x & 31) == 0) { s_m[grp] = M; s_l[grp] = L; }
+  s_acc[grp][threadIdx.x & 31] = acc;
+  __syncthreads();
+  if (grp != 0) return;
+  float Mt = -INFINITY;
+#pragma unroll
+  for (int g2 = 0; g2 < 8; ++g2) Mt = fmaxf(Mt, s_m[g2]);
+  float Lt = 0.f;
+  float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int g2 = 0; g2 < 8; ++g2) {
+    if (s_l[g2] == 0.f) continue;
+    const float f = __builtin_amdgcn_exp2f(s_m[g2] - Mt);
+    const float4 v = s_acc[g2][threadIdx.x & 31];
+    Lt += s_l[g2] * f;
+    a.x += v.x * f; a.y += v.y * f; a.z += v.z * f; a.w += v.w * f;
+  }
+  const int b = bh / Hkv, g = bh % Hkv;
+  const int tok = r / G, h = g * G + r % G;
+  const int Hq = Hkv * G;
+  const int64_t m = static_cast<int64_t>(b) * Lq + tok;
+  T* dst = tiled ? out + xtile_offset(m, h * kDh + d4, Hq * kDh) : out + (m * Hq + h) * kDh + d4;
+  Elem<T>::store(dst, 0, a.x / Lt);
+  Elem<T>::store(dst, 1, a.y / Lt);
+  Elem<T>::store(dst, 2, a.z / Lt);
+  Elem<T>::store(dst, 3, a.w / Lt);
+}
+
 // ------------------------------------------------------------- f32 path
 // One wave per (packed row, b * Hkv): lane j owns dh elements j and j + 64.
 __global__ void attn_f32_kernel(const float* __restrict__ qrot, const float* __restrict__ k_cache,
@@ -545,6 +811,7 @@ static int attn_mask_blk(const AttnArgs& a) {
 
 struct AttnPlan {
   int tiles, nsplit, chunk;
+  bool decode;          // attn_decode_kernel (rows <= kDecRows)
   size_t q_bytes, o_bytes, ml_bytes;
 };
 
@@ -554,7 +821,16 @@ static AttnPlan plan_attention(int B, int Lq, int Hq, int Hkv, int dh, int Tmax,
   const int rows = Lq * G;
   const size_t esz = dtype == DG_BF16 ? 2 : 4;
   p.q_bytes = align_up(static_cast<size_t>(B) * Hkv * rows * dh * esz, 256);
-  if (dtype == DG_BF16) {
+  if (dtype == DG_BF16 && rows <= kDecRows && dh == kDh) {
+    p.decode = true;
+    p.tiles = 1;
+    p.chunk = kDecKeys;
+    // a fixed number of splits (the workspace does not grow with the cache),
+    // each an even share of the row's keys
+    p.nsplit = max(1, min((kDecTargetWgs + B * Hkv - 1) / (B * Hkv), (Tmax + 63) / 64));
+    p.o_bytes = align_up(static_cast<size_t>(p.nsplit) * B * Hkv * rows * dh * 4, 256);
+    p.ml_bytes = align_up(static_cast<size_t>(p.nsplit) * B * Hkv * rows * sizeof(AttnPartialML), 256);
+  } else if (dtype == DG_BF16) {
     p.tiles = (rows + kAttnRows - 1) / kAttnRows;
     const int base = p.tiles * B * Hkv;
     // one workgroup per CU (its LDS): more splits than that only add rounds
@@ -594,19 +870,40 @@ dg_status launch_attention(const AttnArgs& a, void* ws, hipStream_t stream) {
     }
     float* o_part = reinterpret_cast<float*>(w + p.q_bytes);
     AttnPartialML* ml = reinterpret_cast<AttnPartialML*>(w + p.q_bytes + p.o_bytes);
-    const int total = p.tiles * p.nsplit * a.B * a.Hkv;
-    dg_status lst = ensure_lds_limit(reinterpret_cast<const void*>(attn_mfma_kernel),
-                                     static_cast<int>(kAttnSmemBytes));
-    if (lst != DG_OK) return lst;
-    attn_mfma_kernel<<<(total + 7) / 8 * 8, 512, kAttnSmemBytes, stream>>>(
-        static_cast<const bf16_t*>(qrot), static_cast<const bf16_t*>(a.k_cache),
-        static_cast<const bf16_t*>(a.v_cache), a.prefix_len, a.Lq, G, a.Hkv, a.Tmax, p.chunk,
-        p.tiles, p.nsplit, a.B * a.Hkv, attn_mask_blk(a), o_part, ml,
-        a.gate.n_done, a.gate.n, a.gate.row_done);
+    if (p.decode) {
+      const unsigned grid = static_cast<unsigned>(p.nsplit) * a.B * a.Hkv;
+      if (rows <= 2)
+        attn_decode_kernel<2><<<grid, 64 * kDecWaves, 0, stream>>>(
+            static_cast<const bf16_t*>(qrot), static_cast<const bf16_t*>(a.k_cache),
+            static_cast<const bf16_t*>(a.v_cache), a.prefix_len, a.Lq, G, a.Hkv, a.Tmax,
+            p.nsplit, a.B * a.Hkv, attn_mask_blk(a), o_part, ml, a.gate.n_done, a.gate.n,
+            a.gate.row_done);
+      else
+        attn_decode_kernel<4><<<grid, 64 * kDecWaves, 0, stream>>>(
+            static_cast<const bf16_t*>(qrot), static_cast<const bf16_t*>(a.k_cache),
+            static_cast<const bf16_t*>(a.v_cache), a.prefix_len, a.Lq, G, a.Hkv, a.Tmax,
+            p.nsplit, a.B * a.Hkv, attn_mask_blk(a), o_part, ml, a.gate.n_done, a.gate.n,
+            a.gate.row_done);
+    } else {
+      const int total = p.tiles * p.nsplit * a.B * a.Hkv;
+      dg_status lst = ensure_lds_limit(reinterpret_cast<const void*>(attn_mfma_kernel),
+                                       static_cast<int>(kAttnSmemBytes));
+      if (lst != DG_OK) return lst;
+      attn_mfma_kernel<<<(total + 7) / 8 * 8, 512, kAttnSmemBytes, stream>>>(
+          static_cast<const bf16_t*>(qrot), static_cast<const bf16_t*>(a.k_cache),
+          static_cast<const bf16_t*>(a.v_cache), a.prefix_len, a.Lq, G, a.Hkv, a.Tmax, p.chunk,
+          p.tiles, p.nsplit, a.B * a.Hkv, attn_mask_blk(a), o_part, ml,
+          a.gate.n_done, a.gate.n, a.gate.row_done);
+    }
     DG_LAUNCH_CHECK();
-    attn_combine_kernel<bf16_t><<<(a.B * a.Hkv * rows + 7) / 8, 256, 0, stream>>>(
-        o_part, ml, p.nsplit, a.B * a.Hkv, rows, G, a.Hkv, a.Lq, a.out_tiled,
-        static_cast<bf16_t*>(a.out), a.gate.n_done, a.gate.n, a.gate.row_done);
+    if (p.decode)
+      attn_combine_few_kernel<bf16_t><<<a.B * a.Hkv * rows, 256, 0, stream>>>(
+          o_part, ml, p.nsplit, a.B * a.Hkv, rows, G, a.Hkv, a.Lq, a.out_tiled,
+          static_cast<bf16_t*>(a.out), a.gate.n_done, a.gate.n, a.gate.row_done);
+    else
+      attn_combine_kernel<bf16_t><<<(a.B * a.Hkv * rows + 7) / 8, 256, 0, stream>>>(
+          o_part, ml, p.nsplit, a.B * a.Hkv, rows, G, a.Hkv, a.Lq, a.out_tiled,
+          static_cast<bf16_t*>(a.out), a.gate.n_done, a.gate.n, a.gate.row_done);
     DG_LAUNCH_CHECK();
   } else {
     rope_kernel<float><<<a.B * a.Lq, rope_threads(a.dh), 0, stream>>>(

@@ -76,14 +76,32 @@ def test_canvas_attention_bf16_spare_cache():
     _check(case, [1500, 3000], 8192, CANVAS, torch.bfloat16)
 
 
-@pytest.mark.parametrize("Lq", [1, 5, 16])
+@pytest.mark.parametrize("Lq", [1, 2, 5, 16])
 @pytest.mark.parametrize("mode", [CANVAS, CAUSAL])
 def test_attention_bf16_few_queries(Lq, mode):
-    """A few query tokens per row (AR decode): one row tile per KV head and
-    the cache split over many workgroups, most of them empty past the short
-    row's keys; rows with 8000 and 333 cached keys in 8448 slots."""
+    """A few query tokens per row (AR decode): up to 4 packed rows per KV head
+    take the decode kernel (Lq 1 and 2 here), more take one row tile of the
+    MFMA kernel; the cache is split over many workgroups, most of them empty
+    past the short row's keys; rows with 8000 and 333 cached keys in 8448
+    slots."""
     case = attention_case(B=2, Lq=Lq, P=8000, seed=40 + Lq)
     _check(case, [8000, 333], 8448, mode, torch.bfloat16)
+
+
+@pytest.mark.parametrize("Hq,Hkv,Lq", [(8, 8, 1), (8, 8, 3), (16, 4, 1), (16, 8, 2)])
+@pytest.mark.parametrize("mode", [CANVAS, CAUSAL])
+def test_attention_bf16_decode_groups(Hq, Hkv, Lq, mode):
+    """The decode kernel at 1, 3 and 4 packed rows per KV head (one, three
+    and four query heads per group), ragged prefixes and an empty one."""
+    case = attention_case(B=3, Lq=Lq, P=1000, Hq=Hq, Hkv=Hkv, seed=60 + Hq + Hkv + Lq)
+    _check(case, [1000, 77, 0], 1100, mode, torch.bfloat16)
+
+
+def test_attention_bf16_decode_long_prefix():
+    """One token over 20000 cached keys: each decode workgroup walks several
+    256-key chunks with the online-softmax rescale between them."""
+    case = attention_case(B=1, Lq=1, P=20000, seed=70)
+    _check(case, [20000], 20480, CAUSAL, torch.bfloat16)
 
 
 @pytest.mark.parametrize("P", [0, 64, 300])
