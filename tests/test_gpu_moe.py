@@ -112,11 +112,13 @@ def test_moe_ffn_full_size_bs4_sampled(w_dtype, tiled):
 
 @pytest.mark.parametrize("T", [1, 3, 8])
 @pytest.mark.parametrize("tiled", [False, True])
-def test_moe_ffn_full_size_few_tokens(T, tiled):
+@pytest.mark.parametrize("w_dtype", ["fp8", "bf16"])
+def test_moe_ffn_full_size_few_tokens(T, tiled, w_dtype):
     """A few tokens (AR decode: T * k <= 64 slots): half-size work items."""
-    case = moe_case(T=T, w_dtype="fp8", seed=20 + T, skew=False)
+    case = moe_case(T=T, w_dtype=w_dtype, seed=20 + T, skew=False)
     err, _ = _ffn_case(case, 8, tiled=tiled)
-    assert err < TOL["fp8"], err
+    assert err < TOL[w_dtype], err
+
 
 
 @pytest.mark.parametrize("tiled", [False, True])
