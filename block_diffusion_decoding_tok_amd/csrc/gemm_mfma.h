@@ -651,6 +651,40 @@ __global__ __launch_bounds__(64, WPE) void gemm_wave_kernel(GemmArgs a) {
   // the expert's last token tile only
   const int grp_tiles = (a.offsets[grp + 1] - base_pos + MT - 1) / MT;
   const bool item_nt = kNtWaveW && ty - first_tile == grp_tiles - 1;
+
+  // With one chunk in flight (NR = 1), what the epilogue reads besides the
+  // accumulators is fetched before the weight stream, so that its latency is
+  // not added after the last chunk (the scale reads there each waited on the
+  // spot): the item's per-row fp8 scales (16 RT rows; gate/up: the 8 RT gate
+  // rows, then the 8 RT up rows) copied into LDS (direct-to-LDS, no
+  // registers held), and for down each token row's slot and gate (canvas
+  // step +2.8%; the deeper-ring items of a few tokens measured slower with
+  // it and read them at the end).
+  constexpr bool kEpiPrefetch = NR == 1;
+  const float* sc = a.w_scale ? a.w_scale + static_cast<int64_t>(grp) * a.s_group_stride : nullptr;
+  constexpr int kScRows = 16 * RT;
+  constexpr int kScPad = (kScRows + 63) / 64 * 64;   // whole 64-lane copies
+  __shared__ float s_sc[kEpiPrefetch ? kScPad : 1];
+  if constexpr (kEpiPrefetch) {
+    if (!sc) {
+#pragma unroll
+      for (int it = 0; it < kScPad / 64; ++it) s_sc[it * 64 + lane] = 1.f;   // unscaled weights
+    } else {
+#pragma unroll
+      for (int it = 0; it < kScPad / 64; ++it) {
+        const int q = min(it * 64 + lane, kScRows - 1);   // lanes past the rows repeat the last
+        const int row = (MODE == kGateUp) ? (q < 8 * RT ? tx * (8 * RT) + q : a.N / 2 + tx * (8 * RT) + q - 8 * RT)
+                                          : tx * (16 * RT) + q;
+        __builtin_amdgcn_global_load_lds(sc + row, s_sc + it * 64, 4, 0, 0);
+      }
+    }
+  }
+  int e_slot[TB];
+  float e_gate[TB];
+  if constexpr (MODE == kDown && kEpiPrefetch) {
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) e_slot[tb] = xok[tb] ? a.sorted_rows[p_pos[tb]] : -1;
+  }
   const uint4 zero4 = make_uint4(0, 0, 0, 0);
   f32x4_v acc[RT][TB];
 #pragma unroll
@@ -679,6 +713,12 @@ __global__ __launch_bounds__(64, WPE) void gemm_wave_kernel(GemmArgs a) {
 #pragma unroll
     for (int p = 0; p < NR; ++p) {
       issue(ring[p], p);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (MODE == kDown && kEpiPrefetch) {
+      // the gates of the item's slots, behind the first weight chunks
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb) e_gate[tb] = e_slot[tb] >= 0 ? a.gates[e_slot[tb]] : 0.f;
       __builtin_amdgcn_sched_barrier(0);
     }
     for (int c0 = 0; c0 < nchunks; c0 += NR) {
@@ -715,7 +755,9 @@ __global__ __launch_bounds__(64, WPE) void gemm_wave_kernel(GemmArgs a) {
             }
           }
         }
-        if (!kWaveIssueFirst) {
+        // (one chunk in flight: no refill past the last chunk, whose load
+        // the epilogue would otherwise wait for before reusing its registers)
+        if (!kWaveIssueFirst && (NR > 1 || c0 + p + NR < nchunks)) {
           __builtin_amdgcn_sched_barrier(0);
           issue(ring[p], c0 + p + NR);
           __builtin_amdgcn_sched_barrier(0);
@@ -729,8 +771,16 @@ __global__ __launch_bounds__(64, WPE) void gemm_wave_kernel(GemmArgs a) {
     stream_k(std::integral_constant<bool, false>{});
 
   // ---- epilogue (lane: rows 4 g4 + r of each 16-row tile, token l16 of
-  // each 16-token block)
-  const float* sc = a.w_scale ? a.w_scale + static_cast<int64_t>(grp) * a.s_group_stride : nullptr;
+  // each 16-token block).  With the prefetch, the scale copies into LDS are
+  // the only loads still in flight (no refill was issued past the last chunk).
+  if (kEpiPrefetch && sc) __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  // scale of item row q (the epilogue's only use of sc)
+  auto row_scale = [&](int q) {
+    if constexpr (kEpiPrefetch) return s_sc[q];
+    const int row = (MODE == kGateUp) ? (q < 8 * RT ? tx * (8 * RT) + q : a.N / 2 + tx * (8 * RT) + q - 8 * RT)
+                                      : tx * (16 * RT) + q;
+    return sc ? sc[row] : 1.f;
+  };
   if constexpr (MODE == kGateUp) {
     // h = GELU(gate) * up for the item's 16 TB sorted positions (consecutive
     // rows of h) x 8 RT columns, staged through LDS like the down epilogue
@@ -744,11 +794,12 @@ __global__ __launch_bounds__(64, WPE) void gemm_wave_kernel(GemmArgs a) {
       const int row = tb * 16 + l16;
 #pragma unroll
       for (int i = 0; i < RT / 2; ++i) {
-        const int n = tx * NC + i * 16 + g4 * 4;
         float hv[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float sg = sc ? sc[n + r] : 1.f, su = sc ? sc[I + n + r] : 1.f;
+          // item row of gate column tx NC + q (its up row: q + 8 RT)
+          const int q = i * 16 + g4 * 4 + r;
+          const float sg = row_scale(q), su = row_scale(8 * RT + q);
           hv[r] = gelu_erf(acc[i][tb][r] * sg) * (acc[RT / 2 + i][tb][r] * su);
         }
         uint2 pk;
@@ -784,15 +835,21 @@ __global__ __launch_bounds__(64, WPE) void gemm_wave_kernel(GemmArgs a) {
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) {
       const int row = tb * 16 + l16;
-      const int slot = xok[tb] ? a.sorted_rows[p_pos[tb]] : -1;
-      const float g = xok[tb] ? a.gates[slot] : 0.f;
+      int slot;
+      float g;
+      if constexpr (kEpiPrefetch) {
+        slot = e_slot[tb];
+        g = e_gate[tb];
+      } else {
+        slot = xok[tb] ? a.sorted_rows[p_pos[tb]] : -1;
+        g = xok[tb] ? a.gates[slot] : 0.f;
+      }
       if (g4 == 0) s_slot[row] = slot;
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
-        const int n = tx * NC + rt * 16 + g4 * 4;
         float v[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = g * acc[rt][tb][r] * (sc ? sc[n + r] : 1.f);
+        for (int r = 0; r < 4; ++r) v[r] = g * acc[rt][tb][r] * row_scale(rt * 16 + g4 * 4 + r);
         uint2 pk;
         pk.x = pack_bf16x2(v[0], v[1]);
         pk.y = pack_bf16x2(v[2], v[3]);
