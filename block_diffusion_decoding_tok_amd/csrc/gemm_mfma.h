@@ -292,6 +292,33 @@ __global__ __launch_bounds__(256, MINWG) void gemm_stream_kernel(GemmArgs a) {
   }
   __syncthreads();
 
+  // ---- what the expert epilogue reads besides the accumulators, fetched
+  // now so that its latency is not added after the last stage (the scale and
+  // gate reads there each waited on the spot): the item's 128 per-row fp8
+  // scales by direct-to-LDS copies (gate/up: 64 gate rows, then the 64 up
+  // rows; down: 64 RT rows) and, for down, the gate of each token row
+  const float* sc = a.w_scale ? a.w_scale + static_cast<int64_t>(grp) * a.s_group_stride : nullptr;
+  __shared__ float s_esc[128];
+  __shared__ float s_egt[MT];
+  if constexpr (MODE != kDense) {
+    static_assert(MODE == kGateUp || 64 * RT == 128, "128 scale rows per item");
+    static_assert(MT == 64, "one wave copies the token rows' gates");
+    if (sc) {
+      if (wave < 2) {
+        const int q = wave * 64 + lane;
+        const int row = (MODE == kGateUp) ? (q < 64 ? tx * 64 + q : a.N / 2 + tx * 64 + q - 64)
+                                          : tx * 128 + q;
+        __builtin_amdgcn_global_load_lds(sc + row, s_esc + wave * 64, 4, 0, 0);
+      }
+    } else if (tid < 128) {
+      s_esc[tid] = 1.f;                      // unscaled weights
+    }
+  }
+  // down: the gate of token row tid (every thread loads one, unconditionally;
+  // written to LDS by the first MT threads in the epilogue)
+  float e_gt = 0.f;
+  if constexpr (MODE == kDown) e_gt = a.gates[max(s_dst[min(tid, MT - 1)], 0)];
+
   // ---- weight rows of this wave
   const WT* Wg = static_cast<const WT*>(a.W) + static_cast<int64_t>(grp) * a.w_group_stride;
   WRow<WT, TILED> wr_at[RT];
@@ -388,7 +415,10 @@ __global__ __launch_bounds__(256, MINWG) void gemm_stream_kernel(GemmArgs a) {
       const int buf = s & 1;
       store_x(s, buf, xr[p]);
       __syncthreads();
-      load_x(s + PF, xr[p]);
+      // (one stage in flight: no refill past the last stage, whose loads the
+      // epilogue would otherwise wait for)
+      const bool refill = PF > 1 || s + PF < nstages;
+      if (refill) load_x(s + PF, xr[p]);
 #pragma unroll
       for (int j = 0; j < KS; ++j) {
         // widen chunk j of stage s, then refill its slot with stage s + PF
@@ -396,8 +426,10 @@ __global__ __launch_bounds__(256, MINWG) void gemm_stream_kernel(GemmArgs a) {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) wr[p][j][rt].get(wa[rt][0], wa[rt][1]);
         const int c = min((s + PF) * KS + j, nchunks - 1);
+        if (refill) {
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) load_chunk(wr[p][j][rt], rt, c);
+          for (int rt = 0; rt < RT; ++rt) load_chunk(wr[p][j][rt], rt, c);
+        }
         if (s * KS + j >= nchunks) continue;
 #pragma unroll
         for (int tb = 0; tb < TB; ++tb) {
@@ -417,7 +449,6 @@ __global__ __launch_bounds__(256, MINWG) void gemm_stream_kernel(GemmArgs a) {
   }
 
   // ---- epilogue: lane holds rows 4 g4 + r of each 16-row tile, token l16
-  const float* sc = a.w_scale ? a.w_scale + static_cast<int64_t>(grp) * a.s_group_stride : nullptr;
   if constexpr (MODE != kDense) {
     // expert modes: the workgroup's MT rows x NC columns go through LDS (the
     // token stages are free once every wave is past the last one), so that
@@ -426,32 +457,32 @@ __global__ __launch_bounds__(256, MINWG) void gemm_stream_kernel(GemmArgs a) {
     constexpr int OS = NC + 8;
     static_assert(MT * OS <= 2 * MT * XS, "output tile fits the token stages");
     bf16_t* s_o = &s_x[0][0];
-    const int I = a.N / 2;
+    // the copies issued at the start (each wave waits for its own; the
+    // barrier then makes them visible to all)
+    if (MODE == kDown && tid < MT) s_egt[tid] = e_gt;
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __syncthreads();
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) {
       const int t = tb * 16 + l16;
       if (MODE == kGateUp) {
-        const int n = tx * 64 + wave * 16 + g4 * 4;
+        const int q = wave * 16 + g4 * 4;     // item row of gate column tx 64 + q
         float hv[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float sg = sc ? sc[n + r] : 1.f, su = sc ? sc[I + n + r] : 1.f;
-          hv[r] = gelu_erf(acc[0][tb][r] * sg) * (acc[1][tb][r] * su);
-        }
+        for (int r = 0; r < 4; ++r)
+          hv[r] = gelu_erf(acc[0][tb][r] * s_esc[q + r]) * (acc[1][tb][r] * s_esc[64 + q + r]);
         uint2 pk;
         pk.x = pack_bf16x2(hv[0], hv[1]);
         pk.y = pack_bf16x2(hv[2], hv[3]);
         *reinterpret_cast<uint2*>(&s_o[t * OS + wave * 16 + g4 * 4]) = pk;
       } else {
-        const float g = t < m_count ? a.gates[s_dst[t]] : 0.f;
+        const float g = t < m_count ? s_egt[t] : 0.f;
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
           const int nl = wave * (16 * RT) + rt * 16 + g4 * 4;
-          const int n = tx * NC + nl;
           float v[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) v[r] = g * acc[rt][tb][r] * (sc ? sc[n + r] : 1.f);
+          for (int r = 0; r < 4; ++r) v[r] = g * acc[rt][tb][r] * s_esc[nl + r];
           uint2 pk;
           pk.x = pack_bf16x2(v[0], v[1]);
           pk.y = pack_bf16x2(v[2], v[3]);
@@ -461,7 +492,7 @@ __global__ __launch_bounds__(256, MINWG) void gemm_stream_kernel(GemmArgs a) {
     }
     __syncthreads();
     constexpr int PR = NC / 8;               // 16-byte pieces per row
-    const int ld = MODE == kGateUp ? I : a.N;
+    const int ld = MODE == kGateUp ? a.N / 2 : a.N;
 #pragma unroll
     for (int it = 0; it < (MT * PR + 255) / 256; ++it) {
       const int q = it * 256 + tid;
