@@ -1006,36 +1006,96 @@ __global__ __launch_bounds__(64 * NW, WPE) void gemm_splitk_kernel(GemmArgs a) {
     issue(ring[p], p);
     __builtin_amdgcn_sched_barrier(0);
   }
-  for (int c0 = 0; c0 < nchunks; c0 += NR) {
+  // one chunk step: the MMAs of chunk c from slot p, then (refill) the slot
+  // refilled with chunk c + NR (kSplitIssueFirst: refilled before the MMAs)
+  auto step = [&](int p, int c, bool refill) {
+    const Slot cur = ring[p];
+    if (kSplitIssueFirst && refill) {
+      __builtin_amdgcn_sched_barrier(0);
+      issue(ring[p], c + NR);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (c < nchunks) {
 #pragma unroll
-    for (int p = 0; p < NR; ++p) {
-      // refill the slot before or after its MMAs (see kSplitIssueFirst)
-      const Slot cur = ring[p];
-      if (kSplitIssueFirst) {
-        __builtin_amdgcn_sched_barrier(0);
-        issue(ring[p], c0 + p + NR);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      if (c0 + p < nchunks) {
+      for (int tb = 0; tb < TB; ++tb) {
+        const uint4 u0 = xok[tb] ? cur.x[tb][0] : zero4, u1 = xok[tb] ? cur.x[tb][1] : zero4;
+        const bf16x8_v x0 = *reinterpret_cast<const bf16x8_v*>(&u0);
+        const bf16x8_v x1 = *reinterpret_cast<const bf16x8_v*>(&u1);
 #pragma unroll
-        for (int tb = 0; tb < TB; ++tb) {
-          const uint4 u0 = xok[tb] ? cur.x[tb][0] : zero4, u1 = xok[tb] ? cur.x[tb][1] : zero4;
-          const bf16x8_v x0 = *reinterpret_cast<const bf16x8_v*>(&u0);
-          const bf16x8_v x1 = *reinterpret_cast<const bf16x8_v*>(&u1);
-#pragma unroll
-          for (int rt = 0; rt < RT; ++rt) {
-            const bf16x8_v w0 = *reinterpret_cast<const bf16x8_v*>(&cur.w[rt][0]);
-            const bf16x8_v w1 = *reinterpret_cast<const bf16x8_v*>(&cur.w[rt][1]);
-            acc[rt][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w0, x0, acc[rt][tb], 0, 0, 0);
-            acc[rt][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w1, x1, acc[rt][tb], 0, 0, 0);
-          }
+        for (int rt = 0; rt < RT; ++rt) {
+          const bf16x8_v w0 = *reinterpret_cast<const bf16x8_v*>(&cur.w[rt][0]);
+          const bf16x8_v w1 = *reinterpret_cast<const bf16x8_v*>(&cur.w[rt][1]);
+          acc[rt][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w0, x0, acc[rt][tb], 0, 0, 0);
+          acc[rt][tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w1, x1, acc[rt][tb], 0, 0, 0);
         }
       }
-      if (!kSplitIssueFirst) {
-        __builtin_amdgcn_sched_barrier(0);
-        issue(ring[p], c0 + p + NR);
-        __builtin_amdgcn_sched_barrier(0);
+    }
+    if (!kSplitIssueFirst && refill) {
+      __builtin_amdgcn_sched_barrier(0);
+      issue(ring[p], c + NR);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // Tiles of up to 64 weight rows: blocks whose every refill is a chunk
+  // still to come, then at most two blocks that refill only while there is
+  // one, so that no loads past the last chunk are in flight when the
+  // epilogue's own reads (issued below, before the reduction) are waited
+  // for.  Tiles of 128 rows keep one loop with clamped refills: the peeled
+  // tail costs them registers they do not have.
+  constexpr bool kEpiPf = RT <= 4;
+  if constexpr (kEpiPf) {
+    const int n_full = nchunks > NR ? (nchunks - NR) / NR * NR : 0;
+    int c0 = 0;
+    for (; c0 < n_full; c0 += NR) {
+#pragma unroll
+      for (int p = 0; p < NR; ++p) step(p, c0 + p, true);
+    }
+    for (; c0 < nchunks; c0 += NR) {
+#pragma unroll
+      for (int p = 0; p < NR; ++p) step(p, c0 + p, c0 + p + NR < nchunks);
+    }
+  } else {
+    for (int c0 = 0; c0 < nchunks; c0 += NR) {
+#pragma unroll
+      for (int p = 0; p < NR; ++p) step(p, c0 + p, true);
+    }
+  }
+
+  // ---- the epilogue's global reads, issued now so that they complete while
+  // the partial sums pass through LDS: the RoPE form's cache length and
+  // (cos, sin) of each quad's token, the accumulate form's f32 residual
+  constexpr int kPairsAll = (RT / 2) * TB * 64;
+  constexpr int kQuadsAll = RT * TB * 64;
+  constexpr int kPfR = (kPairsAll + 64 * NW - 1) / (64 * NW);
+  constexpr int kPfA = (kQuadsAll + 64 * NW - 1) / (64 * NW);
+  int pf_p[kRopeTile ? kPfR : 1];
+  float4 pf_cs[kRopeTile ? kPfR : 1][2];
+  float4 pf_c[kPfA];
+  if constexpr (kRopeTile && kEpiPf) {
+    if (a.rope) {
+#pragma unroll
+      for (int k = 0; k < kPfR; ++k) {
+        const int q = min(k * 64 * NW + tid, kPairsAll - 1);
+        const int ql = q & 63, blk = q >> 6;
+        const int rt = blk / TB, tb = blk % TB;
+        const int m = min(m0 + tb * 16 + (ql & 15), a.M - 1);
+        const int d0 = (row16(rt) % 8) * 16 + (ql >> 4) * 4;
+        pf_p[k] = a.prefix_len[m / a.Lq];
+        const float4* cs = reinterpret_cast<const float4*>(a.rope_tab + static_cast<int64_t>(m) * 64 + d0);
+        pf_cs[k][0] = cs[0];
+        pf_cs[k][1] = cs[1];
       }
+    }
+  }
+  if (kEpiPf && a.accumulate && a.out_dtype == DG_F32 && !(kRopeTile && a.rope)) {
+#pragma unroll
+    for (int k = 0; k < kPfA; ++k) {
+      const int q = min(k * 64 * NW + tid, kQuadsAll - 1);
+      const int ql = q & 63, blk = q >> 6;
+      const int rt = blk / TB, tb = blk % TB;
+      const int n = n0 + rt * 16 + (ql >> 4) * 4;
+      const int m = min(m0 + tb * 16 + (ql & 15), a.M - 1);
+      pf_c[k] = *reinterpret_cast<const float4*>(static_cast<const float*>(a.out) + static_cast<int64_t>(m) * a.N + n);
     }
   }
 
@@ -1096,16 +1156,26 @@ __global__ __launch_bounds__(64 * NW, WPE) void gemm_splitk_kernel(GemmArgs a) {
         const int head = row16(0) / 8;
         const int d0 = (row16(rt) % 8) * 16 + (ql >> 4) * 4;  // < 64
         const int b = m / a.Lq, i = m % a.Lq;
-        const int pos = a.prefix_len[b] + i;
+        const int k = q0 / (64 * NW);                  // the prefetched values
+        const int pos = (kEpiPf ? pf_p[k] : a.prefix_len[b]) + i;
         if (head >= a.Hq && pos >= a.Tmax) continue;   // past the cache: not written
         float o1[4], o2[4];
         bf16_t* dst;
         if (head < a.Hq + a.Hkv) {
           const float sc = head < a.Hq ? a.q_scale : 1.f;
-          const float2* cs = a.rope_tab + static_cast<int64_t>(m) * 64 + d0;
+          float4 cs4[2];
+          if constexpr (kEpiPf) {
+            cs4[0] = pf_cs[k][0];
+            cs4[1] = pf_cs[k][1];
+          } else {
+            const float4* t = reinterpret_cast<const float4*>(a.rope_tab + static_cast<int64_t>(m) * 64 + d0);
+            cs4[0] = t[0];
+            cs4[1] = t[1];
+          }
+          const float cs[8] = {cs4[0].x, cs4[0].y, cs4[0].z, cs4[0].w, cs4[1].x, cs4[1].y, cs4[1].z, cs4[1].w};
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const float c = cs[r].x, sn = cs[r].y;
+            const float c = cs[2 * r], sn = cs[2 * r + 1];
             o1[r] = (v1[r] * c - v2[r] * sn) * sc;
             o2[r] = (v2[r] * c + v1[r] * sn) * sc;
           }
@@ -1148,7 +1218,7 @@ __global__ __launch_bounds__(64 * NW, WPE) void gemm_splitk_kernel(GemmArgs a) {
     if (a.out_dtype == DG_F32) {
       float* o = static_cast<float*>(a.out) + static_cast<int64_t>(m) * a.N + n;
       if (a.accumulate) {
-        const float4 c = *reinterpret_cast<float4*>(o);
+        const float4 c = kEpiPf ? pf_c[q0 / (64 * NW)] : *reinterpret_cast<const float4*>(o);
         *reinterpret_cast<float4*>(o) = make_float4(c.x + v[0], c.y + v[1], c.z + v[2], c.w + v[3]);
       } else {
         *reinterpret_cast<float4*>(o) = make_float4(v[0], v[1], v[2], v[3]);
