@@ -1324,6 +1324,23 @@ __global__ __launch_bounds__(256, 2) void gemm_dl128_kernel(GemmArgs a) {
 
   // lane: rows 4 g4 + r of row block i, token l16 of token block j
   if (a.rope) {
+    // the rotating waves' cache lengths and (cos, sin), read before the
+    // hand-over so that they arrive while it runs
+    int pf_p[4];
+    float4 pf_cs[4][4][2];
+    if (wr == 0) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int m = min(m0 + (wt * 4 + j) * 16 + l16, a.M - 1);
+        pf_p[j] = a.prefix_len[m / a.Lq];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float4* t = reinterpret_cast<const float4*>(a.rope_tab + static_cast<int64_t>(m) * 64 + i * 16 + g4 * 4);
+          pf_cs[j][i][0] = t[0];
+          pf_cs[j][i][1] = t[1];
+        }
+      }
+    }
     // hand rows 64 .. 127 (the d + 64 halves of the head's pairs) to wave wr = 0
     __syncthreads();                             // every wave is done with the stages
     f32x4_v* s_x = reinterpret_cast<f32x4_v*>(dl128_smem);
@@ -1342,7 +1359,7 @@ __global__ __launch_bounds__(256, 2) void gemm_dl128_kernel(GemmArgs a) {
       const int m = m0 + (wt * 4 + j) * 16 + l16;
       if (m >= a.M) continue;
       const int b = m / a.Lq, i_tok = m % a.Lq;
-      const int pos = a.prefix_len[b] + i_tok;
+      const int pos = pf_p[j] + i_tok;
       if (head >= a.Hq && pos >= a.Tmax) continue;   // past the cache: not written
       bf16_t* dst;
       if (head < a.Hq) {
@@ -1361,10 +1378,11 @@ __global__ __launch_bounds__(256, 2) void gemm_dl128_kernel(GemmArgs a) {
         float o1[4], o2[4];
         if (head < a.Hq + a.Hkv) {
           const float sc = head < a.Hq ? a.q_scale : 1.f;
-          const float2* cs = a.rope_tab + static_cast<int64_t>(m) * 64 + d0;
+          const float4 c01 = pf_cs[j][i][0], c23 = pf_cs[j][i][1];   // (cos, sin) of d0 .. d0 + 3
+          const float cs[8] = {c01.x, c01.y, c01.z, c01.w, c23.x, c23.y, c23.z, c23.w};
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const float c = cs[r].x, sn = cs[r].y;
+            const float c = cs[2 * r], sn = cs[2 * r + 1];
             o1[r] = (v1[r] * c - v2[r] * sn) * sc;
             o2[r] = (v2[r] * c + v1[r] * sn) * sc;
           }
@@ -1379,6 +1397,20 @@ __global__ __launch_bounds__(256, 2) void gemm_dl128_kernel(GemmArgs a) {
     }
     return;
   }
+  // the accumulate form's residual, every piece read before the first store
+  // (each read would otherwise wait behind the stores before it)
+  float4 pf_c[4][4];
+  if (a.accumulate && a.out_dtype == DG_F32) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int m = min(m0 + (wt * 4 + j) * 16 + l16, a.M - 1);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int n = n0 + (wr * 4 + i) * 16 + g4 * 4;
+        pf_c[j][i] = *reinterpret_cast<const float4*>(static_cast<const float*>(a.out) + static_cast<int64_t>(m) * a.N + n);
+      }
+    }
+  }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int m = m0 + (wt * 4 + j) * 16 + l16;
@@ -1390,7 +1422,7 @@ __global__ __launch_bounds__(256, 2) void gemm_dl128_kernel(GemmArgs a) {
       if (a.out_dtype == DG_F32) {
         float* o = static_cast<float*>(a.out) + static_cast<int64_t>(m) * a.N + n;
         if (a.accumulate) {
-          const float4 c4 = *reinterpret_cast<const float4*>(o);
+          const float4 c4 = pf_c[j][i];
           *reinterpret_cast<float4*>(o) = make_float4(c4.x + v[0], c4.y + v[1], c4.z + v[2], c4.w + v[3]);
         } else {
           *reinterpret_cast<float4*>(o) = make_float4(v[0], v[1], v[2], v[3]);
