@@ -1006,8 +1006,9 @@ __global__ __launch_bounds__(64 * NW, WPE) void gemm_splitk_kernel(GemmArgs a) {
     issue(ring[p], p);
     __builtin_amdgcn_sched_barrier(0);
   }
-  // one chunk step: the MMAs of chunk c from slot p, then (refill) the slot
-  // refilled with chunk c + NR (kSplitIssueFirst: refilled before the MMAs)
+  // one chunk step: the MMAs of chunk c from ring slot p; with `refill` the
+  // slot is then loaded with chunk c + NR (before the MMAs under
+  // kSplitIssueFirst)
   auto step = [&](int p, int c, bool refill) {
     const Slot cur = ring[p];
     if (kSplitIssueFirst && refill) {
