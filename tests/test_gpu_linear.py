@@ -41,13 +41,14 @@ def test_linear_projection_shapes(M, N, K, tiled):
     assert rel_err_rows(out.cpu().double().numpy(), _ref(x, w)) < 1e-5
 
 
+@pytest.mark.parametrize("M", [256, 37])
 @pytest.mark.parametrize("tiled", [False, True])
-def test_linear_accumulate_bf16_out(tiled):
-    M, N, K = 256, 2816, 2048
-    x, w = _case(M, N, K, seed=3)
+def test_linear_accumulate_bf16_out(M, tiled):
+    N, K = 2816, 2048
+    x, w = _case(M, N, K, seed=3 + M)
     wd = dg.dg_pack_weights(w.to(DEV)) if tiled else w.to(DEV)
     lay = dg.DG_LAYOUT_TILED if tiled else dg.DG_LAYOUT_ROWMAJOR
-    y0 = torch.randn((M, N), generator=torch.Generator().manual_seed(4))
+    y0 = torch.randn((M, N), generator=torch.Generator().manual_seed(4 + M))
     y = y0.clone().to(DEV)
     dg.dg_linear(x.to(DEV), wd, out=y, accumulate=True, N=N, w_layout=lay)
     ob = dg.dg_linear(x.to(DEV), wd, out_dtype=torch.bfloat16, N=N, w_layout=lay)
