@@ -93,7 +93,7 @@ __global__ void advance_prefix_kernel(int32_t* prefix_len, int B, int L) {
 constexpr int kAttnRows = 128;        // packed rows per workgroup (4 row groups of 32)
 constexpr int kAttnKeys = 128;        // keys per LDS tile (2 halves of 64)
 constexpr int kDh = 128;
-constexpr int kKStride = kDh + 16;    // K tile row stride (elements): 288 B
+constexpr int kKStride = kDh;         // K tile row stride (elements): 256 B, 16-byte pieces XOR-swizzled
 constexpr int kVStride = kAttnKeys + 16;  // V^T tile row stride: 288 B
 constexpr int kKTileElems = kAttnKeys * kKStride;
 constexpr int kVTileElems = kDh * kVStride;
@@ -114,14 +114,15 @@ __device__ __forceinline__ int attn_block_end(int tok, int mask_blk, int Lq) {
   return min(Lq, (tok / mask_blk + 1) * mask_blk);
 }
 
-// LDS row of key k (0..127) of a K tile.  The S^T MFMA's output row 16 b + 4 g
-// + r (b = 0..3 within a 64-key half, g = lane / 16) must hold key 8 g + 4 (b
-// & 1) + r of the half's 32-key chunk b / 2, so that each lane's eight
-// probabilities of a chunk are eight consecutive keys -- the B-operand layout
-// of the PV MFMA over V^T in natural key order.  Keys are stored in that
-// MFMA row order.
-__device__ __forceinline__ int k_lds_row(int k) {
-  return (k & ~31) | (((k >> 2) & 1) << 4) | (((k >> 3) & 3) << 2) | (k & 3);
+// Key held by LDS row r (0..127) of a K tile.  The S^T MFMA's output row
+// 16 b + 4 g + r' (b = 0..3 within a 64-key half, g = lane / 16) must hold
+// key 8 g + 4 (b & 1) + r' of the half's 32-key chunk b / 2, so that each
+// lane's eight probabilities of a chunk are eight consecutive keys -- the
+// B-operand layout of the PV MFMA over V^T in natural key order.  Keys are
+// stored in that MFMA row order: within 32 rows, row bits (4, 3, 2) hold key
+// bits (2, 4, 3).
+__device__ __forceinline__ int k_row_key(int r) {
+  return (r & ~31) | (((r >> 3) & 1) << 4) | (((r >> 2) & 1) << 3) | (((r >> 4) & 1) << 2) | (r & 3);
 }
 
 struct AttnPartialML { float m, l; };
@@ -141,30 +142,40 @@ __device__ __forceinline__ float max_over_g4(float x) {
   return fmax2(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-// Staging of one 128-key tile through registers, loads clamped to the last
-// valid key (past it the scores are masked, and the clamped rows hold finite
-// cache data):
-//   K: 128 keys x 16 chunks of 8 dh = 2048 items of 16 B, four per thread,
-//      stored at the key's MFMA row (k_lds_row);
-//   V: a quad of 4 keys (kq) x one chunk of 8 dh (vch) per thread, stored
-//      transposed into V^T [dh][keys] as 8 rows of 4 keys.
+// Staging of one 128-key V tile through registers, loads clamped to the
+// last valid key (past it the scores are masked, and the clamped rows hold
+// finite cache data): a quad of 4 keys (kq) x one chunk of 8 dh (vch) per
+// thread, stored transposed into V^T [dh][keys] as 8 rows of 4 keys.  (K
+// tiles go to LDS by direct copies, attn_issue_k below.)
 struct AttnStage {
-  uint4 k0, k1, k2, k3, v0, v1, v2, v3;
+  uint4 v0, v1, v2, v3;
 };
 
-__device__ __forceinline__ void attn_load_stage(AttnStage& st, const bf16_t* kbase,
-                                                const bf16_t* vbase, int key0, int k_end, int tid,
-                                                int kq, int vch) {
-  auto kload = [&](int it) {
-    const int item = it * 512 + tid;
-    const int gk = min(key0 + (item >> 4), k_end - 1);
-    return *reinterpret_cast<const uint4*>(kbase + static_cast<int64_t>(gk) * kDh + (item & 15) * 8);
-  };
+// K: the tile's 128 rows of 256 B copied straight into LDS by direct-to-LDS
+// 16-byte loads (no staging registers): LDS row r holds key k_row_key(r),
+// its 16-byte piece p in slot p ^ (r & 15), so that the 16 rows one
+// S-fragment read touches use 16 different slots (no bank conflicts without
+// row padding).  A wave instruction fills 1 KB (4 rows: lane i writes row
+// i / 16, slot i % 16); eight waves issue four each.  Keys past the last
+// valid one are clamped to it.
+__device__ __forceinline__ void attn_issue_k(bf16_t* sk, const bf16_t* kbase, int key0, int k_end,
+                                             int wave, int lane) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = (wave * 4 + i) * 4 + (lane >> 4);
+    const int piece = (lane & 15) ^ (row & 15);
+    const int gk = min(key0 + k_row_key(row), k_end - 1);
+    __builtin_amdgcn_global_load_lds(kbase + static_cast<int64_t>(gk) * kDh + piece * 8,
+                                     sk + (wave * 4 + i) * 4 * kKStride, 16, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void attn_load_v(AttnStage& st, const bf16_t* vbase, int key0, int k_end,
+                                            int kq, int vch) {
   auto vload = [&](int kk) {
     const int gk = min(key0 + kq * 4 + kk, k_end - 1);
     return *reinterpret_cast<const uint4*>(vbase + static_cast<int64_t>(gk) * kDh + vch * 8);
   };
-  st.k0 = kload(0); st.k1 = kload(1); st.k2 = kload(2); st.k3 = kload(3);
   st.v0 = vload(0); st.v1 = vload(1); st.v2 = vload(2); st.v3 = vload(3);
 }
 
@@ -172,13 +183,7 @@ __device__ __forceinline__ uint32_t u4w(const uint4& u, int i) {
   return i == 0 ? u.x : i == 1 ? u.y : i == 2 ? u.z : u.w;
 }
 
-__device__ __forceinline__ void attn_store_stage(const AttnStage& st, bf16_t* sk, bf16_t* sv,
-                                                 int tid, int kq, int vch) {
-  auto kstore = [&](int it, const uint4& v) {
-    const int item = it * 512 + tid;
-    *reinterpret_cast<uint4*>(&sk[k_lds_row(item >> 4) * kKStride + (item & 15) * 8]) = v;
-  };
-  kstore(0, st.k0); kstore(1, st.k1); kstore(2, st.k2); kstore(3, st.k3);
+__device__ __forceinline__ void attn_store_v(const AttnStage& st, bf16_t* sv, int kq, int vch) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     // dh element e of the four keys: low or high halves of word e / 2
@@ -269,16 +274,26 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(
   const bf16_t* kbase = k_cache + static_cast<int64_t>(bh) * Tmax * kDh;
   const bf16_t* vbase = v_cache + static_cast<int64_t>(bh) * Tmax * kDh;
 
-  // K/V tiles: register staging (AttnStage), LDS double buffer
+  // K/V tiles in LDS double buffers: K by direct copies, V through
+  // registers (AttnStage, transposed on the way).  Iteration t stores V(t),
+  // then (after the barrier) copies K(t + 1) and loads V(t + 1); the K buffer
+  // it overwrites held K(t - 1), read before its barrier.
   const int kq = tid & 31, vch = tid >> 5;
   AttnStage st;
-  if (ntiles > 0) attn_load_stage(st, kbase, vbase, k_begin, k_end, tid, kq, vch);
+  if (ntiles > 0) {
+    attn_issue_k(s_k(0), kbase, k_begin, k_end, wave, lane);
+    attn_load_v(st, vbase, k_begin, k_end, kq, vch);
+  }
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t & 1;
-    attn_store_stage(st, s_k(buf), s_v(buf), tid, kq, vch);
+    attn_store_v(st, s_v(buf), kq, vch);
+    // this wave's copies of K(t) have landed; after the barrier every wave's
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __syncthreads();
-    if (t + 1 < ntiles)
-      attn_load_stage(st, kbase, vbase, k_begin + (t + 1) * kAttnKeys, k_end, tid, kq, vch);
+    if (t + 1 < ntiles) {
+      attn_issue_k(s_k(buf ^ 1), kbase, k_begin + (t + 1) * kAttnKeys, k_end, wave, lane);
+      attn_load_v(st, vbase, k_begin + (t + 1) * kAttnKeys, k_end, kq, vch);
+    }
     const int hkey0 = k_begin + t * kAttnKeys + kh * 64;   // first key of this wave's half
     const bf16_t* sk = s_k(buf) + kh * 64 * kKStride;
     const bf16_t* sv = s_v(buf) + kh * 64;
@@ -293,7 +308,7 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(
-            &sk[(kb * 16 + l16) * kKStride + c * 32 + g4 * 8]);
+            &sk[(kb * 16 + l16) * kKStride + ((c * 4 + g4) ^ l16) * 8]);
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
           s_acc[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[qb][c], s_acc[kb][qb], 0, 0, 0);
