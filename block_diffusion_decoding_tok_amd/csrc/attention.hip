@@ -94,9 +94,9 @@ constexpr int kAttnRows = 128;        // packed rows per workgroup (4 row groups
 constexpr int kAttnKeys = 128;        // keys per LDS tile (2 halves of 64)
 constexpr int kDh = 128;
 constexpr int kKStride = kDh;         // K tile row stride (elements): 256 B, 16-byte pieces XOR-swizzled
-constexpr int kVStride = kAttnKeys + 16;  // V^T tile row stride: 288 B
+constexpr int kVStride = kDh;         // V tile row stride (elements): 256 B, 16-byte pieces XOR-swizzled
 constexpr int kKTileElems = kAttnKeys * kKStride;
-constexpr int kVTileElems = kDh * kVStride;
+constexpr int kVTileElems = kAttnKeys * kVStride;
 // A row's running maximum is raised only when a tile's maximum exceeds it by
 // more than this (log2 units): probabilities then stay below 2^8, and the
 // rescale of the output accumulators is skipped on most tiles.
@@ -142,15 +142,6 @@ __device__ __forceinline__ float max_over_g4(float x) {
   return fmax2(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-// Staging of one 128-key V tile through registers, loads clamped to the
-// last valid key (past it the scores are masked, and the clamped rows hold
-// finite cache data): a quad of 4 keys (kq) x one chunk of 8 dh (vch) per
-// thread, stored transposed into V^T [dh][keys] as 8 rows of 4 keys.  (K
-// tiles go to LDS by direct copies, attn_issue_k below.)
-struct AttnStage {
-  uint4 v0, v1, v2, v3;
-};
-
 // K: the tile's 128 rows of 256 B copied straight into LDS by direct-to-LDS
 // 16-byte loads (no staging registers): LDS row r holds key k_row_key(r),
 // its 16-byte piece p in slot p ^ (r & 15), so that the 16 rows one
@@ -170,30 +161,44 @@ __device__ __forceinline__ void attn_issue_k(bf16_t* sk, const bf16_t* kbase, in
   }
 }
 
-__device__ __forceinline__ void attn_load_v(AttnStage& st, const bf16_t* vbase, int key0, int k_end,
-                                            int kq, int vch) {
-  auto vload = [&](int kk) {
-    const int gk = min(key0 + kq * 4 + kk, k_end - 1);
-    return *reinterpret_cast<const uint4*>(vbase + static_cast<int64_t>(gk) * kDh + vch * 8);
-  };
-  st.v0 = vload(0); st.v1 = vload(1); st.v2 = vload(2); st.v3 = vload(3);
-}
-
-__device__ __forceinline__ uint32_t u4w(const uint4& u, int i) {
-  return i == 0 ? u.x : i == 1 ? u.y : i == 2 ? u.z : u.w;
-}
-
-__device__ __forceinline__ void attn_store_v(const AttnStage& st, bf16_t* sv, int kq, int vch) {
+// V: the tile's 128 key rows of 256 B in natural order, copied into LDS the
+// same way, piece p of row r in slot p ^ v_swz(r).  The PV MFMA's A operand
+// is V^T (lane (l16, g4): dh l16 of a 16-row block, 8 consecutive keys);
+// two transposing LDS reads (ds_read_b64_tr_b16) give it: within a group of
+// 16 lanes, lane m reads dh 4 (m & 3) .. + 3 of key m / 4 (of 4 keys), and
+// lane l receives element l % 4 of lanes 4 j + l / 4 (j = 0..3), i.e. dh l of
+// the 4 keys.  v_swz gives the 8 rows two groups read at once (keys 0..3 and
+// 8..11 of a 16-key block) 8 different slot pairs.
+__device__ __forceinline__ int v_swz(int r) { return ((r & 3) | (((r >> 3) & 1) << 2)) << 1; }
+__device__ __forceinline__ void attn_issue_v(bf16_t* sv, const bf16_t* vbase, int key0, int k_end,
+                                             int wave, int lane) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    // dh element e of the four keys: low or high halves of word e / 2
-    const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-    uint2 pk;
-    pk.x = __builtin_amdgcn_perm(u4w(st.v1, e >> 1), u4w(st.v0, e >> 1), sel);
-    pk.y = __builtin_amdgcn_perm(u4w(st.v3, e >> 1), u4w(st.v2, e >> 1), sel);
-    *reinterpret_cast<uint2*>(&sv[(vch * 8 + e) * kVStride + kq * 4]) = pk;
+  for (int i = 0; i < 4; ++i) {
+    const int row = (wave * 4 + i) * 4 + (lane >> 4);
+    const int piece = (lane & 15) ^ v_swz(row);
+    const int gk = min(key0 + row, k_end - 1);
+    __builtin_amdgcn_global_load_lds(vbase + static_cast<int64_t>(gk) * kDh + piece * 8,
+                                     sv + (wave * 4 + i) * 4 * kVStride, 16, 0, 0);
   }
 }
+// The V^T fragment of keys key0 .. key0 + 7 (key0 a multiple of 8, the
+// lane's group's) and dh d0 + l16 (d0 a multiple of 16).
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ bf16x8_t attn_read_vt(const bf16_t* sv, int key0, int d0, int l16) {
+  v4i16_t h[2];
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int row = key0 + half * 4 + (l16 >> 2);
+    const int col = d0 + 4 * (l16 & 3);
+    const bf16_t* p = sv + row * kVStride + (((col >> 3) ^ v_swz(row)) << 3) + (col & 7);
+    h[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16_t*)(p));
+  }
+  const v4i16_t lo = h[0], hi = h[1];
+  typedef short v8i16_t __attribute__((ext_vector_type(8)));
+  const v8i16_t v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
 
 __global__ __launch_bounds__(512) void attn_mfma_kernel(
     const bf16_t* __restrict__ qrot, const bf16_t* __restrict__ k_cache,
@@ -274,29 +279,26 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(
   const bf16_t* kbase = k_cache + static_cast<int64_t>(bh) * Tmax * kDh;
   const bf16_t* vbase = v_cache + static_cast<int64_t>(bh) * Tmax * kDh;
 
-  // K/V tiles in LDS double buffers: K by direct copies, V through
-  // registers (AttnStage, transposed on the way).  Iteration t stores V(t),
-  // then (after the barrier) copies K(t + 1) and loads V(t + 1); the K buffer
-  // it overwrites held K(t - 1), read before its barrier.
-  const int kq = tid & 31, vch = tid >> 5;
-  AttnStage st;
+  // K/V tiles in LDS double buffers, both filled by direct copies (no
+  // staging registers).  Iteration t waits for its copies of tile t, then
+  // (after the barrier) starts those of tile t + 1 into the other buffers,
+  // which held tile t - 1, read before the barrier.
   if (ntiles > 0) {
     attn_issue_k(s_k(0), kbase, k_begin, k_end, wave, lane);
-    attn_load_v(st, vbase, k_begin, k_end, kq, vch);
+    attn_issue_v(s_v(0), vbase, k_begin, k_end, wave, lane);
   }
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t & 1;
-    attn_store_v(st, s_v(buf), kq, vch);
-    // this wave's copies of K(t) have landed; after the barrier every wave's
+    // this wave's copies of tile t have landed; after the barrier every wave's
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __syncthreads();
     if (t + 1 < ntiles) {
       attn_issue_k(s_k(buf ^ 1), kbase, k_begin + (t + 1) * kAttnKeys, k_end, wave, lane);
-      attn_load_v(st, vbase, k_begin + (t + 1) * kAttnKeys, k_end, kq, vch);
+      attn_issue_v(s_v(buf ^ 1), vbase, k_begin + (t + 1) * kAttnKeys, k_end, wave, lane);
     }
     const int hkey0 = k_begin + t * kAttnKeys + kh * 64;   // first key of this wave's half
     const bf16_t* sk = s_k(buf) + kh * 64 * kKStride;
-    const bf16_t* sv = s_v(buf) + kh * 64;
+    const bf16_t* sv = s_v(buf);
 
     // S^T blocks [kb][qb]: MFMA row 4 g4 + r of block kb is key
     // 32 (kb / 2) + 8 g4 + 4 (kb & 1) + r of the half; column = row l16
@@ -374,8 +376,7 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(
     for (int ch = 0; ch < 2; ++ch) {
 #pragma unroll
       for (int d = 0; d < 8; ++d) {
-        const bf16x8_t va = *reinterpret_cast<const bf16x8_t*>(
-            &sv[(d * 16 + l16) * kVStride + ch * 32 + g4 * 8]);
+        const bf16x8_t va = attn_read_vt(sv, kh * 64 + ch * 32 + g4 * 8, d * 16, l16);
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
           acc_o[qb][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pf[qb][ch], acc_o[qb][d], 0, 0, 0);
