@@ -21,8 +21,9 @@
 //      that they share its K/V tiles in one L2; eight waves: four row groups
 //      of 32 packed rows x two halves of every 128-key tile (two waves per
 //      SIMD), merged through LDS at the end; K tile [128 keys][dh] (rows in
-//      MFMA order) and V^T tile [dh][128 keys] staged in LDS (double
-//      buffered); S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_16x16x32_bf16
+//      MFMA order) and V tile [128 keys][dh] copied into LDS by direct-to-LDS
+//      loads (double buffered), V^T fragments read by transposing LDS reads;
+//      S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_16x16x32_bf16
 //      so that the probabilities leave the S MFMA already in the B-operand
 //      layout of the PV MFMA; the running maximum is raised lazily.
 //      f32: attn_f32_kernel, one wave per (query, head) -- parity path.
