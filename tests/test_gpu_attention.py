@@ -62,6 +62,16 @@ def test_canvas_attention_bf16_full_size(B):
     _check(case, [2048] * B, 2304, CANVAS, torch.bfloat16)
 
 
+@pytest.mark.parametrize("B", [1, 4])
+def test_canvas_attention_bf16_canvas_step_size(B):
+    """The canvas step's own shape: 256 queries over an 8192-token prefix and
+    the canvas (16 query / 8 KV heads of 128) in a cache sized for the prompt
+    and four blocks, as bench.py runs it: every workgroup walks up to 9 (batch
+    1) or 33 (batch 4) key tiles through the double-buffered LDS copies."""
+    case = attention_case(B=B, Lq=256, P=8192, seed=40 + B)
+    _check(case, [8192] * B, 8192 + 4 * 256, CANVAS, torch.bfloat16)
+
+
 def test_canvas_attention_bf16_ragged_rows():
     """Different prefix per row, ragged block and key tiles, spare cache."""
     case = attention_case(B=3, Lq=100, P=700, seed=11)
